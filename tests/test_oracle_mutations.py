@@ -1,0 +1,157 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case plants one mistake in the oracle (on the CPU, via monkeypatch: a dropped term, a wrong sign or
+index, a transposed operand, a swapped coefficient) and runs the pins that should notice it; the case
+passes only if at least one of those pins fails.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import test_oracle_attention as ta
+import test_oracle_ema as te
+import test_oracle_select as ts
+from _util import oracle_view
+from block_sparse_attention_quest_amd import workloads as wl
+from oracle import prr_oracle as orc
+
+_orig = {name: getattr(orc, name) for name in dir(orc) if callable(getattr(orc, name))}
+
+
+def _small_fixture(w):
+    q, kv = oracle_view(wl.make_inputs(w))
+    return w, q[0], kv
+
+
+def _sel_fixture():
+    q, kv = oracle_view(wl.make_inputs(ts.W))
+    return q[0], kv, orc.build_meta(kv, ts.W.block, ts.W.num_kv_heads)
+
+
+def _fails(*checks):
+    for fn, args in checks:
+        try:
+            fn(*args)
+        except AssertionError:
+            return True
+    return False
+
+
+# ---- planted mistakes ----
+
+def merge_wrong_sign(a, b):
+    m = max(a.m, b.m)
+    if m == -math.inf:
+        return orc.State(a.acc + b.acc, 0.0, -math.inf)
+    fa = 0.0 if a.m == -math.inf else math.exp(m - a.m)
+    fb = 0.0 if b.m == -math.inf else math.exp(b.m - m)
+    return orc.State(fa * a.acc + fb * b.acc, fa * a.l + fb * b.l, m)
+
+
+def merge_drop_l_term(a, b):
+    s = _orig["merge"](a, b)
+    fa = 0.0 if a.m == -math.inf else math.exp(a.m - s.m) if s.m != -math.inf else 0.0
+    return orc.State(s.acc, fa * a.l, s.m)
+
+
+def gather_v_is_k(kv, b, kvh, blocks, block):
+    K, _ = _orig["gather_kv"](kv, b, kvh, blocks, block)
+    return K, K.copy()
+
+
+def gather_v_wrong_token(kv, b, kvh, blocks, block):
+    K, V = _orig["gather_kv"](kv, b, kvh, blocks, block)
+    return K, V[::-1].copy()
+
+
+def quest_max_only(qbar, mn, mx):
+    s = np.zeros(mn.shape[0])
+    for i in range(mn.shape[1]):
+        s = s + qbar[i] * mx[:, i]
+    return s
+
+
+def rep_query_no_divide(q_all, b, kvh, G):
+    return _orig["representative_query"](q_all, b, kvh, G) * G
+
+
+def rep_query_wrong_heads(q_all, b, kvh, G):
+    return np.mean(q_all[b, kvh::max(1, q_all.shape[1] // G)][:G], axis=0)
+
+
+def topk_ties_to_larger(scores, k):
+    n = scores.shape[0]
+    k = max(0, min(int(k), n))
+    order = np.lexsort((-np.arange(n), -scores))
+    return np.sort(order[:k]).astype(np.int64)
+
+
+def ema_trend_uses_new_level(level, trend, IS, alpha, beta):
+    new_level = alpha * IS + (1.0 - alpha) * level
+    new_trend = beta * (IS - new_level) + (1.0 - beta) * trend
+    return new_level, new_trend
+
+
+def ema_swapped_alpha(level, trend, IS, alpha, beta):
+    new_trend = beta * (IS - level) + (1.0 - beta) * trend
+    new_level = (1.0 - alpha) * IS + alpha * level
+    return new_level, new_trend
+
+
+def ema_predict_minus(level, trend, gamma):
+    return level - gamma * trend
+
+
+def hit_rate_unweighted(IS_row, P, A):
+    return len(np.intersect1d(P, A)) / max(1, len(A))
+
+
+def calibrate_divide_by_T(IS, k, grid=None):
+    H, best = _orig["calibrate"](IS, k, grid)
+    T = np.asarray(IS).shape[0]
+    return H * (T - 1) / T, best
+
+
+def _attention_checks():
+    fx = _small_fixture(ta.SMALL)
+    return [(ta.test_decomposition_identity, (fx,)), (ta.test_dense_case_matches_torch_sdpa, (fx,)),
+            (ta.test_closed_forms, ())]
+
+
+def _select_checks():
+    sel = _sel_fixture()
+    return [(ts.test_quest_score_is_upper_bound, (sel,)), (ts.test_representative_query_is_group_mean, (sel,)),
+            (ts.test_planted_blocks_are_selected, ()), (ts.test_topk_matches_heapq_with_ties, ())]
+
+
+def _ema_checks():
+    return [(te.test_hand_worked_steps, ()), (te.test_calibration_hand_worked, ()),
+            (te.test_ramp_asymptotics, (0.6, 0.3, 0.5))]
+
+
+MUTATIONS = [
+    ("merge", merge_wrong_sign, _attention_checks),
+    ("merge", merge_drop_l_term, _attention_checks),
+    ("gather_kv", gather_v_is_k, _attention_checks),
+    ("gather_kv", gather_v_wrong_token, _attention_checks),
+    ("quest_scores", quest_max_only, _select_checks),
+    ("representative_query", rep_query_no_divide, _select_checks),
+    ("representative_query", rep_query_wrong_heads, _select_checks),
+    ("topk_blocks", topk_ties_to_larger, _select_checks),
+    ("ema_update", ema_trend_uses_new_level, _ema_checks),
+    ("ema_update", ema_swapped_alpha, _ema_checks),
+    ("ema_predict", ema_predict_minus, _ema_checks),
+    ("hit_rate_row", hit_rate_unweighted, _ema_checks),
+    ("calibrate", calibrate_divide_by_T, _ema_checks),
+]
+
+
+@pytest.mark.parametrize("target,mutant,checks", MUTATIONS, ids=[m[1].__name__ for m in MUTATIONS])
+def test_pins_catch_planted_mistake(monkeypatch, target, mutant, checks):
+    monkeypatch.setattr(orc, target, mutant)
+    assert _fails(*checks()), f"no pin noticed the planted mistake {mutant.__name__}"
+
+
+def test_unmutated_oracle_passes_the_same_checks():
+    assert not _fails(*_attention_checks(), *_select_checks(), *_ema_checks())
