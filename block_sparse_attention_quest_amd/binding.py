@@ -1,0 +1,317 @@
+"""ctypes binding of libprr.so (argument marshalling only; every step runs in the HIP library).
+
+Torch provides device memory and streams.  The functions here take torch tensors that already live on
+the GPU, pass their device pointers and the current (or given) torch stream to the C entry points
+declared in include/prr.h, and raise PrrError on a non-zero status.  There is no CPU fallback: if the
+library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libprr.so")
+
+PRR_F32, PRR_BF16 = 0, 1
+PAGE_SIZE = 16
+
+# Every symbol include/prr.h declares.
+EXPORTS = (
+    "prr_max_blocks", "prr_meta_stride", "prr_meta_bytes", "prr_attn_workspace_bytes",
+    "prr_workspace_clear", "prr_build_meta", "prr_select", "prr_predict", "prr_spec_attn",
+    "prr_repair", "prr_strerror",
+)
+
+
+class PrrError(RuntimeError):
+    def __init__(self, status: int, where: str, text: str):
+        super().__init__(f"{where}: {text} (status {status})")
+        self.status = status
+
+
+class KvCacheStruct(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("page_table", ctypes.c_void_p),
+                ("seq_len", ctypes.c_void_p), ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("dtype", ctypes.c_int)]
+
+
+class BlockSetStruct(ctypes.Structure):
+    _fields_ = [("idx", ctypes.c_void_p), ("count", ctypes.c_void_p), ("cap", ctypes.c_int32)]
+
+
+class AttnStateStruct(ctypes.Structure):
+    _fields_ = [("acc", ctypes.c_void_p), ("l", ctypes.c_void_p), ("m", ctypes.c_void_p)]
+
+
+_P = ctypes.POINTER
+_VP, _I32, _SZ, _D, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_double, ctypes.c_float
+
+_SIGS = {
+    "prr_max_blocks": (_I32, [_P(KvCacheStruct), _I32]),
+    "prr_meta_stride": (_I32, [_P(KvCacheStruct), _I32]),
+    "prr_meta_bytes": (_SZ, [_P(KvCacheStruct), _I32]),
+    "prr_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "prr_workspace_clear": (ctypes.c_int, [_VP, _SZ, _VP]),
+    "prr_build_meta": (ctypes.c_int, [_P(KvCacheStruct), _I32, _VP, _VP]),
+    "prr_select": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _VP, _I32, _I32, _P(BlockSetStruct), _VP,
+                                  _P(BlockSetStruct), _P(BlockSetStruct), _VP]),
+    "prr_predict": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _D, _D, _D, _I32, _VP, _VP, _VP,
+                                   _P(BlockSetStruct), _VP]),
+    "prr_spec_attn": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _I32, _P(BlockSetStruct), _F,
+                                     _P(AttnStateStruct), _VP, _SZ, _VP]),
+    "prr_repair": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _I32, _P(BlockSetStruct), _F,
+                                  _P(AttnStateStruct), _VP, _VP, _SZ, _VP]),
+    "prr_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libprr.so and declare its signatures.  Raises if the library has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libprr.so not found at {path}; build it with "
+                          "`python -m block_sparse_attention_quest_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise PrrError(status, where, load_library().prr_strerror(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return PRR_BF16
+    if t.dtype == torch.float32:
+        return PRR_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# --------------------------------------------------------------------------------------------------
+# Tensor-level containers
+# --------------------------------------------------------------------------------------------------
+
+
+@dataclass
+class KVCache:
+    """Paged cache on the device: k [pages][Hkv][16][d], v [pages][Hkv][d][16], page_table [B][P],
+    seq_len [B]."""
+
+    k: torch.Tensor
+    v: torch.Tensor
+    page_table: torch.Tensor
+    seq_len: torch.Tensor
+
+    @property
+    def batch(self) -> int:
+        return self.page_table.shape[0]
+
+    @property
+    def num_kv_heads(self) -> int:
+        return self.k.shape[1]
+
+    @property
+    def head_dim(self) -> int:
+        return self.k.shape[3]
+
+    def struct(self) -> KvCacheStruct:
+        return KvCacheStruct(self.k.data_ptr(), self.v.data_ptr(), self.page_table.data_ptr(),
+                             self.seq_len.data_ptr(), self.batch, self.num_kv_heads, self.head_dim,
+                             self.k.shape[2], self.k.shape[0], self.page_table.shape[1],
+                             _dtype_code(self.k))
+
+
+@dataclass
+class BlockSet:
+    """idx [B][Hkv][cap] int32, count [B][Hkv] int32 (device)."""
+
+    idx: torch.Tensor
+    count: torch.Tensor
+
+    @property
+    def cap(self) -> int:
+        return self.idx.shape[-1]
+
+    @staticmethod
+    def empty(batch: int, hkv: int, cap: int, device="cuda") -> "BlockSet":
+        return BlockSet(torch.zeros((batch, hkv, cap), dtype=torch.int32, device=device),
+                        torch.zeros((batch, hkv), dtype=torch.int32, device=device))
+
+    def struct(self) -> BlockSetStruct:
+        return BlockSetStruct(self.idx.data_ptr(), self.count.data_ptr(), self.cap)
+
+    def lists(self):
+        """Host copy as nested python lists [b][kvh] -> list of block ids."""
+        idx = self.idx.cpu().numpy()
+        cnt = self.count.cpu().numpy()
+        return [[idx[b, h, :cnt[b, h]].tolist() for h in range(idx.shape[1])] for b in range(idx.shape[0])]
+
+
+@dataclass
+class AttnState:
+    """acc [B][Hq][d] (unnormalised), l [B][Hq], m [B][Hq] (natural log units), fp32 device."""
+
+    acc: torch.Tensor
+    l: torch.Tensor
+    m: torch.Tensor
+
+    @staticmethod
+    def empty(batch: int, hq: int, d: int, device="cuda") -> "AttnState":
+        return AttnState(torch.zeros((batch, hq, d), dtype=torch.float32, device=device),
+                         torch.zeros((batch, hq), dtype=torch.float32, device=device),
+                         torch.full((batch, hq), float("-inf"), dtype=torch.float32, device=device))
+
+    def clone(self) -> "AttnState":
+        return AttnState(self.acc.clone(), self.l.clone(), self.m.clone())
+
+    def struct(self) -> AttnStateStruct:
+        return AttnStateStruct(self.acc.data_ptr(), self.l.data_ptr(), self.m.data_ptr())
+
+
+class Workspace:
+    """A zero-initialised device buffer for one stream's attention calls."""
+
+    def __init__(self, nbytes: int, device="cuda"):
+        self.buf = torch.zeros(max(256, int(nbytes)), dtype=torch.uint8, device=device)
+
+    @property
+    def nbytes(self) -> int:
+        return self.buf.numel()
+
+    def ptr(self):
+        return ctypes.c_void_p(self.buf.data_ptr())
+
+
+# --------------------------------------------------------------------------------------------------
+# Entry points
+# --------------------------------------------------------------------------------------------------
+
+
+def max_blocks(kv: KVCache, block: int) -> int:
+    s = kv.struct()
+    return load_library().prr_max_blocks(ctypes.byref(s), block)
+
+
+def meta_stride(kv: KVCache, block: int) -> int:
+    s = kv.struct()
+    return load_library().prr_meta_stride(ctypes.byref(s), block)
+
+
+def attn_workspace_bytes(batch: int, hq: int, hkv: int, d: int, block: int, cap: int) -> int:
+    return load_library().prr_attn_workspace_bytes(batch, hq, hkv, d, block, cap)
+
+
+def workspace_for(kv: KVCache, hq: int, block: int, cap: int) -> Workspace:
+    return Workspace(attn_workspace_bytes(kv.batch, hq, kv.num_kv_heads, kv.head_dim, block, cap),
+                     device=kv.k.device)
+
+
+def workspace_clear(ws: Workspace, stream=None):
+    _check(load_library().prr_workspace_clear(ws.ptr(), ws.nbytes, _stream(stream)), "prr_workspace_clear")
+
+
+def build_meta(kv: KVCache, block: int, meta: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Block min/max metadata [B][Hkv][d][2][stride] in the cache dtype."""
+    lib = load_library()
+    s = kv.struct()
+    if meta is None:
+        stride = lib.prr_meta_stride(ctypes.byref(s), block)
+        meta = torch.empty((kv.batch, kv.num_kv_heads, kv.head_dim, 2, stride), dtype=kv.k.dtype,
+                           device=kv.k.device)
+    _check(lib.prr_build_meta(ctypes.byref(s), block, _ptr(meta), _stream(stream)), "prr_build_meta")
+    return meta
+
+
+def select(q: torch.Tensor, kv: KVCache, meta: torch.Tensor, block: int, topk: int,
+           P: Optional[BlockSet] = None, scores: Optional[torch.Tensor] = None,
+           A: Optional[BlockSet] = None, M: Optional[BlockSet] = None, stream=None):
+    """Quest scores [B][Hkv][Nmax] fp64, A (top-k, ascending) and M = A \\ P when P is given."""
+    lib = load_library()
+    s = kv.struct()
+    nmax = lib.prr_max_blocks(ctypes.byref(s), block)
+    B, H = kv.batch, kv.num_kv_heads
+    dev = kv.k.device
+    if scores is None:
+        scores = torch.zeros((B, H, nmax), dtype=torch.float64, device=dev)
+    if A is None:
+        A = BlockSet.empty(B, H, max(1, topk), dev)
+    if P is not None and M is None:
+        M = BlockSet.empty(B, H, max(1, topk), dev)
+    a_s = A.struct()
+    p_s = P.struct() if P is not None else None
+    m_s = M.struct() if M is not None else None
+    st = lib.prr_select(_ptr(q), q.shape[1], ctypes.byref(s), _ptr(meta), block, topk,
+                        ctypes.byref(p_s) if p_s is not None else None, _ptr(scores), ctypes.byref(a_s),
+                        ctypes.byref(m_s) if m_s is not None else None, _stream(stream))
+    _check(st, "prr_select")
+    return scores, A, M
+
+
+def predict(scores: torch.Tensor, seq_len: torch.Tensor, block: int, alpha: float, beta: float,
+            gamma: float, budget: int, level: torch.Tensor, trend: torch.Tensor, live: torch.Tensor,
+            P_next: Optional[BlockSet] = None, stream=None) -> BlockSet:
+    """One EMA step over scores [B][Hkv][Nmax]; updates level/trend/live in place; returns P_next."""
+    lib = load_library()
+    B, H, nmax = scores.shape
+    if P_next is None:
+        P_next = BlockSet.empty(B, H, max(1, budget), scores.device)
+    ps = P_next.struct()
+    st = lib.prr_predict(_ptr(scores), _ptr(seq_len), B, H, block, nmax, float(alpha), float(beta),
+                         float(gamma), budget, _ptr(level), _ptr(trend), _ptr(live), ctypes.byref(ps),
+                         _stream(stream))
+    _check(st, "prr_predict")
+    return P_next
+
+
+def spec_attn(q: torch.Tensor, kv: KVCache, block: int, P: BlockSet, scale: float,
+              out: Optional[AttnState] = None, ws: Optional[Workspace] = None, stream=None) -> AttnState:
+    """Speculative attention over P: the unnormalised state (acc, l, m) of every query head."""
+    lib = load_library()
+    B, Hq, d = q.shape
+    if out is None:
+        out = AttnState.empty(B, Hq, d, q.device)
+    if ws is None:
+        ws = workspace_for(kv, Hq, block, P.cap)
+    s, ps, os_ = kv.struct(), P.struct(), out.struct()
+    st = lib.prr_spec_attn(_ptr(q), Hq, ctypes.byref(s), block, ctypes.byref(ps), float(scale),
+                           ctypes.byref(os_), ws.ptr(), ws.nbytes, _stream(stream))
+    _check(st, "prr_spec_attn")
+    return out
+
+
+def repair(q: torch.Tensor, kv: KVCache, block: int, M: BlockSet, scale: float, state: AttnState,
+           out: Optional[torch.Tensor] = None, ws: Optional[Workspace] = None, stream=None) -> AttnState:
+    """Fold the missed blocks M into `state` in place; optionally write the normalised output."""
+    lib = load_library()
+    B, Hq, d = q.shape
+    if ws is None:
+        ws = workspace_for(kv, Hq, block, M.cap)
+    s, ms, ss = kv.struct(), M.struct(), state.struct()
+    st = lib.prr_repair(_ptr(q), Hq, ctypes.byref(s), block, ctypes.byref(ms), float(scale),
+                        ctypes.byref(ss), _ptr(out), ws.ptr(), ws.nbytes, _stream(stream))
+    _check(st, "prr_repair")
+    return state

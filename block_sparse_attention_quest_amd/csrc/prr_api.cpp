@@ -1,0 +1,188 @@
+// prr_api.cpp - the extern "C" boundary of libprr.so: argument validation, sizes, dispatch.
+// Every check here runs before anything is enqueued; see include/prr.h for the contract.
+
+#include "prr.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "prr_internal.hpp"
+
+namespace {
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+prr_status check_kv(const prr_kv_cache *kv) {
+    if (!kv || !kv->k || !kv->v || !kv->page_table || !kv->seq_len) return PRR_EINVAL;
+    if (kv->batch <= 0 || kv->num_kv_heads <= 0 || kv->num_pages <= 0 || kv->max_pages <= 0)
+        return PRR_EINVAL;
+    if (kv->page_size != prr::kPage) return PRR_EUNSUPPORTED;
+    if (kv->head_dim != 64 && kv->head_dim != 128) return PRR_EUNSUPPORTED;
+    if (kv->dtype != PRR_F32 && kv->dtype != PRR_BF16) return PRR_EUNSUPPORTED;
+    return PRR_OK;
+}
+
+prr_status check_block(const prr_kv_cache *kv, int32_t block) {
+    if (block <= 0 || block % kv->page_size != 0) return PRR_EINVAL;
+    if ((int64_t)kv->max_pages * kv->page_size % block != 0) return PRR_EINVAL;
+    return PRR_OK;
+}
+
+prr_status check_heads(const prr_kv_cache *kv, int32_t hq) {
+    if (hq <= 0 || hq % kv->num_kv_heads != 0) return PRR_EINVAL;
+    const int G = hq / kv->num_kv_heads;
+    if (!is_pow2(G) || G > 16) return PRR_EUNSUPPORTED;
+    return PRR_OK;
+}
+
+prr_status check_set(const prr_block_set *s) {
+    if (!s || !s->idx || !s->count || s->cap <= 0) return PRR_EINVAL;
+    return PRR_OK;
+}
+
+prr::KvDesc desc(const prr_kv_cache *kv) {
+    prr::KvDesc d;
+    d.k = kv->k;
+    d.v = kv->v;
+    d.page_table = kv->page_table;
+    d.seq_len = kv->seq_len;
+    d.batch = kv->batch;
+    d.hkv = kv->num_kv_heads;
+    d.d = kv->head_dim;
+    d.num_pages = kv->num_pages;
+    d.max_pages = kv->max_pages;
+    d.bf16 = kv->dtype == PRR_BF16;
+    return d;
+}
+
+prr_status hip_status(hipError_t e) { return e == hipSuccess ? PRR_OK : PRR_EHIP; }
+
+#define PRR_TRY(x)                      \
+    do {                                \
+        const prr_status s_ = (x);      \
+        if (s_ != PRR_OK) return s_;    \
+    } while (0)
+
+prr_status attn_common(const void *q, int32_t hq, const prr_kv_cache *kv, int32_t block,
+                       const prr_block_set *set, void *ws, size_t ws_bytes) {
+    if (!q) return PRR_EINVAL;
+    PRR_TRY(check_kv(kv));
+    PRR_TRY(check_block(kv, block));
+    PRR_TRY(check_heads(kv, hq));
+    PRR_TRY(check_set(set));
+    const size_t need = prr::attn_workspace_bytes(kv->batch, hq, kv->num_kv_heads, kv->head_dim, block,
+                                                  set->cap);
+    if (!ws || ws_bytes < need) return PRR_EWORKSPACE;
+    return PRR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t prr_max_blocks(const prr_kv_cache *kv, int32_t block) {
+    if (!kv || block <= 0) return 0;
+    return (int32_t)((int64_t)kv->max_pages * kv->page_size / block);
+}
+
+int32_t prr_meta_stride(const prr_kv_cache *kv, int32_t block) {
+    const int32_t n = prr_max_blocks(kv, block);
+    return (n + 7) / 8 * 8;
+}
+
+size_t prr_meta_bytes(const prr_kv_cache *kv, int32_t block) {
+    if (!kv) return 0;
+    const size_t elem = kv->dtype == PRR_BF16 ? 2 : 4;
+    return (size_t)kv->batch * kv->num_kv_heads * kv->head_dim * 2 * prr_meta_stride(kv, block) * elem;
+}
+
+size_t prr_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block, int32_t cap) {
+    if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block < prr::kPage ||
+        cap <= 0)
+        return 0;
+    return prr::attn_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, block, cap);
+}
+
+prr_status prr_workspace_clear(void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!ws && ws_bytes) return PRR_EINVAL;
+    return hip_status(prr::launch_clear(ws, ws_bytes, stream));
+}
+
+prr_status prr_build_meta(const prr_kv_cache *kv, int32_t block, void *meta, hipStream_t stream) {
+    PRR_TRY(check_kv(kv));
+    PRR_TRY(check_block(kv, block));
+    if (!meta) return PRR_EINVAL;
+    return hip_status(prr::launch_meta(desc(kv), block, prr_meta_stride(kv, block), meta, stream));
+}
+
+prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
+                      int32_t block, int32_t topk, const prr_block_set *P, double *scores,
+                      prr_block_set *A, prr_block_set *M, hipStream_t stream) {
+    if (!q || !meta || !scores) return PRR_EINVAL;
+    PRR_TRY(check_kv(kv));
+    PRR_TRY(check_block(kv, block));
+    PRR_TRY(check_heads(kv, num_q_heads));
+    PRR_TRY(check_set(A));
+    if (topk < 0) return PRR_EINVAL;
+    if (A->cap < topk) return PRR_EINVAL;
+    if ((P == nullptr) != (M == nullptr)) return PRR_EINVAL;
+    if (P) {
+        PRR_TRY(check_set(P));
+        PRR_TRY(check_set(M));
+        if (M->cap < topk) return PRR_EINVAL;
+    }
+    const int nmax = prr_max_blocks(kv, block);
+    if (nmax > prr::kMaxSelectN) return PRR_EUNSUPPORTED;
+    return hip_status(prr::launch_select(desc(kv), q, num_q_heads, meta, block, prr_meta_stride(kv, block),
+                                         nmax, topk, P ? P->idx : nullptr, P ? P->count : nullptr,
+                                         P ? P->cap : 0, scores, A->idx, A->count, A->cap,
+                                         M ? M->idx : nullptr, M ? M->count : nullptr, M ? M->cap : 0,
+                                         stream));
+}
+
+prr_status prr_predict(const double *scores, const int32_t *seq_len, int32_t batch,
+                       int32_t num_kv_heads, int32_t block, int32_t max_blocks, double alpha,
+                       double beta, double gamma, int32_t budget, double *level, double *trend,
+                       int32_t *live, prr_block_set *P_next, hipStream_t stream) {
+    if (!scores || !seq_len || !level || !trend || !live) return PRR_EINVAL;
+    if (batch <= 0 || num_kv_heads <= 0 || block <= 0 || max_blocks <= 0 || budget < 0) return PRR_EINVAL;
+    PRR_TRY(check_set(P_next));
+    if (P_next->cap < budget) return PRR_EINVAL;
+    if (max_blocks > prr::kMaxSelectN) return PRR_EUNSUPPORTED;
+    return hip_status(prr::launch_predict(scores, seq_len, batch, num_kv_heads, block, max_blocks, alpha,
+                                          beta, gamma, budget, level, trend, live, P_next->idx,
+                                          P_next->count, P_next->cap, stream));
+}
+
+prr_status prr_spec_attn(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, int32_t block,
+                         const prr_block_set *P, float scale, prr_attn_state *out, void *ws,
+                         size_t ws_bytes, hipStream_t stream) {
+    PRR_TRY(attn_common(q, num_q_heads, kv, block, P, ws, ws_bytes));
+    if (!out || !out->acc || !out->l || !out->m) return PRR_EINVAL;
+    return hip_status(prr::launch_attn(desc(kv), q, num_q_heads, block, P->idx, P->count, P->cap, scale,
+                                       out->acc, out->l, out->m, nullptr, false, ws, stream));
+}
+
+prr_status prr_repair(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, int32_t block,
+                      const prr_block_set *M, float scale, prr_attn_state *state, float *out,
+                      void *ws, size_t ws_bytes, hipStream_t stream) {
+    PRR_TRY(attn_common(q, num_q_heads, kv, block, M, ws, ws_bytes));
+    if (!state || !state->acc || !state->l || !state->m) return PRR_EINVAL;
+    return hip_status(prr::launch_attn(desc(kv), q, num_q_heads, block, M->idx, M->count, M->cap, scale,
+                                       state->acc, state->l, state->m, out, true, ws, stream));
+}
+
+const char *prr_strerror(prr_status status) {
+    switch (status) {
+        case PRR_OK: return "ok";
+        case PRR_EINVAL: return "invalid argument";
+        case PRR_EUNSUPPORTED: return "unsupported shape or dtype";
+        case PRR_EWORKSPACE: return "workspace missing or too small";
+        case PRR_EHIP: return "HIP launch or runtime error";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

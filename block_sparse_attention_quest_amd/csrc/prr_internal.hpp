@@ -1,0 +1,44 @@
+// Internal launch interface between the C ABI (prr_api.cpp) and the kernels.  Host-side only types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace prr {
+
+constexpr int kPage = 16;          // tokens per page (the only supported page size)
+constexpr int kMaxSelectN = 32768; // blocks per (sequence, kv head) the top-K kernels hold on chip
+
+struct KvDesc {
+    const void *k;
+    const void *v;
+    const int32_t *page_table;
+    const int32_t *seq_len;
+    int batch, hkv, d, num_pages, max_pages;
+    bool bf16;
+};
+
+// Attention workspace: [units] uint32 counters, padded to 256 B, then the per-workgroup partials.
+size_t attn_workspace_bytes(int batch, int hq, int hkv, int d, int block, int cap);
+int attn_wg_per_unit(int block, int cap, bool bf16, int d);
+
+hipError_t launch_attn(const KvDesc &kv, const void *q, int hq, int block, const int32_t *idx,
+                       const int32_t *count, int cap, float scale, float *acc, float *l, float *m,
+                       float *out, bool repair, void *ws, hipStream_t stream);
+
+hipError_t launch_clear(void *ws, size_t bytes, hipStream_t stream);
+
+hipError_t launch_meta(const KvDesc &kv, int block, int stride, void *meta, hipStream_t stream);
+
+hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *meta, int block,
+                         int stride, int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt,
+                         int p_cap, double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap,
+                         int32_t *m_idx, int32_t *m_cnt, int m_cap, hipStream_t stream);
+
+hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batch, int hkv,
+                          int block, int nmax, double alpha, double beta, double gamma, int budget,
+                          double *level, double *trend, int32_t *live, int32_t *p_idx,
+                          int32_t *p_cnt, int p_cap, hipStream_t stream);
+
+}  // namespace prr

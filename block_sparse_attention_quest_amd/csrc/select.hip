@@ -1,0 +1,624 @@
+// select.hip - Quest block metadata, GQA Quest scoring, top-K selection with M = A \ P, and the fused
+// EMA level/trend predictor (gfx950).  Compiled with -ffp-contract=off: every float64 multiply and add
+// below is a separately rounded IEEE operation, in the order the comments state, so scores and
+// predictions are bit-identical to a plain float64 evaluation of the same formulas.
+//
+// Citations:
+//   [paper] "Predict, Reuse, and Repair: Accelerating Dynamic Sparse Attention for Long-Context LLM
+//           Decoding" (full paper text)
+//   [blog]  "PRR: Predict, Reuse, and Repair - Accelerating Dynamic Sparse Attention for Long-Context
+//           LLM Decoding" (xllm-io paper review)
+//
+// Scoring ([paper] A.1): s_p = sum_i max(qbar_i mn_{p,i}, qbar_i mx_{p,i}).  Because rounding is
+// monotone, max(round(qbar mn), round(qbar mx)) = round(qbar mx) when qbar >= 0 and round(qbar mn)
+// otherwise, so the kernel reads only the metadata row the sign of qbar_i selects: half the bytes of
+// reading both, with identical bits.  Metadata is channel-major ([d][2][N]) so a lane owning 8
+// consecutive blocks does one 16-byte load per channel and accumulates its blocks in channel order.
+//
+// Top-K ([paper] §1, §2.1; ties to the smaller block index): one 1024-thread workgroup per
+// (sequence, kv head) keeps all N keys in registers (order-preserving 64-bit images of the fp64 scores)
+// and runs an MSD radix select with 4-bit digits: per pass each thread counts its candidates into
+// packed 8-bit counters, waves reduce with cross-lane adds and one barrier combines waves.  Leading
+// bits shared by every key are skipped, and the search stops as soon as the boundary digit's bucket
+// is taken whole.  Ties on the full key go to the smaller index through a prefix sum over the
+// threads' contiguous index ranges, which also yields the ascending output positions directly.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "prr_internal.hpp"
+
+#pragma clang fp contract(off)
+
+namespace prr {
+namespace {
+
+constexpr int kTK = 1024;            // top-K workgroup size
+constexpr int kTKWaves = kTK / 64;
+
+__device__ __forceinline__ double dadd(double a, double b) {
+#pragma clang fp contract(off)
+    return a + b;
+}
+__device__ __forceinline__ double dmul(double a, double b) {
+#pragma clang fp contract(off)
+    return a * b;
+}
+__device__ __forceinline__ double dsub(double a, double b) {
+#pragma clang fp contract(off)
+    return a - b;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// Order-preserving image of a double (larger double -> larger key); -0.0 maps with +0.0.
+__device__ __forceinline__ uint64_t order_key(double x) {
+    uint64_t b = (uint64_t)__double_as_longlong(x);
+    if (b == 0x8000000000000000ull) b = 0;
+    return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int o) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, o);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+struct TopkSmem {
+    uint32_t hist[2][kTKWaves][8];
+    uint64_t andor[kTKWaves][2];
+    uint32_t scan[2][kTKWaves];
+};
+
+// Exclusive prefix sum over the workgroup in thread order; `total` gets the sum.  `buf` selects one of
+// two LDS slots so back-to-back scans need a single barrier each.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, TopkSmem &sm, int buf, uint32_t &total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t v = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(v, o);
+        if (lane >= o) v += y;
+    }
+    if (lane == 63) sm.scan[buf][wave] = v;
+    __syncthreads();
+    const uint32_t wt = lane < kTKWaves ? sm.scan[buf][lane] : 0u;
+    const uint32_t before = wave_sum(lane < wave ? wt : 0u);
+    total = wave_sum(wt);
+    return before + v - x;
+}
+
+__device__ __forceinline__ uint64_t mask_from(int shift) {   // bits >= shift
+    return shift >= 64 ? 0ull : ~((1ull << shift) - 1ull);
+}
+
+// Widen four 8-bit counters (one u32) into four 16-bit fields (one u64).
+__device__ __forceinline__ uint64_t spread16(uint32_t x) {
+    return (uint64_t)(x & 0xffu) | ((uint64_t)(x & 0xff00u) << 8) | ((uint64_t)(x & 0xff0000u) << 16) |
+           ((uint64_t)(x & 0xff000000u) << 24);
+}
+
+// Select the k largest keys (key descending, index ascending) among the n valid ones.  Thread t owns
+// indices [t*KPT, t*KPT + KPT).  Returns a bitmask over the thread's KPT keys.
+template <int KPT>
+__device__ uint32_t block_topk(const uint64_t (&key)[KPT], int n, int k, TopkSmem &sm) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int base = threadIdx.x * KPT;
+    uint32_t valid = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        if (base + j < n) valid |= 1u << j;
+    if (k <= 0) return 0u;
+    if (k >= n) return valid;
+
+    // common leading bits of all valid keys
+    uint64_t a = ~0ull, o = 0ull;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        if (valid >> j & 1u) {
+            a &= key[j];
+            o |= key[j];
+        }
+#pragma unroll
+    for (int s = 32; s > 0; s >>= 1) {
+        a &= shfl_xor64(a, s);
+        o |= shfl_xor64(o, s);
+    }
+    if (lane == 0) {
+        sm.andor[wave][0] = a;
+        sm.andor[wave][1] = o;
+    }
+    __syncthreads();
+    a = ~0ull;
+    o = 0ull;
+#pragma unroll
+    for (int w = 0; w < kTKWaves; ++w) {
+        a &= sm.andor[w][0];
+        o |= sm.andor[w][1];
+    }
+    const uint64_t diff = a ^ o;
+
+    uint64_t prefix, mask;
+    int remaining = k;
+    bool take_all = false;
+    if (diff == 0) {
+        prefix = a;          // every key equal: pure tie break by index
+        mask = ~0ull;
+    } else {
+        const int top = 63 - __clzll((long long)diff);
+        int shift = (top / 4) * 4;
+        mask = mask_from(shift + 4);
+        prefix = a & mask;
+        int pass = 0;
+        for (; shift >= 0; shift -= 4, ++pass) {
+            uint64_t lo = 0, hi = 0;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                if ((valid >> j & 1u) && (key[j] & mask) == prefix) {
+                    const uint32_t d = (uint32_t)(key[j] >> shift) & 15u;
+                    const uint64_t inc = 1ull << ((d & 7u) * 8u);
+                    if (d & 8u) hi += inc;
+                    else lo += inc;
+                }
+            }
+            const uint64_t w0 = spread16((uint32_t)lo), w1 = spread16((uint32_t)(lo >> 32));
+            const uint64_t w2 = spread16((uint32_t)hi), w3 = spread16((uint32_t)(hi >> 32));
+            uint32_t c8[8] = {(uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32),
+                              (uint32_t)w2, (uint32_t)(w2 >> 32), (uint32_t)w3, (uint32_t)(w3 >> 32)};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c8[i] = wave_sum(c8[i]);
+            const int buf = pass & 1;
+            if (lane == 0) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) sm.hist[buf][wave][i] = c8[i];
+            }
+            __syncthreads();
+            // lane l reads words 2(l>>4), 2(l>>4)+1 of wave (l & 15); reduce over the 16 waves
+            uint32_t x0 = sm.hist[buf][lane & 15][2 * (lane >> 4)];
+            uint32_t x1 = sm.hist[buf][lane & 15][2 * (lane >> 4) + 1];
+#pragma unroll
+            for (int s = 1; s < 16; s <<= 1) {
+                x0 += __shfl_xor(x0, s);
+                x1 += __shfl_xor(x1, s);
+            }
+            uint32_t cnt[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t y0 = __shfl(x0, 16 * q), y1 = __shfl(x1, 16 * q);
+                cnt[4 * q + 0] = y0 & 0xffffu;
+                cnt[4 * q + 1] = y0 >> 16;
+                cnt[4 * q + 2] = y1 & 0xffffu;
+                cnt[4 * q + 3] = y1 >> 16;
+            }
+            int dsel = 0;
+            uint32_t cum = 0, csel = 0;
+            bool found = false;
+#pragma unroll
+            for (int d = 15; d >= 0; --d) {
+                if (!found) {
+                    if (cum + cnt[d] >= (uint32_t)remaining) {
+                        dsel = d;
+                        csel = cnt[d];
+                        found = true;
+                    } else {
+                        cum += cnt[d];
+                    }
+                }
+            }
+            remaining -= (int)cum;
+            prefix |= (uint64_t)dsel << shift;
+            mask |= 15ull << shift;
+            if (csel == (uint32_t)remaining) {
+                take_all = true;
+                break;
+            }
+        }
+    }
+
+    uint32_t sel = 0, tie = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        if (!(valid >> j & 1u)) continue;
+        const uint64_t mk = key[j] & mask;
+        if (mk > prefix) sel |= 1u << j;
+        else if (mk == prefix) tie |= 1u << j;
+    }
+    if (take_all) return sel | tie;
+    // ties on the full key: the `remaining` smallest indices win
+    uint32_t total;
+    const uint32_t before = block_excl_scan(__popc(tie), sm, 0, total);
+    uint32_t r = before;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        if (tie >> j & 1u) {
+            if (r < (uint32_t)remaining) sel |= 1u << j;
+            ++r;
+        }
+    return sel;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Block metadata
+// ------------------------------------------------------------------------------------------------
+
+struct MetaParams {
+    const void *k;
+    const int32_t *page_table;
+    const int32_t *seq_len;
+    void *meta;
+    int hkv, max_pages, num_pages, block, stride, nmax;
+};
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void meta_kernel(MetaParams p) {
+    constexpr int EPL = BF16 ? 8 : 4;          // channels per 16-byte load
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int u = blockIdx.y;
+    const int b = u / p.hkv, kvh = u - b * p.hkv;
+    const int blk = blockIdx.x * 64 + lane;
+    const int slen = min(max(p.seq_len[b], 0), p.max_pages * kPage);
+    const int nb = min((slen + p.block - 1) / p.block, p.nmax);
+    if (blk >= nb) return;
+    const int t0 = blk * p.block;
+    const int t1 = min(t0 + p.block, slen);
+    for (int cg = wave; cg < D / EPL; cg += 4) {
+        float mn[EPL], mx[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            mn[e] = INFINITY;
+            mx[e] = -INFINITY;
+        }
+        for (int t = t0; t < t1; ++t) {
+            int ph = p.page_table[(size_t)b * p.max_pages + t / kPage];
+            ph = min(max(ph, 0), p.num_pages - 1);
+            const size_t off = (((size_t)ph * p.hkv + kvh) * kPage + (t % kPage)) * D + cg * EPL;
+            if constexpr (BF16) {
+                const uint4 raw = *(const uint4 *)((const uint16_t *)p.k + off);
+                const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = bf16_to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1))));
+                    mn[e] = fminf(mn[e], x);
+                    mx[e] = fmaxf(mx[e], x);
+                }
+            } else {
+                const float4 raw = *(const float4 *)((const float *)p.k + off);
+                const float x[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    mn[e] = fminf(mn[e], x[e]);
+                    mx[e] = fmaxf(mx[e], x[e]);
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const int ch = cg * EPL + e;
+            const size_t row = (((size_t)u * D + ch) * 2) * p.stride;
+            if constexpr (BF16) {
+                uint16_t *m16 = (uint16_t *)p.meta;
+                m16[row + blk] = (uint16_t)(__float_as_uint(mn[e]) >> 16);
+                m16[row + p.stride + blk] = (uint16_t)(__float_as_uint(mx[e]) >> 16);
+            } else {
+                float *m32 = (float *)p.meta;
+                m32[row + blk] = mn[e];
+                m32[row + p.stride + blk] = mx[e];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Scoring
+// ------------------------------------------------------------------------------------------------
+
+struct ScoreParams {
+    const void *q;
+    const void *meta;
+    const int32_t *seq_len;
+    double *scores;
+    int hq, hkv, G, block, stride, nmax;
+};
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
+    constexpr int BPL = BF16 ? 8 : 4;   // blocks per lane (one 16-byte load per channel row)
+    __shared__ double s_qbar[D];
+    const int u = blockIdx.y;
+    const int b = u / p.hkv, kvh = u - b * p.hkv;
+    if (threadIdx.x < D) {
+        // qbar_i = (sum_{g=0}^{G-1} q_{kvh G + g, i}) / G, summed in order from +0.0
+        double acc = 0.0;
+        for (int gq = 0; gq < p.G; ++gq) {
+            const size_t off = ((size_t)b * p.hq + (size_t)kvh * p.G + gq) * D + threadIdx.x;
+            const double x = BF16 ? (double)bf16_to_f32(((const uint16_t *)p.q)[off])
+                                  : (double)((const float *)p.q)[off];
+            acc = dadd(acc, x);
+        }
+        s_qbar[threadIdx.x] = acc / (double)p.G;
+    }
+    __syncthreads();
+    const int slen = max(p.seq_len[b], 0);
+    const int nb = min((slen + p.block - 1) / p.block, p.nmax);
+    const int p0 = (blockIdx.x * 256 + threadIdx.x) * BPL;
+    if (p0 >= nb) return;
+    double acc[BPL];
+#pragma unroll
+    for (int e = 0; e < BPL; ++e) acc[e] = 0.0;
+    const size_t ubase = (size_t)u * D * 2 * p.stride + p0;
+#pragma unroll 8
+    for (int i = 0; i < D; ++i) {
+        const double qb = s_qbar[i];
+        // qbar >= 0: the max term is qbar * mx (row 1); otherwise qbar * mn (row 0)
+        const size_t off = ubase + ((size_t)i * 2 + (qb >= 0.0 ? 1 : 0)) * p.stride;
+        if constexpr (BF16) {
+            const uint4 raw = *(const uint4 *)((const uint16_t *)p.meta + off);
+            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const double x = (double)bf16_to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1))));
+                acc[e] = dadd(acc[e], dmul(qb, x));
+            }
+        } else {
+            const float4 raw = *(const float4 *)((const float *)p.meta + off);
+            const float x[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = dadd(acc[e], dmul(qb, (double)x[e]));
+        }
+    }
+    double *out = p.scores + (size_t)u * p.nmax;
+#pragma unroll
+    for (int e = 0; e < BPL; ++e)
+        if (p0 + e < nb) out[p0 + e] = acc[e];
+}
+
+// ------------------------------------------------------------------------------------------------
+// Top-K + set difference
+// ------------------------------------------------------------------------------------------------
+
+struct TopkParams {
+    const double *scores;
+    const int32_t *seq_len;
+    const int32_t *p_idx;
+    const int32_t *p_cnt;
+    int32_t *a_idx;
+    int32_t *a_cnt;
+    int32_t *m_idx;
+    int32_t *m_cnt;
+    int hkv, block, nmax, topk, p_cap, a_cap, m_cap;
+};
+
+template <int KPT>
+__global__ __launch_bounds__(kTK) void topk_kernel(TopkParams p) {
+    __shared__ TopkSmem sm;
+    __shared__ uint32_t s_pbits[kMaxSelectN / 32];
+    const int u = blockIdx.x;
+    const int b = u / p.hkv;
+    const int slen = p.seq_len[b];
+    const int nb = min((slen + p.block - 1) / p.block, p.nmax);
+    const bool want_m = p.m_idx != nullptr;
+    if (want_m) {
+        for (int i = threadIdx.x; i < kMaxSelectN / 32; i += kTK) s_pbits[i] = 0u;
+        __syncthreads();
+        const int pc = min(max(p.p_cnt[u], 0), p.p_cap);
+        for (int i = threadIdx.x; i < pc; i += kTK) {
+            const int x = p.p_idx[(size_t)u * p.p_cap + i];
+            if (x >= 0 && x < nb) atomicOr(&s_pbits[x >> 5], 1u << (x & 31));
+        }
+    }
+    uint64_t key[KPT];
+    const int base = threadIdx.x * KPT;
+    const double *row = p.scores + (size_t)u * p.nmax;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = base + j < nb ? order_key(row[base + j]) : 0ull;
+    const uint32_t sel = block_topk<KPT>(key, nb, p.topk, sm);
+    __syncthreads();   // P bitmap complete (and top-K scratch released)
+    uint32_t inm = 0;
+    if (want_m) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            if ((sel >> j & 1u) && !(s_pbits[(base + j) >> 5] >> ((base + j) & 31) & 1u)) inm |= 1u << j;
+    }
+    uint32_t total;
+    const uint32_t off = block_excl_scan((uint32_t)__popc(sel) | ((uint32_t)__popc(inm) << 16), sm, 1, total);
+    uint32_t oa = off & 0xffffu, om = off >> 16;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        if (sel >> j & 1u) p.a_idx[(size_t)u * p.a_cap + oa++] = base + j;
+        if (inm >> j & 1u) p.m_idx[(size_t)u * p.m_cap + om++] = base + j;
+    }
+    if (threadIdx.x == 0) {
+        p.a_cnt[u] = (int32_t)(total & 0xffffu);
+        if (want_m) p.m_cnt[u] = (int32_t)(total >> 16);
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// EMA update + prediction + top-|P|
+// ------------------------------------------------------------------------------------------------
+
+struct PredictParams {
+    const double *scores;
+    const int32_t *seq_len;
+    double *level;
+    double *trend;
+    int32_t *live;
+    int32_t *p_idx;
+    int32_t *p_cnt;
+    int hkv, block, nmax, budget, p_cap;
+    double alpha, beta, gamma;
+};
+
+template <int KPT>
+__global__ __launch_bounds__(kTK) void predict_kernel(PredictParams p) {
+    __shared__ TopkSmem sm;
+    const int u = blockIdx.x;
+    const int b = u / p.hkv;
+    const int slen = p.seq_len[b];
+    const int nb = min((slen + p.block - 1) / p.block, p.nmax);
+    const int live = min(max(p.live[u], 0), nb);
+    const double one_a = dsub(1.0, p.alpha);
+    const double one_b = dsub(1.0, p.beta);
+    const size_t ro = (size_t)u * p.nmax;
+    const int base = threadIdx.x * KPT;
+    uint64_t key[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int i = base + j;
+        key[j] = 0ull;
+        if (i < nb) {
+            const double is = p.scores[ro + i];
+            double lv, tr;
+            if (i < live) {
+                // trend = beta (IS - level_old) + (1 - beta) trend_old;  level = alpha IS + (1 - alpha) level_old
+                const double l0 = p.level[ro + i], t0 = p.trend[ro + i];
+                tr = dadd(dmul(p.beta, dsub(is, l0)), dmul(one_b, t0));
+                lv = dadd(dmul(p.alpha, is), dmul(one_a, l0));
+            } else {
+                lv = is;      // a block seen for the first time starts at its score with no trend
+                tr = 0.0;
+            }
+            p.level[ro + i] = lv;
+            p.trend[ro + i] = tr;
+            key[j] = order_key(dadd(lv, dmul(p.gamma, tr)));   // prediction level + gamma trend
+        }
+    }
+    const uint32_t sel = block_topk<KPT>(key, nb, p.budget, sm);
+    uint32_t total;
+    const uint32_t off = block_excl_scan((uint32_t)__popc(sel), sm, 1, total);
+    uint32_t o = off;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        if (sel >> j & 1u) p.p_idx[(size_t)u * p.p_cap + o++] = base + j;
+    if (threadIdx.x == 0) {
+        p.p_cnt[u] = (int32_t)total;
+        p.live[u] = nb;
+    }
+}
+
+int kpt_for(int nmax) {
+    int kpt = 1;
+    while (kpt * kTK < nmax) kpt *= 2;
+    return kpt;
+}
+
+}  // namespace
+
+hipError_t launch_meta(const KvDesc &kv, int block, int stride, void *meta, hipStream_t stream) {
+    MetaParams p;
+    p.k = kv.k;
+    p.page_table = kv.page_table;
+    p.seq_len = kv.seq_len;
+    p.meta = meta;
+    p.hkv = kv.hkv;
+    p.max_pages = kv.max_pages;
+    p.num_pages = kv.num_pages;
+    p.block = block;
+    p.stride = stride;
+    p.nmax = (int)((long)kv.max_pages * kPage / block);
+    const dim3 grid((p.nmax + 63) / 64, kv.batch * kv.hkv);
+    if (kv.bf16) {
+        if (kv.d == 128) meta_kernel<true, 128><<<grid, 256, 0, stream>>>(p);
+        else meta_kernel<true, 64><<<grid, 256, 0, stream>>>(p);
+    } else {
+        if (kv.d == 128) meta_kernel<false, 128><<<grid, 256, 0, stream>>>(p);
+        else meta_kernel<false, 64><<<grid, 256, 0, stream>>>(p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *meta, int block,
+                         int stride, int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt,
+                         int p_cap, double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap,
+                         int32_t *m_idx, int32_t *m_cnt, int m_cap, hipStream_t stream) {
+    const int units = kv.batch * kv.hkv;
+    ScoreParams sp;
+    sp.q = q;
+    sp.meta = meta;
+    sp.seq_len = kv.seq_len;
+    sp.scores = scores;
+    sp.hq = hq;
+    sp.hkv = kv.hkv;
+    sp.G = hq / kv.hkv;
+    sp.block = block;
+    sp.stride = stride;
+    sp.nmax = nmax;
+    const int bpl = kv.bf16 ? 8 : 4;
+    const dim3 sgrid((nmax + 256 * bpl - 1) / (256 * bpl), units);
+    if (kv.bf16) {
+        if (kv.d == 128) score_kernel<true, 128><<<sgrid, 256, 0, stream>>>(sp);
+        else score_kernel<true, 64><<<sgrid, 256, 0, stream>>>(sp);
+    } else {
+        if (kv.d == 128) score_kernel<false, 128><<<sgrid, 256, 0, stream>>>(sp);
+        else score_kernel<false, 64><<<sgrid, 256, 0, stream>>>(sp);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    TopkParams tp;
+    tp.scores = scores;
+    tp.seq_len = kv.seq_len;
+    tp.p_idx = p_idx;
+    tp.p_cnt = p_cnt;
+    tp.a_idx = a_idx;
+    tp.a_cnt = a_cnt;
+    tp.m_idx = m_idx;
+    tp.m_cnt = m_cnt;
+    tp.hkv = kv.hkv;
+    tp.block = block;
+    tp.nmax = nmax;
+    tp.topk = topk;
+    tp.p_cap = p_cap;
+    tp.a_cap = a_cap;
+    tp.m_cap = m_cap;
+    switch (kpt_for(nmax)) {
+        case 1: topk_kernel<1><<<units, kTK, 0, stream>>>(tp); break;
+        case 2: topk_kernel<2><<<units, kTK, 0, stream>>>(tp); break;
+        case 4: topk_kernel<4><<<units, kTK, 0, stream>>>(tp); break;
+        case 8: topk_kernel<8><<<units, kTK, 0, stream>>>(tp); break;
+        case 16: topk_kernel<16><<<units, kTK, 0, stream>>>(tp); break;
+        default: topk_kernel<32><<<units, kTK, 0, stream>>>(tp); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batch, int hkv,
+                          int block, int nmax, double alpha, double beta, double gamma, int budget,
+                          double *level, double *trend, int32_t *live, int32_t *p_idx,
+                          int32_t *p_cnt, int p_cap, hipStream_t stream) {
+    PredictParams p;
+    p.scores = scores;
+    p.seq_len = seq_len;
+    p.level = level;
+    p.trend = trend;
+    p.live = live;
+    p.p_idx = p_idx;
+    p.p_cnt = p_cnt;
+    p.hkv = hkv;
+    p.block = block;
+    p.nmax = nmax;
+    p.budget = budget;
+    p.p_cap = p_cap;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.gamma = gamma;
+    const int units = batch * hkv;
+    switch (kpt_for(nmax)) {
+        case 1: predict_kernel<1><<<units, kTK, 0, stream>>>(p); break;
+        case 2: predict_kernel<2><<<units, kTK, 0, stream>>>(p); break;
+        case 4: predict_kernel<4><<<units, kTK, 0, stream>>>(p); break;
+        case 8: predict_kernel<8><<<units, kTK, 0, stream>>>(p); break;
+        case 16: predict_kernel<16><<<units, kTK, 0, stream>>>(p); break;
+        default: predict_kernel<32><<<units, kTK, 0, stream>>>(p); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace prr

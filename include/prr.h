@@ -1,0 +1,169 @@
+/*
+ * prr.h - C ABI of libprr.so, the MI355X (gfx950) hot path of PRR: predict, reuse and repair for
+ * dynamic sparse attention during long-context decoding.
+ *
+ * Citations:
+ *   [paper] "Predict, Reuse, and Repair: Accelerating Dynamic Sparse Attention for Long-Context LLM
+ *           Decoding" (full paper text)
+ *   [blog]  "PRR: Predict, Reuse, and Repair - Accelerating Dynamic Sparse Attention for Long-Context
+ *           LLM Decoding" (xllm-io paper review; equation numbers (1)-(6))
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer named "device" is GPU memory owned by the caller; the library allocates nothing and
+ *     keeps no mutable global state.  Host structs are read only during the call.
+ *   - Work is enqueued on `stream` and runs asynchronously in stream order.  Nothing is copied to the
+ *     host: set sizes stay on the device.
+ *   - Problems the host can see (null pointers, sizes, unsupported shapes, a short workspace) return a
+ *     status BEFORE anything is enqueued.  A failed launch returns PRR_EHIP.
+ *   - Device-side preconditions are the caller's contract: block indices in range and unique within a
+ *     set, M disjoint from P, finite inputs, page-table entries in [0, num_pages).  Out-of-range block
+ *     and page indices are clamped (never read out of bounds) but give unspecified results.
+ *   - Block sets are int32 lists per (sequence, kv head): idx[b][kvh][0 .. count[b][kvh]), any order on
+ *     input; sets produced by the library are unique and ascending.
+ *   - Query head h of a sequence uses kv head h / G with G = num_q_heads / num_kv_heads (contiguous
+ *     grouping); the block set of a kv head is shared by its G query heads ([paper] A.1).
+ */
+#ifndef PRR_H
+#define PRR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum prr_status {
+    PRR_OK = 0,
+    PRR_EINVAL = 1,       /* null pointer, negative or inconsistent size */
+    PRR_EUNSUPPORTED = 2, /* valid but not implemented: head_dim, page size, group size, dtype, N */
+    PRR_EWORKSPACE = 3,   /* workspace missing or smaller than the *_workspace_bytes query */
+    PRR_EHIP = 4          /* a HIP launch or runtime call failed */
+} prr_status;
+
+typedef enum prr_dtype { PRR_F32 = 0, PRR_BF16 = 1 } prr_dtype;
+
+/* Paged KV cache.  Page size must be 16 tokens.  One (page, kv head) tile is contiguous:
+ *   k: [num_pages][num_kv_heads][page_size][head_dim]  (token-major tile)
+ *   v: [num_pages][num_kv_heads][head_dim][page_size]  (channel-major tile)
+ * page_table[b][j] is the physical page holding tokens [16 j, 16 j + 16) of sequence b; seq_len[b] is
+ * the number of valid tokens.  head_dim must be 64 or 128.  q (where an entry point takes it) has the
+ * same dtype as k and v, layout [batch][num_q_heads][head_dim]. */
+typedef struct prr_kv_cache {
+    const void *k;              /* device */
+    const void *v;              /* device */
+    const int32_t *page_table;  /* device, [batch][max_pages] */
+    const int32_t *seq_len;     /* device, [batch] */
+    int32_t batch;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t page_size;
+    int32_t num_pages;
+    int32_t max_pages;
+    prr_dtype dtype;
+} prr_kv_cache;
+
+/* A block set per (sequence, kv head): idx [batch][num_kv_heads][cap], count [batch][num_kv_heads]. */
+typedef struct prr_block_set {
+    int32_t *idx;    /* device */
+    int32_t *count;  /* device */
+    int32_t cap;
+} prr_block_set;
+
+/* Partial attention state per query head ([paper] §4.3, the speculative kernel's extra outputs):
+ *   acc[b][h][:] = sum_j e^{s_j - m} v_j   (unnormalised output; O = acc / l)
+ *   l[b][h]      = sum_j e^{s_j - m}       (softmax denominator)
+ *   m[b][h]      = max_j s_j               (running maximum, natural-log units)
+ * with s_j = scale * (q . k_j) over the tokens of the blocks folded in so far.  The empty state is
+ * acc = 0, l = 0, m = -inf.  All fp32, device. */
+typedef struct prr_attn_state {
+    float *acc;  /* [batch][num_q_heads][head_dim] */
+    float *l;    /* [batch][num_q_heads] */
+    float *m;    /* [batch][num_q_heads] */
+} prr_attn_state;
+
+/* ---- sizes ---------------------------------------------------------------------------------- */
+
+/* Blocks per sequence that the page table can address: max_pages * page_size / block. */
+int32_t prr_max_blocks(const prr_kv_cache *kv, int32_t block);
+
+/* Row length (elements) of the metadata array: prr_max_blocks rounded up to a multiple of 8. */
+int32_t prr_meta_stride(const prr_kv_cache *kv, int32_t block);
+
+/* Bytes of block metadata: batch * num_kv_heads * head_dim * 2 * prr_meta_stride * sizeof(elem). */
+size_t prr_meta_bytes(const prr_kv_cache *kv, int32_t block);
+
+/* Workspace bytes needed by prr_spec_attn / prr_repair for sets of capacity `cap` (blocks). */
+size_t prr_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block, int32_t cap);
+
+/* Zero a workspace on `stream` with a fill kernel (no memset node).  An attention workspace must be
+ * zero before its first use; every attention call leaves it ready for the next one.  Calls that run
+ * concurrently need distinct workspaces. */
+prr_status prr_workspace_clear(void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- entry points --------------------------------------------------------------------------- */
+
+/* Block metadata for Quest selection ([paper] A.1: channel-wise min and max keys m_p, M_p of every
+ * block, stored per kv head).  meta layout: [batch][num_kv_heads][head_dim][2][stride] in the cache
+ * dtype, row 0 = min, row 1 = max, column p = block p (stride = prr_meta_stride).  Blocks at or beyond
+ * ceil(seq_len / block) are not written.  A partial last block uses its valid tokens only.
+ * block must be a positive multiple of page_size.  Reads all of K once; not part of the per-step path. */
+prr_status prr_build_meta(const prr_kv_cache *kv, int32_t block, void *meta, hipStream_t stream);
+
+/* Quest selection, GQA-extended ([paper] A.1; [paper] §1, §2.1 top-K selection; [paper] §3 M = A \ P).
+ *   scores[b][kvh][p] (fp64, row length prr_max_blocks) = sum_{i=0}^{d-1} max(qbar_i mn_{p,i},
+ *       qbar_i mx_{p,i}), qbar = (1/G) sum_g q[b][kvh G + g], summed in channel order from +0.0 in
+ *       float64 with no fused multiply-add, for p < N_b = ceil(seq_len[b] / block);
+ *   A = the min(topk, N_b) highest scores (ties to the smaller block index), ascending;
+ *   M = A \ P (ascending) when P is given.
+ * P may be NULL (then M must be NULL).  A->cap and M->cap must be >= topk.  N_b must not exceed
+ * 32768.  q: [batch][num_q_heads][head_dim], device, dtype of the cache. */
+prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
+                      int32_t block, int32_t topk, const prr_block_set *P, double *scores,
+                      prr_block_set *A, prr_block_set *M, hipStream_t stream);
+
+/* EMA level/trend predictor, one decode step ([paper] §4.1; [blog] Eqs. (2)-(3)).
+ * For every (b, kvh) with N_b = ceil(seq_len[b] / block) blocks and live[b][kvh] blocks that already
+ * carry state: blocks p < live get
+ *     trend = beta (IS - level) + (1 - beta) trend;  level = alpha IS + (1 - alpha) level
+ * (both with the previous level); blocks live <= p < N_b start at level = IS, trend = 0.  Then
+ * live = N_b and P_next = the `budget` blocks with the largest level + gamma trend (ties to the smaller
+ * index), ascending.  All arithmetic fp64 in the order written, no fused multiply-add.
+ * scores, level, trend: [batch][num_kv_heads][max_blocks] fp64, device; live [batch][num_kv_heads]
+ * int32 (zero for a fresh sequence).  P_next->cap >= budget.  max_blocks <= 32768. */
+prr_status prr_predict(const double *scores, const int32_t *seq_len, int32_t batch,
+                       int32_t num_kv_heads, int32_t block, int32_t max_blocks, double alpha,
+                       double beta, double gamma, int32_t budget, double *level, double *trend,
+                       int32_t *live, prr_block_set *P_next, hipStream_t stream);
+
+/* Speculative block-sparse decode attention over P ([paper] §3 and §4.3, the instrumented speculative
+ * kernel that also stores the softmax denominator and running maximum; [paper] §1).  Writes the
+ * unnormalised state of every query head over the tokens of its kv head's blocks in P (tokens at or
+ * beyond seq_len are masked).  An empty P writes the empty state.  scale is the softmax scale
+ * (1/sqrt(head_dim) for standard attention).  ws: prr_attn_workspace_bytes(..., P->cap). */
+prr_status prr_spec_attn(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, int32_t block,
+                         const prr_block_set *P, float scale, prr_attn_state *out, void *ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+/* Incremental repair ([paper] §4.3, repair via online softmax; [blog] Eq. (6)): folds the tokens of the
+ * missed blocks M into `state` in place with the online-softmax recurrence
+ *     m' = max(m, m~),  l' = e^{m - m'} l + e^{m~ - m'} l~,  acc' = e^{m - m'} acc + e^{m~ - m'} acc~
+ * where (acc~, l~, m~) is the attention of the missed tokens.  Reads the state and the missed K/V once
+ * and writes the state once.  An empty M leaves the state bit-for-bit unchanged.  When `out`
+ * ([batch][num_q_heads][head_dim] fp32, device) is non-NULL the normalised output acc'/l' is also
+ * written (0 where l' = 0).  ws: prr_attn_workspace_bytes(..., M->cap). */
+prr_status prr_repair(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, int32_t block,
+                      const prr_block_set *M, float scale, prr_attn_state *state, float *out,
+                      void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Human-readable name of a status code (static string). */
+const char *prr_strerror(prr_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRR_H */

@@ -1,0 +1,116 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header declares, sizes its
+buffers, and rejects bad arguments before anything is enqueued (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_quest_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "prr.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(prr_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        pytest.fail("libprr.so is not built; run `python -m block_sparse_attention_quest_amd.build`")
+    return bd.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = _declared()
+    assert declared == sorted(bd.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_strerror(lib):
+    for code in range(5):
+        assert lib.prr_strerror(code)
+    assert lib.prr_strerror(99) == b"unknown status"
+
+
+def _kv(**kw):
+    base = dict(k=1, v=1, page_table=1, seq_len=1, batch=2, num_kv_heads=8, head_dim=128, page_size=16,
+                num_pages=4096, max_pages=2048, dtype=bd.PRR_BF16)
+    base.update(kw)
+    return bd.KvCacheStruct(**base)
+
+
+def test_sizes(lib):
+    kv = _kv()
+    assert lib.prr_max_blocks(ctypes.byref(kv), 64) == 2048 * 16 // 64
+    assert lib.prr_meta_stride(ctypes.byref(kv), 16) == 2048
+    kv2 = _kv(max_pages=13)
+    assert lib.prr_max_blocks(ctypes.byref(kv2), 16) == 13
+    assert lib.prr_meta_stride(ctypes.byref(kv2), 16) == 16
+    assert lib.prr_meta_bytes(ctypes.byref(kv), 16) == 2 * 8 * 128 * 2 * 2048 * 2
+    ws = lib.prr_attn_workspace_bytes(8, 32, 8, 128, 64, 64)
+    assert ws >= 256 + 64 * 4 * (128 + 2) * 4
+    assert lib.prr_attn_workspace_bytes(0, 32, 8, 128, 64, 64) == 0
+
+
+def _set(cap=64):
+    return bd.BlockSetStruct(1, 1, cap)
+
+
+def _state():
+    return bd.AttnStateStruct(1, 1, 1)
+
+
+def test_attention_argument_errors(lib):
+    kv = _kv()
+    P = _set()
+    st = _state()
+    ws_need = lib.prr_attn_workspace_bytes(2, 32, 8, 128, 64, 64)
+    call = lambda q=1, hq=32, kv=kv, block=64, P=P, out=st, ws=1, wsb=ws_need: lib.prr_spec_attn(
+        q, hq, ctypes.byref(kv) if kv is not None else None, block,
+        ctypes.byref(P) if P is not None else None, 0.1, ctypes.byref(out) if out is not None else None,
+        ws, wsb, None)
+    assert call(q=None) == 1
+    assert call(kv=None) == 1
+    assert call(P=None) == 1
+    assert call(out=None) == 1
+    assert call(block=24) == 1                          # not a multiple of the page size
+    assert call(hq=36) == 1                             # not a multiple of num_kv_heads
+    assert call(hq=8 * 32) == 2                         # group of 32 > 16
+    assert call(hq=8 * 3) == 2                          # group not a power of two
+    assert call(kv=_kv(head_dim=96)) == 2
+    assert call(kv=_kv(page_size=32)) == 2
+    assert call(kv=_kv(dtype=7)) == 2
+    assert call(ws=None) == 3
+    assert call(wsb=ws_need - 1) == 3
+    assert call(P=bd.BlockSetStruct(1, 1, 0)) == 1
+    assert lib.prr_repair(1, 32, ctypes.byref(kv), 64, ctypes.byref(P), 0.1, None, None, 1, ws_need,
+                          None) == 1
+
+
+def test_select_and_predict_argument_errors(lib):
+    kv = _kv()
+    A = _set(64)
+    P = _set(64)
+    M = _set(64)
+    sel = lambda topk=64, A=A, P=P, M=M, meta=1, kv=kv, block=64: lib.prr_select(
+        1, 32, ctypes.byref(kv), meta, block, topk, ctypes.byref(P) if P else None, 1, ctypes.byref(A),
+        ctypes.byref(M) if M else None, None)
+    assert sel(meta=None) == 1
+    assert sel(topk=65) == 1                      # A cap too small
+    assert sel(topk=-1) == 1
+    assert sel(M=None) == 1                       # P without M
+    assert sel(M=_set(10)) == 1
+    assert sel(kv=_kv(max_pages=65536), block=16) == 2   # more than 32768 blocks per sequence
+    pred = lambda budget=64, nmax=2048, P=P: lib.prr_predict(
+        1, 1, 2, 8, 64, nmax, 0.6, 0.3, 0.5, budget, 1, 1, 1, ctypes.byref(P) if P else None, None)
+    assert pred(budget=65) == 1
+    assert pred(P=None) == 1
+    assert pred(nmax=40000) == 2
+    assert lib.prr_build_meta(ctypes.byref(kv), 64, None, None) == 1
+    assert lib.prr_build_meta(ctypes.byref(_kv(max_pages=10)), 64, 1, None) == 1   # 160 tokens % 64

@@ -1,0 +1,281 @@
+"""GPU parity: libprr.so through the C ABI against the CPU oracle on the same seeded inputs.
+
+Block indices, sets, scores, metadata and EMA state must match bit for bit; the attention state must
+match within O 5e-3 (max abs), l 1e-4 (relative), m 1e-4 (relative).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from _gpu import (assert_heads, assert_state, device_kv, require_gpu, sets_to_device, unit_meta,
+                  unit_view)
+from _util import oracle_view
+from block_sparse_attention_quest_amd import binding as bd
+from block_sparse_attention_quest_amd import workloads as wl
+from oracle import prr_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    bd.load_library()
+
+
+def _meta_bits(meta: torch.Tensor, w: wl.Workload):
+    # columns past each sequence's block count are never written (arbitrary bits)
+    with np.errstate(invalid="ignore"):
+        return orc.upcast(wl.to_numpy_bits(meta), w.dtype)
+
+
+# --------------------------------------------------------------------------------------------------
+# Tiny configuration end to end
+# --------------------------------------------------------------------------------------------------
+
+
+def test_tiny_end_to_end():
+    w = wl.C1
+    inp = wl.make_inputs(w, "cuda")
+    q, kv = oracle_view(inp)
+    q = q[0]
+    dkv = device_kv(inp)
+    meta = bd.build_meta(dkv, w.block)
+    ometa = orc.build_meta(kv, w.block, w.num_kv_heads)
+    gm = _meta_bits(meta, w)
+    nb = w.blocks_of(0)
+    assert np.array_equal(gm[0, 0, :, 0, :nb].T, ometa[0][0][0])
+    assert np.array_equal(gm[0, 0, :, 1, :nb].T, ometa[0][0][1])
+
+    scores, A, _ = bd.select(inp.q[0], dkv, meta, w.block, w.topk)
+    oscores, oA, _ = orc.select(q, ometa, w.group, w.topk)
+    assert np.array_equal(scores[0, 0, :nb].cpu().numpy(), oscores[0][0])
+    assert A.lists()[0][0] == list(oA[0][0])
+
+    P = [[wl.make_spec_set(w, oA[0][0], nb, w.spec_hit, w.spec_miss)]]
+    Pd = sets_to_device(P, w.topk)
+    _, A2, M = bd.select(inp.q[0], dkv, meta, w.block, w.topk, P=Pd)
+    oM = orc.set_minus(oA[0][0], P[0][0])
+    assert A2.lists()[0][0] == list(oA[0][0])
+    assert M.lists()[0][0] == list(oM) and len(oM) == 3
+
+    state = bd.spec_attn(inp.q[0], dkv, w.block, Pd, w.scale)
+    spec_ref = orc.spec_states(q, kv, w.block, P, w.scale)
+    assert_heads(state, spec_ref, "spec")
+    out = torch.empty_like(state.acc)
+    bd.repair(inp.q[0], dkv, w.block, M, w.scale, state, out=out)
+    union = [[sorted(set(P[0][0]) | set(oM))]]
+    ref = orc.spec_states(q, kv, w.block, union, w.scale)
+    assert_heads(state, ref, "repair")
+    for h in range(w.num_q_heads):
+        assert np.max(np.abs(out[0, h].double().cpu().numpy() - ref[(0, h)].out)) <= 5e-3
+
+
+# --------------------------------------------------------------------------------------------------
+# Small shapes: head dims, group sizes, block sizes, ragged lengths, empty sets
+# --------------------------------------------------------------------------------------------------
+
+CASES = [
+    # name, B, Hq, Hkv, d, block, lens, dtype
+    ("bf16_d128_g4_s16", 2, 8, 2, 128, 16, [1000, 611], "bf16"),
+    ("bf16_d128_g4_s64", 2, 8, 2, 128, 64, [2048, 1500], "bf16"),
+    ("bf16_d64_g8_s32", 1, 16, 2, 64, 32, [1777], "bf16"),
+    ("bf16_d128_g16_s32", 1, 16, 1, 128, 32, [900], "bf16"),
+    ("bf16_d128_g1_s16", 1, 4, 4, 128, 16, [333], "bf16"),
+    ("bf16_d128_g2_s48", 2, 4, 2, 128, 48, [960, 97], "bf16"),
+    ("f32_d64_g4_s16", 2, 8, 2, 64, 16, [515, 1024], "f32"),
+    ("f32_d128_g2_s32", 1, 4, 2, 128, 32, [700], "f32"),
+]
+
+
+@pytest.fixture(scope="module", params=CASES, ids=[c[0] for c in CASES])
+def small_case(request):
+    name, B, Hq, Hkv, d, S, lens, dt = request.param
+    w = wl.Workload(name, B, Hq, Hkv, d, max(lens), S, 8, dt, seed=100 + len(name), seq_lens=lens)
+    inp = wl.make_inputs(w, "cuda")
+    q, kv = oracle_view(inp)
+    return w, inp, q[0], kv
+
+
+def _random_sets(w, rng, sizes):
+    """Disjoint P, M per unit with the requested sizes (clipped to the number of blocks)."""
+    P, M = [], []
+    for b in range(w.batch):
+        prow, mrow = [], []
+        nb = w.blocks_of(b)
+        for h in range(w.num_kv_heads):
+            n_p, n_m = sizes[(b * w.num_kv_heads + h) % len(sizes)]
+            perm = rng.permutation(nb)
+            n_p = min(n_p, nb)
+            n_m = min(n_m, nb - n_p)
+            prow.append(list(perm[:n_p]))
+            mrow.append(list(perm[n_p:n_p + n_m]))
+        P.append(prow)
+        M.append(mrow)
+    return P, M
+
+
+def test_spec_then_repair_equals_union(small_case):
+    w, inp, q, kv = small_case
+    rng = np.random.default_rng(1)
+    P, M = _random_sets(w, rng, [(5, 3), (0, 4), (7, 0), (1, 1), (11, 9)])
+    dkv = device_kv(inp)
+    cap = 24
+    Pd, Md = sets_to_device(P, cap), sets_to_device(M, cap)
+    state = bd.spec_attn(inp.q[0], dkv, w.block, Pd, w.scale)
+    assert_heads(state, orc.spec_states(q, kv, w.block, P, w.scale), "spec")
+    out = torch.empty_like(state.acc)
+    bd.repair(inp.q[0], dkv, w.block, Md, w.scale, state, out=out)
+    union = [[sorted(set(P[b][h]) | set(M[b][h])) for h in range(w.num_kv_heads)] for b in range(w.batch)]
+    ref = orc.spec_states(q, kv, w.block, union, w.scale)
+    assert_heads(state, ref, "repair")
+    o = out.double().cpu().numpy()
+    for (b, h), st in ref.items():
+        assert np.max(np.abs(o[b, h] - st.out)) <= 5e-3
+
+
+def test_empty_missed_set_leaves_state_bitwise(small_case):
+    w, inp, q, kv = small_case
+    rng = np.random.default_rng(2)
+    P, _ = _random_sets(w, rng, [(6, 0)])
+    dkv = device_kv(inp)
+    state = bd.spec_attn(inp.q[0], dkv, w.block, sets_to_device(P, 8), w.scale)
+    before = state.clone()
+    empty = bd.BlockSet.empty(w.batch, w.num_kv_heads, 8)
+    out = torch.full_like(state.acc, 7.0)
+    bd.repair(inp.q[0], dkv, w.block, empty, w.scale, state, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(state.acc, before.acc) and torch.equal(state.l, before.l)
+    assert torch.equal(state.m, before.m)
+    assert torch.allclose(out, before.acc / before.l[..., None], rtol=1e-6, atol=0)
+
+
+def test_empty_speculation_is_plain_dsa(small_case):
+    w, inp, q, kv = small_case
+    rng = np.random.default_rng(3)
+    A, _ = _random_sets(w, rng, [(8, 0), (3, 0)])
+    dkv = device_kv(inp)
+    empty = bd.BlockSet.empty(w.batch, w.num_kv_heads, 8)
+    state = bd.spec_attn(inp.q[0], dkv, w.block, empty, w.scale)
+    torch.cuda.synchronize()
+    assert torch.all(state.l == 0) and torch.all(state.m == -math.inf) and torch.all(state.acc == 0)
+    bd.repair(inp.q[0], dkv, w.block, sets_to_device(A, 8), w.scale, state)
+    assert_heads(state, orc.spec_states(q, kv, w.block, A, w.scale), "dsa")
+
+
+def test_order_independence_and_determinism(small_case):
+    w, inp, q, kv = small_case
+    rng = np.random.default_rng(4)
+    P, _ = _random_sets(w, rng, [(9, 0)])
+    dkv = device_kv(inp)
+    s1 = bd.spec_attn(inp.q[0], dkv, w.block, sets_to_device(P, 12), w.scale)
+    s2 = bd.spec_attn(inp.q[0], dkv, w.block, sets_to_device(P, 12), w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(s1.acc, s2.acc) and torch.equal(s1.l, s2.l) and torch.equal(s1.m, s2.m)
+    shuffled = [[list(rng.permutation(p)) for p in row] for row in P]
+    s3 = bd.spec_attn(inp.q[0], dkv, w.block, sets_to_device(shuffled, 12), w.scale)
+    ref = orc.spec_states(q, kv, w.block, P, w.scale)
+    assert_heads(s3, ref, "shuffled")
+    # two repairs in sequence equal one repair with the union
+    P2, M2 = _random_sets(w, rng, [(3, 6)])
+    half = [[m[: len(m) // 2] for m in row] for row in M2]
+    rest = [[m[len(m) // 2:] for m in row] for row in M2]
+    st = bd.spec_attn(inp.q[0], dkv, w.block, sets_to_device(P2, 12), w.scale)
+    bd.repair(inp.q[0], dkv, w.block, sets_to_device(half, 12), w.scale, st)
+    bd.repair(inp.q[0], dkv, w.block, sets_to_device(rest, 12), w.scale, st)
+    union = [[sorted(set(P2[b][h]) | set(M2[b][h])) for h in range(w.num_kv_heads)] for b in range(w.batch)]
+    assert_heads(st, orc.spec_states(q, kv, w.block, union, w.scale), "two repairs")
+
+
+def test_meta_scores_topk(small_case):
+    w, inp, q, kv = small_case
+    dkv = device_kv(inp)
+    meta = bd.build_meta(dkv, w.block)
+    ometa = orc.build_meta(kv, w.block, w.num_kv_heads)
+    gm = _meta_bits(meta, w)
+    for kk in (0, 1, 5, 8, 64):      # 64 exceeds every case's block count: A = all blocks
+        A = bd.BlockSet.empty(w.batch, w.num_kv_heads, max(1, kk))
+        scores, A, _ = bd.select(inp.q[0], dkv, meta, w.block, kk, A=A)
+        osc, oA, _ = orc.select(q, ometa, w.group, kk)
+        gs = scores.cpu().numpy()
+        got = A.lists()
+        for b in range(w.batch):
+            nb = w.blocks_of(b)
+            for h in range(w.num_kv_heads):
+                assert np.array_equal(gm[b, h, :, 0, :nb].T, ometa[b][h][0])
+                assert np.array_equal(gm[b, h, :, 1, :nb].T, ometa[b][h][1])
+                assert np.array_equal(gs[b, h, :nb], osc[b][h]), (b, h)
+                assert got[b][h] == list(oA[b][h]), (kk, b, h)
+
+
+def test_select_ties_go_to_smaller_index():
+    """Identical keys in every block give equal scores everywhere: A must be the first K blocks,
+    and M = A minus P in ascending order."""
+    w = wl.Workload("ties", 1, 4, 1, 64, 16 * 40, 16, 7, "bf16", seed=7, shuffle_pages=False)
+    inp = wl.make_inputs(w, "cuda")
+    inp.k_cache[:] = inp.k_cache[0:1, :, 0:1, :].clone()
+    dkv = device_kv(inp)
+    meta = bd.build_meta(dkv, w.block)
+    P = sets_to_device([[[3, 9, 0, 30]]], 8)
+    scores, A, M = bd.select(inp.q[0], dkv, meta, w.block, w.topk, P=P)
+    s = scores[0, 0, :40].cpu().numpy()
+    assert np.all(s == s[0])
+    assert A.lists()[0][0] == list(range(7))
+    assert M.lists()[0][0] == [1, 2, 4, 5, 6]
+
+
+# --------------------------------------------------------------------------------------------------
+# Multi-step predictor trajectory (reduced 128K workload) with births
+# --------------------------------------------------------------------------------------------------
+
+
+def test_predictor_trajectory_bit_exact():
+    w = wl.scaled(wl.C3, name="c3_small", batch=2, context=16384, steps=12, topk=16,
+                  seq_lens=[16384, 12000])
+    inp = wl.make_inputs(w, "cuda")
+    dkv = device_kv(inp)
+    meta = bd.build_meta(dkv, w.block)
+    nmax = bd.max_blocks(dkv, w.block)
+    B, H = w.batch, w.num_kv_heads
+    level = torch.zeros((B, H, nmax), dtype=torch.float64, device="cuda")
+    trend = torch.zeros_like(level)
+    live = torch.zeros((B, H), dtype=torch.int32, device="cuda")
+    alpha, beta, gamma = w.ema
+    views = {(b, h): unit_view(inp, b, h) for b in range(B) for h in range(H)}
+    metas = {k: unit_meta(v[1], w.block) for k, v in views.items()}
+    olevel = {k: np.zeros(0) for k in views}
+    otrend = {k: np.zeros(0) for k in views}
+    olive = {k: 0 for k in views}
+    P = bd.BlockSet.empty(B, H, w.topk)
+    oP = {k: np.zeros(0, dtype=np.int64) for k in views}
+    # lengths grow by one block every 4 steps for sequence 1 (new blocks are born)
+    lens = list(w.lengths)
+    for t in range(w.steps):
+        if t and t % 4 == 0:
+            lens[1] = min(lens[1] + w.block, w.context)
+            inp.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+            bd.build_meta(dkv, w.block, meta)      # the grown sequence's blocks get metadata
+            for h in range(H):
+                metas[(1, h)] = unit_meta(unit_view(inp, 1, h, length=lens[1])[1], w.block)
+        scores, A, M = bd.select(inp.q[t], dkv, meta, w.block, w.topk, P=P)
+        Pn = bd.predict(scores, inp.seq_len, w.block, alpha, beta, gamma, w.topk, level, trend, live)
+        gs, gA, gM, gP = scores.cpu().numpy(), A.lists(), M.lists(), Pn.lists()
+        gl, gt = level.cpu().numpy(), trend.cpu().numpy()
+        for (b, h), (qv, kvv) in views.items():
+            nb = -(-lens[b] // w.block)
+            mn, mx = metas[(b, h)]
+            qv_t = orc.upcast(wl.to_numpy_bits(inp.q[t, b, h * w.group:(h + 1) * w.group]), w.dtype)[None]
+            s = orc.quest_scores(orc.representative_query(qv_t, 0, 0, w.group), mn[:nb], mx[:nb])
+            a = orc.topk_blocks(s, w.topk)
+            assert np.array_equal(gs[b, h, :nb], s), (t, b, h)
+            assert gA[b][h] == list(a), (t, b, h)
+            assert gM[b][h] == list(orc.set_minus(a, oP[(b, h)])), (t, b, h)
+            lv, tr, lvn, pn = orc.predict_step(olevel[(b, h)], otrend[(b, h)], olive[(b, h)], s, alpha, beta,
+                                               gamma, w.topk)
+            olevel[(b, h)], otrend[(b, h)], olive[(b, h)], oP[(b, h)] = lv, tr, lvn, pn
+            assert np.array_equal(gl[b, h, :nb], lv) and np.array_equal(gt[b, h, :nb], tr), (t, b, h)
+            assert gP[b][h] == list(pn), (t, b, h)
+        P = Pn
+    assert live.cpu().numpy().tolist() == [[-(-l // w.block)] * H for l in lens]
