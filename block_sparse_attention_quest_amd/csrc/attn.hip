@@ -74,6 +74,14 @@ struct AttnParams {
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Device-scope (all XCDs) coherent store and load of one float.
+__device__ __forceinline__ void st_dev(float *ptr, float v) {
+    __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float *ptr) {
+    return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Lane-dependent choice between two wave-uniform values, kept as a register select (never an
 // indexed private-array access).
 __device__ __forceinline__ int pick(int second, int a, int b) {
@@ -86,22 +94,38 @@ __device__ __forceinline__ float rescale(float mpart, float mtot) {
     return mpart == -INFINITY ? 0.0f : fexp2(mpart - mtot);
 }
 
-// Physical page and number of valid tokens of entry `gp` of the unit's expanded page list.
-__device__ __forceinline__ void page_info(const AttnParams &p, int b, int u, int gp, int total_pages,
-                                          int slen, int &phys, int &vt) {
-    phys = 0;
-    vt = 0;
-    if (gp < total_pages) {
-        const int li = gp / p.ppb;
-        const int sub = gp - li * p.ppb;
-        const int blk = p.idx[(size_t)u * p.cap + li];
-        const long lp = (long)blk * p.ppb + sub;
-        if (blk >= 0 && lp < p.max_pages) {
-            const long t0 = lp * kPage;
-            vt = (int)min(max((long)slen - t0, 0L), (long)kPage);
-            const int ph = p.page_table[(size_t)b * p.max_pages + lp];
-            phys = min(max(ph, 0), p.num_pages - 1);
-        }
+// Physical pages and valid-token counts of entries page0 .. page0+N-1 of the unit's expanded page
+// list.  Branch-free with clamped indices so the N set lookups, then the N page-table lookups, issue
+// back to back (two dependent memory rounds instead of 2N).  Out-of-range entries get vt = 0.
+template <int N>
+__device__ __forceinline__ void page_info(const AttnParams &p, int b, int u, int page0, int total_pages,
+                                          int slen, int (&phys)[N], int (&vt)[N]) {
+    int sub[N], blk[N];
+    bool inr[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int gp = page0 + i;
+        inr[i] = gp < total_pages;
+        const int gpc = inr[i] ? gp : 0;
+        const int li = gpc / p.ppb;
+        sub[i] = gpc - li * p.ppb;
+        blk[i] = p.idx[(size_t)u * p.cap + li];
+    }
+    long lpc[N];
+    bool ok[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const long lp = (long)blk[i] * p.ppb + sub[i];
+        ok[i] = inr[i] && blk[i] >= 0 && lp < p.max_pages;
+        lpc[i] = ok[i] ? lp : 0;
+    }
+    int ph[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) ph[i] = p.page_table[(size_t)b * p.max_pages + lpc[i]];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        vt[i] = ok[i] ? (int)min(max((long)slen - lpc[i] * kPage, 0L), (long)kPage) : 0;
+        phys[i] = min(max(ph[i], 0), p.num_pages - 1);
     }
 }
 
@@ -161,12 +185,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     // page0 is uniform per wave; readfirstlane keeps the page lookups in scalar registers
     const int page0 = (wg * kWaves + __builtin_amdgcn_readfirstlane(wave)) * PPW;
     int phys[PPW], vt[PPW];
+    page_info<PPW>(p, b, u, page0, total_pages, slen, phys, vt);
 #pragma unroll
     for (int i = 0; i < PPW; ++i) {
-        page_info(p, b, u, page0 + i, total_pages, slen, phys[i], vt[i]);
         phys[i] = __builtin_amdgcn_readfirstlane(phys[i]);
         vt[i] = __builtin_amdgcn_readfirstlane(vt[i]);
     }
+    bool partial = false;   // any page of this wave with fewer than 16 valid tokens
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) partial |= vt[i] < kPage;
 
     const size_t tile_stride = (size_t)p.hkv * kPage * D;   // elements per physical page
     const size_t tile_off = (size_t)kvh * kPage * D;
@@ -205,20 +232,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
                 for (int s = 0; s < KS; ++s) kop[t][h][s] = *(const bf16x8 *)(kp + 32 * s);
             }
             const int pv = pick(g >> 1, phys[2 * t], phys[2 * t + 1]);
-            const int vvt = pick(g >> 1, vt[2 * t], vt[2 * t + 1]);
             const int off = 8 * (g & 1);
 #pragma unroll
             for (int cb = 0; cb < D / 16; ++cb) {
                 vop[t][cb] = *(const bf16x8 *)(vb + (size_t)pv * tile_stride +
                                                (size_t)(16 * cb + r) * kPage + off);
-            }
-            const int nv = vvt - off;  // valid tokens among this lane's 8
-            if (nv < 8) {
-#pragma unroll
-                for (int cb = 0; cb < D / 16; ++cb)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (e >= nv) vop[t][cb][e] = (__bf16)0.0f;
             }
         }
         // S^T tiles
@@ -245,6 +263,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
         m2 = mloc;
         const float msafe = m2 == -INFINITY ? 0.0f : m2;
+        if (partial) {
+            // tokens past the sequence end: zero V so stale cache contents cannot reach the output
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const int nv = pick(g >> 1, vt[2 * t], vt[2 * t + 1]) - 8 * (g & 1);
+#pragma unroll
+                for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (e >= nv) vop[t][cb][e] = (__bf16)0.0f;
+            }
+        }
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             bf16x8 phi, plo;
@@ -281,14 +311,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
 #pragma unroll
             for (int s = 0; s < KS; ++s) kop[pg][s] = *(const f32x4 *)(kp + 16 * s);
 #pragma unroll
-            for (int cb = 0; cb < D / 16; ++cb) {
+            for (int cb = 0; cb < D / 16; ++cb)
                 vop[pg][cb] = *(const f32x4 *)(vf + (size_t)phys[pg] * tile_stride +
                                                (size_t)(16 * cb + j) * kPage + 4 * g);
-                const int nv = vt[pg] - 4 * g;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (e >= nv) vop[pg][cb][e] = 0.0f;
-            }
         }
         float mloc = -INFINITY;
 #pragma unroll
@@ -310,6 +335,17 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
         m2 = mloc;
         const float msafe = m2 == -INFINITY ? 0.0f : m2;
+        if (partial) {
+#pragma unroll
+            for (int pg = 0; pg < PPW; ++pg) {
+                const int nv = vt[pg] - 4 * g;
+#pragma unroll
+                for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (e >= nv) vop[pg][cb][e] = 0.0f;
+            }
+        }
 #pragma unroll
         for (int pg = 0; pg < PPW; ++pg) {
             float pe[4];
@@ -372,32 +408,36 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
                 write_item(p, head, c, D, a, ls, mx, false, 0.0f);
             }
         } else {
-            part[jj * (D + 2) + c] = a;
+            st_dev(&part[jj * (D + 2) + c], a);
             if (c == 0) {
-                part[jj * (D + 2) + D] = ls;
-                part[jj * (D + 2) + D + 1] = mx;
+                st_dev(&part[jj * (D + 2) + D], ls);
+                st_dev(&part[jj * (D + 2) + D + 1], mx);
             }
         }
     }
     if (single) return;
 
-    // cross-workgroup merge: the last workgroup of the unit folds every partial in index order
-    __threadfence();
+    // Cross-workgroup merge: the last workgroup of the unit folds every partial in index order.
+    // Partials are written and read with device-scope (sc1) accesses, which are coherent across the
+    // XCDs' L2s by themselves; waiting for this thread's stores to complete before the barrier, and the
+    // barrier before the counter increment, orders them ahead of it.  This avoids a device-scope
+    // release fence, which would write back every dirty line of the L2.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
-        const uint32_t prev = atomicAdd(&p.counters[u], 1u);
+        const uint32_t prev = __hip_atomic_fetch_add(&p.counters[u], 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == (uint32_t)(nwg - 1));
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
 
     const float *base = p.partials + (size_t)u * p.wg_per_unit * (size_t)G * (D + 2);
     for (int it = threadIdx.x; it < G * D; it += kThreads) {
         const int jj = it / D, c = it - jj * D;
         const size_t head = head0 + jj;
         float mt = -INFINITY;
-        for (int w = 0; w < nwg; ++w) mt = fmaxf(mt, base[((size_t)w * G + jj) * (D + 2) + D + 1]);
+        for (int w = 0; w < nwg; ++w) mt = fmaxf(mt, ld_dev(&base[((size_t)w * G + jj) * (D + 2) + D + 1]));
         float mo = 0.0f, mo2 = -INFINITY;
         if (p.repair) {
             mo = s_mo[jj];
@@ -412,13 +452,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
         }
         for (int w = 0; w < nwg; ++w) {
             const float *pw = base + ((size_t)w * G + jj) * (D + 2);
-            const float f = rescale(pw[D + 1], mt);
-            a += f * pw[c];
-            ls += f * pw[D];
+            const float f = rescale(ld_dev(&pw[D + 1]), mt);
+            a += f * ld_dev(&pw[c]);
+            ls += f * ld_dev(&pw[D]);
         }
         write_item(p, head, c, D, a, ls, mt, p.repair && mt == mo2, mo);
     }
-    if (threadIdx.x == 0) p.counters[u] = 0u;
+    if (threadIdx.x == 0) __hip_atomic_store(&p.counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void clear_kernel(uint32_t *w, size_t n) {

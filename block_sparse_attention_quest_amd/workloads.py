@@ -118,12 +118,14 @@ C1 = Workload("tiny", 1, 4, 1, 64, 1024, 16, 8, "f32", seed=1, shuffle_pages=Fal
               spec_hit=5, spec_miss=3)
 C2 = Workload("llama3_8b_32k", 1, 32, 8, 128, 32768, 16, 128, "bf16", seed=2,
               spec_hit=87, spec_miss=41, planted=32, plant_gain=8.0)
+# query_mean_gain 0.64 puts the mean adjacent-step top-K overlap at ~0.68 (measured with the oracle's
+# selection over all 8 kv heads and 64 steps); block_centre_std barely moves it.
 C3 = Workload("ctx128k_b8_64steps", 8, 32, 8, 128, 131072, 64, 64, "bf16", seed=3, steps=64,
-              drift_rho=0.9, query_mean_gain=1.0, block_centre_std=0.35, ema=(0.6, 0.3, 0.5))
+              drift_rho=0.9, query_mean_gain=0.64, block_centre_std=0.35, ema=(0.6, 0.3, 0.5))
 C4 = Workload("ctx512k_paged", 1, 32, 8, 128, 524288, 16, 256, "bf16", seed=4,
               spec_hit=174, spec_miss=82)
 C5 = Workload("llama70b_share_256k", 4, 64, 8, 128, 262144, 32, 128, "bf16", seed=5, steps=16,
-              drift_rho=0.9, query_mean_gain=1.0, block_centre_std=0.35,
+              drift_rho=0.9, query_mean_gain=0.64, block_centre_std=0.35,
               calib_rows=8192, calib_blocks=512)
 
 CONFIGS = {w.name: w for w in (C1, C2, C3, C4, C5)}
