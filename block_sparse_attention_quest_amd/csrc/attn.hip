@@ -140,6 +140,65 @@ __device__ __forceinline__ void write_item(const AttnParams &p, size_t head, int
     if (p.out) p.out[head * D + c] = lsum > 0.0f ? a / lsum : 0.0f;
 }
 
+// The last workgroup of a unit folds the unit's nwg partial states (and, in repair mode, the incoming
+// state) into the final one.  A thread owns VW consecutive channels of one query head.  Partials are
+// visited in index order, MB at a time: every device-scope load of a batch is issued before any is
+// used, so a batch costs one memory round trip; batches combine with the same online-softmax step
+// (running maximum, rescaled sums), which keeps the result independent of arrival order.
+template <int VW, int D>
+__device__ __forceinline__ void merge_partials(const AttnParams &p, const float *base, int nwg, size_t head0,
+                                               const float *s_mo, const float *s_lo) {
+    constexpr int MB = 16;
+    constexpr int CPH = D / VW;   // channel groups per head
+    const int G = p.G;
+    for (int it = threadIdx.x; it < G * CPH; it += kThreads) {
+        const int jj = it / CPH, c0 = (it - jj * CPH) * VW;
+        const size_t head = head0 + jj;
+        float mt = -INFINITY, ls = 0.0f, a[VW];
+        float mo = 0.0f, mo2 = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < VW; ++v) a[v] = 0.0f;
+        if (p.repair) {
+            mo = s_mo[jj];
+            mo2 = mo == -INFINITY ? -INFINITY : mo * kLog2e;
+            mt = mo2;
+            ls = s_lo[jj];
+#pragma unroll
+            for (int v = 0; v < VW; ++v) a[v] = p.acc[head * D + c0 + v];
+        }
+        for (int w0 = 0; w0 < nwg; w0 += MB) {
+            float pm[MB], pl[MB], pa[MB][VW];
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                const int w = min(w0 + i, nwg - 1);   // clamped: a valid partial, weighted 0 below
+                const float *pw = base + ((size_t)w * G + jj) * (D + 2);
+                pm[i] = ld_dev(&pw[D + 1]);
+                pl[i] = ld_dev(&pw[D]);
+#pragma unroll
+                for (int v = 0; v < VW; ++v) pa[i][v] = ld_dev(&pw[c0 + v]);
+            }
+            float mb = mt;
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                if (w0 + i < nwg) mb = fmaxf(mb, pm[i]);
+            const float fr = rescale(mt, mb);
+            ls *= fr;
+#pragma unroll
+            for (int v = 0; v < VW; ++v) a[v] *= fr;
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                const float f = w0 + i < nwg ? rescale(pm[i], mb) : 0.0f;
+                ls += f * pl[i];
+#pragma unroll
+                for (int v = 0; v < VW; ++v) a[v] += f * pa[i][v];
+            }
+            mt = mb;
+        }
+#pragma unroll
+        for (int v = 0; v < VW; ++v) write_item(p, head, c0 + v, D, a[v], ls, mt, p.repair && mt == mo2, mo);
+    }
+}
+
 template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     constexpr int PPW = pages_per_wave(BF16, D);
@@ -433,31 +492,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     if (!s_last) return;
 
     const float *base = p.partials + (size_t)u * p.wg_per_unit * (size_t)G * (D + 2);
-    for (int it = threadIdx.x; it < G * D; it += kThreads) {
-        const int jj = it / D, c = it - jj * D;
-        const size_t head = head0 + jj;
-        float mt = -INFINITY;
-        for (int w = 0; w < nwg; ++w) mt = fmaxf(mt, ld_dev(&base[((size_t)w * G + jj) * (D + 2) + D + 1]));
-        float mo = 0.0f, mo2 = -INFINITY;
-        if (p.repair) {
-            mo = s_mo[jj];
-            mo2 = mo == -INFINITY ? -INFINITY : mo * kLog2e;
-            mt = fmaxf(mt, mo2);
-        }
-        float a = 0.0f, ls = 0.0f;
-        if (p.repair) {
-            const float fo = rescale(mo2, mt);
-            a = fo * p.acc[head * D + c];
-            ls = fo * s_lo[jj];
-        }
-        for (int w = 0; w < nwg; ++w) {
-            const float *pw = base + ((size_t)w * G + jj) * (D + 2);
-            const float f = rescale(ld_dev(&pw[D + 1]), mt);
-            a += f * ld_dev(&pw[c]);
-            ls += f * ld_dev(&pw[D]);
-        }
-        write_item(p, head, c, D, a, ls, mt, p.repair && mt == mo2, mo);
-    }
+    if (G * D <= 2 * kThreads) merge_partials<2, D>(p, base, nwg, head0, s_mo, s_lo);
+    else merge_partials<4, D>(p, base, nwg, head0, s_mo, s_lo);
     if (threadIdx.x == 0) __hip_atomic_store(&p.counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
