@@ -19,9 +19,8 @@ struct KvDesc {
     bool bf16;
 };
 
-// Attention workspace: [units] uint32 counters, padded to 256 B, then the per-workgroup partials.
+// Attention workspace: [units] uint32 counters, padded to 256 B, then one partial state per chunk.
 size_t attn_workspace_bytes(int batch, int hq, int hkv, int d, int block, int cap);
-int attn_wg_per_unit(int block, int cap, bool bf16, int d);
 
 hipError_t launch_attn(const KvDesc &kv, const void *q, int hq, int block, const int32_t *idx,
                        const int32_t *count, int cap, float scale, float *acc, float *l, float *m,
