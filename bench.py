@@ -1,20 +1,25 @@
 #!/usr/bin/env python3
 """Benchmark of the PRR decode hot path on one MI355X.
 
-Workload: 128K context, batch 8, 32 query / 8 kv heads, head_dim 128, block 64, K = 64 blocks, bf16,
-a drifting query trajectory (AR(1), rho 0.9, ~68% adjacent top-K overlap) with the EMA predictor
-(alpha 0.6, beta 0.3, gamma 0.5) producing P.  Decode step 0 runs with P empty (untimed); each timed
-step t >= 1 does:
+Workload (default): 128K context, batch 8, 32 query / 8 kv heads, head_dim 128, block 64, K = 64
+blocks, bf16, a drifting query trajectory (AR(1), rho 0.9, ~68% adjacent top-K overlap) with the EMA
+predictor (alpha 0.6, beta 0.3, gamma 0.5) producing P.  Decode step 0 runs with P empty (untimed);
+each timed step t >= 1 does, on synthetic inputs already resident in HBM:
 
-  1. flush (a 1 GiB read: evicts L2 and the 256 MB MALL and leaves them clean, as a decode step's
-     other layers mostly read weights), then the overlapped layer step:
-     select || spec_attn(P^t) -> repair(M^t) -> predict, events on each kernel's own stream;
-  2. flush, spec_attn(P^t) alone;  flush, repair(M^t) alone;  flush, select alone (events).
+  1. flush (a 1 GiB read: evicts L2 and the 256 MB MALL, as a decode step's other layers would),
+     then the overlapped layer step: select || spec_attn(P^t) -> repair(M^t) -> predict, with events
+     recorded on each kernel's own stream;
+  2. flush, an empty event pair (the cost of the two event records themselves);
+     flush, spec_attn(P^t) alone;  flush, repair(M^t) alone;  flush, select alone.
 
-value = effective KV GB/s of spec-attn + repair = algorithmic KV bytes ((|P| + |M|) * block * d * 2
-tensors * 2 B, summed over (sequence, kv head)) / (isolated spec time + isolated repair time).
+Kernel time = isolated event time minus the median empty-pair time of the same run (the two event
+records cost ~4 us on this platform whatever runs between them; a kernel launch still carries its own
+dispatch and completion latency).  value = effective KV GB/s of spec-attn + repair = algorithmic KV
+bytes ((|P| + |M|) * block * head_dim * 2 tensors * 2 B, summed over (sequence, kv head) units) /
+(spec kernel time + repair kernel time).  The raw event-bracketed figures are reported beside it.
+
 Also reported: us per layer step (overlapped), per-kernel us, |M|, overlap and hit rate, the roofline
-of the dominant kernel (spec-attn), and the CPU oracle timed on a bounded sample.
+of the dominant kernel (spec-attn), and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -28,7 +33,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E datasheet peak
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E peak
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "spec_attn_ctx128k_b8_hbm_counters.md")
 
 
 def log(*a):
@@ -43,8 +49,8 @@ def parse_args():
     ap.add_argument("--config", default="ctx128k_b8_64steps")
     ap.add_argument("--flush-mib", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-units", type=int, default=8, help="(sequence, kv head) units in the CPU sample")
-    ap.add_argument("--cpu-steps", type=int, default=3, help="decode steps in the CPU sample")
+    ap.add_argument("--cpu-units", type=int, default=32, help="(sequence, kv head) units in the CPU sample")
+    ap.add_argument("--cpu-steps", type=int, default=0, help="decode steps in the CPU sample (0: all timed)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size (HBM counter calibration under rocprofv3)")
     return ap.parse_args()
@@ -54,15 +60,14 @@ def kv_bytes_per_block(w) -> int:
     return w.block * w.kv_bytes_per_token()
 
 
-def load_traffic(profiles_dir: str, kernel_hash: str):
-    """HBM bytes per launch of the dominant kernel from the committed counter summary, or None when
-    absent or taken on a different kernel source."""
-    path = os.path.join(profiles_dir, "spec_attn_ctx128k_b8_hbm_counters.md")
-    if not os.path.exists(path):
+def load_traffic(kernel_hash: str):
+    """HBM bytes per spec-attn launch from the committed counter summary, or None when absent or
+    taken on a different kernel source."""
+    if not os.path.exists(PROFILE_COUNTERS):
         return None
     vals = {}
-    for line in open(path):
-        if ":" in line and line.startswith("- "):
+    for line in open(PROFILE_COUNTERS):
+        if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
     if vals.get("kernel_source_sha256") != kernel_hash:
@@ -75,7 +80,8 @@ def load_traffic(profiles_dir: str, kernel_hash: str):
 
 def cpu_baseline(inp, w, units, steps):
     """Time the oracle on a bounded sample of the same workload: `units` (sequence, kv head) pairs for
-    decode steps 0..steps (step 0 has P empty and is not counted).  BLAS is limited to one thread."""
+    decode steps 0..steps (step 0 has P empty and is not counted), one core (BLAS limited to one
+    thread).  Block metadata is built once per unit before timing, as on the GPU."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -84,9 +90,9 @@ def cpu_baseline(inp, w, units, steps):
 
     G = w.group
     alpha, beta, gamma = w.ema
-    t_attn = 0.0
-    t_all = 0.0
+    t_attn = t_all = 0.0
     nbytes = 0
+    n_unit_steps = 0
     pairs = [(u // w.num_kv_heads, u % w.num_kv_heads) for u in range(units)]
     with threadpool_limits(limits=1):
         for b, h in pairs:
@@ -95,10 +101,11 @@ def cpu_baseline(inp, w, units, steps):
             v = wl.to_numpy_bits(inp.v_cache[pages, h].unsqueeze(1))
             n = pages.numel()
             kv = orc.make_paged_kv(k, v, np.arange(n).reshape(1, n), np.array([w.lengths[b]]), w.dtype)
-            mn, mx = orc.build_meta(kv, w.block, 1)[0][0]       # per-cache setup, not timed
+            mn, mx = orc.build_meta(kv, w.block, 1)[0][0]
             lv, tr, live, P = np.zeros(0), np.zeros(0), 0, np.zeros(0, dtype=np.int64)
+            qs = orc.upcast(wl.to_numpy_bits(inp.q[: steps + 1, b, h * G:(h + 1) * G]), w.dtype)
             for t in range(steps + 1):
-                q = orc.upcast(wl.to_numpy_bits(inp.q[t, b, h * G:(h + 1) * G]), w.dtype)[None]
+                q = qs[t][None]
                 t0 = time.perf_counter()
                 s = orc.quest_scores(orc.representative_query(q, 0, 0, G), mn, mx)
                 A = orc.topk_blocks(s, w.topk)
@@ -108,21 +115,24 @@ def cpu_baseline(inp, w, units, steps):
                 states = [orc.merge(st, orc.head_state(q, kv, 0, g, G, list(M), w.block, w.scale))
                           for g, st in enumerate(states)]
                 t2 = time.perf_counter()
+                nbytes += (len(P) + len(M)) * kv_bytes_per_block(w) if t >= 1 else 0
                 lv, tr, live, P = orc.predict_step(lv, tr, live, s, alpha, beta, gamma, w.topk)
                 t3 = time.perf_counter()
                 if t >= 1:
                     t_attn += t2 - t1
                     t_all += t3 - t0
-                    nbytes += (len(P) + len(M)) * kv_bytes_per_block(w)
+                    n_unit_steps += 1
     return {
         "value": round(nbytes / t_attn / 1e9, 4) if t_attn > 0 else None,
         "unit": "effective KV GB/s (spec-attn + repair)",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{units} (sequence, kv head) units x {steps} decode steps of the same workload; "
-                  f"float64 NumPy, BLAS limited to 1 thread",
-        "us_per_unit_step_attn": round(t_attn / (units * steps) * 1e6, 1),
-        "us_per_unit_step_all": round(t_all / (units * steps) * 1e6, 1),
+        "sample": f"{units} (sequence, kv head) units x {steps} decode steps of the same workload "
+                  f"(float64 NumPy, one thread)",
+        "seconds_attn": round(t_attn, 3),
+        "seconds_all_stages": round(t_all, 3),
+        "us_per_unit_step_attn": round(t_attn / max(1, n_unit_steps) * 1e6, 1),
+        "us_per_unit_step_all": round(t_all / max(1, n_unit_steps) * 1e6, 1),
         "cpu_count_visible": len(os.sched_getaffinity(0)),
     }
 
@@ -130,8 +140,8 @@ def cpu_baseline(inp, w, units, steps):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the PRR hot path here is "
-              "single-GPU and multi-GPU runs are out of scope.", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the PRR hot path here is built and "
+              "measured on a single GPU, and multi-GPU runs are out of scope.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -158,7 +168,6 @@ def main():
     log(f"[bench] inputs + metadata ready in {time.time() - t_gen:.1f}s")
 
     flush_buf = torch.empty(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
-
     flush_buf.fill_(1.0)
     flush_sink = torch.empty((), dtype=torch.float32, device=dev)
 
@@ -181,21 +190,20 @@ def main():
     layer.reset()
     layer.step(inp.q[0])          # decode step 0: P empty (plain DSA through repair), not timed
     torch.cuda.synchronize()
-
-    crit = torch.cuda.current_stream()
-    side = layer.side
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-    rec = []
-    p_counts = torch.zeros((K, B, H), dtype=torch.int32, device=dev)
-    m_counts = torch.zeros_like(p_counts)
-    a_sets = torch.zeros((K, B, H, w.topk), dtype=torch.int32, device=dev)
-    p_sets = torch.zeros_like(a_sets)
     if args.copy_probe_mib:
         src = torch.ones(args.copy_probe_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    crit = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    rec = []
+    p_counts = torch.zeros((K, B, H), dtype=torch.int32, device=dev)
+    m_counts = torch.zeros_like(p_counts)
+    a_sets = torch.zeros((K, B, H, w.topk), dtype=torch.int32, device=dev)
+    p_sets = torch.zeros_like(a_sets)
 
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -211,32 +219,38 @@ def main():
         m_counts[i].copy_(layer.M.count)
         a_sets[i].copy_(layer.A.idx)
         p_sets[i].copy_(P.idx)
-        # 2. isolated kernels on the same sets
-        flush()
-        e0, e1 = ev(), ev()
-        e0.record(crit)
-        bd.spec_attn(q, kv, w.block, P, w.scale, out=iso_state, ws=ws_iso_spec, stream=crit)
-        e1.record(crit)
-        flush()
-        e2, e3 = ev(), ev()
-        e2.record(crit)
-        bd.repair(q, kv, w.block, layer.M, w.scale, iso_state, ws=ws_iso_rep, stream=crit)
-        e3.record(crit)
-        flush()
-        e4, e5 = ev(), ev()
-        e4.record(crit)
-        bd.select(q, kv, layer.meta, w.block, w.topk, P=P, scores=iso_scores, A=iso_A, M=iso_M, stream=crit)
-        e5.record(crit)
-        rec.append((tm, (e0, e1), (e2, e3), (e4, e5)))
+        # 2. isolated: empty event pair, then each kernel on the same sets
+        pairs = []
+        for what in ("empty", "spec", "repair", "select"):
+            flush()
+            e0, e1 = ev(), ev()
+            e0.record(crit)
+            if what == "spec":
+                bd.spec_attn(q, kv, w.block, P, w.scale, out=iso_state, ws=ws_iso_spec, stream=crit)
+            elif what == "repair":
+                bd.repair(q, kv, w.block, layer.M, w.scale, iso_state, ws=ws_iso_rep, stream=crit)
+            elif what == "select":
+                bd.select(q, kv, layer.meta, w.block, w.topk, P=P, scores=iso_scores, A=iso_A, M=iso_M,
+                          stream=crit)
+            e1.record(crit)
+            pairs.append((e0, e1))
+        rec.append((tm, *pairs))
+        if (i + 1) % 16 == 0:
+            log(f"[bench] {i + 1}/{K} steps enqueued")
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
     def el(a, b):
         return a.elapsed_time(b) * 1e3   # microseconds
 
-    spec_us = [el(*r[1]) for r in rec]
-    rep_us = [el(*r[2]) for r in rec]
-    sel_us = [el(*r[3]) for r in rec]
+    empty_us = [el(*r[1]) for r in rec]
+    spec_raw = [el(*r[2]) for r in rec]
+    rep_raw = [el(*r[3]) for r in rec]
+    sel_raw = [el(*r[4]) for r in rec]
+    base_us = float(statistics.median(empty_us))
+    spec_us = [x - base_us for x in spec_raw]
+    rep_us = [x - base_us for x in rep_raw]
+    sel_us = [x - base_us for x in sel_raw]
     step_us = [el(r[0].start, r[0].repair_end) for r in rec]
     pred_us = [el(r[0].repair_end, r[0].predict_end) for r in rec]
     spec_ov_us = [el(r[0].spec_start, r[0].spec_end) for r in rec]
@@ -248,7 +262,9 @@ def main():
     per_blk = kv_bytes_per_block(w)
     spec_bytes = pc.reshape(K, -1).sum(1) * per_blk
     rep_bytes = mc.reshape(K, -1).sum(1) * per_blk
-    value = float((spec_bytes.sum() + rep_bytes.sum()) / ((sum(spec_us) + sum(rep_us)) * 1e-6) / 1e9)
+    tot_bytes = float(spec_bytes.sum() + rep_bytes.sum())
+    value = tot_bytes / ((sum(spec_us) + sum(rep_us)) * 1e-6) / 1e9
+    value_raw = tot_bytes / ((sum(spec_raw) + sum(rep_raw)) * 1e-6) / 1e9
     spec_gbps = float(spec_bytes.sum() / (sum(spec_us) * 1e-6) / 1e9)
     rep_gbps = float(rep_bytes.sum() / (sum(rep_us) * 1e-6) / 1e9)
 
@@ -267,7 +283,7 @@ def main():
     spec_launch_bytes = float(spec_bytes.mean())
     spec_launch_us = float(statistics.mean(spec_us))
     achieved = spec_launch_bytes / (spec_launch_us * 1e-6) / 1e9
-    traffic = load_traffic(os.path.join(ROOT, "profiles"), kernel_hash)
+    traffic = load_traffic(kernel_hash)
 
     med = lambda xs: round(float(statistics.median(xs)), 2)
     result = {
@@ -288,11 +304,18 @@ def main():
                    "spec_budget_blocks": w.topk, "ema": list(w.ema), "decode_steps_timed": K,
                    "parallelism": "none (1 GPU)", "flush_mib_read_between_kernels": args.flush_mib},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+        "timing_note": "kernel us = event-bracketed us minus the median empty event pair (each after the same "
+                       "flush); *_raw figures are the event-bracketed ones",
+        "us_empty_event_pair_median": round(base_us, 2),
+        "value_raw_events_gbps": round(value_raw, 1),
         "us_per_layer_step_median": med(step_us),
         "us_per_layer_step_mean": round(float(statistics.mean(step_us)), 2),
         "us_spec_attn_median": med(spec_us),
         "us_repair_median": med(rep_us),
         "us_select_median": med(sel_us),
+        "us_spec_attn_raw_median": med(spec_raw),
+        "us_repair_raw_median": med(rep_raw),
+        "us_select_raw_median": med(sel_raw),
         "us_predict_median": med(pred_us),
         "in_layer_step": {"us_select_median": med(sel_ov_us), "us_spec_attn_median": med(spec_ov_us),
                           "us_repair_median": med(rep_ov_us)},
@@ -301,17 +324,19 @@ def main():
         "mean_missed_blocks_per_unit": round(float(mc.mean()), 2),
         "adjacent_overlap": round(float(np.mean(overlaps)), 4),
         "hit_rate": round(float(np.mean(hits)), 4),
-        "ms_per_step_note": "wall time per timed step: one overlapped layer step + isolated spec, repair and "
-                            "select, each after a cache flush",
-        "roofline": {"bound": "hbm", "kernel": "attn_kernel<bf16,128> (spec mode)",
+        "ms_per_step_note": "wall time per timed step: one overlapped layer step + isolated empty pair, spec, "
+                            "repair and select, each after a 1 GiB cache flush",
+        "roofline": {"bound": "hbm", "kernel": "attn_spec_bf16<128>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": spec_launch_bytes,
                      "avg_launch_us": round(spec_launch_us, 2), "kernel_source_sha256": kernel_hash},
     }
     if not args.no_cpu_baseline:
-        log(f"[bench] timing the CPU oracle on {args.cpu_units} units x {args.cpu_steps} steps")
-        result["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_units, args.cpu_steps)
+        steps = args.cpu_steps if args.cpu_steps > 0 else K
+        units = min(args.cpu_units, B * H)
+        log(f"[bench] timing the CPU oracle on {units} units x {steps} steps")
+        result["cpu_baseline"] = cpu_baseline(inp, w, units, steps)
     print(json.dumps(result), flush=True)
 
 

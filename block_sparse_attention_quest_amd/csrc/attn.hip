@@ -79,7 +79,6 @@ struct AttnParams {
     int units, hq, hkv, G, cap, ppb, max_pages, num_pages;
     int cp, kmax;  // pages per chunk, chunks per unit at full capacity
     float c2;  // softmax scale * log2(e)
-    int repair;
 };
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -366,7 +365,7 @@ __device__ __forceinline__ void write_item(const AttnParams &p, size_t head, int
 // visited in chunk order, MB at a time: every device-scope load of a batch is issued before any is
 // used, so a batch costs one memory round trip; batches combine with the same online-softmax step
 // (running maximum, rescaled sums), which keeps the result independent of arrival order.
-template <int VW, int D>
+template <int VW, int D, bool REPAIR>
 __device__ __forceinline__ void merge_partials(const AttnParams &p, const float *base, int nch, size_t head0,
                                                const float *s_mo, const float *s_lo) {
     constexpr int MB = 16;
@@ -379,7 +378,7 @@ __device__ __forceinline__ void merge_partials(const AttnParams &p, const float 
         float mo = 0.0f, mo2 = -INFINITY;
 #pragma unroll
         for (int v = 0; v < VW; ++v) a[v] = 0.0f;
-        if (p.repair) {
+        if (REPAIR) {
             mo = s_mo[jj];
             mo2 = mo == -INFINITY ? -INFINITY : mo * kLog2e;
             mt = mo2;
@@ -416,11 +415,11 @@ __device__ __forceinline__ void merge_partials(const AttnParams &p, const float 
             mt = mb;
         }
 #pragma unroll
-        for (int v = 0; v < VW; ++v) write_item(p, head, c0 + v, D, a[v], ls, mt, p.repair && mt == mo2, mo);
+        for (int v = 0; v < VW; ++v) write_item(p, head, c0 + v, D, a[v], ls, mt, REPAIR && mt == mo2, mo);
     }
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool REPAIR>
 __device__ __forceinline__ void attn_body(const AttnParams &p) {
     constexpr int DP = D + 4;  // padded LDS row
     __shared__ float sm_acc[kWaves][16 * DP];
@@ -450,11 +449,11 @@ __device__ __forceinline__ void attn_body(const AttnParams &p) {
         if (k >= nch) continue;
         const int slen = p.seq_len[b];
         const size_t head0 = (size_t)b * p.hq + (size_t)kvh * G;
-        if (p.repair && threadIdx.x < G) {
+        if (REPAIR && threadIdx.x < G) {
             s_mo[threadIdx.x] = p.m[head0 + threadIdx.x];
             s_lo[threadIdx.x] = p.l[head0 + threadIdx.x];
         }
-        if (p.repair && npages == 0) {
+        if (REPAIR && npages == 0) {
             // nothing missed: the state stays bit-for-bit as it is; only the normalised output
             if (p.out) {
                 for (int it = threadIdx.x; it < G * D; it += kThreads) {
@@ -521,7 +520,7 @@ __device__ __forceinline__ void attn_body(const AttnParams &p) {
             }
             if (single) {
                 const size_t head = head0 + jj;
-                if (p.repair) {
+                if (REPAIR) {
                     const float mo = s_mo[jj];
                     const float mo2 = mo == -INFINITY ? -INFINITY : mo * kLog2e;
                     const float mt = fmaxf(mx, mo2);
@@ -559,8 +558,8 @@ __device__ __forceinline__ void attn_body(const AttnParams &p) {
         __syncthreads();
         if (s_last) {
             const float *base = p.partials + (size_t)u * p.kmax * G * (D + 2);
-            if (G * D <= 2 * kThreads) merge_partials<2, D>(p, base, nch, head0, s_mo, s_lo);
-            else merge_partials<4, D>(p, base, nch, head0, s_mo, s_lo);
+            if (G * D <= 2 * kThreads) merge_partials<2, D, REPAIR>(p, base, nch, head0, s_mo, s_lo);
+            else merge_partials<4, D, REPAIR>(p, base, nch, head0, s_mo, s_lo);
             if (threadIdx.x == 0)
                 __hip_atomic_store(&p.counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -571,13 +570,23 @@ __device__ __forceinline__ void attn_body(const AttnParams &p) {
 // bf16 (the streaming path) is held to 256 registers so two waves share each SIMD; the fp32 variant
 // (exact-input checks) may use more.
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel_bf16(AttnParams p) {
-    attn_body<true, D>(p);
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_spec_bf16(AttnParams p) {
+    attn_body<true, D, false>(p);
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_kernel_f32(AttnParams p) {
-    attn_body<false, D>(p);
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_repair_bf16(AttnParams p) {
+    attn_body<true, D, true>(p);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_spec_f32(AttnParams p) {
+    attn_body<false, D, false>(p);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_repair_f32(AttnParams p) {
+    attn_body<false, D, true>(p);
 }
 
 __global__ void clear_kernel(uint32_t *w, size_t n) {
@@ -628,7 +637,6 @@ hipError_t launch_attn(const KvDesc &kv, const void *q, int hq, int block, const
     p.max_pages = kv.max_pages;
     p.num_pages = kv.num_pages;
     p.c2 = scale * kLog2e;
-    p.repair = repair ? 1 : 0;
     // About two resident workgroups per CU.  The chunk size spreads a full set (count = cap) over
     // that many workgroups; repair sets are usually a fraction of the capacity (the missed part of the
     // selection), so repair uses half that chunk size to keep the chip busy.
@@ -649,11 +657,21 @@ hipError_t launch_attn(const KvDesc &kv, const void *q, int hq, int block, const
     const int grid = (int)std::min<long>((long)units * p.kmax, target);
     const dim3 blk(kThreads);
     if (kv.bf16) {
-        if (kv.d == 128) attn_kernel_bf16<128><<<grid, blk, 0, stream>>>(p);
-        else attn_kernel_bf16<64><<<grid, blk, 0, stream>>>(p);
+        if (repair) {
+            if (kv.d == 128) attn_repair_bf16<128><<<grid, blk, 0, stream>>>(p);
+            else attn_repair_bf16<64><<<grid, blk, 0, stream>>>(p);
+        } else {
+            if (kv.d == 128) attn_spec_bf16<128><<<grid, blk, 0, stream>>>(p);
+            else attn_spec_bf16<64><<<grid, blk, 0, stream>>>(p);
+        }
     } else {
-        if (kv.d == 128) attn_kernel_f32<128><<<grid, blk, 0, stream>>>(p);
-        else attn_kernel_f32<64><<<grid, blk, 0, stream>>>(p);
+        if (repair) {
+            if (kv.d == 128) attn_repair_f32<128><<<grid, blk, 0, stream>>>(p);
+            else attn_repair_f32<64><<<grid, blk, 0, stream>>>(p);
+        } else {
+            if (kv.d == 128) attn_spec_f32<128><<<grid, blk, 0, stream>>>(p);
+            else attn_spec_f32<64><<<grid, blk, 0, stream>>>(p);
+        }
     }
     return hipGetLastError();
 }

@@ -2,22 +2,26 @@
 
 Usage:
   python -m block_sparse_attention_quest_amd.profiling stats <kernel_stats.csv> <out.md> "<command>"
-  python -m block_sparse_attention_quest_amd.profiling hbm <fetch_counter_collection.csv>
-        <write_counter_collection.csv> <out.md> "<commands>" [--copy-mib N]
+        [--trace <kernel_trace.csv>]
+  python -m block_sparse_attention_quest_amd.profiling hbm <fetch counter_collection.csv>
+        <write counter_collection.csv> <out.md> --copy-mib N "<fetch command>" "<write command>"
 
-`stats` turns rocprofv3 --kernel-trace --stats output into a short table.  `hbm` averages FETCH_SIZE and
-WRITE_SIZE (KiB per dispatch) of the speculative-attention launches, scales them by what the same
-counters read for a plain device copy of known size (the copy probe bench.py runs with
---copy-probe-mib), and records the attention source hash so stale numbers are ignored.
+`stats` turns rocprofv3 --kernel-trace --stats output into a short table.  `hbm` takes FETCH_SIZE and
+WRITE_SIZE (KiB per dispatch) of every speculative-attention launch, scales each counter by what it reads
+for a plain device copy of known size (the copy probe bench.py runs with --copy-probe-mib: the copy
+kernel with the largest WRITE_SIZE, matched by dispatch id in the FETCH_SIZE run), and
+records the attention source hash so that bench.py ignores the numbers once the kernel changes.
 """
 from __future__ import annotations
 
 import csv
 import hashlib
 import os
+import statistics
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
+SPEC_KERNEL = "attn_spec_bf16"
 
 
 def kernel_source_hash() -> str:
@@ -33,59 +37,115 @@ def _short(name: str) -> str:
     return n[:70]
 
 
-def stats_table(path: str, top: int = 14) -> str:
+def _get(row: dict, *keys, default=""):
+    for k in keys:
+        if k in row:
+            return row[k]
+    return default
+
+
+def stats_table(path: str, top: int = 16) -> str:
     rows = list(csv.DictReader(open(path)))
-    rows.sort(key=lambda r: -float(r.get("TotalDurationNs", 0)))
+    rows.sort(key=lambda r: -float(_get(r, "TotalDurationNs", default=0)))
     out = ["| kernel | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|"]
     for r in rows[:top]:
         out.append("| `{}` | {} | {:.2f} | {:.2f} | {:.2f} | {:.1f} |".format(
             _short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
-            float(r["MaxNs"]) / 1e3, float(r.get("Percentage", 0))))
+            float(r["MaxNs"]) / 1e3, float(_get(r, "Percentage", default=0))))
     return "\n".join(out)
 
 
-def _counter_rows(path: str, counter: str):
+def trace_averages(path: str, names=("attn_spec_bf16", "attn_repair_bf16")) -> str:
+    """Average duration of each named kernel per stream over its launches that did work: launches
+    shorter than a fifth of the kernel's longest (warm-up calls over empty sets) are left out.  The
+    stream that also runs the cache-flush reductions is the one bench.py times kernels alone on; the
+    other carries the overlapped layer step's speculative pass."""
+    rows = list(csv.DictReader(open(path)))
+    flush_streams = {r["Stream_Id"] for r in rows if "reduce_kernel" in r["Kernel_Name"]}
+    out = ["| kernel | stream | launches with work | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    for nm in names:
+        sel = [r for r in rows if nm in r["Kernel_Name"]]
+        if not sel:
+            continue
+        dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        top = max(dur(r) for r in sel)
+        for sid in sorted({r["Stream_Id"] for r in sel}):
+            ds = [dur(r) for r in sel if r["Stream_Id"] == sid and dur(r) >= 0.2 * top]
+            if not ds:
+                continue
+            kind = "flush stream (isolated launches + critical path)" if sid in flush_streams else "side stream"
+            out.append(f"| `{nm}` | {sid}: {kind} | {len(ds)} | {statistics.mean(ds):.2f} | {min(ds):.2f} | "
+                       f"{max(ds):.2f} |")
+    return "\n".join(out)
+
+
+def _per_dispatch(path: str, counter: str) -> dict:
+    """{dispatch id: (kernel name, summed counter value)} for one counter."""
+    out = {}
     for r in csv.DictReader(open(path)):
-        if r.get("Counter_Name", r.get("Counter-Name", "")) == counter:
-            yield r
+        if _get(r, "Counter_Name", "Counter-Name") != counter:
+            continue
+        did = int(_get(r, "Dispatch_Id", "Dispatch-Id"))
+        name = _get(r, "Kernel_Name", "Kernel-Name")
+        val = float(_get(r, "Counter_Value", "Counter-Value", default=0))
+        prev = out.get(did, (name, 0.0))
+        out[did] = (name, prev[1] + val)
+    return out
 
 
-def _per_dispatch(path: str, counter: str, match) -> list:
-    vals = {}
-    for r in _counter_rows(path, counter):
-        name = r.get("Kernel_Name", r.get("Kernel-Name", ""))
-        if match(name):
-            key = r.get("Dispatch_Id", r.get("Dispatch-Id", len(vals)))
-            vals[key] = vals.get(key, 0.0) + float(r.get("Counter_Value", r.get("Counter-Value", 0)))
-    return list(vals.values())
-
-
-def hbm_summary(fetch_csv: str, write_csv: str, copy_mib: int, spec_calls_expected=None) -> dict:
-    is_attn = lambda n: "attn_kernel" in n
-    is_copy = lambda n: ("copy" in n.lower() or "elementwise" in n.lower()) and "attn" not in n
-    f_attn = _per_dispatch(fetch_csv, "FETCH_SIZE", is_attn)
-    w_attn = _per_dispatch(write_csv, "WRITE_SIZE", is_attn)
-    f_copy = _per_dispatch(fetch_csv, "FETCH_SIZE", is_copy)
-    w_copy = _per_dispatch(write_csv, "WRITE_SIZE", is_copy)
+def hbm_summary(fetch_csv: str, write_csv: str, copy_mib: int) -> dict:
+    fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _per_dispatch(write_csv, "WRITE_SIZE")
+    # the probe copy: the copy kernel with the largest write, matched by dispatch id across the runs
+    copies = [(v, d) for d, (n, v) in write.items() if "copyBuffer" in n]
+    if not copies:
+        raise SystemExit("no copy dispatch found in the WRITE_SIZE run")
+    copy_write, copy_id = max(copies)
+    copy_fetch = fetch[copy_id][1]
     known = copy_mib * 1024.0   # KiB read and written by the probe copy
-    f_scale = known / max(f_copy) if f_copy and max(f_copy) > 0 else 1.0
-    w_scale = known / max(w_copy) if w_copy and max(w_copy) > 0 else 1.0
-    return {"attn_dispatches": len(f_attn), "fetch_kib_per_dispatch": f_attn, "write_kib_per_dispatch": w_attn,
-            "copy_fetch_kib": max(f_copy) if f_copy else None, "copy_write_kib": max(w_copy) if w_copy else None,
-            "fetch_scale": f_scale, "write_scale": w_scale}
+    f_scale = known / copy_fetch
+    w_scale = known / copy_write
+    spec = [(d, f, write[d][1]) for d, (n, f) in sorted(fetch.items()) if SPEC_KERNEL in n and d in write]
+    top = max(f for _, f, _ in spec)
+    spec = [x for x in spec if x[1] >= 0.1 * top]   # launches over an empty set (warm-up) carry no K/V
+    per_launch = [(f * f_scale + wv * w_scale) * 1024.0 for _, f, wv in spec]
+    return {"spec_dispatches": len(spec), "fetch_kib_mean": statistics.mean(f for _, f, _ in spec),
+            "write_kib_mean": statistics.mean(wv for _, _, wv in spec), "copy_fetch_kib": copy_fetch,
+            "copy_write_kib": copy_write, "fetch_scale": f_scale, "write_scale": w_scale,
+            "hbm_bytes_per_launch": statistics.mean(per_launch)}
 
 
 def main(argv):
-    if argv[0] == "stats":
+    if argv and argv[0] == "stats":
         _, src, out, cmd = argv[:4]
-        text = ["# Kernel statistics", "", "Command:", "", "```", cmd, "```", "", stats_table(src), ""]
+        text = ["# Kernel statistics (rocprofv3 --kernel-trace --stats)", "", "Command:", "", "```", cmd, "```",
+                "", stats_table(src), ""]
+        if "--trace" in argv:
+            text += ["Attention launches over non-empty sets (from the kernel trace of the same run):", "",
+                     trace_averages(argv[argv.index("--trace") + 1]), ""]
         open(out, "w").write("\n".join(text))
-    elif argv[0] == "hbm":
-        fetch_csv, write_csv, out, cmd = argv[1:5]
-        copy_mib = int(argv[argv.index("--copy-mib") + 1]) if "--copy-mib" in argv else 0
+    elif argv and argv[0] == "hbm":
+        fetch_csv, write_csv, out = argv[1:4]
+        i = argv.index("--copy-mib")
+        copy_mib = int(argv[i + 1])
+        cmds = [a for k, a in enumerate(argv[4:], start=4) if k not in (i, i + 1)]
         s = hbm_summary(fetch_csv, write_csv, copy_mib)
-        print(s)
-        raise SystemExit("hbm summary printed; write the profile by hand from these numbers")
+        lines = ["# HBM traffic of the speculative-attention kernel (rocprofv3 --pmc)", "",
+                 "FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by what it reads for a "
+                 f"{copy_mib} MiB device copy (known bytes read and written) in the same run.", "",
+                 "Commands:", "", "```", *cmds, "```", "",
+                 f"- kernel: `{SPEC_KERNEL}<128>`",
+                 f"- kernel_source_sha256: `{kernel_source_hash()}`",
+                 f"- spec_dispatches: {s['spec_dispatches']}",
+                 f"- fetch_kib_per_dispatch_mean: {s['fetch_kib_mean']:.1f}",
+                 f"- write_kib_per_dispatch_mean: {s['write_kib_mean']:.1f}",
+                 f"- copy_fetch_kib: {s['copy_fetch_kib']:.1f}",
+                 f"- copy_write_kib: {s['copy_write_kib']:.1f}",
+                 f"- fetch_scale: {s['fetch_scale']:.4f}",
+                 f"- write_scale: {s['write_scale']:.4f}",
+                 f"- hbm_bytes_per_launch: {s['hbm_bytes_per_launch']:.0f}", ""]
+        open(out, "w").write("\n".join(lines))
+        print("\n".join(lines))
     else:
         raise SystemExit(__doc__)
 
