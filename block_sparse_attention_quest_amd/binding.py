@@ -23,7 +23,7 @@ PAGE_SIZE = 16
 EXPORTS = (
     "prr_max_blocks", "prr_meta_stride", "prr_meta_bytes", "prr_attn_workspace_bytes",
     "prr_workspace_clear", "prr_build_meta", "prr_select", "prr_predict", "prr_spec_attn",
-    "prr_repair", "prr_strerror",
+    "prr_repair", "prr_calibrate_workspace_bytes", "prr_calibrate", "prr_strerror",
 )
 
 
@@ -66,6 +66,8 @@ _SIGS = {
                                      _P(AttnStateStruct), _VP, _SZ, _VP]),
     "prr_repair": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _I32, _P(BlockSetStruct), _F,
                                   _P(AttnStateStruct), _VP, _VP, _SZ, _VP]),
+    "prr_calibrate_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "prr_calibrate": (ctypes.c_int, [_VP, _I32, _I32, _I32, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]),
     "prr_strerror": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -315,3 +317,33 @@ def repair(q: torch.Tensor, kv: KVCache, block: int, M: BlockSet, scale: float, 
                         ctypes.byref(ss), _ptr(out), ws.ptr(), ws.nbytes, _stream(stream))
     _check(st, "prr_repair")
     return state
+
+
+def calibration_grid(device="cuda") -> torch.Tensor:
+    """The 80 candidates (alpha, beta, gamma) of the online calibration, alpha-major: alpha in
+    {0.2, 0.4, 0.6, 0.8}, beta in {0.1, ..., 0.5}, gamma in {0, 0.25, 0.5, 0.75} ([paper] §4.2), as
+    float64 values of the decimal literals."""
+    alphas = (0.2, 0.4, 0.6, 0.8)
+    betas = (0.1, 0.2, 0.3, 0.4, 0.5)
+    gammas = (0.0, 0.25, 0.5, 0.75)
+    vals = [(a, b, g) for a in alphas for b in betas for g in gammas]
+    return torch.tensor(vals, dtype=torch.float64, device=device)
+
+
+def calibrate(scores: torch.Tensor, topk: int, grid: Optional[torch.Tensor] = None, ws: Optional[Workspace] = None,
+              stream=None):
+    """Grid search of the predictor parameters over a prefill score matrix scores [rows][blocks] (fp32,
+    device).  Returns (H [n] fp64 device tensor, best [1] int32 device tensor)."""
+    lib = load_library()
+    rows, blocks = scores.shape
+    if grid is None:
+        grid = calibration_grid(scores.device)
+    n = grid.shape[0]
+    H = torch.empty(n, dtype=torch.float64, device=scores.device)
+    best = torch.empty(1, dtype=torch.int32, device=scores.device)
+    if ws is None:
+        ws = Workspace(lib.prr_calibrate_workspace_bytes(rows, blocks, n), device=scores.device)
+    st = lib.prr_calibrate(_ptr(scores), rows, blocks, int(topk), _ptr(grid), n, _ptr(H), _ptr(best), ws.ptr(),
+                           ws.nbytes, _stream(stream))
+    _check(st, "prr_calibrate")
+    return H, best

@@ -3,7 +3,7 @@
 Usage: python -m block_sparse_attention_quest_amd.build [--verbose]
 
 Every HIP translation unit is compiled with -Xclang -target-feature -Xclang -packed-fp32-ops (no
-packed fp32 VALU ops).  select.hip, which must reproduce plain float64 arithmetic bit for bit, is also
+packed fp32 VALU ops).  select.hip and calib.hip, which must reproduce plain float64 arithmetic bit for bit, are also
 compiled with -ffp-contract=off (no fused multiply-add).
 """
 from __future__ import annotations
@@ -25,6 +25,7 @@ ARCH = "gfx950"
 SOURCES = {
     "attn.hip": [],
     "select.hip": ["-ffp-contract=off"],
+    "calib.hip": ["-ffp-contract=off"],
     "prr_api.cpp": ["-x", "hip"],
 }
 

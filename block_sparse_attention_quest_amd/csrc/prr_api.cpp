@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdint>
 
 #include "prr_internal.hpp"
 
@@ -172,6 +173,22 @@ prr_status prr_repair(const void *q, int32_t num_q_heads, const prr_kv_cache *kv
     if (!state || !state->acc || !state->l || !state->m) return PRR_EINVAL;
     return hip_status(prr::launch_attn(desc(kv), q, num_q_heads, block, M->idx, M->count, M->cap, scale,
                                        state->acc, state->l, state->m, out, true, ws, stream));
+}
+
+size_t prr_calibrate_workspace_bytes(int32_t rows, int32_t blocks, int32_t n_candidates) {
+    if (rows <= 0 || blocks <= 0 || n_candidates <= 0) return 0;
+    return prr::calib_workspace_bytes(rows, blocks, n_candidates);
+}
+
+prr_status prr_calibrate(const float *scores, int32_t rows, int32_t blocks, int32_t topk, const double *grid,
+                         int32_t n_candidates, double *H, int32_t *best, void *ws, size_t ws_bytes,
+                         hipStream_t stream) {
+    if (!scores || !grid || !H || !best) return PRR_EINVAL;
+    if (rows <= 0 || blocks <= 0 || topk < 0 || n_candidates <= 0) return PRR_EINVAL;
+    if (blocks > prr::kMaxCalibBlocks || n_candidates > prr::kMaxCalibGrid) return PRR_EUNSUPPORTED;
+    if ((int64_t)rows * blocks > INT32_MAX) return PRR_EUNSUPPORTED;
+    if (!ws || ws_bytes < prr::calib_workspace_bytes(rows, blocks, n_candidates)) return PRR_EWORKSPACE;
+    return hip_status(prr::launch_calibrate(scores, rows, blocks, topk, grid, n_candidates, H, best, ws, stream));
 }
 
 const char *prr_strerror(prr_status status) {

@@ -9,6 +9,8 @@ namespace prr {
 
 constexpr int kPage = 16;          // tokens per page (the only supported page size)
 constexpr int kMaxSelectN = 32768; // blocks per (sequence, kv head) the top-K kernels hold on chip
+constexpr int kMaxCalibBlocks = 1024; // calibration: blocks per prefill row (16 per lane of a wave)
+constexpr int kMaxCalibGrid = 4096;   // calibration: candidates (alpha, beta, gamma)
 
 struct KvDesc {
     const void *k;
@@ -39,5 +41,11 @@ hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batc
                           int block, int nmax, double alpha, double beta, double gamma, int budget,
                           double *level, double *trend, int32_t *live, int32_t *p_idx,
                           int32_t *p_cnt, int p_cap, hipStream_t stream);
+
+// Calibration workspace: A-set masks per row, EMA checkpoints per (candidate, chunk), chunk sums.
+size_t calib_workspace_bytes(int rows, int blocks, int n);
+
+hipError_t launch_calibrate(const float *scores, int rows, int blocks, int k, const double *grid, int n,
+                            double *H, int32_t *best, void *ws, hipStream_t stream);
 
 }  // namespace prr

@@ -159,6 +159,25 @@ prr_status prr_repair(const void *q, int32_t num_q_heads, const prr_kv_cache *kv
                       const prr_block_set *M, float scale, prr_attn_state *state, float *out,
                       void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Workspace bytes needed by prr_calibrate for `rows` x `blocks` scores and `n_candidates` candidates. */
+size_t prr_calibrate_workspace_bytes(int32_t rows, int32_t blocks, int32_t n_candidates);
+
+/* Online predictor calibration ([paper] §4.2, prefill trajectory and grid search; [blog] Eqs. (4)-(5)).
+ * scores [rows][blocks] (fp32, device) is the prefill score matrix: row phi holds the block scores at
+ * prefill token phi.  grid [n_candidates][3] (fp64, device) lists candidates (alpha, beta, gamma).  For
+ * each candidate the EMA level/trend predictor runs over the rows: row 0 sets level = IS_0, trend = 0;
+ * each later row phi is predicted (level + gamma trend), the `topk` highest predictions P_phi are
+ * compared with the `topk` highest true scores A_phi of the row (ties to the smaller block index) by
+ *     h_phi = sum_{b in P_phi n A_phi} IS_{phi,b} / sum_{b in A_phi} IS_{phi,b}   (0 when A_phi is empty),
+ * and the row is absorbed with the update of prr_predict (float64, same operation order, no fused
+ * multiply-add).  H[c] = mean of h_phi over phi = 1 .. rows-1 (0 when rows = 1), written to H
+ * [n_candidates] (fp64, device); *best (int32, device) = the first candidate with the largest H.
+ * Predicted and true sets are exact; H follows float64 rounding of a fixed reduction order.
+ * blocks <= 1024, n_candidates <= 4096.  ws: prr_calibrate_workspace_bytes (no initialisation needed). */
+prr_status prr_calibrate(const float *scores, int32_t rows, int32_t blocks, int32_t topk, const double *grid,
+                         int32_t n_candidates, double *H, int32_t *best, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char *prr_strerror(prr_status status);
 

@@ -114,3 +114,22 @@ def test_select_and_predict_argument_errors(lib):
     assert pred(nmax=40000) == 2
     assert lib.prr_build_meta(ctypes.byref(kv), 64, None, None) == 1
     assert lib.prr_build_meta(ctypes.byref(_kv(max_pages=10)), 64, 1, None) == 1   # 160 tokens % 64
+
+
+def test_calibrate_argument_errors(lib):
+    need = lib.prr_calibrate_workspace_bytes(8192, 512, 80)
+    assert need >= 80 * 128 * 2 * 512 * 8
+    assert lib.prr_calibrate_workspace_bytes(0, 512, 80) == 0
+    call = lambda s=1, rows=8192, blocks=512, k=128, grid=1, n=80, H=1, best=1, ws=1, wsb=need: lib.prr_calibrate(
+        s, rows, blocks, k, grid, n, H, best, ws, wsb, None)
+    assert call(s=None) == 1
+    assert call(grid=None) == 1
+    assert call(H=None) == 1
+    assert call(best=None) == 1
+    assert call(rows=0) == 1
+    assert call(k=-1) == 1
+    assert call(n=0) == 1
+    assert call(blocks=1025) == 2
+    assert call(n=5000) == 2
+    assert call(ws=None) == 3
+    assert call(wsb=need - 1) == 3
