@@ -7,10 +7,11 @@ predictor (alpha 0.6, beta 0.3, gamma 0.5) producing P.  Decode step 0 runs with
 each timed step t >= 1 does, on synthetic inputs already resident in HBM:
 
   1. flush (a 1 GiB read: evicts L2 and the 256 MB MALL, as a decode step's other layers would),
-     then the overlapped layer step: select || spec_attn(P^t) -> repair(M^t) -> predict, with events
-     recorded on each kernel's own stream;
+     then the overlapped layer step: select || spec_attn(P^t) -> repair(M^t), with predict on a third
+     stream next to repair, and events recorded on each kernel's own stream;
   2. flush, an empty event pair (the cost of the two event records themselves);
-     flush, spec_attn(P^t) alone;  flush, repair(M^t) alone;  flush, select alone.
+     flush, spec_attn(P^t) alone;  flush, repair(M^t) alone;  flush, select alone;  flush, predict alone
+     (on copies of the predictor state).
 
 Kernel time = isolated event time minus the median empty-pair time of the same run (the two event
 records cost ~4 us on this platform whatever runs between them; a kernel launch still carries its own
@@ -182,6 +183,9 @@ def main():
     iso_M = bd.BlockSet.empty(B, H, w.topk, dev)
     ws_iso_spec = bd.workspace_for(kv, w.num_q_heads, w.block, w.topk)
     ws_iso_rep = bd.workspace_for(kv, w.num_q_heads, w.block, w.topk)
+    iso_level, iso_trend = torch.empty_like(layer.level), torch.empty_like(layer.trend)
+    iso_live = torch.empty_like(layer.live)
+    iso_P = bd.BlockSet.empty(B, H, w.topk, dev)
 
     # warmup: a few layer steps, then start the trajectory afresh
     for t in range(args.warmup):
@@ -221,7 +225,11 @@ def main():
         p_sets[i].copy_(P.idx)
         # 2. isolated: empty event pair, then each kernel on the same sets
         pairs = []
-        for what in ("empty", "spec", "repair", "select"):
+        crit.wait_stream(layer.aux)
+        iso_level.copy_(layer.level)
+        iso_trend.copy_(layer.trend)
+        iso_live.copy_(layer.live)
+        for what in ("empty", "spec", "repair", "select", "predict"):
             flush()
             e0, e1 = ev(), ev()
             e0.record(crit)
@@ -232,6 +240,9 @@ def main():
             elif what == "select":
                 bd.select(q, kv, layer.meta, w.block, w.topk, P=P, scores=iso_scores, A=iso_A, M=iso_M,
                           stream=crit)
+            elif what == "predict":
+                bd.predict(layer.scores, kv.seq_len, w.block, *w.ema, w.topk, iso_level, iso_trend, iso_live,
+                           P_next=iso_P, stream=crit)
             e1.record(crit)
             pairs.append((e0, e1))
         rec.append((tm, *pairs))
@@ -247,12 +258,14 @@ def main():
     spec_raw = [el(*r[2]) for r in rec]
     rep_raw = [el(*r[3]) for r in rec]
     sel_raw = [el(*r[4]) for r in rec]
+    pred_raw = [el(*r[5]) for r in rec]
     base_us = float(statistics.median(empty_us))
     spec_us = [x - base_us for x in spec_raw]
     rep_us = [x - base_us for x in rep_raw]
     sel_us = [x - base_us for x in sel_raw]
+    pred_us = [x - base_us for x in pred_raw]
     step_us = [el(r[0].start, r[0].repair_end) for r in rec]
-    pred_us = [el(r[0].repair_end, r[0].predict_end) for r in rec]
+    pred_ov_us = [el(r[0].predict_start, r[0].predict_end) for r in rec]
     spec_ov_us = [el(r[0].spec_start, r[0].spec_end) for r in rec]
     sel_ov_us = [el(r[0].start, r[0].select_end) for r in rec]
     rep_ov_us = [el(r[0].repair_start, r[0].repair_end) for r in rec]
@@ -317,15 +330,18 @@ def main():
         "us_repair_raw_median": med(rep_raw),
         "us_select_raw_median": med(sel_raw),
         "us_predict_median": med(pred_us),
+        "us_predict_raw_median": med(pred_raw),
         "in_layer_step": {"us_select_median": med(sel_ov_us), "us_spec_attn_median": med(spec_ov_us),
-                          "us_repair_median": med(rep_ov_us)},
+                          "us_repair_median": med(rep_ov_us), "us_predict_median": med(pred_ov_us),
+                          "note": "event-bracketed on each kernel's own stream; select on the critical stream, "
+                                  "spec-attn on the side stream, predict on a third stream next to repair"},
         "spec_attn_gbps": round(spec_gbps, 1),
         "repair_gbps": round(rep_gbps, 1),
         "mean_missed_blocks_per_unit": round(float(mc.mean()), 2),
         "adjacent_overlap": round(float(np.mean(overlaps)), 4),
         "hit_rate": round(float(np.mean(hits)), 4),
         "ms_per_step_note": "wall time per timed step: one overlapped layer step + isolated empty pair, spec, "
-                            "repair and select, each after a 1 GiB cache flush",
+                            "repair, select and predict, each after a 1 GiB cache flush",
         "roofline": {"bound": "hbm", "kernel": "attn_spec_bf16<128>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -14,8 +14,9 @@
 //
 // How it maps to CDNA4.
 //   * Work list.  A unit's set expands to count * (block / 16) pages, cut into chunks of cp pages
-//     (8..32, a multiple of 8, chosen at launch so that sets at full capacity fill about two
-//     workgroups per CU; half that for repair, whose sets are the missed part of a selection).  Chunk
+//     (8..32, a multiple of 8, chosen at launch so that sets at full capacity spread over one
+//     workgroup per CU for the speculative pass, which shares the chip with selection, and two per CU
+//     for repair, with half the chunk size since repair sets are the missed part of a selection).  Chunk
 //     c belongs to unit c mod units, so a unit's chunks are dispatched to the same XCD and every XCD
 //     gets the same number of units.  Workgroup i takes chunks i, i + grid, ...; a chunk past its
 //     unit's set size is skipped after one load.  The set size, set entries and page-table entries are
@@ -637,15 +638,18 @@ hipError_t launch_attn(const KvDesc &kv, const void *q, int hq, int block, const
     p.max_pages = kv.max_pages;
     p.num_pages = kv.num_pages;
     p.c2 = scale * kLog2e;
-    // About two resident workgroups per CU.  The chunk size spreads a full set (count = cap) over
-    // that many workgroups; repair sets are usually a fraction of the capacity (the missed part of the
-    // selection), so repair uses half that chunk size to keep the chip busy.
+    // Workgroups in flight.  The speculative pass runs next to selection, so it keeps one workgroup per
+    // CU (half of every SIMD's registers) and leaves the other half to the selection kernels; a
+    // workgroup then walks several chunks in turn.  Repair runs alone on the critical path and takes two
+    // workgroups per CU.  The chunk size spreads a full set (count = cap) over the target; repair sets
+    // are usually a fraction of the capacity (the missed part of the selection), so repair uses half
+    // of that chunk size to keep the chip busy.
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) cus = n;
     }
-    const long target = 2L * cus;
+    const long target = repair ? 2L * cus : (long)cus;
     const long cap_pages = (long)cap * p.ppb;
     const long full = (long)units * cap_pages;
     const int cmax = kv.bf16 ? kChunkMax : kChunkMaxF32;

@@ -12,13 +12,15 @@
 // Scoring ([paper] A.1): s_p = sum_i max(qbar_i mn_{p,i}, qbar_i mx_{p,i}).  Because rounding is
 // monotone, max(round(qbar mn), round(qbar mx)) = round(qbar mx) when qbar >= 0 and round(qbar mn)
 // otherwise, so the kernel reads only the metadata row the sign of qbar_i selects: half the bytes of
-// reading both, with identical bits.  Metadata is channel-major ([d][2][N]) so a lane owning 8
-// consecutive blocks does one 16-byte load per channel and accumulates its blocks in channel order.
+// reading both, with identical bits.  Metadata is channel-major ([d][2][N]): a lane owns one block,
+// issues one load per channel for all d channels before using any (a wave's load covers 64 consecutive
+// blocks), then accumulates in channel order.
 //
-// Top-K ([paper] §1, §2.1; ties to the smaller block index): one 1024-thread workgroup per
-// (sequence, kv head) keeps all N keys in registers (order-preserving 64-bit images of the fp64 scores)
-// and runs an MSD radix select with 4-bit digits: per pass each thread counts its candidates into
-// packed 8-bit counters, waves reduce with cross-lane adds and one barrier combines waves.  Leading
+// Top-K ([paper] §1, §2.1; ties to the smaller block index): one workgroup per (sequence, kv head) keeps
+// all N keys in registers (order-preserving 64-bit images of the fp64 scores; 256 threads with up to 8
+// contiguous keys each up to 2048 keys) and runs an MSD radix select with 4-bit digits: per pass each
+// lane counts its candidates' digits in 16-bit fields, waves reduce them with DPP row operations, one
+// barrier combines the waves, and a 16-lane suffix sum with one ballot picks the boundary digit.  Leading
 // bits shared by every key are skipped, and the search stops as soon as the boundary digit's bucket
 // is taken whole.  Ties on the full key go to the smaller index through a prefix sum over the
 // threads' contiguous index ranges, which also yields the ascending output positions directly.
@@ -35,8 +37,7 @@
 namespace prr {
 namespace {
 
-constexpr int kTK = 1024;            // top-K workgroup size
-constexpr int kTKWaves = kTK / 64;
+constexpr int kTopkKeysPerThread = 32;   // upper bound on keys held per thread by the top-K kernels
 
 __device__ __forceinline__ double dadd(double a, double b) {
 #pragma clang fp contract(off)
@@ -72,15 +73,49 @@ __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int o) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+template <int W>
 struct TopkSmem {
-    uint32_t hist[2][kTKWaves][8];
-    uint64_t andor[kTKWaves][2];
-    uint32_t scan[2][kTKWaves];
+    uint32_t hist[2][W][8];      // per wave: 16 digit counts as 16-bit fields
+    uint32_t tot[W][16];         // per wave: the workgroup's digit counts (each wave its own copy)
+    uint64_t andor[W][2];
+    uint32_t scan[2][W];
 };
 
-// Exclusive prefix sum over the workgroup in thread order; `total` gets the sum.  `buf` selects one of
-// two LDS slots so back-to-back scans need a single barrier each.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, TopkSmem &sm, int buf, uint32_t &total) {
+// Reductions over the 64 lanes of a wave with DPP row operations (quad swaps, half-row and row
+// mirrors, then the row-15 and row-31 broadcasts); the result is complete in lane 63 only.
+__device__ __forceinline__ uint32_t dpp_sum63(uint32_t x) {
+    x += __builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x140, 0xF, 0xF, false);  // row_mirror
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);  // row_bcast15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);  // row_bcast31 into rows 2, 3
+    return x;
+}
+__device__ __forceinline__ uint32_t dpp_and63(uint32_t x) {
+    x &= __builtin_amdgcn_update_dpp(~0u, x, 0xB1, 0xF, 0xF, false);
+    x &= __builtin_amdgcn_update_dpp(~0u, x, 0x4E, 0xF, 0xF, false);
+    x &= __builtin_amdgcn_update_dpp(~0u, x, 0x141, 0xF, 0xF, false);
+    x &= __builtin_amdgcn_update_dpp(~0u, x, 0x140, 0xF, 0xF, false);
+    x &= __builtin_amdgcn_update_dpp(~0u, x, 0x142, 0xA, 0xF, false);
+    x &= __builtin_amdgcn_update_dpp(~0u, x, 0x143, 0xC, 0xF, false);
+    return x;
+}
+__device__ __forceinline__ uint32_t dpp_or63(uint32_t x) {
+    x |= __builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, false);
+    x |= __builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, false);
+    x |= __builtin_amdgcn_update_dpp(0u, x, 0x141, 0xF, 0xF, false);
+    x |= __builtin_amdgcn_update_dpp(0u, x, 0x140, 0xF, 0xF, false);
+    x |= __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);
+    x |= __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);
+    return x;
+}
+
+// Exclusive prefix sum over the workgroup (W waves) in thread order; `total` gets the sum.  `buf` selects
+// one of two LDS slots so back-to-back scans need a single barrier each.  A one-wave workgroup scans in
+// registers only.
+template <int W>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, TopkSmem<W> &sm, int buf, uint32_t &total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t v = x;
 #pragma unroll
@@ -88,12 +123,17 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, TopkSmem &sm, in
         const uint32_t y = __shfl_up(v, o);
         if (lane >= o) v += y;
     }
-    if (lane == 63) sm.scan[buf][wave] = v;
-    __syncthreads();
-    const uint32_t wt = lane < kTKWaves ? sm.scan[buf][lane] : 0u;
-    const uint32_t before = wave_sum(lane < wave ? wt : 0u);
-    total = wave_sum(wt);
-    return before + v - x;
+    if constexpr (W == 1) {
+        total = __shfl(v, 63);
+        return v - x;
+    } else {
+        if (lane == 63) sm.scan[buf][wave] = v;
+        __syncthreads();
+        const uint32_t wt = lane < W ? sm.scan[buf][lane] : 0u;
+        const uint32_t before = wave_sum(lane < wave ? wt : 0u);
+        total = wave_sum(wt);
+        return before + v - x;
+    }
 }
 
 __device__ __forceinline__ uint64_t mask_from(int shift) {   // bits >= shift
@@ -108,8 +148,8 @@ __device__ __forceinline__ uint64_t spread16(uint32_t x) {
 
 // Select the k largest keys (key descending, index ascending) among the n valid ones.  Thread t owns
 // indices [t*KPT, t*KPT + KPT).  Returns a bitmask over the thread's KPT keys.
-template <int KPT>
-__device__ uint32_t block_topk(const uint64_t (&key)[KPT], int n, int k, TopkSmem &sm) {
+template <int KPT, int W>
+__device__ uint32_t block_topk(const uint64_t (&key)[KPT], int n, int k, TopkSmem<W> &sm) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int base = threadIdx.x * KPT;
     uint32_t valid = 0;
@@ -127,22 +167,27 @@ __device__ uint32_t block_topk(const uint64_t (&key)[KPT], int n, int k, TopkSme
             a &= key[j];
             o |= key[j];
         }
-#pragma unroll
-    for (int s = 32; s > 0; s >>= 1) {
-        a &= shfl_xor64(a, s);
-        o |= shfl_xor64(o, s);
+    {
+        const uint32_t alo = __builtin_amdgcn_readlane(dpp_and63((uint32_t)a), 63);
+        const uint32_t ahi = __builtin_amdgcn_readlane(dpp_and63((uint32_t)(a >> 32)), 63);
+        const uint32_t olo = __builtin_amdgcn_readlane(dpp_or63((uint32_t)o), 63);
+        const uint32_t ohi = __builtin_amdgcn_readlane(dpp_or63((uint32_t)(o >> 32)), 63);
+        a = ((uint64_t)ahi << 32) | alo;
+        o = ((uint64_t)ohi << 32) | olo;
     }
-    if (lane == 0) {
-        sm.andor[wave][0] = a;
-        sm.andor[wave][1] = o;
-    }
-    __syncthreads();
-    a = ~0ull;
-    o = 0ull;
+    if constexpr (W > 1) {
+        if (lane == 0) {
+            sm.andor[wave][0] = a;
+            sm.andor[wave][1] = o;
+        }
+        __syncthreads();
+        a = ~0ull;
+        o = 0ull;
 #pragma unroll
-    for (int w = 0; w < kTKWaves; ++w) {
-        a &= sm.andor[w][0];
-        o |= sm.andor[w][1];
+        for (int w = 0; w < W; ++w) {
+            a &= sm.andor[w][0];
+            o |= sm.andor[w][1];
+        }
     }
     const uint64_t diff = a ^ o;
 
@@ -159,6 +204,9 @@ __device__ uint32_t block_topk(const uint64_t (&key)[KPT], int n, int k, TopkSme
         prefix = a & mask;
         int pass = 0;
         for (; shift >= 0; shift -= 4, ++pass) {
+            // per-lane counts of the candidates' digits as packed 8-bit fields (digits 0-7 in lo, 8-15
+            // in hi; at most 32 keys per lane), widened to 16-bit fields (digit d in word d >> 1) for
+            // the wave sum, which reaches at most 64 * 32
             uint64_t lo = 0, hi = 0;
 #pragma unroll
             for (int j = 0; j < KPT; ++j) {
@@ -171,48 +219,34 @@ __device__ uint32_t block_topk(const uint64_t (&key)[KPT], int n, int k, TopkSme
             }
             const uint64_t w0 = spread16((uint32_t)lo), w1 = spread16((uint32_t)(lo >> 32));
             const uint64_t w2 = spread16((uint32_t)hi), w3 = spread16((uint32_t)(hi >> 32));
-            uint32_t c8[8] = {(uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32),
-                              (uint32_t)w2, (uint32_t)(w2 >> 32), (uint32_t)w3, (uint32_t)(w3 >> 32)};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) c8[i] = wave_sum(c8[i]);
+            uint32_t c[8] = {(uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32),
+                             (uint32_t)w2, (uint32_t)(w2 >> 32), (uint32_t)w3, (uint32_t)(w3 >> 32)};
             const int buf = pass & 1;
-            if (lane == 0) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) sm.hist[buf][wave][i] = c8[i];
+            for (int w = 0; w < 8; ++w) c[w] = dpp_sum63(c[w]);
+            if (lane == 63) {
+#pragma unroll
+                for (int w = 0; w < 8; ++w) sm.hist[buf][wave][w] = c[w];
             }
             __syncthreads();
-            // lane l reads words 2(l>>4), 2(l>>4)+1 of wave (l & 15); reduce over the 16 waves
-            uint32_t x0 = sm.hist[buf][lane & 15][2 * (lane >> 4)];
-            uint32_t x1 = sm.hist[buf][lane & 15][2 * (lane >> 4) + 1];
+            // lane d < 16: the workgroup's count of digit d; then the suffix sums S(d) = sum_{d' >= d}
+            uint32_t tot = 0;
+            if (lane < 16) {
 #pragma unroll
-            for (int s = 1; s < 16; s <<= 1) {
-                x0 += __shfl_xor(x0, s);
-                x1 += __shfl_xor(x1, s);
+                for (int w = 0; w < W; ++w) tot += (sm.hist[buf][w][lane >> 1] >> ((lane & 1) * 16)) & 0xffffu;
+                sm.tot[wave][lane] = tot;
             }
-            uint32_t cnt[16];
+            __builtin_amdgcn_wave_barrier();
+            uint32_t suf = 0;
+            if (lane < 16) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t y0 = __shfl(x0, 16 * q), y1 = __shfl(x1, 16 * q);
-                cnt[4 * q + 0] = y0 & 0xffffu;
-                cnt[4 * q + 1] = y0 >> 16;
-                cnt[4 * q + 2] = y1 & 0xffffu;
-                cnt[4 * q + 3] = y1 >> 16;
+                for (int d = 0; d < 16; ++d) suf += d >= lane ? sm.tot[wave][d] : 0u;
             }
-            int dsel = 0;
-            uint32_t cum = 0, csel = 0;
-            bool found = false;
-#pragma unroll
-            for (int d = 15; d >= 0; --d) {
-                if (!found) {
-                    if (cum + cnt[d] >= (uint32_t)remaining) {
-                        dsel = d;
-                        csel = cnt[d];
-                        found = true;
-                    } else {
-                        cum += cnt[d];
-                    }
-                }
-            }
+            // the boundary digit: the largest d with S(d) >= remaining (S falls as d grows)
+            const uint64_t ge = __ballot(lane < 16 && suf >= (uint32_t)remaining);
+            const int dsel = 63 - __clzll((long long)ge);
+            const uint32_t csel = __builtin_amdgcn_readlane(tot, dsel);
+            const uint32_t cum = __builtin_amdgcn_readlane(suf, dsel) - csel;
             remaining -= (int)cum;
             prefix |= (uint64_t)dsel << shift;
             mask |= 15ull << shift;
@@ -330,8 +364,9 @@ struct ScoreParams {
 
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
-    constexpr int BPL = BF16 ? 8 : 4;   // blocks per lane (one 16-byte load per channel row)
+    constexpr int BPL = 1;   // blocks per lane: one load per channel (2 bytes bf16, 4 bytes fp32)
     __shared__ double s_qbar[D];
+    __shared__ int s_row[D];             // metadata row of channel i: 1 (max) when qbar_i >= 0, else 0 (min)
     const int u = blockIdx.y;
     const int b = u / p.hkv, kvh = u - b * p.hkv;
     if (threadIdx.x < D) {
@@ -343,36 +378,50 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
                                   : (double)((const float *)p.q)[off];
             acc = dadd(acc, x);
         }
-        s_qbar[threadIdx.x] = acc / (double)p.G;
+        const double qb = acc / (double)p.G;
+        s_qbar[threadIdx.x] = qb;
+        s_row[threadIdx.x] = qb >= 0.0 ? 1 : 0;
     }
     __syncthreads();
     const int slen = max(p.seq_len[b], 0);
     const int nb = min((slen + p.block - 1) / p.block, p.nmax);
     const int p0 = (blockIdx.x * 256 + threadIdx.x) * BPL;
     if (p0 >= nb) return;
+    // every channel's load is issued before the first is used: one memory round trip per thread.  The
+    // row (min or max) depends on the sign of qbar_i only, so the row address is wave-uniform (scalar)
+    // and each lane adds its own block offset.
+    // Buffer loads: the unit's metadata is one buffer resource (scalar base), the row offset a scalar
+    // and the lane's block offset the only vector operand, shared by all d loads.
+    constexpr int ES = BF16 ? 2 : 4;   // element size
+    const char *ubase = (const char *)p.meta + (size_t)u * D * 2 * p.stride * ES;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)ubase, (short)0, D * 2 * p.stride * ES, 0x00020000);
+    const int voff = p0 * ES;
+    uint32_t raw[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+        // qbar >= 0: the max term is qbar * mx (row 1); otherwise qbar * mn (row 0)
+        const int sgn = __builtin_amdgcn_readfirstlane(s_row[i]);
+        if constexpr (BF16)
+            raw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsrc, voff, (2 * i + sgn) * p.stride * ES, 0);
+        else
+            raw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, (2 * i + sgn) * p.stride * ES, 0);
+    }
     double acc[BPL];
 #pragma unroll
     for (int e = 0; e < BPL; ++e) acc[e] = 0.0;
-    const size_t ubase = (size_t)u * D * 2 * p.stride + p0;
-#pragma unroll 8
+#pragma unroll
     for (int i = 0; i < D; ++i) {
+        // the accumulation is a sequential chain; a scheduling barrier every 16 channels lets the qbar
+        // reads run at most 16 channels ahead (hoisting all of them would hold 2 D doubles in registers)
+        const uint32_t r = raw[i];
         const double qb = s_qbar[i];
-        // qbar >= 0: the max term is qbar * mx (row 1); otherwise qbar * mn (row 0)
-        const size_t off = ubase + ((size_t)i * 2 + (qb >= 0.0 ? 1 : 0)) * p.stride;
-        if constexpr (BF16) {
-            const uint4 raw = *(const uint4 *)((const uint16_t *)p.meta + off);
-            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const double x = (double)bf16_to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1))));
-                acc[e] = dadd(acc[e], dmul(qb, x));
-            }
-        } else {
-            const float4 raw = *(const float4 *)((const float *)p.meta + off);
-            const float x[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = dadd(acc[e], dmul(qb, (double)x[e]));
+        for (int e = 0; e < BPL; ++e) {
+            const double x = BF16 ? (double)bf16_to_f32((uint16_t)(r >> (16 * e))) : (double)__uint_as_float(r);
+            acc[e] = dadd(acc[e], dmul(qb, x));
         }
+        if (i % 16 == 15) __builtin_amdgcn_sched_barrier(0);
     }
     double *out = p.scores + (size_t)u * p.nmax;
 #pragma unroll
@@ -396,30 +445,35 @@ struct TopkParams {
     int hkv, block, nmax, topk, p_cap, a_cap, m_cap;
 };
 
-template <int KPT>
-__global__ __launch_bounds__(kTK) void topk_kernel(TopkParams p) {
-    __shared__ TopkSmem sm;
-    __shared__ uint32_t s_pbits[kMaxSelectN / 32];
+template <int KPT, int TPB>
+__global__ __launch_bounds__(TPB) void topk_kernel(TopkParams p) {
+    constexpr int W = TPB / 64;
+    __shared__ TopkSmem<W> sm;
+    __shared__ uint32_t s_pbits[TPB * KPT / 32];
     const int u = blockIdx.x;
     const int b = u / p.hkv;
     const int slen = p.seq_len[b];
     const int nb = min((slen + p.block - 1) / p.block, p.nmax);
     const bool want_m = p.m_idx != nullptr;
+    // the score loads go out first; the P bitmap is built while they are in flight
+    uint64_t key[KPT];
+    const int base = threadIdx.x * KPT;
+    const double *row = p.scores + (size_t)u * p.nmax;
+    double sv[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) sv[j] = base + j < nb ? row[base + j] : 0.0;
     if (want_m) {
-        for (int i = threadIdx.x; i < kMaxSelectN / 32; i += kTK) s_pbits[i] = 0u;
+        for (int i = threadIdx.x; i < TPB * KPT / 32; i += TPB) s_pbits[i] = 0u;
         __syncthreads();
         const int pc = min(max(p.p_cnt[u], 0), p.p_cap);
-        for (int i = threadIdx.x; i < pc; i += kTK) {
+        for (int i = threadIdx.x; i < pc; i += TPB) {
             const int x = p.p_idx[(size_t)u * p.p_cap + i];
             if (x >= 0 && x < nb) atomicOr(&s_pbits[x >> 5], 1u << (x & 31));
         }
     }
-    uint64_t key[KPT];
-    const int base = threadIdx.x * KPT;
-    const double *row = p.scores + (size_t)u * p.nmax;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = base + j < nb ? order_key(row[base + j]) : 0ull;
-    const uint32_t sel = block_topk<KPT>(key, nb, p.topk, sm);
+    for (int j = 0; j < KPT; ++j) key[j] = base + j < nb ? order_key(sv[j]) : 0ull;
+    const uint32_t sel = block_topk<KPT, W>(key, nb, p.topk, sm);
     __syncthreads();   // P bitmap complete (and top-K scratch released)
     uint32_t inm = 0;
     if (want_m) {
@@ -457,9 +511,10 @@ struct PredictParams {
     double alpha, beta, gamma;
 };
 
-template <int KPT>
-__global__ __launch_bounds__(kTK) void predict_kernel(PredictParams p) {
-    __shared__ TopkSmem sm;
+template <int KPT, int TPB>
+__global__ __launch_bounds__(TPB) void predict_kernel(PredictParams p) {
+    constexpr int W = TPB / 64;
+    __shared__ TopkSmem<W> sm;
     const int u = blockIdx.x;
     const int b = u / p.hkv;
     const int slen = p.seq_len[b];
@@ -475,11 +530,12 @@ __global__ __launch_bounds__(kTK) void predict_kernel(PredictParams p) {
         const int i = base + j;
         key[j] = 0ull;
         if (i < nb) {
+            // the state is loaded whether or not the block is live, so these loads do not wait for `live`
             const double is = p.scores[ro + i];
+            const double l0 = p.level[ro + i], t0 = p.trend[ro + i];
             double lv, tr;
             if (i < live) {
                 // trend = beta (IS - level_old) + (1 - beta) trend_old;  level = alpha IS + (1 - alpha) level_old
-                const double l0 = p.level[ro + i], t0 = p.trend[ro + i];
                 tr = dadd(dmul(p.beta, dsub(is, l0)), dmul(one_b, t0));
                 lv = dadd(dmul(p.alpha, is), dmul(one_a, l0));
             } else {
@@ -491,7 +547,7 @@ __global__ __launch_bounds__(kTK) void predict_kernel(PredictParams p) {
             key[j] = order_key(dadd(lv, dmul(p.gamma, tr)));   // prediction level + gamma trend
         }
     }
-    const uint32_t sel = block_topk<KPT>(key, nb, p.budget, sm);
+    const uint32_t sel = block_topk<KPT, W>(key, nb, p.budget, sm);
     uint32_t total;
     const uint32_t off = block_excl_scan((uint32_t)__popc(sel), sm, 1, total);
     uint32_t o = off;
@@ -504,11 +560,43 @@ __global__ __launch_bounds__(kTK) void predict_kernel(PredictParams p) {
     }
 }
 
-int kpt_for(int nmax) {
-    int kpt = 1;
-    while (kpt * kTK < nmax) kpt *= 2;
-    return kpt;
+// Workgroup shape of the top-K kernels for rows of up to nmax keys: one wave per SIMD (256 threads) with
+// up to 8 keys each up to 2048 keys (the radix passes' cost is the per-wave work, so four busy SIMDs
+// with a few keys each beat many waves or one wave with many keys); 1024 threads with up to 32 keys
+// beyond that.
+void topk_shape(int nmax, int &tpb, int &kpt) {
+    tpb = nmax <= 128 ? 64 : nmax <= 2048 ? 256 : 1024;
+    kpt = 1;
+    while (kpt * tpb < nmax) kpt *= 2;
 }
+
+template <template <int, int> class Launch, typename P>
+hipError_t dispatch_topk(int nmax, int units, const P &p, hipStream_t stream) {
+    int tpb, kpt;
+    topk_shape(nmax, tpb, kpt);
+#define PRR_CASE(T, K) \
+    if (tpb == T && kpt == K) return Launch<K, T>::run(units, p, stream);
+    PRR_CASE(64, 1) PRR_CASE(64, 2) PRR_CASE(256, 1) PRR_CASE(256, 2) PRR_CASE(256, 4) PRR_CASE(256, 8)
+    PRR_CASE(1024, 4) PRR_CASE(1024, 8) PRR_CASE(1024, 16) PRR_CASE(1024, 32)
+#undef PRR_CASE
+    return hipErrorInvalidValue;
+}
+
+template <int KPT, int TPB>
+struct TopkLaunch {
+    static hipError_t run(int units, const TopkParams &p, hipStream_t stream) {
+        topk_kernel<KPT, TPB><<<units, TPB, 0, stream>>>(p);
+        return hipGetLastError();
+    }
+};
+
+template <int KPT, int TPB>
+struct PredictLaunch {
+    static hipError_t run(int units, const PredictParams &p, hipStream_t stream) {
+        predict_kernel<KPT, TPB><<<units, TPB, 0, stream>>>(p);
+        return hipGetLastError();
+    }
+};
 
 }  // namespace
 
@@ -551,8 +639,7 @@ hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *me
     sp.block = block;
     sp.stride = stride;
     sp.nmax = nmax;
-    const int bpl = kv.bf16 ? 8 : 4;
-    const dim3 sgrid((nmax + 256 * bpl - 1) / (256 * bpl), units);
+    const dim3 sgrid((nmax + 255) / 256, units);   // one block per lane
     if (kv.bf16) {
         if (kv.d == 128) score_kernel<true, 128><<<sgrid, 256, 0, stream>>>(sp);
         else score_kernel<true, 64><<<sgrid, 256, 0, stream>>>(sp);
@@ -578,15 +665,7 @@ hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *me
     tp.p_cap = p_cap;
     tp.a_cap = a_cap;
     tp.m_cap = m_cap;
-    switch (kpt_for(nmax)) {
-        case 1: topk_kernel<1><<<units, kTK, 0, stream>>>(tp); break;
-        case 2: topk_kernel<2><<<units, kTK, 0, stream>>>(tp); break;
-        case 4: topk_kernel<4><<<units, kTK, 0, stream>>>(tp); break;
-        case 8: topk_kernel<8><<<units, kTK, 0, stream>>>(tp); break;
-        case 16: topk_kernel<16><<<units, kTK, 0, stream>>>(tp); break;
-        default: topk_kernel<32><<<units, kTK, 0, stream>>>(tp); break;
-    }
-    return hipGetLastError();
+    return dispatch_topk<TopkLaunch>(nmax, units, tp, stream);
 }
 
 hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batch, int hkv,
@@ -610,15 +689,7 @@ hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batc
     p.beta = beta;
     p.gamma = gamma;
     const int units = batch * hkv;
-    switch (kpt_for(nmax)) {
-        case 1: predict_kernel<1><<<units, kTK, 0, stream>>>(p); break;
-        case 2: predict_kernel<2><<<units, kTK, 0, stream>>>(p); break;
-        case 4: predict_kernel<4><<<units, kTK, 0, stream>>>(p); break;
-        case 8: predict_kernel<8><<<units, kTK, 0, stream>>>(p); break;
-        case 16: predict_kernel<16><<<units, kTK, 0, stream>>>(p); break;
-        default: predict_kernel<32><<<units, kTK, 0, stream>>>(p); break;
-    }
-    return hipGetLastError();
+    return dispatch_topk<PredictLaunch>(nmax, units, p, stream);
 }
 
 }  // namespace prr
