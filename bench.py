@@ -7,11 +7,14 @@ predictor (alpha 0.6, beta 0.3, gamma 0.5) producing P.  Decode step 0 runs with
 each timed step t >= 1 does, on synthetic inputs already resident in HBM:
 
   1. flush (a 1 GiB read: evicts L2 and the 256 MB MALL, as a decode step's other layers would),
-     then the overlapped layer step: select || spec_attn(P^t) -> repair(M^t), with predict on a third
-     stream next to repair, and events recorded on each kernel's own stream;
+     then the layer step on one stream: select_spec (scoring || spec_attn(P^t) in one grid, then top-K)
+     -> repair(M^t) -> predict, with an event after each;
   2. flush, an empty event pair (the cost of the two event records themselves);
      flush, spec_attn(P^t) alone;  flush, repair(M^t) alone;  flush, select alone;  flush, predict alone
-     (on copies of the predictor state).
+     (on copies of the predictor state);  flush, select_spec alone.
+The trajectory is then replayed twice with only a start and an end event per step: the single-stream
+step (the reported us per layer step: start to the end of repair) and, for comparison, the pages'
+three-stream schedule (select on the critical stream, spec_attn on a side stream, predict on a third).
 
 Kernel time = isolated event time minus the median empty-pair time of the same run (the two event
 records cost ~4 us on this platform whatever runs between them; a kernel launch still carries its own
@@ -19,7 +22,7 @@ dispatch and completion latency).  value = effective KV GB/s of spec-attn + repa
 bytes ((|P| + |M|) * block * head_dim * 2 tensors * 2 B, summed over (sequence, kv head) units) /
 (spec kernel time + repair kernel time).  The raw event-bracketed figures are reported beside it.
 
-Also reported: us per layer step (overlapped), per-kernel us, |M|, overlap and hit rate, the roofline
+Also reported: us per layer step, per-kernel us, |M|, overlap and hit rate, the roofline
 of the dominant kernel (spec-attn), and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -151,7 +154,7 @@ def main():
     from block_sparse_attention_quest_amd import binding as bd
     from block_sparse_attention_quest_amd import profiling
     from block_sparse_attention_quest_amd import workloads as wl
-    from block_sparse_attention_quest_amd.layer_step import PRRLayer, StepTimers
+    from block_sparse_attention_quest_amd.layer_step import PRRLayer, StepTimers, TwoStreamTimers
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     bd.load_library()
@@ -208,6 +211,7 @@ def main():
     m_counts = torch.zeros_like(p_counts)
     a_sets = torch.zeros((K, B, H, w.topk), dtype=torch.int32, device=dev)
     p_sets = torch.zeros_like(a_sets)
+    iso_names = ("empty", "spec", "repair", "select", "predict", "select_spec")
 
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -215,7 +219,7 @@ def main():
         t = 1 + i
         q = inp.q[t]
         P = layer.P_cur
-        # 1. overlapped layer step
+        # 1. layer step with a breakdown
         flush()
         tm = StepTimers.make()
         layer.step(q, tm)
@@ -225,11 +229,10 @@ def main():
         p_sets[i].copy_(P.idx)
         # 2. isolated: empty event pair, then each kernel on the same sets
         pairs = []
-        crit.wait_stream(layer.aux)
         iso_level.copy_(layer.level)
         iso_trend.copy_(layer.trend)
         iso_live.copy_(layer.live)
-        for what in ("empty", "spec", "repair", "select", "predict"):
+        for what in iso_names:
             flush()
             e0, e1 = ev(), ev()
             e0.record(crit)
@@ -243,6 +246,9 @@ def main():
             elif what == "predict":
                 bd.predict(layer.scores, kv.seq_len, w.block, *w.ema, w.topk, iso_level, iso_trend, iso_live,
                            P_next=iso_P, stream=crit)
+            elif what == "select_spec":
+                bd.select_spec(q, kv, layer.meta, w.block, w.topk, P, w.scale, scores=iso_scores, A=iso_A,
+                               M=iso_M, out=iso_state, ws=ws_iso_spec, stream=crit)
             e1.record(crit)
             pairs.append((e0, e1))
         rec.append((tm, *pairs))
@@ -251,24 +257,41 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
+    def replay(two_streams: bool):
+        """Replay the trajectory with a start and an end event per step only."""
+        layer.reset()
+        layer.step(inp.q[0])
+        torch.cuda.synchronize()
+        out = []
+        for i in range(K):
+            flush()
+            if two_streams:
+                tm = TwoStreamTimers(ev(), None, None, None, None, ev())
+                layer.step_two_streams(inp.q[1 + i], tm)
+            else:
+                tm = StepTimers.lean()
+                layer.step(inp.q[1 + i], tm)
+            out.append((tm.start, tm.repair_end))
+        torch.cuda.synchronize()
+        return out
+
+    lean_one = replay(False)
+    lean_two = replay(True)
+
     def el(a, b):
         return a.elapsed_time(b) * 1e3   # microseconds
 
-    empty_us = [el(*r[1]) for r in rec]
-    spec_raw = [el(*r[2]) for r in rec]
-    rep_raw = [el(*r[3]) for r in rec]
-    sel_raw = [el(*r[4]) for r in rec]
-    pred_raw = [el(*r[5]) for r in rec]
-    base_us = float(statistics.median(empty_us))
-    spec_us = [x - base_us for x in spec_raw]
-    rep_us = [x - base_us for x in rep_raw]
-    sel_us = [x - base_us for x in sel_raw]
-    pred_us = [x - base_us for x in pred_raw]
-    step_us = [el(r[0].start, r[0].repair_end) for r in rec]
-    pred_ov_us = [el(r[0].predict_start, r[0].predict_end) for r in rec]
-    spec_ov_us = [el(r[0].spec_start, r[0].spec_end) for r in rec]
-    sel_ov_us = [el(r[0].start, r[0].select_end) for r in rec]
-    rep_ov_us = [el(r[0].repair_start, r[0].repair_end) for r in rec]
+    iso_raw = {nm: [el(*r[1 + j]) for r in rec] for j, nm in enumerate(iso_names)}
+    base_us = float(statistics.median(iso_raw["empty"]))
+    iso_us = {nm: [x - base_us for x in xs] for nm, xs in iso_raw.items()}
+    spec_raw, rep_raw = iso_raw["spec"], iso_raw["repair"]
+    spec_us, rep_us = iso_us["spec"], iso_us["repair"]
+    step_lean_us = [el(a, b) for a, b in lean_one]
+    step_two_us = [el(a, b) for a, b in lean_two]
+    step_tm_us = [el(r[0].start, r[0].repair_end) for r in rec]
+    ss_ov_us = [el(r[0].start, r[0].select_spec_end) for r in rec]
+    rep_ov_us = [el(r[0].select_spec_end, r[0].repair_end) for r in rec]
+    pred_ov_us = [el(r[0].repair_end, r[0].predict_end) for r in rec]
 
     pc = p_counts.cpu().numpy().astype(np.int64)
     mc = m_counts.cpu().numpy().astype(np.int64)
@@ -321,27 +344,33 @@ def main():
                        "flush); *_raw figures are the event-bracketed ones",
         "us_empty_event_pair_median": round(base_us, 2),
         "value_raw_events_gbps": round(value_raw, 1),
-        "us_per_layer_step_median": med(step_us),
-        "us_per_layer_step_mean": round(float(statistics.mean(step_us)), 2),
+        "us_per_layer_step_median": med(step_lean_us),
+        "us_per_layer_step_p10_p90": [round(float(np.percentile(step_lean_us, 10)), 2),
+                                      round(float(np.percentile(step_lean_us, 90)), 2)],
+        "layer_step_note": "event-bracketed, start of select_spec to the end of repair, one stream; the "
+                           "predictor follows repair on the same stream (off this path)",
+        "us_per_layer_step_two_streams_median": med(step_two_us),
         "us_spec_attn_median": med(spec_us),
+        "us_spec_attn_p10_p90": [round(float(np.percentile(spec_us, 10)), 2),
+                                 round(float(np.percentile(spec_us, 90)), 2)],
         "us_repair_median": med(rep_us),
-        "us_select_median": med(sel_us),
-        "us_spec_attn_raw_median": med(spec_raw),
-        "us_repair_raw_median": med(rep_raw),
-        "us_select_raw_median": med(sel_raw),
-        "us_predict_median": med(pred_us),
-        "us_predict_raw_median": med(pred_raw),
-        "in_layer_step": {"us_select_median": med(sel_ov_us), "us_spec_attn_median": med(spec_ov_us),
-                          "us_repair_median": med(rep_ov_us), "us_predict_median": med(pred_ov_us),
-                          "note": "event-bracketed on each kernel's own stream; select on the critical stream, "
-                                  "spec-attn on the side stream, predict on a third stream next to repair"},
+        "us_repair_p10_p90": [round(float(np.percentile(rep_us, 10)), 2),
+                              round(float(np.percentile(rep_us, 90)), 2)],
+        "us_select_median": med(iso_us["select"]),
+        "us_select_spec_median": med(iso_us["select_spec"]),
+        "us_select_plus_spec_median": med([a + b for a, b in zip(iso_us["select"], spec_us)]),
+        "us_predict_median": med(iso_us["predict"]),
+        "raw_event_us_median": {nm: med(xs) for nm, xs in iso_raw.items()},
+        "in_layer_step": {"us_select_spec_median": med(ss_ov_us), "us_repair_median": med(rep_ov_us),
+                          "us_predict_median": med(pred_ov_us), "us_to_repair_end_median": med(step_tm_us),
+                          "note": "one stream with an event after each call (the events add their own cost)"},
         "spec_attn_gbps": round(spec_gbps, 1),
         "repair_gbps": round(rep_gbps, 1),
         "mean_missed_blocks_per_unit": round(float(mc.mean()), 2),
         "adjacent_overlap": round(float(np.mean(overlaps)), 4),
         "hit_rate": round(float(np.mean(hits)), 4),
-        "ms_per_step_note": "wall time per timed step: one overlapped layer step + isolated empty pair, spec, "
-                            "repair, select and predict, each after a 1 GiB cache flush",
+        "ms_per_step_note": "wall time per timed step of the first pass: one layer step + isolated empty pair, "
+                            "spec, repair, select, predict and select_spec, each after a 1 GiB cache flush",
         "roofline": {"bound": "hbm", "kernel": "attn_spec_bf16<128>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -22,7 +22,7 @@ PAGE_SIZE = 16
 # Every symbol include/prr.h declares.
 EXPORTS = (
     "prr_max_blocks", "prr_meta_stride", "prr_meta_bytes", "prr_attn_workspace_bytes",
-    "prr_workspace_clear", "prr_build_meta", "prr_select", "prr_predict", "prr_spec_attn",
+    "prr_workspace_clear", "prr_build_meta", "prr_select", "prr_select_spec", "prr_predict", "prr_spec_attn",
     "prr_repair", "prr_calibrate_workspace_bytes", "prr_calibrate", "prr_strerror",
 )
 
@@ -60,6 +60,9 @@ _SIGS = {
     "prr_build_meta": (ctypes.c_int, [_P(KvCacheStruct), _I32, _VP, _VP]),
     "prr_select": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _VP, _I32, _I32, _P(BlockSetStruct), _VP,
                                   _P(BlockSetStruct), _P(BlockSetStruct), _VP]),
+    "prr_select_spec": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _VP, _I32, _I32, _P(BlockSetStruct), _VP,
+                                       _P(BlockSetStruct), _P(BlockSetStruct), _F, _P(AttnStateStruct), _VP, _SZ,
+                                       _VP]),
     "prr_predict": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _D, _D, _D, _I32, _VP, _VP, _VP,
                                    _P(BlockSetStruct), _VP]),
     "prr_spec_attn": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _I32, _P(BlockSetStruct), _F,
@@ -271,6 +274,35 @@ def select(q: torch.Tensor, kv: KVCache, meta: torch.Tensor, block: int, topk: i
                         ctypes.byref(m_s) if m_s is not None else None, _stream(stream))
     _check(st, "prr_select")
     return scores, A, M
+
+
+def select_spec(q: torch.Tensor, kv: KVCache, meta: torch.Tensor, block: int, topk: int, P: BlockSet,
+                scale: float, scores: Optional[torch.Tensor] = None, A: Optional[BlockSet] = None,
+                M: Optional[BlockSet] = None, out: Optional[AttnState] = None, ws: Optional[Workspace] = None,
+                stream=None):
+    """select(q, ..., P) and spec_attn(q, ..., P) as one launch; returns (scores, A, M, state)."""
+    lib = load_library()
+    s = kv.struct()
+    nmax = lib.prr_max_blocks(ctypes.byref(s), block)
+    B, Hq, d = q.shape
+    H = kv.num_kv_heads
+    dev = kv.k.device
+    if scores is None:
+        scores = torch.zeros((B, H, nmax), dtype=torch.float64, device=dev)
+    if A is None:
+        A = BlockSet.empty(B, H, max(1, topk), dev)
+    if M is None:
+        M = BlockSet.empty(B, H, max(1, topk), dev)
+    if out is None:
+        out = AttnState.empty(B, Hq, d, dev)
+    if ws is None:
+        ws = workspace_for(kv, Hq, block, P.cap)
+    a_s, p_s, m_s, o_s = A.struct(), P.struct(), M.struct(), out.struct()
+    st = lib.prr_select_spec(_ptr(q), Hq, ctypes.byref(s), _ptr(meta), block, topk, ctypes.byref(p_s),
+                             _ptr(scores), ctypes.byref(a_s), ctypes.byref(m_s), float(scale), ctypes.byref(o_s),
+                             ws.ptr(), ws.nbytes, _stream(stream))
+    _check(st, "prr_select_spec")
+    return scores, A, M, out
 
 
 def predict(scores: torch.Tensor, seq_len: torch.Tensor, block: int, alpha: float, beta: float,

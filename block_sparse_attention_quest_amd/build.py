@@ -26,6 +26,7 @@ SOURCES = {
     "attn.hip": [],
     "select.hip": ["-ffp-contract=off"],
     "calib.hip": ["-ffp-contract=off"],
+    "step.hip": [],
     "prr_api.cpp": ["-x", "hip"],
 }
 

@@ -1,0 +1,664 @@
+// attn_core.hpp - device code of the speculative block-sparse decode attention and incremental
+// repair (gfx950), shared by the attention kernels and the fused selection + speculation launch.
+//
+// Citations:
+//   [paper] "Predict, Reuse, and Repair: Accelerating Dynamic Sparse Attention for Long-Context LLM
+//           Decoding" (full paper text)
+//   [blog]  "PRR: Predict, Reuse, and Repair - Accelerating Dynamic Sparse Attention for Long-Context
+//           LLM Decoding" (xllm-io paper review)
+//
+// What is computed.  For every (sequence b, kv head) unit and each of its G query heads: the attention
+// state (acc, l, m) of the query over the tokens of the unit's block set ([paper] §4.3: the speculative
+// pass stores the softmax denominator and running maximum next to the output).  In repair mode the new
+// tokens' state is folded into the existing state with the online-softmax recurrence ([paper] §4.3,
+// [blog] Eq. (6)); work and traffic scale with the number of missed blocks only.
+//
+// How it maps to CDNA4.
+//   * Work list.  A unit's set expands to count * (block / 16) pages, cut into chunks of cp pages
+//     (8..256, a multiple of 8, chosen at launch so that sets at full capacity spread over about one
+//     workgroup per CU; half that chunk size for repair, whose sets are the missed part of a
+//     selection).  Chunk
+//     c belongs to unit c mod units, so a unit's chunks are dispatched to the same XCD and every XCD
+//     gets the same number of units.  Workgroup i takes chunks i, i + grid, ...; a chunk past its
+//     unit's set size is skipped after one load.  The set size, set entries and page-table entries are
+//     looked up with addresses that do not depend on each other where possible: two memory rounds
+//     before the first K/V load.
+//   * Streaming.  Each of the 4 waves of a workgroup owns a quarter of the chunk (up to 64 pages, one
+//     page-table lookup per lane, broadcast with readlane as the wave walks) and walks it in tiles
+//     (bf16: 32 tokens = 2 pages; fp32: 16 tokens = 1 page) with two tiles in flight: the next tile's
+//     K and V are loaded into registers while the current one is multiplied.  Loads go straight from
+//     HBM into MFMA operand registers as 16-byte loads: K page tiles are token-major ([16][d]) so a lane
+//     reads 8 channels of one token; V page tiles are channel-major ([d][16]) so a lane reads 8 tokens
+//     of one channel.
+//   * bf16: S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16.  Query heads are MFMA columns
+//     (G of 16 used), so one K/V tile read serves the whole GQA group.  The QK output rows are assigned
+//     to tokens so that each lane ends up holding exactly the 8 consecutive tokens that the PV
+//     B-operand needs: no shuffle between the two products.  P enters PV as a bf16 hi + lo pair
+//     (two MFMAs), which keeps the product at ~2^-17 relative error while V stays exact.
+//   * fp32: the same structure on v_mfma_f32_16x16x4_f32.
+//   * Softmax: online across tiles (running maximum per query, rescaled sums); waves merge in LDS;
+//     chunks of one unit merge through a small workspace: the last chunk of a unit to finish
+//     (device-scope counter) folds the partials in chunk order, so results are deterministic.
+//   * Exponentials use the hardware base-2 exponential on log2(e)-prescaled scores; m is stored in
+//     natural-log units.
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "prr_internal.hpp"
+
+namespace prr {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kChunkMin = 8;     // pages per chunk: a multiple of 8 (2 pages per wave) ...
+constexpr int kChunkMax = 256;   // ... up to 64 pages per wave: one page-table lookup per lane
+constexpr int kMaxPagesPerWave = kChunkMax / kWaves;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct AttnParams {
+    const void *q;
+    const void *k;
+    const void *v;
+    const int32_t *page_table;
+    const int32_t *seq_len;
+    const int32_t *idx;
+    const int32_t *count;
+    float *acc;
+    float *l;
+    float *m;
+    float *out;
+    uint32_t *counters;
+    float *partials;
+    int units, hq, hkv, G, cap, ppb, max_pages, num_pages;
+    int cp, kmax;  // pages per chunk, chunks per unit at full capacity
+    float c2;  // softmax scale * log2(e)
+};
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Device-scope (all XCDs) coherent store and load of one float.
+__device__ __forceinline__ void st_dev(float *ptr, float v) {
+    __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float *ptr) {
+    return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Lane-dependent choice between two wave-uniform values, kept as a register select (never an
+// indexed private-array access).
+__device__ __forceinline__ int pick(int second, int a, int b) {
+    int r;
+    asm volatile("" : "=v"(r) : "0"(second ? b : a));
+    return r;
+}
+
+__device__ __forceinline__ float rescale(float mpart, float mtot) {
+    return mpart == -INFINITY ? 0.0f : fexp2(mpart - mtot);
+}
+
+__device__ __forceinline__ int unit_pages(const AttnParams &p, int u) {
+    return min(max(p.count[u], 0), p.cap) * p.ppb;
+}
+
+// Page lookups of the wave's pages wbeg .. wbeg + N - 1 of the unit's expanded page list.  Lane
+// i < N looks up page wbeg + i with vector loads: the set entry, then the page-table entry (two
+// dependent memory rounds, through the vector memory path, which keeps many more requests in flight
+// than the scalar cache).  The addresses do not depend on the set size, so these loads are issued
+// together with the load of the set size; finish() masks entries at or past wend and broadcasts
+// physical page and valid-token count to scalar registers.
+struct PageLookup {
+    int ph;     // physical page (raw)
+    int lp;     // logical page (0 when the set entry is out of range)
+    bool lp_ok; // set entry in range
+};
+
+__device__ __forceinline__ PageLookup page_lookup(const AttnParams &p, int b, int u, int wbeg, int pw) {
+    const int i = threadIdx.x & 63;
+    PageLookup r;
+    r.ph = 0;
+    r.lp = 0;
+    r.lp_ok = false;
+    if (i < pw) {
+        const int gpc = min(wbeg + i, p.cap * p.ppb - 1);
+        const int li = gpc / p.ppb;
+        const int sub = gpc - li * p.ppb;
+        const int blk = p.idx[(size_t)u * p.cap + li];
+        const long lp = (long)blk * p.ppb + sub;
+        r.lp_ok = blk >= 0 && lp < p.max_pages;
+        r.lp = r.lp_ok ? (int)lp : 0;
+        r.ph = p.page_table[(size_t)b * p.max_pages + r.lp];
+    }
+    return r;
+}
+
+// Lane i's page of the wave list: physical page (clamped into the cache) and valid-token count.
+// Entries at or past wend are padding: valid-token count 0 (the tile computation masks them out) and
+// the wave's last real page as the address, which was just read and is served from cache.
+struct LanePage {
+    int ph;
+    int vt;
+};
+
+__device__ __forceinline__ LanePage page_finish(const AttnParams &p, const PageLookup &r, int wbeg, int wend,
+                                                int slen) {
+    const int i = threadIdx.x & 63;
+    const bool in = wbeg + i < wend;
+    const int ph = min(max(r.ph, 0), p.num_pages - 1);
+    const int last = __builtin_amdgcn_readlane(ph, wend - wbeg - 1);
+    LanePage lp;
+    lp.vt = in && r.lp_ok ? min(max(slen - r.lp * kPage, 0), kPage) : 0;
+    lp.ph = in ? ph : last;
+    return lp;
+}
+
+// Page i of the wave list, broadcast from lane i (i is wave-uniform).
+__device__ __forceinline__ int lane_val(int v, int i) { return __builtin_amdgcn_readlane(v, i); }
+
+// Per-wave running state: lane (j, g) holds channels 16 cb + 4 g + i of query column j, the running
+// maximum of column j (log2 units) and the lane's share of the denominator.
+template <int D>
+struct WaveState {
+    f32x4 o[D / 16];
+    float m;
+    float l;
+};
+
+// ---- bf16 tiles: 32 tokens (2 pages) ----
+
+template <int D>
+struct TileB {
+    bf16x8 k[2][D / 32];   // half h, k-step s: row r of S^T -> token 8(r>>2) + 4h + (r&3)
+    bf16x8 v[D / 16];      // channel block cb: channel 16 cb + r, tokens 8(g&1) .. +8 of page g>>1
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(TileB<D> &t, const __bf16 *kb, const __bf16 *vb, size_t stride,
+                                          int pa, int pb, int r, int g) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int tt = 8 * (r >> 2) + 4 * h + (r & 3);
+        const int ph = pick(tt >> 4, pa, pb);
+        const __bf16 *kp = kb + (size_t)ph * stride + (tt & 15) * D + 8 * g;
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) t.k[h][s] = *(const bf16x8 *)(kp + 32 * s);
+    }
+    const int pv = pick(g >> 1, pa, pb);
+    const __bf16 *vp = vb + (size_t)pv * stride + (size_t)r * kPage + 8 * (g & 1);
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) t.v[cb] = *(const bf16x8 *)(vp + (size_t)cb * 16 * kPage);
+}
+
+template <int D>
+__device__ __forceinline__ void compute_tile(TileB<D> &t, const bf16x8 (&qop)[D / 32], WaveState<D> &st,
+                                             int vta, int vtb, float c2, int g) {
+    const int vvt = pick(g >> 1, vta, vtb);
+    float sc[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s)
+            acc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[h][s], qop[s], acc4, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float x = 8 * (g & 1) + 4 * h + i < vvt ? acc4[i] * c2 : -INFINITY;
+            sc[4 * h + i] = x;
+            tmax = fmaxf(tmax, x);
+        }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mnew = fmaxf(st.m, tmax);
+    const float alpha = rescale(st.m, mnew);
+    const float msafe = mnew == -INFINITY ? 0.0f : mnew;
+    st.m = mnew;
+    st.l *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) st.o[cb] *= alpha;
+    if (vta < kPage || vtb < kPage) {
+        // tokens past the sequence end: zero V so stale cache contents cannot reach the output
+        const int nv = vvt - 8 * (g & 1);
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (e >= nv) t.v[cb][e] = (__bf16)0.0f;
+    }
+    bf16x8 phi, plo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float pe = fexp2(sc[e] - msafe);
+        st.l += pe;
+        const __bf16 hi = (__bf16)pe;
+        phi[e] = hi;
+        plo[e] = (__bf16)(pe - (float)hi);
+    }
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) {
+        st.o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.v[cb], phi, st.o[cb], 0, 0, 0);
+        st.o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.v[cb], plo, st.o[cb], 0, 0, 0);
+    }
+}
+
+// Walk nt bf16 tiles (tile t = pages 2t and 2t + 1 of the wave list, held by lanes 2t and 2t + 1 of
+// pg) with the next tile's loads in flight.  The tile count is padded to an even number >= 2 (padding
+// pages are masked and re-read cached addresses), so the steady-state loop issues both of its loads
+// unconditionally: every path into the loop header then has the same loads outstanding and the
+// compiler's wait counts keep one tile in flight while the other is multiplied.  The loop is not
+// unrolled, so register use does not depend on the tile count.  q is loaded first so that the first
+// tile waits for q and its own loads only.
+template <int D>
+__device__ __forceinline__ void wave_pass_bf16(const AttnParams &p, size_t head0, int kvh, int j, int g,
+                                               LanePage pg, int nt, WaveState<D> &st) {
+    const size_t stride = (size_t)p.hkv * kPage * D;   // elements per physical page
+    const __bf16 *kb = (const __bf16 *)p.k + (size_t)kvh * kPage * D;
+    const __bf16 *vb = (const __bf16 *)p.v + (size_t)kvh * kPage * D;
+    bf16x8 qop[D / 32];
+    const __bf16 *qb = (const __bf16 *)p.q + (head0 + (j < p.G ? j : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) qop[s] = *(const bf16x8 *)(qb + 32 * s + 8 * g);
+    auto load = [&](TileB<D> &tb, int t) {
+        load_tile<D>(tb, kb, vb, stride, lane_val(pg.ph, 2 * t), lane_val(pg.ph, 2 * t + 1), j, g);
+    };
+    auto comp = [&](TileB<D> &tb, int t) {
+        compute_tile<D>(tb, qop, st, lane_val(pg.vt, 2 * t), lane_val(pg.vt, 2 * t + 1), p.c2, g);
+    };
+    const int nte = (nt + 1) & ~1;
+    TileB<D> buf[2];
+    load(buf[0], 0);
+    load(buf[1], 1);
+    if (j >= p.G) {
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) qop[s] = bf16x8{};
+    }
+    int t = 0;
+#pragma unroll 1
+    for (; t + 2 < nte; t += 2) {
+        comp(buf[0], t);
+        load(buf[0], t + 2);
+        comp(buf[1], t + 1);
+        load(buf[1], t + 3);
+    }
+    comp(buf[0], t);
+    comp(buf[1], t + 1);
+}
+
+// ---- fp32 tiles: 16 tokens (1 page) ----
+
+template <int D>
+struct TileF {
+    f32x4 k[D / 16];   // token j, channels 16 s + 4 g .. +4
+    f32x4 v[D / 16];   // channel 16 cb + j, tokens 4 g .. +4
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(TileF<D> &t, const float *kf, const float *vf, size_t stride, int ph,
+                                          int j, int g) {
+    const float *kp = kf + (size_t)ph * stride + j * D + 4 * g;
+    const float *vp = vf + (size_t)ph * stride + (size_t)j * kPage + 4 * g;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) t.k[s] = *(const f32x4 *)(kp + 16 * s);
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) t.v[cb] = *(const f32x4 *)(vp + (size_t)cb * 16 * kPage);
+}
+
+template <int D>
+__device__ __forceinline__ void compute_tile(TileF<D> &t, const f32x4 (&qop)[D / 16], WaveState<D> &st, int vtp,
+                                             float c2, int g) {
+    f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            acc4 = __builtin_amdgcn_mfma_f32_16x16x4f32(t.k[s][e], qop[s][e], acc4, 0, 0, 0);
+    float sc[4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        sc[i] = 4 * g + i < vtp ? acc4[i] * c2 : -INFINITY;
+        tmax = fmaxf(tmax, sc[i]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mnew = fmaxf(st.m, tmax);
+    const float alpha = rescale(st.m, mnew);
+    const float msafe = mnew == -INFINITY ? 0.0f : mnew;
+    st.m = mnew;
+    st.l *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) st.o[cb] *= alpha;
+    if (vtp < kPage) {
+        const int nv = vtp - 4 * g;
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (e >= nv) t.v[cb][e] = 0.0f;
+    }
+    float pe[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        pe[i] = fexp2(sc[i] - msafe);
+        st.l += pe[i];
+    }
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            st.o[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.v[cb][e], pe[e], st.o[cb], 0, 0, 0);
+}
+
+// Walk nt fp32 tiles (tile t = page t of the wave list), structured like the bf16 walk.
+template <int D>
+__device__ __forceinline__ void wave_pass_f32(const AttnParams &p, size_t head0, int kvh, int j, int g,
+                                              LanePage pg, int nt, WaveState<D> &st) {
+    const size_t stride = (size_t)p.hkv * kPage * D;
+    const float *kf = (const float *)p.k + (size_t)kvh * kPage * D;
+    const float *vf = (const float *)p.v + (size_t)kvh * kPage * D;
+    f32x4 qop[D / 16];
+    const float *qf = (const float *)p.q + (head0 + (j < p.G ? j : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qop[s] = *(const f32x4 *)(qf + 16 * s + 4 * g);
+    auto load = [&](TileF<D> &tf, int t) { load_tile<D>(tf, kf, vf, stride, lane_val(pg.ph, t), j, g); };
+    auto comp = [&](TileF<D> &tf, int t) { compute_tile<D>(tf, qop, st, lane_val(pg.vt, t), p.c2, g); };
+    const int nte = (nt + 1) & ~1;
+    TileF<D> buf[2];
+    load(buf[0], 0);
+    load(buf[1], 1);
+    if (j >= p.G) {
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) qop[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    int t = 0;
+#pragma unroll 1
+    for (; t + 2 < nte; t += 2) {
+        comp(buf[0], t);
+        load(buf[0], t + 2);
+        comp(buf[1], t + 1);
+        load(buf[1], t + 3);
+    }
+    comp(buf[0], t);
+    comp(buf[1], t + 1);
+}
+
+// Final write of one (query j, channel c) item: state in natural-log units, optional normalised out.
+__device__ __forceinline__ void write_item(const AttnParams &p, size_t head, int c, int D, float a,
+                                           float lsum, float m2, bool keep_m, float m_old) {
+    p.acc[head * D + c] = a;
+    if (c == 0) {
+        p.l[head] = lsum;
+        p.m[head] = keep_m ? m_old : (m2 == -INFINITY ? -INFINITY : m2 * kLn2);
+    }
+    if (p.out) p.out[head * D + c] = lsum > 0.0f ? a / lsum : 0.0f;
+}
+
+// The last chunk of a unit folds the unit's nch partial states (and, in repair mode, the incoming
+// state) into the final one.  A thread owns VW consecutive channels of one query head.  Partials are
+// visited in chunk order, MB at a time: every device-scope load of a batch is issued before any is
+// used, so a batch costs one memory round trip; batches combine with the same online-softmax step
+// (running maximum, rescaled sums), which keeps the result independent of arrival order.
+template <int VW, int D, bool REPAIR>
+__device__ __forceinline__ void merge_partials(const AttnParams &p, const float *base, int nch, size_t head0,
+                                               const float *s_mo, const float *s_lo) {
+    constexpr int MB = 16;
+    constexpr int CPH = D / VW;   // channel groups per head
+    const int G = p.G;
+    for (int it = threadIdx.x; it < G * CPH; it += kThreads) {
+        const int jj = it / CPH, c0 = (it - jj * CPH) * VW;
+        const size_t head = head0 + jj;
+        float mt = -INFINITY, ls = 0.0f, a[VW];
+        float mo = 0.0f, mo2 = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < VW; ++v) a[v] = 0.0f;
+        if (REPAIR) {
+            mo = s_mo[jj];
+            mo2 = mo == -INFINITY ? -INFINITY : mo * kLog2e;
+            mt = mo2;
+            ls = s_lo[jj];
+#pragma unroll
+            for (int v = 0; v < VW; ++v) a[v] = p.acc[head * D + c0 + v];
+        }
+        for (int w0 = 0; w0 < nch; w0 += MB) {
+            float pm[MB], pl[MB], pa[MB][VW];
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                const int w = min(w0 + i, nch - 1);   // clamped: a valid partial, weighted 0 below
+                const float *pw = base + ((size_t)w * G + jj) * (D + 2);
+                pm[i] = ld_dev(&pw[D + 1]);
+                pl[i] = ld_dev(&pw[D]);
+#pragma unroll
+                for (int v = 0; v < VW; ++v) pa[i][v] = ld_dev(&pw[c0 + v]);
+            }
+            float mb = mt;
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                if (w0 + i < nch) mb = fmaxf(mb, pm[i]);
+            const float fr = rescale(mt, mb);
+            ls *= fr;
+#pragma unroll
+            for (int v = 0; v < VW; ++v) a[v] *= fr;
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                const float f = w0 + i < nch ? rescale(pm[i], mb) : 0.0f;
+                ls += f * pl[i];
+#pragma unroll
+                for (int v = 0; v < VW; ++v) a[v] += f * pa[i][v];
+            }
+            mt = mb;
+        }
+#pragma unroll
+        for (int v = 0; v < VW; ++v) write_item(p, head, c0 + v, D, a[v], ls, mt, REPAIR && mt == mo2, mo);
+    }
+}
+
+template <bool BF16, int D, bool REPAIR>
+__device__ __forceinline__ void attn_body(const AttnParams &p, int wg, int nwg) {
+    constexpr int DP = D + 4;  // padded LDS row
+    __shared__ float sm_acc[kWaves][16 * DP];
+    __shared__ float sm_m[kWaves][16];
+    __shared__ float sm_l[kWaves][16];
+    __shared__ float s_mo[16], s_lo[16];   // repair: the incoming state's m and l per query head
+    __shared__ int s_last;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = lane & 15;   // query column / operand row
+    const int g = lane >> 4;   // lane group (k slice)
+    const int G = p.G;
+    const int cp = p.cp;
+    const int pw = cp / kWaves;   // pages per wave: an even number from 2 to 64
+    const int total = p.units * p.kmax;
+
+    // Chunk c covers pages [k cp, (k + 1) cp) of unit u = c mod units, k = c / units.  Chunks past a
+    // unit's set size are skipped; chunk 0 of a unit with an empty set still writes its output.
+    for (int c = wg; c < total; c += nwg) {
+        const int u = c % p.units, k = c / p.units;
+        const int b = u / p.hkv, kvh = u - b * p.hkv;
+        const int wbeg = k * cp + wave * pw;
+        const PageLookup look = page_lookup(p, b, u, wbeg, pw);
+        const int npages = unit_pages(p, u);
+        const int nch = max(1, (npages + cp - 1) / cp);
+        if (k >= nch) continue;
+        const int slen = p.seq_len[b];
+        const size_t head0 = (size_t)b * p.hq + (size_t)kvh * G;
+        if (REPAIR && threadIdx.x < G) {
+            s_mo[threadIdx.x] = p.m[head0 + threadIdx.x];
+            s_lo[threadIdx.x] = p.l[head0 + threadIdx.x];
+        }
+        if (REPAIR && npages == 0) {
+            // nothing missed: the state stays bit-for-bit as it is; only the normalised output
+            if (p.out) {
+                for (int it = threadIdx.x; it < G * D; it += kThreads) {
+                    const int jj = it / D, cc = it - jj * D;
+                    const size_t head = head0 + jj;
+                    const float lo_ = p.l[head];
+                    p.out[head * D + cc] = lo_ > 0.0f ? p.acc[head * D + cc] / lo_ : 0.0f;
+                }
+            }
+            __syncthreads();
+            continue;
+        }
+
+        const int cend = min(npages, k * cp + cp);
+        const int wend = min(cend, wbeg + pw);
+
+        WaveState<D> st;
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb) st.o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st.m = -INFINITY;
+        st.l = 0.0f;
+        if (wbeg < wend) {
+            const LanePage pg = page_finish(p, look, wbeg, wend, slen);
+            const int nw = wend - wbeg;   // pages of this wave, 1 .. pw
+            if constexpr (BF16) wave_pass_bf16<D>(p, head0, kvh, j, g, pg, (nw + 1) / 2, st);
+            else wave_pass_f32<D>(p, head0, kvh, j, g, pg, nw, st);
+        }
+        // wave state -> LDS (lane (j, g) holds channels 16 cb + 4 g + i of query j)
+        float lsum = st.l;
+        lsum += __shfl_xor(lsum, 16);
+        lsum += __shfl_xor(lsum, 32);
+        if (j < G) {
+#pragma unroll
+            for (int cb = 0; cb < D / 16; ++cb) *(f32x4 *)&sm_acc[wave][j * DP + 16 * cb + 4 * g] = st.o[cb];
+            if (g == 0) {
+                sm_m[wave][j] = st.m;
+                sm_l[wave][j] = lsum;
+            }
+        }
+        __syncthreads();
+
+        const bool single = (nch == 1);
+        float *part = p.partials + ((size_t)u * p.kmax + k) * G * (D + 2);
+        for (int it = threadIdx.x; it < G * D; it += kThreads) {
+            const int jj = it / D, cc = it - jj * D;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm_m[w][jj]);
+            float a = 0.0f, ls = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float f = rescale(sm_m[w][jj], mx);
+                a += f * sm_acc[w][jj * DP + cc];
+                ls += f * sm_l[w][jj];
+            }
+            if (single) {
+                const size_t head = head0 + jj;
+                if (REPAIR) {
+                    const float mo = s_mo[jj];
+                    const float mo2 = mo == -INFINITY ? -INFINITY : mo * kLog2e;
+                    const float mt = fmaxf(mx, mo2);
+                    const float fo = rescale(mo2, mt), fn = rescale(mx, mt);
+                    write_item(p, head, cc, D, fo * p.acc[head * D + cc] + fn * a, fo * s_lo[jj] + fn * ls,
+                               mt, mt == mo2, mo);
+                } else {
+                    write_item(p, head, cc, D, a, ls, mx, false, 0.0f);
+                }
+            } else {
+                st_dev(&part[jj * (D + 2) + cc], a);
+                if (cc == 0) {
+                    st_dev(&part[jj * (D + 2) + D], ls);
+                    st_dev(&part[jj * (D + 2) + D + 1], mx);
+                }
+            }
+        }
+        if (single) {
+            __syncthreads();   // LDS is reused by the next chunk
+            continue;
+        }
+
+        // Cross-chunk merge: the last chunk of the unit to finish folds every partial in chunk order.
+        // Partials are written and read with device-scope (sc1) accesses, which are coherent across
+        // the XCDs' L2s by themselves; waiting for this thread's stores to complete before the barrier,
+        // and the barrier before the counter increment, orders them ahead of it.  This avoids a
+        // device-scope release fence, which would write back every dirty line of the L2.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t prev = __hip_atomic_fetch_add(&p.counters[u], 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            s_last = (prev == (uint32_t)(nch - 1));
+        }
+        __syncthreads();
+        if (s_last) {
+            const float *base = p.partials + (size_t)u * p.kmax * G * (D + 2);
+            if (G * D <= 2 * kThreads) merge_partials<2, D, REPAIR>(p, base, nch, head0, s_mo, s_lo);
+            else merge_partials<4, D, REPAIR>(p, base, nch, head0, s_mo, s_lo);
+            if (threadIdx.x == 0)
+                __hip_atomic_store(&p.counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+    }
+}
+
+
+size_t counters_bytes(int units) { return ((size_t)units * 4 + 255) / 256 * 256; }
+
+// Partials kept per launch: every chunk of every unit at the smallest chunk size.
+size_t max_chunks(int units, int block, int cap) {
+    const long pages = (long)cap * (block / kPage);
+    return (size_t)units * (size_t)std::max<long>(1, (pages + kChunkMin - 1) / kChunkMin);
+}
+
+// Fills the kernel parameters of one speculative (repair = false) or repair launch and returns its
+// grid size (workgroups).
+int attn_setup(AttnParams &p, const KvDesc &kv, const void *q, int hq, int block, const int32_t *idx,
+               const int32_t *count, int cap, float scale, float *acc, float *l, float *m, float *out,
+               bool repair, void *ws) {
+    p.q = q;
+    p.k = kv.k;
+    p.v = kv.v;
+    p.page_table = kv.page_table;
+    p.seq_len = kv.seq_len;
+    p.idx = idx;
+    p.count = count;
+    p.acc = acc;
+    p.l = l;
+    p.m = m;
+    p.out = out;
+    const int units = kv.batch * kv.hkv;
+    p.counters = (uint32_t *)ws;
+    p.partials = (float *)((char *)ws + counters_bytes(units));
+    p.units = units;
+    p.hq = hq;
+    p.hkv = kv.hkv;
+    p.G = hq / kv.hkv;
+    p.cap = cap;
+    p.ppb = block / kPage;
+    p.max_pages = kv.max_pages;
+    p.num_pages = kv.num_pages;
+    p.c2 = scale * kLog2e;
+    // Workgroups in flight: about one per CU, i.e. one wave on every SIMD, which leaves the other half of
+    // each SIMD's registers to the selection kernels that run beside the speculative pass.  A full set
+    // (count = cap) is spread over that many chunks, each as large as the work allows (fewer chunks
+    // mean fewer partial states to merge); repair sets are usually a fraction of the capacity (the
+    // missed part of a selection), so repair uses half that chunk size to keep the chip busy.
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) cus = n;
+    }
+    const long target = cus;
+    const long cap_pages = (long)cap * p.ppb;
+    const long full = (long)units * cap_pages;
+    auto round8 = [](long x) { return (x + kChunkMin - 1) / kChunkMin * kChunkMin; };
+    long cp = std::min<long>(std::max<long>(round8((full + target - 1) / target), kChunkMin), kChunkMax);
+    if (repair) cp = std::max<long>(kChunkMin, round8(cp / 2));
+    p.cp = (int)cp;
+    p.kmax = (int)std::max<long>(1, (cap_pages + cp - 1) / cp);
+    return (int)std::min<long>((long)units * p.kmax, target);
+}
+
+}  // namespace
+}  // namespace prr

@@ -143,6 +143,24 @@ prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv
                                          stream));
 }
 
+prr_status prr_select_spec(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
+                           int32_t block, int32_t topk, const prr_block_set *P, double *scores,
+                           prr_block_set *A, prr_block_set *M, float scale, prr_attn_state *out, void *ws,
+                           size_t ws_bytes, hipStream_t stream) {
+    if (!meta || !scores || !P || !M) return PRR_EINVAL;
+    PRR_TRY(attn_common(q, num_q_heads, kv, block, P, ws, ws_bytes));
+    PRR_TRY(check_set(A));
+    PRR_TRY(check_set(M));
+    if (topk < 0 || A->cap < topk || M->cap < topk) return PRR_EINVAL;
+    if (!out || !out->acc || !out->l || !out->m) return PRR_EINVAL;
+    const int nmax = prr_max_blocks(kv, block);
+    if (nmax > prr::kMaxSelectN) return PRR_EUNSUPPORTED;
+    return hip_status(prr::launch_select_spec(desc(kv), q, num_q_heads, meta, block, prr_meta_stride(kv, block),
+                                              nmax, topk, P->idx, P->count, P->cap, scores, A->idx, A->count,
+                                              A->cap, M->idx, M->count, M->cap, scale, out->acc, out->l, out->m,
+                                              ws, stream));
+}
+
 prr_status prr_predict(const double *scores, const int32_t *seq_len, int32_t batch,
                        int32_t num_kv_heads, int32_t block, int32_t max_blocks, double alpha,
                        double beta, double gamma, int32_t budget, double *level, double *trend,

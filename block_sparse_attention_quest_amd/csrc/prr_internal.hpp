@@ -37,6 +37,19 @@ hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *me
                          int p_cap, double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap,
                          int32_t *m_idx, int32_t *m_cnt, int m_cap, hipStream_t stream);
 
+// Top-K + M = A \ P from scores already in place (the second half of launch_select).
+hipError_t launch_topk(const KvDesc &kv, int block, int nmax, int topk, const double *scores,
+                       const int32_t *p_idx, const int32_t *p_cnt, int p_cap, int32_t *a_idx, int32_t *a_cnt,
+                       int a_cap, int32_t *m_idx, int32_t *m_cnt, int m_cap, hipStream_t stream);
+
+// Selection and the speculative pass over P in one grid (bf16 caches; fp32 caches run the two in turn),
+// then the top-K.  ws is the speculative pass's attention workspace.
+hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,
+                              int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
+                              double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
+                              int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m,
+                              void *ws, hipStream_t stream);
+
 hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batch, int hkv,
                           int block, int nmax, double alpha, double beta, double gamma, int budget,
                           double *level, double *trend, int32_t *live, int32_t *p_idx,

@@ -1,0 +1,509 @@
+// select_core.hpp - device code of GQA Quest scoring, top-K selection with M = A \ P, and the fused
+// EMA level/trend predictor (gfx950), shared by the selection kernels and the fused selection +
+// speculation launch.  Floating-point contraction is off for all of it: every float64 multiply and add
+// below is a separately rounded IEEE operation, in the order the comments state, so scores and
+// predictions are bit-identical to a plain float64 evaluation of the same formulas.
+//
+// Citations:
+//   [paper] "Predict, Reuse, and Repair: Accelerating Dynamic Sparse Attention for Long-Context LLM
+//           Decoding" (full paper text)
+//   [blog]  "PRR: Predict, Reuse, and Repair - Accelerating Dynamic Sparse Attention for Long-Context
+//           LLM Decoding" (xllm-io paper review)
+//
+// Scoring ([paper] A.1): s_p = sum_i max(qbar_i mn_{p,i}, qbar_i mx_{p,i}).  Because rounding is
+// monotone, max(round(qbar mn), round(qbar mx)) = round(qbar mx) when qbar >= 0 and round(qbar mn)
+// otherwise, so the kernel reads only the metadata row the sign of qbar_i selects: half the bytes of
+// reading both, with identical bits.  Metadata is channel-major ([d][2][N]): a lane owns one block,
+// issues one load per channel for all d channels before using any (a wave's load covers 64 consecutive
+// blocks), then accumulates in channel order.
+//
+// Top-K ([paper] §1, §2.1; ties to the smaller block index): one workgroup per (sequence, kv head) keeps
+// all N keys in registers (order-preserving 64-bit images of the fp64 scores; 256 threads with up to 8
+// contiguous keys each up to 2048 keys) and runs an MSD radix select with 4-bit digits: per pass each
+// lane counts its candidates' digits in 16-bit fields, waves reduce them with DPP row operations, one
+// barrier combines the waves, and a 16-lane suffix sum with one ballot picks the boundary digit.  Leading
+// bits shared by every key are skipped, and the search stops as soon as the boundary digit's bucket
+// is taken whole.  Ties on the full key go to the smaller index through a prefix sum over the
+// threads' contiguous index ranges, which also yields the ascending output positions directly.
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "prr_internal.hpp"
+
+#pragma clang fp contract(off)
+
+namespace prr {
+namespace {
+
+constexpr int kTopkKeysPerThread = 32;   // upper bound on keys held per thread by the top-K kernels
+
+__device__ __forceinline__ double dadd(double a, double b) {
+#pragma clang fp contract(off)
+    return a + b;
+}
+__device__ __forceinline__ double dmul(double a, double b) {
+#pragma clang fp contract(off)
+    return a * b;
+}
+__device__ __forceinline__ double dsub(double a, double b) {
+#pragma clang fp contract(off)
+    return a - b;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// Order-preserving image of a double (larger double -> larger key); -0.0 maps with +0.0.
+__device__ __forceinline__ uint64_t order_key(double x) {
+    uint64_t b = (uint64_t)__double_as_longlong(x);
+    if (b == 0x8000000000000000ull) b = 0;
+    return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int o) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, o);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int W>
+struct TopkSmem {
+    uint32_t hist[2][W][8];      // per wave: 16 digit counts as 16-bit fields
+    uint32_t tot[W][16];         // per wave: the workgroup's digit counts (each wave its own copy)
+    uint64_t andor[W][2];
+    uint32_t scan[2][W];
+};
+
+// Reductions over the 64 lanes of a wave with DPP row operations (quad swaps, half-row and row
+// mirrors, then the row-15 and row-31 broadcasts); the result is complete in lane 63 only.
+__device__ __forceinline__ uint32_t dpp_sum63(uint32_t x) {
+    x += __builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x140, 0xF, 0xF, false);  // row_mirror
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);  // row_bcast15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);  // row_bcast31 into rows 2, 3
+    return x;
+}
+__device__ __forceinline__ uint32_t dpp_and63(uint32_t x) {
+    x &= __builtin_amdgcn_update_dpp(~0u, x, 0xB1, 0xF, 0xF, false);
+    x &= __builtin_amdgcn_update_dpp(~0u, x, 0x4E, 0xF, 0xF, false);
+    x &= __builtin_amdgcn_update_dpp(~0u, x, 0x141, 0xF, 0xF, false);
+    x &= __builtin_amdgcn_update_dpp(~0u, x, 0x140, 0xF, 0xF, false);
+    x &= __builtin_amdgcn_update_dpp(~0u, x, 0x142, 0xA, 0xF, false);
+    x &= __builtin_amdgcn_update_dpp(~0u, x, 0x143, 0xC, 0xF, false);
+    return x;
+}
+__device__ __forceinline__ uint32_t dpp_or63(uint32_t x) {
+    x |= __builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, false);
+    x |= __builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, false);
+    x |= __builtin_amdgcn_update_dpp(0u, x, 0x141, 0xF, 0xF, false);
+    x |= __builtin_amdgcn_update_dpp(0u, x, 0x140, 0xF, 0xF, false);
+    x |= __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);
+    x |= __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);
+    return x;
+}
+
+// Exclusive prefix sum over the workgroup (W waves) in thread order; `total` gets the sum.  `buf` selects
+// one of two LDS slots so back-to-back scans need a single barrier each.  A one-wave workgroup scans in
+// registers only.
+template <int W>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, TopkSmem<W> &sm, int buf, uint32_t &total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t v = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(v, o);
+        if (lane >= o) v += y;
+    }
+    if constexpr (W == 1) {
+        total = __shfl(v, 63);
+        return v - x;
+    } else {
+        if (lane == 63) sm.scan[buf][wave] = v;
+        __syncthreads();
+        const uint32_t wt = lane < W ? sm.scan[buf][lane] : 0u;
+        const uint32_t before = wave_sum(lane < wave ? wt : 0u);
+        total = wave_sum(wt);
+        return before + v - x;
+    }
+}
+
+__device__ __forceinline__ uint64_t mask_from(int shift) {   // bits >= shift
+    return shift >= 64 ? 0ull : ~((1ull << shift) - 1ull);
+}
+
+// Widen four 8-bit counters (one u32) into four 16-bit fields (one u64).
+__device__ __forceinline__ uint64_t spread16(uint32_t x) {
+    return (uint64_t)(x & 0xffu) | ((uint64_t)(x & 0xff00u) << 8) | ((uint64_t)(x & 0xff0000u) << 16) |
+           ((uint64_t)(x & 0xff000000u) << 24);
+}
+
+// Select the k largest keys (key descending, index ascending) among the n valid ones.  Thread t owns
+// indices [t*KPT, t*KPT + KPT).  Returns a bitmask over the thread's KPT keys.
+template <int KPT, int W>
+__device__ uint32_t block_topk(const uint64_t (&key)[KPT], int n, int k, TopkSmem<W> &sm) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int base = threadIdx.x * KPT;
+    uint32_t valid = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        if (base + j < n) valid |= 1u << j;
+    if (k <= 0) return 0u;
+    if (k >= n) return valid;
+
+    // common leading bits of all valid keys
+    uint64_t a = ~0ull, o = 0ull;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        if (valid >> j & 1u) {
+            a &= key[j];
+            o |= key[j];
+        }
+    {
+        const uint32_t alo = __builtin_amdgcn_readlane(dpp_and63((uint32_t)a), 63);
+        const uint32_t ahi = __builtin_amdgcn_readlane(dpp_and63((uint32_t)(a >> 32)), 63);
+        const uint32_t olo = __builtin_amdgcn_readlane(dpp_or63((uint32_t)o), 63);
+        const uint32_t ohi = __builtin_amdgcn_readlane(dpp_or63((uint32_t)(o >> 32)), 63);
+        a = ((uint64_t)ahi << 32) | alo;
+        o = ((uint64_t)ohi << 32) | olo;
+    }
+    if constexpr (W > 1) {
+        if (lane == 0) {
+            sm.andor[wave][0] = a;
+            sm.andor[wave][1] = o;
+        }
+        __syncthreads();
+        a = ~0ull;
+        o = 0ull;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            a &= sm.andor[w][0];
+            o |= sm.andor[w][1];
+        }
+    }
+    const uint64_t diff = a ^ o;
+
+    uint64_t prefix, mask;
+    int remaining = k;
+    bool take_all = false;
+    if (diff == 0) {
+        prefix = a;          // every key equal: pure tie break by index
+        mask = ~0ull;
+    } else {
+        const int top = 63 - __clzll((long long)diff);
+        int shift = (top / 4) * 4;
+        mask = mask_from(shift + 4);
+        prefix = a & mask;
+        int pass = 0;
+        for (; shift >= 0; shift -= 4, ++pass) {
+            // per-lane counts of the candidates' digits as packed 8-bit fields (digits 0-7 in lo, 8-15
+            // in hi; at most 32 keys per lane), widened to 16-bit fields (digit d in word d >> 1) for
+            // the wave sum, which reaches at most 64 * 32
+            uint64_t lo = 0, hi = 0;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                if ((valid >> j & 1u) && (key[j] & mask) == prefix) {
+                    const uint32_t d = (uint32_t)(key[j] >> shift) & 15u;
+                    const uint64_t inc = 1ull << ((d & 7u) * 8u);
+                    if (d & 8u) hi += inc;
+                    else lo += inc;
+                }
+            }
+            const uint64_t w0 = spread16((uint32_t)lo), w1 = spread16((uint32_t)(lo >> 32));
+            const uint64_t w2 = spread16((uint32_t)hi), w3 = spread16((uint32_t)(hi >> 32));
+            uint32_t c[8] = {(uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32),
+                             (uint32_t)w2, (uint32_t)(w2 >> 32), (uint32_t)w3, (uint32_t)(w3 >> 32)};
+            const int buf = pass & 1;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) c[w] = dpp_sum63(c[w]);
+            if (lane == 63) {
+#pragma unroll
+                for (int w = 0; w < 8; ++w) sm.hist[buf][wave][w] = c[w];
+            }
+            __syncthreads();
+            // lane d < 16: the workgroup's count of digit d; then the suffix sums S(d) = sum_{d' >= d}
+            uint32_t tot = 0;
+            if (lane < 16) {
+#pragma unroll
+                for (int w = 0; w < W; ++w) tot += (sm.hist[buf][w][lane >> 1] >> ((lane & 1) * 16)) & 0xffffu;
+                sm.tot[wave][lane] = tot;
+            }
+            __builtin_amdgcn_wave_barrier();
+            uint32_t suf = 0;
+            if (lane < 16) {
+#pragma unroll
+                for (int d = 0; d < 16; ++d) suf += d >= lane ? sm.tot[wave][d] : 0u;
+            }
+            // the boundary digit: the largest d with S(d) >= remaining (S falls as d grows)
+            const uint64_t ge = __ballot(lane < 16 && suf >= (uint32_t)remaining);
+            const int dsel = 63 - __clzll((long long)ge);
+            const uint32_t csel = __builtin_amdgcn_readlane(tot, dsel);
+            const uint32_t cum = __builtin_amdgcn_readlane(suf, dsel) - csel;
+            remaining -= (int)cum;
+            prefix |= (uint64_t)dsel << shift;
+            mask |= 15ull << shift;
+            if (csel == (uint32_t)remaining) {
+                take_all = true;
+                break;
+            }
+        }
+    }
+
+    uint32_t sel = 0, tie = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        if (!(valid >> j & 1u)) continue;
+        const uint64_t mk = key[j] & mask;
+        if (mk > prefix) sel |= 1u << j;
+        else if (mk == prefix) tie |= 1u << j;
+    }
+    if (take_all) return sel | tie;
+    // ties on the full key: the `remaining` smallest indices win
+    uint32_t total;
+    const uint32_t before = block_excl_scan(__popc(tie), sm, 0, total);
+    uint32_t r = before;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        if (tie >> j & 1u) {
+            if (r < (uint32_t)remaining) sel |= 1u << j;
+            ++r;
+        }
+    return sel;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Scoring
+// ------------------------------------------------------------------------------------------------
+
+struct ScoreParams {
+    const void *q;
+    const void *meta;
+    const int32_t *seq_len;
+    double *scores;
+    int hq, hkv, G, block, stride, nmax;
+};
+
+// Scores blocks [256 bx, 256 bx + 256) of unit u (one per lane).
+template <bool BF16, int D>
+__device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u) {
+    constexpr int BPL = 1;   // blocks per lane: one load per channel (2 bytes bf16, 4 bytes fp32)
+    __shared__ double s_qbar[D];
+    __shared__ int s_row[D];             // metadata row of channel i: 1 (max) when qbar_i >= 0, else 0 (min)
+    const int b = u / p.hkv, kvh = u - b * p.hkv;
+    if (threadIdx.x < D) {
+        // qbar_i = (sum_{g=0}^{G-1} q_{kvh G + g, i}) / G, summed in order from +0.0
+        double acc = 0.0;
+        for (int gq = 0; gq < p.G; ++gq) {
+            const size_t off = ((size_t)b * p.hq + (size_t)kvh * p.G + gq) * D + threadIdx.x;
+            const double x = BF16 ? (double)bf16_to_f32(((const uint16_t *)p.q)[off])
+                                  : (double)((const float *)p.q)[off];
+            acc = dadd(acc, x);
+        }
+        const double qb = acc / (double)p.G;
+        s_qbar[threadIdx.x] = qb;
+        s_row[threadIdx.x] = qb >= 0.0 ? 1 : 0;
+    }
+    __syncthreads();
+    const int slen = max(p.seq_len[b], 0);
+    const int nb = min((slen + p.block - 1) / p.block, p.nmax);
+    const int p0 = (bx * 256 + threadIdx.x) * BPL;
+    if (p0 >= nb) return;
+    // every channel's load is issued before the first is used: one memory round trip per thread.  The
+    // row (min or max) depends on the sign of qbar_i only, so the row address is wave-uniform (scalar)
+    // and each lane adds its own block offset.
+    // Buffer loads: the unit's metadata is one buffer resource (scalar base), the row offset a scalar
+    // and the lane's block offset the only vector operand, shared by all d loads.
+    constexpr int ES = BF16 ? 2 : 4;   // element size
+    const char *ubase = (const char *)p.meta + (size_t)u * D * 2 * p.stride * ES;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)ubase, (short)0, D * 2 * p.stride * ES, 0x00020000);
+    const int voff = p0 * ES;
+    uint32_t raw[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+        // qbar >= 0: the max term is qbar * mx (row 1); otherwise qbar * mn (row 0)
+        const int sgn = __builtin_amdgcn_readfirstlane(s_row[i]);
+        if constexpr (BF16)
+            raw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsrc, voff, (2 * i + sgn) * p.stride * ES, 0);
+        else
+            raw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, (2 * i + sgn) * p.stride * ES, 0);
+    }
+    double acc[BPL];
+#pragma unroll
+    for (int e = 0; e < BPL; ++e) acc[e] = 0.0;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+        // the accumulation is a sequential chain; a scheduling barrier every 16 channels lets the qbar
+        // reads run at most 16 channels ahead (hoisting all of them would hold 2 D doubles in registers)
+        const uint32_t r = raw[i];
+        const double qb = s_qbar[i];
+#pragma unroll
+        for (int e = 0; e < BPL; ++e) {
+            const double x = BF16 ? (double)bf16_to_f32((uint16_t)(r >> (16 * e))) : (double)__uint_as_float(r);
+            acc[e] = dadd(acc[e], dmul(qb, x));
+        }
+        if (i % 16 == 15) __builtin_amdgcn_sched_barrier(0);
+    }
+    double *out = p.scores + (size_t)u * p.nmax;
+#pragma unroll
+    for (int e = 0; e < BPL; ++e)
+        if (p0 + e < nb) out[p0 + e] = acc[e];
+}
+
+// ------------------------------------------------------------------------------------------------
+// Top-K + set difference
+// ------------------------------------------------------------------------------------------------
+
+struct TopkParams {
+    const double *scores;
+    const int32_t *seq_len;
+    const int32_t *p_idx;
+    const int32_t *p_cnt;
+    int32_t *a_idx;
+    int32_t *a_cnt;
+    int32_t *m_idx;
+    int32_t *m_cnt;
+    int hkv, block, nmax, topk, p_cap, a_cap, m_cap;
+};
+
+// Top-K of unit u's scores and M = A \ P, by a workgroup of TPB threads holding KPT keys each.
+template <int KPT, int TPB>
+__device__ __forceinline__ void topk_body(const TopkParams &p, int u) {
+    constexpr int W = TPB / 64;
+    __shared__ TopkSmem<W> sm;
+    __shared__ uint32_t s_pbits[TPB * KPT / 32];
+    const int b = u / p.hkv;
+    const int slen = p.seq_len[b];
+    const int nb = min((slen + p.block - 1) / p.block, p.nmax);
+    const bool want_m = p.m_idx != nullptr;
+    // the score loads go out first; the P bitmap is built while they are in flight
+    uint64_t key[KPT];
+    const int base = threadIdx.x * KPT;
+    const double *row = p.scores + (size_t)u * p.nmax;
+    double sv[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) sv[j] = base + j < nb ? row[base + j] : 0.0;
+    if (want_m) {
+        for (int i = threadIdx.x; i < TPB * KPT / 32; i += TPB) s_pbits[i] = 0u;
+        __syncthreads();
+        const int pc = min(max(p.p_cnt[u], 0), p.p_cap);
+        for (int i = threadIdx.x; i < pc; i += TPB) {
+            const int x = p.p_idx[(size_t)u * p.p_cap + i];
+            if (x >= 0 && x < nb) atomicOr(&s_pbits[x >> 5], 1u << (x & 31));
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = base + j < nb ? order_key(sv[j]) : 0ull;
+    const uint32_t sel = block_topk<KPT, W>(key, nb, p.topk, sm);
+    __syncthreads();   // P bitmap complete (and top-K scratch released)
+    uint32_t inm = 0;
+    if (want_m) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            if ((sel >> j & 1u) && !(s_pbits[(base + j) >> 5] >> ((base + j) & 31) & 1u)) inm |= 1u << j;
+    }
+    uint32_t total;
+    const uint32_t off = block_excl_scan((uint32_t)__popc(sel) | ((uint32_t)__popc(inm) << 16), sm, 1, total);
+    uint32_t oa = off & 0xffffu, om = off >> 16;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        if (sel >> j & 1u) p.a_idx[(size_t)u * p.a_cap + oa++] = base + j;
+        if (inm >> j & 1u) p.m_idx[(size_t)u * p.m_cap + om++] = base + j;
+    }
+    if (threadIdx.x == 0) {
+        p.a_cnt[u] = (int32_t)(total & 0xffffu);
+        if (want_m) p.m_cnt[u] = (int32_t)(total >> 16);
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// EMA update + prediction + top-|P|
+// ------------------------------------------------------------------------------------------------
+
+struct PredictParams {
+    const double *scores;
+    const int32_t *seq_len;
+    double *level;
+    double *trend;
+    int32_t *live;
+    int32_t *p_idx;
+    int32_t *p_cnt;
+    int hkv, block, nmax, budget, p_cap;
+    double alpha, beta, gamma;
+};
+
+// EMA update, prediction and top-|P| of unit u, by a workgroup of TPB threads holding KPT keys each.
+template <int KPT, int TPB>
+__device__ __forceinline__ void predict_body(const PredictParams &p, int u) {
+    constexpr int W = TPB / 64;
+    __shared__ TopkSmem<W> sm;
+    const int b = u / p.hkv;
+    const int slen = p.seq_len[b];
+    const int nb = min((slen + p.block - 1) / p.block, p.nmax);
+    const int live = min(max(p.live[u], 0), nb);
+    const double one_a = dsub(1.0, p.alpha);
+    const double one_b = dsub(1.0, p.beta);
+    const size_t ro = (size_t)u * p.nmax;
+    const int base = threadIdx.x * KPT;
+    uint64_t key[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int i = base + j;
+        key[j] = 0ull;
+        if (i < nb) {
+            // the state is loaded whether or not the block is live, so these loads do not wait for `live`
+            const double is = p.scores[ro + i];
+            const double l0 = p.level[ro + i], t0 = p.trend[ro + i];
+            double lv, tr;
+            if (i < live) {
+                // trend = beta (IS - level_old) + (1 - beta) trend_old;  level = alpha IS + (1 - alpha) level_old
+                tr = dadd(dmul(p.beta, dsub(is, l0)), dmul(one_b, t0));
+                lv = dadd(dmul(p.alpha, is), dmul(one_a, l0));
+            } else {
+                lv = is;      // a block seen for the first time starts at its score with no trend
+                tr = 0.0;
+            }
+            p.level[ro + i] = lv;
+            p.trend[ro + i] = tr;
+            key[j] = order_key(dadd(lv, dmul(p.gamma, tr)));   // prediction level + gamma trend
+        }
+    }
+    const uint32_t sel = block_topk<KPT, W>(key, nb, p.budget, sm);
+    uint32_t total;
+    const uint32_t off = block_excl_scan((uint32_t)__popc(sel), sm, 1, total);
+    uint32_t o = off;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        if (sel >> j & 1u) p.p_idx[(size_t)u * p.p_cap + o++] = base + j;
+    if (threadIdx.x == 0) {
+        p.p_cnt[u] = (int32_t)total;
+        p.live[u] = nb;
+    }
+}
+
+// Workgroup shape of the top-K kernels for rows of up to nmax keys: one wave per SIMD (256 threads) with
+// up to 8 keys each up to 2048 keys (the radix passes' cost is the per-wave work, so four busy SIMDs
+// with a few keys each beat many waves or one wave with many keys); 1024 threads with up to 32 keys
+// beyond that.
+void topk_shape(int nmax, int &tpb, int &kpt) {
+    tpb = nmax <= 128 ? 64 : nmax <= 2048 ? 256 : 1024;
+    kpt = 1;
+    while (kpt * tpb < nmax) kpt *= 2;
+}
+
+}  // namespace
+}  // namespace prr
+
+// back to the default (contraction allowed) for code that follows the include
+#pragma clang fp contract(fast)

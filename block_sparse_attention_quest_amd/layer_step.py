@@ -1,20 +1,26 @@
-"""One PRR decode layer step on three HIP streams (orchestration only; all compute is in libprr.so).
+"""One PRR decode layer step (orchestration only; all compute is in libprr.so).
 
-The speculative pass over the predicted set P runs on a side stream while Quest selection runs on the
-critical stream; repair waits for both.  The predictor needs only the selection's scores, so it runs on a
-third stream next to repair, off the critical path ([paper] §1 and Figure 1 flow, §3: speculation
-overlaps selection, repair handles M = A \\ P after it; [paper] §4.1 predictor and A.5: prediction is off
-the critical path).
+The method runs the speculative pass over the predicted set P concurrently with Quest selection, then
+repairs the state with the missed blocks M = A \\ P; the predictor needs only the selection's scores and
+is off the critical path ([paper] §1 and the Figure 1 flow, §3; [paper] §4.1 and A.5).
 
 Citations: [paper] "Predict, Reuse, and Repair: Accelerating Dynamic Sparse Attention for Long-Context
 LLM Decoding" (full paper text).
 
-Stream order per step (no host synchronisation, no device-to-host copy):
-  critical:  wait(e_pred: P^t written) -> record e_ready -> select(q^t, P^t) -> A^t, M^t, IS^t
-             -> record e_sel;  wait(e_spec) -> repair(M^t) -> O^t
-  side:      wait(e_ready) -> spec_attn(P^t) -> record e_spec   (submitted after select)
-  predictor: wait(e_sel) -> predict(IS^t) -> P^{t+1} (the other P buffer) -> record e_pred
-At the first step P is empty, so repair computes plain block-sparse attention over A.
+Two schedules of the same work, with identical results:
+
+* ``step`` (the default): one stream.  ``prr_select_spec`` runs scoring and the speculative pass in one
+  grid (their workgroups share the GPU, so the overlap happens inside the launch), the top-K follows,
+  then repair, then the predictor:
+      select_spec(q^t, P^t) -> A^t, M^t, IS^t, state  ->  repair(M^t) -> O^t  ->  predict(IS^t) -> P^{t+1}
+  On this GPU a dependency between two streams costs about 10 us from the producer's end to the
+  consumer's start, against about 1 us between kernels of one stream, so this is the fast schedule.
+* ``step_two_streams``: the pages' schedule on three streams (selection on the critical stream, the
+  speculative pass on a side stream, the predictor on a third), joined by events.  Kept to measure the
+  difference.
+
+Neither synchronises with the host or copies to it.  At the first step P is empty, so repair computes
+plain block-sparse attention over A.
 """
 from __future__ import annotations
 
@@ -28,20 +34,38 @@ from . import binding as bd
 
 @dataclass
 class StepTimers:
-    """Optional timing events, recorded on the stream each kernel runs on."""
+    """Optional timing events of ``step`` (all on the one stream); a field left None is not recorded."""
 
-    start: torch.cuda.Event
-    select_end: torch.cuda.Event
-    spec_start: torch.cuda.Event
-    spec_end: torch.cuda.Event
-    repair_start: torch.cuda.Event
-    repair_end: torch.cuda.Event
-    predict_start: torch.cuda.Event
-    predict_end: torch.cuda.Event
+    start: Optional[torch.cuda.Event]
+    select_spec_end: Optional[torch.cuda.Event]
+    repair_end: Optional[torch.cuda.Event]
+    predict_end: Optional[torch.cuda.Event]
 
     @staticmethod
     def make() -> "StepTimers":
-        return StepTimers(*[torch.cuda.Event(enable_timing=True) for _ in range(8)])
+        return StepTimers(*[torch.cuda.Event(enable_timing=True) for _ in range(4)])
+
+    @staticmethod
+    def lean() -> "StepTimers":
+        """Start and end of repair only (no event between the calls)."""
+        return StepTimers(torch.cuda.Event(enable_timing=True), None, torch.cuda.Event(enable_timing=True), None)
+
+
+@dataclass
+class TwoStreamTimers:
+    """Optional timing events of ``step_two_streams``, each on the stream its kernel runs on; a field left
+    None is not recorded."""
+
+    start: Optional[torch.cuda.Event]
+    select_end: Optional[torch.cuda.Event]
+    spec_start: Optional[torch.cuda.Event]
+    spec_end: Optional[torch.cuda.Event]
+    repair_start: Optional[torch.cuda.Event]
+    repair_end: Optional[torch.cuda.Event]
+
+    @staticmethod
+    def make() -> "TwoStreamTimers":
+        return TwoStreamTimers(*[torch.cuda.Event(enable_timing=True) for _ in range(6)])
 
 
 class PRRLayer:
@@ -49,9 +73,7 @@ class PRRLayer:
     block sets (P double-buffered), attention state and workspaces."""
 
     def __init__(self, kv: bd.KVCache, num_q_heads: int, block: int, topk: int, budget: int,
-                 ema=(0.6, 0.3, 0.5), scale: Optional[float] = None,
-                 side_stream: Optional[torch.cuda.Stream] = None,
-                 predict_stream: Optional[torch.cuda.Stream] = None):
+                 ema=(0.6, 0.3, 0.5), scale: Optional[float] = None):
         dev = kv.k.device
         self.kv = kv
         self.hq = num_q_heads
@@ -75,13 +97,7 @@ class PRRLayer:
         self.out = torch.zeros((B, num_q_heads, d), dtype=torch.float32, device=dev)
         self.ws_spec = bd.workspace_for(kv, num_q_heads, block, max(1, budget))
         self.ws_repair = bd.workspace_for(kv, num_q_heads, block, max(1, topk))
-        self.side = side_stream if side_stream is not None else torch.cuda.Stream(device=dev)
-        self.aux = predict_stream if predict_stream is not None else torch.cuda.Stream(device=dev)
-        self.e_ready = torch.cuda.Event()
-        self.e_spec = torch.cuda.Event()
-        self.e_sel = torch.cuda.Event()
-        self.e_pred = torch.cuda.Event()
-        self.e_pred.record(self.aux)
+        self._streams = None
 
     @property
     def P_cur(self) -> bd.BlockSet:
@@ -89,7 +105,8 @@ class PRRLayer:
 
     def reset(self):
         """Forget the predictor state (a fresh decode: the first step runs with P empty)."""
-        torch.cuda.current_stream().wait_event(self.e_pred)
+        if self._streams is not None:
+            torch.cuda.current_stream().wait_event(self._streams[3])
         self.level.zero_()
         self.trend.zero_()
         self.live.zero_()
@@ -98,43 +115,71 @@ class PRRLayer:
         self.cur = 0
 
     def step(self, q: torch.Tensor, timers: Optional[StepTimers] = None) -> torch.Tensor:
-        """Enqueue one layer step for queries q [B][Hq][d]; returns the normalised output tensor
-        (valid once the critical stream reaches it)."""
+        """Enqueue one layer step for queries q [B][Hq][d] on the current stream; returns the normalised
+        output tensor (valid once the stream reaches it)."""
+        s = torch.cuda.current_stream()
+        if self._streams is not None:
+            s.wait_event(self._streams[3])   # a previous two-stream step's predictor
+        P, Pn = self.P[self.cur], self.P[1 - self.cur]
+        if timers and timers.start:
+            timers.start.record(s)
+        bd.select_spec(q, self.kv, self.meta, self.block, self.topk, P, self.scale, scores=self.scores, A=self.A,
+                       M=self.M, out=self.state, ws=self.ws_spec, stream=s)
+        if timers and timers.select_spec_end:
+            timers.select_spec_end.record(s)
+        bd.repair(q, self.kv, self.block, self.M, self.scale, self.state, out=self.out, ws=self.ws_repair,
+                  stream=s)
+        if timers and timers.repair_end:
+            timers.repair_end.record(s)
+        bd.predict(self.scores, self.kv.seq_len, self.block, self.alpha, self.beta, self.gamma, self.budget,
+                   self.level, self.trend, self.live, P_next=Pn, stream=s)
+        if timers and timers.predict_end:
+            timers.predict_end.record(s)
+        self.cur = 1 - self.cur
+        return self.out
+
+    def step_two_streams(self, q: torch.Tensor, timers: Optional[TwoStreamTimers] = None) -> torch.Tensor:
+        """The same step on three streams joined by events (the pages' schedule):
+          critical:  wait(e_pred) -> record e_ready -> select -> record e_sel; wait(e_spec) -> repair
+          side:      wait(e_ready) -> spec_attn(P) -> record e_spec
+          predictor: wait(e_sel) -> predict -> record e_pred
+        """
         crit = torch.cuda.current_stream()
-        side, aux = self.side, self.aux
-        P = self.P[self.cur]
-        Pn = self.P[1 - self.cur]
-        if timers:
+        if self._streams is None:
+            dev = self.kv.k.device
+            e_pred = torch.cuda.Event()
+            aux = torch.cuda.Stream(device=dev)
+            e_pred.record(aux)
+            self._streams = (torch.cuda.Stream(device=dev), aux, (torch.cuda.Event(), torch.cuda.Event(),
+                                                                  torch.cuda.Event()), e_pred)
+        side, aux, (e_ready, e_sel, e_spec), e_pred = self._streams
+        P, Pn = self.P[self.cur], self.P[1 - self.cur]
+        if timers and timers.start:
             timers.start.record(crit)
-        crit.wait_event(self.e_pred)          # P^t written by the previous step's predictor
-        self.e_ready.record(crit)             # q, P^t and the previous repair's state are in place
-        side.wait_event(self.e_ready)
-        # selection is submitted first so that its workgroups are dispatched ahead of the speculative
-        # pass, which would otherwise fill every SIMD and push selection behind it
-        bd.select(q, self.kv, self.meta, self.block, self.topk, P=P, scores=self.scores, A=self.A,
-                  M=self.M, stream=crit)
-        self.e_sel.record(crit)
-        if timers:
+        crit.wait_event(e_pred)
+        e_ready.record(crit)
+        side.wait_event(e_ready)
+        bd.select(q, self.kv, self.meta, self.block, self.topk, P=P, scores=self.scores, A=self.A, M=self.M,
+                  stream=crit)
+        e_sel.record(crit)
+        if timers and timers.select_end:
             timers.select_end.record(crit)
+        if timers and timers.spec_start:
             timers.spec_start.record(side)
         bd.spec_attn(q, self.kv, self.block, P, self.scale, out=self.state, ws=self.ws_spec, stream=side)
-        if timers:
+        if timers and timers.spec_end:
             timers.spec_end.record(side)
-        self.e_spec.record(side)
-        aux.wait_event(self.e_sel)
-        if timers:
-            timers.predict_start.record(aux)
+        e_spec.record(side)
+        aux.wait_event(e_sel)
         bd.predict(self.scores, self.kv.seq_len, self.block, self.alpha, self.beta, self.gamma, self.budget,
                    self.level, self.trend, self.live, P_next=Pn, stream=aux)
-        if timers:
-            timers.predict_end.record(aux)
-        self.e_pred.record(aux)
-        crit.wait_event(self.e_spec)
-        if timers:
+        e_pred.record(aux)
+        crit.wait_event(e_spec)
+        if timers and timers.repair_start:
             timers.repair_start.record(crit)
         bd.repair(q, self.kv, self.block, self.M, self.scale, self.state, out=self.out, ws=self.ws_repair,
                   stream=crit)
-        if timers:
+        if timers and timers.repair_end:
             timers.repair_end.record(crit)
         self.cur = 1 - self.cur
         return self.out

@@ -125,6 +125,18 @@ prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv
                       int32_t block, int32_t topk, const prr_block_set *P, double *scores,
                       prr_block_set *A, prr_block_set *M, hipStream_t stream);
 
+/* Selection and the speculative pass over P together (the overlap of [paper] §1, Figure 1 flow, and §3:
+ * speculation over P runs concurrently with selection; the two only read P).  Computes exactly what
+ *     prr_select(q, num_q_heads, kv, meta, block, topk, P, scores, A, M) and
+ *     prr_spec_attn(q, num_q_heads, kv, block, P, scale, out, ws, ws_bytes)
+ * compute, as one grid whose workgroups do either part (bf16 caches; fp32 caches run the two calls in
+ * turn), followed by the top-K on the same stream.  P and M must be non-NULL; A->cap and M->cap >= topk;
+ * N_b <= 32768.  ws: prr_attn_workspace_bytes(..., P->cap), as for prr_spec_attn. */
+prr_status prr_select_spec(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
+                           int32_t block, int32_t topk, const prr_block_set *P, double *scores,
+                           prr_block_set *A, prr_block_set *M, float scale, prr_attn_state *out, void *ws,
+                           size_t ws_bytes, hipStream_t stream);
+
 /* EMA level/trend predictor, one decode step ([paper] §4.1; [blog] Eqs. (2)-(3)).
  * For every (b, kvh) with N_b = ceil(seq_len[b] / block) blocks and live[b][kvh] blocks that already
  * carry state: blocks p < live get

@@ -133,3 +133,27 @@ def test_calibrate_argument_errors(lib):
     assert call(n=5000) == 2
     assert call(ws=None) == 3
     assert call(wsb=need - 1) == 3
+
+
+def test_select_spec_argument_errors(lib):
+    kv = _kv()
+    A, P, M = _set(64), _set(64), _set(64)
+    st = _state()
+    need = lib.prr_attn_workspace_bytes(2, 32, 8, 128, 64, 64)
+    call = lambda q=1, meta=1, topk=64, P=P, A=A, M=M, out=st, ws=1, wsb=need, kv=kv, block=64: lib.prr_select_spec(
+        q, 32, ctypes.byref(kv), meta, block, topk, ctypes.byref(P) if P else None, 1,
+        ctypes.byref(A) if A else None, ctypes.byref(M) if M else None, 0.1,
+        ctypes.byref(out) if out else None, ws, wsb, None)
+    assert call(q=None) == 1
+    assert call(meta=None) == 1
+    assert call(P=None) == 1                      # P and M are required
+    assert call(M=None) == 1
+    assert call(A=None) == 1
+    assert call(out=None) == 1
+    assert call(topk=65) == 1                     # A and M caps too small
+    assert call(M=_set(10)) == 1
+    assert call(topk=-1) == 1
+    assert call(ws=None) == 3
+    assert call(wsb=need - 1) == 3
+    assert call(block=24) == 1
+    assert call(kv=_kv(max_pages=65536), block=16, wsb=lib.prr_attn_workspace_bytes(2, 32, 8, 128, 16, 64)) == 2

@@ -98,8 +98,7 @@ def test_llama3_8b_layer_32k():
         assert set(inp.planted[0, h].tolist()) <= set(a.tolist()), h   # planted blocks are selected
         P[0][h] = list(wl.make_spec_set(w, a, nb, w.spec_hit, w.spec_miss, salt=h))
     Pd = sets_to_device(P, w.topk)
-    scores2, A2, M = bd.select(inp.q[0], kv, meta, w.block, w.topk, P=Pd)
-    state = bd.spec_attn(inp.q[0], kv, w.block, Pd, w.scale)
+    scores2, A2, M, state = bd.select_spec(inp.q[0], kv, meta, w.block, w.topk, Pd, w.scale)
     spec_copy = state.clone()
     out = torch.empty_like(state.acc)
     bd.repair(inp.q[0], kv, w.block, M, w.scale, state, out=out)
@@ -113,8 +112,8 @@ def test_llama3_8b_layer_32k():
 
 
 def _trajectory(w, steps, units, ema):
-    """Run `steps` layer steps through PRRLayer (two streams, as bench.py does) and check sampled units
-    against the oracle's select / spec / repair / predict, step by step."""
+    """Run `steps` layer steps through PRRLayer (the single-stream step bench.py times) and check sampled
+    units against the oracle's select / spec / repair / predict, step by step."""
     inp = wl.make_inputs(w, "cuda")
     kv = device_kv(inp)
     layer = PRRLayer(kv, w.num_q_heads, w.block, w.topk, w.topk, ema=ema, scale=w.scale)
@@ -160,8 +159,7 @@ def test_ctx512k_paged_selection_and_repair():
         _, a, ometas[h] = _check_unit_selection(inp, 0, h, 0, meta, scores, A)
         P[0][h] = list(wl.make_spec_set(w, a, nb, w.spec_hit, w.spec_miss, salt=h))
     Pd = sets_to_device(P, w.topk)
-    scores2, A2, M = bd.select(inp.q[0], kv, meta, w.block, w.topk, P=Pd)
-    state = bd.spec_attn(inp.q[0], kv, w.block, Pd, w.scale)
+    scores2, A2, M, state = bd.select_spec(inp.q[0], kv, meta, w.block, w.topk, Pd, w.scale)
     spec_copy = state.clone()
     out = torch.empty_like(state.acc)
     bd.repair(inp.q[0], kv, w.block, M, w.scale, state, out=out)
@@ -183,3 +181,23 @@ def test_llama70b_share_calibrated_trajectory():
     assert j == int(np.argmax(H.cpu().numpy()))
     ema = tuple(float(x) for x in grid[j])
     _trajectory(wl.scaled(w, steps=3), 3, [(0, 0), (2, 6), (3, 3)], ema)
+
+
+def test_two_stream_schedule_matches_one_stream():
+    """The pages' three-stream schedule and the single-stream step give the same sets, predictor state
+    and output, bit for bit, over a few steps of the 128K batch-8 trajectory (reduced to 32K)."""
+    w = wl.scaled(wl.C3, name="c3_32k", context=32768, steps=5)
+    inp = wl.make_inputs(w, "cuda")
+    kv = device_kv(inp)
+    a = PRRLayer(kv, w.num_q_heads, w.block, w.topk, w.topk, ema=w.ema, scale=w.scale)
+    b = PRRLayer(kv, w.num_q_heads, w.block, w.topk, w.topk, ema=w.ema, scale=w.scale)
+    for t in range(w.steps):
+        oa = a.step(inp.q[t]).clone()
+        ob = b.step_two_streams(inp.q[t])
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob), t
+        assert a.A.lists() == b.A.lists() and a.M.lists() == b.M.lists(), t
+        assert a.P_cur.lists() == b.P_cur.lists(), t
+        assert torch.equal(a.level, b.level) and torch.equal(a.trend, b.trend), t
+        for name in ("acc", "l", "m"):
+            assert torch.equal(getattr(a.state, name), getattr(b.state, name)), (t, name)

@@ -136,6 +136,26 @@ def test_spec_then_repair_equals_union(small_case):
         assert np.max(np.abs(o[b, h] - st.out)) <= 5e-3
 
 
+def test_select_spec_matches_separate_calls(small_case):
+    """The fused launch computes what prr_select and prr_spec_attn compute: scores, A and M bit for bit,
+    the state bit for bit (same chunking and merge order) and within tolerance of the oracle."""
+    w, inp, q, kv = small_case
+    rng = np.random.default_rng(5)
+    P, _ = _random_sets(w, rng, [(5, 0), (0, 0), (7, 0), (1, 0), (11, 0)])
+    dkv = device_kv(inp)
+    meta = bd.build_meta(dkv, w.block)
+    Pd = sets_to_device(P, 16)
+    for kk in (0, 3, 8, 64):
+        scores, A, M = bd.select(inp.q[0], dkv, meta, w.block, kk, P=Pd)
+        state = bd.spec_attn(inp.q[0], dkv, w.block, Pd, w.scale)
+        fs, fA, fM, fstate = bd.select_spec(inp.q[0], dkv, meta, w.block, kk, Pd, w.scale)
+        assert torch.equal(fs, scores)
+        assert fA.lists() == A.lists() and fM.lists() == M.lists()
+        for name in ("acc", "l", "m"):
+            assert torch.equal(getattr(fstate, name), getattr(state, name)), name
+    assert_heads(fstate, orc.spec_states(q, kv, w.block, P, w.scale), "fused spec")
+
+
 def test_empty_missed_set_leaves_state_bitwise(small_case):
     w, inp, q, kv = small_case
     rng = np.random.default_rng(2)
