@@ -53,7 +53,7 @@ def parse_args():
     ap.add_argument("--config", default="ctx128k_b8_64steps")
     ap.add_argument("--flush-mib", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-units", type=int, default=32, help="(sequence, kv head) units in the CPU sample")
+    ap.add_argument("--cpu-units", type=int, default=64, help="(sequence, kv head) units in the CPU sample")
     ap.add_argument("--cpu-steps", type=int, default=0, help="decode steps in the CPU sample (0: all timed)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size (HBM counter calibration under rocprofv3)")

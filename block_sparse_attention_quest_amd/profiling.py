@@ -25,9 +25,12 @@ SPEC_KERNEL = "attn_spec_bf16"
 
 
 def kernel_source_hash() -> str:
-    """sha256 (first 16 hex digits) of the attention kernel source."""
-    with open(os.path.join(PKG, "csrc", "attn.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 (first 16 hex digits) of the attention kernel source (device code and kernel file)."""
+    h = hashlib.sha256()
+    for name in ("attn_core.hpp", "attn.hip"):
+        with open(os.path.join(PKG, "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _short(name: str) -> str:
