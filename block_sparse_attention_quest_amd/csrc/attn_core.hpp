@@ -603,7 +603,9 @@ __device__ __forceinline__ void attn_body(const AttnParams &p, int wg, int nwg) 
 }
 
 
-size_t counters_bytes(int units) { return ((size_t)units * 4 + 255) / 256 * 256; }
+// Workspace counters: one chunk-arrival counter per unit (attention), then one scoring-arrival counter
+// per unit (the fused selection + speculation launch), padded to 256 bytes.
+size_t counters_bytes(int units) { return ((size_t)units * 8 + 255) / 256 * 256; }
 
 // Partials kept per launch: every chunk of every unit at the smallest chunk size.
 size_t max_chunks(int units, int block, int cap) {

@@ -21,7 +21,8 @@ struct KvDesc {
     bool bf16;
 };
 
-// Attention workspace: [units] uint32 counters, padded to 256 B, then one partial state per chunk.
+// Attention workspace: 2 x [units] uint32 counters (chunk arrivals, scoring arrivals), padded to 256 B,
+// then one partial state per chunk.
 size_t attn_workspace_bytes(int batch, int hq, int hkv, int d, int block, int cap);
 
 hipError_t launch_attn(const KvDesc &kv, const void *q, int hq, int block, const int32_t *idx,

@@ -170,7 +170,8 @@ hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *me
     sp.block = block;
     sp.stride = stride;
     sp.nmax = nmax;
-    const dim3 sgrid((nmax + 255) / 256, units);   // one block per lane
+    const int bpw = 256 * (kv.bf16 ? kScoreBPL<true> : kScoreBPL<false>);   // blocks per workgroup
+    const dim3 sgrid((nmax + bpw - 1) / bpw, units);
     if (kv.bf16) {
         if (kv.d == 128) score_kernel<true, 128><<<sgrid, 256, 0, stream>>>(sp);
         else score_kernel<true, 64><<<sgrid, 256, 0, stream>>>(sp);

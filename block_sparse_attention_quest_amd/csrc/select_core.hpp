@@ -294,10 +294,16 @@ struct ScoreParams {
     int hq, hkv, G, block, stride, nmax;
 };
 
-// Scores blocks [256 bx, 256 bx + 256) of unit u (one per lane).
-template <bool BF16, int D>
+// Blocks per lane of the scoring workgroups: two for bf16 metadata (one 4-byte load per channel covers
+// both), one for fp32.
+template <bool BF16>
+constexpr int kScoreBPL = BF16 ? 2 : 1;
+
+// Scores blocks [256 BPL bx, 256 BPL (bx + 1)) of unit u (BPL consecutive blocks per lane).  COHERENT:
+// the scores are stored with device-scope stores, for a reader on another XCD within the same launch.
+template <bool BF16, int D, bool COHERENT = false>
 __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u) {
-    constexpr int BPL = 1;   // blocks per lane: one load per channel (2 bytes bf16, 4 bytes fp32)
+    constexpr int BPL = kScoreBPL<BF16>;   // one 4-byte load per channel
     __shared__ double s_qbar[D];
     __shared__ int s_row[D];             // metadata row of channel i: 1 (max) when qbar_i >= 0, else 0 (min)
     const int b = u / p.hkv, kvh = u - b * p.hkv;
@@ -334,7 +340,9 @@ __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u) 
     for (int i = 0; i < D; ++i) {
         // qbar >= 0: the max term is qbar * mx (row 1); otherwise qbar * mn (row 0)
         const int sgn = __builtin_amdgcn_readfirstlane(s_row[i]);
-        if constexpr (BF16)
+        if constexpr (BF16 && BPL == 2)
+            raw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, (2 * i + sgn) * p.stride * ES, 0);
+        else if constexpr (BF16)
             raw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsrc, voff, (2 * i + sgn) * p.stride * ES, 0);
         else
             raw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, (2 * i + sgn) * p.stride * ES, 0);
@@ -353,12 +361,20 @@ __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u) 
             const double x = BF16 ? (double)bf16_to_f32((uint16_t)(r >> (16 * e))) : (double)__uint_as_float(r);
             acc[e] = dadd(acc[e], dmul(qb, x));
         }
+        // the chains of a lane's blocks advance together, channel by channel (otherwise the compiler runs
+        // one chain to the end first and parks the other's operands in spare registers)
+        if constexpr (BPL == 2) asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));
         if (i % 16 == 15) __builtin_amdgcn_sched_barrier(0);
     }
     double *out = p.scores + (size_t)u * p.nmax;
 #pragma unroll
     for (int e = 0; e < BPL; ++e)
-        if (p0 + e < nb) out[p0 + e] = acc[e];
+        if (p0 + e < nb) {
+            if constexpr (COHERENT)
+                __hip_atomic_store(&out[p0 + e], acc[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+                out[p0 + e] = acc[e];
+        }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -378,7 +394,8 @@ struct TopkParams {
 };
 
 // Top-K of unit u's scores and M = A \ P, by a workgroup of TPB threads holding KPT keys each.
-template <int KPT, int TPB>
+// COHERENT: the scores are read with device-scope loads (written by other workgroups of the same launch).
+template <int KPT, int TPB, bool COHERENT = false>
 __device__ __forceinline__ void topk_body(const TopkParams &p, int u) {
     constexpr int W = TPB / 64;
     __shared__ TopkSmem<W> sm;
@@ -393,7 +410,12 @@ __device__ __forceinline__ void topk_body(const TopkParams &p, int u) {
     const double *row = p.scores + (size_t)u * p.nmax;
     double sv[KPT];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) sv[j] = base + j < nb ? row[base + j] : 0.0;
+    for (int j = 0; j < KPT; ++j) {
+        if constexpr (COHERENT)
+            sv[j] = base + j < nb ? __hip_atomic_load(&row[base + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0;
+        else
+            sv[j] = base + j < nb ? row[base + j] : 0.0;
+    }
     if (want_m) {
         for (int i = threadIdx.x; i < TPB * KPT / 32; i += TPB) s_pbits[i] = 0u;
         __syncthreads();

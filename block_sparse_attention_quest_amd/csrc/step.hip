@@ -8,12 +8,18 @@
 // Figure 1 flow, §3): the two only read P and are independent.  On this GPU a dependency between two
 // streams costs about 10 us from the producer's end to the consumer's start, while kernels on one
 // stream follow each other about 1 us apart, so the overlap is made inside one grid instead: the first
-// workgroups run the speculative chunks (the attention kernels' chunk walk over n_spec workgroups),
-// the rest score blocks (one workgroup per 256 blocks of a unit).  Dispatch follows the workgroup
-// index, so the speculative workgroups are resident first, about one per CU, and the scoring
-// workgroups stream through the remaining slots.  Both parts are HBM-bound; their prologues and tails
-// overlap each other's streaming.  The top-K (with M = A \ P) follows as its own kernel on the same
-// stream.
+// workgroups score blocks (one workgroup per 512 blocks of a unit), the rest run the speculative chunks
+// (the attention kernels' chunk walk over n_spec workgroups).  Dispatch follows the workgroup index, so
+// the scoring workgroups issue their loads first: the memory system serves them ahead of the
+// speculative stream, selection finishes early and its top-K runs under the speculative pass, which is
+// the longer of the two.  At 128K, batch 8 the grid is 256 scoring + 256 speculative workgroups: all of
+// them resident at once (two per CU).
+//
+// Top-K (with M = A \ P).  When a unit has at most 2048 blocks, the last scoring workgroup of the unit
+// to finish (a device-scope arrival counter; nobody waits) runs the unit's top-K with the same 256
+// threads, so the top-K of most units overlaps the speculative pass.  Scores are stored and read with
+// device-scope accesses, which are coherent across the XCDs' L2s.  Larger units take the separate
+// top-K kernel after the launch.
 
 #include "select_core.hpp"
 #include "attn_core.hpp"
@@ -21,17 +27,34 @@
 namespace prr {
 namespace {
 
-// Workgroups [0, n_spec) run the speculative pass; workgroup n_spec + s scores blocks
-// [256 (s mod nsx), +256) of unit s / nsx.  Register use is the attention part's (two waves per SIMD).
-template <int D>
+// Workgroup s < nsx * units scores blocks [512 (s mod nsx), +512) of unit s / nsx and, if it is the
+// unit's last to finish and KPT > 0, runs the unit's top-K (KPT keys per thread, 256 KPT >= the unit's
+// block count); the remaining n_spec workgroups run the speculative pass.  Register use is the
+// attention part's (two waves per SIMD).
+template <int D, int KPT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void select_spec_kernel(
-    AttnParams ap, ScoreParams sp, int n_spec, int nsx) {
-    if ((int)blockIdx.x < n_spec) {
-        attn_body<true, D, false>(ap, blockIdx.x, n_spec);
+    AttnParams ap, ScoreParams sp, TopkParams tp, uint32_t *arrivals, int n_score, int nsx) {
+    if ((int)blockIdx.x >= n_score) {
+        attn_body<true, D, false>(ap, (int)blockIdx.x - n_score, (int)gridDim.x - n_score);
         return;
     }
-    const int s = (int)blockIdx.x - n_spec;
-    score_body<true, D>(sp, s % nsx, s / nsx);
+    const int s = (int)blockIdx.x;
+    const int u = s / nsx;
+    score_body<true, D, KPT != 0>(sp, s - u * nsx, u);
+    if constexpr (KPT != 0) {
+        __shared__ int s_last;
+        // this workgroup's score stores are complete before its arrival is counted
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t prev = __hip_atomic_fetch_add(&arrivals[u], 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            s_last = prev == (uint32_t)(nsx - 1);
+            if (s_last) __hip_atomic_store(&arrivals[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (s_last) topk_body<KPT, 256, true>(tp, u);
+    }
 }
 
 }  // namespace
@@ -61,14 +84,38 @@ hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const voi
     sp.block = block;
     sp.stride = stride;
     sp.nmax = nmax;
+    TopkParams tp;
+    tp.scores = scores;
+    tp.seq_len = kv.seq_len;
+    tp.p_idx = p_idx;
+    tp.p_cnt = p_cnt;
+    tp.a_idx = a_idx;
+    tp.a_cnt = a_cnt;
+    tp.m_idx = m_idx;
+    tp.m_cnt = m_cnt;
+    tp.hkv = kv.hkv;
+    tp.block = block;
+    tp.nmax = nmax;
+    tp.topk = topk;
+    tp.p_cap = p_cap;
+    tp.a_cap = a_cap;
+    tp.m_cap = m_cap;
     const int units = kv.batch * kv.hkv;
-    const int nsx = (nmax + 255) / 256;
+    uint32_t *arrivals = (uint32_t *)ws + units;   // the scoring-arrival counters of the workspace
+    const int nsx = (nmax + 256 * kScoreBPL<true> - 1) / (256 * kScoreBPL<true>);
     const long grid = (long)n_spec + (long)nsx * units;
     if (grid > 0x7fffffffL) return hipErrorInvalidValue;
-    if (kv.d == 128) select_spec_kernel<128><<<(int)grid, 256, 0, stream>>>(ap, sp, n_spec, nsx);
-    else select_spec_kernel<64><<<(int)grid, 256, 0, stream>>>(ap, sp, n_spec, nsx);
+    // keys per thread of the fused top-K (0: the unit is too large; the top-K kernel follows)
+    const int kpt = nmax <= 256 ? 1 : nmax <= 512 ? 2 : nmax <= 1024 ? 4 : nmax <= 2048 ? 8 : 0;
+#define PRR_SS(DD, K)                                                                                    \
+    if (kv.d == DD && kpt == K) {                                                                        \
+        select_spec_kernel<DD, K><<<(int)grid, 256, 0, stream>>>(ap, sp, tp, arrivals, nsx * units, nsx); \
+    } else
+    PRR_SS(128, 0) PRR_SS(128, 1) PRR_SS(128, 2) PRR_SS(128, 4) PRR_SS(128, 8)
+    PRR_SS(64, 0) PRR_SS(64, 1) PRR_SS(64, 2) PRR_SS(64, 4) PRR_SS(64, 8) { return hipErrorInvalidValue; }
+#undef PRR_SS
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || kpt != 0) return e;
     return launch_topk(kv, block, nmax, topk, scores, p_idx, p_cnt, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt,
                        m_cap, stream);
 }

@@ -95,7 +95,8 @@ int32_t prr_meta_stride(const prr_kv_cache *kv, int32_t block);
 /* Bytes of block metadata: batch * num_kv_heads * head_dim * 2 * prr_meta_stride * sizeof(elem). */
 size_t prr_meta_bytes(const prr_kv_cache *kv, int32_t block);
 
-/* Workspace bytes needed by prr_spec_attn / prr_repair for sets of capacity `cap` (blocks). */
+/* Workspace bytes needed by prr_spec_attn / prr_repair / prr_select_spec for sets of capacity `cap`
+ * (blocks): arrival counters (per (sequence, kv head) unit) and one partial attention state per chunk. */
 size_t prr_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block, int32_t cap);
 
