@@ -6,16 +6,18 @@
 namespace prr {
 namespace {
 
-// bf16 (the streaming path) is held to 256 registers so two waves share each SIMD; the fp32 variant
-// (exact-input checks) may use more.
+// bf16 speculation is held to 256 registers so two waves share each SIMD (in the fused launch the second
+// belongs to selection), with two tiles in flight per wave.  Repair runs alone: one wave per SIMD with
+// up to 512 registers and four tiles in flight, so a wave's share of a repair chunk is requested in one
+// go.  The fp32 variants (exact-input checks) may use more registers.
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_spec_bf16(AttnParams p) {
-    attn_body<true, D, false>(p, blockIdx.x, gridDim.x);
+    attn_body<true, D, false, 2>(p, blockIdx.x, gridDim.x);
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_repair_bf16(AttnParams p) {
-    attn_body<true, D, true>(p, blockIdx.x, gridDim.x);
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1))) void attn_repair_bf16(AttnParams p) {
+    attn_body<true, D, true, 4>(p, blockIdx.x, gridDim.x);
 }
 
 template <int D>

@@ -253,13 +253,13 @@ __device__ __forceinline__ void compute_tile(TileB<D> &t, const bf16x8 (&qop)[D 
 }
 
 // Walk nt bf16 tiles (tile t = pages 2t and 2t + 1 of the wave list, held by lanes 2t and 2t + 1 of
-// pg) with the next tile's loads in flight.  The tile count is padded to an even number >= 2 (padding
-// pages are masked and re-read cached addresses), so the steady-state loop issues both of its loads
-// unconditionally: every path into the loop header then has the same loads outstanding and the
-// compiler's wait counts keep one tile in flight while the other is multiplied.  The loop is not
-// unrolled, so register use does not depend on the tile count.  q is loaded first so that the first
-// tile waits for q and its own loads only.
-template <int D>
+// pg) with NBUF tiles in flight: while one is multiplied, the next NBUF - 1 are loading.  The tile count
+// is padded to a multiple of NBUF (padding pages are masked and re-read cached addresses), so the
+// steady-state loop issues all of its loads unconditionally: every path into the loop header then has
+// the same loads outstanding and the compiler's wait counts keep the other tiles in flight while one is
+// multiplied.  The loop is not unrolled, so register use does not depend on the tile count.  q is loaded
+// first so that the first tile waits for q and its own loads only.
+template <int D, int NBUF>
 __device__ __forceinline__ void wave_pass_bf16(const AttnParams &p, size_t head0, int kvh, int j, int g,
                                                LanePage pg, int nt, WaveState<D> &st) {
     const size_t stride = (size_t)p.hkv * kPage * D;   // elements per physical page
@@ -275,24 +275,25 @@ __device__ __forceinline__ void wave_pass_bf16(const AttnParams &p, size_t head0
     auto comp = [&](TileB<D> &tb, int t) {
         compute_tile<D>(tb, qop, st, lane_val(pg.vt, 2 * t), lane_val(pg.vt, 2 * t + 1), p.c2, g);
     };
-    const int nte = (nt + 1) & ~1;
-    TileB<D> buf[2];
-    load(buf[0], 0);
-    load(buf[1], 1);
+    const int nte = (nt + NBUF - 1) / NBUF * NBUF;   // <= 32: pages 2t, 2t + 1 stay below lane 64
+    TileB<D> buf[NBUF];
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) load(buf[b], b);
     if (j >= p.G) {
 #pragma unroll
         for (int s = 0; s < D / 32; ++s) qop[s] = bf16x8{};
     }
     int t = 0;
 #pragma unroll 1
-    for (; t + 2 < nte; t += 2) {
-        comp(buf[0], t);
-        load(buf[0], t + 2);
-        comp(buf[1], t + 1);
-        load(buf[1], t + 3);
+    for (; t + NBUF < nte; t += NBUF) {
+#pragma unroll
+        for (int b = 0; b < NBUF; ++b) {
+            comp(buf[b], t + b);
+            load(buf[b], t + NBUF + b);
+        }
     }
-    comp(buf[0], t);
-    comp(buf[1], t + 1);
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) comp(buf[b], t + b);
 }
 
 // ---- fp32 tiles: 16 tokens (1 page) ----
@@ -463,7 +464,7 @@ __device__ __forceinline__ void merge_partials(const AttnParams &p, const float 
     }
 }
 
-template <bool BF16, int D, bool REPAIR>
+template <bool BF16, int D, bool REPAIR, int NBUF = 2>
 __device__ __forceinline__ void attn_body(const AttnParams &p, int wg, int nwg) {
     constexpr int DP = D + 4;  // padded LDS row
     __shared__ float sm_acc[kWaves][16 * DP];
@@ -522,7 +523,7 @@ __device__ __forceinline__ void attn_body(const AttnParams &p, int wg, int nwg) 
         if (wbeg < wend) {
             const LanePage pg = page_finish(p, look, wbeg, wend, slen);
             const int nw = wend - wbeg;   // pages of this wave, 1 .. pw
-            if constexpr (BF16) wave_pass_bf16<D>(p, head0, kvh, j, g, pg, (nw + 1) / 2, st);
+            if constexpr (BF16) wave_pass_bf16<D, NBUF>(p, head0, kvh, j, g, pg, (nw + 1) / 2, st);
             else wave_pass_f32<D>(p, head0, kvh, j, g, pg, nw, st);
         }
         // wave state -> LDS (lane (j, g) holds channels 16 cb + 4 g + i of query j)
