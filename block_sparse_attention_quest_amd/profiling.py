@@ -58,7 +58,7 @@ def stats_table(path: str, top: int = 16) -> str:
     return "\n".join(out)
 
 
-def trace_averages(path: str, names=("attn_spec_bf16", "attn_repair_bf16")) -> str:
+def trace_averages(path: str, names=("attn_spec_bf16", "attn_repair_bf16", "select_spec_kernel")) -> str:
     """Average duration of each named kernel per stream over its launches that did work: launches
     shorter than a fifth of the kernel's longest (warm-up calls over empty sets) are left out.  The
     stream that also runs the cache-flush reductions is the one bench.py times kernels alone on; the
@@ -96,7 +96,10 @@ def _per_dispatch(path: str, counter: str) -> dict:
     return out
 
 
-def hbm_summary(fetch_csv: str, write_csv: str, copy_mib: int) -> dict:
+def hbm_summary(fetch_csv: str, write_csv: str, copy_mib: int, kernel: str = None) -> dict:
+    """HBM bytes per launch of `kernel` (default: the speculative-attention kernel) from FETCH_SIZE and
+    WRITE_SIZE, each scaled by its reading for the probe copy of copy_mib MiB in the same run."""
+    kernel = kernel or SPEC_KERNEL
     fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
     write = _per_dispatch(write_csv, "WRITE_SIZE")
     # the probe copy: the copy kernel with the largest write, matched by dispatch id across the runs
@@ -108,14 +111,23 @@ def hbm_summary(fetch_csv: str, write_csv: str, copy_mib: int) -> dict:
     known = copy_mib * 1024.0   # KiB read and written by the probe copy
     f_scale = known / copy_fetch
     w_scale = known / copy_write
-    spec = [(d, f, write[d][1]) for d, (n, f) in sorted(fetch.items()) if SPEC_KERNEL in n and d in write]
-    top = max(f for _, f, _ in spec)
-    spec = [x for x in spec if x[1] >= 0.1 * top]   # launches over an empty set (warm-up) carry no K/V
-    per_launch = [(f * f_scale + wv * w_scale) * 1024.0 for _, f, wv in spec]
-    return {"spec_dispatches": len(spec), "fetch_kib_mean": statistics.mean(f for _, f, _ in spec),
-            "write_kib_mean": statistics.mean(wv for _, _, wv in spec), "copy_fetch_kib": copy_fetch,
+    sel = [(d, f, write[d][1]) for d, (n, f) in sorted(fetch.items()) if kernel in n and d in write]
+    if not sel:
+        return None
+    top = max(f for _, f, _ in sel)
+    sel = [x for x in sel if x[1] >= 0.1 * top]   # launches over an empty set (warm-up) carry no K/V
+    per_launch = [(f * f_scale + wv * w_scale) * 1024.0 for _, f, wv in sel]
+    # the median: a few launches of a run work on other sets (the first decode step has P empty, so its
+    # repair covers all of A and its speculative part is empty)
+    return {"spec_dispatches": len(sel), "fetch_kib_mean": statistics.median(f for _, f, _ in sel),
+            "write_kib_mean": statistics.median(wv for _, _, wv in sel), "copy_fetch_kib": copy_fetch,
             "copy_write_kib": copy_write, "fetch_scale": f_scale, "write_scale": w_scale,
-            "hbm_bytes_per_launch": statistics.mean(per_launch)}
+            "hbm_bytes_per_launch": statistics.median(per_launch)}
+
+
+# Other kernels reported beside the speculative pass: name, algorithmic bytes per launch at the
+# 128K batch-8 workload (None where it depends on the step's sets).
+OTHER_KERNELS = (("attn_repair_bf16", None), ("select_spec_kernel", None), ("score_kernel", None))
 
 
 def main(argv):
@@ -140,13 +152,20 @@ def main(argv):
                  f"- kernel: `{SPEC_KERNEL}<128>`",
                  f"- kernel_source_sha256: `{kernel_source_hash()}`",
                  f"- spec_dispatches: {s['spec_dispatches']}",
-                 f"- fetch_kib_per_dispatch_mean: {s['fetch_kib_mean']:.1f}",
-                 f"- write_kib_per_dispatch_mean: {s['write_kib_mean']:.1f}",
+                 f"- fetch_kib_per_dispatch_median: {s['fetch_kib_mean']:.1f}",
+                 f"- write_kib_per_dispatch_median: {s['write_kib_mean']:.1f}",
                  f"- copy_fetch_kib: {s['copy_fetch_kib']:.1f}",
                  f"- copy_write_kib: {s['copy_write_kib']:.1f}",
                  f"- fetch_scale: {s['fetch_scale']:.4f}",
                  f"- write_scale: {s['write_scale']:.4f}",
-                 f"- hbm_bytes_per_launch: {s['hbm_bytes_per_launch']:.0f}", ""]
+                 f"- hbm_bytes_per_launch: {s['hbm_bytes_per_launch']:.0f}", "",
+                 "Other kernels of the same runs (same scaling; launches that did work):", "",
+                 "| kernel | dispatches | HBM bytes per launch, median (read + write) |", "|---|---|---|"]
+        for name, _ in OTHER_KERNELS:
+            o = hbm_summary(fetch_csv, write_csv, copy_mib, name)
+            if o:
+                lines.append(f"| `{name}` | {o['spec_dispatches']} | {o['hbm_bytes_per_launch']:.0f} |")
+        lines.append("")
         open(out, "w").write("\n".join(lines))
         print("\n".join(lines))
     else:
