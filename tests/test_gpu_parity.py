@@ -299,3 +299,44 @@ def test_predictor_trajectory_bit_exact():
             assert gP[b][h] == list(pn), (t, b, h)
         P = Pn
     assert live.cpu().numpy().tolist() == [[-(-l // w.block)] * H for l in lens]
+
+
+@pytest.mark.parametrize("nblocks", [300, 900, 2048, 2049])
+def test_select_spec_fused_topk_shapes(nblocks):
+    """The fused launch's top-K runs in the last scoring workgroup with 1, 2, 4 or 8 keys per thread
+    (units of up to 256, 512, 1024, 2048 blocks) and falls back to the separate top-K kernel beyond
+    2048 blocks: every shape against the separate calls (bit for bit) and the oracle's scores and sets."""
+    lens = [nblocks * 16, nblocks * 16 - 37]
+    w = wl.Workload(f"fused_{nblocks}", 2, 8, 2, 64, max(lens), 16, 40, "bf16", seed=900 + nblocks,
+                    seq_lens=lens)
+    inp = wl.make_inputs(w, "cuda")
+    q, kv = oracle_view(inp)
+    q = q[0]
+    dkv = device_kv(inp)
+    meta = bd.build_meta(dkv, w.block)
+    rng = np.random.default_rng(nblocks)
+    P, _ = _random_sets(w, rng, [(30, 0), (0, 0), (40, 0), (7, 0)])
+    Pd = sets_to_device(P, 48)
+    scores, A, M = bd.select(inp.q[0], dkv, meta, w.block, w.topk, P=Pd)
+    state = bd.spec_attn(inp.q[0], dkv, w.block, Pd, w.scale)
+    fs, fA, fM, fstate = bd.select_spec(inp.q[0], dkv, meta, w.block, w.topk, Pd, w.scale)
+    # a second call on the same workspace: the arrival counters were left at zero
+    ws = bd.workspace_for(dkv, w.num_q_heads, w.block, Pd.cap)
+    for _ in range(2):
+        fs2, fA2, fM2, fstate2 = bd.select_spec(inp.q[0], dkv, meta, w.block, w.topk, Pd, w.scale, ws=ws)
+        assert fA2.lists() == A.lists() and fM2.lists() == M.lists()
+    assert torch.equal(fs, scores) and torch.equal(fs2, scores)
+    assert fA.lists() == A.lists() and fM.lists() == M.lists()
+    for name in ("acc", "l", "m"):
+        assert torch.equal(getattr(fstate, name), getattr(state, name)), name
+    ometa = orc.build_meta(kv, w.block, w.num_kv_heads)
+    osc, oA, _ = orc.select(q, ometa, w.group, w.topk)
+    gs = fs.cpu().numpy()
+    got_a, got_m = fA.lists(), fM.lists()
+    for b in range(w.batch):
+        nb = w.blocks_of(b)
+        for h in range(w.num_kv_heads):
+            assert np.array_equal(gs[b, h, :nb], osc[b][h]), (b, h)
+            assert got_a[b][h] == list(oA[b][h]), (b, h)
+            assert got_m[b][h] == list(orc.set_minus(oA[b][h], P[b][h])), (b, h)
+    assert_heads(fstate, orc.spec_states(q, kv, w.block, P, w.scale), "fused spec")
