@@ -55,6 +55,10 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=64, help="(sequence, kv head) units in the CPU sample")
     ap.add_argument("--cpu-steps", type=int, default=0, help="decode steps in the CPU sample (0: all timed)")
+    ap.add_argument("--delta-sweep", default="",
+                    help="comma-separated speculation budgets |P| = delta K to time as extra layer steps "
+                         "(e.g. 1,1.25,1.5,2); empty: none")
+    ap.add_argument("--delta-steps", type=int, default=24, help="decode steps timed per delta")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size (HBM counter calibration under rocprofv3)")
     return ap.parse_args()
@@ -139,6 +143,49 @@ def cpu_baseline(inp, w, units, steps):
         "us_per_unit_step_all": round(t_all / max(1, n_unit_steps) * 1e6, 1),
         "cpu_count_visible": len(os.sched_getaffinity(0)),
     }
+
+
+def delta_sweep(args, w, inp, kv, meta, flush, ev):
+    """Layer-step time against the speculation budget |P| = delta K (the pages' critical-path-aware budget):
+    for each delta, a fresh trajectory (step 0 untimed), then `delta_steps` lean one-stream steps."""
+    import numpy as np
+    import torch
+
+    from block_sparse_attention_quest_amd.layer_step import PRRLayer, StepTimers
+
+    out = []
+    n = min(args.delta_steps, w.steps - 1)
+    for d in [float(x) for x in args.delta_sweep.split(",") if x.strip()]:
+        budget = max(1, int(round(d * w.topk)))
+        L = PRRLayer(kv, w.num_q_heads, w.block, w.topk, budget, ema=w.ema, scale=w.scale)
+        for t in range(3):
+            L.step(inp.q[t])
+        torch.cuda.synchronize()
+        L.reset()
+        L.step(inp.q[0])
+        torch.cuda.synchronize()
+        times, hits, missed, pc = [], [], [], []
+        for i in range(n):
+            P = L.P_cur
+            flush()
+            tm = StepTimers.lean()
+            L.step(inp.q[1 + i], tm)
+            torch.cuda.synchronize()
+            times.append(tm.start.elapsed_time(tm.repair_end) * 1e3)
+            a = L.A.idx.cpu().numpy()
+            p_idx, p_cnt = P.idx.cpu().numpy(), P.count.cpu().numpy()
+            mc = L.M.count.cpu().numpy()
+            for b in range(w.batch):
+                for h in range(w.num_kv_heads):
+                    hits.append(len(set(a[b, h].tolist()) & set(p_idx[b, h, :p_cnt[b, h]].tolist())) / w.topk)
+            missed.append(float(mc.mean()))
+            pc.append(float(p_cnt.mean()))
+        out.append({"delta": d, "budget_blocks": budget, "us_layer_step_median": round(float(np.median(times)), 2),
+                    "hit_rate": round(float(np.mean(hits)), 4), "mean_missed_blocks": round(float(np.mean(missed)), 2),
+                    "mean_P_blocks": round(float(np.mean(pc)), 2), "steps": n})
+        del L
+        log(f"[bench] delta {d}: {out[-1]}")
+    return out
 
 
 def main():
@@ -377,6 +424,8 @@ def main():
                      "traffic": traffic, "algorithmic_bytes_per_launch": spec_launch_bytes,
                      "avg_launch_us": round(spec_launch_us, 2), "kernel_source_sha256": kernel_hash},
     }
+    if args.delta_sweep:
+        result["delta_sweep"] = delta_sweep(args, w, inp, kv, layer.meta, flush, ev)
     if not args.no_cpu_baseline:
         steps = args.cpu_steps if args.cpu_steps > 0 else K
         units = min(args.cpu_units, B * H)
