@@ -22,7 +22,8 @@ PAGE_SIZE = 16
 # Every symbol include/prr.h declares.
 EXPORTS = (
     "prr_max_blocks", "prr_meta_stride", "prr_meta_bytes", "prr_attn_workspace_bytes",
-    "prr_workspace_clear", "prr_build_meta", "prr_select", "prr_select_spec", "prr_predict", "prr_spec_attn",
+    "prr_workspace_clear", "prr_build_meta", "prr_append", "prr_select", "prr_select_spec", "prr_predict",
+    "prr_spec_attn",
     "prr_repair", "prr_calibrate_workspace_bytes", "prr_calibrate", "prr_strerror",
 )
 
@@ -58,6 +59,7 @@ _SIGS = {
     "prr_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "prr_workspace_clear": (ctypes.c_int, [_VP, _SZ, _VP]),
     "prr_build_meta": (ctypes.c_int, [_P(KvCacheStruct), _I32, _VP, _VP]),
+    "prr_append": (ctypes.c_int, [_P(KvCacheStruct), _I32, _VP, _VP, _VP, _VP, _VP]),
     "prr_select": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _VP, _I32, _I32, _P(BlockSetStruct), _VP,
                                   _P(BlockSetStruct), _P(BlockSetStruct), _VP]),
     "prr_select_spec": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _VP, _I32, _I32, _P(BlockSetStruct), _VP,
@@ -249,6 +251,15 @@ def build_meta(kv: KVCache, block: int, meta: Optional[torch.Tensor] = None, str
                            device=kv.k.device)
     _check(lib.prr_build_meta(ctypes.byref(s), block, _ptr(meta), _stream(stream)), "prr_build_meta")
     return meta
+
+
+def append(kv: KVCache, block: int, k_new: torch.Tensor, v_new: torch.Tensor, meta: torch.Tensor, stream=None):
+    """Append one token per sequence (k_new, v_new: [B][Hkv][d]) to the paged cache at position seq_len,
+    fold its key into the metadata of its block, and advance kv.seq_len in place."""
+    lib = load_library()
+    s = kv.struct()
+    _check(lib.prr_append(ctypes.byref(s), block, _ptr(k_new), _ptr(v_new), _ptr(meta), _ptr(kv.seq_len),
+                          _stream(stream)), "prr_append")
 
 
 def select(q: torch.Tensor, kv: KVCache, meta: torch.Tensor, block: int, topk: int,

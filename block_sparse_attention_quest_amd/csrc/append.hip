@@ -1,0 +1,109 @@
+// append.hip - one decode step's new token into the paged cache and its block's metadata (gfx950).
+//
+// Citations:
+//   [paper] "Predict, Reuse, and Repair: Accelerating Dynamic Sparse Attention for Long-Context LLM
+//           Decoding" (full paper text)
+//
+// Decoding appends one token per sequence and step.  Its key and value go to the page that holds
+// position t = seq_len[b] (slot t mod 16); the block metadata of the block that holds t (the channel-wise
+// min and max keys of [paper] A.1) absorbs the new key: a block's first token sets both rows, later ones
+// take the running min / max, in token order, exactly as a rebuild over the block's valid tokens does.
+// Blocks born this way take part in selection at once; the predictor starts their state at the next
+// call ([paper] §4.1, state initialisation).  seq_len[b] then advances by one.
+//
+// One workgroup per sequence: its threads cover (kv head, channel); the length is read before and
+// written after a workgroup barrier.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "prr_internal.hpp"
+
+namespace prr {
+namespace {
+
+struct AppendParams {
+    void *k;
+    void *v;
+    const int32_t *page_table;
+    int32_t *seq_len;
+    const void *k_new;
+    const void *v_new;
+    void *meta;
+    int hkv, max_pages, num_pages, block, stride;
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+    __shared__ int s_t;
+    const int b = blockIdx.x;
+    if (threadIdx.x == 0) s_t = p.seq_len[b];
+    __syncthreads();
+    const int t = s_t;
+    // a full cache (or a negative length) is the caller's contract; nothing is written then
+    if (t < 0 || t >= p.max_pages * kPage) return;
+    const int ph = p.page_table[(size_t)b * p.max_pages + t / kPage];
+    if (ph < 0 || ph >= p.num_pages) return;
+    const int slot = t % kPage;
+    const int blk = t / p.block;
+    const bool first = (t % p.block) == 0;
+    for (int idx = threadIdx.x; idx < p.hkv * D; idx += blockDim.x) {
+        const int h = idx / D, i = idx - h * D;
+        const size_t src = ((size_t)b * p.hkv + h) * D + i;
+        const size_t kdst = (((size_t)ph * p.hkv + h) * kPage + slot) * D + i;      // [page][Hkv][16][d]
+        const size_t vdst = (((size_t)ph * p.hkv + h) * D + i) * kPage + slot;      // [page][Hkv][d][16]
+        const size_t row = (((size_t)b * p.hkv + h) * D + i) * 2 * p.stride;        // [B][Hkv][d][2][stride]
+        if constexpr (BF16) {
+            const uint16_t kx = ((const uint16_t *)p.k_new)[src];
+            ((uint16_t *)p.k)[kdst] = kx;
+            ((uint16_t *)p.v)[vdst] = ((const uint16_t *)p.v_new)[src];
+            uint16_t *m16 = (uint16_t *)p.meta;
+            const float x = bf16_bits_to_f32(kx);
+            const float mn = first ? x : fminf(bf16_bits_to_f32(m16[row + blk]), x);
+            const float mx = first ? x : fmaxf(bf16_bits_to_f32(m16[row + p.stride + blk]), x);
+            m16[row + blk] = (uint16_t)(__float_as_uint(mn) >> 16);
+            m16[row + p.stride + blk] = (uint16_t)(__float_as_uint(mx) >> 16);
+        } else {
+            const float x = ((const float *)p.k_new)[src];
+            ((float *)p.k)[kdst] = x;
+            ((float *)p.v)[vdst] = ((const float *)p.v_new)[src];
+            float *m32 = (float *)p.meta;
+            m32[row + blk] = first ? x : fminf(m32[row + blk], x);
+            m32[row + p.stride + blk] = first ? x : fmaxf(m32[row + p.stride + blk], x);
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) p.seq_len[b] = t + 1;
+}
+
+}  // namespace
+
+hipError_t launch_append(const KvDesc &kv, void *k, void *v, int32_t *seq_len, const void *k_new,
+                         const void *v_new, int block, int stride, void *meta, hipStream_t stream) {
+    AppendParams p;
+    p.k = k;
+    p.v = v;
+    p.page_table = kv.page_table;
+    p.seq_len = seq_len;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.meta = meta;
+    p.hkv = kv.hkv;
+    p.max_pages = kv.max_pages;
+    p.num_pages = kv.num_pages;
+    p.block = block;
+    p.stride = stride;
+    if (kv.bf16) {
+        if (kv.d == 128) append_kernel<true, 128><<<kv.batch, 256, 0, stream>>>(p);
+        else append_kernel<true, 64><<<kv.batch, 256, 0, stream>>>(p);
+    } else {
+        if (kv.d == 128) append_kernel<false, 128><<<kv.batch, 256, 0, stream>>>(p);
+        else append_kernel<false, 64><<<kv.batch, 256, 0, stream>>>(p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace prr

@@ -118,6 +118,16 @@ prr_status prr_build_meta(const prr_kv_cache *kv, int32_t block, void *meta, hip
     return hip_status(prr::launch_meta(desc(kv), block, prr_meta_stride(kv, block), meta, stream));
 }
 
+prr_status prr_append(const prr_kv_cache *kv, int32_t block, const void *k_new, const void *v_new, void *meta,
+                      int32_t *seq_len, hipStream_t stream) {
+    PRR_TRY(check_kv(kv));
+    PRR_TRY(check_block(kv, block));
+    if (!k_new || !v_new || !meta || !seq_len) return PRR_EINVAL;
+    if (seq_len != kv->seq_len) return PRR_EINVAL;   // the cache's own length array is advanced
+    return hip_status(prr::launch_append(desc(kv), const_cast<void *>(kv->k), const_cast<void *>(kv->v), seq_len,
+                                         k_new, v_new, block, prr_meta_stride(kv, block), meta, stream));
+}
+
 prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
                       int32_t block, int32_t topk, const prr_block_set *P, double *scores,
                       prr_block_set *A, prr_block_set *M, hipStream_t stream) {

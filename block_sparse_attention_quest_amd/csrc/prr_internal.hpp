@@ -56,6 +56,11 @@ hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batc
                           double *level, double *trend, int32_t *live, int32_t *p_idx,
                           int32_t *p_cnt, int p_cap, hipStream_t stream);
 
+// Decode append: token seq_len[b] of every sequence into the cache and its block's metadata, then
+// seq_len[b] += 1.
+hipError_t launch_append(const KvDesc &kv, void *k, void *v, int32_t *seq_len, const void *k_new,
+                         const void *v_new, int block, int stride, void *meta, hipStream_t stream);
+
 // Calibration workspace: A-set masks per row, EMA checkpoints per (candidate, chunk), chunk sums.
 size_t calib_workspace_bytes(int rows, int blocks, int n);
 

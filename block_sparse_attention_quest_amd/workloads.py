@@ -33,7 +33,7 @@ import torch
 PAGE_SIZE = 16
 
 # Component ids used to derive independent seeds (seed * 64 + id).
-_Q, _K, _V, _PLANT, _PERM, _CENTRE, _DRIFT, _PSET, _CALIB, _LEN = range(10)
+_Q, _K, _V, _PLANT, _PERM, _CENTRE, _DRIFT, _PSET, _CALIB, _LEN, _APPK, _APPV = range(12)
 
 
 @dataclass(frozen=True)
@@ -70,6 +70,8 @@ class Workload:
     # prefill score matrix for calibration (rows x blocks); 0 = none
     calib_rows: int = 0
     calib_blocks: int = 0
+    # decode-loop appends: tokens per sequence the cache has room for beyond the initial lengths
+    append_tokens: int = 0
 
     # ---- derived sizes ----
     @property
@@ -84,7 +86,7 @@ class Workload:
 
     @property
     def max_pages(self) -> int:
-        longest = max(self.lengths)
+        longest = max(self.lengths) + self.append_tokens
         # room for whole blocks so a block's pages always exist in the table
         nblk = -(-longest // self.block)
         return nblk * (self.block // PAGE_SIZE)
@@ -233,6 +235,15 @@ def make_inputs(w: Workload, device="cpu") -> Inputs:
     v_cache = torch.randn((w.num_pages, w.num_kv_heads, w.head_dim, PAGE_SIZE), generator=gv,
                           device=device, dtype=torch.float32).to(w.torch_dtype)
     return Inputs(w, q, k_cache, v_cache, page_table, seq_len, planted)
+
+
+def make_append_tokens(w: Workload, device="cpu"):
+    """Keys and values of the decode-loop appends, [append_tokens][B][Hkv][d] each, N(0, 1) in the
+    workload dtype."""
+    shape = (w.append_tokens, w.batch, w.num_kv_heads, w.head_dim)
+    k = torch.randn(shape, generator=_gen(w, _APPK, device), device=device, dtype=torch.float32)
+    v = torch.randn(shape, generator=_gen(w, _APPV, device), device=device, dtype=torch.float32)
+    return k.to(w.torch_dtype), v.to(w.torch_dtype)
 
 
 def make_spec_set(w: Workload, selected: np.ndarray, n_blocks: int, n_hit: int, n_miss: int,

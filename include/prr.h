@@ -114,6 +114,19 @@ prr_status prr_workspace_clear(void *ws, size_t ws_bytes, hipStream_t stream);
  * block must be a positive multiple of page_size.  Reads all of K once; not part of the per-step path. */
 prr_status prr_build_meta(const prr_kv_cache *kv, int32_t block, void *meta, hipStream_t stream);
 
+/* Decode-loop append (one token per sequence and step; [paper] §4.1: blocks are born as decoding grows
+ * the context, and [paper] A.1: the metadata of the block being filled must cover its tokens).  For every
+ * sequence b with t = seq_len[b] < max_pages * page_size: writes k_new[b][h] to the K cache and
+ * v_new[b][h] to the V cache at position t (physical page page_table[b][t / page_size], slot t mod
+ * page_size; the V tile is channel-major), updates the metadata of block t / block (row 0 = channel-wise
+ * min, row 1 = max; the block's first token sets both, later tokens take the running min/max, which equals
+ * a rebuild by prr_build_meta over the block's valid tokens), then sets seq_len[b] = t + 1.  A sequence
+ * whose cache is full (or whose page-table entry is out of range) is left untouched.
+ * k_new, v_new: [batch][num_kv_heads][head_dim] in the cache dtype, device.  seq_len must be kv->seq_len
+ * (written in place); kv->k and kv->v are written.  meta as for prr_build_meta. */
+prr_status prr_append(const prr_kv_cache *kv, int32_t block, const void *k_new, const void *v_new, void *meta,
+                      int32_t *seq_len, hipStream_t stream);
+
 /* Quest selection, GQA-extended ([paper] A.1; [paper] §1, §2.1 top-K selection; [paper] §3 M = A \ P).
  *   scores[b][kvh][p] (fp64, row length prr_max_blocks) = sum_{i=0}^{d-1} max(qbar_i mn_{p,i},
  *       qbar_i mx_{p,i}), qbar = (1/G) sum_g q[b][kvh G + g], summed in channel order from +0.0 in

@@ -157,3 +157,18 @@ def test_select_spec_argument_errors(lib):
     assert call(wsb=need - 1) == 3
     assert call(block=24) == 1
     assert call(kv=_kv(max_pages=65536), block=16, wsb=lib.prr_attn_workspace_bytes(2, 32, 8, 128, 16, 64)) == 2
+
+
+def test_append_argument_errors(lib):
+    kv = _kv()
+    sl = kv.seq_len
+    call = lambda kv=kv, block=64, k=1, v=1, meta=1, seq=sl: lib.prr_append(
+        ctypes.byref(kv) if kv is not None else None, block, k, v, meta, seq, None)
+    assert call(kv=None) == 1
+    assert call(k=None) == 1
+    assert call(v=None) == 1
+    assert call(meta=None) == 1
+    assert call(seq=None) == 1
+    assert call(seq=sl + 4) == 1                  # must be the cache's own length array
+    assert call(block=24) == 1
+    assert call(kv=_kv(head_dim=96)) == 2
