@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E peak
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "spec_attn_ctx128k_b8_hbm_counters.md")
+PROFILE_WORKLOAD = "ctx128k_b8_64steps"   # the workload (fixed context) those counters were taken on
 
 
 def log(*a):
@@ -55,6 +56,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=64, help="(sequence, kv head) units in the CPU sample")
     ap.add_argument("--cpu-steps", type=int, default=0, help="decode steps in the CPU sample (0: all timed)")
+    ap.add_argument("--append", action="store_true",
+                    help="decode-loop mode: every timed step first appends one token per sequence (prr_append, "
+                         "timed alone) so the context grows by one token per step")
     ap.add_argument("--delta-sweep", default="",
                     help="comma-separated speculation budgets |P| = delta K to time as extra layer steps "
                          "(e.g. 1,1.25,1.5,2); empty: none")
@@ -208,13 +212,17 @@ def main():
     dev = torch.device("cuda:0")
     K = args.steps
     base = wl.CONFIGS[args.config]
-    w = wl.scaled(base, steps=max(base.steps, args.warmup + 1, K + 1))
+    w = wl.scaled(base, steps=max(base.steps, args.warmup + 1, K + 1),
+                  append_tokens=(K + 1) if args.append else 0)
     log(f"[bench] generating {w.name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} "
         f"T={w.context} S={w.block} K={w.topk} steps={w.steps}")
     t_gen = time.time()
     inp = wl.make_inputs(w, dev)
     kv = bd.KVCache(inp.k_cache, inp.v_cache, inp.page_table, inp.seq_len)
     layer = PRRLayer(kv, w.num_q_heads, w.block, w.topk, w.topk, ema=w.ema, scale=w.scale)
+    if args.append:
+        k_app, v_app = wl.make_append_tokens(w, dev)
+        len0 = inp.seq_len.clone()
     torch.cuda.synchronize()
     log(f"[bench] inputs + metadata ready in {time.time() - t_gen:.1f}s")
 
@@ -259,6 +267,7 @@ def main():
     a_sets = torch.zeros((K, B, H, w.topk), dtype=torch.int32, device=dev)
     p_sets = torch.zeros_like(a_sets)
     iso_names = ("empty", "spec", "repair", "select", "predict", "select_spec")
+    append_pairs = []
 
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -266,6 +275,13 @@ def main():
         t = 1 + i
         q = inp.q[t]
         P = layer.P_cur
+        if args.append:
+            flush()
+            e0, e1 = ev(), ev()
+            e0.record(crit)
+            bd.append(kv, w.block, k_app[i], v_app[i], layer.meta, stream=crit)
+            e1.record(crit)
+            append_pairs.append((e0, e1))
         # 1. layer step with a breakdown
         flush()
         tm = StepTimers.make()
@@ -307,10 +323,15 @@ def main():
     def replay(two_streams: bool):
         """Replay the trajectory with a start and an end event per step only."""
         layer.reset()
+        if args.append:   # back to the initial context: lengths, then the metadata of every block
+            inp.seq_len.copy_(len0)
+            bd.build_meta(kv, w.block, layer.meta)
         layer.step(inp.q[0])
         torch.cuda.synchronize()
         out = []
         for i in range(K):
+            if args.append:
+                bd.append(kv, w.block, k_app[i], v_app[i], layer.meta, stream=crit)
             flush()
             if two_streams:
                 tm = TwoStreamTimers(ev(), None, None, None, None, ev())
@@ -366,7 +387,7 @@ def main():
     spec_launch_bytes = float(spec_bytes.mean())
     spec_launch_us = float(statistics.mean(spec_us))
     achieved = spec_launch_bytes / (spec_launch_us * 1e-6) / 1e9
-    traffic = load_traffic(kernel_hash)
+    traffic = load_traffic(kernel_hash) if (w.name == PROFILE_WORKLOAD and not args.append) else None
 
     med = lambda xs: round(float(statistics.median(xs)), 2)
     result = {
@@ -424,6 +445,15 @@ def main():
                      "traffic": traffic, "algorithmic_bytes_per_launch": spec_launch_bytes,
                      "avg_launch_us": round(spec_launch_us, 2), "kernel_source_sha256": kernel_hash},
     }
+    if args.append:
+        result["decode_append"] = {
+            "us_append_median": round(float(statistics.median(
+                [el(a, b) - base_us for a, b in append_pairs])), 2),
+            "note": "each timed step appends one token per sequence before its layer step (context grows "
+                    "by one token per step); append time = event time minus the empty pair"}
+        if args.delta_sweep:
+            log("[bench] --delta-sweep is skipped in --append mode")
+            args.delta_sweep = ""
     if args.delta_sweep:
         result["delta_sweep"] = delta_sweep(args, w, inp, kv, layer.meta, flush, ev)
     if not args.no_cpu_baseline:

@@ -45,38 +45,49 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     const int t = s_t;
     // a full cache (or a negative length) is the caller's contract; nothing is written then
     if (t < 0 || t >= p.max_pages * kPage) return;
+    // the page-table entry only decides where the token goes: the metadata and token loads below do not
+    // wait for it (stores are skipped for an out-of-range entry)
     const int ph = p.page_table[(size_t)b * p.max_pages + t / kPage];
-    if (ph < 0 || ph >= p.num_pages) return;
     const int slot = t % kPage;
     const int blk = t / p.block;
     const bool first = (t % p.block) == 0;
+#pragma unroll 4
     for (int idx = threadIdx.x; idx < p.hkv * D; idx += blockDim.x) {
         const int h = idx / D, i = idx - h * D;
         const size_t src = ((size_t)b * p.hkv + h) * D + i;
         const size_t kdst = (((size_t)ph * p.hkv + h) * kPage + slot) * D + i;      // [page][Hkv][16][d]
         const size_t vdst = (((size_t)ph * p.hkv + h) * D + i) * kPage + slot;      // [page][Hkv][d][16]
         const size_t row = (((size_t)b * p.hkv + h) * D + i) * 2 * p.stride;        // [B][Hkv][d][2][stride]
+        const bool ok = ph >= 0 && ph < p.num_pages;
         if constexpr (BF16) {
             const uint16_t kx = ((const uint16_t *)p.k_new)[src];
-            ((uint16_t *)p.k)[kdst] = kx;
-            ((uint16_t *)p.v)[vdst] = ((const uint16_t *)p.v_new)[src];
+            const uint16_t vx = ((const uint16_t *)p.v_new)[src];
             uint16_t *m16 = (uint16_t *)p.meta;
+            const uint16_t mn0 = m16[row + blk], mx0 = m16[row + p.stride + blk];
             const float x = bf16_bits_to_f32(kx);
-            const float mn = first ? x : fminf(bf16_bits_to_f32(m16[row + blk]), x);
-            const float mx = first ? x : fmaxf(bf16_bits_to_f32(m16[row + p.stride + blk]), x);
-            m16[row + blk] = (uint16_t)(__float_as_uint(mn) >> 16);
-            m16[row + p.stride + blk] = (uint16_t)(__float_as_uint(mx) >> 16);
+            const float mn = first ? x : fminf(bf16_bits_to_f32(mn0), x);
+            const float mx = first ? x : fmaxf(bf16_bits_to_f32(mx0), x);
+            if (ok) {
+                ((uint16_t *)p.k)[kdst] = kx;
+                ((uint16_t *)p.v)[vdst] = vx;
+                m16[row + blk] = (uint16_t)(__float_as_uint(mn) >> 16);
+                m16[row + p.stride + blk] = (uint16_t)(__float_as_uint(mx) >> 16);
+            }
         } else {
             const float x = ((const float *)p.k_new)[src];
-            ((float *)p.k)[kdst] = x;
-            ((float *)p.v)[vdst] = ((const float *)p.v_new)[src];
+            const float vx = ((const float *)p.v_new)[src];
             float *m32 = (float *)p.meta;
-            m32[row + blk] = first ? x : fminf(m32[row + blk], x);
-            m32[row + p.stride + blk] = first ? x : fmaxf(m32[row + p.stride + blk], x);
+            const float mn0 = m32[row + blk], mx0 = m32[row + p.stride + blk];
+            if (ok) {
+                ((float *)p.k)[kdst] = x;
+                ((float *)p.v)[vdst] = vx;
+                m32[row + blk] = first ? x : fminf(mn0, x);
+                m32[row + p.stride + blk] = first ? x : fmaxf(mx0, x);
+            }
         }
     }
     __syncthreads();
-    if (threadIdx.x == 0) p.seq_len[b] = t + 1;
+    if (threadIdx.x == 0 && ph >= 0 && ph < p.num_pages) p.seq_len[b] = t + 1;
 }
 
 }  // namespace

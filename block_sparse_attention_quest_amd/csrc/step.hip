@@ -15,7 +15,7 @@
 // the longer of the two.  At 128K, batch 8 the grid is 256 scoring + 256 speculative workgroups: all of
 // them resident at once (two per CU).
 //
-// Top-K (with M = A \ P).  When a unit has at most 2048 blocks, the last scoring workgroup of the unit
+// Top-K (with M = A \ P).  When a unit has at most 4096 blocks, the last scoring workgroup of the unit
 // to finish (a device-scope arrival counter; nobody waits) runs the unit's top-K with the same 256
 // threads, so the top-K of most units overlaps the speculative pass.  Scores are stored and read with
 // device-scope accesses, which are coherent across the XCDs' L2s.  Larger units take the separate
@@ -106,13 +106,16 @@ hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const voi
     const long grid = (long)n_spec + (long)nsx * units;
     if (grid > 0x7fffffffL) return hipErrorInvalidValue;
     // keys per thread of the fused top-K (0: the unit is too large; the top-K kernel follows)
-    const int kpt = nmax <= 256 ? 1 : nmax <= 512 ? 2 : nmax <= 1024 ? 4 : nmax <= 2048 ? 8 : 0;
+    // (measured at 8192 blocks, 32 keys per thread on 256 threads lose to the separate 1024-thread kernel)
+    const int kpt = nmax <= 256 ? 1 : nmax <= 512 ? 2 : nmax <= 1024 ? 4 : nmax <= 2048 ? 8
+                  : nmax <= 4096 ? 16 : 0;
 #define PRR_SS(DD, K)                                                                                    \
     if (kv.d == DD && kpt == K) {                                                                        \
         select_spec_kernel<DD, K><<<(int)grid, 256, 0, stream>>>(ap, sp, tp, arrivals, nsx * units, nsx); \
     } else
-    PRR_SS(128, 0) PRR_SS(128, 1) PRR_SS(128, 2) PRR_SS(128, 4) PRR_SS(128, 8)
-    PRR_SS(64, 0) PRR_SS(64, 1) PRR_SS(64, 2) PRR_SS(64, 4) PRR_SS(64, 8) { return hipErrorInvalidValue; }
+    PRR_SS(128, 0) PRR_SS(128, 1) PRR_SS(128, 2) PRR_SS(128, 4) PRR_SS(128, 8) PRR_SS(128, 16)
+    PRR_SS(64, 0) PRR_SS(64, 1) PRR_SS(64, 2) PRR_SS(64, 4) PRR_SS(64, 8) PRR_SS(64, 16)
+    { return hipErrorInvalidValue; }
 #undef PRR_SS
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || kpt != 0) return e;

@@ -301,11 +301,11 @@ def test_predictor_trajectory_bit_exact():
     assert live.cpu().numpy().tolist() == [[-(-l // w.block)] * H for l in lens]
 
 
-@pytest.mark.parametrize("nblocks", [300, 900, 2048, 2049])
+@pytest.mark.parametrize("nblocks", [300, 900, 2048, 2049, 4097])
 def test_select_spec_fused_topk_shapes(nblocks):
-    """The fused launch's top-K runs in the last scoring workgroup with 1, 2, 4 or 8 keys per thread
-    (units of up to 256, 512, 1024, 2048 blocks) and falls back to the separate top-K kernel beyond
-    2048 blocks: every shape against the separate calls (bit for bit) and the oracle's scores and sets."""
+    """The fused launch's top-K runs in the last scoring workgroup with 1, 2, 4, 8 or 16 keys per thread
+    (units of up to 256, 512, 1024, 2048, 4096 blocks) and falls back to the separate top-K kernel beyond
+    4096 blocks: every shape against the separate calls (bit for bit) and the oracle's scores and sets."""
     lens = [nblocks * 16, nblocks * 16 - 37]
     w = wl.Workload(f"fused_{nblocks}", 2, 8, 2, 64, max(lens), 16, 40, "bf16", seed=900 + nblocks,
                     seq_lens=lens)
