@@ -239,7 +239,7 @@ def main():
     iso_scores = torch.zeros_like(layer.scores)
     iso_A = bd.BlockSet.empty(B, H, w.topk, dev)
     iso_M = bd.BlockSet.empty(B, H, w.topk, dev)
-    ws_iso_spec = bd.workspace_for(kv, w.num_q_heads, w.block, w.topk)
+    ws_iso_spec = bd.select_spec_workspace_for(kv, w.num_q_heads, w.block, w.topk, w.topk)
     ws_iso_rep = bd.workspace_for(kv, w.num_q_heads, w.block, w.topk)
     iso_level, iso_trend = torch.empty_like(layer.level), torch.empty_like(layer.trend)
     iso_live = torch.empty_like(layer.live)
@@ -371,6 +371,7 @@ def main():
     value_raw = tot_bytes / ((sum(spec_raw) + sum(rep_raw)) * 1e-6) / 1e9
     spec_gbps = float(spec_bytes.sum() / (sum(spec_us) * 1e-6) / 1e9)
     rep_gbps = float(rep_bytes.sum() / (sum(rep_us) * 1e-6) / 1e9)
+    step_gbps = [(sb + rb) / ((a + b) * 1e-6) / 1e9 for sb, rb, a, b in zip(spec_bytes, rep_bytes, spec_us, rep_us)]
 
     A_all = a_sets.cpu().numpy()
     P_all = p_sets.cpu().numpy()
@@ -408,6 +409,9 @@ def main():
                    "spec_budget_blocks": w.topk, "ema": list(w.ema), "decode_steps_timed": K,
                    "parallelism": "none (1 GPU)", "flush_mib_read_between_kernels": args.flush_mib},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+        "value_median_step_gbps": round(float(statistics.median(step_gbps)), 1),
+        "value_note": "value = all timed steps' KV bytes / their summed spec + repair kernel time (one slow step "
+                      "counts in full); value_median_step_gbps = the median step's own figure",
         "timing_note": "kernel us = event-bracketed us minus the median empty event pair (each after the same "
                        "flush); *_raw figures are the event-bracketed ones",
         "us_empty_event_pair_median": round(base_us, 2),

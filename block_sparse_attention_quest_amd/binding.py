@@ -22,7 +22,8 @@ PAGE_SIZE = 16
 # Every symbol include/prr.h declares.
 EXPORTS = (
     "prr_max_blocks", "prr_meta_stride", "prr_meta_bytes", "prr_attn_workspace_bytes",
-    "prr_workspace_clear", "prr_build_meta", "prr_append", "prr_select", "prr_select_spec", "prr_predict",
+    "prr_workspace_clear", "prr_build_meta", "prr_append", "prr_select", "prr_select_spec_workspace_bytes",
+    "prr_select_spec", "prr_predict",
     "prr_spec_attn",
     "prr_repair", "prr_calibrate_workspace_bytes", "prr_calibrate", "prr_strerror",
 )
@@ -62,6 +63,7 @@ _SIGS = {
     "prr_append": (ctypes.c_int, [_P(KvCacheStruct), _I32, _VP, _VP, _VP, _VP, _VP]),
     "prr_select": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _VP, _I32, _I32, _P(BlockSetStruct), _VP,
                                   _P(BlockSetStruct), _P(BlockSetStruct), _VP]),
+    "prr_select_spec_workspace_bytes": (_SZ, [_P(KvCacheStruct), _I32, _I32, _I32, _I32]),
     "prr_select_spec": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _VP, _I32, _I32, _P(BlockSetStruct), _VP,
                                        _P(BlockSetStruct), _P(BlockSetStruct), _F, _P(AttnStateStruct), _VP, _SZ,
                                        _VP]),
@@ -237,6 +239,13 @@ def workspace_for(kv: KVCache, hq: int, block: int, cap: int) -> Workspace:
                      device=kv.k.device)
 
 
+def select_spec_workspace_for(kv: KVCache, hq: int, block: int, topk: int, cap: int) -> Workspace:
+    """Workspace for prr_select_spec (attention workspace plus top-K candidates)."""
+    s = kv.struct()
+    return Workspace(load_library().prr_select_spec_workspace_bytes(ctypes.byref(s), hq, block, topk, cap),
+                     kv.k.device)
+
+
 def workspace_clear(ws: Workspace, stream=None):
     _check(load_library().prr_workspace_clear(ws.ptr(), ws.nbytes, _stream(stream)), "prr_workspace_clear")
 
@@ -307,7 +316,7 @@ def select_spec(q: torch.Tensor, kv: KVCache, meta: torch.Tensor, block: int, to
     if out is None:
         out = AttnState.empty(B, Hq, d, dev)
     if ws is None:
-        ws = workspace_for(kv, Hq, block, P.cap)
+        ws = select_spec_workspace_for(kv, Hq, block, topk, P.cap)
     a_s, p_s, m_s, o_s = A.struct(), P.struct(), M.struct(), out.struct()
     st = lib.prr_select_spec(_ptr(q), Hq, ctypes.byref(s), _ptr(meta), block, topk, ctypes.byref(p_s),
                              _ptr(scores), ctypes.byref(a_s), ctypes.byref(m_s), float(scale), ctypes.byref(o_s),

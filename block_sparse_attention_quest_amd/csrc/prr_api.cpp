@@ -153,18 +153,32 @@ prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv
                                          stream));
 }
 
+size_t prr_select_spec_workspace_bytes(const prr_kv_cache *kv, int32_t num_q_heads, int32_t block, int32_t topk,
+                                       int32_t cap) {
+    if (!kv || kv->batch <= 0 || kv->num_kv_heads <= 0 || num_q_heads <= 0 || kv->head_dim <= 0 ||
+        block < prr::kPage || cap <= 0 || topk < 0)
+        return 0;
+    return prr::select_spec_workspace_bytes(kv->batch, num_q_heads, kv->num_kv_heads, kv->head_dim, block, cap,
+                                            prr_max_blocks(kv, block), topk);
+}
+
 prr_status prr_select_spec(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
                            int32_t block, int32_t topk, const prr_block_set *P, double *scores,
                            prr_block_set *A, prr_block_set *M, float scale, prr_attn_state *out, void *ws,
                            size_t ws_bytes, hipStream_t stream) {
-    if (!meta || !scores || !P || !M) return PRR_EINVAL;
-    PRR_TRY(attn_common(q, num_q_heads, kv, block, P, ws, ws_bytes));
+    if (!q || !meta || !scores || !P || !M) return PRR_EINVAL;
+    PRR_TRY(check_kv(kv));
+    PRR_TRY(check_block(kv, block));
+    PRR_TRY(check_heads(kv, num_q_heads));
+    PRR_TRY(check_set(P));
     PRR_TRY(check_set(A));
     PRR_TRY(check_set(M));
     if (topk < 0 || A->cap < topk || M->cap < topk) return PRR_EINVAL;
     if (!out || !out->acc || !out->l || !out->m) return PRR_EINVAL;
     const int nmax = prr_max_blocks(kv, block);
     if (nmax > prr::kMaxSelectN) return PRR_EUNSUPPORTED;
+    if (!ws || ws_bytes < prr_select_spec_workspace_bytes(kv, num_q_heads, block, topk, P->cap))
+        return PRR_EWORKSPACE;
     return hip_status(prr::launch_select_spec(desc(kv), q, num_q_heads, meta, block, prr_meta_stride(kv, block),
                                               nmax, topk, P->idx, P->count, P->cap, scores, A->idx, A->count,
                                               A->cap, M->idx, M->count, M->cap, scale, out->acc, out->l, out->m,

@@ -43,8 +43,21 @@ hipError_t launch_topk(const KvDesc &kv, int block, int nmax, int topk, const do
                        const int32_t *p_idx, const int32_t *p_cnt, int p_cap, int32_t *a_idx, int32_t *a_cnt,
                        int a_cap, int32_t *m_idx, int32_t *m_cnt, int m_cap, hipStream_t stream);
 
+// How prr_select_spec ranks a unit's blocks: kpt keys per thread inside the launch (two: over candidates
+// of a two-stage top-K with kl candidates per scoring workgroup), or kpt = 0: the separate top-K kernel.
+struct SelectSpecPlan {
+    bool two;
+    int kl;
+    int kpt;
+};
+SelectSpecPlan select_spec_plan(int nmax, int topk);
+
+// Workspace of prr_select_spec: the speculative pass's attention workspace, then (two-stage top-K) the
+// candidates of every scoring workgroup.
+size_t select_spec_workspace_bytes(int batch, int hq, int hkv, int d, int block, int cap, int nmax, int topk);
+
 // Selection and the speculative pass over P in one grid (bf16 caches; fp32 caches run the two in turn),
-// then the top-K.  ws is the speculative pass's attention workspace.
+// then the top-K.  ws: select_spec_workspace_bytes.
 hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,
                               int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
                               double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,

@@ -302,7 +302,7 @@ constexpr int kScoreBPL = BF16 ? 2 : 1;
 // Scores blocks [256 BPL bx, 256 BPL (bx + 1)) of unit u (BPL consecutive blocks per lane).  COHERENT:
 // the scores are stored with device-scope stores, for a reader on another XCD within the same launch.
 template <bool BF16, int D, bool COHERENT = false>
-__device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u) {
+__device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u, double (&kept)[kScoreBPL<BF16>]) {
     constexpr int BPL = kScoreBPL<BF16>;   // one 4-byte load per channel
     __shared__ double s_qbar[D];
     __shared__ int s_row[D];             // metadata row of channel i: 1 (max) when qbar_i >= 0, else 0 (min)
@@ -368,6 +368,8 @@ __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u) 
     }
     double *out = p.scores + (size_t)u * p.nmax;
 #pragma unroll
+    for (int e = 0; e < BPL; ++e) kept[e] = acc[e];
+#pragma unroll
     for (int e = 0; e < BPL; ++e)
         if (p0 + e < nb) {
             if constexpr (COHERENT)
@@ -375,6 +377,13 @@ __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u) 
             else
                 out[p0 + e] = acc[e];
         }
+}
+
+// The same without handing the scores back.
+template <bool BF16, int D, bool COHERENT = false>
+__device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u) {
+    double kept[kScoreBPL<BF16>];
+    score_body<BF16, D, COHERENT>(p, bx, u, kept);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -442,6 +451,117 @@ __device__ __forceinline__ void topk_body(const TopkParams &p, int u) {
     for (int j = 0; j < KPT; ++j) {
         if (sel >> j & 1u) p.a_idx[(size_t)u * p.a_cap + oa++] = base + j;
         if (inm >> j & 1u) p.m_idx[(size_t)u * p.m_cap + om++] = base + j;
+    }
+    if (threadIdx.x == 0) {
+        p.a_cnt[u] = (int32_t)(total & 0xffffu);
+        if (want_m) p.m_cnt[u] = (int32_t)(total >> 16);
+    }
+}
+
+// ---- two-stage top-K for long rows ----
+//
+// The K largest keys of a row are among the union of the K largest of every part of it (a key beaten by
+// fewer than K keys of the whole row is beaten by fewer than K of its part), so a row too long for one
+// workgroup's registers is ranked in two stages: each scoring workgroup keeps the local top-kl (kl =
+// min(K, its block count)) of its own blocks as candidates (order key, block index), in ascending block
+// order; the unit's last workgroup ranks the candidates of all parts.  Candidate positions then follow
+// the block order, so ties still go to the smaller block index.
+
+constexpr int kMaxTwoStageBlocks = 16384;   // P bitmap of the second stage (LDS)
+
+__device__ __forceinline__ void st_dev_u64(uint64_t *ptr, uint64_t v) {
+    __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_i32(int32_t *ptr, int32_t v) {
+    __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Stage 1: the local top-kl of the workgroup's blocks [first_block, first_block + 256 BPL) (lane t holds
+// blocks first_block + BPL t + e with scores kept[e]); n_local of them exist.  Writes the candidates and
+// their count with device-scope stores.
+template <int BPL>
+__device__ __forceinline__ void local_candidates(const double (&kept)[BPL], int n_local, int kl, int first_block,
+                                                 uint64_t *ckey, int32_t *cidx, int32_t *ccnt, TopkSmem<4> &sm) {
+    uint64_t key[BPL];
+    const int base = threadIdx.x * BPL;
+#pragma unroll
+    for (int e = 0; e < BPL; ++e) key[e] = base + e < n_local ? order_key(kept[e]) : 0ull;
+    const uint32_t sel = block_topk<BPL, 4>(key, n_local, kl, sm);
+    __syncthreads();   // top-K scratch released
+    uint32_t total;
+    uint32_t off = block_excl_scan((uint32_t)__popc(sel), sm, 1, total);
+#pragma unroll
+    for (int e = 0; e < BPL; ++e)
+        if (sel >> e & 1u) {
+            st_dev_u64(&ckey[off], key[e]);
+            st_dev_i32(&cidx[off], first_block + base + e);
+            ++off;
+        }
+    if (threadIdx.x == 0) st_dev_i32(ccnt, (int32_t)total);
+}
+
+// Stage 2: the top-K of unit u over its nparts x kl candidate slots (part c holds ccnt[c] candidates)
+// and M = A \ P, written like topk_body.  256 threads with KPT slots each (256 KPT >= nparts kl).
+template <int KPT>
+__device__ __forceinline__ void topk_candidates_body(const TopkParams &p, int u, const uint64_t *ckey,
+                                                     const int32_t *cidx, const int32_t *ccnt, int nparts,
+                                                     int kl) {
+    constexpr int TPB = 256, W = 4;
+    __shared__ TopkSmem<W> sm;
+    __shared__ uint32_t s_pbits[kMaxTwoStageBlocks / 32];
+    __shared__ int s_cnt[TPB];
+    __shared__ int s_total;
+    const int b = u / p.hkv;
+    const int slen = p.seq_len[b];
+    const int nb = min((slen + p.block - 1) / p.block, p.nmax);
+    const bool want_m = p.m_idx != nullptr;
+    if (threadIdx.x < nparts)
+        s_cnt[threadIdx.x] = __hip_atomic_load(&ccnt[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (want_m)
+        for (int i = threadIdx.x; i < (nb + 31) / 32; i += TPB) s_pbits[i] = 0u;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int t = 0;
+        for (int c = 0; c < nparts; ++c) t += s_cnt[c];
+        s_total = t;
+    }
+    const int base = threadIdx.x * KPT;
+    uint64_t key[KPT];
+    int32_t idx[KPT];
+    uint32_t valid = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int pos = base + j;
+        const int c = pos / kl, slot = pos - c * kl;
+        const bool ok = c < nparts && slot < s_cnt[min(c, nparts - 1)];
+        key[j] = ok ? __hip_atomic_load(&ckey[pos], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+        idx[j] = ok ? __hip_atomic_load(&cidx[pos], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+        if (ok) valid |= 1u << j;
+    }
+    if (want_m) {
+        const int pc = min(max(p.p_cnt[u], 0), p.p_cap);
+        for (int i = threadIdx.x; i < pc; i += TPB) {
+            const int x = p.p_idx[(size_t)u * p.p_cap + i];
+            if (x >= 0 && x < nb) atomicOr(&s_pbits[x >> 5], 1u << (x & 31));
+        }
+    }
+    __syncthreads();   // counts total, P bitmap complete
+    // valid candidate keys are images of finite scores, all above the padding key 0
+    const uint32_t sel = s_total <= p.topk ? valid : block_topk<KPT, W>(key, nparts * kl, p.topk, sm) & valid;
+    __syncthreads();
+    uint32_t inm = 0;
+    if (want_m) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            if ((sel >> j & 1u) && !(s_pbits[idx[j] >> 5] >> (idx[j] & 31) & 1u)) inm |= 1u << j;
+    }
+    uint32_t total;
+    const uint32_t off = block_excl_scan((uint32_t)__popc(sel) | ((uint32_t)__popc(inm) << 16), sm, 1, total);
+    uint32_t oa = off & 0xffffu, om = off >> 16;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        if (sel >> j & 1u) p.a_idx[(size_t)u * p.a_cap + oa++] = idx[j];
+        if (inm >> j & 1u) p.m_idx[(size_t)u * p.m_cap + om++] = idx[j];
     }
     if (threadIdx.x == 0) {
         p.a_cnt[u] = (int32_t)(total & 0xffffu);

@@ -15,11 +15,15 @@
 // the longer of the two.  At 128K, batch 8 the grid is 256 scoring + 256 speculative workgroups: all of
 // them resident at once (two per CU).
 //
-// Top-K (with M = A \ P).  When a unit has at most 4096 blocks, the last scoring workgroup of the unit
-// to finish (a device-scope arrival counter; nobody waits) runs the unit's top-K with the same 256
-// threads, so the top-K of most units overlaps the speculative pass.  Scores are stored and read with
-// device-scope accesses, which are coherent across the XCDs' L2s.  Larger units take the separate
-// top-K kernel after the launch.
+// Top-K (with M = A \ P).  The last scoring workgroup of a unit to finish (a device-scope arrival
+// counter; nobody waits) runs the unit's top-K with the same 256 threads, so the top-K of most units
+// overlaps the speculative pass:
+//   * up to 2048 blocks per unit, over all of the unit's scores (up to 8 per thread), stored and re-read
+//     with device-scope accesses, which are coherent across the XCDs' L2s;
+//   * beyond that, in two stages: every scoring workgroup first keeps the local top-min(K, 512) of its
+//     own 512 blocks as candidates, and the last one ranks the candidates of all workgroups of the unit
+//     (up to 16 per thread; the selection is exact, see select_core.hpp);
+// otherwise (more candidates than that) the separate top-K kernel follows the launch.
 
 #include "select_core.hpp"
 #include "attn_core.hpp"
@@ -31,16 +35,35 @@ namespace {
 // unit's last to finish and KPT > 0, runs the unit's top-K (KPT keys per thread, 256 KPT >= the unit's
 // block count); the remaining n_spec workgroups run the speculative pass.  Register use is the
 // attention part's (two waves per SIMD).
-template <int D, int KPT>
+struct CandParams {
+    uint64_t *key;   // [units][nsx][kl]
+    int32_t *idx;    // [units][nsx][kl]
+    int32_t *cnt;    // [units][nsx]
+    int kl;
+};
+
+template <int D, int KPT, bool TWO>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void select_spec_kernel(
-    AttnParams ap, ScoreParams sp, TopkParams tp, uint32_t *arrivals, int n_score, int nsx) {
+    AttnParams ap, ScoreParams sp, TopkParams tp, CandParams cp, uint32_t *arrivals, int n_score, int nsx) {
     if ((int)blockIdx.x >= n_score) {
         attn_body<true, D, false>(ap, (int)blockIdx.x - n_score, (int)gridDim.x - n_score);
         return;
     }
     const int s = (int)blockIdx.x;
     const int u = s / nsx;
-    score_body<true, D, KPT != 0>(sp, s - u * nsx, u);
+    const int bx = s - u * nsx;
+    double kept[kScoreBPL<true>] = {0.0, 0.0};
+    score_body<true, D, KPT != 0 && !TWO>(sp, bx, u, kept);
+    if constexpr (TWO) {
+        __shared__ TopkSmem<4> sm;
+        constexpr int BPW = 256 * kScoreBPL<true>;   // blocks per scoring workgroup
+        const int b = u / sp.hkv;
+        const int nb = min((max(sp.seq_len[b], 0) + sp.block - 1) / sp.block, sp.nmax);
+        const int n_local = min(max(nb - bx * BPW, 0), BPW);
+        const size_t part = (size_t)u * nsx + bx;
+        local_candidates<kScoreBPL<true>>(kept, n_local, cp.kl, bx * BPW, cp.key + part * cp.kl,
+                                          cp.idx + part * cp.kl, cp.cnt + part, sm);
+    }
     if constexpr (KPT != 0) {
         __shared__ int s_last;
         // this workgroup's score stores are complete before its arrival is counted
@@ -53,11 +76,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
             if (s_last) __hip_atomic_store(&arrivals[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
-        if (s_last) topk_body<KPT, 256, true>(tp, u);
+        if (s_last) {
+            if constexpr (TWO)
+                topk_candidates_body<KPT>(tp, u, cp.key + (size_t)u * nsx * cp.kl, cp.idx + (size_t)u * nsx * cp.kl,
+                                          cp.cnt + (size_t)u * nsx, nsx, cp.kl);
+            else
+                topk_body<KPT, 256, true>(tp, u);
+        }
     }
 }
 
 }  // namespace
+
+SelectSpecPlan select_spec_plan(int nmax, int topk) {
+    SelectSpecPlan pl;
+    pl.two = false;
+    pl.kl = 0;
+    pl.kpt = nmax <= 256 ? 1 : nmax <= 512 ? 2 : nmax <= 1024 ? 4 : nmax <= 2048 ? 8 : 0;
+    if (pl.kpt == 0 && nmax <= kMaxTwoStageBlocks) {
+        const int bpw = 256 * kScoreBPL<true>;
+        const int nsx = (nmax + bpw - 1) / bpw;
+        const int kl = std::max(1, std::min(topk, bpw));
+        const long slots = (long)nsx * kl;
+        const int kpt = slots <= 256 ? 1 : slots <= 512 ? 2 : slots <= 1024 ? 4 : slots <= 2048 ? 8
+                      : slots <= 4096 ? 16 : 0;
+        if (kpt) {
+            pl.two = true;
+            pl.kl = kl;
+            pl.kpt = kpt;
+        }
+    }
+    return pl;
+}
+
+size_t select_spec_workspace_bytes(int batch, int hq, int hkv, int d, int block, int cap, int nmax, int topk) {
+    const size_t attn = attn_workspace_bytes(batch, hq, hkv, d, block, cap);
+    const SelectSpecPlan pl = select_spec_plan(nmax, topk);
+    if (!pl.two) return attn;
+    const int bpw = 256 * kScoreBPL<true>;
+    const size_t parts = (size_t)batch * hkv * ((nmax + bpw - 1) / bpw);
+    return attn + parts * pl.kl * 12 + parts * 4;
+}
 
 hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,
                               int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
@@ -105,16 +164,23 @@ hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const voi
     const int nsx = (nmax + 256 * kScoreBPL<true> - 1) / (256 * kScoreBPL<true>);
     const long grid = (long)n_spec + (long)nsx * units;
     if (grid > 0x7fffffffL) return hipErrorInvalidValue;
-    // keys per thread of the fused top-K (0: the unit is too large; the top-K kernel follows)
-    // (measured at 8192 blocks, 32 keys per thread on 256 threads lose to the separate 1024-thread kernel)
-    const int kpt = nmax <= 256 ? 1 : nmax <= 512 ? 2 : nmax <= 1024 ? 4 : nmax <= 2048 ? 8
-                  : nmax <= 4096 ? 16 : 0;
-#define PRR_SS(DD, K)                                                                                    \
-    if (kv.d == DD && kpt == K) {                                                                        \
-        select_spec_kernel<DD, K><<<(int)grid, 256, 0, stream>>>(ap, sp, tp, arrivals, nsx * units, nsx); \
+    const SelectSpecPlan plan = select_spec_plan(nmax, topk);
+    CandParams cp;
+    cp.kl = plan.kl;
+    char *cbase = (char *)ws + attn_workspace_bytes(kv.batch, hq, kv.hkv, kv.d, block, p_cap);
+    cp.key = (uint64_t *)cbase;
+    cp.idx = (int32_t *)(cbase + (size_t)units * nsx * plan.kl * 8);
+    cp.cnt = (int32_t *)(cbase + (size_t)units * nsx * plan.kl * 12);
+    const int kpt = plan.kpt;
+    const bool two = plan.two;
+#define PRR_SS(DD, K, T)                                                                                      \
+    if (kv.d == DD && kpt == K && two == T) {                                                                 \
+        select_spec_kernel<DD, K, T><<<(int)grid, 256, 0, stream>>>(ap, sp, tp, cp, arrivals, nsx * units, nsx); \
     } else
-    PRR_SS(128, 0) PRR_SS(128, 1) PRR_SS(128, 2) PRR_SS(128, 4) PRR_SS(128, 8) PRR_SS(128, 16)
-    PRR_SS(64, 0) PRR_SS(64, 1) PRR_SS(64, 2) PRR_SS(64, 4) PRR_SS(64, 8) PRR_SS(64, 16)
+    PRR_SS(128, 0, false) PRR_SS(128, 1, false) PRR_SS(128, 2, false) PRR_SS(128, 4, false) PRR_SS(128, 8, false)
+    PRR_SS(128, 1, true) PRR_SS(128, 2, true) PRR_SS(128, 4, true) PRR_SS(128, 8, true) PRR_SS(128, 16, true)
+    PRR_SS(64, 0, false) PRR_SS(64, 1, false) PRR_SS(64, 2, false) PRR_SS(64, 4, false) PRR_SS(64, 8, false)
+    PRR_SS(64, 1, true) PRR_SS(64, 2, true) PRR_SS(64, 4, true) PRR_SS(64, 8, true) PRR_SS(64, 16, true)
     { return hipErrorInvalidValue; }
 #undef PRR_SS
     hipError_t e = hipGetLastError();

@@ -95,7 +95,7 @@ class PRRLayer:
         self.M = bd.BlockSet.empty(B, H, max(1, topk), dev)
         self.state = bd.AttnState.empty(B, num_q_heads, d, dev)
         self.out = torch.zeros((B, num_q_heads, d), dtype=torch.float32, device=dev)
-        self.ws_spec = bd.workspace_for(kv, num_q_heads, block, max(1, budget))
+        self.ws_spec = bd.select_spec_workspace_for(kv, num_q_heads, block, topk, max(1, budget))
         self.ws_repair = bd.workspace_for(kv, num_q_heads, block, max(1, topk))
         self._streams = None
 

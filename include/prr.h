@@ -145,7 +145,11 @@ prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv
  *     prr_spec_attn(q, num_q_heads, kv, block, P, scale, out, ws, ws_bytes)
  * compute, as one grid whose workgroups do either part (bf16 caches; fp32 caches run the two calls in
  * turn), followed by the top-K on the same stream.  P and M must be non-NULL; A->cap and M->cap >= topk;
- * N_b <= 32768.  ws: prr_attn_workspace_bytes(..., P->cap), as for prr_spec_attn. */
+ * N_b <= 32768.  ws: prr_select_spec_workspace_bytes(kv, num_q_heads, block, topk, P->cap): the attention
+ * workspace of prr_spec_attn plus room for top-K candidates. */
+size_t prr_select_spec_workspace_bytes(const prr_kv_cache *kv, int32_t num_q_heads, int32_t block, int32_t topk,
+                                       int32_t cap);
+
 prr_status prr_select_spec(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
                            int32_t block, int32_t topk, const prr_block_set *P, double *scores,
                            prr_block_set *A, prr_block_set *M, float scale, prr_attn_state *out, void *ws,

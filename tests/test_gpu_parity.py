@@ -301,13 +301,16 @@ def test_predictor_trajectory_bit_exact():
     assert live.cpu().numpy().tolist() == [[-(-l // w.block)] * H for l in lens]
 
 
-@pytest.mark.parametrize("nblocks", [300, 900, 2048, 2049, 4097])
-def test_select_spec_fused_topk_shapes(nblocks):
-    """The fused launch's top-K runs in the last scoring workgroup with 1, 2, 4, 8 or 16 keys per thread
-    (units of up to 256, 512, 1024, 2048, 4096 blocks) and falls back to the separate top-K kernel beyond
-    4096 blocks: every shape against the separate calls (bit for bit) and the oracle's scores and sets."""
+@pytest.mark.parametrize("nblocks,topk", [(300, 40), (900, 40), (2048, 40), (2049, 40), (4097, 40),
+                                         (8192, 128), (4096, 600)])
+def test_select_spec_fused_topk_shapes(nblocks, topk):
+    """The fused launch's top-K runs in the last scoring workgroup: over all scores with 1, 2, 4 or 8 keys
+    per thread (units of up to 2048 blocks), and beyond that in two stages (local top-min(K, 512)
+    candidates of every scoring workgroup, then the top-K of the candidates, up to 16 per thread; K = 600
+    caps the local candidates at 512).  Every shape against the separate calls (bit for bit) and the
+    oracle's scores and sets."""
     lens = [nblocks * 16, nblocks * 16 - 37]
-    w = wl.Workload(f"fused_{nblocks}", 2, 8, 2, 64, max(lens), 16, 40, "bf16", seed=900 + nblocks,
+    w = wl.Workload(f"fused_{nblocks}", 2, 8, 2, 64, max(lens), 16, topk, "bf16", seed=900 + nblocks,
                     seq_lens=lens)
     inp = wl.make_inputs(w, "cuda")
     q, kv = oracle_view(inp)
@@ -317,11 +320,12 @@ def test_select_spec_fused_topk_shapes(nblocks):
     rng = np.random.default_rng(nblocks)
     P, _ = _random_sets(w, rng, [(30, 0), (0, 0), (40, 0), (7, 0)])
     Pd = sets_to_device(P, 48)
+    assert w.topk <= 600
     scores, A, M = bd.select(inp.q[0], dkv, meta, w.block, w.topk, P=Pd)
     state = bd.spec_attn(inp.q[0], dkv, w.block, Pd, w.scale)
     fs, fA, fM, fstate = bd.select_spec(inp.q[0], dkv, meta, w.block, w.topk, Pd, w.scale)
     # a second call on the same workspace: the arrival counters were left at zero
-    ws = bd.workspace_for(dkv, w.num_q_heads, w.block, Pd.cap)
+    ws = bd.select_spec_workspace_for(dkv, w.num_q_heads, w.block, w.topk, Pd.cap)
     for _ in range(2):
         fs2, fA2, fM2, fstate2 = bd.select_spec(inp.q[0], dkv, meta, w.block, w.topk, Pd, w.scale, ws=ws)
         assert fA2.lists() == A.lists() and fM2.lists() == M.lists()
