@@ -210,6 +210,59 @@ def build_meta(kv: PagedKV, block: int, Hkv: int) -> list:
     return out
 
 
+def block_mean(kv: PagedKV, b: int, kvh: int, p: int, block: int) -> np.ndarray:
+    """Channel-wise mean key of block p over its valid tokens: the block compressed to one representative
+    ([paper] §2.1: selection compresses each block, e.g. by its mean).  The tokens are summed one after
+    another from +0.0 in float64, the sum is divided by their count, and the mean is rounded once to
+    float32 (the stored summary)."""
+    K, _ = gather_kv(kv, b, kvh, [p], block)
+    acc = np.zeros(K.shape[1])
+    for t in range(K.shape[0]):
+        acc = acc + K[t]
+    return (acc / K.shape[0]).astype(np.float32).astype(np.float64)
+
+
+def build_mean_meta(kv: PagedKV, block: int, Hkv: int) -> list:
+    """[b][kvh] -> mean [N_b][d] for every block of every sequence."""
+    out = []
+    for b in range(kv.seq_len.shape[0]):
+        row = []
+        for h in range(Hkv):
+            nb = num_blocks(kv, b, block)
+            mean = np.empty((nb, kv.head_dim))
+            for p in range(nb):
+                mean[p] = block_mean(kv, b, h, p, block)
+            row.append(mean)
+        out.append(row)
+    return out
+
+
+def mean_scores(qbar: np.ndarray, mean: np.ndarray) -> np.ndarray:
+    """Mean-pooled criticality s_p = sum_i Qbar_i mean_{p,i} for every block p, channels added one after
+    another from +0.0 with a separate multiply and add.  mean: [N][d]."""
+    s = np.zeros(mean.shape[0])
+    for i in range(mean.shape[1]):
+        s = s + qbar[i] * mean[:, i]
+    return s
+
+
+def select_mean(q_all: np.ndarray, mean_meta: list, G: int, k: int, P=None):
+    """Selection with mean-pooled scores for every (b, kvh): scores, A = top-k, M = A \\ P."""
+    scores, A, M = [], [], []
+    for b in range(len(mean_meta)):
+        srow, arow, mrow = [], [], []
+        for h in range(len(mean_meta[0])):
+            s = mean_scores(representative_query(q_all, b, h, G), mean_meta[b][h])
+            a = topk_blocks(s, k)
+            srow.append(s)
+            arow.append(a)
+            mrow.append(set_minus(a, P[b][h]) if P is not None else None)
+        scores.append(srow)
+        A.append(arow)
+        M.append(mrow)
+    return scores, A, M
+
+
 def representative_query(q_all: np.ndarray, b: int, kvh: int, G: int) -> np.ndarray:
     """Q_bar = (1/G) sum_g Q_g over the G query heads sharing kv head kvh ([paper] A.1)."""
     acc = np.zeros(q_all.shape[2])

@@ -11,6 +11,7 @@ import pytest
 
 import test_oracle_attention as ta
 import test_oracle_ema as te
+import test_oracle_mean as tm
 import test_oracle_select as ts
 from _util import oracle_view
 from block_sparse_attention_quest_amd import workloads as wl
@@ -113,6 +114,35 @@ def calibrate_divide_by_T(IS, k, grid=None):
     return H * (T - 1) / T, best
 
 
+def mean_divides_by_block_size(kv, b, kvh, p, block):
+    K, _ = orc.gather_kv(kv, b, kvh, [p], block)
+    acc = np.zeros(K.shape[1])
+    for t in range(K.shape[0]):
+        acc = acc + K[t]
+    return (acc / block).astype(np.float32).astype(np.float64)
+
+
+def mean_scores_abs(qbar, mean):
+    s = np.zeros(mean.shape[0])
+    for i in range(mean.shape[1]):
+        s = s + abs(qbar[i]) * mean[:, i]
+    return s
+
+
+def mean_skips_first_token(kv, b, kvh, p, block):
+    K, _ = orc.gather_kv(kv, b, kvh, [p], block)
+    K = K[1:] if K.shape[0] > 1 else K
+    return (K.sum(axis=0) / K.shape[0]).astype(np.float32).astype(np.float64)
+
+
+def _mean_checks():
+    q, kv = oracle_view(wl.make_inputs(tm.W))
+    fxm = (q[0], kv, orc.build_meta(kv, tm.W.block, tm.W.num_kv_heads),
+           orc.build_mean_meta(kv, tm.W.block, tm.W.num_kv_heads))
+    return [(tm.test_mean_matches_numpy_mean, (fxm,)), (tm.test_mean_score_bounded_by_quest_score, (fxm,)),
+            (tm.test_identical_keys_and_partial_blocks, ()), (tm.test_single_token_blocks_score_is_dot_product, ())]
+
+
 def _attention_checks():
     fx = _small_fixture(ta.SMALL)
     return [(ta.test_decomposition_identity, (fx,)), (ta.test_dense_case_matches_torch_sdpa, (fx,)),
@@ -144,6 +174,9 @@ MUTATIONS = [
     ("ema_predict", ema_predict_minus, _ema_checks),
     ("hit_rate_row", hit_rate_unweighted, _ema_checks),
     ("calibrate", calibrate_divide_by_T, _ema_checks),
+    ("block_mean", mean_divides_by_block_size, _mean_checks),
+    ("block_mean", mean_skips_first_token, _mean_checks),
+    ("mean_scores", mean_scores_abs, _mean_checks),
 ]
 
 
@@ -154,4 +187,4 @@ def test_pins_catch_planted_mistake(monkeypatch, target, mutant, checks):
 
 
 def test_unmutated_oracle_passes_the_same_checks():
-    assert not _fails(*_attention_checks(), *_select_checks(), *_ema_checks())
+    assert not _fails(*_attention_checks(), *_select_checks(), *_ema_checks(), *_mean_checks())
