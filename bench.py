@@ -56,6 +56,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=64, help="(sequence, kv head) units in the CPU sample")
     ap.add_argument("--cpu-steps", type=int, default=0, help="decode steps in the CPU sample (0: all timed)")
+    ap.add_argument("--score-mode", choices=("quest", "mean"), default="quest",
+                    help="block summary selection scores: Quest's min/max bound or the block's mean key")
     ap.add_argument("--append", action="store_true",
                     help="decode-loop mode: every timed step first appends one token per sequence (prr_append, "
                          "timed alone) so the context grows by one token per step")
@@ -90,7 +92,7 @@ def load_traffic(kernel_hash: str):
         return None
 
 
-def cpu_baseline(inp, w, units, steps):
+def cpu_baseline(inp, w, units, steps, score_mode="quest"):
     """Time the oracle on a bounded sample of the same workload: `units` (sequence, kv head) pairs for
     decode steps 0..steps (step 0 has P empty and is not counted), one core (BLAS limited to one
     thread).  Block metadata is built once per unit before timing, as on the GPU."""
@@ -113,13 +115,17 @@ def cpu_baseline(inp, w, units, steps):
             v = wl.to_numpy_bits(inp.v_cache[pages, h].unsqueeze(1))
             n = pages.numel()
             kv = orc.make_paged_kv(k, v, np.arange(n).reshape(1, n), np.array([w.lengths[b]]), w.dtype)
-            mn, mx = orc.build_meta(kv, w.block, 1)[0][0]
+            if score_mode == "quest":
+                mn, mx = orc.build_meta(kv, w.block, 1)[0][0]
+            else:
+                mean = orc.build_mean_meta(kv, w.block, 1)[0][0]
             lv, tr, live, P = np.zeros(0), np.zeros(0), 0, np.zeros(0, dtype=np.int64)
             qs = orc.upcast(wl.to_numpy_bits(inp.q[: steps + 1, b, h * G:(h + 1) * G]), w.dtype)
             for t in range(steps + 1):
                 q = qs[t][None]
                 t0 = time.perf_counter()
-                s = orc.quest_scores(orc.representative_query(q, 0, 0, G), mn, mx)
+                qbar = orc.representative_query(q, 0, 0, G)
+                s = orc.quest_scores(qbar, mn, mx) if score_mode == "quest" else orc.mean_scores(qbar, mean)
                 A = orc.topk_blocks(s, w.topk)
                 M = orc.set_minus(A, P)
                 t1 = time.perf_counter()
@@ -219,7 +225,8 @@ def main():
     t_gen = time.time()
     inp = wl.make_inputs(w, dev)
     kv = bd.KVCache(inp.k_cache, inp.v_cache, inp.page_table, inp.seq_len)
-    layer = PRRLayer(kv, w.num_q_heads, w.block, w.topk, w.topk, ema=w.ema, scale=w.scale)
+    layer = PRRLayer(kv, w.num_q_heads, w.block, w.topk, w.topk, ema=w.ema, scale=w.scale,
+                     score_mode=args.score_mode)
     if args.append:
         k_app, v_app = wl.make_append_tokens(w, dev)
         len0 = inp.seq_len.clone()
@@ -279,7 +286,7 @@ def main():
             flush()
             e0, e1 = ev(), ev()
             e0.record(crit)
-            bd.append(kv, w.block, k_app[i], v_app[i], layer.meta, stream=crit)
+            layer.append(k_app[i], v_app[i], stream=crit)
             e1.record(crit)
             append_pairs.append((e0, e1))
         # 1. layer step with a breakdown
@@ -305,13 +312,13 @@ def main():
                 bd.repair(q, kv, w.block, layer.M, w.scale, iso_state, ws=ws_iso_rep, stream=crit)
             elif what == "select":
                 bd.select(q, kv, layer.meta, w.block, w.topk, P=P, scores=iso_scores, A=iso_A, M=iso_M,
-                          stream=crit)
+                          mode=args.score_mode, stream=crit)
             elif what == "predict":
                 bd.predict(layer.scores, kv.seq_len, w.block, *w.ema, w.topk, iso_level, iso_trend, iso_live,
                            P_next=iso_P, stream=crit)
             elif what == "select_spec":
                 bd.select_spec(q, kv, layer.meta, w.block, w.topk, P, w.scale, scores=iso_scores, A=iso_A,
-                               M=iso_M, out=iso_state, ws=ws_iso_spec, stream=crit)
+                               M=iso_M, out=iso_state, ws=ws_iso_spec, mode=args.score_mode, stream=crit)
             e1.record(crit)
             pairs.append((e0, e1))
         rec.append((tm, *pairs))
@@ -325,13 +332,13 @@ def main():
         layer.reset()
         if args.append:   # back to the initial context: lengths, then the metadata of every block
             inp.seq_len.copy_(len0)
-            bd.build_meta(kv, w.block, layer.meta)
+            (bd.build_meta if args.score_mode == "quest" else bd.build_mean_meta)(kv, w.block, layer.meta)
         layer.step(inp.q[0])
         torch.cuda.synchronize()
         out = []
         for i in range(K):
             if args.append:
-                bd.append(kv, w.block, k_app[i], v_app[i], layer.meta, stream=crit)
+                layer.append(k_app[i], v_app[i], stream=crit)
             flush()
             if two_streams:
                 tm = TwoStreamTimers(ev(), None, None, None, None, ev())
@@ -388,7 +395,9 @@ def main():
     spec_launch_bytes = float(spec_bytes.mean())
     spec_launch_us = float(statistics.mean(spec_us))
     achieved = spec_launch_bytes / (spec_launch_us * 1e-6) / 1e9
-    traffic = load_traffic(kernel_hash) if (w.name == PROFILE_WORKLOAD and not args.append) else None
+    # the committed counters were taken on the default run (Quest scoring, no appends)
+    traffic = (load_traffic(kernel_hash)
+               if (w.name == PROFILE_WORKLOAD and not args.append and args.score_mode == "quest") else None)
 
     med = lambda xs: round(float(statistics.median(xs)), 2)
     result = {
@@ -407,6 +416,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "context": w.context, "block": w.block, "topk_blocks": w.topk,
                    "spec_budget_blocks": w.topk, "ema": list(w.ema), "decode_steps_timed": K,
+                   "score_mode": args.score_mode,
                    "parallelism": "none (1 GPU)", "flush_mib_read_between_kernels": args.flush_mib},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "value_median_step_gbps": round(float(statistics.median(step_gbps)), 1),
@@ -464,7 +474,7 @@ def main():
         steps = args.cpu_steps if args.cpu_steps > 0 else K
         units = min(args.cpu_units, B * H)
         log(f"[bench] timing the CPU oracle on {units} units x {steps} steps")
-        result["cpu_baseline"] = cpu_baseline(inp, w, units, steps)
+        result["cpu_baseline"] = cpu_baseline(inp, w, units, steps, args.score_mode)
     print(json.dumps(result), flush=True)
 
 

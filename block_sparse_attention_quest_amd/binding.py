@@ -22,7 +22,7 @@ PAGE_SIZE = 16
 # Every symbol include/prr.h declares.
 EXPORTS = (
     "prr_max_blocks", "prr_meta_stride", "prr_meta_bytes", "prr_attn_workspace_bytes",
-    "prr_workspace_clear", "prr_build_meta", "prr_append", "prr_select", "prr_select_spec_workspace_bytes",
+    "prr_workspace_clear", "prr_build_meta", "prr_mean_meta_bytes", "prr_build_mean_meta", "prr_append", "prr_select", "prr_select_spec_workspace_bytes",
     "prr_select_spec", "prr_predict",
     "prr_spec_attn",
     "prr_repair", "prr_calibrate_workspace_bytes", "prr_calibrate", "prr_strerror",
@@ -60,13 +60,15 @@ _SIGS = {
     "prr_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "prr_workspace_clear": (ctypes.c_int, [_VP, _SZ, _VP]),
     "prr_build_meta": (ctypes.c_int, [_P(KvCacheStruct), _I32, _VP, _VP]),
-    "prr_append": (ctypes.c_int, [_P(KvCacheStruct), _I32, _VP, _VP, _VP, _VP, _VP]),
-    "prr_select": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _VP, _I32, _I32, _P(BlockSetStruct), _VP,
-                                  _P(BlockSetStruct), _P(BlockSetStruct), _VP]),
+    "prr_mean_meta_bytes": (_SZ, [_P(KvCacheStruct), _I32]),
+    "prr_build_mean_meta": (ctypes.c_int, [_P(KvCacheStruct), _I32, _VP, _VP]),
+    "prr_append": (ctypes.c_int, [_P(KvCacheStruct), _I32, _VP, _VP, _VP, ctypes.c_int, _VP, _VP]),
+    "prr_select": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _VP, ctypes.c_int, _I32, _I32,
+                                  _P(BlockSetStruct), _VP, _P(BlockSetStruct), _P(BlockSetStruct), _VP]),
     "prr_select_spec_workspace_bytes": (_SZ, [_P(KvCacheStruct), _I32, _I32, _I32, _I32]),
-    "prr_select_spec": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _VP, _I32, _I32, _P(BlockSetStruct), _VP,
-                                       _P(BlockSetStruct), _P(BlockSetStruct), _F, _P(AttnStateStruct), _VP, _SZ,
-                                       _VP]),
+    "prr_select_spec": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _VP, ctypes.c_int, _I32, _I32,
+                                       _P(BlockSetStruct), _VP, _P(BlockSetStruct), _P(BlockSetStruct), _F,
+                                       _P(AttnStateStruct), _VP, _SZ, _VP]),
     "prr_predict": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _D, _D, _D, _I32, _VP, _VP, _VP,
                                    _P(BlockSetStruct), _VP]),
     "prr_spec_attn": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _I32, _P(BlockSetStruct), _F,
@@ -79,6 +81,15 @@ _SIGS = {
 }
 
 _lib = None
+
+# prr_score_mode: how selection scores a block (Quest's min/max bound, or the block's mean key)
+SCORE_MODES = {"quest": 0, "mean": 1}
+
+
+def _mode(mode: str) -> int:
+    if mode not in SCORE_MODES:
+        raise ValueError(f"score mode must be one of {sorted(SCORE_MODES)}, not {mode!r}")
+    return SCORE_MODES[mode]
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -262,19 +273,34 @@ def build_meta(kv: KVCache, block: int, meta: Optional[torch.Tensor] = None, str
     return meta
 
 
-def append(kv: KVCache, block: int, k_new: torch.Tensor, v_new: torch.Tensor, meta: torch.Tensor, stream=None):
-    """Append one token per sequence (k_new, v_new: [B][Hkv][d]) to the paged cache at position seq_len,
-    fold its key into the metadata of its block, and advance kv.seq_len in place."""
+def build_mean_meta(kv: KVCache, block: int, meta: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Mean-pooled block metadata [B][Hkv][d][stride] fp32 (the channel-wise mean key of every block)."""
     lib = load_library()
     s = kv.struct()
-    _check(lib.prr_append(ctypes.byref(s), block, _ptr(k_new), _ptr(v_new), _ptr(meta), _ptr(kv.seq_len),
-                          _stream(stream)), "prr_append")
+    if meta is None:
+        stride = lib.prr_meta_stride(ctypes.byref(s), block)
+        meta = torch.empty((kv.batch, kv.num_kv_heads, kv.head_dim, stride), dtype=torch.float32,
+                           device=kv.k.device)
+    _check(lib.prr_build_mean_meta(ctypes.byref(s), block, _ptr(meta), _stream(stream)), "prr_build_mean_meta")
+    return meta
+
+
+def append(kv: KVCache, block: int, k_new: torch.Tensor, v_new: torch.Tensor, meta: torch.Tensor,
+           mode: str = "quest", stream=None):
+    """Append one token per sequence (k_new, v_new: [B][Hkv][d]) to the paged cache at position seq_len,
+    fold its key into the metadata of its block (min/max for mode "quest", the block mean for "mean"),
+    and advance kv.seq_len in place."""
+    lib = load_library()
+    s = kv.struct()
+    _check(lib.prr_append(ctypes.byref(s), block, _ptr(k_new), _ptr(v_new), _ptr(meta), _mode(mode),
+                          _ptr(kv.seq_len), _stream(stream)), "prr_append")
 
 
 def select(q: torch.Tensor, kv: KVCache, meta: torch.Tensor, block: int, topk: int,
            P: Optional[BlockSet] = None, scores: Optional[torch.Tensor] = None,
-           A: Optional[BlockSet] = None, M: Optional[BlockSet] = None, stream=None):
-    """Quest scores [B][Hkv][Nmax] fp64, A (top-k, ascending) and M = A \\ P when P is given."""
+           A: Optional[BlockSet] = None, M: Optional[BlockSet] = None, mode: str = "quest", stream=None):
+    """Block scores [B][Hkv][Nmax] fp64 (Quest's bound, or the mean key's product for mode "mean"),
+    A (top-k, ascending) and M = A \\ P when P is given."""
     lib = load_library()
     s = kv.struct()
     nmax = lib.prr_max_blocks(ctypes.byref(s), block)
@@ -289,7 +315,7 @@ def select(q: torch.Tensor, kv: KVCache, meta: torch.Tensor, block: int, topk: i
     a_s = A.struct()
     p_s = P.struct() if P is not None else None
     m_s = M.struct() if M is not None else None
-    st = lib.prr_select(_ptr(q), q.shape[1], ctypes.byref(s), _ptr(meta), block, topk,
+    st = lib.prr_select(_ptr(q), q.shape[1], ctypes.byref(s), _ptr(meta), _mode(mode), block, topk,
                         ctypes.byref(p_s) if p_s is not None else None, _ptr(scores), ctypes.byref(a_s),
                         ctypes.byref(m_s) if m_s is not None else None, _stream(stream))
     _check(st, "prr_select")
@@ -299,7 +325,7 @@ def select(q: torch.Tensor, kv: KVCache, meta: torch.Tensor, block: int, topk: i
 def select_spec(q: torch.Tensor, kv: KVCache, meta: torch.Tensor, block: int, topk: int, P: BlockSet,
                 scale: float, scores: Optional[torch.Tensor] = None, A: Optional[BlockSet] = None,
                 M: Optional[BlockSet] = None, out: Optional[AttnState] = None, ws: Optional[Workspace] = None,
-                stream=None):
+                mode: str = "quest", stream=None):
     """select(q, ..., P) and spec_attn(q, ..., P) as one launch; returns (scores, A, M, state)."""
     lib = load_library()
     s = kv.struct()
@@ -318,7 +344,7 @@ def select_spec(q: torch.Tensor, kv: KVCache, meta: torch.Tensor, block: int, to
     if ws is None:
         ws = select_spec_workspace_for(kv, Hq, block, topk, P.cap)
     a_s, p_s, m_s, o_s = A.struct(), P.struct(), M.struct(), out.struct()
-    st = lib.prr_select_spec(_ptr(q), Hq, ctypes.byref(s), _ptr(meta), block, topk, ctypes.byref(p_s),
+    st = lib.prr_select_spec(_ptr(q), Hq, ctypes.byref(s), _ptr(meta), _mode(mode), block, topk, ctypes.byref(p_s),
                              _ptr(scores), ctypes.byref(a_s), ctypes.byref(m_s), float(scale), ctypes.byref(o_s),
                              ws.ptr(), ws.nbytes, _stream(stream))
     _check(st, "prr_select_spec")

@@ -11,6 +11,10 @@
 // Blocks born this way take part in selection at once; the predictor starts their state at the next
 // call ([paper] §4.1, state initialisation).  seq_len[b] then advances by one.
 //
+// Mean-pooled metadata (the fp32 channel-wise block means) is recomputed for the block after the token
+// is written: float64 sum over the block's valid tokens in token order, divided by their count, rounded
+// once to float32, as a rebuild does.
+//
 // One workgroup per sequence: its threads cover (kv head, channel); the length is read before and
 // written after a workgroup barrier.
 
@@ -36,7 +40,12 @@ struct AppendParams {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
-template <bool BF16, int D>
+__device__ __forceinline__ double dadd_exact(double a, double b) {
+#pragma clang fp contract(off)
+    return a + b;
+}
+
+template <bool BF16, int D, bool MEAN>
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     __shared__ int s_t;
     const int b = blockIdx.x;
@@ -59,7 +68,17 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
         const size_t vdst = (((size_t)ph * p.hkv + h) * D + i) * kPage + slot;      // [page][Hkv][d][16]
         const size_t row = (((size_t)b * p.hkv + h) * D + i) * 2 * p.stride;        // [B][Hkv][d][2][stride]
         const bool ok = ph >= 0 && ph < p.num_pages;
-        if constexpr (BF16) {
+        if constexpr (MEAN) {
+            if (ok) {
+                if constexpr (BF16) {
+                    ((uint16_t *)p.k)[kdst] = ((const uint16_t *)p.k_new)[src];
+                    ((uint16_t *)p.v)[vdst] = ((const uint16_t *)p.v_new)[src];
+                } else {
+                    ((float *)p.k)[kdst] = ((const float *)p.k_new)[src];
+                    ((float *)p.v)[vdst] = ((const float *)p.v_new)[src];
+                }
+            }
+        } else if constexpr (BF16) {
             const uint16_t kx = ((const uint16_t *)p.k_new)[src];
             const uint16_t vx = ((const uint16_t *)p.v_new)[src];
             uint16_t *m16 = (uint16_t *)p.meta;
@@ -86,6 +105,25 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
             }
         }
     }
+    if constexpr (MEAN) {
+        __syncthreads();   // the new key is in the cache for every thread of the workgroup
+        if (ph >= 0 && ph < p.num_pages) {
+            const int t0 = blk * p.block;
+            for (int idx = threadIdx.x; idx < p.hkv * D; idx += blockDim.x) {
+                const int h = idx / D, i = idx - h * D;
+                double acc = 0.0;
+                for (int tt = t0; tt <= t; ++tt) {
+                    int pg = p.page_table[(size_t)b * p.max_pages + tt / kPage];
+                    pg = min(max(pg, 0), p.num_pages - 1);
+                    const size_t off = (((size_t)pg * p.hkv + h) * kPage + (tt % kPage)) * D + i;
+                    const double x = BF16 ? (double)bf16_bits_to_f32(((const uint16_t *)p.k)[off])
+                                          : (double)((const float *)p.k)[off];
+                    acc = dadd_exact(acc, x);
+                }
+                ((float *)p.meta)[(((size_t)b * p.hkv + h) * D + i) * p.stride + blk] = (float)(acc / (double)(t - t0 + 1));
+            }
+        }
+    }
     __syncthreads();
     if (threadIdx.x == 0 && ph >= 0 && ph < p.num_pages) p.seq_len[b] = t + 1;
 }
@@ -93,7 +131,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 }  // namespace
 
 hipError_t launch_append(const KvDesc &kv, void *k, void *v, int32_t *seq_len, const void *k_new,
-                         const void *v_new, int block, int stride, void *meta, hipStream_t stream) {
+                         const void *v_new, int block, int stride, void *meta, bool mean, hipStream_t stream) {
     AppendParams p;
     p.k = k;
     p.v = v;
@@ -107,13 +145,12 @@ hipError_t launch_append(const KvDesc &kv, void *k, void *v, int32_t *seq_len, c
     p.num_pages = kv.num_pages;
     p.block = block;
     p.stride = stride;
-    if (kv.bf16) {
-        if (kv.d == 128) append_kernel<true, 128><<<kv.batch, 256, 0, stream>>>(p);
-        else append_kernel<true, 64><<<kv.batch, 256, 0, stream>>>(p);
-    } else {
-        if (kv.d == 128) append_kernel<false, 128><<<kv.batch, 256, 0, stream>>>(p);
-        else append_kernel<false, 64><<<kv.batch, 256, 0, stream>>>(p);
-    }
+#define PRR_AP(BF, DD, MN) \
+    if (kv.bf16 == BF && kv.d == DD && mean == MN) append_kernel<BF, DD, MN><<<kv.batch, 256, 0, stream>>>(p); else
+    PRR_AP(true, 128, false) PRR_AP(true, 64, false) PRR_AP(false, 128, false) PRR_AP(false, 64, false)
+    PRR_AP(true, 128, true) PRR_AP(true, 64, true) PRR_AP(false, 128, true) PRR_AP(false, 64, true)
+    { return hipErrorInvalidValue; }
+#undef PRR_AP
     return hipGetLastError();
 }
 

@@ -115,23 +115,38 @@ prr_status prr_build_meta(const prr_kv_cache *kv, int32_t block, void *meta, hip
     PRR_TRY(check_kv(kv));
     PRR_TRY(check_block(kv, block));
     if (!meta) return PRR_EINVAL;
-    return hip_status(prr::launch_meta(desc(kv), block, prr_meta_stride(kv, block), meta, stream));
+    return hip_status(prr::launch_meta(desc(kv), block, prr_meta_stride(kv, block), meta, false, stream));
+}
+
+size_t prr_mean_meta_bytes(const prr_kv_cache *kv, int32_t block) {
+    if (!kv) return 0;
+    return (size_t)kv->batch * kv->num_kv_heads * kv->head_dim * prr_meta_stride(kv, block) * sizeof(float);
+}
+
+prr_status prr_build_mean_meta(const prr_kv_cache *kv, int32_t block, float *meta, hipStream_t stream) {
+    PRR_TRY(check_kv(kv));
+    PRR_TRY(check_block(kv, block));
+    if (!meta) return PRR_EINVAL;
+    return hip_status(prr::launch_meta(desc(kv), block, prr_meta_stride(kv, block), meta, true, stream));
 }
 
 prr_status prr_append(const prr_kv_cache *kv, int32_t block, const void *k_new, const void *v_new, void *meta,
-                      int32_t *seq_len, hipStream_t stream) {
+                      prr_score_mode mode, int32_t *seq_len, hipStream_t stream) {
     PRR_TRY(check_kv(kv));
     PRR_TRY(check_block(kv, block));
     if (!k_new || !v_new || !meta || !seq_len) return PRR_EINVAL;
+    if (mode != PRR_SCORE_QUEST && mode != PRR_SCORE_MEAN) return PRR_EINVAL;
     if (seq_len != kv->seq_len) return PRR_EINVAL;   // the cache's own length array is advanced
     return hip_status(prr::launch_append(desc(kv), const_cast<void *>(kv->k), const_cast<void *>(kv->v), seq_len,
-                                         k_new, v_new, block, prr_meta_stride(kv, block), meta, stream));
+                                         k_new, v_new, block, prr_meta_stride(kv, block), meta,
+                                         mode == PRR_SCORE_MEAN, stream));
 }
 
 prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
-                      int32_t block, int32_t topk, const prr_block_set *P, double *scores,
+                      prr_score_mode mode, int32_t block, int32_t topk, const prr_block_set *P, double *scores,
                       prr_block_set *A, prr_block_set *M, hipStream_t stream) {
     if (!q || !meta || !scores) return PRR_EINVAL;
+    if (mode != PRR_SCORE_QUEST && mode != PRR_SCORE_MEAN) return PRR_EINVAL;
     PRR_TRY(check_kv(kv));
     PRR_TRY(check_block(kv, block));
     PRR_TRY(check_heads(kv, num_q_heads));
@@ -150,7 +165,7 @@ prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv
                                          nmax, topk, P ? P->idx : nullptr, P ? P->count : nullptr,
                                          P ? P->cap : 0, scores, A->idx, A->count, A->cap,
                                          M ? M->idx : nullptr, M ? M->count : nullptr, M ? M->cap : 0,
-                                         stream));
+                                         mode == PRR_SCORE_MEAN, stream));
 }
 
 size_t prr_select_spec_workspace_bytes(const prr_kv_cache *kv, int32_t num_q_heads, int32_t block, int32_t topk,
@@ -163,10 +178,11 @@ size_t prr_select_spec_workspace_bytes(const prr_kv_cache *kv, int32_t num_q_hea
 }
 
 prr_status prr_select_spec(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
-                           int32_t block, int32_t topk, const prr_block_set *P, double *scores,
-                           prr_block_set *A, prr_block_set *M, float scale, prr_attn_state *out, void *ws,
-                           size_t ws_bytes, hipStream_t stream) {
+                           prr_score_mode mode, int32_t block, int32_t topk, const prr_block_set *P,
+                           double *scores, prr_block_set *A, prr_block_set *M, float scale, prr_attn_state *out,
+                           void *ws, size_t ws_bytes, hipStream_t stream) {
     if (!q || !meta || !scores || !P || !M) return PRR_EINVAL;
+    if (mode != PRR_SCORE_QUEST && mode != PRR_SCORE_MEAN) return PRR_EINVAL;
     PRR_TRY(check_kv(kv));
     PRR_TRY(check_block(kv, block));
     PRR_TRY(check_heads(kv, num_q_heads));
@@ -182,7 +198,7 @@ prr_status prr_select_spec(const void *q, int32_t num_q_heads, const prr_kv_cach
     return hip_status(prr::launch_select_spec(desc(kv), q, num_q_heads, meta, block, prr_meta_stride(kv, block),
                                               nmax, topk, P->idx, P->count, P->cap, scores, A->idx, A->count,
                                               A->cap, M->idx, M->count, M->cap, scale, out->acc, out->l, out->m,
-                                              ws, stream));
+                                              ws, mode == PRR_SCORE_MEAN, stream));
 }
 
 prr_status prr_predict(const double *scores, const int32_t *seq_len, int32_t batch,

@@ -31,12 +31,14 @@ hipError_t launch_attn(const KvDesc &kv, const void *q, int hq, int block, const
 
 hipError_t launch_clear(void *ws, size_t bytes, hipStream_t stream);
 
-hipError_t launch_meta(const KvDesc &kv, int block, int stride, void *meta, hipStream_t stream);
+// Block metadata: min/max keys ([d][2][stride] per unit, cache dtype) or, mean = true, the fp32 block
+// means ([d][stride] per unit).
+hipError_t launch_meta(const KvDesc &kv, int block, int stride, void *meta, bool mean, hipStream_t stream);
 
 hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *meta, int block,
                          int stride, int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt,
                          int p_cap, double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap,
-                         int32_t *m_idx, int32_t *m_cnt, int m_cap, hipStream_t stream);
+                         int32_t *m_idx, int32_t *m_cnt, int m_cap, bool mean, hipStream_t stream);
 
 // Top-K + M = A \ P from scores already in place (the second half of launch_select).
 hipError_t launch_topk(const KvDesc &kv, int block, int nmax, int topk, const double *scores,
@@ -62,7 +64,7 @@ hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const voi
                               int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
                               double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
                               int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m,
-                              void *ws, hipStream_t stream);
+                              void *ws, bool mean, hipStream_t stream);
 
 hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batch, int hkv,
                           int block, int nmax, double alpha, double beta, double gamma, int budget,
@@ -72,7 +74,7 @@ hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batc
 // Decode append: token seq_len[b] of every sequence into the cache and its block's metadata, then
 // seq_len[b] += 1.
 hipError_t launch_append(const KvDesc &kv, void *k, void *v, int32_t *seq_len, const void *k_new,
-                         const void *v_new, int block, int stride, void *meta, hipStream_t stream);
+                         const void *v_new, int block, int stride, void *meta, bool mean, hipStream_t stream);
 
 // Calibration workspace: A-set masks per row, EMA checkpoints per (candidate, chunk), chunk sums.
 size_t calib_workspace_bytes(int rows, int blocks, int n);

@@ -82,13 +82,59 @@ __global__ __launch_bounds__(256) void meta_kernel(MetaParams p) {
     }
 }
 
+// Mean-pooled block summary: the channel-wise mean key of every block over its valid tokens, summed in
+// float64 in token order, divided by the token count and rounded once to float32.  Layout [B][Hkv][d]
+// [stride] fp32.  Lane = block (64 per workgroup), waves take channel groups.
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void mean_meta_kernel(MetaParams p) {
+    constexpr int EPL = BF16 ? 8 : 4;          // channels per 16-byte load
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int u = blockIdx.y;
+    const int b = u / p.hkv, kvh = u - b * p.hkv;
+    const int blk = blockIdx.x * 64 + lane;
+    const int slen = max(p.seq_len[b], 0);
+    const int nb = min((slen + p.block - 1) / p.block, p.nmax);
+    if (blk >= nb) return;
+    const int t0 = blk * p.block;
+    const int t1 = min(t0 + p.block, slen);
+    for (int cg = wave; cg < D / EPL; cg += 4) {
+        double acc[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = 0.0;
+        for (int t = t0; t < t1; ++t) {
+            int ph = p.page_table[(size_t)b * p.max_pages + t / kPage];
+            ph = min(max(ph, 0), p.num_pages - 1);
+            const size_t off = (((size_t)ph * p.hkv + kvh) * kPage + (t % kPage)) * D + cg * EPL;
+            if constexpr (BF16) {
+                const uint4 raw = *(const uint4 *)((const uint16_t *)p.k + off);
+                const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[e] = dadd(acc[e], (double)bf16_to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1)))));
+            } else {
+                const float4 raw = *(const float4 *)((const float *)p.k + off);
+                const float x[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = dadd(acc[e], (double)x[e]);
+            }
+        }
+        const double n = (double)(t1 - t0);
+        float *m32 = (float *)p.meta;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const int ch = cg * EPL + e;
+            m32[((size_t)u * D + ch) * p.stride + blk] = (float)(acc[e] / n);
+        }
+    }
+}
+
 // ------------------------------------------------------------------------------------------------
 // Kernels
 // ------------------------------------------------------------------------------------------------
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool MEAN>
 __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
-    score_body<BF16, D>(p, blockIdx.x, blockIdx.y);
+    score_body<BF16, D, false, MEAN>(p, blockIdx.x, blockIdx.y);
 }
 
 template <int KPT, int TPB>
@@ -131,7 +177,7 @@ struct PredictLaunch {
 
 }  // namespace
 
-hipError_t launch_meta(const KvDesc &kv, int block, int stride, void *meta, hipStream_t stream) {
+hipError_t launch_meta(const KvDesc &kv, int block, int stride, void *meta, bool mean, hipStream_t stream) {
     MetaParams p;
     p.k = kv.k;
     p.page_table = kv.page_table;
@@ -144,7 +190,15 @@ hipError_t launch_meta(const KvDesc &kv, int block, int stride, void *meta, hipS
     p.stride = stride;
     p.nmax = (int)((long)kv.max_pages * kPage / block);
     const dim3 grid((p.nmax + 63) / 64, kv.batch * kv.hkv);
-    if (kv.bf16) {
+    if (mean) {
+        if (kv.bf16) {
+            if (kv.d == 128) mean_meta_kernel<true, 128><<<grid, 256, 0, stream>>>(p);
+            else mean_meta_kernel<true, 64><<<grid, 256, 0, stream>>>(p);
+        } else {
+            if (kv.d == 128) mean_meta_kernel<false, 128><<<grid, 256, 0, stream>>>(p);
+            else mean_meta_kernel<false, 64><<<grid, 256, 0, stream>>>(p);
+        }
+    } else if (kv.bf16) {
         if (kv.d == 128) meta_kernel<true, 128><<<grid, 256, 0, stream>>>(p);
         else meta_kernel<true, 64><<<grid, 256, 0, stream>>>(p);
     } else {
@@ -157,7 +211,7 @@ hipError_t launch_meta(const KvDesc &kv, int block, int stride, void *meta, hipS
 hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *meta, int block,
                          int stride, int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt,
                          int p_cap, double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap,
-                         int32_t *m_idx, int32_t *m_cnt, int m_cap, hipStream_t stream) {
+                         int32_t *m_idx, int32_t *m_cnt, int m_cap, bool mean, hipStream_t stream) {
     const int units = kv.batch * kv.hkv;
     ScoreParams sp;
     sp.q = q;
@@ -170,14 +224,23 @@ hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *me
     sp.block = block;
     sp.stride = stride;
     sp.nmax = nmax;
-    const int bpw = 256 * (kv.bf16 ? kScoreBPL<true> : kScoreBPL<false>);   // blocks per workgroup
+    const int bpw = 256 * (mean ? 1 : kv.bf16 ? kScoreBPL<true> : kScoreBPL<false>);   // blocks per workgroup
     const dim3 sgrid((nmax + bpw - 1) / bpw, units);
-    if (kv.bf16) {
-        if (kv.d == 128) score_kernel<true, 128><<<sgrid, 256, 0, stream>>>(sp);
-        else score_kernel<true, 64><<<sgrid, 256, 0, stream>>>(sp);
+    if (mean) {
+        // the fp32 block means do not depend on the cache dtype beyond q's
+        if (kv.bf16) {
+            if (kv.d == 128) score_kernel<true, 128, true><<<sgrid, 256, 0, stream>>>(sp);
+            else score_kernel<true, 64, true><<<sgrid, 256, 0, stream>>>(sp);
+        } else {
+            if (kv.d == 128) score_kernel<false, 128, true><<<sgrid, 256, 0, stream>>>(sp);
+            else score_kernel<false, 64, true><<<sgrid, 256, 0, stream>>>(sp);
+        }
+    } else if (kv.bf16) {
+        if (kv.d == 128) score_kernel<true, 128, false><<<sgrid, 256, 0, stream>>>(sp);
+        else score_kernel<true, 64, false><<<sgrid, 256, 0, stream>>>(sp);
     } else {
-        if (kv.d == 128) score_kernel<false, 128><<<sgrid, 256, 0, stream>>>(sp);
-        else score_kernel<false, 64><<<sgrid, 256, 0, stream>>>(sp);
+        if (kv.d == 128) score_kernel<false, 128, false><<<sgrid, 256, 0, stream>>>(sp);
+        else score_kernel<false, 64, false><<<sgrid, 256, 0, stream>>>(sp);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -17,6 +17,9 @@
 // issues one load per channel for all d channels before using any (a wave's load covers 64 consecutive
 // blocks), then accumulates in channel order.
 //
+// Mean-pooled scoring ([paper] §2.1: selection compresses each block, e.g. by its mean): s_p = sum_i
+// qbar_i mean_{p,i} over the fp32 block means ([d][N] per unit), in channel order, one block per lane.
+//
 // Top-K ([paper] §1, §2.1; ties to the smaller block index): one workgroup per (sequence, kv head) keeps
 // all N keys in registers (order-preserving 64-bit images of the fp64 scores; 256 threads with up to 8
 // contiguous keys each up to 2048 keys) and runs an MSD radix select with 4-bit digits: per pass each
@@ -294,16 +297,17 @@ struct ScoreParams {
     int hq, hkv, G, block, stride, nmax;
 };
 
-// Blocks per lane of the scoring workgroups: two for bf16 metadata (one 4-byte load per channel covers
-// both), one for fp32.
-template <bool BF16>
-constexpr int kScoreBPL = BF16 ? 2 : 1;
+// Blocks per lane of the scoring workgroups: two for bf16 min/max metadata (one 4-byte load per channel
+// covers both), one for fp32 metadata (fp32 min/max, or the fp32 block means of mean-pooled scoring).
+template <bool BF16, bool MEAN = false>
+constexpr int kScoreBPL = (BF16 && !MEAN) ? 2 : 1;
 
 // Scores blocks [256 BPL bx, 256 BPL (bx + 1)) of unit u (BPL consecutive blocks per lane).  COHERENT:
 // the scores are stored with device-scope stores, for a reader on another XCD within the same launch.
-template <bool BF16, int D, bool COHERENT = false>
-__device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u, double (&kept)[kScoreBPL<BF16>]) {
-    constexpr int BPL = kScoreBPL<BF16>;   // one 4-byte load per channel
+template <bool BF16, int D, bool COHERENT = false, bool MEAN = false>
+__device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u,
+                                           double (&kept)[kScoreBPL<BF16, MEAN>]) {
+    constexpr int BPL = kScoreBPL<BF16, MEAN>;   // one 4-byte load per channel
     __shared__ double s_qbar[D];
     __shared__ int s_row[D];             // metadata row of channel i: 1 (max) when qbar_i >= 0, else 0 (min)
     const int b = u / p.hkv, kvh = u - b * p.hkv;
@@ -330,17 +334,21 @@ __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u, 
     // and each lane adds its own block offset.
     // Buffer loads: the unit's metadata is one buffer resource (scalar base), the row offset a scalar
     // and the lane's block offset the only vector operand, shared by all d loads.
-    constexpr int ES = BF16 ? 2 : 4;   // element size
-    const char *ubase = (const char *)p.meta + (size_t)u * D * 2 * p.stride * ES;
+    // mean-pooled scoring: one fp32 row (the block means) per channel, [d][stride]
+    constexpr int ES = (BF16 && !MEAN) ? 2 : 4;   // element size
+    constexpr int ROWS = MEAN ? 1 : 2;            // rows per channel
+    const char *ubase = (const char *)p.meta + (size_t)u * D * ROWS * p.stride * ES;
     const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void *)ubase, (short)0, D * 2 * p.stride * ES, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void *)ubase, (short)0, D * ROWS * p.stride * ES, 0x00020000);
     const int voff = p0 * ES;
     uint32_t raw[D];
 #pragma unroll
     for (int i = 0; i < D; ++i) {
         // qbar >= 0: the max term is qbar * mx (row 1); otherwise qbar * mn (row 0)
         const int sgn = __builtin_amdgcn_readfirstlane(s_row[i]);
-        if constexpr (BF16 && BPL == 2)
+        if constexpr (MEAN)
+            raw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, i * p.stride * ES, 0);
+        else if constexpr (BF16 && BPL == 2)
             raw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, (2 * i + sgn) * p.stride * ES, 0);
         else if constexpr (BF16)
             raw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsrc, voff, (2 * i + sgn) * p.stride * ES, 0);
@@ -358,7 +366,8 @@ __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u, 
         const double qb = s_qbar[i];
 #pragma unroll
         for (int e = 0; e < BPL; ++e) {
-            const double x = BF16 ? (double)bf16_to_f32((uint16_t)(r >> (16 * e))) : (double)__uint_as_float(r);
+            const double x = (BF16 && !MEAN) ? (double)bf16_to_f32((uint16_t)(r >> (16 * e)))
+                                             : (double)__uint_as_float(r);
             acc[e] = dadd(acc[e], dmul(qb, x));
         }
         // the chains of a lane's blocks advance together, channel by channel (otherwise the compiler runs
@@ -380,10 +389,10 @@ __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u, 
 }
 
 // The same without handing the scores back.
-template <bool BF16, int D, bool COHERENT = false>
+template <bool BF16, int D, bool COHERENT = false, bool MEAN = false>
 __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u) {
-    double kept[kScoreBPL<BF16>];
-    score_body<BF16, D, COHERENT>(p, bx, u, kept);
+    double kept[kScoreBPL<BF16, MEAN>];
+    score_body<BF16, D, COHERENT, MEAN>(p, bx, u, kept);
 }
 
 // ------------------------------------------------------------------------------------------------

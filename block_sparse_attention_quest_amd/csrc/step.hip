@@ -122,11 +122,11 @@ hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const voi
                               int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
                               double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
                               int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m,
-                              void *ws, hipStream_t stream) {
-    if (!kv.bf16) {
-        // fp32 caches (exact-input checks): the two passes one after the other
+                              void *ws, bool mean, hipStream_t stream) {
+    if (!kv.bf16 || mean) {
+        // fp32 caches (exact-input checks) and mean-pooled scoring: the two passes one after the other
         hipError_t e = launch_select(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_cap, scores,
-                                     a_idx, a_cnt, a_cap, m_idx, m_cnt, m_cap, stream);
+                                     a_idx, a_cnt, a_cap, m_idx, m_cnt, m_cap, mean, stream);
         if (e != hipSuccess) return e;
         return launch_attn(kv, q, hq, block, p_idx, p_cnt, p_cap, scale, acc, l, m, nullptr, false, ws, stream);
     }

@@ -70,10 +70,14 @@ class TwoStreamTimers:
 
 class PRRLayer:
     """Device state of one attention layer for a batch: paged cache, block metadata, predictor state,
-    block sets (P double-buffered), attention state and workspaces."""
+    block sets (P double-buffered), attention state and workspaces.
+
+    score_mode "quest" scores blocks by Quest's bound over channel-wise min/max keys; "mean" by the
+    product of the representative query with each block's mean key (the two block summaries the pages
+    name for selection).  The metadata kept in ``meta`` is the one the mode reads."""
 
     def __init__(self, kv: bd.KVCache, num_q_heads: int, block: int, topk: int, budget: int,
-                 ema=(0.6, 0.3, 0.5), scale: Optional[float] = None):
+                 ema=(0.6, 0.3, 0.5), scale: Optional[float] = None, score_mode: str = "quest"):
         dev = kv.k.device
         self.kv = kv
         self.hq = num_q_heads
@@ -83,7 +87,10 @@ class PRRLayer:
         self.alpha, self.beta, self.gamma = (float(x) for x in ema)
         self.scale = float(scale) if scale is not None else kv.head_dim ** -0.5
         B, H, d = kv.batch, kv.num_kv_heads, kv.head_dim
-        self.meta = bd.build_meta(kv, block)
+        if score_mode not in bd.SCORE_MODES:
+            raise ValueError(f"score_mode must be one of {sorted(bd.SCORE_MODES)}")
+        self.score_mode = score_mode
+        self.meta = bd.build_meta(kv, block) if score_mode == "quest" else bd.build_mean_meta(kv, block)
         self.nmax = bd.max_blocks(kv, block)
         self.scores = torch.zeros((B, H, self.nmax), dtype=torch.float64, device=dev)
         self.level = torch.zeros_like(self.scores)
@@ -102,6 +109,10 @@ class PRRLayer:
     @property
     def P_cur(self) -> bd.BlockSet:
         return self.P[self.cur]
+
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
+        """Append one decoded token per sequence to the cache and fold it into this layer's metadata."""
+        bd.append(self.kv, self.block, k_new, v_new, self.meta, mode=self.score_mode, stream=stream)
 
     def reset(self):
         """Forget the predictor state (a fresh decode: the first step runs with P empty)."""
@@ -124,7 +135,7 @@ class PRRLayer:
         if timers and timers.start:
             timers.start.record(s)
         bd.select_spec(q, self.kv, self.meta, self.block, self.topk, P, self.scale, scores=self.scores, A=self.A,
-                       M=self.M, out=self.state, ws=self.ws_spec, stream=s)
+                       M=self.M, out=self.state, ws=self.ws_spec, mode=self.score_mode, stream=s)
         if timers and timers.select_spec_end:
             timers.select_spec_end.record(s)
         bd.repair(q, self.kv, self.block, self.M, self.scale, self.state, out=self.out, ws=self.ws_repair,
@@ -160,7 +171,7 @@ class PRRLayer:
         e_ready.record(crit)
         side.wait_event(e_ready)
         bd.select(q, self.kv, self.meta, self.block, self.topk, P=P, scores=self.scores, A=self.A, M=self.M,
-                  stream=crit)
+                  mode=self.score_mode, stream=crit)
         e_sel.record(crit)
         if timers and timers.select_end:
             timers.select_end.record(crit)

@@ -45,6 +45,14 @@ typedef enum prr_status {
 
 typedef enum prr_dtype { PRR_F32 = 0, PRR_BF16 = 1 } prr_dtype;
 
+/* How selection scores a block ([paper] §2.1: each block is compressed to a representative scored
+ * against the query):
+ *   PRR_SCORE_QUEST  Quest's bound over the channel-wise min/max keys ([paper] A.1; metadata of
+ *                    prr_build_meta);
+ *   PRR_SCORE_MEAN   the block's mean key ("e.g., mean"): sum_i qbar_i mean_{p,i} (metadata of
+ *                    prr_build_mean_meta). */
+typedef enum prr_score_mode { PRR_SCORE_QUEST = 0, PRR_SCORE_MEAN = 1 } prr_score_mode;
+
 /* Paged KV cache.  Page size must be 16 tokens.  One (page, kv head) tile is contiguous:
  *   k: [num_pages][num_kv_heads][page_size][head_dim]  (token-major tile)
  *   v: [num_pages][num_kv_heads][head_dim][page_size]  (channel-major tile)
@@ -114,18 +122,28 @@ prr_status prr_workspace_clear(void *ws, size_t ws_bytes, hipStream_t stream);
  * block must be a positive multiple of page_size.  Reads all of K once; not part of the per-step path. */
 prr_status prr_build_meta(const prr_kv_cache *kv, int32_t block, void *meta, hipStream_t stream);
 
+/* Bytes of mean-pooled block metadata: batch * num_kv_heads * head_dim * prr_meta_stride * 4. */
+size_t prr_mean_meta_bytes(const prr_kv_cache *kv, int32_t block);
+
+/* Mean-pooled block metadata ([paper] §2.1: a block compressed to its mean key).  meta layout:
+ * [batch][num_kv_heads][head_dim][stride] fp32, column p = block p: the channel-wise mean of the block's
+ * valid tokens, summed in float64 in token order, divided by their count, rounded once to float32.
+ * Blocks at or beyond ceil(seq_len / block) are not written. */
+prr_status prr_build_mean_meta(const prr_kv_cache *kv, int32_t block, float *meta, hipStream_t stream);
+
 /* Decode-loop append (one token per sequence and step; [paper] §4.1: blocks are born as decoding grows
  * the context, and [paper] A.1: the metadata of the block being filled must cover its tokens).  For every
  * sequence b with t = seq_len[b] < max_pages * page_size: writes k_new[b][h] to the K cache and
  * v_new[b][h] to the V cache at position t (physical page page_table[b][t / page_size], slot t mod
  * page_size; the V tile is channel-major), updates the metadata of block t / block (row 0 = channel-wise
  * min, row 1 = max; the block's first token sets both, later tokens take the running min/max, which equals
- * a rebuild by prr_build_meta over the block's valid tokens), then sets seq_len[b] = t + 1.  A sequence
+ * a rebuild by prr_build_meta over the block's valid tokens; with mode PRR_SCORE_MEAN, meta holds block
+ * means and the block's mean is recomputed as prr_build_mean_meta does), then sets seq_len[b] = t + 1.  A sequence
  * whose cache is full (or whose page-table entry is out of range) is left untouched.
  * k_new, v_new: [batch][num_kv_heads][head_dim] in the cache dtype, device.  seq_len must be kv->seq_len
  * (written in place); kv->k and kv->v are written.  meta as for prr_build_meta. */
 prr_status prr_append(const prr_kv_cache *kv, int32_t block, const void *k_new, const void *v_new, void *meta,
-                      int32_t *seq_len, hipStream_t stream);
+                      prr_score_mode mode, int32_t *seq_len, hipStream_t stream);
 
 /* Quest selection, GQA-extended ([paper] A.1; [paper] §1, §2.1 top-K selection; [paper] §3 M = A \ P).
  *   scores[b][kvh][p] (fp64, row length prr_max_blocks) = sum_{i=0}^{d-1} max(qbar_i mn_{p,i},
@@ -136,7 +154,7 @@ prr_status prr_append(const prr_kv_cache *kv, int32_t block, const void *k_new, 
  * P may be NULL (then M must be NULL).  A->cap and M->cap must be >= topk.  N_b must not exceed
  * 32768.  q: [batch][num_q_heads][head_dim], device, dtype of the cache. */
 prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
-                      int32_t block, int32_t topk, const prr_block_set *P, double *scores,
+                      prr_score_mode mode, int32_t block, int32_t topk, const prr_block_set *P, double *scores,
                       prr_block_set *A, prr_block_set *M, hipStream_t stream);
 
 /* Selection and the speculative pass over P together (the overlap of [paper] §1, Figure 1 flow, and §3:
@@ -151,9 +169,9 @@ size_t prr_select_spec_workspace_bytes(const prr_kv_cache *kv, int32_t num_q_hea
                                        int32_t cap);
 
 prr_status prr_select_spec(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
-                           int32_t block, int32_t topk, const prr_block_set *P, double *scores,
-                           prr_block_set *A, prr_block_set *M, float scale, prr_attn_state *out, void *ws,
-                           size_t ws_bytes, hipStream_t stream);
+                           prr_score_mode mode, int32_t block, int32_t topk, const prr_block_set *P,
+                           double *scores, prr_block_set *A, prr_block_set *M, float scale, prr_attn_state *out,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* EMA level/trend predictor, one decode step ([paper] §4.1; [blog] Eqs. (2)-(3)).
  * For every (b, kvh) with N_b = ceil(seq_len[b] / block) blocks and live[b][kvh] blocks that already

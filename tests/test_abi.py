@@ -98,10 +98,12 @@ def test_select_and_predict_argument_errors(lib):
     A = _set(64)
     P = _set(64)
     M = _set(64)
-    sel = lambda topk=64, A=A, P=P, M=M, meta=1, kv=kv, block=64: lib.prr_select(
-        1, 32, ctypes.byref(kv), meta, block, topk, ctypes.byref(P) if P else None, 1, ctypes.byref(A),
+    sel = lambda topk=64, A=A, P=P, M=M, meta=1, kv=kv, block=64, mode=0: lib.prr_select(
+        1, 32, ctypes.byref(kv), meta, mode, block, topk, ctypes.byref(P) if P else None, 1, ctypes.byref(A),
         ctypes.byref(M) if M else None, None)
     assert sel(meta=None) == 1
+    assert sel(mode=2) == 1                       # unknown score mode
+    assert sel(mode=-1) == 1
     assert sel(topk=65) == 1                      # A cap too small
     assert sel(topk=-1) == 1
     assert sel(M=None) == 1                       # P without M
@@ -114,6 +116,11 @@ def test_select_and_predict_argument_errors(lib):
     assert pred(nmax=40000) == 2
     assert lib.prr_build_meta(ctypes.byref(kv), 64, None, None) == 1
     assert lib.prr_build_meta(ctypes.byref(_kv(max_pages=10)), 64, 1, None) == 1   # 160 tokens % 64
+    assert lib.prr_build_mean_meta(ctypes.byref(kv), 64, None, None) == 1
+    assert lib.prr_build_mean_meta(ctypes.byref(_kv(max_pages=10)), 64, 1, None) == 1
+    assert lib.prr_build_mean_meta(None, 64, 1, None) == 1
+    # fp32 [B][Hkv][d][stride]: 2 * 8 * 128 * 2048 * 4
+    assert lib.prr_mean_meta_bytes(ctypes.byref(kv), 16) == 2 * 8 * 128 * 2048 * 4
 
 
 def test_calibrate_argument_errors(lib):
@@ -140,12 +147,13 @@ def test_select_spec_argument_errors(lib):
     A, P, M = _set(64), _set(64), _set(64)
     st = _state()
     need = lib.prr_attn_workspace_bytes(2, 32, 8, 128, 64, 64)
-    call = lambda q=1, meta=1, topk=64, P=P, A=A, M=M, out=st, ws=1, wsb=need, kv=kv, block=64: lib.prr_select_spec(
-        q, 32, ctypes.byref(kv), meta, block, topk, ctypes.byref(P) if P else None, 1,
+    call = lambda q=1, meta=1, topk=64, P=P, A=A, M=M, out=st, ws=1, wsb=need, kv=kv, block=64, mode=0: lib.prr_select_spec(
+        q, 32, ctypes.byref(kv), meta, mode, block, topk, ctypes.byref(P) if P else None, 1,
         ctypes.byref(A) if A else None, ctypes.byref(M) if M else None, 0.1,
         ctypes.byref(out) if out else None, ws, wsb, None)
     assert call(q=None) == 1
     assert call(meta=None) == 1
+    assert call(mode=3) == 1
     assert call(P=None) == 1                      # P and M are required
     assert call(M=None) == 1
     assert call(A=None) == 1
@@ -162,9 +170,10 @@ def test_select_spec_argument_errors(lib):
 def test_append_argument_errors(lib):
     kv = _kv()
     sl = kv.seq_len
-    call = lambda kv=kv, block=64, k=1, v=1, meta=1, seq=sl: lib.prr_append(
-        ctypes.byref(kv) if kv is not None else None, block, k, v, meta, seq, None)
+    call = lambda kv=kv, block=64, k=1, v=1, meta=1, seq=sl, mode=0: lib.prr_append(
+        ctypes.byref(kv) if kv is not None else None, block, k, v, meta, mode, seq, None)
     assert call(kv=None) == 1
+    assert call(mode=5) == 1
     assert call(k=None) == 1
     assert call(v=None) == 1
     assert call(meta=None) == 1

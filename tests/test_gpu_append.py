@@ -47,18 +47,20 @@ APPEND_CASES = [
 ]
 
 
+@pytest.mark.parametrize("mode", ["quest", "mean"])
 @pytest.mark.parametrize("case", APPEND_CASES, ids=[c[0] for c in APPEND_CASES])
-def test_append_matches_definition_and_rebuild(case):
+def test_append_matches_definition_and_rebuild(case, mode):
     name, B, Hq, Hkv, d, S, lens, dt, n = case
     w = wl.Workload(name, B, Hq, Hkv, d, max(lens), S, 4, dt, seed=300 + n, seq_lens=lens, append_tokens=n)
     inp = wl.make_inputs(w, "cuda")
     dkv = device_kv(inp)
-    meta = bd.build_meta(dkv, S)
+    build = bd.build_meta if mode == "quest" else bd.build_mean_meta
+    meta = build(dkv, S)
     k_host, v_host = inp.k_cache.cpu().clone(), inp.v_cache.cpu().clone()
     pt, sl = inp.page_table.cpu(), inp.seq_len.cpu().clone()
     kn, vn = wl.make_append_tokens(w, "cuda")
     for t in range(n):
-        bd.append(dkv, S, kn[t], vn[t], meta)
+        bd.append(dkv, S, kn[t], vn[t], meta, mode=mode)
         _expected_append(k_host, v_host, pt, sl, kn[t].cpu(), vn[t].cpu())
     torch.cuda.synchronize()
     assert torch.equal(inp.seq_len.cpu(), sl)
@@ -67,10 +69,18 @@ def test_append_matches_definition_and_rebuild(case):
     assert torch.equal(inp.v_cache.cpu().view(torch.int16 if dt == "bf16" else torch.int32),
                        v_host.view(torch.int16 if dt == "bf16" else torch.int32))
     # the incrementally kept metadata equals a rebuild, bit for bit, on every existing block
-    rebuilt = bd.build_meta(dkv, S)
+    rebuilt = build(dkv, S)
     gm = wl.to_numpy_bits(meta)
     gr = wl.to_numpy_bits(rebuilt)
     _, okv = _host_kv(w, k_host, v_host, pt, sl)
+    if mode == "mean":
+        omean = orc.build_mean_meta(okv, S, Hkv)
+        for b in range(B):
+            nb = -(-int(sl[b]) // S)
+            assert np.array_equal(gm[b, ..., :nb], gr[b, ..., :nb]), b
+            for h in range(Hkv):
+                assert np.array_equal(gm[b, h, :, :nb].T.astype(np.float64), omean[b][h]), (b, h)
+        return
     ometa = orc.build_meta(okv, S, Hkv)
     for b in range(B):
         nb = -(-int(sl[b]) // S)
@@ -87,33 +97,35 @@ def _host_kv(w, k, v, pt, sl):
                                 wl.to_numpy_bits(sl), w.dtype)
 
 
-def test_append_to_a_full_cache_changes_nothing():
+@pytest.mark.parametrize("mode", ["quest", "mean"])
+def test_append_to_a_full_cache_changes_nothing(mode):
     # 1024 tokens in blocks of 64: the page table has exactly 64 pages, all full
     w = wl.Workload("full", 2, 4, 1, 64, 1024, 64, 4, "bf16", seed=77)
     inp = wl.make_inputs(w, "cuda")
     dkv = device_kv(inp)
-    meta = bd.build_meta(dkv, w.block)
+    meta = (bd.build_meta if mode == "quest" else bd.build_mean_meta)(dkv, w.block)
     before = (inp.k_cache.clone(), inp.v_cache.clone(), meta.clone(), inp.seq_len.clone())
     ww = wl.scaled(w, append_tokens=1)
     kn, vn = wl.make_append_tokens(ww, "cuda")
-    bd.append(dkv, w.block, kn[0], vn[0], meta)
+    bd.append(dkv, w.block, kn[0], vn[0], meta, mode=mode)
     torch.cuda.synchronize()
     for a, b in zip((inp.k_cache, inp.v_cache, meta, inp.seq_len), before):
         assert torch.equal(a, b)
 
 
-def test_decode_trajectory_with_appends():
+@pytest.mark.parametrize("mode", ["quest", "mean"])
+def test_decode_trajectory_with_appends(mode):
     """Every step appends one token per sequence, then runs the one-stream layer step.  Per unit and
     step: scores, A, M, the predictor state and P^{t+1} bit for bit, the repaired state and output within
     tolerance, all against the oracle on the host copy of the grown cache.  Sequence 1 starts a new
-    block mid-run."""
+    block mid-run.  Both block summaries: Quest's min/max bound and the mean key."""
     steps = 6
     w = wl.Workload("append_traj", 2, 8, 2, 128, 2000, 32, 8, "bf16", seed=31, steps=steps,
                     seq_lens=[2000, 1950], drift_rho=0.9, query_mean_gain=0.64, block_centre_std=0.35,
                     append_tokens=steps)
     inp = wl.make_inputs(w, "cuda")
     dkv = device_kv(inp)
-    layer = PRRLayer(dkv, w.num_q_heads, w.block, w.topk, w.topk, ema=w.ema, scale=w.scale)
+    layer = PRRLayer(dkv, w.num_q_heads, w.block, w.topk, w.topk, ema=w.ema, scale=w.scale, score_mode=mode)
     alpha, beta, gamma = w.ema
     kn, vn = wl.make_append_tokens(w, "cuda")
     k_host, v_host = inp.k_cache.cpu().clone(), inp.v_cache.cpu().clone()
@@ -123,7 +135,7 @@ def test_decode_trajectory_with_appends():
     born = False
     for t in range(steps):
         nb_before = [-(-int(x) // w.block) for x in sl]
-        bd.append(dkv, w.block, kn[t], vn[t], layer.meta)
+        layer.append(kn[t], vn[t])
         _expected_append(k_host, v_host, pt, sl, kn[t].cpu(), vn[t].cpu())
         born |= any(-(-int(x) // w.block) > n for x, n in zip(sl, nb_before))
         P_before = layer.P_cur.lists()
@@ -139,8 +151,12 @@ def test_decode_trajectory_with_appends():
             lv, tr, live, P = ost[(b, h)]
             assert sorted(P_before[b][h]) == list(P), (t, b, h)
             q, kv = unit_view(host, b, h, step=t, length=int(sl[b]))
-            mn, mx = unit_meta(kv, w.block)
-            s = orc.quest_scores(orc.representative_query(q, 0, 0, w.group), mn, mx)
+            qbar = orc.representative_query(q, 0, 0, w.group)
+            if mode == "quest":
+                mn, mx = unit_meta(kv, w.block)
+                s = orc.quest_scores(qbar, mn, mx)
+            else:
+                s = orc.mean_scores(qbar, orc.build_mean_meta(kv, w.block, 1)[0][0])
             a = orc.topk_blocks(s, w.topk)
             nb = s.shape[0]
             assert np.array_equal(scores[b, h, :nb], s), (t, b, h)
