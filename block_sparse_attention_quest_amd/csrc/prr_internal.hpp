@@ -52,7 +52,7 @@ struct SelectSpecPlan {
     int kl;
     int kpt;
 };
-SelectSpecPlan select_spec_plan(int nmax, int topk);
+SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean);
 
 // Workspace of prr_select_spec: the speculative pass's attention workspace, then (two-stage top-K) the
 // candidates of every scoring workgroup.

@@ -224,7 +224,7 @@ hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *me
     sp.block = block;
     sp.stride = stride;
     sp.nmax = nmax;
-    const int bpw = 256 * (mean ? 1 : kv.bf16 ? kScoreBPL<true> : kScoreBPL<false>);   // blocks per workgroup
+    const int bpw = 256 * (mean ? kScoreBPL<true, true> : kv.bf16 ? kScoreBPL<true> : kScoreBPL<false>);
     const dim3 sgrid((nmax + bpw - 1) / bpw, units);
     if (mean) {
         // the fp32 block means do not depend on the cache dtype beyond q's

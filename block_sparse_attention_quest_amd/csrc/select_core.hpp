@@ -298,16 +298,17 @@ struct ScoreParams {
 };
 
 // Blocks per lane of the scoring workgroups: two for bf16 min/max metadata (one 4-byte load per channel
-// covers both), one for fp32 metadata (fp32 min/max, or the fp32 block means of mean-pooled scoring).
+// covers both) and for the fp32 block means of mean-pooled scoring (one 8-byte load per channel, in two
+// halves of the channels), one for fp32 min/max.
 template <bool BF16, bool MEAN = false>
-constexpr int kScoreBPL = (BF16 && !MEAN) ? 2 : 1;
+constexpr int kScoreBPL = (BF16 || MEAN) ? 2 : 1;
 
 // Scores blocks [256 BPL bx, 256 BPL (bx + 1)) of unit u (BPL consecutive blocks per lane).  COHERENT:
 // the scores are stored with device-scope stores, for a reader on another XCD within the same launch.
 template <bool BF16, int D, bool COHERENT = false, bool MEAN = false>
 __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u,
                                            double (&kept)[kScoreBPL<BF16, MEAN>]) {
-    constexpr int BPL = kScoreBPL<BF16, MEAN>;   // one 4-byte load per channel
+    constexpr int BPL = kScoreBPL<BF16, MEAN>;
     __shared__ double s_qbar[D];
     __shared__ int s_row[D];             // metadata row of channel i: 1 (max) when qbar_i >= 0, else 0 (min)
     const int b = u / p.hkv, kvh = u - b * p.hkv;
@@ -334,46 +335,63 @@ __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u,
     // and each lane adds its own block offset.
     // Buffer loads: the unit's metadata is one buffer resource (scalar base), the row offset a scalar
     // and the lane's block offset the only vector operand, shared by all d loads.
-    // mean-pooled scoring: one fp32 row (the block means) per channel, [d][stride]
+    // Mean-pooled scoring: one fp32 row (the block means) per channel, [d][stride].
     constexpr int ES = (BF16 && !MEAN) ? 2 : 4;   // element size
     constexpr int ROWS = MEAN ? 1 : 2;            // rows per channel
     const char *ubase = (const char *)p.meta + (size_t)u * D * ROWS * p.stride * ES;
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void *)ubase, (short)0, D * ROWS * p.stride * ES, 0x00020000);
     const int voff = p0 * ES;
-    uint32_t raw[D];
-#pragma unroll
-    for (int i = 0; i < D; ++i) {
-        // qbar >= 0: the max term is qbar * mx (row 1); otherwise qbar * mn (row 0)
-        const int sgn = __builtin_amdgcn_readfirstlane(s_row[i]);
-        if constexpr (MEAN)
-            raw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, i * p.stride * ES, 0);
-        else if constexpr (BF16 && BPL == 2)
-            raw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, (2 * i + sgn) * p.stride * ES, 0);
-        else if constexpr (BF16)
-            raw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsrc, voff, (2 * i + sgn) * p.stride * ES, 0);
-        else
-            raw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, (2 * i + sgn) * p.stride * ES, 0);
-    }
     double acc[BPL];
 #pragma unroll
     for (int e = 0; e < BPL; ++e) acc[e] = 0.0;
+    if constexpr (MEAN) {
+        // blocks p0 and p0 + 1 of one channel are adjacent fp32 values (8-byte aligned: p0 and the row
+        // stride are even).  Channels are taken in two halves, each loaded before it is used, so that the
+        // loaded pairs take D registers like the other layouts.
 #pragma unroll
-    for (int i = 0; i < D; ++i) {
-        // the accumulation is a sequential chain; a scheduling barrier every 16 channels lets the qbar
-        // reads run at most 16 channels ahead (hoisting all of them would hold 2 D doubles in registers)
-        const uint32_t r = raw[i];
-        const double qb = s_qbar[i];
+        for (int half = 0; half < 2; ++half) {
+            uint32_t lo[D / 2], hi[D / 2];
 #pragma unroll
-        for (int e = 0; e < BPL; ++e) {
-            const double x = (BF16 && !MEAN) ? (double)bf16_to_f32((uint16_t)(r >> (16 * e)))
-                                             : (double)__uint_as_float(r);
-            acc[e] = dadd(acc[e], dmul(qb, x));
+            for (int j = 0; j < D / 2; ++j) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, (half * D / 2 + j) * p.stride * ES, 0);
+                lo[j] = v[0];
+                hi[j] = v[1];
+            }
+#pragma unroll
+            for (int j = 0; j < D / 2; ++j) {
+                const double qb = s_qbar[half * D / 2 + j];
+                acc[0] = dadd(acc[0], dmul(qb, (double)__uint_as_float(lo[j])));
+                acc[1] = dadd(acc[1], dmul(qb, (double)__uint_as_float(hi[j])));
+                asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));
+                if (j % 16 == 15) __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        // the chains of a lane's blocks advance together, channel by channel (otherwise the compiler runs
-        // one chain to the end first and parks the other's operands in spare registers)
-        if constexpr (BPL == 2) asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));
-        if (i % 16 == 15) __builtin_amdgcn_sched_barrier(0);
+    } else {
+        uint32_t raw[D];
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            // qbar >= 0: the max term is qbar * mx (row 1); otherwise qbar * mn (row 0).  bf16: the 4 bytes
+            // hold blocks p0 and p0 + 1; fp32: block p0.
+            const int sgn = __builtin_amdgcn_readfirstlane(s_row[i]);
+            raw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, (2 * i + sgn) * p.stride * ES, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            // the accumulation is a sequential chain; a scheduling barrier every 16 channels lets the qbar
+            // reads run at most 16 channels ahead (hoisting all of them would hold 2 D doubles in registers)
+            const uint32_t r = raw[i];
+            const double qb = s_qbar[i];
+#pragma unroll
+            for (int e = 0; e < BPL; ++e) {
+                const double x = BF16 ? (double)bf16_to_f32((uint16_t)(r >> (16 * e))) : (double)__uint_as_float(r);
+                acc[e] = dadd(acc[e], dmul(qb, x));
+            }
+            // the chains of a lane's blocks advance together, channel by channel (otherwise the compiler
+            // runs one chain to the end first and parks the other's operands in spare registers)
+            if constexpr (BPL == 2) asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));
+            if (i % 16 == 15) __builtin_amdgcn_sched_barrier(0);
+        }
     }
     double *out = p.scores + (size_t)u * p.nmax;
 #pragma unroll

@@ -8,7 +8,8 @@
 // Figure 1 flow, §3): the two only read P and are independent.  On this GPU a dependency between two
 // streams costs about 10 us from the producer's end to the consumer's start, while kernels on one
 // stream follow each other about 1 us apart, so the overlap is made inside one grid instead: the first
-// workgroups score blocks (one workgroup per 512 blocks of a unit), the rest run the speculative chunks
+// workgroups score blocks (one workgroup per 512 blocks of a unit with min/max metadata, per 256 with
+// block means), the rest run the speculative chunks
 // (the attention kernels' chunk walk over n_spec workgroups).  Dispatch follows the workgroup index, so
 // the scoring workgroups issue their loads first: the memory system serves them ahead of the
 // speculative stream, selection finishes early and its top-K runs under the speculative pass, which is
@@ -31,10 +32,11 @@
 namespace prr {
 namespace {
 
-// Workgroup s < nsx * units scores blocks [512 (s mod nsx), +512) of unit s / nsx and, if it is the
-// unit's last to finish and KPT > 0, runs the unit's top-K (KPT keys per thread, 256 KPT >= the unit's
-// block count); the remaining n_spec workgroups run the speculative pass.  Register use is the
-// attention part's (two waves per SIMD).
+// Workgroup s < nsx * units scores blocks [BPW (s mod nsx), +BPW) of unit s / nsx (BPW = 512 blocks for
+// bf16 min/max metadata, 256 for fp32 block means: MEAN) and, if it is the unit's last to finish and
+// KPT > 0, runs the unit's top-K (KPT keys per thread, 256 KPT >= the unit's block count); the remaining
+// n_spec workgroups run the speculative pass.  Register use is the attention part's (two waves per
+// SIMD).
 struct CandParams {
     uint64_t *key;   // [units][nsx][kl]
     int32_t *idx;    // [units][nsx][kl]
@@ -42,7 +44,7 @@ struct CandParams {
     int kl;
 };
 
-template <int D, int KPT, bool TWO>
+template <int D, int KPT, bool TWO, bool MEAN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void select_spec_kernel(
     AttnParams ap, ScoreParams sp, TopkParams tp, CandParams cp, uint32_t *arrivals, int n_score, int nsx) {
     if ((int)blockIdx.x >= n_score) {
@@ -52,16 +54,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     const int s = (int)blockIdx.x;
     const int u = s / nsx;
     const int bx = s - u * nsx;
-    double kept[kScoreBPL<true>] = {0.0, 0.0};
-    score_body<true, D, KPT != 0 && !TWO>(sp, bx, u, kept);
+    constexpr int BPL = kScoreBPL<true, MEAN>;
+    double kept[BPL] = {};
+    score_body<true, D, KPT != 0 && !TWO, MEAN>(sp, bx, u, kept);
     if constexpr (TWO) {
         __shared__ TopkSmem<4> sm;
-        constexpr int BPW = 256 * kScoreBPL<true>;   // blocks per scoring workgroup
+        constexpr int BPW = 256 * BPL;   // blocks per scoring workgroup
         const int b = u / sp.hkv;
         const int nb = min((max(sp.seq_len[b], 0) + sp.block - 1) / sp.block, sp.nmax);
         const int n_local = min(max(nb - bx * BPW, 0), BPW);
         const size_t part = (size_t)u * nsx + bx;
-        local_candidates<kScoreBPL<true>>(kept, n_local, cp.kl, bx * BPW, cp.key + part * cp.kl,
+        local_candidates<BPL>(kept, n_local, cp.kl, bx * BPW, cp.key + part * cp.kl,
                                           cp.idx + part * cp.kl, cp.cnt + part, sm);
     }
     if constexpr (KPT != 0) {
@@ -88,13 +91,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 
 }  // namespace
 
-SelectSpecPlan select_spec_plan(int nmax, int topk) {
+static int score_bpw(bool mean) { return 256 * (mean ? kScoreBPL<true, true> : kScoreBPL<true, false>); }
+
+SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean) {
     SelectSpecPlan pl;
     pl.two = false;
     pl.kl = 0;
     pl.kpt = nmax <= 256 ? 1 : nmax <= 512 ? 2 : nmax <= 1024 ? 4 : nmax <= 2048 ? 8 : 0;
     if (pl.kpt == 0 && nmax <= kMaxTwoStageBlocks) {
-        const int bpw = 256 * kScoreBPL<true>;
+        const int bpw = score_bpw(mean);
         const int nsx = (nmax + bpw - 1) / bpw;
         const int kl = std::max(1, std::min(topk, bpw));
         const long slots = (long)nsx * kl;
@@ -109,13 +114,20 @@ SelectSpecPlan select_spec_plan(int nmax, int topk) {
     return pl;
 }
 
+// Candidate slots of the two-stage top-K: [units][nsx][kl] keys (8 bytes) and indices (4), [units][nsx]
+// counts.  The workspace covers both block summaries.
+static size_t candidate_bytes(int units, int nmax, int topk, bool mean) {
+    const SelectSpecPlan pl = select_spec_plan(nmax, topk, mean);
+    if (!pl.two) return 0;
+    const int bpw = score_bpw(mean);
+    const size_t parts = (size_t)units * ((nmax + bpw - 1) / bpw);
+    return parts * pl.kl * 12 + parts * 4;
+}
+
 size_t select_spec_workspace_bytes(int batch, int hq, int hkv, int d, int block, int cap, int nmax, int topk) {
     const size_t attn = attn_workspace_bytes(batch, hq, hkv, d, block, cap);
-    const SelectSpecPlan pl = select_spec_plan(nmax, topk);
-    if (!pl.two) return attn;
-    const int bpw = 256 * kScoreBPL<true>;
-    const size_t parts = (size_t)batch * hkv * ((nmax + bpw - 1) / bpw);
-    return attn + parts * pl.kl * 12 + parts * 4;
+    return attn + std::max(candidate_bytes(batch * hkv, nmax, topk, false),
+                           candidate_bytes(batch * hkv, nmax, topk, true));
 }
 
 hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,
@@ -123,8 +135,8 @@ hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const voi
                               double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
                               int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m,
                               void *ws, bool mean, hipStream_t stream) {
-    if (!kv.bf16 || mean) {
-        // fp32 caches (exact-input checks) and mean-pooled scoring: the two passes one after the other
+    if (!kv.bf16) {
+        // fp32 caches (exact-input checks): the two passes one after the other
         hipError_t e = launch_select(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_cap, scores,
                                      a_idx, a_cnt, a_cap, m_idx, m_cnt, m_cap, mean, stream);
         if (e != hipSuccess) return e;
@@ -161,10 +173,11 @@ hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const voi
     tp.m_cap = m_cap;
     const int units = kv.batch * kv.hkv;
     uint32_t *arrivals = (uint32_t *)ws + units;   // the scoring-arrival counters of the workspace
-    const int nsx = (nmax + 256 * kScoreBPL<true> - 1) / (256 * kScoreBPL<true>);
+    const int bpw = score_bpw(mean);
+    const int nsx = (nmax + bpw - 1) / bpw;
     const long grid = (long)n_spec + (long)nsx * units;
     if (grid > 0x7fffffffL) return hipErrorInvalidValue;
-    const SelectSpecPlan plan = select_spec_plan(nmax, topk);
+    const SelectSpecPlan plan = select_spec_plan(nmax, topk, mean);
     CandParams cp;
     cp.kl = plan.kl;
     char *cbase = (char *)ws + attn_workspace_bytes(kv.batch, hq, kv.hkv, kv.d, block, p_cap);
@@ -173,15 +186,18 @@ hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const voi
     cp.cnt = (int32_t *)(cbase + (size_t)units * nsx * plan.kl * 12);
     const int kpt = plan.kpt;
     const bool two = plan.two;
-#define PRR_SS(DD, K, T)                                                                                      \
-    if (kv.d == DD && kpt == K && two == T) {                                                                 \
-        select_spec_kernel<DD, K, T><<<(int)grid, 256, 0, stream>>>(ap, sp, tp, cp, arrivals, nsx * units, nsx); \
+#define PRR_SS(DD, K, T, MN)                                                                               \
+    if (kv.d == DD && kpt == K && two == T && mean == MN) {                                                 \
+        select_spec_kernel<DD, K, T, MN><<<(int)grid, 256, 0, stream>>>(ap, sp, tp, cp, arrivals, nsx * units, \
+                                                                        nsx);                               \
     } else
-    PRR_SS(128, 0, false) PRR_SS(128, 1, false) PRR_SS(128, 2, false) PRR_SS(128, 4, false) PRR_SS(128, 8, false)
-    PRR_SS(128, 1, true) PRR_SS(128, 2, true) PRR_SS(128, 4, true) PRR_SS(128, 8, true) PRR_SS(128, 16, true)
-    PRR_SS(64, 0, false) PRR_SS(64, 1, false) PRR_SS(64, 2, false) PRR_SS(64, 4, false) PRR_SS(64, 8, false)
-    PRR_SS(64, 1, true) PRR_SS(64, 2, true) PRR_SS(64, 4, true) PRR_SS(64, 8, true) PRR_SS(64, 16, true)
+#define PRR_SS_ALL(DD, MN)                                                                                  \
+    PRR_SS(DD, 0, false, MN) PRR_SS(DD, 1, false, MN) PRR_SS(DD, 2, false, MN) PRR_SS(DD, 4, false, MN)       \
+    PRR_SS(DD, 8, false, MN) PRR_SS(DD, 1, true, MN) PRR_SS(DD, 2, true, MN) PRR_SS(DD, 4, true, MN)          \
+    PRR_SS(DD, 8, true, MN) PRR_SS(DD, 16, true, MN)
+    PRR_SS_ALL(128, false) PRR_SS_ALL(64, false) PRR_SS_ALL(128, true) PRR_SS_ALL(64, true)
     { return hipErrorInvalidValue; }
+#undef PRR_SS_ALL
 #undef PRR_SS
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || kpt != 0) return e;

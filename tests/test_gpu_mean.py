@@ -1,8 +1,8 @@
 """GPU parity of mean-pooled block selection (the block summarised by its mean key, one of the two
 summaries the pages name for selection) against the oracle: the fp32 block means bit for bit, the fp64
 scores bit for bit, A and M exactly; the fused selection + speculative launch in this mode against the
-separate calls.  Sizes span several scoring workgroups (256 blocks each) with a ragged tail, plus
-sequences of one token and of none."""
+separate calls.  Sizes span several scoring workgroups (256 blocks each) with a ragged tail, the
+fused launch's single- and two-stage top-K, and sequences of one token and of none."""
 import numpy as np
 import pytest
 import torch
@@ -27,6 +27,9 @@ CASES = [
     ("bf16_d128_s16_ragged", 2, 8, 2, 128, 16, [20811, 9000], "bf16", 64, None),
     ("f32_d64_s64", 1, 4, 1, 64, 64, [33000], "f32", 40, None),
     ("bf16_d64_s32_short", 3, 8, 1, 64, 32, [4097, 1, 600], "bf16", 16, 2),
+    # 2500 blocks: the fused launch ranks per-workgroup candidates (two-stage top-K), K above the 256
+    # blocks of one scoring workgroup
+    ("bf16_d128_s16_two_stage", 1, 8, 2, 128, 16, [40000], "bf16", 300, None),
 ]
 
 
