@@ -22,8 +22,8 @@ PAGE_SIZE = 16
 # Every symbol include/prr.h declares.
 EXPORTS = (
     "prr_max_blocks", "prr_meta_stride", "prr_meta_bytes", "prr_attn_workspace_bytes",
-    "prr_workspace_clear", "prr_build_meta", "prr_mean_meta_bytes", "prr_build_mean_meta", "prr_append", "prr_select", "prr_select_spec_workspace_bytes",
-    "prr_select_spec", "prr_predict",
+    "prr_workspace_clear", "prr_build_meta", "prr_mean_meta_bytes", "prr_build_mean_meta", "prr_append",
+    "prr_select", "prr_select_spec_workspace_bytes", "prr_select_spec", "prr_select_spec_predict", "prr_predict",
     "prr_spec_attn",
     "prr_repair", "prr_calibrate_workspace_bytes", "prr_calibrate", "prr_strerror",
 )
@@ -50,6 +50,14 @@ class AttnStateStruct(ctypes.Structure):
     _fields_ = [("acc", ctypes.c_void_p), ("l", ctypes.c_void_p), ("m", ctypes.c_void_p)]
 
 
+class PredictArgsStruct(ctypes.Structure):
+    _fields_ = [("scores", ctypes.c_void_p), ("seq_len", ctypes.c_void_p), ("batch", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("block", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("alpha", ctypes.c_double), ("beta", ctypes.c_double), ("gamma", ctypes.c_double),
+                ("budget", ctypes.c_int32), ("level", ctypes.c_void_p), ("trend", ctypes.c_void_p),
+                ("live", ctypes.c_void_p), ("P_next", ctypes.POINTER(BlockSetStruct))]
+
+
 _P = ctypes.POINTER
 _VP, _I32, _SZ, _D, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_double, ctypes.c_float
 
@@ -69,6 +77,9 @@ _SIGS = {
     "prr_select_spec": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _VP, ctypes.c_int, _I32, _I32,
                                        _P(BlockSetStruct), _VP, _P(BlockSetStruct), _P(BlockSetStruct), _F,
                                        _P(AttnStateStruct), _VP, _SZ, _VP]),
+    "prr_select_spec_predict": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _VP, ctypes.c_int, _I32, _I32,
+                                               _P(BlockSetStruct), _VP, _P(BlockSetStruct), _P(BlockSetStruct),
+                                               _F, _P(AttnStateStruct), _VP, _SZ, _P(PredictArgsStruct), _VP]),
     "prr_predict": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _D, _D, _D, _I32, _VP, _VP, _VP,
                                    _P(BlockSetStruct), _VP]),
     "prr_spec_attn": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _I32, _P(BlockSetStruct), _F,
@@ -325,8 +336,9 @@ def select(q: torch.Tensor, kv: KVCache, meta: torch.Tensor, block: int, topk: i
 def select_spec(q: torch.Tensor, kv: KVCache, meta: torch.Tensor, block: int, topk: int, P: BlockSet,
                 scale: float, scores: Optional[torch.Tensor] = None, A: Optional[BlockSet] = None,
                 M: Optional[BlockSet] = None, out: Optional[AttnState] = None, ws: Optional[Workspace] = None,
-                mode: str = "quest", stream=None):
-    """select(q, ..., P) and spec_attn(q, ..., P) as one launch; returns (scores, A, M, state)."""
+                mode: str = "quest", pred: Optional["PredictArgs"] = None, stream=None):
+    """select(q, ..., P) and spec_attn(q, ..., P) as one launch; returns (scores, A, M, state).  pred: a
+    predictor step over other buffers (typically the previous layer's) carried by the same launch."""
     lib = load_library()
     s = kv.struct()
     nmax = lib.prr_max_blocks(ctypes.byref(s), block)
@@ -344,11 +356,43 @@ def select_spec(q: torch.Tensor, kv: KVCache, meta: torch.Tensor, block: int, to
     if ws is None:
         ws = select_spec_workspace_for(kv, Hq, block, topk, P.cap)
     a_s, p_s, m_s, o_s = A.struct(), P.struct(), M.struct(), out.struct()
-    st = lib.prr_select_spec(_ptr(q), Hq, ctypes.byref(s), _ptr(meta), _mode(mode), block, topk, ctypes.byref(p_s),
-                             _ptr(scores), ctypes.byref(a_s), ctypes.byref(m_s), float(scale), ctypes.byref(o_s),
-                             ws.ptr(), ws.nbytes, _stream(stream))
-    _check(st, "prr_select_spec")
+    if pred is None:
+        st = lib.prr_select_spec(_ptr(q), Hq, ctypes.byref(s), _ptr(meta), _mode(mode), block, topk,
+                                 ctypes.byref(p_s), _ptr(scores), ctypes.byref(a_s), ctypes.byref(m_s), float(scale),
+                                 ctypes.byref(o_s), ws.ptr(), ws.nbytes, _stream(stream))
+        _check(st, "prr_select_spec")
+    else:
+        pn = pred.P_next.struct()
+        pa = pred.struct(pn)
+        st = lib.prr_select_spec_predict(_ptr(q), Hq, ctypes.byref(s), _ptr(meta), _mode(mode), block, topk,
+                                         ctypes.byref(p_s), _ptr(scores), ctypes.byref(a_s), ctypes.byref(m_s),
+                                         float(scale), ctypes.byref(o_s), ws.ptr(), ws.nbytes, ctypes.byref(pa),
+                                         _stream(stream))
+        _check(st, "prr_select_spec_predict")
     return scores, A, M, out
+
+
+@dataclass
+class PredictArgs:
+    """One predictor step's operands (those of predict()), to be carried by a select_spec launch."""
+
+    scores: torch.Tensor
+    seq_len: torch.Tensor
+    block: int
+    alpha: float
+    beta: float
+    gamma: float
+    budget: int
+    level: torch.Tensor
+    trend: torch.Tensor
+    live: torch.Tensor
+    P_next: "BlockSet"
+
+    def struct(self, p_next_struct) -> PredictArgsStruct:
+        B, H, nmax = self.scores.shape
+        return PredictArgsStruct(_ptr(self.scores), _ptr(self.seq_len), B, H, self.block, nmax, float(self.alpha),
+                                 float(self.beta), float(self.gamma), self.budget, _ptr(self.level),
+                                 _ptr(self.trend), _ptr(self.live), ctypes.pointer(p_next_struct))
 
 
 def predict(scores: torch.Tensor, seq_len: torch.Tensor, block: int, alpha: float, beta: float,

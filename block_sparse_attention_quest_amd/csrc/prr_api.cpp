@@ -177,10 +177,23 @@ size_t prr_select_spec_workspace_bytes(const prr_kv_cache *kv, int32_t num_q_hea
                                             prr_max_blocks(kv, block), topk);
 }
 
-prr_status prr_select_spec(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
-                           prr_score_mode mode, int32_t block, int32_t topk, const prr_block_set *P,
-                           double *scores, prr_block_set *A, prr_block_set *M, float scale, prr_attn_state *out,
-                           void *ws, size_t ws_bytes, hipStream_t stream) {
+static prr_status check_predict(const double *scores, const int32_t *seq_len, int32_t batch,
+                                int32_t num_kv_heads, int32_t block, int32_t max_blocks, int32_t budget,
+                                const double *level, const double *trend, const int32_t *live,
+                                const prr_block_set *P_next) {
+    if (!scores || !seq_len || !level || !trend || !live) return PRR_EINVAL;
+    if (batch <= 0 || num_kv_heads <= 0 || block <= 0 || max_blocks <= 0 || budget < 0) return PRR_EINVAL;
+    PRR_TRY(check_set(P_next));
+    if (P_next->cap < budget) return PRR_EINVAL;
+    if (max_blocks > prr::kMaxSelectN) return PRR_EUNSUPPORTED;
+    return PRR_OK;
+}
+
+prr_status prr_select_spec_predict(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
+                                   prr_score_mode mode, int32_t block, int32_t topk, const prr_block_set *P,
+                                   double *scores, prr_block_set *A, prr_block_set *M, float scale,
+                                   prr_attn_state *out, void *ws, size_t ws_bytes, const prr_predict_args *pred,
+                                   hipStream_t stream) {
     if (!q || !meta || !scores || !P || !M) return PRR_EINVAL;
     if (mode != PRR_SCORE_QUEST && mode != PRR_SCORE_MEAN) return PRR_EINVAL;
     PRR_TRY(check_kv(kv));
@@ -195,21 +208,55 @@ prr_status prr_select_spec(const void *q, int32_t num_q_heads, const prr_kv_cach
     if (nmax > prr::kMaxSelectN) return PRR_EUNSUPPORTED;
     if (!ws || ws_bytes < prr_select_spec_workspace_bytes(kv, num_q_heads, block, topk, P->cap))
         return PRR_EWORKSPACE;
+    prr::PredictArgs pa;
+    if (pred) {
+        PRR_TRY(check_predict(pred->scores, pred->seq_len, pred->batch, pred->num_kv_heads, pred->block,
+                              pred->max_blocks, pred->budget, pred->level, pred->trend, pred->live, pred->P_next));
+        // the predictor writes level, trend, live and P_next while the selection writes scores, A and M
+        // and reads P: none of them may be shared
+        const void *sel_bufs[] = {scores, P->idx, P->count, A->idx, A->count, M->idx, M->count};
+        const void *pred_out[] = {pred->level, pred->trend, pred->live, pred->P_next->idx, pred->P_next->count};
+        for (const void *x : pred_out)
+            for (const void *y : sel_bufs)
+                if (x == y) return PRR_EINVAL;
+        if ((const void *)pred->scores == (const void *)scores) return PRR_EINVAL;
+        pa.scores = pred->scores;
+        pa.seq_len = pred->seq_len;
+        pa.batch = pred->batch;
+        pa.hkv = pred->num_kv_heads;
+        pa.block = pred->block;
+        pa.nmax = pred->max_blocks;
+        pa.budget = pred->budget;
+        pa.alpha = pred->alpha;
+        pa.beta = pred->beta;
+        pa.gamma = pred->gamma;
+        pa.level = pred->level;
+        pa.trend = pred->trend;
+        pa.live = pred->live;
+        pa.p_idx = pred->P_next->idx;
+        pa.p_cnt = pred->P_next->count;
+        pa.p_cap = pred->P_next->cap;
+    }
     return hip_status(prr::launch_select_spec(desc(kv), q, num_q_heads, meta, block, prr_meta_stride(kv, block),
                                               nmax, topk, P->idx, P->count, P->cap, scores, A->idx, A->count,
                                               A->cap, M->idx, M->count, M->cap, scale, out->acc, out->l, out->m,
-                                              ws, mode == PRR_SCORE_MEAN, stream));
+                                              ws, mode == PRR_SCORE_MEAN, pred ? &pa : nullptr, stream));
+}
+
+prr_status prr_select_spec(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
+                           prr_score_mode mode, int32_t block, int32_t topk, const prr_block_set *P,
+                           double *scores, prr_block_set *A, prr_block_set *M, float scale, prr_attn_state *out,
+                           void *ws, size_t ws_bytes, hipStream_t stream) {
+    return prr_select_spec_predict(q, num_q_heads, kv, meta, mode, block, topk, P, scores, A, M, scale, out, ws,
+                                   ws_bytes, nullptr, stream);
 }
 
 prr_status prr_predict(const double *scores, const int32_t *seq_len, int32_t batch,
                        int32_t num_kv_heads, int32_t block, int32_t max_blocks, double alpha,
                        double beta, double gamma, int32_t budget, double *level, double *trend,
                        int32_t *live, prr_block_set *P_next, hipStream_t stream) {
-    if (!scores || !seq_len || !level || !trend || !live) return PRR_EINVAL;
-    if (batch <= 0 || num_kv_heads <= 0 || block <= 0 || max_blocks <= 0 || budget < 0) return PRR_EINVAL;
-    PRR_TRY(check_set(P_next));
-    if (P_next->cap < budget) return PRR_EINVAL;
-    if (max_blocks > prr::kMaxSelectN) return PRR_EUNSUPPORTED;
+    PRR_TRY(check_predict(scores, seq_len, batch, num_kv_heads, block, max_blocks, budget, level, trend, live,
+                          P_next));
     return hip_status(prr::launch_predict(scores, seq_len, batch, num_kv_heads, block, max_blocks, alpha,
                                           beta, gamma, budget, level, trend, live, P_next->idx,
                                           P_next->count, P_next->cap, stream));

@@ -60,11 +60,30 @@ size_t select_spec_workspace_bytes(int batch, int hq, int hkv, int d, int block,
 
 // Selection and the speculative pass over P in one grid (bf16 caches; fp32 caches run the two in turn),
 // then the top-K.  ws: select_spec_workspace_bytes.
+// One predictor step (the arguments of launch_predict), for a launch that carries it along.
+struct PredictArgs {
+    const double *scores;
+    const int32_t *seq_len;
+    int batch, hkv, block, nmax, budget;
+    double alpha, beta, gamma;
+    double *level;
+    double *trend;
+    int32_t *live;
+    int32_t *p_idx;
+    int32_t *p_cnt;
+    int p_cap;
+};
+
+// Rows of at most this many blocks let the predictor step run inside the selection + speculative launch.
+constexpr int kMaxFusedPredictN = 2048;
+
+// pred (may be null): a predictor step over other buffers, run by extra workgroups of the same launch
+// when its rows fit (kMaxFusedPredictN), else as its own launch after it on the stream.
 hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,
                               int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
                               double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
                               int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m,
-                              void *ws, bool mean, hipStream_t stream);
+                              void *ws, bool mean, const PredictArgs *pred, hipStream_t stream);
 
 hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batch, int hkv,
                           int block, int nmax, double alpha, double beta, double gamma, int budget,

@@ -25,6 +25,11 @@
 //     own 512 blocks as candidates, and the last one ranks the candidates of all workgroups of the unit
 //     (up to 16 per thread; the selection is exact, see select_core.hpp);
 // otherwise (more candidates than that) the separate top-K kernel follows the launch.
+//
+// Predictor step of another layer.  In a stack of layers the predictor of layer l needs only layer l's
+// scores and is off the critical path ([paper] §1, §4.1); its workgroups can ride along in layer l + 1's
+// launch, after the speculative ones in dispatch order, so they take the slots the scoring workgroups
+// leave.  The two touch disjoint buffers.
 
 #include "select_core.hpp"
 #include "attn_core.hpp"
@@ -35,8 +40,9 @@ namespace {
 // Workgroup s < nsx * units scores blocks [BPW (s mod nsx), +BPW) of unit s / nsx (BPW = 512 blocks for
 // bf16 min/max metadata, 256 for fp32 block means: MEAN) and, if it is the unit's last to finish and
 // KPT > 0, runs the unit's top-K (KPT keys per thread, 256 KPT >= the unit's block count); the remaining
-// n_spec workgroups run the speculative pass.  Register use is the attention part's (two waves per
-// SIMD).
+// n_spec workgroups run the speculative pass, and (PRED) the last n_pred workgroups each run the predictor
+// step of one unit of another layer (8 keys per thread: rows of up to 2048 blocks).  Register use is the
+// attention part's (two waves per SIMD).
 struct CandParams {
     uint64_t *key;   // [units][nsx][kl]
     int32_t *idx;    // [units][nsx][kl]
@@ -44,11 +50,18 @@ struct CandParams {
     int kl;
 };
 
-template <int D, int KPT, bool TWO, bool MEAN>
+template <int D, int KPT, bool TWO, bool MEAN, bool PRED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void select_spec_kernel(
-    AttnParams ap, ScoreParams sp, TopkParams tp, CandParams cp, uint32_t *arrivals, int n_score, int nsx) {
+    AttnParams ap, ScoreParams sp, TopkParams tp, CandParams cp, PredictParams pp, uint32_t *arrivals,
+    int n_score, int nsx, int n_spec) {
+    if constexpr (PRED) {
+        if ((int)blockIdx.x >= n_score + n_spec) {
+            predict_body<8, 256>(pp, (int)blockIdx.x - n_score - n_spec);
+            return;
+        }
+    }
     if ((int)blockIdx.x >= n_score) {
-        attn_body<true, D, false>(ap, (int)blockIdx.x - n_score, (int)gridDim.x - n_score);
+        attn_body<true, D, false>(ap, (int)blockIdx.x - n_score, n_spec);
         return;
     }
     const int s = (int)blockIdx.x;
@@ -134,13 +147,21 @@ hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const voi
                               int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
                               double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
                               int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m,
-                              void *ws, bool mean, hipStream_t stream) {
+                              void *ws, bool mean, const PredictArgs *pred, hipStream_t stream) {
+    auto predict_alone = [&]() -> hipError_t {
+        if (!pred) return hipSuccess;
+        return launch_predict(pred->scores, pred->seq_len, pred->batch, pred->hkv, pred->block, pred->nmax,
+                              pred->alpha, pred->beta, pred->gamma, pred->budget, pred->level, pred->trend,
+                              pred->live, pred->p_idx, pred->p_cnt, pred->p_cap, stream);
+    };
     if (!kv.bf16) {
-        // fp32 caches (exact-input checks): the two passes one after the other
+        // fp32 caches (exact-input checks): the passes one after the other
         hipError_t e = launch_select(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_cap, scores,
                                      a_idx, a_cnt, a_cap, m_idx, m_cnt, m_cap, mean, stream);
         if (e != hipSuccess) return e;
-        return launch_attn(kv, q, hq, block, p_idx, p_cnt, p_cap, scale, acc, l, m, nullptr, false, ws, stream);
+        e = launch_attn(kv, q, hq, block, p_idx, p_cnt, p_cap, scale, acc, l, m, nullptr, false, ws, stream);
+        if (e != hipSuccess) return e;
+        return predict_alone();
     }
     AttnParams ap;
     const int n_spec = attn_setup(ap, kv, q, hq, block, p_idx, p_cnt, p_cap, scale, acc, l, m, nullptr, false, ws);
@@ -175,7 +196,28 @@ hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const voi
     uint32_t *arrivals = (uint32_t *)ws + units;   // the scoring-arrival counters of the workspace
     const int bpw = score_bpw(mean);
     const int nsx = (nmax + bpw - 1) / bpw;
-    const long grid = (long)n_spec + (long)nsx * units;
+    const bool fuse_pred = pred && pred->nmax <= kMaxFusedPredictN;
+    PredictParams pp = {};
+    int n_pred = 0;
+    if (fuse_pred) {
+        pp.scores = pred->scores;
+        pp.seq_len = pred->seq_len;
+        pp.level = pred->level;
+        pp.trend = pred->trend;
+        pp.live = pred->live;
+        pp.p_idx = pred->p_idx;
+        pp.p_cnt = pred->p_cnt;
+        pp.hkv = pred->hkv;
+        pp.block = pred->block;
+        pp.nmax = pred->nmax;
+        pp.budget = pred->budget;
+        pp.p_cap = pred->p_cap;
+        pp.alpha = pred->alpha;
+        pp.beta = pred->beta;
+        pp.gamma = pred->gamma;
+        n_pred = pred->batch * pred->hkv;
+    }
+    const long grid = (long)n_spec + (long)nsx * units + n_pred;
     if (grid > 0x7fffffffL) return hipErrorInvalidValue;
     const SelectSpecPlan plan = select_spec_plan(nmax, topk, mean);
     CandParams cp;
@@ -186,23 +228,30 @@ hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const voi
     cp.cnt = (int32_t *)(cbase + (size_t)units * nsx * plan.kl * 12);
     const int kpt = plan.kpt;
     const bool two = plan.two;
-#define PRR_SS(DD, K, T, MN)                                                                               \
-    if (kv.d == DD && kpt == K && two == T && mean == MN) {                                                 \
-        select_spec_kernel<DD, K, T, MN><<<(int)grid, 256, 0, stream>>>(ap, sp, tp, cp, arrivals, nsx * units, \
-                                                                        nsx);                               \
+#define PRR_SS(DD, K, T, MN, PR)                                                                           \
+    if (kv.d == DD && kpt == K && two == T && mean == MN && fuse_pred == PR) {                              \
+        select_spec_kernel<DD, K, T, MN, PR><<<(int)grid, 256, 0, stream>>>(ap, sp, tp, cp, pp, arrivals,      \
+                                                                            nsx * units, nsx, n_spec);      \
     } else
-#define PRR_SS_ALL(DD, MN)                                                                                  \
-    PRR_SS(DD, 0, false, MN) PRR_SS(DD, 1, false, MN) PRR_SS(DD, 2, false, MN) PRR_SS(DD, 4, false, MN)       \
-    PRR_SS(DD, 8, false, MN) PRR_SS(DD, 1, true, MN) PRR_SS(DD, 2, true, MN) PRR_SS(DD, 4, true, MN)          \
-    PRR_SS(DD, 8, true, MN) PRR_SS(DD, 16, true, MN)
-    PRR_SS_ALL(128, false) PRR_SS_ALL(64, false) PRR_SS_ALL(128, true) PRR_SS_ALL(64, true)
+#define PRR_SS_K(DD, MN, PR)                                                                                \
+    PRR_SS(DD, 0, false, MN, PR) PRR_SS(DD, 1, false, MN, PR) PRR_SS(DD, 2, false, MN, PR)                    \
+    PRR_SS(DD, 4, false, MN, PR) PRR_SS(DD, 8, false, MN, PR) PRR_SS(DD, 1, true, MN, PR)                     \
+    PRR_SS(DD, 2, true, MN, PR) PRR_SS(DD, 4, true, MN, PR) PRR_SS(DD, 8, true, MN, PR)                       \
+    PRR_SS(DD, 16, true, MN, PR)
+#define PRR_SS_ALL(MN, PR) PRR_SS_K(128, MN, PR) PRR_SS_K(64, MN, PR)
+    PRR_SS_ALL(false, false) PRR_SS_ALL(true, false) PRR_SS_ALL(false, true) PRR_SS_ALL(true, true)
     { return hipErrorInvalidValue; }
 #undef PRR_SS_ALL
+#undef PRR_SS_K
 #undef PRR_SS
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || kpt != 0) return e;
-    return launch_topk(kv, block, nmax, topk, scores, p_idx, p_cnt, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt,
-                       m_cap, stream);
+    if (e != hipSuccess) return e;
+    if (kpt == 0) {
+        e = launch_topk(kv, block, nmax, topk, scores, p_idx, p_cnt, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt,
+                        m_cap, stream);
+        if (e != hipSuccess) return e;
+    }
+    return fuse_pred ? hipSuccess : predict_alone();
 }
 
 }  // namespace prr

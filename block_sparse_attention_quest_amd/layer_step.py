@@ -105,6 +105,7 @@ class PRRLayer:
         self.ws_spec = bd.select_spec_workspace_for(kv, num_q_heads, block, topk, max(1, budget))
         self.ws_repair = bd.workspace_for(kv, num_q_heads, block, max(1, topk))
         self._streams = None
+        self.pending_predict: Optional[bd.PredictArgs] = None
 
     @property
     def P_cur(self) -> bd.BlockSet:
@@ -116,6 +117,7 @@ class PRRLayer:
 
     def reset(self):
         """Forget the predictor state (a fresh decode: the first step runs with P empty)."""
+        self.pending_predict = None
         if self._streams is not None:
             torch.cuda.current_stream().wait_event(self._streams[3])
         self.level.zero_()
@@ -125,29 +127,45 @@ class PRRLayer:
             p.count.zero_()
         self.cur = 0
 
-    def step(self, q: torch.Tensor, timers: Optional[StepTimers] = None) -> torch.Tensor:
+    def step(self, q: torch.Tensor, timers: Optional[StepTimers] = None, carry: Optional[bd.PredictArgs] = None,
+             defer_predict: bool = False) -> torch.Tensor:
         """Enqueue one layer step for queries q [B][Hq][d] on the current stream; returns the normalised
-        output tensor (valid once the stream reaches it)."""
+        output tensor (valid once the stream reaches it).
+
+        carry: another layer's pending predictor step, run by workgroups of this step's selection +
+        speculative launch.  defer_predict: leave this step's predictor pending (``pending_predict``) for
+        a later launch to carry; it must run before this layer's next step."""
         s = torch.cuda.current_stream()
         if self._streams is not None:
             s.wait_event(self._streams[3])   # a previous two-stream step's predictor
+        if self.pending_predict is not None:
+            raise RuntimeError("this layer's previous predictor step has not been run")
         P, Pn = self.P[self.cur], self.P[1 - self.cur]
         if timers and timers.start:
             timers.start.record(s)
         bd.select_spec(q, self.kv, self.meta, self.block, self.topk, P, self.scale, scores=self.scores, A=self.A,
-                       M=self.M, out=self.state, ws=self.ws_spec, mode=self.score_mode, stream=s)
+                       M=self.M, out=self.state, ws=self.ws_spec, mode=self.score_mode, pred=carry, stream=s)
         if timers and timers.select_spec_end:
             timers.select_spec_end.record(s)
         bd.repair(q, self.kv, self.block, self.M, self.scale, self.state, out=self.out, ws=self.ws_repair,
                   stream=s)
         if timers and timers.repair_end:
             timers.repair_end.record(s)
-        bd.predict(self.scores, self.kv.seq_len, self.block, self.alpha, self.beta, self.gamma, self.budget,
-                   self.level, self.trend, self.live, P_next=Pn, stream=s)
+        args = bd.PredictArgs(self.scores, self.kv.seq_len, self.block, self.alpha, self.beta, self.gamma,
+                              self.budget, self.level, self.trend, self.live, Pn)
+        if defer_predict:
+            self.pending_predict = args
+        else:
+            run_predict(args, s)
         if timers and timers.predict_end:
             timers.predict_end.record(s)
         self.cur = 1 - self.cur
         return self.out
+
+    def take_pending_predict(self) -> Optional[bd.PredictArgs]:
+        """Hand the deferred predictor step to the caller (who must enqueue it) and clear it."""
+        args, self.pending_predict = self.pending_predict, None
+        return args
 
     def step_two_streams(self, q: torch.Tensor, timers: Optional[TwoStreamTimers] = None) -> torch.Tensor:
         """The same step on three streams joined by events (the pages' schedule):
@@ -194,3 +212,50 @@ class PRRLayer:
             timers.repair_end.record(crit)
         self.cur = 1 - self.cur
         return self.out
+
+
+def run_predict(args: bd.PredictArgs, stream=None):
+    """Enqueue a predictor step on its own."""
+    bd.predict(args.scores, args.seq_len, args.block, args.alpha, args.beta, args.gamma, args.budget, args.level,
+               args.trend, args.live, P_next=args.P_next, stream=stream)
+
+
+class PRRStack:
+    """The attention layers of a model through one decode step each, in order ([paper] §1 and the
+    Figure 1 flow for each layer; [paper] §4.2: every layer has its own calibrated (alpha, beta, gamma)).
+
+    Each layer keeps its own cache (and sequence lengths), metadata, predictor state and sets.  A layer's
+    predictor needs only that layer's scores, so it is deferred and carried by the next layer's
+    selection + speculative launch, whose spare workgroup slots absorb it; the last layer's rides in
+    the first layer's launch of the next decode step.  ``flush`` runs a still-pending one on its own
+    (before reading predictor state, or at the end of decoding).  Results equal running every layer's
+    steps one after another."""
+
+    def __init__(self, layers: list):
+        self.layers = list(layers)
+        self.pending: Optional[bd.PredictArgs] = None
+        self.pending_owner = -1
+
+    def step(self, qs, k_new=None, v_new=None) -> list:
+        """One decode step through every layer: qs[l] [B][Hq][d]; k_new[l], v_new[l] [B][Hkv][d] (optional)
+        are appended to layer l's cache first.  Returns each layer's output tensor."""
+        outs = []
+        for i, layer in enumerate(self.layers):
+            if self.pending_owner == i:
+                # a layer's own predictor writes the set its next selection reads: it runs first, alone
+                self.flush()
+            if k_new is not None:
+                layer.append(k_new[i], v_new[i])
+            outs.append(layer.step(qs[i], carry=self.pending, defer_predict=True))
+            self.pending, self.pending_owner = layer.take_pending_predict(), i
+        return outs
+
+    def flush(self, stream=None):
+        if self.pending is not None:
+            run_predict(self.pending, stream)
+        self.pending, self.pending_owner = None, -1
+
+    def reset(self):
+        self.pending, self.pending_owner = None, -1
+        for layer in self.layers:
+            layer.reset()

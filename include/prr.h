@@ -151,6 +151,8 @@ prr_status prr_append(const prr_kv_cache *kv, int32_t block, const void *k_new, 
  *       float64 with no fused multiply-add, for p < N_b = ceil(seq_len[b] / block);
  *   A = the min(topk, N_b) highest scores (ties to the smaller block index), ascending;
  *   M = A \ P (ascending) when P is given.
+ * With mode PRR_SCORE_MEAN, meta holds block means (prr_build_mean_meta) and scores[b][kvh][p] =
+ * sum_i qbar_i mean_{p,i}, with the same qbar, order and precision.
  * P may be NULL (then M must be NULL).  A->cap and M->cap must be >= topk.  N_b must not exceed
  * 32768.  q: [batch][num_q_heads][head_dim], device, dtype of the cache. */
 prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
@@ -186,6 +188,36 @@ prr_status prr_predict(const double *scores, const int32_t *seq_len, int32_t bat
                        int32_t num_kv_heads, int32_t block, int32_t max_blocks, double alpha,
                        double beta, double gamma, int32_t budget, double *level, double *trend,
                        int32_t *live, prr_block_set *P_next, hipStream_t stream);
+
+/* The arguments of prr_predict, for prr_select_spec_predict. */
+typedef struct prr_predict_args {
+    const double *scores;
+    const int32_t *seq_len;
+    int32_t batch;
+    int32_t num_kv_heads;
+    int32_t block;
+    int32_t max_blocks;
+    double alpha, beta, gamma;
+    int32_t budget;
+    double *level;
+    double *trend;
+    int32_t *live;
+    prr_block_set *P_next;
+} prr_predict_args;
+
+/* prr_select_spec, plus (pred non-NULL) the predictor step prr_predict would run on *pred, typically
+ * the previous layer's: in a stack of layers the predictor of one layer needs only that layer's scores
+ * and is off the critical path ([paper] §1 and the Figure 1 flow; [paper] §4.1), so its workgroups join
+ * this launch and use the slots selection leaves while the speculative pass runs (rows of up to 2048
+ * blocks; longer rows get their own launch after this one, on the same stream).  Results equal
+ * prr_select_spec(...) followed by prr_predict(*pred).  The predictor's buffers must not overlap any
+ * buffer of the selection or speculative pass (PRR_EINVAL for the same scores, set or state pointers).
+ * pred NULL: exactly prr_select_spec. */
+prr_status prr_select_spec_predict(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
+                                   prr_score_mode mode, int32_t block, int32_t topk, const prr_block_set *P,
+                                   double *scores, prr_block_set *A, prr_block_set *M, float scale,
+                                   prr_attn_state *out, void *ws, size_t ws_bytes, const prr_predict_args *pred,
+                                   hipStream_t stream);
 
 /* Speculative block-sparse decode attention over P ([paper] §3 and §4.3, the instrumented speculative
  * kernel that also stores the softmax denominator and running maximum; [paper] §1).  Writes the

@@ -181,3 +181,46 @@ def test_append_argument_errors(lib):
     assert call(seq=sl + 4) == 1                  # must be the cache's own length array
     assert call(block=24) == 1
     assert call(kv=_kv(head_dim=96)) == 2
+
+
+def test_select_spec_predict_argument_errors(lib):
+    """The carried predictor step is checked like prr_predict, and may share no buffer with the selection
+    or speculative pass (every call here is rejected before anything is enqueued)."""
+    kv = _kv()
+    A = bd.BlockSetStruct(0x1000, 0x1100, 64)
+    P = bd.BlockSetStruct(0x1200, 0x1300, 64)
+    M = bd.BlockSetStruct(0x1400, 0x1500, 64)
+    Pn = bd.BlockSetStruct(0x2000, 0x2100, 64)
+    st = _state()
+    scores = 0x3000
+    need = lib.prr_select_spec_workspace_bytes(ctypes.byref(kv), 32, 64, 64, 64)
+
+    def pred(**kw):
+        f = dict(scores=0x4000, seq_len=0x4100, batch=2, num_kv_heads=8, block=64, max_blocks=2048, alpha=0.6,
+                 beta=0.3, gamma=0.5, budget=64, level=0x4200, trend=0x4300, live=0x4400, P_next=Pn)
+        f.update(kw)
+        pn = f.pop("P_next")
+        return bd.PredictArgsStruct(**f, P_next=ctypes.pointer(pn) if pn is not None else None)
+
+    def call(pa):
+        return lib.prr_select_spec_predict(1, 32, ctypes.byref(kv), 1, 0, 64, 64, ctypes.byref(P), scores,
+                                           ctypes.byref(A), ctypes.byref(M), 0.1, ctypes.byref(st), 1, need,
+                                           ctypes.byref(pa), None)
+
+    assert call(pred(scores=None)) == 1
+    assert call(pred(live=None)) == 1
+    assert call(pred(P_next=None)) == 1
+    assert call(pred(budget=65)) == 1                 # P_next cap too small
+    assert call(pred(budget=-1)) == 1
+    assert call(pred(batch=0)) == 1
+    assert call(pred(max_blocks=40000)) == 2
+    # shared buffers
+    assert call(pred(scores=scores)) == 1
+    assert call(pred(level=scores)) == 1
+    assert call(pred(trend=0x1000)) == 1              # A's indices
+    assert call(pred(P_next=bd.BlockSetStruct(0x1200, 0x2100, 64))) == 1   # writes the P being read
+    assert call(pred(P_next=bd.BlockSetStruct(0x2000, 0x1500, 64))) == 1   # M's counts
+    # the selection's own checks still apply
+    assert lib.prr_select_spec_predict(1, 32, ctypes.byref(kv), 1, 0, 64, 64, ctypes.byref(P), scores,
+                                       ctypes.byref(A), ctypes.byref(M), 0.1, ctypes.byref(st), 1, need - 1,
+                                       ctypes.byref(pred()), None) == 3
