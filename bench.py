@@ -28,6 +28,7 @@ of the dominant kernel (spec-attn), and the CPU oracle timed on a bounded sample
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import statistics
@@ -56,6 +57,10 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=64, help="(sequence, kv head) units in the CPU sample")
     ap.add_argument("--cpu-steps", type=int, default=0, help="decode steps in the CPU sample (0: all timed)")
+    ap.add_argument("--stack", type=int, default=0,
+                    help="also time a stack of this many layers (own caches and predictor state each) with each "
+                         "layer's predictor carried by the next layer's launch, against the same layers run "
+                         "with the predictor on its own")
     ap.add_argument("--score-mode", choices=("quest", "mean"), default="quest",
                     help="block summary selection scores: Quest's min/max bound or the block's mean key")
     ap.add_argument("--append", action="store_true",
@@ -155,6 +160,31 @@ def cpu_baseline(inp, w, units, steps, score_mode="quest"):
     }
 
 
+class EventPool:
+    """Timing events made before a timed region.  torch creates a HIP event at its first record, and a
+    creation can hold the host for milliseconds; when the GPU has drained its queue meanwhile, the stall
+    lands between two timing events.  reserve(n) creates n events (one record each) up front; calling
+    the pool hands them out."""
+
+    def __init__(self):
+        self.free = []
+
+    def reserve(self, n: int):
+        import torch
+
+        s = torch.cuda.current_stream()
+        for _ in range(max(0, n - len(self.free))):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(s)
+            self.free.append(e)
+        torch.cuda.synchronize()
+
+    def __call__(self):
+        import torch
+
+        return self.free.pop() if self.free else torch.cuda.Event(enable_timing=True)
+
+
 def delta_sweep(args, w, inp, kv, meta, flush, ev):
     """Layer-step time against the speculation budget |P| = delta K (the pages' critical-path-aware budget):
     for each delta, a fresh trajectory (step 0 untimed), then `delta_steps` lean one-stream steps."""
@@ -173,12 +203,12 @@ def delta_sweep(args, w, inp, kv, meta, flush, ev):
         torch.cuda.synchronize()
         L.reset()
         L.step(inp.q[0])
-        torch.cuda.synchronize()
+        ev.reserve(2 * n)
         times, hits, missed, pc = [], [], [], []
         for i in range(n):
             P = L.P_cur
             flush()
-            tm = StepTimers.lean()
+            tm = StepTimers(ev(), None, ev(), None)
             L.step(inp.q[1 + i], tm)
             torch.cuda.synchronize()
             times.append(tm.start.elapsed_time(tm.repair_end) * 1e3)
@@ -196,6 +226,70 @@ def delta_sweep(args, w, inp, kv, meta, flush, ev):
         del L
         log(f"[bench] delta {d}: {out[-1]}")
     return out
+
+
+def measure_stack(args, w, layer0, inp0, flush, ev):
+    """Decode steps through args.stack layers of the workload's shape (layer 0 is the main layer, the others
+    get inputs of their own seeds): per-layer time with the predictor carried by the next layer's launch
+    (PRRStack) against the same layers with the predictor as its own launch.  The cache is flushed before
+    every layer, outside the timed region."""
+    import torch
+
+    from block_sparse_attention_quest_amd import binding as bd
+    from block_sparse_attention_quest_amd import workloads as wl
+    from block_sparse_attention_quest_amd.layer_step import PRRLayer, PRRStack, StepTimers
+
+    L, K = args.stack, args.steps
+    layers, qs = [layer0], [inp0.q]
+    for i in range(1, L):
+        wi = wl.scaled(w, seed=w.seed + 1000 * i)
+        inp = wl.make_inputs(wi, layer0.kv.k.device)
+        kv = bd.KVCache(inp.k_cache, inp.v_cache, inp.page_table, inp.seq_len)
+        layers.append(PRRLayer(kv, w.num_q_heads, w.block, w.topk, w.topk, ema=w.ema, scale=w.scale,
+                               score_mode=args.score_mode))
+        qs.append(inp.q)
+        del inp
+    torch.cuda.synchronize()
+    log(f"[bench] stack of {L} layers ready")
+    el = lambda a, b: a.elapsed_time(b) * 1e3
+
+    def run(carried: bool, K: int):
+        ev.reserve(2 * L * K)
+        for layer in layers:
+            layer.reset()
+        stack = PRRStack(layers)
+        for layer in layers:   # decode step 0 (P empty), not timed
+            layer.step(qs[layers.index(layer)][0])
+        torch.cuda.synchronize()
+        per_layer = []
+        for i in range(K):
+            t = 1 + i
+            if carried:
+                tms = [StepTimers(ev(), None, ev(), None) for _ in range(L)]
+                stack.step([q[t] for q in qs], timers=tms, before_layer=lambda l: flush())
+                per_layer.append([(tm.start, tm.repair_end) for tm in tms])
+            else:
+                row = []
+                for li, layer in enumerate(layers):
+                    flush()
+                    tm = StepTimers(ev(), None, None, ev())
+                    layer.step(qs[li][t], tm)
+                    row.append((tm.start, tm.predict_end))
+                per_layer.append(row)
+        stack.flush()
+        torch.cuda.synchronize()
+        return [el(a, b) for row in per_layer for a, b in row]
+
+    run(True, 2)   # first launches of the carrying kernels (code object loads), not timed
+    alone = run(False, K)
+    carried = run(True, K)
+    for layer in layers[1:]:
+        del layer
+    med = lambda xs: round(float(statistics.median(xs)), 2)
+    return {"layers": L, "us_per_layer_carried_median": med(carried), "us_per_layer_alone_median": med(alone),
+            "note": "per layer: carried = start of its select_spec (which also runs the previous layer's "
+                    "predictor) to the end of its repair; alone = start of select_spec to the end of its own "
+                    "predictor launch; both one stream, cache flushed before every layer"}
 
 
 def main():
@@ -252,9 +346,24 @@ def main():
     iso_live = torch.empty_like(layer.live)
     iso_P = bd.BlockSet.empty(B, H, w.topk, dev)
 
-    # warmup: a few layer steps, then start the trajectory afresh
+    # warmup: a few layer steps and every call the timed loop isolates (a kernel's first launch in the
+    # process loads its code object, milliseconds that would land in one timed step), then start the
+    # trajectory afresh
     for t in range(args.warmup):
-        layer.step(inp.q[t % w.steps])
+        q = inp.q[t % w.steps]
+        layer.step(q)
+        P = layer.P_cur
+        bd.spec_attn(q, kv, w.block, P, w.scale, out=iso_state, ws=ws_iso_spec)
+        bd.repair(q, kv, w.block, layer.M, w.scale, iso_state, ws=ws_iso_rep)
+        bd.select(q, kv, layer.meta, w.block, w.topk, P=P, scores=iso_scores, A=iso_A, M=iso_M,
+                  mode=args.score_mode)
+        bd.select_spec(q, kv, layer.meta, w.block, w.topk, P, w.scale, scores=iso_scores, A=iso_A, M=iso_M,
+                       out=iso_state, ws=ws_iso_spec, mode=args.score_mode)
+        iso_level.copy_(layer.level)
+        iso_trend.copy_(layer.trend)
+        iso_live.copy_(layer.live)
+        bd.predict(layer.scores, kv.seq_len, w.block, *w.ema, w.topk, iso_level, iso_trend, iso_live, P_next=iso_P)
+        flush()
     torch.cuda.synchronize()
     layer.reset()
     layer.step(inp.q[0])          # decode step 0: P empty (plain DSA through repair), not timed
@@ -267,7 +376,8 @@ def main():
         del src, dst
 
     crit = torch.cuda.current_stream()
-    ev = lambda: torch.cuda.Event(enable_timing=True)
+    ev = EventPool()
+    ev.reserve(K * (2 + 4 + 2 * 6))
     rec = []
     p_counts = torch.zeros((K, B, H), dtype=torch.int32, device=dev)
     m_counts = torch.zeros_like(p_counts)
@@ -277,6 +387,7 @@ def main():
     append_pairs = []
 
     torch.cuda.synchronize()
+    gc.disable()   # no collector pauses between a kernel and its timing event
     wall0 = time.perf_counter()
     for i in range(K):
         t = 1 + i
@@ -291,7 +402,7 @@ def main():
             append_pairs.append((e0, e1))
         # 1. layer step with a breakdown
         flush()
-        tm = StepTimers.make()
+        tm = StepTimers(ev(), ev(), ev(), ev())
         layer.step(q, tm)
         p_counts[i].copy_(P.count)
         m_counts[i].copy_(layer.M.count)
@@ -334,7 +445,7 @@ def main():
             inp.seq_len.copy_(len0)
             (bd.build_meta if args.score_mode == "quest" else bd.build_mean_meta)(kv, w.block, layer.meta)
         layer.step(inp.q[0])
-        torch.cuda.synchronize()
+        ev.reserve(2 * K)
         out = []
         for i in range(K):
             if args.append:
@@ -344,7 +455,7 @@ def main():
                 tm = TwoStreamTimers(ev(), None, None, None, None, ev())
                 layer.step_two_streams(inp.q[1 + i], tm)
             else:
-                tm = StepTimers.lean()
+                tm = StepTimers(ev(), None, ev(), None)
                 layer.step(inp.q[1 + i], tm)
             out.append((tm.start, tm.repair_end))
         torch.cuda.synchronize()
@@ -435,6 +546,8 @@ def main():
         "us_spec_attn_median": med(spec_us),
         "us_spec_attn_p10_p90": [round(float(np.percentile(spec_us, 10)), 2),
                                  round(float(np.percentile(spec_us, 90)), 2)],
+        "us_spec_attn_max": round(float(max(spec_us)), 2),
+        "us_repair_max": round(float(max(rep_us)), 2),
         "us_repair_median": med(rep_us),
         "us_repair_p10_p90": [round(float(np.percentile(rep_us, 10)), 2),
                               round(float(np.percentile(rep_us, 90)), 2)],
@@ -470,11 +583,14 @@ def main():
             args.delta_sweep = ""
     if args.delta_sweep:
         result["delta_sweep"] = delta_sweep(args, w, inp, kv, layer.meta, flush, ev)
+    if args.stack > 1 and not args.append:
+        result["stack"] = measure_stack(args, w, layer, inp, flush, ev)
     if not args.no_cpu_baseline:
         steps = args.cpu_steps if args.cpu_steps > 0 else K
         units = min(args.cpu_units, B * H)
         log(f"[bench] timing the CPU oracle on {units} units x {steps} steps")
         result["cpu_baseline"] = cpu_baseline(inp, w, units, steps, args.score_mode)
+    gc.enable()
     print(json.dumps(result), flush=True)
 
 

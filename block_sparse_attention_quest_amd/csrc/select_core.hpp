@@ -312,6 +312,7 @@ __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u,
     __shared__ double s_qbar[D];
     __shared__ int s_row[D];             // metadata row of channel i: 1 (max) when qbar_i >= 0, else 0 (min)
     const int b = u / p.hkv, kvh = u - b * p.hkv;
+    const int slen_raw = p.seq_len[b];   // in flight with the query loads
     if (threadIdx.x < D) {
         // qbar_i = (sum_{g=0}^{G-1} q_{kvh G + g, i}) / G, summed in order from +0.0
         double acc = 0.0;
@@ -326,7 +327,7 @@ __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u,
         s_row[threadIdx.x] = qb >= 0.0 ? 1 : 0;
     }
     __syncthreads();
-    const int slen = max(p.seq_len[b], 0);
+    const int slen = max(slen_raw, 0);
     const int nb = min((slen + p.block - 1) / p.block, p.nmax);
     const int p0 = (bx * 256 + threadIdx.x) * BPL;
     if (p0 >= nb) return;
@@ -437,10 +438,12 @@ __device__ __forceinline__ void topk_body(const TopkParams &p, int u) {
     __shared__ TopkSmem<W> sm;
     __shared__ uint32_t s_pbits[TPB * KPT / 32];
     const int b = u / p.hkv;
-    const int slen = p.seq_len[b];
-    const int nb = min((slen + p.block - 1) / p.block, p.nmax);
     const bool want_m = p.m_idx != nullptr;
-    // the score loads go out first; the P bitmap is built while they are in flight
+    // Every load goes out at once (one memory round trip): the length, P's count, the whole score row
+    // and P's first TPB entries, none waiting for another; the row past the unit's block count and P
+    // past its count are masked afterwards.
+    const int slen = p.seq_len[b];
+    const int pcnt = want_m ? p.p_cnt[u] : 0;
     uint64_t key[KPT];
     const int base = threadIdx.x * KPT;
     const double *row = p.scores + (size_t)u * p.nmax;
@@ -448,15 +451,19 @@ __device__ __forceinline__ void topk_body(const TopkParams &p, int u) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         if constexpr (COHERENT)
-            sv[j] = base + j < nb ? __hip_atomic_load(&row[base + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0;
+            sv[j] = base + j < p.nmax ? __hip_atomic_load(&row[base + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                      : 0.0;
         else
-            sv[j] = base + j < nb ? row[base + j] : 0.0;
+            sv[j] = base + j < p.nmax ? row[base + j] : 0.0;
     }
+    const int x0 = want_m && (int)threadIdx.x < p.p_cap ? p.p_idx[(size_t)u * p.p_cap + threadIdx.x] : -1;
+    const int nb = min((slen + p.block - 1) / p.block, p.nmax);
     if (want_m) {
         for (int i = threadIdx.x; i < TPB * KPT / 32; i += TPB) s_pbits[i] = 0u;
         __syncthreads();
-        const int pc = min(max(p.p_cnt[u], 0), p.p_cap);
-        for (int i = threadIdx.x; i < pc; i += TPB) {
+        const int pc = min(max(pcnt, 0), p.p_cap);
+        if ((int)threadIdx.x < pc && x0 >= 0 && x0 < nb) atomicOr(&s_pbits[x0 >> 5], 1u << (x0 & 31));
+        for (int i = threadIdx.x + TPB; i < pc; i += TPB) {
             const int x = p.p_idx[(size_t)u * p.p_cap + i];
             if (x >= 0 && x < nb) atomicOr(&s_pbits[x >> 5], 1u << (x & 31));
         }
@@ -539,11 +546,26 @@ __device__ __forceinline__ void topk_candidates_body(const TopkParams &p, int u,
     __shared__ int s_cnt[TPB];
     __shared__ int s_total;
     const int b = u / p.hkv;
-    const int slen = p.seq_len[b];
-    const int nb = min((slen + p.block - 1) / p.block, p.nmax);
     const bool want_m = p.m_idx != nullptr;
-    if (threadIdx.x < nparts)
-        s_cnt[threadIdx.x] = __hip_atomic_load(&ccnt[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Every load goes out at once, as in topk_body: the length, P's count, the part counts, every
+    // candidate slot and P's first TPB entries; slots past their part's count are masked afterwards.
+    const int slen = p.seq_len[b];
+    const int pcnt = want_m ? p.p_cnt[u] : 0;
+    const int my_cnt = (int)threadIdx.x < nparts
+                           ? __hip_atomic_load(&ccnt[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+    const int base = threadIdx.x * KPT;
+    const int nslots = nparts * kl;
+    uint64_t key[KPT];
+    int32_t idx[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int pos = base + j;
+        key[j] = pos < nslots ? __hip_atomic_load(&ckey[pos], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+        idx[j] = pos < nslots ? __hip_atomic_load(&cidx[pos], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+    }
+    const int x0 = want_m && (int)threadIdx.x < p.p_cap ? p.p_idx[(size_t)u * p.p_cap + threadIdx.x] : -1;
+    const int nb = min((slen + p.block - 1) / p.block, p.nmax);
+    if ((int)threadIdx.x < nparts) s_cnt[threadIdx.x] = my_cnt;
     if (want_m)
         for (int i = threadIdx.x; i < (nb + 31) / 32; i += TPB) s_pbits[i] = 0u;
     __syncthreads();
@@ -552,22 +574,18 @@ __device__ __forceinline__ void topk_candidates_body(const TopkParams &p, int u,
         for (int c = 0; c < nparts; ++c) t += s_cnt[c];
         s_total = t;
     }
-    const int base = threadIdx.x * KPT;
-    uint64_t key[KPT];
-    int32_t idx[KPT];
     uint32_t valid = 0;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         const int pos = base + j;
         const int c = pos / kl, slot = pos - c * kl;
-        const bool ok = c < nparts && slot < s_cnt[min(c, nparts - 1)];
-        key[j] = ok ? __hip_atomic_load(&ckey[pos], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
-        idx[j] = ok ? __hip_atomic_load(&cidx[pos], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-        if (ok) valid |= 1u << j;
+        if (c < nparts && slot < s_cnt[min(c, nparts - 1)]) valid |= 1u << j;
+        else key[j] = 0ull;
     }
     if (want_m) {
-        const int pc = min(max(p.p_cnt[u], 0), p.p_cap);
-        for (int i = threadIdx.x; i < pc; i += TPB) {
+        const int pc = min(max(pcnt, 0), p.p_cap);
+        if ((int)threadIdx.x < pc && x0 >= 0 && x0 < nb) atomicOr(&s_pbits[x0 >> 5], 1u << (x0 & 31));
+        for (int i = threadIdx.x + TPB; i < pc; i += TPB) {
             const int x = p.p_idx[(size_t)u * p.p_cap + i];
             if (x >= 0 && x < nb) atomicOr(&s_pbits[x >> 5], 1u << (x & 31));
         }
@@ -618,22 +636,39 @@ __device__ __forceinline__ void predict_body(const PredictParams &p, int u) {
     constexpr int W = TPB / 64;
     __shared__ TopkSmem<W> sm;
     const int b = u / p.hkv;
+    // Up to 16 keys per thread every load goes out at once (one memory round trip): the length, the live
+    // count and the row's scores and state over all max_blocks columns; columns past the unit's block
+    // count are not used.  With 32 keys per thread the state would not fit in registers: the loads then
+    // wait for the length and cover the unit's blocks only.
+    constexpr bool PREFETCH = KPT <= 16;
     const int slen = p.seq_len[b];
-    const int nb = min((slen + p.block - 1) / p.block, p.nmax);
-    const int live = min(max(p.live[u], 0), nb);
-    const double one_a = dsub(1.0, p.alpha);
-    const double one_b = dsub(1.0, p.beta);
+    const int live_raw = p.live[u];
     const size_t ro = (size_t)u * p.nmax;
     const int base = threadIdx.x * KPT;
+    double is_v[PREFETCH ? KPT : 1], l0_v[PREFETCH ? KPT : 1], t0_v[PREFETCH ? KPT : 1];
+    if constexpr (PREFETCH) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int i = base + j;
+            const bool in = i < p.nmax;
+            is_v[j] = in ? p.scores[ro + i] : 0.0;
+            l0_v[j] = in ? p.level[ro + i] : 0.0;
+            t0_v[j] = in ? p.trend[ro + i] : 0.0;
+        }
+    }
+    const int nb = min((slen + p.block - 1) / p.block, p.nmax);
+    const int live = min(max(live_raw, 0), nb);
+    const double one_a = dsub(1.0, p.alpha);
+    const double one_b = dsub(1.0, p.beta);
     uint64_t key[KPT];
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         const int i = base + j;
         key[j] = 0ull;
         if (i < nb) {
-            // the state is loaded whether or not the block is live, so these loads do not wait for `live`
-            const double is = p.scores[ro + i];
-            const double l0 = p.level[ro + i], t0 = p.trend[ro + i];
+            const double is = PREFETCH ? is_v[PREFETCH ? j : 0] : p.scores[ro + i];
+            const double l0 = PREFETCH ? l0_v[PREFETCH ? j : 0] : p.level[ro + i];
+            const double t0 = PREFETCH ? t0_v[PREFETCH ? j : 0] : p.trend[ro + i];
             double lv, tr;
             if (i < live) {
                 // trend = beta (IS - level_old) + (1 - beta) trend_old;  level = alpha IS + (1 - alpha) level_old

@@ -27,9 +27,11 @@
 // otherwise (more candidates than that) the separate top-K kernel follows the launch.
 //
 // Predictor step of another layer.  In a stack of layers the predictor of layer l needs only layer l's
-// scores and is off the critical path ([paper] §1, §4.1); its workgroups can ride along in layer l + 1's
-// launch, after the speculative ones in dispatch order, so they take the slots the scoring workgroups
-// leave.  The two touch disjoint buffers.
+// scores and is off the critical path ([paper] §1, §4.1), so layer l + 1's launch can carry it.  The
+// scoring workgroups take its units from a work counter once their own scoring is done (and the top-K,
+// for a unit's last arriver): the ones that finish first take most of them, the speculative pass keeps
+// every slot it had (extra workgroups at the end of the grid would wait for a free slot and run past
+// it), and the top-K is not delayed.  The two touch disjoint buffers.
 
 #include "select_core.hpp"
 #include "attn_core.hpp"
@@ -40,8 +42,10 @@ namespace {
 // Workgroup s < nsx * units scores blocks [BPW (s mod nsx), +BPW) of unit s / nsx (BPW = 512 blocks for
 // bf16 min/max metadata, 256 for fp32 block means: MEAN) and, if it is the unit's last to finish and
 // KPT > 0, runs the unit's top-K (KPT keys per thread, 256 KPT >= the unit's block count); the remaining
-// n_spec workgroups run the speculative pass, and (PRED) the last n_pred workgroups each run the predictor
-// step of one unit of another layer (8 keys per thread: rows of up to 2048 blocks).  Register use is the
+// n_spec workgroups run the speculative pass.  PRED: the scoring workgroups then draw the n_pred units
+// of another layer's predictor step from *pred_ctr (8 keys per thread: rows of up to 2048 blocks); every
+// workgroup draws until it gets an index >= n_pred, so the launch makes exactly n_pred + n_score draws
+// and the one that draws the last index resets the counter for the next launch.  Register use is the
 // attention part's (two waves per SIMD).
 struct CandParams {
     uint64_t *key;   // [units][nsx][kl]
@@ -53,13 +57,7 @@ struct CandParams {
 template <int D, int KPT, bool TWO, bool MEAN, bool PRED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void select_spec_kernel(
     AttnParams ap, ScoreParams sp, TopkParams tp, CandParams cp, PredictParams pp, uint32_t *arrivals,
-    int n_score, int nsx, int n_spec) {
-    if constexpr (PRED) {
-        if ((int)blockIdx.x >= n_score + n_spec) {
-            predict_body<8, 256>(pp, (int)blockIdx.x - n_score - n_spec);
-            return;
-        }
-    }
+    uint32_t *pred_ctr, int n_score, int nsx, int n_spec, int n_pred) {
     if ((int)blockIdx.x >= n_score) {
         attn_body<true, D, false>(ap, (int)blockIdx.x - n_score, n_spec);
         return;
@@ -77,8 +75,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
         const int nb = min((max(sp.seq_len[b], 0) + sp.block - 1) / sp.block, sp.nmax);
         const int n_local = min(max(nb - bx * BPW, 0), BPW);
         const size_t part = (size_t)u * nsx + bx;
-        local_candidates<BPL>(kept, n_local, cp.kl, bx * BPW, cp.key + part * cp.kl,
-                                          cp.idx + part * cp.kl, cp.cnt + part, sm);
+        local_candidates<BPL>(kept, n_local, cp.kl, bx * BPW, cp.key + part * cp.kl, cp.idx + part * cp.kl,
+                              cp.cnt + part, sm);
     }
     if constexpr (KPT != 0) {
         __shared__ int s_last;
@@ -98,6 +96,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
                                           cp.cnt + (size_t)u * nsx, nsx, cp.kl);
             else
                 topk_body<KPT, 256, true>(tp, u);
+        }
+    }
+    if constexpr (PRED) {
+        __shared__ int s_j;
+        for (;;) {
+            __syncthreads();   // the workgroup's shared scratch is free again, s_j read by every thread
+            if (threadIdx.x == 0) {
+                const uint32_t j = __hip_atomic_fetch_add(pred_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (j == (uint32_t)(n_pred + n_score - 1))
+                    __hip_atomic_store(pred_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_j = (int)j;
+            }
+            __syncthreads();
+            const int j = s_j;
+            if (j >= n_pred) break;
+            predict_body<8, 256>(pp, j);
         }
     }
 }
@@ -137,10 +151,15 @@ static size_t candidate_bytes(int units, int nmax, int topk, bool mean) {
     return parts * pl.kl * 12 + parts * 4;
 }
 
+// The carried predictor's work counter sits after the candidates, in a 256-byte slot of its own.
+static size_t pred_counter_offset(int batch, int hq, int hkv, int d, int block, int cap, int nmax, int topk) {
+    const size_t cand = std::max(candidate_bytes(batch * hkv, nmax, topk, false),
+                                 candidate_bytes(batch * hkv, nmax, topk, true));
+    return attn_workspace_bytes(batch, hq, hkv, d, block, cap) + (cand + 255) / 256 * 256;
+}
+
 size_t select_spec_workspace_bytes(int batch, int hq, int hkv, int d, int block, int cap, int nmax, int topk) {
-    const size_t attn = attn_workspace_bytes(batch, hq, hkv, d, block, cap);
-    return attn + std::max(candidate_bytes(batch * hkv, nmax, topk, false),
-                           candidate_bytes(batch * hkv, nmax, topk, true));
+    return pred_counter_offset(batch, hq, hkv, d, block, cap, nmax, topk) + 256;
 }
 
 hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,
@@ -217,7 +236,9 @@ hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const voi
         pp.gamma = pred->gamma;
         n_pred = pred->batch * pred->hkv;
     }
-    const long grid = (long)n_spec + (long)nsx * units + n_pred;
+    const long grid = (long)n_spec + (long)nsx * units;
+    uint32_t *pred_ctr =
+        (uint32_t *)((char *)ws + pred_counter_offset(kv.batch, hq, kv.hkv, kv.d, block, p_cap, nmax, topk));
     if (grid > 0x7fffffffL) return hipErrorInvalidValue;
     const SelectSpecPlan plan = select_spec_plan(nmax, topk, mean);
     CandParams cp;
@@ -231,7 +252,8 @@ hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const voi
 #define PRR_SS(DD, K, T, MN, PR)                                                                           \
     if (kv.d == DD && kpt == K && two == T && mean == MN && fuse_pred == PR) {                              \
         select_spec_kernel<DD, K, T, MN, PR><<<(int)grid, 256, 0, stream>>>(ap, sp, tp, cp, pp, arrivals,      \
-                                                                            nsx * units, nsx, n_spec);      \
+                                                                            pred_ctr, nsx * units, nsx, n_spec, \
+                                                                            n_pred);                        \
     } else
 #define PRR_SS_K(DD, MN, PR)                                                                                \
     PRR_SS(DD, 0, false, MN, PR) PRR_SS(DD, 1, false, MN, PR) PRR_SS(DD, 2, false, MN, PR)                    \

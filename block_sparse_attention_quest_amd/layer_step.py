@@ -236,17 +236,21 @@ class PRRStack:
         self.pending: Optional[bd.PredictArgs] = None
         self.pending_owner = -1
 
-    def step(self, qs, k_new=None, v_new=None) -> list:
+    def step(self, qs, k_new=None, v_new=None, timers=None, before_layer=None) -> list:
         """One decode step through every layer: qs[l] [B][Hq][d]; k_new[l], v_new[l] [B][Hkv][d] (optional)
-        are appended to layer l's cache first.  Returns each layer's output tensor."""
+        are appended to layer l's cache first.  Returns each layer's output tensor.  timers[l]: optional
+        StepTimers of layer l's step; before_layer(l): optional work enqueued before layer l (e.g. the
+        rest of the model's layer)."""
         outs = []
         for i, layer in enumerate(self.layers):
             if self.pending_owner == i:
                 # a layer's own predictor writes the set its next selection reads: it runs first, alone
                 self.flush()
+            if before_layer is not None:
+                before_layer(i)
             if k_new is not None:
                 layer.append(k_new[i], v_new[i])
-            outs.append(layer.step(qs[i], carry=self.pending, defer_predict=True))
+            outs.append(layer.step(qs[i], timers[i] if timers else None, carry=self.pending, defer_predict=True))
             self.pending, self.pending_owner = layer.take_pending_predict(), i
         return outs
 

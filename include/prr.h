@@ -166,7 +166,8 @@ prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv
  * compute, as one grid whose workgroups do either part (bf16 caches; fp32 caches run the two calls in
  * turn), followed by the top-K on the same stream.  P and M must be non-NULL; A->cap and M->cap >= topk;
  * N_b <= 32768.  ws: prr_select_spec_workspace_bytes(kv, num_q_heads, block, topk, P->cap): the attention
- * workspace of prr_spec_attn plus room for top-K candidates. */
+ * workspace of prr_spec_attn plus room for top-K candidates and a work counter (zeroed once like an
+ * attention workspace; every call leaves it ready for the next). */
 size_t prr_select_spec_workspace_bytes(const prr_kv_cache *kv, int32_t num_q_heads, int32_t block, int32_t topk,
                                        int32_t cap);
 
