@@ -39,8 +39,26 @@ import numpy as np
 # --------------------------------------------------------------------------------------------------
 
 
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """Values of 8-bit E4M3 floating-point codes (the OCP 8-bit format in its FN variant: no
+    infinities): bit 7 the sign, bits 6-3 the exponent field E (bias 7), bits 2-0 the mantissa field M.
+    E = 0 holds the subnormals M * 2^-9 (and the zeros); otherwise the value is (1 + M/8) * 2^(E - 7);
+    E = 15 with M = 7 is NaN, so the largest finite magnitude is 448."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    return np.where((e == 15) & (m == 7), np.nan, sign * mag)
+
+
 def upcast(arr: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact float64 values of stored elements: raw bf16 bit patterns (uint16) or fp32."""
+    """Exact float64 values of stored elements: raw bf16 bit patterns (uint16), fp32, or for an fp8
+    cache its E4M3 codes (uint8); an fp8 cache keeps queries and min/max metadata in bf16, so uint16
+    arrays under "fp8" are bf16 bit patterns."""
+    if dtype == "fp8":
+        a = np.asarray(arr)
+        return upcast(a, "bf16") if a.dtype == np.uint16 else fp8_e4m3_decode(a)
     if dtype == "bf16":
         a = np.asarray(arr, dtype=np.uint16).astype(np.uint32) << 16
         return a.view(np.float32).astype(np.float64)

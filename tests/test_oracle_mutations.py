@@ -11,6 +11,7 @@ import pytest
 
 import test_oracle_attention as ta
 import test_oracle_ema as te
+import test_oracle_fp8 as tf
 import test_oracle_mean as tm
 import test_oracle_select as ts
 from _util import oracle_view
@@ -135,6 +136,32 @@ def mean_skips_first_token(kv, b, kvh, p, block):
     return (K.sum(axis=0) / K.shape[0]).astype(np.float32).astype(np.float64)
 
 
+def fp8_bias_8(codes):
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e, m = (c >> 3) & 0xF, c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -10, (1.0 + m / 8.0) * np.exp2((e - 8).astype(np.float64)))
+    return np.where((e == 15) & (m == 7), np.nan, sign * mag)
+
+
+def fp8_subnormals_flushed(codes):
+    v = _orig["fp8_e4m3_decode"](codes)
+    e = (np.asarray(codes, dtype=np.uint8) >> 3) & 0xF
+    return np.where(e == 0, 0.0 * v, v)
+
+
+def fp8_no_nan(codes):
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e, m = (c >> 3) & 0xF, c & 0x7
+    return sign * np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+
+
+def _fp8_checks():
+    return [(tf.test_decode_matches_torch_float8_e4m3fn, ()), (tf.test_known_codes, ()),
+            (tf.test_positive_codes_increase_and_negatives_mirror, ())]
+
+
 def _mean_checks():
     q, kv = oracle_view(wl.make_inputs(tm.W))
     fxm = (q[0], kv, orc.build_meta(kv, tm.W.block, tm.W.num_kv_heads),
@@ -177,6 +204,9 @@ MUTATIONS = [
     ("block_mean", mean_divides_by_block_size, _mean_checks),
     ("block_mean", mean_skips_first_token, _mean_checks),
     ("mean_scores", mean_scores_abs, _mean_checks),
+    ("fp8_e4m3_decode", fp8_bias_8, _fp8_checks),
+    ("fp8_e4m3_decode", fp8_subnormals_flushed, _fp8_checks),
+    ("fp8_e4m3_decode", fp8_no_nan, _fp8_checks),
 ]
 
 
@@ -187,4 +217,4 @@ def test_pins_catch_planted_mistake(monkeypatch, target, mutant, checks):
 
 
 def test_unmutated_oracle_passes_the_same_checks():
-    assert not _fails(*_attention_checks(), *_select_checks(), *_ema_checks(), *_mean_checks())
+    assert not _fails(*_attention_checks(), *_select_checks(), *_ema_checks(), *_mean_checks(), *_fp8_checks())
