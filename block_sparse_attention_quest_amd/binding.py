@@ -16,7 +16,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libprr.so")
 
-PRR_F32, PRR_BF16 = 0, 1
+PRR_F32, PRR_BF16, PRR_FP8 = 0, 1, 2
 PAGE_SIZE = 16
 
 # Every symbol include/prr.h declares.
@@ -139,6 +139,8 @@ def _dtype_code(t: torch.Tensor) -> int:
         return PRR_BF16
     if t.dtype == torch.float32:
         return PRR_F32
+    if t.dtype == torch.float8_e4m3fn:
+        return PRR_FP8
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -273,13 +275,13 @@ def workspace_clear(ws: Workspace, stream=None):
 
 
 def build_meta(kv: KVCache, block: int, meta: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Block min/max metadata [B][Hkv][d][2][stride] in the cache dtype."""
+    """Block min/max metadata [B][Hkv][d][2][stride] in the cache dtype (bf16 for an fp8 cache)."""
     lib = load_library()
     s = kv.struct()
     if meta is None:
         stride = lib.prr_meta_stride(ctypes.byref(s), block)
-        meta = torch.empty((kv.batch, kv.num_kv_heads, kv.head_dim, 2, stride), dtype=kv.k.dtype,
-                           device=kv.k.device)
+        dt = torch.bfloat16 if kv.k.dtype == torch.float8_e4m3fn else kv.k.dtype
+        meta = torch.empty((kv.batch, kv.num_kv_heads, kv.head_dim, 2, stride), dtype=dt, device=kv.k.device)
     _check(lib.prr_build_meta(ctypes.byref(s), block, _ptr(meta), _stream(stream)), "prr_build_meta")
     return meta
 

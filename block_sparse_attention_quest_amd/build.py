@@ -27,6 +27,7 @@ SOURCES = {
     "select.hip": ["-ffp-contract=off"],
     "calib.hip": ["-ffp-contract=off"],
     "step.hip": [],
+    "step_fp8.hip": [],
     "append.hip": [],
     "prr_api.cpp": ["-x", "hip"],
 }

@@ -22,6 +22,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "kv_types.hpp"
 #include "prr_internal.hpp"
 
 namespace prr {
@@ -40,12 +41,28 @@ struct AppendParams {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
+// Element i of a cache-typed array, exactly as a float.
+template <int KT>
+__device__ __forceinline__ float elem_f32(const void *a, size_t i) {
+    if constexpr (KT == kKtF32) return ((const float *)a)[i];
+    else if constexpr (KT == kKtBf16) return bf16_bits_to_f32(((const uint16_t *)a)[i]);
+    else return fp8_to_f32(((const uint8_t *)a)[i]);
+}
+
+// dst[di] = src[si] for cache-typed arrays (a plain copy of the element's bytes).
+template <int KT>
+__device__ __forceinline__ void copy_elem(void *dst, size_t di, const void *src, size_t si) {
+    if constexpr (KT == kKtF32) ((float *)dst)[di] = ((const float *)src)[si];
+    else if constexpr (KT == kKtBf16) ((uint16_t *)dst)[di] = ((const uint16_t *)src)[si];
+    else ((uint8_t *)dst)[di] = ((const uint8_t *)src)[si];
+}
+
 __device__ __forceinline__ double dadd_exact(double a, double b) {
 #pragma clang fp contract(off)
     return a + b;
 }
 
-template <bool BF16, int D, bool MEAN>
+template <int KT, int D, bool MEAN>
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     __shared__ int s_t;
     const int b = blockIdx.x;
@@ -60,6 +77,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     const int slot = t % kPage;
     const int blk = t / p.block;
     const bool first = (t % p.block) == 0;
+    const bool ok = ph >= 0 && ph < p.num_pages;
 #pragma unroll 4
     for (int idx = threadIdx.x; idx < p.hkv * D; idx += blockDim.x) {
         const int h = idx / D, i = idx - h * D;
@@ -67,28 +85,21 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
         const size_t kdst = (((size_t)ph * p.hkv + h) * kPage + slot) * D + i;      // [page][Hkv][16][d]
         const size_t vdst = (((size_t)ph * p.hkv + h) * D + i) * kPage + slot;      // [page][Hkv][d][16]
         const size_t row = (((size_t)b * p.hkv + h) * D + i) * 2 * p.stride;        // [B][Hkv][d][2][stride]
-        const bool ok = ph >= 0 && ph < p.num_pages;
         if constexpr (MEAN) {
             if (ok) {
-                if constexpr (BF16) {
-                    ((uint16_t *)p.k)[kdst] = ((const uint16_t *)p.k_new)[src];
-                    ((uint16_t *)p.v)[vdst] = ((const uint16_t *)p.v_new)[src];
-                } else {
-                    ((float *)p.k)[kdst] = ((const float *)p.k_new)[src];
-                    ((float *)p.v)[vdst] = ((const float *)p.v_new)[src];
-                }
+                copy_elem<KT>(p.k, kdst, p.k_new, src);
+                copy_elem<KT>(p.v, vdst, p.v_new, src);
             }
-        } else if constexpr (BF16) {
-            const uint16_t kx = ((const uint16_t *)p.k_new)[src];
-            const uint16_t vx = ((const uint16_t *)p.v_new)[src];
+        } else if constexpr (KT != kKtF32) {
+            // bf16 metadata (an fp8 key is a bf16 value, so min and max stay exact)
+            const float x = elem_f32<KT>(p.k_new, src);
             uint16_t *m16 = (uint16_t *)p.meta;
             const uint16_t mn0 = m16[row + blk], mx0 = m16[row + p.stride + blk];
-            const float x = bf16_bits_to_f32(kx);
             const float mn = first ? x : fminf(bf16_bits_to_f32(mn0), x);
             const float mx = first ? x : fmaxf(bf16_bits_to_f32(mx0), x);
             if (ok) {
-                ((uint16_t *)p.k)[kdst] = kx;
-                ((uint16_t *)p.v)[vdst] = vx;
+                copy_elem<KT>(p.k, kdst, p.k_new, src);
+                copy_elem<KT>(p.v, vdst, p.v_new, src);
                 m16[row + blk] = (uint16_t)(__float_as_uint(mn) >> 16);
                 m16[row + p.stride + blk] = (uint16_t)(__float_as_uint(mx) >> 16);
             }
@@ -107,7 +118,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     }
     if constexpr (MEAN) {
         __syncthreads();   // the new key is in the cache for every thread of the workgroup
-        if (ph >= 0 && ph < p.num_pages) {
+        if (ok) {
             const int t0 = blk * p.block;
             for (int idx = threadIdx.x; idx < p.hkv * D; idx += blockDim.x) {
                 const int h = idx / D, i = idx - h * D;
@@ -116,16 +127,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
                     int pg = p.page_table[(size_t)b * p.max_pages + tt / kPage];
                     pg = min(max(pg, 0), p.num_pages - 1);
                     const size_t off = (((size_t)pg * p.hkv + h) * kPage + (tt % kPage)) * D + i;
-                    const double x = BF16 ? (double)bf16_bits_to_f32(((const uint16_t *)p.k)[off])
-                                          : (double)((const float *)p.k)[off];
-                    acc = dadd_exact(acc, x);
+                    acc = dadd_exact(acc, (double)elem_f32<KT>(p.k, off));
                 }
                 ((float *)p.meta)[(((size_t)b * p.hkv + h) * D + i) * p.stride + blk] = (float)(acc / (double)(t - t0 + 1));
             }
         }
     }
     __syncthreads();
-    if (threadIdx.x == 0 && ph >= 0 && ph < p.num_pages) p.seq_len[b] = t + 1;
+    if (threadIdx.x == 0 && ok) p.seq_len[b] = t + 1;
 }
 
 }  // namespace
@@ -145,11 +154,13 @@ hipError_t launch_append(const KvDesc &kv, void *k, void *v, int32_t *seq_len, c
     p.num_pages = kv.num_pages;
     p.block = block;
     p.stride = stride;
-#define PRR_AP(BF, DD, MN) \
-    if (kv.bf16 == BF && kv.d == DD && mean == MN) append_kernel<BF, DD, MN><<<kv.batch, 256, 0, stream>>>(p); else
-    PRR_AP(true, 128, false) PRR_AP(true, 64, false) PRR_AP(false, 128, false) PRR_AP(false, 64, false)
-    PRR_AP(true, 128, true) PRR_AP(true, 64, true) PRR_AP(false, 128, true) PRR_AP(false, 64, true)
+    const int kt = kv.fp8 ? kKtFp8 : kv.bf16 ? kKtBf16 : kKtF32;
+#define PRR_AP(KT, DD, MN) \
+    if (kt == KT && kv.d == DD && mean == MN) append_kernel<KT, DD, MN><<<kv.batch, 256, 0, stream>>>(p); else
+#define PRR_AP_T(KT) PRR_AP(KT, 128, false) PRR_AP(KT, 64, false) PRR_AP(KT, 128, true) PRR_AP(KT, 64, true)
+    PRR_AP_T(kKtF32) PRR_AP_T(kKtBf16) PRR_AP_T(kKtFp8)
     { return hipErrorInvalidValue; }
+#undef PRR_AP_T
 #undef PRR_AP
     return hipGetLastError();
 }

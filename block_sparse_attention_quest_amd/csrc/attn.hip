@@ -12,22 +12,33 @@ namespace {
 // go.  The fp32 variants (exact-input checks) may use more registers.
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_spec_bf16(AttnParams p) {
-    attn_body<true, D, false, 2>(p, blockIdx.x, gridDim.x);
+    attn_body<kKtBf16, D, false, 2>(p, blockIdx.x, gridDim.x);
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1))) void attn_repair_bf16(AttnParams p) {
-    attn_body<true, D, true, 4>(p, blockIdx.x, gridDim.x);
+    attn_body<kKtBf16, D, true, 4>(p, blockIdx.x, gridDim.x);
+}
+
+// fp8 tiles take half the registers of bf16 ones: twice as many in flight for the same bytes.
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_spec_fp8(AttnParams p) {
+    attn_body<kKtFp8, D, false, 2>(p, blockIdx.x, gridDim.x);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1))) void attn_repair_fp8(AttnParams p) {
+    attn_body<kKtFp8, D, true, 4>(p, blockIdx.x, gridDim.x);
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_spec_f32(AttnParams p) {
-    attn_body<false, D, false>(p, blockIdx.x, gridDim.x);
+    attn_body<kKtF32, D, false>(p, blockIdx.x, gridDim.x);
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_repair_f32(AttnParams p) {
-    attn_body<false, D, true>(p, blockIdx.x, gridDim.x);
+    attn_body<kKtF32, D, true>(p, blockIdx.x, gridDim.x);
 }
 
 __global__ void clear_kernel(uint32_t *w, size_t n) {
@@ -49,7 +60,15 @@ hipError_t launch_attn(const KvDesc &kv, const void *q, int hq, int block, const
     AttnParams p;
     const int grid = attn_setup(p, kv, q, hq, block, idx, count, cap, scale, acc, l, m, out, repair, ws);
     const dim3 blk(kThreads);
-    if (kv.bf16) {
+    if (kv.fp8) {
+        if (repair) {
+            if (kv.d == 128) attn_repair_fp8<128><<<grid, blk, 0, stream>>>(p);
+            else attn_repair_fp8<64><<<grid, blk, 0, stream>>>(p);
+        } else {
+            if (kv.d == 128) attn_spec_fp8<128><<<grid, blk, 0, stream>>>(p);
+            else attn_spec_fp8<64><<<grid, blk, 0, stream>>>(p);
+        }
+    } else if (kv.bf16) {
         if (repair) {
             if (kv.d == 128) attn_repair_bf16<128><<<grid, blk, 0, stream>>>(p);
             else attn_repair_bf16<64><<<grid, blk, 0, stream>>>(p);

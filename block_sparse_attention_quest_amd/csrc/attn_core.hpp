@@ -35,6 +35,10 @@
 //     to tokens so that each lane ends up holding exactly the 8 consecutive tokens that the PV
 //     B-operand needs: no shuffle between the two products.  P enters PV as a bf16 hi + lo pair
 //     (two MFMAs), which keeps the product at ~2^-17 relative error while V stays exact.
+//   * fp8 (E4M3 codes, bf16 queries): the bf16 structure on half the bytes.  A lane loads 16 channels of
+//     a K token (the channels of two k-steps; the query operand takes the same channel order) and 8
+//     tokens of a V channel, and converts them to bf16 in registers, exactly; the products are the bf16
+//     ones.
 //   * fp32: the same structure on v_mfma_f32_16x16x4_f32.
 //   * Softmax: online across tiles (running maximum per query, rescaled sums); waves merge in LDS;
 //     chunks of one unit merge through a small workspace: the last chunk of a unit to finish
@@ -50,6 +54,7 @@
 
 #include <algorithm>
 
+#include "kv_types.hpp"
 #include "prr_internal.hpp"
 
 namespace prr {
@@ -296,6 +301,105 @@ __device__ __forceinline__ void wave_pass_bf16(const AttnParams &p, size_t head0
     for (int b = 0; b < NBUF; ++b) comp(buf[b], t + b);
 }
 
+// ---- fp8 tiles: 32 tokens (2 pages) of E4M3 codes ----
+
+template <int D>
+struct TileE {
+    uint4 k[2][D / 64];   // half h, m: row r of S^T -> token 8(r>>2) + 4h + (r&3), channels 64 m + 16 g .. +16
+    uint2 v[D / 16];      // channel block cb: channel 16 cb + r, tokens 8(g&1) .. +8 of page g>>1
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(TileE<D> &t, const uint8_t *kb, const uint8_t *vb, size_t stride,
+                                          int pa, int pb, int r, int g) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int tt = 8 * (r >> 2) + 4 * h + (r & 3);
+        const int ph = pick(tt >> 4, pa, pb);
+        const uint8_t *kp = kb + (size_t)ph * stride + (tt & 15) * D + 16 * g;
+#pragma unroll
+        for (int m = 0; m < D / 64; ++m) t.k[h][m] = *(const uint4 *)(kp + 64 * m);
+    }
+    const int pv = pick(g >> 1, pa, pb);
+    const uint8_t *vp = vb + (size_t)pv * stride + (size_t)r * kPage + 8 * (g & 1);
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) t.v[cb] = *(const uint2 *)(vp + (size_t)cb * 16 * kPage);
+}
+
+// Eight E4M3 codes (bytes of lo, then of hi) as eight bf16 values, exactly.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+    const bf16x2v a = fp8x2_to_bf16<false>(lo), b = fp8x2_to_bf16<true>(lo);
+    const bf16x2v c = fp8x2_to_bf16<false>(hi), d = fp8x2_to_bf16<true>(hi);
+    bf16x8 r;
+    r[0] = a[0];
+    r[1] = a[1];
+    r[2] = b[0];
+    r[3] = b[1];
+    r[4] = c[0];
+    r[5] = c[1];
+    r[6] = d[0];
+    r[7] = d[1];
+    return r;
+}
+
+// The tile in bf16 (k-step 2 m + e takes channels 64 m + 16 g + 8 e .. +8), then the bf16 products.
+template <int D>
+__device__ __forceinline__ void compute_tile(const TileE<D> &t, const bf16x8 (&qop)[D / 32], WaveState<D> &st,
+                                             int vta, int vtb, float c2, int g) {
+    TileB<D> tb;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int m = 0; m < D / 64; ++m) {
+            tb.k[h][2 * m] = fp8x8_to_bf16(t.k[h][m].x, t.k[h][m].y);
+            tb.k[h][2 * m + 1] = fp8x8_to_bf16(t.k[h][m].z, t.k[h][m].w);
+        }
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb) tb.v[cb] = fp8x8_to_bf16(t.v[cb].x, t.v[cb].y);
+    compute_tile<D>(tb, qop, st, vta, vtb, c2, g);
+}
+
+// Walk nt fp8 tiles, structured like the bf16 walk; the query operand takes the fp8 tiles' channel
+// order.
+template <int D, int NBUF>
+__device__ __forceinline__ void wave_pass_fp8(const AttnParams &p, size_t head0, int kvh, int j, int g,
+                                              LanePage pg, int nt, WaveState<D> &st) {
+    const size_t stride = (size_t)p.hkv * kPage * D;   // bytes per physical page
+    const uint8_t *kb = (const uint8_t *)p.k + (size_t)kvh * kPage * D;
+    const uint8_t *vb = (const uint8_t *)p.v + (size_t)kvh * kPage * D;
+    bf16x8 qop[D / 32];
+    const __bf16 *qb = (const __bf16 *)p.q + (head0 + (j < p.G ? j : 0)) * D;
+#pragma unroll
+    for (int m = 0; m < D / 64; ++m)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) qop[2 * m + e] = *(const bf16x8 *)(qb + 64 * m + 16 * g + 8 * e);
+    auto load = [&](TileE<D> &tb, int t) {
+        load_tile<D>(tb, kb, vb, stride, lane_val(pg.ph, 2 * t), lane_val(pg.ph, 2 * t + 1), j, g);
+    };
+    auto comp = [&](TileE<D> &tb, int t) {
+        compute_tile<D>(tb, qop, st, lane_val(pg.vt, 2 * t), lane_val(pg.vt, 2 * t + 1), p.c2, g);
+    };
+    const int nte = (nt + NBUF - 1) / NBUF * NBUF;   // <= 32: pages 2t, 2t + 1 stay below lane 64
+    TileE<D> buf[NBUF];
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) load(buf[b], b);
+    if (j >= p.G) {
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) qop[s] = bf16x8{};
+    }
+    int t = 0;
+#pragma unroll 1
+    for (; t + NBUF < nte; t += NBUF) {
+#pragma unroll
+        for (int b = 0; b < NBUF; ++b) {
+            comp(buf[b], t + b);
+            load(buf[b], t + NBUF + b);
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) comp(buf[b], t + b);
+}
+
 // ---- fp32 tiles: 16 tokens (1 page) ----
 
 template <int D>
@@ -464,7 +568,7 @@ __device__ __forceinline__ void merge_partials(const AttnParams &p, const float 
     }
 }
 
-template <bool BF16, int D, bool REPAIR, int NBUF = 2>
+template <int KT, int D, bool REPAIR, int NBUF = 2>
 __device__ __forceinline__ void attn_body(const AttnParams &p, int wg, int nwg) {
     constexpr int DP = D + 4;  // padded LDS row
     __shared__ float sm_acc[kWaves][16 * DP];
@@ -523,7 +627,8 @@ __device__ __forceinline__ void attn_body(const AttnParams &p, int wg, int nwg) 
         if (wbeg < wend) {
             const LanePage pg = page_finish(p, look, wbeg, wend, slen);
             const int nw = wend - wbeg;   // pages of this wave, 1 .. pw
-            if constexpr (BF16) wave_pass_bf16<D, NBUF>(p, head0, kvh, j, g, pg, (nw + 1) / 2, st);
+            if constexpr (KT == kKtBf16) wave_pass_bf16<D, NBUF>(p, head0, kvh, j, g, pg, (nw + 1) / 2, st);
+            else if constexpr (KT == kKtFp8) wave_pass_fp8<D, NBUF>(p, head0, kvh, j, g, pg, (nw + 1) / 2, st);
             else wave_pass_f32<D>(p, head0, kvh, j, g, pg, nw, st);
         }
         // wave state -> LDS (lane (j, g) holds channels 16 cb + 4 g + i of query j)

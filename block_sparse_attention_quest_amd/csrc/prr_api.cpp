@@ -20,7 +20,7 @@ prr_status check_kv(const prr_kv_cache *kv) {
         return PRR_EINVAL;
     if (kv->page_size != prr::kPage) return PRR_EUNSUPPORTED;
     if (kv->head_dim != 64 && kv->head_dim != 128) return PRR_EUNSUPPORTED;
-    if (kv->dtype != PRR_F32 && kv->dtype != PRR_BF16) return PRR_EUNSUPPORTED;
+    if (kv->dtype != PRR_F32 && kv->dtype != PRR_BF16 && kv->dtype != PRR_FP8) return PRR_EUNSUPPORTED;
     return PRR_OK;
 }
 
@@ -54,6 +54,7 @@ prr::KvDesc desc(const prr_kv_cache *kv) {
     d.num_pages = kv->num_pages;
     d.max_pages = kv->max_pages;
     d.bf16 = kv->dtype == PRR_BF16;
+    d.fp8 = kv->dtype == PRR_FP8;
     return d;
 }
 
@@ -94,7 +95,7 @@ int32_t prr_meta_stride(const prr_kv_cache *kv, int32_t block) {
 
 size_t prr_meta_bytes(const prr_kv_cache *kv, int32_t block) {
     if (!kv) return 0;
-    const size_t elem = kv->dtype == PRR_BF16 ? 2 : 4;
+    const size_t elem = kv->dtype == PRR_F32 ? 4 : 2;   // bf16 for bf16 and fp8 caches
     return (size_t)kv->batch * kv->num_kv_heads * kv->head_dim * 2 * prr_meta_stride(kv, block) * elem;
 }
 

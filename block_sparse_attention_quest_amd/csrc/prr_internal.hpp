@@ -18,7 +18,8 @@ struct KvDesc {
     const int32_t *page_table;
     const int32_t *seq_len;
     int batch, hkv, d, num_pages, max_pages;
-    bool bf16;
+    bool bf16;   // bf16 K/V and queries
+    bool fp8;    // E4M3 K/V, bf16 queries and metadata
 };
 
 // Attention workspace: 2 x [units] uint32 counters (chunk arrivals, scoring arrivals), padded to 256 B,
@@ -54,6 +55,9 @@ struct SelectSpecPlan {
 };
 SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean);
 
+// Offset of the carried predictor's work counter in the prr_select_spec workspace.
+size_t pred_counter_offset(int batch, int hq, int hkv, int d, int block, int cap, int nmax, int topk);
+
 // Workspace of prr_select_spec: the speculative pass's attention workspace, then (two-stage top-K) the
 // candidates of every scoring workgroup.
 size_t select_spec_workspace_bytes(int batch, int hq, int hkv, int d, int block, int cap, int nmax, int topk);
@@ -84,6 +88,13 @@ hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const voi
                               double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
                               int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m,
                               void *ws, bool mean, const PredictArgs *pred, hipStream_t stream);
+
+// The fused launch for fp8 caches (compiled in its own file; arguments as launch_select_spec).
+hipError_t launch_select_spec_fp8(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,
+                                  int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
+                                  double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
+                                  int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m, void *ws,
+                                  bool mean, const PredictArgs *pred, hipStream_t stream);
 
 hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batch, int hkv,
                           int block, int nmax, double alpha, double beta, double gamma, int budget,

@@ -7,6 +7,7 @@
 //           Decoding" (full paper text)
 
 #include "select_core.hpp"
+#include "kv_types.hpp"
 
 namespace prr {
 namespace {
@@ -23,9 +24,42 @@ struct MetaParams {
     int hkv, max_pages, num_pages, block, stride, nmax;
 };
 
-template <bool BF16, int D>
+// 16 bytes of K at element offset off: the channels they hold as floats (4 for f32, 8 for bf16, 16
+// for fp8), exactly.
+template <int KT>
+constexpr int kElemsPer16B = KT == kKtF32 ? 4 : KT == kKtBf16 ? 8 : 16;
+
+template <int KT>
+__device__ __forceinline__ void load16_as_f32(const void *k, size_t off, float (&x)[kElemsPer16B<KT>]) {
+    if constexpr (KT == kKtF32) {
+        const float4 raw = *(const float4 *)((const float *)k + off);
+        x[0] = raw.x;
+        x[1] = raw.y;
+        x[2] = raw.z;
+        x[3] = raw.w;
+    } else if constexpr (KT == kKtBf16) {
+        const uint4 raw = *(const uint4 *)((const uint16_t *)k + off);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = bf16_to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1))));
+    } else {
+        const uint4 raw = *(const uint4 *)((const uint8_t *)k + off);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float f[4];
+            fp8x4_to_f32(w[q], f);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[4 * q + e] = f[e];
+        }
+    }
+}
+
+// Quest min/max metadata, [B][Hkv][d][2][stride]: fp32 for an f32 cache, bf16 otherwise (an fp8 key is a
+// bf16 value, so its min and max are too).  Lane = block (64 per workgroup), waves take channel groups.
+template <int KT, int D>
 __global__ __launch_bounds__(256) void meta_kernel(MetaParams p) {
-    constexpr int EPL = BF16 ? 8 : 4;          // channels per 16-byte load
+    constexpr int EPL = kElemsPer16B<KT>;   // channels per 16-byte load
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int u = blockIdx.y;
     const int b = u / p.hkv, kvh = u - b * p.hkv;
@@ -46,30 +80,19 @@ __global__ __launch_bounds__(256) void meta_kernel(MetaParams p) {
             int ph = p.page_table[(size_t)b * p.max_pages + t / kPage];
             ph = min(max(ph, 0), p.num_pages - 1);
             const size_t off = (((size_t)ph * p.hkv + kvh) * kPage + (t % kPage)) * D + cg * EPL;
-            if constexpr (BF16) {
-                const uint4 raw = *(const uint4 *)((const uint16_t *)p.k + off);
-                const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+            float x[EPL];
+            load16_as_f32<KT>(p.k, off, x);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = bf16_to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1))));
-                    mn[e] = fminf(mn[e], x);
-                    mx[e] = fmaxf(mx[e], x);
-                }
-            } else {
-                const float4 raw = *(const float4 *)((const float *)p.k + off);
-                const float x[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    mn[e] = fminf(mn[e], x[e]);
-                    mx[e] = fmaxf(mx[e], x[e]);
-                }
+            for (int e = 0; e < EPL; ++e) {
+                mn[e] = fminf(mn[e], x[e]);
+                mx[e] = fmaxf(mx[e], x[e]);
             }
         }
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
             const int ch = cg * EPL + e;
             const size_t row = (((size_t)u * D + ch) * 2) * p.stride;
-            if constexpr (BF16) {
+            if constexpr (KT != kKtF32) {
                 uint16_t *m16 = (uint16_t *)p.meta;
                 m16[row + blk] = (uint16_t)(__float_as_uint(mn[e]) >> 16);
                 m16[row + p.stride + blk] = (uint16_t)(__float_as_uint(mx[e]) >> 16);
@@ -85,9 +108,9 @@ __global__ __launch_bounds__(256) void meta_kernel(MetaParams p) {
 // Mean-pooled block summary: the channel-wise mean key of every block over its valid tokens, summed in
 // float64 in token order, divided by the token count and rounded once to float32.  Layout [B][Hkv][d]
 // [stride] fp32.  Lane = block (64 per workgroup), waves take channel groups.
-template <bool BF16, int D>
+template <int KT, int D>
 __global__ __launch_bounds__(256) void mean_meta_kernel(MetaParams p) {
-    constexpr int EPL = BF16 ? 8 : 4;          // channels per 16-byte load
+    constexpr int EPL = kElemsPer16B<KT>;   // channels per 16-byte load
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int u = blockIdx.y;
     const int b = u / p.hkv, kvh = u - b * p.hkv;
@@ -105,18 +128,10 @@ __global__ __launch_bounds__(256) void mean_meta_kernel(MetaParams p) {
             int ph = p.page_table[(size_t)b * p.max_pages + t / kPage];
             ph = min(max(ph, 0), p.num_pages - 1);
             const size_t off = (((size_t)ph * p.hkv + kvh) * kPage + (t % kPage)) * D + cg * EPL;
-            if constexpr (BF16) {
-                const uint4 raw = *(const uint4 *)((const uint16_t *)p.k + off);
-                const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+            float x[EPL];
+            load16_as_f32<KT>(p.k, off, x);
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    acc[e] = dadd(acc[e], (double)bf16_to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1)))));
-            } else {
-                const float4 raw = *(const float4 *)((const float *)p.k + off);
-                const float x[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = dadd(acc[e], (double)x[e]);
-            }
+            for (int e = 0; e < EPL; ++e) acc[e] = dadd(acc[e], (double)x[e]);
         }
         const double n = (double)(t1 - t0);
         float *m32 = (float *)p.meta;
@@ -190,21 +205,16 @@ hipError_t launch_meta(const KvDesc &kv, int block, int stride, void *meta, bool
     p.stride = stride;
     p.nmax = (int)((long)kv.max_pages * kPage / block);
     const dim3 grid((p.nmax + 63) / 64, kv.batch * kv.hkv);
-    if (mean) {
-        if (kv.bf16) {
-            if (kv.d == 128) mean_meta_kernel<true, 128><<<grid, 256, 0, stream>>>(p);
-            else mean_meta_kernel<true, 64><<<grid, 256, 0, stream>>>(p);
-        } else {
-            if (kv.d == 128) mean_meta_kernel<false, 128><<<grid, 256, 0, stream>>>(p);
-            else mean_meta_kernel<false, 64><<<grid, 256, 0, stream>>>(p);
-        }
-    } else if (kv.bf16) {
-        if (kv.d == 128) meta_kernel<true, 128><<<grid, 256, 0, stream>>>(p);
-        else meta_kernel<true, 64><<<grid, 256, 0, stream>>>(p);
-    } else {
-        if (kv.d == 128) meta_kernel<false, 128><<<grid, 256, 0, stream>>>(p);
-        else meta_kernel<false, 64><<<grid, 256, 0, stream>>>(p);
-    }
+    const int kt = kv.fp8 ? kKtFp8 : kv.bf16 ? kKtBf16 : kKtF32;
+#define PRR_META(KT, DD)                                                                             \
+    if (kt == KT && kv.d == DD) {                                                                    \
+        if (mean) mean_meta_kernel<KT, DD><<<grid, 256, 0, stream>>>(p);                             \
+        else meta_kernel<KT, DD><<<grid, 256, 0, stream>>>(p);                                       \
+    } else
+    PRR_META(kKtF32, 128) PRR_META(kKtF32, 64) PRR_META(kKtBf16, 128) PRR_META(kKtBf16, 64)
+    PRR_META(kKtFp8, 128) PRR_META(kKtFp8, 64)
+    { return hipErrorInvalidValue; }
+#undef PRR_META
     return hipGetLastError();
 }
 
@@ -224,18 +234,19 @@ hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *me
     sp.block = block;
     sp.stride = stride;
     sp.nmax = nmax;
-    const int bpw = 256 * (mean ? kScoreBPL<true, true> : kv.bf16 ? kScoreBPL<true> : kScoreBPL<false>);
+    const bool bq = kv.bf16 || kv.fp8;   // bf16 queries (and bf16 min/max metadata)
+    const int bpw = 256 * (mean ? kScoreBPL<true, true> : bq ? kScoreBPL<true> : kScoreBPL<false>);
     const dim3 sgrid((nmax + bpw - 1) / bpw, units);
     if (mean) {
         // the fp32 block means do not depend on the cache dtype beyond q's
-        if (kv.bf16) {
+        if (bq) {
             if (kv.d == 128) score_kernel<true, 128, true><<<sgrid, 256, 0, stream>>>(sp);
             else score_kernel<true, 64, true><<<sgrid, 256, 0, stream>>>(sp);
         } else {
             if (kv.d == 128) score_kernel<false, 128, true><<<sgrid, 256, 0, stream>>>(sp);
             else score_kernel<false, 64, true><<<sgrid, 256, 0, stream>>>(sp);
         }
-    } else if (kv.bf16) {
+    } else if (bq) {
         if (kv.d == 128) score_kernel<true, 128, false><<<sgrid, 256, 0, stream>>>(sp);
         else score_kernel<true, 64, false><<<sgrid, 256, 0, stream>>>(sp);
     } else {

@@ -1,0 +1,247 @@
+// step_core.hpp - selection and the speculative pass over P as one launch (gfx950).
+//
+// Citations:
+//   [paper] "Predict, Reuse, and Repair: Accelerating Dynamic Sparse Attention for Long-Context LLM
+//           Decoding" (full paper text)
+//
+// The method overlaps the speculative pass over the predicted set P with selection ([paper] §1 and the
+// Figure 1 flow, §3): the two only read P and are independent.  On this GPU a dependency between two
+// streams costs about 10 us from the producer's end to the consumer's start, while kernels on one
+// stream follow each other about 1 us apart, so the overlap is made inside one grid instead: the first
+// workgroups score blocks (one workgroup per 512 blocks of a unit with min/max metadata, per 256 with
+// block means), the rest run the speculative chunks
+// (the attention kernels' chunk walk over n_spec workgroups).  Dispatch follows the workgroup index, so
+// the scoring workgroups issue their loads first: the memory system serves them ahead of the
+// speculative stream, selection finishes early and its top-K runs under the speculative pass, which is
+// the longer of the two.  At 128K, batch 8 the grid is 256 scoring + 256 speculative workgroups: all of
+// them resident at once (two per CU).
+//
+// Top-K (with M = A \ P).  The last scoring workgroup of a unit to finish (a device-scope arrival
+// counter; nobody waits) runs the unit's top-K with the same 256 threads, so the top-K of most units
+// overlaps the speculative pass:
+//   * up to 2048 blocks per unit, over all of the unit's scores (up to 8 per thread), stored and re-read
+//     with device-scope accesses, which are coherent across the XCDs' L2s;
+//   * beyond that, in two stages: every scoring workgroup first keeps the local top-min(K, 512) of its
+//     own 512 blocks as candidates, and the last one ranks the candidates of all workgroups of the unit
+//     (up to 16 per thread; the selection is exact, see select_core.hpp);
+// otherwise (more candidates than that) the separate top-K kernel follows the launch.
+//
+// Predictor step of another layer.  In a stack of layers the predictor of layer l needs only layer l's
+// scores and is off the critical path ([paper] §1, §4.1), so layer l + 1's launch can carry it.  The
+// scoring workgroups take its units from a work counter once their own scoring is done (and the top-K,
+// for a unit's last arriver): the ones that finish first take most of them, the speculative pass keeps
+// every slot it had (extra workgroups at the end of the grid would wait for a free slot and run past
+// it), and the top-K is not delayed.  The two touch disjoint buffers.
+
+#pragma once
+
+#include "select_core.hpp"
+#include "attn_core.hpp"
+
+namespace prr {
+namespace {
+
+// Workgroup s < nsx * units scores blocks [BPW (s mod nsx), +BPW) of unit s / nsx (BPW = 512 blocks for
+// bf16 min/max metadata, 256 for fp32 block means: MEAN) and, if it is the unit's last to finish and
+// KPT > 0, runs the unit's top-K (KPT keys per thread, 256 KPT >= the unit's block count); the remaining
+// n_spec workgroups run the speculative pass.  PRED: the scoring workgroups then draw the n_pred units
+// of another layer's predictor step from *pred_ctr (8 keys per thread: rows of up to 2048 blocks); every
+// workgroup draws until it gets an index >= n_pred, so the launch makes exactly n_pred + n_score draws
+// and the one that draws the last index resets the counter for the next launch.  Register use is the
+// attention part's (two waves per SIMD).
+struct CandParams {
+    uint64_t *key;   // [units][nsx][kl]
+    int32_t *idx;    // [units][nsx][kl]
+    int32_t *cnt;    // [units][nsx]
+    int kl;
+};
+
+template <int KT, int D, int KPT, bool TWO, bool MEAN, bool PRED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void select_spec_kernel(
+    AttnParams ap, ScoreParams sp, TopkParams tp, CandParams cp, PredictParams pp, uint32_t *arrivals,
+    uint32_t *pred_ctr, int n_score, int nsx, int n_spec, int n_pred) {
+    if ((int)blockIdx.x >= n_score) {
+        attn_body<KT, D, false>(ap, (int)blockIdx.x - n_score, n_spec);
+        return;
+    }
+    const int s = (int)blockIdx.x;
+    const int u = s / nsx;
+    const int bx = s - u * nsx;
+    constexpr int BPL = kScoreBPL<true, MEAN>;
+    double kept[BPL] = {};
+    score_body<true, D, KPT != 0 && !TWO, MEAN>(sp, bx, u, kept);
+    if constexpr (TWO) {
+        __shared__ TopkSmem<4> sm;
+        constexpr int BPW = 256 * BPL;   // blocks per scoring workgroup
+        const int b = u / sp.hkv;
+        const int nb = min((max(sp.seq_len[b], 0) + sp.block - 1) / sp.block, sp.nmax);
+        const int n_local = min(max(nb - bx * BPW, 0), BPW);
+        const size_t part = (size_t)u * nsx + bx;
+        local_candidates<BPL>(kept, n_local, cp.kl, bx * BPW, cp.key + part * cp.kl, cp.idx + part * cp.kl,
+                              cp.cnt + part, sm);
+    }
+    if constexpr (KPT != 0) {
+        __shared__ int s_last;
+        // this workgroup's score stores are complete before its arrival is counted
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t prev = __hip_atomic_fetch_add(&arrivals[u], 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            s_last = prev == (uint32_t)(nsx - 1);
+            if (s_last) __hip_atomic_store(&arrivals[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (s_last) {
+            if constexpr (TWO)
+                topk_candidates_body<KPT>(tp, u, cp.key + (size_t)u * nsx * cp.kl, cp.idx + (size_t)u * nsx * cp.kl,
+                                          cp.cnt + (size_t)u * nsx, nsx, cp.kl);
+            else
+                topk_body<KPT, 256, true>(tp, u);
+        }
+    }
+    if constexpr (PRED) {
+        __shared__ int s_j;
+        for (;;) {
+            __syncthreads();   // the workgroup's shared scratch is free again, s_j read by every thread
+            if (threadIdx.x == 0) {
+                const uint32_t j = __hip_atomic_fetch_add(pred_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (j == (uint32_t)(n_pred + n_score - 1))
+                    __hip_atomic_store(pred_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_j = (int)j;
+            }
+            __syncthreads();
+            const int j = s_j;
+            if (j >= n_pred) break;
+            predict_body<8, 256>(pp, j);
+        }
+    }
+}
+
+}  // namespace
+
+// Blocks per scoring workgroup of the fused launch (bf16 queries): 512 for min/max metadata, 512 for
+// block means (two per lane either way).
+inline int select_spec_score_bpw(bool mean) {
+    return 256 * (mean ? kScoreBPL<true, true> : kScoreBPL<true, false>);
+}
+
+// The fused launch for caches of element type KT (bf16 or fp8; an f32 cache runs the passes in turn).
+template <int KT>
+hipError_t launch_select_spec_t(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,
+                              int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
+                              double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
+                              int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m,
+                              void *ws, bool mean, const PredictArgs *pred, hipStream_t stream) {
+    auto predict_alone = [&]() -> hipError_t {
+        if (!pred) return hipSuccess;
+        return launch_predict(pred->scores, pred->seq_len, pred->batch, pred->hkv, pred->block, pred->nmax,
+                              pred->alpha, pred->beta, pred->gamma, pred->budget, pred->level, pred->trend,
+                              pred->live, pred->p_idx, pred->p_cnt, pred->p_cap, stream);
+    };
+    if constexpr (KT == kKtF32) {
+        // fp32 caches (exact-input checks): the passes one after the other
+        hipError_t e = launch_select(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_cap, scores,
+                                     a_idx, a_cnt, a_cap, m_idx, m_cnt, m_cap, mean, stream);
+        if (e != hipSuccess) return e;
+        e = launch_attn(kv, q, hq, block, p_idx, p_cnt, p_cap, scale, acc, l, m, nullptr, false, ws, stream);
+        if (e != hipSuccess) return e;
+        return predict_alone();
+    } else {
+    AttnParams ap;
+    const int n_spec = attn_setup(ap, kv, q, hq, block, p_idx, p_cnt, p_cap, scale, acc, l, m, nullptr, false, ws);
+    ScoreParams sp;
+    sp.q = q;
+    sp.meta = meta;
+    sp.seq_len = kv.seq_len;
+    sp.scores = scores;
+    sp.hq = hq;
+    sp.hkv = kv.hkv;
+    sp.G = hq / kv.hkv;
+    sp.block = block;
+    sp.stride = stride;
+    sp.nmax = nmax;
+    TopkParams tp;
+    tp.scores = scores;
+    tp.seq_len = kv.seq_len;
+    tp.p_idx = p_idx;
+    tp.p_cnt = p_cnt;
+    tp.a_idx = a_idx;
+    tp.a_cnt = a_cnt;
+    tp.m_idx = m_idx;
+    tp.m_cnt = m_cnt;
+    tp.hkv = kv.hkv;
+    tp.block = block;
+    tp.nmax = nmax;
+    tp.topk = topk;
+    tp.p_cap = p_cap;
+    tp.a_cap = a_cap;
+    tp.m_cap = m_cap;
+    const int units = kv.batch * kv.hkv;
+    uint32_t *arrivals = (uint32_t *)ws + units;   // the scoring-arrival counters of the workspace
+    const int bpw = select_spec_score_bpw(mean);
+    const int nsx = (nmax + bpw - 1) / bpw;
+    const bool fuse_pred = pred && pred->nmax <= kMaxFusedPredictN;
+    PredictParams pp = {};
+    int n_pred = 0;
+    if (fuse_pred) {
+        pp.scores = pred->scores;
+        pp.seq_len = pred->seq_len;
+        pp.level = pred->level;
+        pp.trend = pred->trend;
+        pp.live = pred->live;
+        pp.p_idx = pred->p_idx;
+        pp.p_cnt = pred->p_cnt;
+        pp.hkv = pred->hkv;
+        pp.block = pred->block;
+        pp.nmax = pred->nmax;
+        pp.budget = pred->budget;
+        pp.p_cap = pred->p_cap;
+        pp.alpha = pred->alpha;
+        pp.beta = pred->beta;
+        pp.gamma = pred->gamma;
+        n_pred = pred->batch * pred->hkv;
+    }
+    const long grid = (long)n_spec + (long)nsx * units;
+    uint32_t *pred_ctr =
+        (uint32_t *)((char *)ws + pred_counter_offset(kv.batch, hq, kv.hkv, kv.d, block, p_cap, nmax, topk));
+    if (grid > 0x7fffffffL) return hipErrorInvalidValue;
+    const SelectSpecPlan plan = select_spec_plan(nmax, topk, mean);
+    CandParams cp;
+    cp.kl = plan.kl;
+    char *cbase = (char *)ws + attn_workspace_bytes(kv.batch, hq, kv.hkv, kv.d, block, p_cap);
+    cp.key = (uint64_t *)cbase;
+    cp.idx = (int32_t *)(cbase + (size_t)units * nsx * plan.kl * 8);
+    cp.cnt = (int32_t *)(cbase + (size_t)units * nsx * plan.kl * 12);
+    const int kpt = plan.kpt;
+    const bool two = plan.two;
+#define PRR_SS(DD, K, T, MN, PR)                                                                           \
+    if (kv.d == DD && kpt == K && two == T && mean == MN && fuse_pred == PR) {                              \
+        select_spec_kernel<KT, DD, K, T, MN, PR><<<(int)grid, 256, 0, stream>>>(ap, sp, tp, cp, pp, arrivals,      \
+                                                                            pred_ctr, nsx * units, nsx, n_spec, \
+                                                                            n_pred);                        \
+    } else
+#define PRR_SS_K(DD, MN, PR)                                                                                \
+    PRR_SS(DD, 0, false, MN, PR) PRR_SS(DD, 1, false, MN, PR) PRR_SS(DD, 2, false, MN, PR)                    \
+    PRR_SS(DD, 4, false, MN, PR) PRR_SS(DD, 8, false, MN, PR) PRR_SS(DD, 1, true, MN, PR)                     \
+    PRR_SS(DD, 2, true, MN, PR) PRR_SS(DD, 4, true, MN, PR) PRR_SS(DD, 8, true, MN, PR)                       \
+    PRR_SS(DD, 16, true, MN, PR)
+#define PRR_SS_ALL(MN, PR) PRR_SS_K(128, MN, PR) PRR_SS_K(64, MN, PR)
+    PRR_SS_ALL(false, false) PRR_SS_ALL(true, false) PRR_SS_ALL(false, true) PRR_SS_ALL(true, true)
+    { return hipErrorInvalidValue; }
+#undef PRR_SS_ALL
+#undef PRR_SS_K
+#undef PRR_SS
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (kpt == 0) {
+        e = launch_topk(kv, block, nmax, topk, scores, p_idx, p_cnt, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt,
+                        m_cap, stream);
+        if (e != hipSuccess) return e;
+    }
+    return fuse_pred ? hipSuccess : predict_alone();
+    }
+}
+
+
+}  // namespace prr

@@ -48,7 +48,7 @@ class Workload:
     context: int              # tokens per sequence (all sequences unless seq_lens is given)
     block: int                # selection block size S in tokens (multiple of PAGE_SIZE)
     topk: int                 # budget K in blocks
-    dtype: str                # "f32" or "bf16" (q, K and V share it)
+    dtype: str                # "f32" or "bf16" (q, K and V share it), or "fp8" (E4M3 K and V, bf16 q)
     seed: int
     steps: int = 1            # decode steps with distinct queries
     shuffle_pages: bool = True
@@ -105,13 +105,19 @@ class Workload:
 
     @property
     def torch_dtype(self):
-        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+        """dtype of the K/V cache."""
+        return {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[self.dtype]
+
+    @property
+    def q_torch_dtype(self):
+        """dtype of the queries (an fp8 cache is queried in bf16)."""
+        return torch.bfloat16 if self.dtype == "fp8" else self.torch_dtype
 
     def blocks_of(self, b: int) -> int:
         return -(-self.lengths[b] // self.block)
 
     def kv_bytes_per_token(self) -> int:
-        return 2 * self.head_dim * (4 if self.dtype == "f32" else 2)
+        return 2 * self.head_dim * {"f32": 4, "bf16": 2, "fp8": 1}[self.dtype]
 
 
 # The five configurations of the hot path (tiny parity case, Llama-3-8B layer, 128K x 64 steps,
@@ -187,7 +193,7 @@ def make_queries(w: Workload, device="cpu") -> torch.Tensor:
             qs.append(mu + x)
             x = w.drift_rho * x + innov * torch.randn(shape, generator=g, device=device)
         q = torch.stack(qs)
-    return q.to(w.torch_dtype)
+    return q.to(w.q_torch_dtype)
 
 
 def _block_pages(w: Workload, page_table: torch.Tensor, b: int, blocks: torch.Tensor) -> torch.Tensor:
@@ -229,11 +235,11 @@ def make_inputs(w: Workload, device="cpu") -> Inputs:
                 u = u / torch.linalg.vector_norm(u)
                 pages = _block_pages(w, page_table, b, torch.from_numpy(ids).to(device))
                 k[pages.reshape(-1), h] += w.plant_gain * u
-    k_cache = k.to(w.torch_dtype)
+    k_cache = to_cache_dtype(k, w)
     del k
     gv = _gen(w, _V, device)
-    v_cache = torch.randn((w.num_pages, w.num_kv_heads, w.head_dim, PAGE_SIZE), generator=gv,
-                          device=device, dtype=torch.float32).to(w.torch_dtype)
+    v_cache = to_cache_dtype(torch.randn((w.num_pages, w.num_kv_heads, w.head_dim, PAGE_SIZE), generator=gv,
+                                         device=device, dtype=torch.float32), w)
     return Inputs(w, q, k_cache, v_cache, page_table, seq_len, planted)
 
 
@@ -243,7 +249,14 @@ def make_append_tokens(w: Workload, device="cpu"):
     shape = (w.append_tokens, w.batch, w.num_kv_heads, w.head_dim)
     k = torch.randn(shape, generator=_gen(w, _APPK, device), device=device, dtype=torch.float32)
     v = torch.randn(shape, generator=_gen(w, _APPV, device), device=device, dtype=torch.float32)
-    return k.to(w.torch_dtype), v.to(w.torch_dtype)
+    return to_cache_dtype(k, w), to_cache_dtype(v, w)
+
+
+def to_cache_dtype(x: torch.Tensor, w: Workload) -> torch.Tensor:
+    """Round generated fp32 values to the cache dtype (fp8: clamped to E4M3's finite range first)."""
+    if w.dtype == "fp8":
+        x = x.clamp(-448.0, 448.0)
+    return x.to(w.torch_dtype)
 
 
 def make_spec_set(w: Workload, selected: np.ndarray, n_blocks: int, n_hit: int, n_miss: int,
@@ -292,8 +305,11 @@ def ragged_lengths(w: Workload, lo: int, hi: int, salt: int = 0) -> list:
 # ---- host views used by both sides (layout decoding only, no arithmetic of the method) ----
 
 def to_numpy_bits(t: torch.Tensor) -> np.ndarray:
-    """Host copy; bf16 tensors come back as their raw uint16 bit patterns."""
+    """Host copy; bf16 tensors come back as their raw uint16 bit patterns, fp8 tensors as their uint8
+    codes."""
     t = t.detach().cpu().contiguous()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
     return t.numpy()

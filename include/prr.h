@@ -43,7 +43,11 @@ typedef enum prr_status {
     PRR_EHIP = 4          /* a HIP launch or runtime call failed */
 } prr_status;
 
-typedef enum prr_dtype { PRR_F32 = 0, PRR_BF16 = 1 } prr_dtype;
+/* Cache element types.  PRR_FP8: k and v hold 8-bit E4M3 codes (the OCP 8-bit floating-point format,
+ * FN variant: bias 7, subnormals, no infinities; the NaN codes 0x7F / 0xFF must not occur), one byte per
+ * element; queries and min/max metadata are bf16 (every finite E4M3 value is a bf16 value, so keys and
+ * values enter the bf16 products exactly).  Low-bit KV is the pages' future work ([paper] Limitations). */
+typedef enum prr_dtype { PRR_F32 = 0, PRR_BF16 = 1, PRR_FP8 = 2 } prr_dtype;
 
 /* How selection scores a block ([paper] §2.1: each block is compressed to a representative scored
  * against the query):
@@ -58,7 +62,7 @@ typedef enum prr_score_mode { PRR_SCORE_QUEST = 0, PRR_SCORE_MEAN = 1 } prr_scor
  *   v: [num_pages][num_kv_heads][head_dim][page_size]  (channel-major tile)
  * page_table[b][j] is the physical page holding tokens [16 j, 16 j + 16) of sequence b; seq_len[b] is
  * the number of valid tokens.  head_dim must be 64 or 128.  q (where an entry point takes it) has the
- * same dtype as k and v, layout [batch][num_q_heads][head_dim]. */
+ * same dtype as k and v (bf16 for an fp8 cache), layout [batch][num_q_heads][head_dim]. */
 typedef struct prr_kv_cache {
     const void *k;              /* device */
     const void *v;              /* device */
@@ -117,7 +121,7 @@ prr_status prr_workspace_clear(void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Block metadata for Quest selection ([paper] A.1: channel-wise min and max keys m_p, M_p of every
  * block, stored per kv head).  meta layout: [batch][num_kv_heads][head_dim][2][stride] in the cache
- * dtype, row 0 = min, row 1 = max, column p = block p (stride = prr_meta_stride).  Blocks at or beyond
+ * dtype (bf16 for an fp8 cache: exact), row 0 = min, row 1 = max, column p = block p (stride = prr_meta_stride).  Blocks at or beyond
  * ceil(seq_len / block) are not written.  A partial last block uses its valid tokens only.
  * block must be a positive multiple of page_size.  Reads all of K once; not part of the per-step path. */
 prr_status prr_build_meta(const prr_kv_cache *kv, int32_t block, void *meta, hipStream_t stream);
@@ -140,7 +144,7 @@ prr_status prr_build_mean_meta(const prr_kv_cache *kv, int32_t block, float *met
  * a rebuild by prr_build_meta over the block's valid tokens; with mode PRR_SCORE_MEAN, meta holds block
  * means and the block's mean is recomputed as prr_build_mean_meta does), then sets seq_len[b] = t + 1.  A sequence
  * whose cache is full (or whose page-table entry is out of range) is left untouched.
- * k_new, v_new: [batch][num_kv_heads][head_dim] in the cache dtype, device.  seq_len must be kv->seq_len
+ * k_new, v_new: [batch][num_kv_heads][head_dim] in the cache dtype (E4M3 codes for fp8), device.  seq_len must be kv->seq_len
  * (written in place); kv->k and kv->v are written.  meta as for prr_build_meta. */
 prr_status prr_append(const prr_kv_cache *kv, int32_t block, const void *k_new, const void *v_new, void *meta,
                       prr_score_mode mode, int32_t *seq_len, hipStream_t stream);
@@ -154,7 +158,7 @@ prr_status prr_append(const prr_kv_cache *kv, int32_t block, const void *k_new, 
  * With mode PRR_SCORE_MEAN, meta holds block means (prr_build_mean_meta) and scores[b][kvh][p] =
  * sum_i qbar_i mean_{p,i}, with the same qbar, order and precision.
  * P may be NULL (then M must be NULL).  A->cap and M->cap must be >= topk.  N_b must not exceed
- * 32768.  q: [batch][num_q_heads][head_dim], device, dtype of the cache. */
+ * 32768.  q: [batch][num_q_heads][head_dim], device, dtype of the cache (bf16 for fp8). */
 prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
                       prr_score_mode mode, int32_t block, int32_t topk, const prr_block_set *P, double *scores,
                       prr_block_set *A, prr_block_set *M, hipStream_t stream);

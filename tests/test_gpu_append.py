@@ -44,6 +44,7 @@ APPEND_CASES = [
     ("bf16_d128_s32", 2, 8, 2, 128, 32, [1000, 1023], "bf16", 70),
     ("bf16_d64_s64", 2, 4, 1, 64, 64, [640, 17], "bf16", 50),
     ("f32_d64_s16", 1, 4, 1, 64, 16, [500], "f32", 40),
+    ("fp8_d128_s32", 2, 8, 2, 128, 32, [700, 1023], "fp8", 45),
 ]
 
 
@@ -64,10 +65,9 @@ def test_append_matches_definition_and_rebuild(case, mode):
         _expected_append(k_host, v_host, pt, sl, kn[t].cpu(), vn[t].cpu())
     torch.cuda.synchronize()
     assert torch.equal(inp.seq_len.cpu(), sl)
-    assert torch.equal(inp.k_cache.cpu().view(torch.int16 if dt == "bf16" else torch.int32),
-                       k_host.view(torch.int16 if dt == "bf16" else torch.int32))
-    assert torch.equal(inp.v_cache.cpu().view(torch.int16 if dt == "bf16" else torch.int32),
-                       v_host.view(torch.int16 if dt == "bf16" else torch.int32))
+    bits = {"bf16": torch.int16, "f32": torch.int32, "fp8": torch.uint8}[dt]
+    assert torch.equal(inp.k_cache.cpu().view(bits), k_host.view(bits))
+    assert torch.equal(inp.v_cache.cpu().view(bits), v_host.view(bits))
     # the incrementally kept metadata equals a rebuild, bit for bit, on every existing block
     rebuilt = build(dkv, S)
     gm = wl.to_numpy_bits(meta)
@@ -113,14 +113,15 @@ def test_append_to_a_full_cache_changes_nothing(mode):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("mode", ["quest", "mean"])
-def test_decode_trajectory_with_appends(mode):
+def test_decode_trajectory_with_appends(mode, dtype):
     """Every step appends one token per sequence, then runs the one-stream layer step.  Per unit and
     step: scores, A, M, the predictor state and P^{t+1} bit for bit, the repaired state and output within
     tolerance, all against the oracle on the host copy of the grown cache.  Sequence 1 starts a new
     block mid-run.  Both block summaries: Quest's min/max bound and the mean key."""
     steps = 6
-    w = wl.Workload("append_traj", 2, 8, 2, 128, 2000, 32, 8, "bf16", seed=31, steps=steps,
+    w = wl.Workload("append_traj", 2, 8, 2, 128, 2000, 32, 8, dtype, seed=31, steps=steps,
                     seq_lens=[2000, 1950], drift_rho=0.9, query_mean_gain=0.64, block_centre_std=0.35,
                     append_tokens=steps)
     inp = wl.make_inputs(w, "cuda")

@@ -30,6 +30,7 @@ CASES = [
     # 2500 blocks: the fused launch ranks per-workgroup candidates (two-stage top-K), K above the 256
     # blocks of one scoring workgroup
     ("bf16_d128_s16_two_stage", 1, 8, 2, 128, 16, [40000], "bf16", 300, None),
+    ("fp8_d128_s32", 2, 8, 2, 128, 32, [9000, 4100], "fp8", 32, None),
 ]
 
 

@@ -85,6 +85,9 @@ CASES = [
     ("bf16_d128_g16_s32", 1, 16, 1, 128, 32, [900], "bf16"),
     ("bf16_d128_g1_s16", 1, 4, 4, 128, 16, [333], "bf16"),
     ("bf16_d128_g2_s48", 2, 4, 2, 128, 48, [960, 97], "bf16"),
+    ("fp8_d128_g4_s16", 2, 8, 2, 128, 16, [1000, 611], "fp8"),
+    ("fp8_d64_g8_s32", 1, 16, 2, 64, 32, [1777], "fp8"),
+    ("fp8_d128_g2_s64", 2, 4, 2, 128, 64, [2048, 97], "fp8"),
     ("f32_d64_g4_s16", 2, 8, 2, 64, 16, [515, 1024], "f32"),
     ("f32_d128_g2_s32", 1, 4, 2, 128, 32, [700], "f32"),
 ]
