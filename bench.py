@@ -61,6 +61,8 @@ def parse_args():
                     help="also time a stack of this many layers (own caches and predictor state each) with each "
                          "layer's predictor carried by the next layer's launch, against the same layers run "
                          "with the predictor on its own")
+    ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default=None,
+                    help="cache element type (default: the workload's, bf16); fp8 = E4M3 K/V with bf16 queries")
     ap.add_argument("--score-mode", choices=("quest", "mean"), default="quest",
                     help="block summary selection scores: Quest's min/max bound or the block's mean key")
     ap.add_argument("--append", action="store_true",
@@ -313,7 +315,7 @@ def main():
     K = args.steps
     base = wl.CONFIGS[args.config]
     w = wl.scaled(base, steps=max(base.steps, args.warmup + 1, K + 1),
-                  append_tokens=(K + 1) if args.append else 0)
+                  append_tokens=(K + 1) if args.append else 0, dtype=args.kv_dtype or base.dtype)
     log(f"[bench] generating {w.name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} "
         f"T={w.context} S={w.block} K={w.topk} steps={w.steps}")
     t_gen = time.time()
@@ -508,7 +510,8 @@ def main():
     achieved = spec_launch_bytes / (spec_launch_us * 1e-6) / 1e9
     # the committed counters were taken on the default run (Quest scoring, no appends)
     traffic = (load_traffic(kernel_hash)
-               if (w.name == PROFILE_WORKLOAD and not args.append and args.score_mode == "quest") else None)
+               if (w.name == PROFILE_WORKLOAD and not args.append and args.score_mode == "quest"
+                   and w.dtype == "bf16") else None)
 
     med = lambda xs: round(float(statistics.median(xs)), 2)
     result = {
@@ -522,12 +525,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "context": w.context, "block": w.block, "topk_blocks": w.topk,
                    "spec_budget_blocks": w.topk, "ema": list(w.ema), "decode_steps_timed": K,
-                   "score_mode": args.score_mode,
+                   "score_mode": args.score_mode, "kv_dtype": w.dtype,
                    "parallelism": "none (1 GPU)", "flush_mib_read_between_kernels": args.flush_mib},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "value_median_step_gbps": round(float(statistics.median(step_gbps)), 1),
@@ -566,7 +569,7 @@ def main():
         "hit_rate": round(float(np.mean(hits)), 4),
         "ms_per_step_note": "wall time per timed step of the first pass: one layer step + isolated empty pair, "
                             "spec, repair, select, predict and select_spec, each after a 1 GiB cache flush",
-        "roofline": {"bound": "hbm", "kernel": "attn_spec_bf16<128>",
+        "roofline": {"bound": "hbm", "kernel": f"attn_spec_{w.dtype}<{w.head_dim}>",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": spec_launch_bytes,
