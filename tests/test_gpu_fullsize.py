@@ -145,6 +145,11 @@ def test_ctx128k_batch8_trajectory():
     _trajectory(wl.C3, 4, [(0, 0), (3, 5), (5, 2), (7, 7)], wl.C3.ema)
 
 
+def test_ctx128k_batch8_fp8_trajectory():
+    """The same workload with an fp8 (E4M3) cache, as `bench.py --kv-dtype fp8` runs it."""
+    _trajectory(wl.scaled(wl.C3, dtype="fp8"), 3, [(1, 1), (6, 4)], wl.C3.ema)
+
+
 def test_ctx512k_paged_selection_and_repair():
     w = wl.C4
     inp = wl.make_inputs(w, "cuda")
