@@ -29,6 +29,7 @@ SOURCES = {
     "step.hip": [],
     "step_fp8.hip": [],
     "append.hip": [],
+    "check.hip": [],
     "prr_api.cpp": ["-x", "hip"],
 }
 

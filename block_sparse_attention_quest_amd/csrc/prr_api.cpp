@@ -60,6 +60,15 @@ prr::KvDesc desc(const prr_kv_cache *kv) {
 
 prr_status hip_status(hipError_t e) { return e == hipSuccess ? PRR_OK : PRR_EHIP; }
 
+// Checking mode: an input set's device-side preconditions (entries in range, no repeats).
+prr_status check_input_set(const prr_kv_cache *kv, int32_t block, const prr_block_set *s, hipStream_t stream) {
+    if (!s || !prr::checks_enabled()) return PRR_OK;
+    int violation = 0;
+    const hipError_t e = prr::check_sets(desc(kv), block, s->idx, s->count, s->cap, stream, &violation);
+    if (e != hipSuccess) return PRR_EHIP;
+    return violation ? PRR_EINVAL : PRR_OK;
+}
+
 #define PRR_TRY(x)                      \
     do {                                \
         const prr_status s_ = (x);      \
@@ -162,6 +171,7 @@ prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv
     }
     const int nmax = prr_max_blocks(kv, block);
     if (nmax > prr::kMaxSelectN) return PRR_EUNSUPPORTED;
+    PRR_TRY(check_input_set(kv, block, P, stream));
     return hip_status(prr::launch_select(desc(kv), q, num_q_heads, meta, block, prr_meta_stride(kv, block),
                                          nmax, topk, P ? P->idx : nullptr, P ? P->count : nullptr,
                                          P ? P->cap : 0, scores, A->idx, A->count, A->cap,
@@ -238,6 +248,7 @@ prr_status prr_select_spec_predict(const void *q, int32_t num_q_heads, const prr
         pa.p_cnt = pred->P_next->count;
         pa.p_cap = pred->P_next->cap;
     }
+    PRR_TRY(check_input_set(kv, block, P, stream));
     return hip_status(prr::launch_select_spec(desc(kv), q, num_q_heads, meta, block, prr_meta_stride(kv, block),
                                               nmax, topk, P->idx, P->count, P->cap, scores, A->idx, A->count,
                                               A->cap, M->idx, M->count, M->cap, scale, out->acc, out->l, out->m,
@@ -268,6 +279,7 @@ prr_status prr_spec_attn(const void *q, int32_t num_q_heads, const prr_kv_cache 
                          size_t ws_bytes, hipStream_t stream) {
     PRR_TRY(attn_common(q, num_q_heads, kv, block, P, ws, ws_bytes));
     if (!out || !out->acc || !out->l || !out->m) return PRR_EINVAL;
+    PRR_TRY(check_input_set(kv, block, P, stream));
     return hip_status(prr::launch_attn(desc(kv), q, num_q_heads, block, P->idx, P->count, P->cap, scale,
                                        out->acc, out->l, out->m, nullptr, false, ws, stream));
 }
@@ -277,6 +289,7 @@ prr_status prr_repair(const void *q, int32_t num_q_heads, const prr_kv_cache *kv
                       void *ws, size_t ws_bytes, hipStream_t stream) {
     PRR_TRY(attn_common(q, num_q_heads, kv, block, M, ws, ws_bytes));
     if (!state || !state->acc || !state->l || !state->m) return PRR_EINVAL;
+    PRR_TRY(check_input_set(kv, block, M, stream));
     return hip_status(prr::launch_attn(desc(kv), q, num_q_heads, block, M->idx, M->count, M->cap, scale,
                                        state->acc, state->l, state->m, out, true, ws, stream));
 }

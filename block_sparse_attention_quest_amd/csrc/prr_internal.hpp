@@ -32,6 +32,12 @@ hipError_t launch_attn(const KvDesc &kv, const void *q, int hq, int block, const
 
 hipError_t launch_clear(void *ws, size_t bytes, hipStream_t stream);
 
+// Checking mode (PRR_CHECK=1 in the environment): validates a block set on the stream and waits for the
+// result; *violation gets a bit mask (1 count outside [0, cap], 2 entry out of range, 4 repeated entry).
+bool checks_enabled();
+hipError_t check_sets(const KvDesc &kv, int block, const int32_t *idx, const int32_t *count, int cap,
+                      hipStream_t stream, int *violation);
+
 // Block metadata: min/max keys ([d][2][stride] per unit, cache dtype) or, mean = true, the fp32 block
 // means ([d][stride] per unit).
 hipError_t launch_meta(const KvDesc &kv, int block, int stride, void *meta, bool mean, hipStream_t stream);

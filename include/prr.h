@@ -18,6 +18,12 @@
  *   - Device-side preconditions are the caller's contract: block indices in range and unique within a
  *     set, M disjoint from P, finite inputs, page-table entries in [0, num_pages).  Out-of-range block
  *     and page indices are clamped (never read out of bounds) but give unspecified results.
+ *   - Checking mode: with PRR_CHECK=1 in the environment (read once per process), prr_spec_attn,
+ *     prr_repair, prr_select, prr_select_spec and prr_select_spec_predict first check every input
+ *     set on the stream (count within [0, cap], entries within [0, ceil(seq_len / block)), no repeats),
+ *     wait for the result and return PRR_EINVAL, with nothing else enqueued, if one fails.  The mode
+ *     synchronises with the host and keeps its result in one device word of the library, so calls in it
+ *     must not overlap; it is for debugging.
  *   - Block sets are int32 lists per (sequence, kv head): idx[b][kvh][0 .. count[b][kvh]), any order on
  *     input; sets produced by the library are unique and ascending.
  *   - Query head h of a sequence uses kv head h / G with G = num_q_heads / num_kv_heads (contiguous
