@@ -347,6 +347,7 @@ def main():
     iso_level, iso_trend = torch.empty_like(layer.level), torch.empty_like(layer.trend)
     iso_live = torch.empty_like(layer.live)
     iso_P = bd.BlockSet.empty(B, H, w.topk, dev)
+    ws_iso_pred = bd.predict_workspace_for(B, H, layer.nmax, w.topk, dev)
 
     # warmup: a few layer steps and every call the timed loop isolates (a kernel's first launch in the
     # process loads its code object, milliseconds that would land in one timed step), then start the
@@ -364,7 +365,8 @@ def main():
         iso_level.copy_(layer.level)
         iso_trend.copy_(layer.trend)
         iso_live.copy_(layer.live)
-        bd.predict(layer.scores, kv.seq_len, w.block, *w.ema, w.topk, iso_level, iso_trend, iso_live, P_next=iso_P)
+        bd.predict(layer.scores, kv.seq_len, w.block, *w.ema, w.topk, iso_level, iso_trend, iso_live, P_next=iso_P,
+                   ws=ws_iso_pred)
         flush()
     torch.cuda.synchronize()
     layer.reset()
@@ -428,7 +430,7 @@ def main():
                           mode=args.score_mode, stream=crit)
             elif what == "predict":
                 bd.predict(layer.scores, kv.seq_len, w.block, *w.ema, w.topk, iso_level, iso_trend, iso_live,
-                           P_next=iso_P, stream=crit)
+                           P_next=iso_P, ws=ws_iso_pred, stream=crit)
             elif what == "select_spec":
                 bd.select_spec(q, kv, layer.meta, w.block, w.topk, P, w.scale, scores=iso_scores, A=iso_A,
                                M=iso_M, out=iso_state, ws=ws_iso_spec, mode=args.score_mode, stream=crit)

@@ -23,7 +23,8 @@ PAGE_SIZE = 16
 EXPORTS = (
     "prr_max_blocks", "prr_meta_stride", "prr_meta_bytes", "prr_attn_workspace_bytes",
     "prr_workspace_clear", "prr_build_meta", "prr_mean_meta_bytes", "prr_build_mean_meta", "prr_append",
-    "prr_select", "prr_select_spec_workspace_bytes", "prr_select_spec", "prr_select_spec_predict", "prr_predict",
+    "prr_select", "prr_select_spec_workspace_bytes", "prr_select_spec", "prr_select_spec_predict", "prr_predict_workspace_bytes",
+    "prr_predict",
     "prr_spec_attn",
     "prr_repair", "prr_calibrate_workspace_bytes", "prr_calibrate", "prr_strerror",
 )
@@ -55,7 +56,8 @@ class PredictArgsStruct(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("block", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
                 ("alpha", ctypes.c_double), ("beta", ctypes.c_double), ("gamma", ctypes.c_double),
                 ("budget", ctypes.c_int32), ("level", ctypes.c_void_p), ("trend", ctypes.c_void_p),
-                ("live", ctypes.c_void_p), ("P_next", ctypes.POINTER(BlockSetStruct))]
+                ("live", ctypes.c_void_p), ("P_next", ctypes.POINTER(BlockSetStruct)), ("ws", ctypes.c_void_p),
+                ("ws_bytes", ctypes.c_size_t)]
 
 
 _P = ctypes.POINTER
@@ -80,8 +82,9 @@ _SIGS = {
     "prr_select_spec_predict": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _VP, ctypes.c_int, _I32, _I32,
                                                _P(BlockSetStruct), _VP, _P(BlockSetStruct), _P(BlockSetStruct),
                                                _F, _P(AttnStateStruct), _VP, _SZ, _P(PredictArgsStruct), _VP]),
+    "prr_predict_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "prr_predict": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _D, _D, _D, _I32, _VP, _VP, _VP,
-                                   _P(BlockSetStruct), _VP]),
+                                   _P(BlockSetStruct), _VP, _SZ, _VP]),
     "prr_spec_attn": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _I32, _P(BlockSetStruct), _F,
                                      _P(AttnStateStruct), _VP, _SZ, _VP]),
     "prr_repair": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _I32, _P(BlockSetStruct), _F,
@@ -270,6 +273,12 @@ def select_spec_workspace_for(kv: KVCache, hq: int, block: int, topk: int, cap: 
                      kv.k.device)
 
 
+def predict_workspace_for(batch: int, num_kv_heads: int, max_blocks: int, budget: int, device="cuda"):
+    """Workspace for predict() (None where the rows are short enough not to need one)."""
+    n = load_library().prr_predict_workspace_bytes(batch, num_kv_heads, max_blocks, budget)
+    return Workspace(n, device) if n else None
+
+
 def workspace_clear(ws: Workspace, stream=None):
     _check(load_library().prr_workspace_clear(ws.ptr(), ws.nbytes, _stream(stream)), "prr_workspace_clear")
 
@@ -389,18 +398,22 @@ class PredictArgs:
     trend: torch.Tensor
     live: torch.Tensor
     P_next: "BlockSet"
+    ws: Optional["Workspace"] = None
 
     def struct(self, p_next_struct) -> PredictArgsStruct:
         B, H, nmax = self.scores.shape
         return PredictArgsStruct(_ptr(self.scores), _ptr(self.seq_len), B, H, self.block, nmax, float(self.alpha),
                                  float(self.beta), float(self.gamma), self.budget, _ptr(self.level),
-                                 _ptr(self.trend), _ptr(self.live), ctypes.pointer(p_next_struct))
+                                 _ptr(self.trend), _ptr(self.live), ctypes.pointer(p_next_struct),
+                                 self.ws.ptr() if self.ws is not None else None,
+                                 self.ws.nbytes if self.ws is not None else 0)
 
 
 def predict(scores: torch.Tensor, seq_len: torch.Tensor, block: int, alpha: float, beta: float,
             gamma: float, budget: int, level: torch.Tensor, trend: torch.Tensor, live: torch.Tensor,
-            P_next: Optional[BlockSet] = None, stream=None) -> BlockSet:
-    """One EMA step over scores [B][Hkv][Nmax]; updates level/trend/live in place; returns P_next."""
+            P_next: Optional[BlockSet] = None, ws: Optional[Workspace] = None, stream=None) -> BlockSet:
+    """One EMA step over scores [B][Hkv][Nmax]; updates level/trend/live in place; returns P_next.  ws
+    (predict_workspace_for): long rows are then updated in parallel parts."""
     lib = load_library()
     B, H, nmax = scores.shape
     if P_next is None:
@@ -408,6 +421,7 @@ def predict(scores: torch.Tensor, seq_len: torch.Tensor, block: int, alpha: floa
     ps = P_next.struct()
     st = lib.prr_predict(_ptr(scores), _ptr(seq_len), B, H, block, nmax, float(alpha), float(beta),
                          float(gamma), budget, _ptr(level), _ptr(trend), _ptr(live), ctypes.byref(ps),
+                         ws.ptr() if ws is not None else None, ws.nbytes if ws is not None else 0,
                          _stream(stream))
     _check(st, "prr_predict")
     return P_next

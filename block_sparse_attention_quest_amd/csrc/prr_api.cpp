@@ -247,6 +247,10 @@ prr_status prr_select_spec_predict(const void *q, int32_t num_q_heads, const prr
         pa.p_idx = pred->P_next->idx;
         pa.p_cnt = pred->P_next->count;
         pa.p_cap = pred->P_next->cap;
+        const size_t need = prr::predict_workspace_bytes(pred->batch, pred->num_kv_heads, pred->max_blocks,
+                                                         pred->budget);
+        if (pred->ws && pred->ws_bytes < need) return PRR_EWORKSPACE;
+        pa.ws = need ? pred->ws : nullptr;
     }
     PRR_TRY(check_input_set(kv, block, P, stream));
     return hip_status(prr::launch_select_spec(desc(kv), q, num_q_heads, meta, block, prr_meta_stride(kv, block),
@@ -263,15 +267,22 @@ prr_status prr_select_spec(const void *q, int32_t num_q_heads, const prr_kv_cach
                                    ws_bytes, nullptr, stream);
 }
 
+size_t prr_predict_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t max_blocks, int32_t budget) {
+    if (batch <= 0 || num_kv_heads <= 0 || max_blocks <= 0 || budget < 0) return 0;
+    return prr::predict_workspace_bytes(batch, num_kv_heads, max_blocks, budget);
+}
+
 prr_status prr_predict(const double *scores, const int32_t *seq_len, int32_t batch,
                        int32_t num_kv_heads, int32_t block, int32_t max_blocks, double alpha,
                        double beta, double gamma, int32_t budget, double *level, double *trend,
-                       int32_t *live, prr_block_set *P_next, hipStream_t stream) {
+                       int32_t *live, prr_block_set *P_next, void *ws, size_t ws_bytes, hipStream_t stream) {
     PRR_TRY(check_predict(scores, seq_len, batch, num_kv_heads, block, max_blocks, budget, level, trend, live,
                           P_next));
+    const size_t need = prr::predict_workspace_bytes(batch, num_kv_heads, max_blocks, budget);
+    if (ws && ws_bytes < need) return PRR_EWORKSPACE;
     return hip_status(prr::launch_predict(scores, seq_len, batch, num_kv_heads, block, max_blocks, alpha,
                                           beta, gamma, budget, level, trend, live, P_next->idx,
-                                          P_next->count, P_next->cap, stream));
+                                          P_next->count, P_next->cap, need ? ws : nullptr, stream));
 }
 
 prr_status prr_spec_attn(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, int32_t block,

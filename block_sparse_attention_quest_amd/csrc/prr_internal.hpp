@@ -82,6 +82,7 @@ struct PredictArgs {
     int32_t *p_idx;
     int32_t *p_cnt;
     int p_cap;
+    void *ws;   // predictor workspace for long rows (may be null)
 };
 
 // Rows of at most this many blocks let the predictor step run inside the selection + speculative launch.
@@ -102,10 +103,13 @@ hipError_t launch_select_spec_fp8(const KvDesc &kv, const void *q, int hq, const
                                   int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m, void *ws,
                                   bool mean, const PredictArgs *pred, hipStream_t stream);
 
+// ws (may be null): rows longer than 2048 blocks are then updated by 512-block parts in parallel and
+// ranked in two stages (predict_workspace_bytes; 0 where one workgroup per unit is used regardless).
+size_t predict_workspace_bytes(int batch, int hkv, int nmax, int budget);
 hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batch, int hkv,
                           int block, int nmax, double alpha, double beta, double gamma, int budget,
                           double *level, double *trend, int32_t *live, int32_t *p_idx,
-                          int32_t *p_cnt, int p_cap, hipStream_t stream);
+                          int32_t *p_cnt, int p_cap, void *ws, hipStream_t stream);
 
 // Decode append: token seq_len[b] of every sequence into the cache and its block's metadata, then
 // seq_len[b] += 1.

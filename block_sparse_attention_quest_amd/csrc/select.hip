@@ -162,6 +162,35 @@ __global__ __launch_bounds__(TPB) void predict_kernel(PredictParams p) {
     predict_body<KPT, TPB>(p, blockIdx.x);
 }
 
+// Long predictor rows: grid (parts, units) of 256 threads; the last part of a unit to arrive (a
+// device-scope counter, reset by it) ranks the unit's candidates, KPT slots per thread.
+template <int KPT>
+__global__ __launch_bounds__(256) void predict_parts_kernel(PredictParams p, TopkParams tp, CandParams cp,
+                                                            uint32_t *arrivals, int nparts) {
+    __shared__ TopkSmem<4> sm;
+    __shared__ int s_last;
+    const int part = blockIdx.x, u = blockIdx.y;
+    const size_t pi = (size_t)u * nparts + part;
+    predict_part_body(p, u, part, cp.key + pi * cp.kl, cp.idx + pi * cp.kl, cp.cnt + pi, cp.kl, sm);
+    // this workgroup's state and candidate stores are complete before its arrival is counted
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(&arrivals[u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev == (uint32_t)(nparts - 1);
+        if (s_last) __hip_atomic_store(&arrivals[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (s_last) {
+        topk_candidates_body<KPT>(tp, u, cp.key + (size_t)u * nparts * cp.kl, cp.idx + (size_t)u * nparts * cp.kl,
+                                  cp.cnt + (size_t)u * nparts, nparts, cp.kl);
+        if (threadIdx.x == 0) {
+            const int b = u / p.hkv;
+            p.live[u] = min((p.seq_len[b] + p.block - 1) / p.block, p.nmax);
+        }
+    }
+}
+
 template <template <int, int> class Launch, typename P>
 hipError_t dispatch_topk(int nmax, int units, const P &p, hipStream_t stream) {
     int tpb, kpt;
@@ -281,10 +310,35 @@ hipError_t launch_topk(const KvDesc &kv, int block, int nmax, int topk, const do
     return dispatch_topk<TopkLaunch>(nmax, kv.batch * kv.hkv, tp, stream);
 }
 
+// Two-stage predictor shape for rows of nmax blocks: parts of 512 blocks, kl = min(budget, 512)
+// candidates each, ranked with kpt slots per thread (0: one workgroup per unit instead).
+struct PredictPlan {
+    int nparts, kl, kpt;
+};
+
+static PredictPlan predict_plan(int nmax, int budget) {
+    PredictPlan pl{0, 0, 0};
+    if (nmax <= 2048 || budget <= 0) return pl;   // one workgroup per unit holds the whole row
+    pl.nparts = (nmax + 511) / 512;
+    pl.kl = std::min(budget, 512);
+    const long slots = (long)pl.nparts * pl.kl;
+    pl.kpt = slots <= 1024 ? 4 : slots <= 2048 ? 8 : slots <= 4096 ? 16 : 0;
+    if (pl.nparts > 256 || pl.kpt == 0) pl = PredictPlan{0, 0, 0};
+    return pl;
+}
+
+size_t predict_workspace_bytes(int batch, int hkv, int nmax, int budget) {
+    const PredictPlan pl = predict_plan(nmax, budget);
+    if (pl.kpt == 0) return 0;
+    const size_t units = (size_t)batch * hkv;
+    const size_t parts = units * pl.nparts;
+    return (units * 4 + 255) / 256 * 256 + parts * pl.kl * 12 + parts * 4;
+}
+
 hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batch, int hkv,
                           int block, int nmax, double alpha, double beta, double gamma, int budget,
                           double *level, double *trend, int32_t *live, int32_t *p_idx,
-                          int32_t *p_cnt, int p_cap, hipStream_t stream) {
+                          int32_t *p_cnt, int p_cap, void *ws, hipStream_t stream) {
     PredictParams p;
     p.scores = scores;
     p.seq_len = seq_len;
@@ -302,7 +356,31 @@ hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batc
     p.beta = beta;
     p.gamma = gamma;
     const int units = batch * hkv;
-    return dispatch_topk<PredictLaunch>(nmax, units, p, stream);
+    const PredictPlan pl = predict_plan(nmax, budget);
+    if (!ws || pl.kpt == 0) return dispatch_topk<PredictLaunch>(nmax, units, p, stream);
+    TopkParams tp = {};
+    tp.seq_len = seq_len;
+    tp.a_idx = p_idx;
+    tp.a_cnt = p_cnt;
+    tp.m_idx = nullptr;   // no set difference
+    tp.hkv = hkv;
+    tp.block = block;
+    tp.nmax = nmax;
+    tp.topk = budget;
+    tp.a_cap = p_cap;
+    uint32_t *arrivals = (uint32_t *)ws;
+    char *cbase = (char *)ws + ((size_t)units * 4 + 255) / 256 * 256;
+    const size_t slots = (size_t)units * pl.nparts * pl.kl;
+    CandParams cp;
+    cp.key = (uint64_t *)cbase;
+    cp.idx = (int32_t *)(cbase + slots * 8);
+    cp.cnt = (int32_t *)(cbase + slots * 12);
+    cp.kl = pl.kl;
+    const dim3 grid(pl.nparts, units);
+    if (pl.kpt == 4) predict_parts_kernel<4><<<grid, 256, 0, stream>>>(p, tp, cp, arrivals, pl.nparts);
+    else if (pl.kpt == 8) predict_parts_kernel<8><<<grid, 256, 0, stream>>>(p, tp, cp, arrivals, pl.nparts);
+    else predict_parts_kernel<16><<<grid, 256, 0, stream>>>(p, tp, cp, arrivals, pl.nparts);
+    return hipGetLastError();
 }
 
 }  // namespace prr

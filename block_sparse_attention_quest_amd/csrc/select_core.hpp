@@ -503,6 +503,15 @@ __device__ __forceinline__ void topk_body(const TopkParams &p, int u) {
 
 constexpr int kMaxTwoStageBlocks = 16384;   // P bitmap of the second stage (LDS)
 
+// Candidate slots of a two-stage top-K: [units][parts][kl] order keys and block indices, [units][parts]
+// counts (device memory of the caller's workspace).
+struct CandParams {
+    uint64_t *key;
+    int32_t *idx;
+    int32_t *cnt;
+    int kl;
+};
+
 __device__ __forceinline__ void st_dev_u64(uint64_t *ptr, uint64_t v) {
     __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -694,6 +703,55 @@ __device__ __forceinline__ void predict_body(const PredictParams &p, int u) {
         p.p_cnt[u] = (int32_t)total;
         p.live[u] = nb;
     }
+}
+
+// Long rows in parts (the predictor's counterpart of the two-stage top-K): workgroup `part` of unit u
+// updates the EMA state of blocks [512 part, +512) (two per thread, the arithmetic of predict_body) and
+// keeps the local top-min(budget, 512) of their predictions as candidates; the unit's last part to
+// finish ranks the candidates of all parts (topk_candidates_body) into P_next and sets live.
+__device__ __forceinline__ void predict_part_body(const PredictParams &p, int u, int part, uint64_t *ckey,
+                                                  int32_t *cidx, int32_t *ccnt, int kl, TopkSmem<4> &sm) {
+    constexpr int BPL = 2, BPW = 256 * BPL;
+    const int b = u / p.hkv;
+    const int slen = p.seq_len[b];
+    const int live_raw = p.live[u];
+    const size_t ro = (size_t)u * p.nmax;
+    const int first = part * BPW;
+    const int base = first + (int)threadIdx.x * BPL;
+    double is_v[BPL], l0_v[BPL], t0_v[BPL];
+#pragma unroll
+    for (int e = 0; e < BPL; ++e) {
+        const int i = base + e;
+        const bool in = i < p.nmax;
+        is_v[e] = in ? p.scores[ro + i] : 0.0;
+        l0_v[e] = in ? p.level[ro + i] : 0.0;
+        t0_v[e] = in ? p.trend[ro + i] : 0.0;
+    }
+    const int nb = min((slen + p.block - 1) / p.block, p.nmax);
+    const int live = min(max(live_raw, 0), nb);
+    const double one_a = dsub(1.0, p.alpha);
+    const double one_b = dsub(1.0, p.beta);
+    double pred[BPL];
+#pragma unroll
+    for (int e = 0; e < BPL; ++e) {
+        const int i = base + e;
+        pred[e] = 0.0;
+        if (i < nb) {
+            double lv, tr;
+            if (i < live) {
+                tr = dadd(dmul(p.beta, dsub(is_v[e], l0_v[e])), dmul(one_b, t0_v[e]));
+                lv = dadd(dmul(p.alpha, is_v[e]), dmul(one_a, l0_v[e]));
+            } else {
+                lv = is_v[e];
+                tr = 0.0;
+            }
+            p.level[ro + i] = lv;
+            p.trend[ro + i] = tr;
+            pred[e] = dadd(lv, dmul(p.gamma, tr));
+        }
+    }
+    const int n_local = min(max(nb - first, 0), BPW);
+    local_candidates<BPL>(pred, n_local, kl, first, ckey, cidx, ccnt, sm);
 }
 
 // Workgroup shape of the top-K kernels for rows of up to nmax keys: one wave per SIMD (256 threads) with

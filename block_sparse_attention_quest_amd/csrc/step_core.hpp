@@ -8,9 +8,9 @@
 // Figure 1 flow, §3): the two only read P and are independent.  On this GPU a dependency between two
 // streams costs about 10 us from the producer's end to the consumer's start, while kernels on one
 // stream follow each other about 1 us apart, so the overlap is made inside one grid instead: the first
-// workgroups score blocks (one workgroup per 512 blocks of a unit with min/max metadata, per 256 with
-// block means), the rest run the speculative chunks
-// (the attention kernels' chunk walk over n_spec workgroups).  Dispatch follows the workgroup index, so
+// workgroups score blocks (one workgroup per 512 blocks of a unit, two per lane, for min/max metadata and
+// for block means alike), the rest run the speculative chunks (the attention kernels' chunk walk over
+// n_spec workgroups, on bf16 or fp8 tiles: KT).  Dispatch follows the workgroup index, so
 // the scoring workgroups issue their loads first: the memory system serves them ahead of the
 // speculative stream, selection finishes early and its top-K runs under the speculative pass, which is
 // the longer of the two.  At 128K, batch 8 the grid is 256 scoring + 256 speculative workgroups: all of
@@ -41,21 +41,14 @@
 namespace prr {
 namespace {
 
-// Workgroup s < nsx * units scores blocks [BPW (s mod nsx), +BPW) of unit s / nsx (BPW = 512 blocks for
-// bf16 min/max metadata, 256 for fp32 block means: MEAN) and, if it is the unit's last to finish and
+// Workgroup s < nsx * units scores blocks [BPW (s mod nsx), +BPW) of unit s / nsx (BPW = 512 blocks, two
+// per lane, for bf16 min/max metadata and for fp32 block means: MEAN) and, if it is the unit's last to finish and
 // KPT > 0, runs the unit's top-K (KPT keys per thread, 256 KPT >= the unit's block count); the remaining
 // n_spec workgroups run the speculative pass.  PRED: the scoring workgroups then draw the n_pred units
 // of another layer's predictor step from *pred_ctr (8 keys per thread: rows of up to 2048 blocks); every
 // workgroup draws until it gets an index >= n_pred, so the launch makes exactly n_pred + n_score draws
 // and the one that draws the last index resets the counter for the next launch.  Register use is the
 // attention part's (two waves per SIMD).
-struct CandParams {
-    uint64_t *key;   // [units][nsx][kl]
-    int32_t *idx;    // [units][nsx][kl]
-    int32_t *cnt;    // [units][nsx]
-    int kl;
-};
-
 template <int KT, int D, int KPT, bool TWO, bool MEAN, bool PRED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void select_spec_kernel(
     AttnParams ap, ScoreParams sp, TopkParams tp, CandParams cp, PredictParams pp, uint32_t *arrivals,
@@ -137,7 +130,7 @@ hipError_t launch_select_spec_t(const KvDesc &kv, const void *q, int hq, const v
         if (!pred) return hipSuccess;
         return launch_predict(pred->scores, pred->seq_len, pred->batch, pred->hkv, pred->block, pred->nmax,
                               pred->alpha, pred->beta, pred->gamma, pred->budget, pred->level, pred->trend,
-                              pred->live, pred->p_idx, pred->p_cnt, pred->p_cap, stream);
+                              pred->live, pred->p_idx, pred->p_cnt, pred->p_cap, pred->ws, stream);
     };
     if constexpr (KT == kKtF32) {
         // fp32 caches (exact-input checks): the passes one after the other

@@ -104,6 +104,7 @@ class PRRLayer:
         self.out = torch.zeros((B, num_q_heads, d), dtype=torch.float32, device=dev)
         self.ws_spec = bd.select_spec_workspace_for(kv, num_q_heads, block, topk, max(1, budget))
         self.ws_repair = bd.workspace_for(kv, num_q_heads, block, max(1, topk))
+        self.ws_predict = bd.predict_workspace_for(B, H, self.nmax, budget, dev)
         self._streams = None
         self.pending_predict: Optional[bd.PredictArgs] = None
 
@@ -152,7 +153,7 @@ class PRRLayer:
         if timers and timers.repair_end:
             timers.repair_end.record(s)
         args = bd.PredictArgs(self.scores, self.kv.seq_len, self.block, self.alpha, self.beta, self.gamma,
-                              self.budget, self.level, self.trend, self.live, Pn)
+                              self.budget, self.level, self.trend, self.live, Pn, self.ws_predict)
         if defer_predict:
             self.pending_predict = args
         else:
@@ -201,7 +202,7 @@ class PRRLayer:
         e_spec.record(side)
         aux.wait_event(e_sel)
         bd.predict(self.scores, self.kv.seq_len, self.block, self.alpha, self.beta, self.gamma, self.budget,
-                   self.level, self.trend, self.live, P_next=Pn, stream=aux)
+                   self.level, self.trend, self.live, P_next=Pn, ws=self.ws_predict, stream=aux)
         e_pred.record(aux)
         crit.wait_event(e_spec)
         if timers and timers.repair_start:
@@ -217,7 +218,7 @@ class PRRLayer:
 def run_predict(args: bd.PredictArgs, stream=None):
     """Enqueue a predictor step on its own."""
     bd.predict(args.scores, args.seq_len, args.block, args.alpha, args.beta, args.gamma, args.budget, args.level,
-               args.trend, args.live, P_next=args.P_next, stream=stream)
+               args.trend, args.live, P_next=args.P_next, ws=args.ws, stream=stream)
 
 
 class PRRStack:

@@ -194,11 +194,18 @@ prr_status prr_select_spec(const void *q, int32_t num_q_heads, const prr_kv_cach
  * live = N_b and P_next = the `budget` blocks with the largest level + gamma trend (ties to the smaller
  * index), ascending.  All arithmetic fp64 in the order written, no fused multiply-add.
  * scores, level, trend: [batch][num_kv_heads][max_blocks] fp64, device; live [batch][num_kv_heads]
- * int32 (zero for a fresh sequence).  P_next->cap >= budget.  max_blocks <= 32768. */
+ * int32 (zero for a fresh sequence).  P_next->cap >= budget.  max_blocks <= 32768.
+ * ws (may be NULL): prr_predict_workspace_bytes of caller memory, zeroed once like an attention workspace
+ * (every call leaves it ready for the next).  With it, rows of more than 2048 blocks are updated by
+ * 512-block parts in parallel and P_next is ranked from the parts' local top-|P| candidates (exact, as
+ * in the two-stage top-K); without it one workgroup per (b, kvh) does the whole row.  Same results
+ * either way.  A non-NULL ws smaller than the query gives PRR_EWORKSPACE. */
+size_t prr_predict_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t max_blocks, int32_t budget);
+
 prr_status prr_predict(const double *scores, const int32_t *seq_len, int32_t batch,
                        int32_t num_kv_heads, int32_t block, int32_t max_blocks, double alpha,
                        double beta, double gamma, int32_t budget, double *level, double *trend,
-                       int32_t *live, prr_block_set *P_next, hipStream_t stream);
+                       int32_t *live, prr_block_set *P_next, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* The arguments of prr_predict, for prr_select_spec_predict. */
 typedef struct prr_predict_args {
@@ -214,6 +221,8 @@ typedef struct prr_predict_args {
     double *trend;
     int32_t *live;
     prr_block_set *P_next;
+    void *ws;          /* as prr_predict's (may be NULL) */
+    size_t ws_bytes;
 } prr_predict_args;
 
 /* prr_select_spec, plus (pred non-NULL) the predictor step prr_predict would run on *pred, typically

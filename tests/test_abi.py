@@ -109,10 +109,15 @@ def test_select_and_predict_argument_errors(lib):
     assert sel(M=None) == 1                       # P without M
     assert sel(M=_set(10)) == 1
     assert sel(kv=_kv(max_pages=65536), block=16) == 2   # more than 32768 blocks per sequence
-    pred = lambda budget=64, nmax=2048, P=P: lib.prr_predict(
-        1, 1, 2, 8, 64, nmax, 0.6, 0.3, 0.5, budget, 1, 1, 1, ctypes.byref(P) if P else None, None)
+    pred = lambda budget=64, nmax=2048, P=P, ws=None, wsb=0: lib.prr_predict(
+        1, 1, 2, 8, 64, nmax, 0.6, 0.3, 0.5, budget, 1, 1, 1, ctypes.byref(P) if P else None, ws, wsb, None)
     assert pred(budget=65) == 1
     assert pred(P=None) == 1
+    # long rows: parts of 512 blocks, min(budget, 512) candidates each, plus counters
+    need = lib.prr_predict_workspace_bytes(2, 8, 8192, 64)
+    assert need == 256 + 16 * 16 * 64 * 12 + 16 * 16 * 4
+    assert lib.prr_predict_workspace_bytes(2, 8, 2048, 64) == 0   # one workgroup per row: none needed
+    assert pred(nmax=8192, ws=1, wsb=need - 1) == 3
     assert pred(nmax=40000) == 2
     assert lib.prr_build_meta(ctypes.byref(kv), 64, None, None) == 1
     assert lib.prr_build_meta(ctypes.byref(_kv(max_pages=10)), 64, 1, None) == 1   # 160 tokens % 64
@@ -200,7 +205,7 @@ def test_select_spec_predict_argument_errors(lib):
                  beta=0.3, gamma=0.5, budget=64, level=0x4200, trend=0x4300, live=0x4400, P_next=Pn)
         f.update(kw)
         pn = f.pop("P_next")
-        return bd.PredictArgsStruct(**f, P_next=ctypes.pointer(pn) if pn is not None else None)
+        return bd.PredictArgsStruct(**f, P_next=ctypes.pointer(pn) if pn is not None else None, ws=None, ws_bytes=0)
 
     def call(pa):
         return lib.prr_select_spec_predict(1, 32, ctypes.byref(kv), 1, 0, 64, 64, ctypes.byref(P), scores,
