@@ -92,13 +92,17 @@ struct AttnParams {
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Device-scope (all XCDs) coherent store and load of one float.
-__device__ __forceinline__ void st_dev(float *ptr, float v) {
-    __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Device-scope (all XCDs) coherent store and load of two adjacent floats (8-byte aligned), x in the
+// low word.
+__device__ __forceinline__ void st_dev2(float *ptr, float x, float y) {
+    const uint64_t w = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
+    __hip_atomic_store((uint64_t *)ptr, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float ld_dev(const float *ptr) {
-    return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint64_t ld_dev2(const float *ptr) {
+    return __hip_atomic_load((const uint64_t *)ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ float lo_f(uint64_t w) { return __uint_as_float((uint32_t)w); }
+__device__ __forceinline__ float hi_f(uint64_t w) { return __uint_as_float((uint32_t)(w >> 32)); }
 
 // Lane-dependent choice between two wave-uniform values, kept as a register select (never an
 // indexed private-array access).
@@ -511,16 +515,18 @@ __device__ __forceinline__ void write_item(const AttnParams &p, size_t head, int
 
 // The last chunk of a unit folds the unit's nch partial states (and, in repair mode, the incoming
 // state) into the final one.  A thread owns VW consecutive channels of one query head.  Partials are
-// visited in chunk order, MB at a time: every device-scope load of a batch is issued before any is
-// used, so a batch costs one memory round trip; batches combine with the same online-softmax step
-// (running maximum, rescaled sums), which keeps the result independent of arrival order.
+// visited in chunk order, MB at a time: every device-scope load of a batch (8 bytes each: l and m, then
+// channel pairs) is issued before any is used, so a batch costs one memory round trip; slots past nch
+// are the empty state (l = 0, m = -inf, acc = 0), which the merge step leaves without effect.  Batches
+// combine with the same online-softmax step (running maximum, rescaled sums), which keeps the result
+// independent of arrival order.
 template <int VW, int D, bool REPAIR>
 __device__ __forceinline__ void merge_partials(const AttnParams &p, const float *base, int nch, size_t head0,
-                                               const float *s_mo, const float *s_lo) {
-    constexpr int MB = 16;
+                                               const float *s_mo, const float *s_lo, int tid) {
+    constexpr int MB = 8;
     constexpr int CPH = D / VW;   // channel groups per head
     const int G = p.G;
-    for (int it = threadIdx.x; it < G * CPH; it += kThreads) {
+    for (int it = tid; it < G * CPH; it += kThreads) {
         const int jj = it / CPH, c0 = (it - jj * CPH) * VW;
         const size_t head = head0 + jj;
         float mt = -INFINITY, ls = 0.0f, a[VW];
@@ -536,30 +542,35 @@ __device__ __forceinline__ void merge_partials(const AttnParams &p, const float 
             for (int v = 0; v < VW; ++v) a[v] = p.acc[head * D + c0 + v];
         }
         for (int w0 = 0; w0 < nch; w0 += MB) {
-            float pm[MB], pl[MB], pa[MB][VW];
+            uint64_t lm[MB], pa[MB][VW / 2];
 #pragma unroll
             for (int i = 0; i < MB; ++i) {
-                const int w = min(w0 + i, nch - 1);   // clamped: a valid partial, weighted 0 below
-                const float *pw = base + ((size_t)w * G + jj) * (D + 2);
-                pm[i] = ld_dev(&pw[D + 1]);
-                pl[i] = ld_dev(&pw[D]);
+                lm[i] = (uint64_t)__float_as_uint(-INFINITY) << 32;
 #pragma unroll
-                for (int v = 0; v < VW; ++v) pa[i][v] = ld_dev(&pw[c0 + v]);
+                for (int v = 0; v < VW / 2; ++v) pa[i][v] = 0;
+                if (w0 + i < nch) {
+                    const float *pw = base + ((size_t)(w0 + i) * G + jj) * (D + 2);
+                    lm[i] = ld_dev2(&pw[D]);
+#pragma unroll
+                    for (int v = 0; v < VW / 2; ++v) pa[i][v] = ld_dev2(&pw[c0 + 2 * v]);
+                }
             }
             float mb = mt;
 #pragma unroll
-            for (int i = 0; i < MB; ++i)
-                if (w0 + i < nch) mb = fmaxf(mb, pm[i]);
+            for (int i = 0; i < MB; ++i) mb = fmaxf(mb, hi_f(lm[i]));
             const float fr = rescale(mt, mb);
             ls *= fr;
 #pragma unroll
             for (int v = 0; v < VW; ++v) a[v] *= fr;
 #pragma unroll
             for (int i = 0; i < MB; ++i) {
-                const float f = w0 + i < nch ? rescale(pm[i], mb) : 0.0f;
-                ls += f * pl[i];
+                const float f = rescale(hi_f(lm[i]), mb);
+                ls += f * lo_f(lm[i]);
 #pragma unroll
-                for (int v = 0; v < VW; ++v) a[v] += f * pa[i][v];
+                for (int v = 0; v < VW / 2; ++v) {
+                    a[2 * v] += f * lo_f(pa[i][v]);
+                    a[2 * v + 1] += f * hi_f(pa[i][v]);
+                }
             }
             mt = mb;
         }
@@ -593,15 +604,19 @@ __device__ __forceinline__ void attn_body(const AttnParams &p, int wg, int nwg) 
         const int b = u / p.hkv, kvh = u - b * p.hkv;
         const int wbeg = k * cp + wave * pw;
         const PageLookup look = page_lookup(p, b, u, wbeg, pw);
+        // In repair mode the incoming m and l go out with the set lookups and reach LDS only after the
+        // tile walk, so no tile load waits for them.
+        float mo_in = 0.0f, lo_in = 0.0f;
+        if (REPAIR && threadIdx.x < G) {
+            const size_t h = (size_t)b * p.hq + (size_t)kvh * G + threadIdx.x;
+            mo_in = p.m[h];
+            lo_in = p.l[h];
+        }
         const int npages = unit_pages(p, u);
         const int nch = max(1, (npages + cp - 1) / cp);
         if (k >= nch) continue;
         const int slen = p.seq_len[b];
         const size_t head0 = (size_t)b * p.hq + (size_t)kvh * G;
-        if (REPAIR && threadIdx.x < G) {
-            s_mo[threadIdx.x] = p.m[head0 + threadIdx.x];
-            s_lo[threadIdx.x] = p.l[head0 + threadIdx.x];
-        }
         if (REPAIR && npages == 0) {
             // nothing missed: the state stays bit-for-bit as it is; only the normalised output
             if (p.out) {
@@ -643,20 +658,30 @@ __device__ __forceinline__ void attn_body(const AttnParams &p, int wg, int nwg) 
                 sm_l[wave][j] = lsum;
             }
         }
+        if (REPAIR && threadIdx.x < G) {
+            s_mo[threadIdx.x] = mo_in;
+            s_lo[threadIdx.x] = lo_in;
+        }
         __syncthreads();
 
         const bool single = (nch == 1);
         float *part = p.partials + ((size_t)u * p.kmax + k) * G * (D + 2);
-        for (int it = threadIdx.x; it < G * D; it += kThreads) {
-            const int jj = it / D, cc = it - jj * D;
+        // The thread index as an opaque value: the per-thread offsets below are then computed here,
+        // after the tile walk, instead of being hoisted to the kernel start and kept live through it.
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        for (int it = tid; it < G * D / 2; it += kThreads) {
+            const int jj = it / (D / 2), cc = (it - jj * (D / 2)) * 2;   // channels cc, cc + 1
             float mx = -INFINITY;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm_m[w][jj]);
-            float a = 0.0f, ls = 0.0f;
+            float a0 = 0.0f, a1 = 0.0f, ls = 0.0f;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) {
                 const float f = rescale(sm_m[w][jj], mx);
-                a += f * sm_acc[w][jj * DP + cc];
+                const float2 x = *(const float2 *)&sm_acc[w][jj * DP + cc];
+                a0 += f * x.x;
+                a1 += f * x.y;
                 ls += f * sm_l[w][jj];
             }
             if (single) {
@@ -666,17 +691,16 @@ __device__ __forceinline__ void attn_body(const AttnParams &p, int wg, int nwg) 
                     const float mo2 = mo == -INFINITY ? -INFINITY : mo * kLog2e;
                     const float mt = fmaxf(mx, mo2);
                     const float fo = rescale(mo2, mt), fn = rescale(mx, mt);
-                    write_item(p, head, cc, D, fo * p.acc[head * D + cc] + fn * a, fo * s_lo[jj] + fn * ls,
-                               mt, mt == mo2, mo);
+                    const float lt = fo * s_lo[jj] + fn * ls;
+                    write_item(p, head, cc, D, fo * p.acc[head * D + cc] + fn * a0, lt, mt, mt == mo2, mo);
+                    write_item(p, head, cc + 1, D, fo * p.acc[head * D + cc + 1] + fn * a1, lt, mt, mt == mo2, mo);
                 } else {
-                    write_item(p, head, cc, D, a, ls, mx, false, 0.0f);
+                    write_item(p, head, cc, D, a0, ls, mx, false, 0.0f);
+                    write_item(p, head, cc + 1, D, a1, ls, mx, false, 0.0f);
                 }
             } else {
-                st_dev(&part[jj * (D + 2) + cc], a);
-                if (cc == 0) {
-                    st_dev(&part[jj * (D + 2) + D], ls);
-                    st_dev(&part[jj * (D + 2) + D + 1], mx);
-                }
+                st_dev2(&part[jj * (D + 2) + cc], a0, a1);
+                if (cc == 0) st_dev2(&part[jj * (D + 2) + D], ls, mx);
             }
         }
         if (single) {
@@ -699,8 +723,8 @@ __device__ __forceinline__ void attn_body(const AttnParams &p, int wg, int nwg) 
         __syncthreads();
         if (s_last) {
             const float *base = p.partials + (size_t)u * p.kmax * G * (D + 2);
-            if (G * D <= 2 * kThreads) merge_partials<2, D, REPAIR>(p, base, nch, head0, s_mo, s_lo);
-            else merge_partials<4, D, REPAIR>(p, base, nch, head0, s_mo, s_lo);
+            if (G * D <= 2 * kThreads) merge_partials<2, D, REPAIR>(p, base, nch, head0, s_mo, s_lo, tid);
+            else merge_partials<4, D, REPAIR>(p, base, nch, head0, s_mo, s_lo, tid);
             if (threadIdx.x == 0)
                 __hip_atomic_store(&p.counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
