@@ -7,17 +7,17 @@ namespace prr {
 namespace {
 
 // bf16 speculation is held to 256 registers so two waves share each SIMD (in the fused launch the second
-// belongs to selection), with two tiles in flight per wave.  Repair runs alone: one wave per SIMD with
-// up to 512 registers and four tiles in flight, so a wave's share of a repair chunk is requested in one
-// go.  The fp32 variants (exact-input checks) may use more registers.
+// belongs to selection), with two tiles in flight per wave.  Repair runs alone with the same budget: two
+// workgroups per CU, so a set at full capacity gets a workgroup per chunk.  The fp32 variants
+// (exact-input checks) may use more registers.
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_spec_bf16(AttnParams p) {
     attn_body<kKtBf16, D, false, 2>(p, blockIdx.x, gridDim.x);
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1))) void attn_repair_bf16(AttnParams p) {
-    attn_body<kKtBf16, D, true, 4>(p, blockIdx.x, gridDim.x);
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_repair_bf16(AttnParams p) {
+    attn_body<kKtBf16, D, true, 2>(p, blockIdx.x, gridDim.x);
 }
 
 // fp8 tiles take half the registers of bf16 ones: twice as many in flight for the same bytes.
@@ -27,8 +27,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1))) void attn_repair_fp8(AttnParams p) {
-    attn_body<kKtFp8, D, true, 4>(p, blockIdx.x, gridDim.x);
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_repair_fp8(AttnParams p) {
+    attn_body<kKtFp8, D, true, 2>(p, blockIdx.x, gridDim.x);
 }
 
 template <int D>

@@ -775,7 +775,9 @@ int attn_setup(AttnParams &p, const KvDesc &kv, const void *q, int hq, int block
     // each SIMD's registers to the selection kernels that run beside the speculative pass.  A full set
     // (count = cap) is spread over that many chunks, each as large as the work allows (fewer chunks
     // mean fewer partial states to merge); repair sets are usually a fraction of the capacity (the
-    // missed part of a selection), so repair uses half that chunk size to keep the chip busy.
+    // missed part of a selection), so repair uses half that chunk size to keep the chip busy, and up
+    // to two workgroups per CU (it runs alone, two waves per SIMD), so that every chunk of a set at full
+    // capacity has a workgroup of its own instead of waiting for another chunk of the same workgroup.
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
         int n = 0;
@@ -789,7 +791,7 @@ int attn_setup(AttnParams &p, const KvDesc &kv, const void *q, int hq, int block
     if (repair) cp = std::max<long>(kChunkMin, round8(cp / 2));
     p.cp = (int)cp;
     p.kmax = (int)std::max<long>(1, (cap_pages + cp - 1) / cp);
-    return (int)std::min<long>((long)units * p.kmax, target);
+    return (int)std::min<long>((long)units * p.kmax, repair ? 2 * target : target);
 }
 
 }  // namespace
