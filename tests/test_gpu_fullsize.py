@@ -206,3 +206,36 @@ def test_two_stream_schedule_matches_one_stream():
         assert torch.equal(a.level, b.level) and torch.equal(a.trend, b.trend), t
         for name in ("acc", "l", "m"):
             assert torch.equal(getattr(a.state, name), getattr(b.state, name)), (t, name)
+
+
+def test_largest_chunks_and_several_chunks_per_workgroup():
+    """Sets of thousands of blocks: chunks reach their 256-page maximum (64 pages per wave, the longest
+    tile walk), and a unit has more chunks than the launch has workgroups, so workgroups walk several
+    chunks in turn - the speculative pass for units with a large P, repair for units with a large M.
+    Sampled units of both kinds against the oracle."""
+    w = wl.Workload("big_sets", 4, 8, 4, 64, 81920, 16, 8, "bf16", seed=321)
+    inp = wl.make_inputs(w, "cuda")
+    dkv = device_kv(inp)
+    nb = w.blocks_of(0)
+    cap = 4800
+    rng = np.random.default_rng(9)
+    P, M = [], []
+    for b in range(w.batch):
+        prow, mrow = [], []
+        for h in range(w.num_kv_heads):
+            u = b * w.num_kv_heads + h
+            n_p, n_m = (cap - 13 * u, 300) if u % 2 == 0 else (200, cap - 13 * u)
+            perm = rng.permutation(nb)
+            prow.append(sorted(perm[:n_p].tolist()))
+            mrow.append(sorted(perm[n_p:n_p + n_m].tolist()))
+        P.append(prow)
+        M.append(mrow)
+    print(f"[big sets] B={w.batch} kv heads={w.num_kv_heads} blocks={nb} cap={cap}", flush=True)
+    state = bd.spec_attn(inp.q[0], dkv, w.block, sets_to_device(P, cap), w.scale)
+    spec = state.clone()
+    out = torch.empty_like(state.acc)
+    bd.repair(inp.q[0], dkv, w.block, sets_to_device(M, cap), w.scale, state, out=out)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (0, 1), (3, 3), (2, 2)):
+        _check_unit_attention(spec, None, inp, b, h, 0, P[b][h], "spec")
+        _check_unit_attention(state, out, inp, b, h, 0, set(P[b][h]) | set(M[b][h]), "repair")
