@@ -208,12 +208,14 @@ def test_two_stream_schedule_matches_one_stream():
             assert torch.equal(getattr(a.state, name), getattr(b.state, name)), (t, name)
 
 
-def test_largest_chunks_and_several_chunks_per_workgroup():
+@pytest.mark.parametrize("dtype,hq,d", [("bf16", 8, 64), ("fp8", 16, 128), ("bf16", 64, 128)],
+                         ids=["bf16_g2_d64", "fp8_g4_d128", "bf16_g16_d128"])
+def test_largest_chunks_and_several_chunks_per_workgroup(dtype, hq, d):
     """Sets of thousands of blocks: chunks reach their 256-page maximum (64 pages per wave, the longest
     tile walk), and a unit has more chunks than the launch has workgroups, so workgroups walk several
     chunks in turn - the speculative pass for units with a large P, repair for units with a large M.
     Sampled units of both kinds against the oracle."""
-    w = wl.Workload("big_sets", 4, 8, 4, 64, 81920, 16, 8, "bf16", seed=321)
+    w = wl.Workload("big_sets", 4, hq, 4, d, 81920, 16, 8, dtype, seed=321)
     inp = wl.make_inputs(w, "cuda")
     dkv = device_kv(inp)
     nb = w.blocks_of(0)
@@ -230,7 +232,8 @@ def test_largest_chunks_and_several_chunks_per_workgroup():
             mrow.append(sorted(perm[n_p:n_p + n_m].tolist()))
         P.append(prow)
         M.append(mrow)
-    print(f"[big sets] B={w.batch} kv heads={w.num_kv_heads} blocks={nb} cap={cap}", flush=True)
+    print(f"[big sets] {dtype} G={w.group} d={d} B={w.batch} kv heads={w.num_kv_heads} blocks={nb} cap={cap}",
+          flush=True)
     state = bd.spec_attn(inp.q[0], dkv, w.block, sets_to_device(P, cap), w.scale)
     spec = state.clone()
     out = torch.empty_like(state.acc)
