@@ -19,11 +19,13 @@
 // Top-K (with M = A \ P).  The last scoring workgroup of a unit to finish (a device-scope arrival
 // counter; nobody waits) runs the unit's top-K with the same 256 threads, so the top-K of most units
 // overlaps the speculative pass:
-//   * up to 2048 blocks per unit, over all of the unit's scores (up to 8 per thread), stored and re-read
+//   * up to 1024 blocks per unit, over all of the unit's scores (up to 4 per thread), stored and re-read
 //     with device-scope accesses, which are coherent across the XCDs' L2s;
 //   * beyond that, in two stages: every scoring workgroup first keeps the local top-min(K, 512) of its
-//     own 512 blocks as candidates, and the last one ranks the candidates of all workgroups of the unit
-//     (up to 16 per thread; the selection is exact, see select_core.hpp);
+//     own 512 blocks as candidates (in parallel, right after scoring), and the last one ranks the
+//     candidates of all workgroups of the unit (up to 16 per thread; the selection is exact, see
+//     select_core.hpp).  At 2048 blocks and K = 64 the last workgroup ranks 256 candidates instead of
+//     2048 scores;
 // otherwise (more candidates than that) the separate top-K kernel follows the launch.
 //
 // Predictor step of another layer.  In a stack of layers the predictor of layer l needs only layer l's
