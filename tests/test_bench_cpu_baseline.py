@@ -1,0 +1,41 @@
+"""bench.py's oracle timing on the CPU: the one-thread leg and the worker-process leg run the same
+speculative attention and repair work on a small workload and report consistent figures."""
+import os
+import sys
+
+from block_sparse_attention_quest_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import bench
+    return bench
+
+
+def test_cpu_baseline_one_thread_and_worker_processes():
+    bench = _bench()
+    w = wl.scaled(wl.C3, context=4096, batch=1)
+    inp = wl.make_inputs(w, "cpu")
+    units, steps = 3, 3
+    pool = bench.OraclePool(2)
+    try:
+        r = bench.cpu_baseline(inp, w, units, steps, pool=pool)
+    finally:
+        pool.close()
+    assert all(not p.is_alive() for p in pool.procs)
+    assert r["kind"] == "oracle" and r["cores"] == 2
+    assert r["value"] > 0 and r["value_one_thread"] > 0 and r["seconds_attn"] > 0
+    # both legs time the same bytes: their ratio is the ratio of their times
+    ratio = r["value"] / r["value_one_thread"]
+    assert abs(ratio - r["seconds_attn_one_thread"] / r["seconds_attn"]) <= 0.02 * ratio + 1e-3
+
+
+def test_cpu_baseline_without_pool_is_the_one_thread_leg():
+    bench = _bench()
+    w = wl.scaled(wl.C3, context=4096, batch=1)
+    inp = wl.make_inputs(w, "cpu")
+    r = bench.cpu_baseline(inp, w, 2, 2)
+    assert r["cores"] == 1 and r["value"] == r["value_one_thread"]
