@@ -43,10 +43,6 @@
 namespace prr {
 namespace {
 
-// Cache-policy operand of a buffer load that streams its data without keeping it in the caches (the nt
-// bit on gfx950).
-constexpr int kMetaNt = 2;
-
 constexpr int kTopkKeysPerThread = 32;   // upper bound on keys held per thread by the top-K kernels
 
 __device__ __forceinline__ double dadd(double a, double b) {
@@ -339,8 +335,7 @@ __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u,
     // row (min or max) depends on the sign of qbar_i only, so the row address is wave-uniform (scalar)
     // and each lane adds its own block offset.
     // Buffer loads: the unit's metadata is one buffer resource (scalar base), the row offset a scalar
-    // and the lane's block offset the only vector operand, shared by all d loads.  Each metadata word is
-    // read once per step, so the loads are non-temporal (kMetaNt).
+    // and the lane's block offset the only vector operand, shared by all d loads.
     // Mean-pooled scoring: one fp32 row (the block means) per channel, [d][stride].
     constexpr int ES = (BF16 && !MEAN) ? 2 : 4;   // element size
     constexpr int ROWS = MEAN ? 1 : 2;            // rows per channel
@@ -360,7 +355,7 @@ __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u,
             uint32_t lo[D / 2], hi[D / 2];
 #pragma unroll
             for (int j = 0; j < D / 2; ++j) {
-                const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, (half * D / 2 + j) * p.stride * ES, kMetaNt);
+                const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, (half * D / 2 + j) * p.stride * ES, 0);
                 lo[j] = v[0];
                 hi[j] = v[1];
             }
@@ -380,7 +375,7 @@ __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u,
             // qbar >= 0: the max term is qbar * mx (row 1); otherwise qbar * mn (row 0).  bf16: the 4 bytes
             // hold blocks p0 and p0 + 1; fp32: block p0.
             const int sgn = __builtin_amdgcn_readfirstlane(s_row[i]);
-            raw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, (2 * i + sgn) * p.stride * ES, kMetaNt);
+            raw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, (2 * i + sgn) * p.stride * ES, 0);
         }
 #pragma unroll
         for (int i = 0; i < D; ++i) {
