@@ -758,10 +758,10 @@ size_t max_chunks(int units, int block, int cap) {
 }
 
 // Fills the kernel parameters of one speculative (repair = false) or repair launch and returns its
-// grid size (workgroups).
+// grid size (workgroups).  target_wgs: workgroups to spread a full set over (default: one per CU).
 int attn_setup(AttnParams &p, const KvDesc &kv, const void *q, int hq, int block, const int32_t *idx,
                const int32_t *count, int cap, float scale, float *acc, float *l, float *m, float *out,
-               bool repair, void *ws) {
+               bool repair, void *ws, int target_wgs = 0) {
     p.q = q;
     p.k = kv.k;
     p.v = kv.v;
@@ -797,7 +797,7 @@ int attn_setup(AttnParams &p, const KvDesc &kv, const void *q, int hq, int block
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) cus = n;
     }
-    const long target = cus;
+    const long target = target_wgs > 0 ? target_wgs : cus;
     const long cap_pages = (long)cap * p.ppb;
     const long full = (long)units * cap_pages;
     auto round8 = [](long x) { return (x + kChunkMin - 1) / kChunkMin * kChunkMin; };

@@ -170,11 +170,15 @@ prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv
                       prr_block_set *A, prr_block_set *M, hipStream_t stream);
 
 /* Selection and the speculative pass over P together (the overlap of [paper] §1, Figure 1 flow, and §3:
- * speculation over P runs concurrently with selection; the two only read P).  Computes exactly what
+ * speculation over P runs concurrently with selection; the two only read P).  Computes what
  *     prr_select(q, num_q_heads, kv, meta, block, topk, P, scores, A, M) and
  *     prr_spec_attn(q, num_q_heads, kv, block, P, scale, out, ws, ws_bytes)
  * compute, as one grid whose workgroups do either part (bf16 caches; fp32 caches run the two calls in
- * turn), followed by the top-K on the same stream.  P and M must be non-NULL; A->cap and M->cap >= topk;
+ * turn), followed by the top-K on the same stream.  scores, A and M are the same bit for bit.  The state
+ * is too while the scoring workgroups (ceil(N_max / 512) per (sequence, kv head)) number at most the
+ * GPU's compute units; with more of them the speculative pass is cut into fewer, longer chunks so that the
+ * whole grid is resident at once, and the state then differs from prr_spec_attn's by rounding only (the
+ * order of the sums changes).  P and M must be non-NULL; A->cap and M->cap >= topk;
  * N_b <= 32768.  ws: prr_select_spec_workspace_bytes(kv, num_q_heads, block, topk, P->cap): the attention
  * workspace of prr_spec_attn plus room for top-K candidates and a work counter (zeroed once like an
  * attention workspace; every call leaves it ready for the next). */

@@ -347,3 +347,41 @@ def test_select_spec_fused_topk_shapes(nblocks, topk):
             assert got_a[b][h] == list(oA[b][h]), (b, h)
             assert got_m[b][h] == list(orc.set_minus(oA[b][h], P[b][h])), (b, h)
     assert_heads(fstate, orc.spec_states(q, kv, w.block, P, w.scale), "fused spec")
+
+
+def test_select_spec_with_more_scoring_workgroups_than_cus():
+    """Many units (64 sequences x 8 kv heads, one scoring workgroup each): the scoring workgroups alone
+    outnumber the CUs, so the fused launch spreads the speculative pass over the remaining slots with
+    longer chunks than prr_spec_attn uses.  Scores, A and M stay bit for bit; the state matches the
+    separate call within the parity tolerance and the oracle on sampled units."""
+    lens = wl.ragged_lengths(wl.Workload("many_units", 64, 32, 8, 128, 2048, 16, 8, "bf16", seed=41), 900, 2048)
+    w = wl.Workload("many_units", 64, 32, 8, 128, max(lens), 16, 16, "bf16", seed=41, seq_lens=lens)
+    inp = wl.make_inputs(w, "cuda")
+    dkv = device_kv(inp)
+    meta = bd.build_meta(dkv, w.block)
+    rng = np.random.default_rng(7)
+    P, _ = _random_sets(w, rng, [(40, 0), (0, 0), (90, 0), (3, 0), (128, 0)])
+    Pd = sets_to_device(P, 128)
+    scores, A, M = bd.select(inp.q[0], dkv, meta, w.block, w.topk, P=Pd)
+    state = bd.spec_attn(inp.q[0], dkv, w.block, Pd, w.scale)
+    fs, fA, fM, fstate = bd.select_spec(inp.q[0], dkv, meta, w.block, w.topk, Pd, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(fs, scores)
+    assert fA.lists() == A.lists() and fM.lists() == M.lists()
+    a1, a2 = state.acc.double(), fstate.acc.double()
+    l1, l2 = state.l.double(), fstate.l.double()
+    m1, m2 = state.m.double(), fstate.m.double()
+    assert torch.equal(l1 == 0, l2 == 0)
+    live = l1 > 0
+    assert torch.all((l1[live] - l2[live]).abs() <= 1e-4 * l1[live])
+    assert torch.all((m1[live] - m2[live]).abs() <= 1e-4 * torch.clamp(m1[live].abs(), min=1.0))
+    o1 = a1[live] / l1[live][:, None]
+    o2 = a2[live] / l2[live][:, None]
+    assert float((o1 - o2).abs().max()) <= 5e-3
+    for b, h in ((0, 0), (17, 2), (63, 7)):
+        q, kv = unit_view(inp, b, h)
+        for g in range(w.group):
+            ref = orc.head_state(q, kv, 0, g, w.group, sorted(P[b][h]), w.block, w.scale)
+            hq = h * w.group + g
+            assert_state(fstate.acc[b, hq].double().cpu().numpy(), float(fstate.l[b, hq]), float(fstate.m[b, hq]),
+                         ref, f"fused b={b} kvh={h} g={g}")
