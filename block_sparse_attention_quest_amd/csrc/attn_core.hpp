@@ -95,9 +95,9 @@ struct AttnParams {
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // A K/V tile load: plain, or non-temporal (NT: the line is streamed through without being kept in the
-// caches).  The speculative pass reads each of its tiles once and uses NT loads; at 128K context, batch 8
-// they took it from 30.6 to 29.2 us.  Repair, whose tiles arrive in one burst, measured 1.3 us slower
-// with them and keeps plain loads.
+// caches).  Every tile is read once.  V tiles always use NT loads; K tiles use them in the speculative
+// pass only.  Measured at 128K context, batch 8: NT loads took the speculative pass from 30.6 to 29.2 us;
+// in repair, whose tiles arrive in one burst, NT on V alone saved 0.5 us, while NT on K cost 1.1 us.
 template <bool NT, typename T>
 __device__ __forceinline__ T ld_tile(const void *ptr) {
     if constexpr (NT) return __builtin_nontemporal_load((const T *)ptr);
@@ -217,7 +217,7 @@ __device__ __forceinline__ void load_tile(TileB<D> &t, const __bf16 *kb, const _
     const int pv = pick(g >> 1, pa, pb);
     const __bf16 *vp = vb + (size_t)pv * stride + (size_t)r * kPage + 8 * (g & 1);
 #pragma unroll
-    for (int cb = 0; cb < D / 16; ++cb) t.v[cb] = ld_tile<NT, bf16x8>(vp + (size_t)cb * 16 * kPage);
+    for (int cb = 0; cb < D / 16; ++cb) t.v[cb] = ld_tile<true, bf16x8>(vp + (size_t)cb * 16 * kPage);
 }
 
 template <int D>
@@ -339,7 +339,7 @@ __device__ __forceinline__ void load_tile(TileE<D> &t, const uint8_t *kb, const 
     const int pv = pick(g >> 1, pa, pb);
     const uint8_t *vp = vb + (size_t)pv * stride + (size_t)r * kPage + 8 * (g & 1);
 #pragma unroll
-    for (int cb = 0; cb < D / 16; ++cb) t.v[cb] = ld_tile<NT, u32x2>(vp + (size_t)cb * 16 * kPage);
+    for (int cb = 0; cb < D / 16; ++cb) t.v[cb] = ld_tile<true, u32x2>(vp + (size_t)cb * 16 * kPage);
 }
 
 // Eight E4M3 codes (bytes of lo, then of hi) as eight bf16 values, exactly.
