@@ -2,7 +2,7 @@
 
 Usage:
   python -m block_sparse_attention_quest_amd.profiling stats <kernel_stats.csv> <out.md> "<command>"
-        [--trace <kernel_trace.csv>]
+        [--trace <kernel_trace.csv>] [--bench-log <bench.py output of the same run>]
   python -m block_sparse_attention_quest_amd.profiling hbm <fetch counter_collection.csv>
         <write counter_collection.csv> <out.md> --copy-mib N "<fetch command>" "<write command>"
 
@@ -59,13 +59,16 @@ def stats_table(path: str, top: int = 16) -> str:
 
 
 def trace_averages(path: str, names=("attn_spec_bf16", "attn_repair_bf16", "select_spec_kernel")) -> str:
-    """Average duration of each named kernel per stream over its launches that did work: launches
-    shorter than a fifth of the kernel's longest (warm-up calls over empty sets) are left out.  The
+    """Average and median duration of each named kernel per stream over its launches that did work:
+    launches shorter than a fifth of the kernel's longest (calls over empty sets) are left out; the
+    warm-up steps' launches, which run slower, stay in (the median is the figure to compare with a
+    timed run).  The
     stream that also runs the cache-flush reductions is the one bench.py times kernels alone on; the
     other carries the overlapped layer step's speculative pass."""
     rows = list(csv.DictReader(open(path)))
     flush_streams = {r["Stream_Id"] for r in rows if "reduce_kernel" in r["Kernel_Name"]}
-    out = ["| kernel | stream | launches with work | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    out = ["| kernel | stream | launches with work | avg us | median us | min us | max us |",
+           "|---|---|---|---|---|---|---|"]
     for nm in names:
         sel = [r for r in rows if nm in r["Kernel_Name"]]
         if not sel:
@@ -77,9 +80,25 @@ def trace_averages(path: str, names=("attn_spec_bf16", "attn_repair_bf16", "sele
             if not ds:
                 continue
             kind = "flush stream (isolated launches + critical path)" if sid in flush_streams else "side stream"
-            out.append(f"| `{nm}` | {sid}: {kind} | {len(ds)} | {statistics.mean(ds):.2f} | {min(ds):.2f} | "
-                       f"{max(ds):.2f} |")
+            out.append(f"| `{nm}` | {sid}: {kind} | {len(ds)} | {statistics.mean(ds):.2f} | "
+                       f"{statistics.median(ds):.2f} | {min(ds):.2f} | {max(ds):.2f} |")
     return "\n".join(out)
+
+
+def bench_in_run(log_path: str) -> str:
+    """bench.py's own kernel times (HIP events) from the JSON line of the profiled run, for the
+    cross-check of the two clocks on the same launches."""
+    import json
+
+    line = [ln for ln in open(log_path) if ln.startswith('{"metric"')][-1]
+    d = json.loads(line)
+    rows = ["bench.py's own figures in the same (profiled) run, event time minus the empty event pair, median "
+            "over the timed steps:", "", "| kernel | us |", "|---|---|"]
+    for key, name in (("us_spec_attn_median", "attn_spec_bf16"), ("us_repair_median", "attn_repair_bf16"),
+                      ("us_select_spec_median", "select_spec_kernel")):
+        if d.get(key) is not None:
+            rows.append(f"| `{name}` | {d[key]:.2f} |")
+    return "\n".join(rows)
 
 
 def _per_dispatch(path: str, counter: str) -> dict:
@@ -138,6 +157,8 @@ def main(argv):
         if "--trace" in argv:
             text += ["Attention launches over non-empty sets (from the kernel trace of the same run):", "",
                      trace_averages(argv[argv.index("--trace") + 1]), ""]
+        if "--bench-log" in argv:
+            text += [bench_in_run(argv[argv.index("--bench-log") + 1]), ""]
         open(out, "w").write("\n".join(text))
     elif argv and argv[0] == "hbm":
         fetch_csv, write_csv, out = argv[1:4]
