@@ -58,8 +58,22 @@ struct SelectSpecPlan {
     bool two;
     int kl;
     int kpt;
+    // three stages (rows with more candidate slots than one ranking holds): the launch keeps the parts'
+    // candidates only (kpt = 0); then ng groups of gp parts per unit keep their top-kl2 each (kpt2 slots per
+    // thread) and the unit's last group ranks the ng kl2 group candidates (kpt3 slots per thread).
+    bool three;
+    int gp, ng, kl2, kpt2, kpt3;
 };
 SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean);
+
+// The second and third stages of a three-stage top-K (plan.three): nparts parts of kl candidates per
+// unit at cand1 (keys, then indices, then counts, as the fused launch writes them); the group candidates
+// go to cand2 (same layout, ng x kl2 slots per unit), the per-unit group arrival counters to arrivals
+// (zero at rest; the last group of a unit resets its counter).
+hipError_t launch_topk_groups(const KvDesc &kv, int block, int nmax, int topk, const int32_t *p_idx,
+                              const int32_t *p_cnt, int p_cap, int32_t *a_idx, int32_t *a_cnt, int a_cap,
+                              int32_t *m_idx, int32_t *m_cnt, int m_cap, const SelectSpecPlan &plan, int nparts,
+                              void *cand1, void *cand2, uint32_t *arrivals, hipStream_t stream);
 
 // Offset of the carried predictor's work counter in the prr_select_spec workspace.
 size_t pred_counter_offset(int batch, int hq, int hkv, int d, int block, int cap, int nmax, int topk);

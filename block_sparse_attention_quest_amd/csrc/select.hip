@@ -191,6 +191,34 @@ __global__ __launch_bounds__(256) void predict_parts_kernel(PredictParams p, Top
     }
 }
 
+// Second and third stages of a three-stage top-K: grid (groups, units) of 256 threads.  Group g of unit
+// u keeps the top-kl2 of the candidates of parts [g gp, (g + 1) gp); the unit's last group to arrive (a
+// device-scope counter, reset by it) ranks the groups' candidates into A and M.
+template <int KPT2, int KPT3>
+__global__ __launch_bounds__(256) void topk_groups_kernel(TopkParams tp, CandParams c1, CandParams c2,
+                                                          uint32_t *arrivals, int nparts, int gp, int ng) {
+    __shared__ int s_last;
+    const int g = blockIdx.x, u = blockIdx.y;
+    const int p0 = g * gp;
+    const int gparts = min(gp, nparts - p0);
+    const size_t in = (size_t)u * nparts + p0;
+    const size_t out = (size_t)u * ng + g;
+    group_candidates<KPT2>(c1.key + in * c1.kl, c1.idx + in * c1.kl, c1.cnt + in, gparts, c1.kl, c2.kl,
+                           c2.key + out * c2.kl, c2.idx + out * c2.kl, c2.cnt + out);
+    // this group's candidate stores are complete before its arrival is counted
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(&arrivals[u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev == (uint32_t)(ng - 1);
+        if (s_last) __hip_atomic_store(&arrivals[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (s_last)
+        topk_candidates_body<KPT3>(tp, u, c2.key + (size_t)u * ng * c2.kl, c2.idx + (size_t)u * ng * c2.kl,
+                                   c2.cnt + (size_t)u * ng, ng, c2.kl);
+}
+
 template <template <int, int> class Launch, typename P>
 hipError_t dispatch_topk(int nmax, int units, const P &p, hipStream_t stream) {
     int tpb, kpt;
@@ -308,6 +336,48 @@ hipError_t launch_topk(const KvDesc &kv, int block, int nmax, int topk, const do
     tp.a_cap = a_cap;
     tp.m_cap = m_cap;
     return dispatch_topk<TopkLaunch>(nmax, kv.batch * kv.hkv, tp, stream);
+}
+
+hipError_t launch_topk_groups(const KvDesc &kv, int block, int nmax, int topk, const int32_t *p_idx,
+                              const int32_t *p_cnt, int p_cap, int32_t *a_idx, int32_t *a_cnt, int a_cap,
+                              int32_t *m_idx, int32_t *m_cnt, int m_cap, const SelectSpecPlan &plan, int nparts,
+                              void *cand1, void *cand2, uint32_t *arrivals, hipStream_t stream) {
+    TopkParams tp = {};
+    tp.seq_len = kv.seq_len;
+    tp.p_idx = p_idx;
+    tp.p_cnt = p_cnt;
+    tp.a_idx = a_idx;
+    tp.a_cnt = a_cnt;
+    tp.m_idx = m_idx;
+    tp.m_cnt = m_cnt;
+    tp.hkv = kv.hkv;
+    tp.block = block;
+    tp.nmax = nmax;
+    tp.topk = topk;
+    tp.p_cap = p_cap;
+    tp.a_cap = a_cap;
+    tp.m_cap = m_cap;
+    const int units = kv.batch * kv.hkv;
+    const size_t s1 = (size_t)units * nparts * plan.kl, s2 = (size_t)units * plan.ng * plan.kl2;
+    CandParams c1, c2;
+    c1.key = (uint64_t *)cand1;
+    c1.idx = (int32_t *)((char *)cand1 + s1 * 8);
+    c1.cnt = (int32_t *)((char *)cand1 + s1 * 12);
+    c1.kl = plan.kl;
+    c2.key = (uint64_t *)cand2;
+    c2.idx = (int32_t *)((char *)cand2 + s2 * 8);
+    c2.cnt = (int32_t *)((char *)cand2 + s2 * 12);
+    c2.kl = plan.kl2;
+    const dim3 grid(plan.ng, units);
+#define PRR_TG(K2, K3)                                                                                      \
+    if (plan.kpt2 == K2 && plan.kpt3 == K3) {                                                               \
+        topk_groups_kernel<K2, K3><<<grid, 256, 0, stream>>>(tp, c1, c2, arrivals, nparts, plan.gp, plan.ng); \
+        return hipGetLastError();                                                                           \
+    }
+    PRR_TG(8, 1) PRR_TG(8, 2) PRR_TG(8, 4) PRR_TG(8, 8) PRR_TG(8, 16)
+    PRR_TG(16, 1) PRR_TG(16, 2) PRR_TG(16, 4) PRR_TG(16, 8) PRR_TG(16, 16)
+#undef PRR_TG
+    return hipErrorInvalidValue;
 }
 
 // Two-stage predictor shape for rows of nmax blocks: parts of 512 blocks, kl = min(budget, 512)

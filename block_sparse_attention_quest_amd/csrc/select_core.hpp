@@ -501,7 +501,7 @@ __device__ __forceinline__ void topk_body(const TopkParams &p, int u) {
 // order; the unit's last workgroup ranks the candidates of all parts.  Candidate positions then follow
 // the block order, so ties still go to the smaller block index.
 
-constexpr int kMaxTwoStageBlocks = 16384;   // P bitmap of the second stage (LDS)
+constexpr int kMaxTwoStageBlocks = 32768;   // P bitmap of the final candidate ranking (LDS)
 
 // Candidate slots of a two-stage top-K: [units][parts][kl] order keys and block indices, [units][parts]
 // counts (device memory of the caller's workspace).
@@ -541,6 +541,63 @@ __device__ __forceinline__ void local_candidates(const double (&kept)[BPL], int 
             ++off;
         }
     if (threadIdx.x == 0) st_dev_i32(ccnt, (int32_t)total);
+}
+
+// Middle stage of a three-stage top-K (rows with more candidate slots than one ranking holds): the top
+// kout of the candidate slots of gparts consecutive parts (part c holds ccnt[c] of its kl slots), 256
+// threads with KPT slots each (256 KPT >= gparts kl), written as the candidates of one group in slot
+// order, with device-scope stores.  Slot order is block order, so ties still go to the smaller index,
+// and the selection stays exact: a block beaten by fewer than K blocks of the row is beaten by fewer
+// than K of its group's candidates.
+template <int KPT>
+__device__ __forceinline__ void group_candidates(const uint64_t *ckey, const int32_t *cidx, const int32_t *ccnt,
+                                                 int gparts, int kl, int kout, uint64_t *okey, int32_t *oidx,
+                                                 int32_t *ocnt) {
+    constexpr int TPB = 256, W = 4;
+    __shared__ TopkSmem<W> sm;
+    __shared__ int s_cnt[TPB];
+    __shared__ int s_total;
+    const int my_cnt = (int)threadIdx.x < gparts
+                           ? __hip_atomic_load(&ccnt[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+    const int base = threadIdx.x * KPT;
+    const int nslots = gparts * kl;
+    uint64_t key[KPT];
+    int32_t idx[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int pos = base + j;
+        key[j] = pos < nslots ? __hip_atomic_load(&ckey[pos], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+        idx[j] = pos < nslots ? __hip_atomic_load(&cidx[pos], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+    }
+    if ((int)threadIdx.x < gparts) s_cnt[threadIdx.x] = my_cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int t = 0;
+        for (int c = 0; c < gparts; ++c) t += s_cnt[c];
+        s_total = t;
+    }
+    uint32_t valid = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int pos = base + j;
+        const int c = pos / kl, slot = pos - c * kl;
+        if (c < gparts && slot < s_cnt[min(c, gparts - 1)]) valid |= 1u << j;
+        else key[j] = 0ull;
+    }
+    __syncthreads();   // s_total
+    // valid candidate keys are images of finite scores, all above the padding key 0
+    const uint32_t sel = s_total <= kout ? valid : block_topk<KPT, W>(key, nslots, kout, sm) & valid;
+    __syncthreads();
+    uint32_t total;
+    uint32_t off = block_excl_scan((uint32_t)__popc(sel), sm, 1, total);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        if (sel >> j & 1u) {
+            st_dev_u64(&okey[off], key[j]);
+            st_dev_i32(&oidx[off], idx[j]);
+            ++off;
+        }
+    if (threadIdx.x == 0) st_dev_i32(ocnt, (int32_t)total);
 }
 
 // Stage 2: the top-K of unit u over its nparts x kl candidate slots (part c holds ccnt[c] candidates)

@@ -12,7 +12,7 @@ namespace prr {
 // launch from 37.2 to 35.4 us: the candidate selection runs in every scoring workgroup in parallel, and
 // the unit's last workgroup ranks 256 candidates instead of 2048 scores.
 SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean) {
-    SelectSpecPlan pl;
+    SelectSpecPlan pl = {};
     pl.two = false;
     pl.kl = 0;
     pl.kpt = nmax <= 256 ? 1 : nmax <= 512 ? 2 : nmax <= 1024 ? 4 : 0;
@@ -27,19 +27,50 @@ SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean) {
             pl.two = true;
             pl.kl = kl;
             pl.kpt = kpt;
+        } else {
+            // three stages: groups of parts with up to 2048 candidate slots keep their top-K each, and
+            // one ranking of the groups' candidates (up to 4096 slots) follows.  At 32768 blocks and
+            // K = 256 (8 groups of 8 parts) this took the 512K layer step from 96.9 to 73.6 us; groups of
+            // 4096 slots (4 per unit, fewer workgroups) took 76.7 us.
+            const int gp = std::max(1, 2048 / kl);
+            const int ng = (nsx + gp - 1) / gp;
+            const int kl2 = std::min(topk, gp * kl);
+            const long slots2 = (long)std::min(gp, nsx) * kl, slots3 = (long)ng * kl2;
+            const int kpt2 = slots2 <= 2048 ? 8 : 16;
+            const int kpt3 = slots3 <= 256 ? 1 : slots3 <= 512 ? 2 : slots3 <= 1024 ? 4 : slots3 <= 2048 ? 8
+                           : slots3 <= 4096 ? 16 : 0;
+            if (kpt3) {
+                pl.two = true;
+                pl.kl = kl;
+                pl.kpt = 0;
+                pl.three = true;
+                pl.gp = gp;
+                pl.ng = ng;
+                pl.kl2 = kl2;
+                pl.kpt2 = kpt2;
+                pl.kpt3 = kpt3;
+            }
         }
     }
     return pl;
 }
 
 // Candidate slots of the two-stage top-K: [units][nsx][kl] keys (8 bytes) and indices (4), [units][nsx]
-// counts.  The workspace covers both block summaries.
+// counts.  The workspace covers both block summaries.  A three-stage top-K appends the group candidates
+// ([units][ng][kl2] keys and indices, [units][ng] counts) and one group arrival counter per unit.
+static size_t three_stage_bytes(int units, const SelectSpecPlan &pl) {
+    const size_t groups = (size_t)units * pl.ng;
+    return (groups * pl.kl2 * 12 + groups * 4 + 255) / 256 * 256 + ((size_t)units * 4 + 255) / 256 * 256;
+}
+
 static size_t candidate_bytes(int units, int nmax, int topk, bool mean) {
     const SelectSpecPlan pl = select_spec_plan(nmax, topk, mean);
     if (!pl.two) return 0;
     const int bpw = select_spec_score_bpw(mean);
     const size_t parts = (size_t)units * ((nmax + bpw - 1) / bpw);
-    return parts * pl.kl * 12 + parts * 4;
+    size_t bytes = parts * pl.kl * 12 + parts * 4;
+    if (pl.three) bytes = (bytes + 255) / 256 * 256 + three_stage_bytes(units, pl);   // group slots 256-aligned
+    return bytes;
 }
 
 // The carried predictor's work counter sits after the candidates, in a 256-byte slot of its own.

@@ -230,7 +230,8 @@ hipError_t launch_select_spec_t(const KvDesc &kv, const void *q, int hq, const v
                                                                             n_pred);                        \
     } else
 #define PRR_SS_K(DD, MN, PR)                                                                                \
-    PRR_SS(DD, 0, false, MN, PR) PRR_SS(DD, 1, false, MN, PR) PRR_SS(DD, 2, false, MN, PR)                    \
+    PRR_SS(DD, 0, false, MN, PR) PRR_SS(DD, 0, true, MN, PR) PRR_SS(DD, 1, false, MN, PR)                     \
+    PRR_SS(DD, 2, false, MN, PR)                                                                            \
     PRR_SS(DD, 4, false, MN, PR) PRR_SS(DD, 8, false, MN, PR) PRR_SS(DD, 1, true, MN, PR)                     \
     PRR_SS(DD, 2, true, MN, PR) PRR_SS(DD, 4, true, MN, PR) PRR_SS(DD, 8, true, MN, PR)                       \
     PRR_SS(DD, 16, true, MN, PR)
@@ -242,7 +243,16 @@ hipError_t launch_select_spec_t(const KvDesc &kv, const void *q, int hq, const v
 #undef PRR_SS
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (kpt == 0) {
+    if (plan.three) {
+        // the parts' candidates are in place; groups of them, then the unit's ranking
+        const size_t s1 = (size_t)units * nsx * plan.kl;
+        char *cand2 = cbase + (s1 * 12 + (size_t)units * nsx * 4 + 255) / 256 * 256;
+        const size_t s2 = (size_t)units * plan.ng * plan.kl2;
+        uint32_t *garr = (uint32_t *)(cand2 + (s2 * 12 + (size_t)units * plan.ng * 4 + 255) / 256 * 256);
+        e = launch_topk_groups(kv, block, nmax, topk, p_idx, p_cnt, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt, m_cap,
+                               plan, nsx, cbase, cand2, garr, stream);
+        if (e != hipSuccess) return e;
+    } else if (kpt == 0) {
         e = launch_topk(kv, block, nmax, topk, scores, p_idx, p_cnt, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt,
                         m_cap, stream);
         if (e != hipSuccess) return e;

@@ -305,12 +305,14 @@ def test_predictor_trajectory_bit_exact():
 
 
 @pytest.mark.parametrize("nblocks,topk", [(300, 40), (900, 40), (2048, 40), (2049, 40), (4097, 40),
-                                         (8192, 128), (4096, 600)])
+                                         (8192, 128), (4096, 600), (8192, 600), (16384, 300)])
 def test_select_spec_fused_topk_shapes(nblocks, topk):
-    """The fused launch's top-K runs in the last scoring workgroup: over all scores with 1, 2, 4 or 8 keys
-    per thread (units of up to 2048 blocks), and beyond that in two stages (local top-min(K, 512)
+    """The fused launch's top-K runs in the last scoring workgroup: over all scores with 1, 2 or 4 keys
+    per thread (units of up to 1024 blocks), and beyond that in two stages (local top-min(K, 512)
     candidates of every scoring workgroup, then the top-K of the candidates, up to 16 per thread; K = 600
-    caps the local candidates at 512).  Every shape against the separate calls (bit for bit) and the
+    caps the local candidates at 512).  With more than 4096 candidate slots (8192 blocks at K = 600,
+    16384 at K = 300) a third stage follows the launch: groups of parts (up to 2048 candidate slots) keep
+    their top-K, and the unit's last group ranks the groups' candidates.  Every shape against the separate calls (bit for bit) and the
     oracle's scores and sets."""
     lens = [nblocks * 16, nblocks * 16 - 37]
     w = wl.Workload(f"fused_{nblocks}", 2, 8, 2, 64, max(lens), 16, topk, "bf16", seed=900 + nblocks,
