@@ -69,11 +69,13 @@ SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean);
 // The second and third stages of a three-stage top-K (plan.three): nparts parts of kl candidates per
 // unit at cand1 (keys, then indices, then counts, as the fused launch writes them); the group candidates
 // go to cand2 (same layout, ng x kl2 slots per unit), the per-unit group arrival counters to arrivals
-// (zero at rest; the last group of a unit resets its counter).
+// (zero at rest; the last group of a unit resets its counter).  live (a predictor step's, may be null):
+// set to the unit's block count by its last group.
 hipError_t launch_topk_groups(const KvDesc &kv, int block, int nmax, int topk, const int32_t *p_idx,
                               const int32_t *p_cnt, int p_cap, int32_t *a_idx, int32_t *a_cnt, int a_cap,
                               int32_t *m_idx, int32_t *m_cnt, int m_cap, const SelectSpecPlan &plan, int nparts,
-                              void *cand1, void *cand2, uint32_t *arrivals, hipStream_t stream);
+                              void *cand1, void *cand2, uint32_t *arrivals, hipStream_t stream,
+                              int32_t *live = nullptr);
 
 // Offset of the carried predictor's work counter in the prr_select_spec workspace.
 size_t pred_counter_offset(int batch, int hq, int hkv, int d, int block, int cap, int nmax, int topk);

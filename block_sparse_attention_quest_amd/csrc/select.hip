@@ -196,7 +196,8 @@ __global__ __launch_bounds__(256) void predict_parts_kernel(PredictParams p, Top
 // device-scope counter, reset by it) ranks the groups' candidates into A and M.
 template <int KPT2, int KPT3>
 __global__ __launch_bounds__(256) void topk_groups_kernel(TopkParams tp, CandParams c1, CandParams c2,
-                                                          uint32_t *arrivals, int nparts, int gp, int ng) {
+                                                          uint32_t *arrivals, int nparts, int gp, int ng,
+                                                          int32_t *live) {
     __shared__ int s_last;
     const int g = blockIdx.x, u = blockIdx.y;
     const int p0 = g * gp;
@@ -214,9 +215,23 @@ __global__ __launch_bounds__(256) void topk_groups_kernel(TopkParams tp, CandPar
         if (s_last) __hip_atomic_store(&arrivals[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    if (s_last)
+    if (s_last) {
         topk_candidates_body<KPT3>(tp, u, c2.key + (size_t)u * ng * c2.kl, c2.idx + (size_t)u * ng * c2.kl,
                                    c2.cnt + (size_t)u * ng, ng, c2.kl);
+        if (live && threadIdx.x == 0) {   // a predictor step: its blocks are all live from now on
+            const int b = u / tp.hkv;
+            live[u] = min((tp.seq_len[b] + tp.block - 1) / tp.block, tp.nmax);
+        }
+    }
+}
+
+// First stage of a three-stage predictor step: part `part` of unit u updates its blocks' EMA state and
+// keeps its local candidates (predict_part_body); the groups follow in topk_groups_kernel.
+__global__ __launch_bounds__(256) void predict_parts_only_kernel(PredictParams p, CandParams cp, int nparts) {
+    __shared__ TopkSmem<4> sm;
+    const int part = blockIdx.x, u = blockIdx.y;
+    const size_t pi = (size_t)u * nparts + part;
+    predict_part_body(p, u, part, cp.key + pi * cp.kl, cp.idx + pi * cp.kl, cp.cnt + pi, cp.kl, sm);
 }
 
 template <template <int, int> class Launch, typename P>
@@ -341,7 +356,7 @@ hipError_t launch_topk(const KvDesc &kv, int block, int nmax, int topk, const do
 hipError_t launch_topk_groups(const KvDesc &kv, int block, int nmax, int topk, const int32_t *p_idx,
                               const int32_t *p_cnt, int p_cap, int32_t *a_idx, int32_t *a_cnt, int a_cap,
                               int32_t *m_idx, int32_t *m_cnt, int m_cap, const SelectSpecPlan &plan, int nparts,
-                              void *cand1, void *cand2, uint32_t *arrivals, hipStream_t stream) {
+                              void *cand1, void *cand2, uint32_t *arrivals, hipStream_t stream, int32_t *live) {
     TopkParams tp = {};
     tp.seq_len = kv.seq_len;
     tp.p_idx = p_idx;
@@ -371,7 +386,7 @@ hipError_t launch_topk_groups(const KvDesc &kv, int block, int nmax, int topk, c
     const dim3 grid(plan.ng, units);
 #define PRR_TG(K2, K3)                                                                                      \
     if (plan.kpt2 == K2 && plan.kpt3 == K3) {                                                               \
-        topk_groups_kernel<K2, K3><<<grid, 256, 0, stream>>>(tp, c1, c2, arrivals, nparts, plan.gp, plan.ng); \
+        topk_groups_kernel<K2, K3><<<grid, 256, 0, stream>>>(tp, c1, c2, arrivals, nparts, plan.gp, plan.ng, live); \
         return hipGetLastError();                                                                           \
     }
     PRR_TG(8, 1) PRR_TG(8, 2) PRR_TG(8, 4) PRR_TG(8, 8) PRR_TG(8, 16)
@@ -380,29 +395,49 @@ hipError_t launch_topk_groups(const KvDesc &kv, int block, int nmax, int topk, c
     return hipErrorInvalidValue;
 }
 
-// Two-stage predictor shape for rows of nmax blocks: parts of 512 blocks, kl = min(budget, 512)
-// candidates each, ranked with kpt slots per thread (0: one workgroup per unit instead).
+// Part-parallel predictor shape for rows of nmax blocks: parts of 512 blocks, kl = min(budget, 512)
+// candidates each, ranked with kpt slots per thread (two stages), or (kpt = 0, groups.three) through
+// groups of parts first (three stages); neither: one workgroup per unit.
 struct PredictPlan {
     int nparts, kl, kpt;
+    SelectSpecPlan groups;
 };
 
 static PredictPlan predict_plan(int nmax, int budget) {
-    PredictPlan pl{0, 0, 0};
+    PredictPlan pl = {};
     if (nmax <= 2048 || budget <= 0) return pl;   // one workgroup per unit holds the whole row
     pl.nparts = (nmax + 511) / 512;
     pl.kl = std::min(budget, 512);
     const long slots = (long)pl.nparts * pl.kl;
     pl.kpt = slots <= 1024 ? 4 : slots <= 2048 ? 8 : slots <= 4096 ? 16 : 0;
-    if (pl.nparts > 256 || pl.kpt == 0) pl = PredictPlan{0, 0, 0};
+    if (pl.kpt == 0 && pl.nparts <= 256) {
+        // three stages, as the selection's: groups of parts (up to 2048 candidate slots) keep their
+        // top-|P|, then one ranking of the groups' candidates (up to 4096 slots)
+        SelectSpecPlan &g = pl.groups;
+        g.kl = pl.kl;
+        g.gp = std::max(1, 2048 / pl.kl);
+        g.ng = (pl.nparts + g.gp - 1) / g.gp;
+        g.kl2 = std::min(budget, g.gp * pl.kl);
+        const long s2 = (long)std::min(g.gp, pl.nparts) * pl.kl, s3 = (long)g.ng * g.kl2;
+        g.kpt2 = s2 <= 2048 ? 8 : 16;
+        g.kpt3 = s3 <= 256 ? 1 : s3 <= 512 ? 2 : s3 <= 1024 ? 4 : s3 <= 2048 ? 8 : s3 <= 4096 ? 16 : 0;
+        g.three = g.kpt3 != 0;
+    }
+    if (pl.nparts > 256 || (pl.kpt == 0 && !pl.groups.three)) pl = PredictPlan{};
     return pl;
 }
 
 size_t predict_workspace_bytes(int batch, int hkv, int nmax, int budget) {
     const PredictPlan pl = predict_plan(nmax, budget);
-    if (pl.kpt == 0) return 0;
+    if (pl.kpt == 0 && !pl.groups.three) return 0;
     const size_t units = (size_t)batch * hkv;
     const size_t parts = units * pl.nparts;
-    return (units * 4 + 255) / 256 * 256 + parts * pl.kl * 12 + parts * 4;
+    size_t bytes = (units * 4 + 255) / 256 * 256 + parts * pl.kl * 12 + parts * 4;
+    if (pl.groups.three) {
+        const size_t groups = units * pl.groups.ng;
+        bytes = (bytes + 255) / 256 * 256 + groups * pl.groups.kl2 * 12 + groups * 4;
+    }
+    return bytes;
 }
 
 hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batch, int hkv,
@@ -427,7 +462,7 @@ hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batc
     p.gamma = gamma;
     const int units = batch * hkv;
     const PredictPlan pl = predict_plan(nmax, budget);
-    if (!ws || pl.kpt == 0) return dispatch_topk<PredictLaunch>(nmax, units, p, stream);
+    if (!ws || (pl.kpt == 0 && !pl.groups.three)) return dispatch_topk<PredictLaunch>(nmax, units, p, stream);
     TopkParams tp = {};
     tp.seq_len = seq_len;
     tp.a_idx = p_idx;
@@ -447,6 +482,19 @@ hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batc
     cp.cnt = (int32_t *)(cbase + slots * 12);
     cp.kl = pl.kl;
     const dim3 grid(pl.nparts, units);
+    if (pl.groups.three) {
+        predict_parts_only_kernel<<<grid, 256, 0, stream>>>(p, cp, pl.nparts);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const size_t s1bytes = slots * 12 + (size_t)units * pl.nparts * 4;
+        char *cand2 = cbase + (s1bytes + 255) / 256 * 256;
+        KvDesc kv = {};
+        kv.seq_len = seq_len;
+        kv.batch = batch;
+        kv.hkv = hkv;
+        return launch_topk_groups(kv, block, nmax, budget, nullptr, nullptr, 0, p_idx, p_cnt, p_cap, nullptr, nullptr,
+                                  0, pl.groups, pl.nparts, cbase, cand2, arrivals, stream, live);
+    }
     if (pl.kpt == 4) predict_parts_kernel<4><<<grid, 256, 0, stream>>>(p, tp, cp, arrivals, pl.nparts);
     else if (pl.kpt == 8) predict_parts_kernel<8><<<grid, 256, 0, stream>>>(p, tp, cp, arrivals, pl.nparts);
     else predict_parts_kernel<16><<<grid, 256, 0, stream>>>(p, tp, cp, arrivals, pl.nparts);

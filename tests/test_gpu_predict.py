@@ -1,5 +1,6 @@
 """The predictor over long rows: with a workspace, rows of more than 2048 blocks are updated by 512-block
-parts and P_next is ranked from the parts' candidates.  Against the one-workgroup-per-row path and the
+parts and P_next is ranked from the parts' candidates (through groups of parts when the candidate slots
+outnumber one ranking's).  Against the one-workgroup-per-row path and the
 oracle, step by step (births at the first step, several steps, ragged lengths, budgets below and above
 one part's 512 blocks): level, trend, live and P_next bit for bit."""
 import numpy as np
@@ -24,6 +25,9 @@ CASES = [
     ("n8192_k128", 2, 2, 16, [131072, 100000], 128),
     ("n3500_k600", 1, 2, 32, [112000], 600),
     ("n3000_k64_ragged", 3, 1, 16, [48000, 2000, 33000], 64),
+    # more candidate slots than one ranking holds: groups of parts in between (three stages)
+    ("n32768_k256_three", 1, 2, 16, [524288], 256),
+    ("n16384_k300_three_ragged", 2, 1, 16, [262144, 150000], 300),
 ]
 
 
