@@ -202,8 +202,9 @@ prr_status prr_select_spec(const void *q, int32_t num_q_heads, const prr_kv_cach
  * ws (may be NULL): prr_predict_workspace_bytes of caller memory, zeroed once like an attention workspace
  * (every call leaves it ready for the next).  With it, rows of more than 2048 blocks are updated by
  * 512-block parts in parallel and P_next is ranked from the parts' local top-|P| candidates (exact, as
- * in the two-stage top-K); without it one workgroup per (b, kvh) does the whole row.  Same results
- * either way.  A non-NULL ws smaller than the query gives PRR_EWORKSPACE. */
+ * in the two-stage top-K; with more than 4096 candidate slots, groups of parts keep their top-|P| in
+ * between); without it one workgroup per (b, kvh) does the whole row.  Same results either way.  A
+ * non-NULL ws smaller than the query gives PRR_EWORKSPACE. */
 size_t prr_predict_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t max_blocks, int32_t budget);
 
 prr_status prr_predict(const double *scores, const int32_t *seq_len, int32_t batch,
