@@ -2,7 +2,7 @@
 summaries the pages name for selection) against the oracle: the fp32 block means bit for bit, the fp64
 scores bit for bit, A and M exactly; the fused selection + speculative launch in this mode against the
 separate calls.  Sizes span several scoring workgroups (256 blocks each) with a ragged tail, the
-fused launch's single- and two-stage top-K, and sequences of one token and of none."""
+fused launch's single-, two- and three-stage top-K, and sequences of one token and of none."""
 import numpy as np
 import pytest
 import torch
@@ -31,6 +31,9 @@ CASES = [
     # blocks of one scoring workgroup
     ("bf16_d128_s16_two_stage", 1, 8, 2, 128, 16, [40000], "bf16", 300, None),
     ("fp8_d128_s32", 2, 8, 2, 128, 32, [9000, 4100], "fp8", 32, None),
+    # 8192 blocks at K = 600: more candidate slots than one ranking holds, so groups of parts rank
+    # their candidates after the fused launch (three-stage top-K)
+    ("bf16_d64_s16_three_stage", 1, 4, 1, 64, 16, [131072], "bf16", 600, None),
 ]
 
 
