@@ -117,6 +117,11 @@ def test_select_and_predict_argument_errors(lib):
     need = lib.prr_predict_workspace_bytes(2, 8, 8192, 64)
     assert need == 256 + 16 * 16 * 64 * 12 + 16 * 16 * 4
     assert lib.prr_predict_workspace_bytes(2, 8, 2048, 64) == 0   # one workgroup per row: none needed
+    # more than 4096 candidate slots (64 parts x 256): groups of 8 parts in between, 8 groups per unit
+    units = 1 * 8
+    stage1 = 256 + units * 64 * 256 * 12 + units * 64 * 4
+    assert lib.prr_predict_workspace_bytes(1, 8, 32768, 256) == \
+        (stage1 + 255) // 256 * 256 + units * 8 * 256 * 12 + units * 8 * 4
     assert pred(nmax=8192, ws=1, wsb=need - 1) == 3
     assert pred(nmax=40000) == 2
     assert lib.prr_build_meta(ctypes.byref(kv), 64, None, None) == 1
@@ -229,3 +234,24 @@ def test_select_spec_predict_argument_errors(lib):
     assert lib.prr_select_spec_predict(1, 32, ctypes.byref(kv), 1, 0, 64, 64, ctypes.byref(P), scores,
                                        ctypes.byref(A), ctypes.byref(M), 0.1, ctypes.byref(st), 1, need - 1,
                                        ctypes.byref(pred()), None) == 3
+
+
+def test_select_spec_workspace_for_three_stage_rows(lib):
+    """Rows with more candidate slots than one ranking holds (32768 blocks at K = 256: 64 parts of 256
+    candidates) need room for the groups' candidates and a group arrival counter per unit on top of the
+    parts' candidates; shorter rows (8192 blocks: two stages) do not."""
+    long_kv = _kv(max_pages=32768)    # 32768 blocks of 16 tokens
+    short_kv = _kv(max_pages=8192)    # 8192 blocks
+    attn = lambda kv: lib.prr_attn_workspace_bytes(kv.batch, 32, kv.num_kv_heads, kv.head_dim, 16, 256)
+    units = long_kv.batch * long_kv.num_kv_heads
+    parts1 = units * 64
+    stage1 = parts1 * 256 * 12 + parts1 * 4
+    groups = units * 8
+    three = (stage1 + 255) // 256 * 256 + (groups * 256 * 12 + groups * 4 + 255) // 256 * 256 \
+        + (units * 4 + 255) // 256 * 256
+    need_long = lib.prr_select_spec_workspace_bytes(ctypes.byref(long_kv), 32, 16, 256, 256)
+    assert need_long == attn(long_kv) + (three + 255) // 256 * 256 + 256
+    parts2 = units * 16
+    two = parts2 * 256 * 12 + parts2 * 4
+    need_short = lib.prr_select_spec_workspace_bytes(ctypes.byref(short_kv), 32, 16, 256, 256)
+    assert need_short == attn(short_kv) + (two + 255) // 256 * 256 + 256
