@@ -72,6 +72,16 @@ def parse_args():
                     help="comma-separated speculation budgets |P| = delta K to time as extra layer steps "
                          "(e.g. 1,1.25,1.5,2); empty: none")
     ap.add_argument("--delta-steps", type=int, default=24, help="decode steps timed per delta")
+    ap.add_argument("--budget-profile", default="",
+                    help="comma-separated context lengths (tokens): profile selection and speculative-attention "
+                         "latency over them and --budget-deltas, fit the budget table and report its choices "
+                         "(e.g. 4096,8192,16384,32768,65536); empty: none")
+    ap.add_argument("--budget-deltas", default="0.25,0.5,0.75,1,1.5,2,3,4",
+                    help="budget ratios |P| = delta K profiled by --budget-profile")
+    ap.add_argument("--budget-degree", type=int, default=2, help="degree of the budget table's regression")
+    ap.add_argument("--budget-check", default="131072,262144",
+                    help="off-grid context lengths where the table's estimates are compared with measurements")
+    ap.add_argument("--budget-reps", type=int, default=20, help="timed runs per profiled point")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size (HBM counter calibration under rocprofv3)")
     return ap.parse_args()
@@ -352,6 +362,105 @@ def delta_sweep(args, w, inp, kv, meta, flush, ev):
         del L
         log(f"[bench] delta {d}: {out[-1]}")
     return out
+
+
+def _budget_point(w, T, deltas, reps, flush, ev, base_us, seed):
+    """Median selection latency and speculative-attention latency at each delta for the workload's shape
+    at T tokens (each run after the cache flush, event time minus the empty pair).  P at delta is a
+    seeded random set of round(delta K) distinct blocks per (sequence, kv head)."""
+    import numpy as np
+    import torch
+
+    from block_sparse_attention_quest_amd import binding as bd
+    from block_sparse_attention_quest_amd import workloads as wl
+
+    wt = wl.scaled(w, context=T, steps=2, append_tokens=0)
+    inp = wl.make_inputs(wt, "cuda")
+    kv = bd.KVCache(inp.k_cache, inp.v_cache, inp.page_table, inp.seq_len)
+    meta = bd.build_meta(kv, wt.block)
+    B, H, N = wt.batch, wt.num_kv_heads, bd.max_blocks(kv, wt.block)
+    budgets = [max(1, min(N, int(round(d * wt.topk)))) for d in deltas]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    order = torch.argsort(torch.rand((B, H, N), generator=gen, device="cuda"), dim=-1).to(torch.int32)
+    sets = []
+    for nb in budgets:
+        idx = torch.sort(order[..., :nb], dim=-1).values.contiguous()
+        sets.append(bd.BlockSet(idx, torch.full((B, H), nb, dtype=torch.int32, device="cuda")))
+    ws = bd.workspace_for(kv, wt.num_q_heads, wt.block, max(budgets))
+    state = bd.AttnState.empty(B, wt.num_q_heads, wt.head_dim, "cuda")
+    scores = torch.zeros((B, H, N), dtype=torch.float64, device="cuda")
+    A = bd.BlockSet.empty(B, H, wt.topk, "cuda")
+    M = bd.BlockSet.empty(B, H, wt.topk, "cuda")
+    q = inp.q[0]
+    P1 = sets[min(range(len(deltas)), key=lambda j: abs(deltas[j] - 1.0))]
+    crit = torch.cuda.current_stream()
+
+    def timed(fn):
+        ev.reserve(2 * reps)
+        pairs = []
+        for _ in range(reps):
+            flush()
+            e0, e1 = ev(), ev()
+            e0.record(crit)
+            fn()
+            e1.record(crit)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) * 1e3 - base_us for a, b in pairs]))
+
+    for P in sets:   # warm every shape once
+        bd.spec_attn(q, kv, wt.block, P, wt.scale, out=state, ws=ws)
+    bd.select(q, kv, meta, wt.block, wt.topk, P=P1, scores=scores, A=A, M=M)
+    t_sel = timed(lambda: bd.select(q, kv, meta, wt.block, wt.topk, P=P1, scores=scores, A=A, M=M, stream=crit))
+    t_spec = [timed(lambda P=P: bd.spec_attn(q, kv, wt.block, P, wt.scale, out=state, ws=ws, stream=crit))
+              for P in sets]
+    del inp, kv, meta, order, sets, ws, state, scores
+    torch.cuda.empty_cache()
+    return t_sel, t_spec, budgets
+
+
+def budget_profile(args, w, flush, ev, base_us):
+    """The pages' critical-path-aware budget (§4.4, A.6): profile selection and speculative-attention
+    latency over context lengths and budget ratios, fit the library's budget table, and report the
+    largest delta whose speculative pass fits the selection window at each profiled length and at
+    off-grid lengths (where the estimates are also compared with measurements)."""
+    from block_sparse_attention_quest_amd import binding as bd
+
+    ctx = [int(x) for x in args.budget_profile.split(",") if x.strip()]
+    deltas = [float(x) for x in args.budget_deltas.split(",") if x.strip()]
+    check = [int(x) for x in args.budget_check.split(",") if x.strip()]
+    sel, spec = [], [[] for _ in deltas]
+    for i, T in enumerate(ctx):
+        t_sel, t_spec, budgets = _budget_point(w, T, deltas, args.budget_reps, flush, ev, base_us, seed=100 + i)
+        sel.append(t_sel)
+        for j, t in enumerate(t_spec):
+            spec[j].append(t)
+        log(f"[bench] budget profile T={T}: select {t_sel:.2f} us, spec {[round(t, 2) for t in t_spec]} us")
+    tab = bd.BudgetTable([float(T) for T in ctx], sel, deltas, spec, args.budget_degree)
+
+    def pick(T):
+        j, est = tab.choose(float(T))
+        return {"context": T, "delta": deltas[j] if j >= 0 else None, "choice": j,
+                "est_us_select": round(float(est[0]), 2),
+                "est_us_spec": [round(float(e), 2) for e in est[1:]]}
+
+    choices = [pick(T) for T in ctx]
+    checks = []
+    for i, T in enumerate(check):
+        c = pick(T)
+        t_sel, t_spec, _ = _budget_point(w, T, deltas, args.budget_reps, flush, ev, base_us, seed=200 + i)
+        c["measured_us_select"] = round(t_sel, 2)
+        c["measured_us_spec"] = [round(t, 2) for t in t_spec]
+        fits = [j for j, t in enumerate(t_spec) if t <= t_sel]
+        c["measured_choice"] = max(fits) if fits else -1
+        checks.append(c)
+        log(f"[bench] budget check T={T}: {c}")
+    return {"ctx": ctx, "deltas": deltas, "budget_blocks_at_K": [max(1, int(round(d * w.topk))) for d in deltas],
+            "us_select": [round(t, 2) for t in sel], "us_spec": [[round(t, 2) for t in r] for r in spec],
+            "degree": args.budget_degree, "coef": tab.coef.tolist(), "choices": choices, "checks": checks,
+            "note": "kernels timed alone, after the cache flush, minus the empty event pair; selection = "
+                    "prr_select (scores, top-K, M), speculation = prr_spec_attn over round(delta K) blocks"}
 
 
 def measure_stack(args, w, layer0, inp0, flush, ev):
@@ -715,6 +824,8 @@ def main():
             args.delta_sweep = ""
     if args.delta_sweep:
         result["delta_sweep"] = delta_sweep(args, w, inp, kv, layer.meta, flush, ev)
+    if args.budget_profile:
+        result["budget"] = budget_profile(args, w, flush, ev, base_us)
     if args.stack > 1 and not args.append:
         result["stack"] = measure_stack(args, w, layer, inp, flush, ev)
     if not args.no_cpu_baseline:

@@ -26,7 +26,8 @@ EXPORTS = (
     "prr_select", "prr_select_spec_workspace_bytes", "prr_select_spec", "prr_select_spec_predict", "prr_predict_workspace_bytes",
     "prr_predict",
     "prr_spec_attn",
-    "prr_repair", "prr_calibrate_workspace_bytes", "prr_calibrate", "prr_strerror",
+    "prr_repair", "prr_calibrate_workspace_bytes", "prr_calibrate", "prr_budget_fit", "prr_budget_choose",
+    "prr_strerror",
 )
 
 
@@ -91,6 +92,8 @@ _SIGS = {
                                   _P(AttnStateStruct), _VP, _VP, _SZ, _VP]),
     "prr_calibrate_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "prr_calibrate": (ctypes.c_int, [_VP, _I32, _I32, _I32, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]),
+    "prr_budget_fit": (ctypes.c_int, [_VP, _I32, _VP, _VP, _I32, _VP, _I32, _VP]),
+    "prr_budget_choose": (ctypes.c_int, [_VP, _I32, _VP, _VP, _I32, _VP, _I32, _VP, _D, _VP, _VP]),
     "prr_strerror": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -485,3 +488,37 @@ def calibrate(scores: torch.Tensor, topk: int, grid: Optional[torch.Tensor] = No
                            ws.nbytes, _stream(stream))
     _check(st, "prr_calibrate")
     return H, best
+
+
+class BudgetTable:
+    """The speculation-budget table ([paper] §4.4, A.6): profiled selection and speculative-attention
+    latencies over context lengths `ctx` and budget ratios `deltas` (t_spec[j][i] at deltas[j], ctx[i]),
+    with the library's polynomial fit of `degree`.  choose(T) returns (index of the largest delta whose
+    speculative latency fits the selection window at T tokens, or -1; the estimates).  Host arrays only:
+    no GPU work."""
+
+    def __init__(self, ctx, t_select, deltas, t_spec, degree: int = 2):
+        import numpy as np
+
+        self.ctx = np.ascontiguousarray(ctx, dtype=np.float64)
+        self.t_select = np.ascontiguousarray(t_select, dtype=np.float64)
+        self.deltas = np.ascontiguousarray(deltas, dtype=np.float64)
+        self.t_spec = np.ascontiguousarray(t_spec, dtype=np.float64)
+        if self.t_spec.shape != (len(self.deltas), len(self.ctx)) or self.t_select.shape != self.ctx.shape:
+            raise ValueError("t_spec must be [len(deltas)][len(ctx)] and t_select [len(ctx)]")
+        self.degree = int(degree)
+        self.coef = np.zeros((1 + len(self.deltas), self.degree + 1), dtype=np.float64)
+        _check(load_library().prr_budget_fit(*self._table(), self.coef.ctypes.data), "prr_budget_fit")
+
+    def _table(self):
+        return (self.ctx.ctypes.data, len(self.ctx), self.t_select.ctypes.data, self.deltas.ctypes.data,
+                len(self.deltas), self.t_spec.ctypes.data, self.degree)
+
+    def choose(self, context: float):
+        import numpy as np
+
+        est = np.zeros(1 + len(self.deltas), dtype=np.float64)
+        choice = ctypes.c_int32(0)
+        _check(load_library().prr_budget_choose(*self._table(), self.coef.ctypes.data, float(context),
+                                                ctypes.addressof(choice), est.ctypes.data), "prr_budget_choose")
+        return int(choice.value), est

@@ -30,6 +30,7 @@ SOURCES = {
     "step_fp8.hip": [],
     "append.hip": [],
     "check.hip": [],
+    "budget.cpp": ["-ffp-contract=off"],
     "prr_api.cpp": ["-x", "hip"],
 }
 

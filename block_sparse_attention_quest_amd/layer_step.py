@@ -264,3 +264,13 @@ class PRRStack:
         self.pending, self.pending_owner = None, -1
         for layer in self.layers:
             layer.reset()
+
+
+def speculation_budget(table: bd.BudgetTable, context: int, topk: int) -> int:
+    """|P| in blocks for a layer at `context` tokens ([paper] §4.4; Eq. 1, |P| <= delta |A|): round(delta K)
+    for the table's largest delta whose speculative pass fits the selection window.  When no profiled
+    delta fits, the smallest one is taken (speculation over fewer blocks leaves more to repair, which is
+    on the critical path as well), and never fewer than one block."""
+    j, _ = table.choose(float(context))
+    delta = float(table.deltas[j if j >= 0 else 0])
+    return max(1, int(round(delta * topk)))

@@ -283,6 +283,35 @@ prr_status prr_calibrate(const float *scores, int32_t rows, int32_t blocks, int3
                          int32_t n_candidates, double *H, int32_t *best, void *ws, size_t ws_bytes,
                          hipStream_t stream);
 
+/* Critical-path-aware speculation budget ([paper] §4.4, A.6; Eq. 1: |P| <= delta |A|).  Host code:
+ * every pointer is HOST memory, nothing touches the GPU, and both calls are pure functions of their
+ * arguments (thread-safe).  The caller profiles once, per configuration, the selection latency and the
+ * speculative-attention latency (any one time unit) over a grid of context lengths and budget ratios:
+ *   ctx      [n_ctx]             context lengths in tokens, strictly ascending, > 0
+ *   t_select [n_ctx]             selection latency at each length
+ *   deltas   [n_delta]           budget ratios, strictly ascending, >= 0
+ *   t_spec   [n_delta][n_ctx]    speculative-attention latency with |P| = delta K at each length
+ * 1 <= n_ctx, n_delta <= PRR_BUDGET_MAX_POINTS; 0 <= degree <= min(PRR_BUDGET_MAX_DEGREE, n_ctx - 1);
+ * every value finite.  Violations return PRR_EINVAL and write nothing.
+ *
+ * prr_budget_fit: ordinary least-squares polynomials of `degree` in x = T / ctx[n_ctx - 1], one for the
+ * selection latency and one per delta (the pages estimate lengths outside the grid by polynomial
+ * regression).  coef [1 + n_delta][degree + 1]: row 0 selection, row 1 + j delta j; coef[r][k]
+ * multiplies x^k.  Solved by Householder QR in float64.
+ *
+ * prr_budget_choose: the estimates at `context` tokens (> 0): the table row itself when `context` equals
+ * a profiled length, else the polynomials of prr_budget_fit (coef from the same table and degree).
+ * *choice = the largest j with est_spec[j] <= est_select (the largest delta whose speculative pass fits
+ * the selection window), or -1 when none fits.  est [1 + n_delta] (nullable) receives est_select then
+ * est_spec[0 .. n_delta). */
+#define PRR_BUDGET_MAX_POINTS 64
+#define PRR_BUDGET_MAX_DEGREE 4
+prr_status prr_budget_fit(const double *ctx, int32_t n_ctx, const double *t_select, const double *deltas,
+                          int32_t n_delta, const double *t_spec, int32_t degree, double *coef);
+prr_status prr_budget_choose(const double *ctx, int32_t n_ctx, const double *t_select, const double *deltas,
+                             int32_t n_delta, const double *t_spec, int32_t degree, const double *coef,
+                             double context, int32_t *choice, double *est);
+
 /* Human-readable name of a status code (static string). */
 const char *prr_strerror(prr_status status);
 

@@ -425,3 +425,43 @@ def calibrate(IS: np.ndarray, k: int, grid: np.ndarray = None):
         H[j] = total / (T - 1) if T > 1 else 0.0
     best = int(np.argmax(H))   # first maximum in grid order
     return H, best
+
+
+# --------------------------------------------------------------------------------------------------
+# Critical-path-aware speculation budget ([paper] §4.4, A.6; [blog] Eq. (1))
+# --------------------------------------------------------------------------------------------------
+
+
+def budget_fit(ctx, t_select, deltas, t_spec, degree: int) -> np.ndarray:
+    """Polynomial regression of the profiled latencies over context length ([paper] A.6: lengths outside
+    the profiled grid are estimated by polynomial regression).  Reading (the pages name no degree, basis
+    or fitting criterion): ordinary least squares of `degree` in x = T / max(ctx), one polynomial for
+    the selection latency and one per budget ratio for the speculative latency (t_spec[j][i] at
+    deltas[j], ctx[i]).  Returns coef [1 + len(deltas)][degree + 1], coef[r][k] multiplying x^k, row 0
+    selection.  The least-squares solve is numpy.linalg.lstsq."""
+    ctx = np.asarray(ctx, dtype=np.float64)
+    x = ctx / ctx[-1]
+    V = np.vander(x, degree + 1, increasing=True)
+    rows = [np.asarray(t_select, dtype=np.float64)] + [np.asarray(r, dtype=np.float64) for r in t_spec]
+    return np.array([np.linalg.lstsq(V, y, rcond=None)[0] for y in rows])
+
+
+def budget_estimates(ctx, t_select, t_spec, coef: np.ndarray, context: float) -> np.ndarray:
+    """Latency estimates at `context` tokens ([paper] §4.4: the profiles are a table indexed by context
+    length; A.6: regression for lengths outside it): the profiled row itself at a profiled length, else
+    sum_k coef[r][k] x^k with x = context / max(ctx).  Returns [est_select, est_spec(delta_0), ...]."""
+    ctx = [float(c) for c in ctx]
+    if float(context) in ctx:
+        i = ctx.index(float(context))
+        return np.array([float(t_select[i])] + [float(r[i]) for r in t_spec])
+    x = float(context) / ctx[-1]
+    return np.array([sum(c * x ** k for k, c in enumerate(row)) for row in coef])
+
+
+def budget_choose(ctx, t_select, deltas, t_spec, coef: np.ndarray, context: float):
+    """The largest profiled budget ratio whose speculative latency fits the selection window at
+    `context` tokens ([paper] §4.4: speculation must not outlast selection, else it extends the critical
+    path).  Reading: 'fits' is est_spec <= est_select; -1 when no ratio fits.  Returns (index, estimates)."""
+    est = budget_estimates(ctx, t_select, t_spec, coef, context)
+    fits = [j for j in range(len(deltas)) if est[1 + j] <= est[0]]
+    return (max(fits) if fits else -1), est
