@@ -75,11 +75,14 @@ def parse_args():
     ap.add_argument("--budget-profile", default="",
                     help="comma-separated context lengths (tokens): profile selection and speculative-attention "
                          "latency over them and --budget-deltas, fit the budget table and report its choices "
-                         "(e.g. 4096,8192,16384,32768,65536); empty: none")
+                         "(e.g. 16384,32768,65536,131072; every length must hold the largest budget, max(delta) K blocks); "
+                         "empty: none")
     ap.add_argument("--budget-deltas", default="0.25,0.5,0.75,1,1.5,2,3,4",
                     help="budget ratios |P| = delta K profiled by --budget-profile")
-    ap.add_argument("--budget-degree", type=int, default=2, help="degree of the budget table's regression")
-    ap.add_argument("--budget-check", default="131072,262144",
+    ap.add_argument("--budget-degree", type=int, default=1,
+                    help="degree of the budget table's regression (selection reads metadata in proportion to the "
+                         "context and speculation is flat in it, so lines extrapolate best)")
+    ap.add_argument("--budget-check", default="98304,262144,524288",
                     help="off-grid context lengths where the table's estimates are compared with measurements")
     ap.add_argument("--budget-reps", type=int, default=20, help="timed runs per profiled point")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -423,13 +426,18 @@ def _budget_point(w, T, deltas, reps, flush, ev, base_us, seed):
 def budget_profile(args, w, flush, ev, base_us):
     """The pages' critical-path-aware budget (§4.4, A.6): profile selection and speculative-attention
     latency over context lengths and budget ratios, fit the library's budget table, and report the
-    largest delta whose speculative pass fits the selection window at each profiled length and at
+    largest delta whose speculative pass ends no later than selection at each profiled length and at
     off-grid lengths (where the estimates are also compared with measurements)."""
     from block_sparse_attention_quest_amd import binding as bd
 
     ctx = [int(x) for x in args.budget_profile.split(",") if x.strip()]
     deltas = [float(x) for x in args.budget_deltas.split(",") if x.strip()]
     check = [int(x) for x in args.budget_check.split(",") if x.strip()]
+    short = [T for T in ctx + check if -(-T // w.block) < int(round(max(deltas) * w.topk))]
+    if short:
+        # a budget larger than the context is clipped to every block: that point measures no delta
+        raise ValueError(f"context lengths {short} hold fewer than max(delta) K = "
+                         f"{int(round(max(deltas) * w.topk))} blocks of {w.block} tokens")
     sel, spec = [], [[] for _ in deltas]
     for i, T in enumerate(ctx):
         t_sel, t_spec, budgets = _budget_point(w, T, deltas, args.budget_reps, flush, ev, base_us, seed=100 + i)

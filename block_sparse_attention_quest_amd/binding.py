@@ -494,7 +494,7 @@ class BudgetTable:
     """The speculation-budget table ([paper] §4.4, A.6): profiled selection and speculative-attention
     latencies over context lengths `ctx` and budget ratios `deltas` (t_spec[j][i] at deltas[j], ctx[i]),
     with the library's polynomial fit of `degree`.  choose(T) returns (index of the largest delta whose
-    speculative latency fits the selection window at T tokens, or -1; the estimates).  Host arrays only:
+    speculative latency is at most the selection latency at T tokens, or -1; the estimates).  Host arrays only:
     no GPU work."""
 
     def __init__(self, ctx, t_select, deltas, t_spec, degree: int = 2):

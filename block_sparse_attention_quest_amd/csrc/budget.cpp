@@ -9,8 +9,8 @@
 // lengthens the speculative pass; the pages keep that pass inside the selection window.  They profile,
 // once per configuration, the selection latency and the speculative-attention latency over a grid of
 // context lengths and budget ratios, keep the results in a table indexed by context length, estimate
-// lengths outside the grid by polynomial regression, and at run time take the largest delta whose
-// speculative latency fits the selection window.
+// lengths outside the grid by polynomial regression, and at run time pick the biggest ratio for which
+// speculation ends no later than selection.
 //
 // Readings where the pages leave a step open:
 //   * the regression is an ordinary least-squares polynomial in x = T / T_max (T_max the longest
@@ -18,7 +18,7 @@
 //     selection latency and one per profiled delta for the speculative latency, of a degree the caller
 //     picks (the pages name none);
 //   * a length in the grid reads the table itself; any other length reads the polynomials;
-//   * "fits within the window" is est_spec(delta) <= est_select; when no profiled delta fits, the choice
+//   * a ratio qualifies when est_spec(delta) <= est_select; when no profiled delta does, the choice
 //     is -1 and the caller decides (a grid that holds delta = 0 always has a fitting entry).
 //
 // The fit solves the least-squares problem by Householder QR of the Vandermonde matrix (no normal

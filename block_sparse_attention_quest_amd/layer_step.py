@@ -268,7 +268,7 @@ class PRRStack:
 
 def speculation_budget(table: bd.BudgetTable, context: int, topk: int) -> int:
     """|P| in blocks for a layer at `context` tokens ([paper] §4.4; Eq. 1, |P| <= delta |A|): round(delta K)
-    for the table's largest delta whose speculative pass fits the selection window.  When no profiled
+    for the table's largest delta whose speculative pass ends no later than selection.  When no profiled
     delta fits, the smallest one is taken (speculation over fewer blocks leaves more to repair, which is
     on the critical path as well), and never fewer than one block."""
     j, _ = table.choose(float(context))

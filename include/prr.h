@@ -301,8 +301,8 @@ prr_status prr_calibrate(const float *scores, int32_t rows, int32_t blocks, int3
  *
  * prr_budget_choose: the estimates at `context` tokens (> 0): the table row itself when `context` equals
  * a profiled length, else the polynomials of prr_budget_fit (coef from the same table and degree).
- * *choice = the largest j with est_spec[j] <= est_select (the largest delta whose speculative pass fits
- * the selection window), or -1 when none fits.  est [1 + n_delta] (nullable) receives est_select then
+ * *choice = the largest j with est_spec[j] <= est_select (the largest delta whose speculative pass ends
+ * no later than selection), or -1 when there is none.  est [1 + n_delta] (nullable) receives est_select then
  * est_spec[0 .. n_delta). */
 #define PRR_BUDGET_MAX_POINTS 64
 #define PRR_BUDGET_MAX_DEGREE 4

@@ -459,7 +459,7 @@ def budget_estimates(ctx, t_select, t_spec, coef: np.ndarray, context: float) ->
 
 
 def budget_choose(ctx, t_select, deltas, t_spec, coef: np.ndarray, context: float):
-    """The largest profiled budget ratio whose speculative latency fits the selection window at
+    """The largest profiled budget ratio whose speculative latency is at most the selection latency at
     `context` tokens ([paper] §4.4: speculation must not outlast selection, else it extends the critical
     path).  Reading: 'fits' is est_spec <= est_select; -1 when no ratio fits.  Returns (index, estimates)."""
     est = budget_estimates(ctx, t_select, t_spec, coef, context)
