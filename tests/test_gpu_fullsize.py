@@ -111,12 +111,14 @@ def test_llama3_8b_layer_32k():
         _check_unit_attention(state, out, inp, 0, h, 0, set(P[0][h]) | set(m_h.tolist()), "repair")
 
 
-def _trajectory(w, steps, units, ema):
+def _trajectory(w, steps, units, ema, budget=None):
     """Run `steps` layer steps through PRRLayer (the single-stream step bench.py times) and check sampled
-    units against the oracle's select / spec / repair / predict, step by step."""
+    units against the oracle's select / spec / repair / predict, step by step.  budget: |P| in blocks
+    (default K)."""
+    budget = w.topk if budget is None else budget
     inp = wl.make_inputs(w, "cuda")
     kv = device_kv(inp)
-    layer = PRRLayer(kv, w.num_q_heads, w.block, w.topk, w.topk, ema=ema, scale=w.scale)
+    layer = PRRLayer(kv, w.num_q_heads, w.block, w.topk, budget, ema=ema, scale=w.scale)
     alpha, beta, gamma = ema
     metas = {u: unit_meta(_kv_view(inp, *u), w.block) for u in units}
     ost = {u: (np.zeros(0), np.zeros(0), 0, np.zeros(0, dtype=np.int64)) for u in units}
@@ -133,7 +135,7 @@ def _trajectory(w, steps, units, ema):
                                             P_before, layer.M, metas[(b, h)])
             m_h = orc.set_minus(a, P)
             _check_unit_attention(layer.state, out, inp, b, h, t, set(P.tolist()) | set(m_h.tolist()), f"step {t}")
-            lv, tr, live, P = orc.predict_step(lv, tr, live, s, alpha, beta, gamma, w.topk)
+            lv, tr, live, P = orc.predict_step(lv, tr, live, s, alpha, beta, gamma, budget)
             nb = w.blocks_of(b)
             assert np.array_equal(lv_dev[b, h, :nb], lv) and np.array_equal(tr_dev[b, h, :nb], tr), (t, b, h)
             assert P_after[b][h] == list(P), (t, b, h)
@@ -143,6 +145,20 @@ def _trajectory(w, steps, units, ema):
 
 def test_ctx128k_batch8_trajectory():
     _trajectory(wl.C3, 4, [(0, 0), (3, 5), (5, 2), (7, 7)], wl.C3.ema)
+
+
+@pytest.mark.parametrize("select_us,want_delta", [(15.0, 0.5), (30.0, 2.0)])
+def test_ctx128k_batch8_trajectory_with_planned_budget(select_us, want_delta):
+    """|P| sized by the speculation-budget planner: a latency table (speculation 10 us + 9 us per unit of
+    delta, selection flat at `select_us`) picks delta at 128K, and the layer runs with |P| = delta K."""
+    from block_sparse_attention_quest_amd.layer_step import speculation_budget
+
+    deltas = [0.25, 0.5, 1.0, 2.0, 3.0]
+    ctx = [16384.0, 65536.0, 131072.0]
+    tab = bd.BudgetTable(ctx, [select_us] * 3, deltas, [[10.0 + 9.0 * d] * 3 for d in deltas], 1)
+    budget = speculation_budget(tab, wl.C3.context, wl.C3.topk)
+    assert budget == int(round(want_delta * wl.C3.topk))
+    _trajectory(wl.C3, 3, [(2, 3), (6, 0)], wl.C3.ema, budget)
 
 
 def test_ctx128k_batch8_fp8_trajectory():
