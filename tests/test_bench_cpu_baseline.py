@@ -39,3 +39,21 @@ def test_cpu_baseline_without_pool_is_the_one_thread_leg():
     inp = wl.make_inputs(w, "cpu")
     r = bench.cpu_baseline(inp, w, 2, 2)
     assert r["cores"] == 1 and r["value"] == r["value_one_thread"]
+
+
+def test_budget_profile_rejects_lengths_that_clip_the_largest_budget():
+    """A profiled length must hold max(delta) K blocks, else that point measures a clipped budget; the
+    check runs before any GPU work."""
+    import argparse
+
+    import pytest
+
+    bench = _bench()
+    w = wl.C3   # K = 64 blocks of 64 tokens
+    args = argparse.Namespace(budget_profile="8192,65536", budget_deltas="0.5,1,4", budget_check="",
+                              budget_degree=1, budget_reps=1)
+    with pytest.raises(ValueError, match=r"\[8192\]"):   # 128 blocks < 4 x 64
+        bench.budget_profile(args, w, None, None, 0.0)
+    args.budget_profile, args.budget_check = "16384,65536", "12288"
+    with pytest.raises(ValueError, match=r"\[12288\]"):
+        bench.budget_profile(args, w, None, None, 0.0)
