@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 import test_oracle_attention as ta
+import test_oracle_budget as tb
 import test_oracle_ema as te
 import test_oracle_fp8 as tf
 import test_oracle_mean as tm
@@ -157,6 +158,50 @@ def fp8_no_nan(codes):
     return sign * np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
 
 
+def budget_fit_unscaled_x(ctx, t_select, deltas, t_spec, degree):
+    V = np.vander(np.asarray(ctx, dtype=np.float64), degree + 1, increasing=True)
+    rows = [np.asarray(t_select, dtype=np.float64)] + [np.asarray(r, dtype=np.float64) for r in t_spec]
+    return np.array([np.linalg.lstsq(V, y, rcond=None)[0] for y in rows])
+
+
+def budget_fit_drops_top_power(ctx, t_select, deltas, t_spec, degree):
+    c = _orig["budget_fit"](ctx, t_select, deltas, t_spec, max(0, degree - 1))
+    return np.concatenate([c, np.zeros((c.shape[0], degree + 1 - c.shape[1]))], axis=1)
+
+
+def budget_estimates_never_read_table(ctx, t_select, t_spec, coef, context):
+    x = float(context) / float(ctx[-1])
+    return np.array([sum(c * x ** k for k, c in enumerate(row)) for row in coef])
+
+
+def budget_estimates_scaled_by_shortest(ctx, t_select, t_spec, coef, context):
+    if float(context) in [float(c) for c in ctx]:
+        return _orig["budget_estimates"](ctx, t_select, t_spec, coef, context)
+    x = float(context) / float(ctx[0])
+    return np.array([sum(c * x ** k for k, c in enumerate(row)) for row in coef])
+
+
+def budget_choose_strict(ctx, t_select, deltas, t_spec, coef, context):
+    est = orc.budget_estimates(ctx, t_select, t_spec, coef, context)
+    fits = [j for j in range(len(deltas)) if est[1 + j] < est[0]]
+    return (max(fits) if fits else -1), est
+
+
+def budget_choose_smallest(ctx, t_select, deltas, t_spec, coef, context):
+    est = orc.budget_estimates(ctx, t_select, t_spec, coef, context)
+    fits = [j for j in range(len(deltas)) if est[1 + j] <= est[0]]
+    return (min(fits) if fits else -1), est
+
+
+def _budget_checks():
+    hand = [(tb.test_choice_on_the_hand_table, (c, w)) for c, w in [(4096.0, 1), (8192.0, 2), (16384.0, 2)]]
+    return [(tb.test_fit_recovers_an_exact_polynomial, (2,)), (tb.test_degree_zero_is_the_mean_and_degree_one_the_textbook_line, ()),
+            (tb.test_residual_is_orthogonal_to_every_column, (2,)), (tb.test_as_many_points_as_coefficients_interpolates, ()),
+            *hand, (tb.test_off_grid_length_reads_the_line, ()),
+            (tb.test_no_fitting_ratio_gives_minus_one_and_delta_zero_always_fits, ()),
+            (tb.test_longer_selection_never_lowers_the_choice, ())]
+
+
 def _fp8_checks():
     return [(tf.test_decode_matches_torch_float8_e4m3fn, ()), (tf.test_known_codes, ()),
             (tf.test_positive_codes_increase_and_negatives_mirror, ())]
@@ -207,6 +252,12 @@ MUTATIONS = [
     ("fp8_e4m3_decode", fp8_bias_8, _fp8_checks),
     ("fp8_e4m3_decode", fp8_subnormals_flushed, _fp8_checks),
     ("fp8_e4m3_decode", fp8_no_nan, _fp8_checks),
+    ("budget_fit", budget_fit_unscaled_x, _budget_checks),
+    ("budget_fit", budget_fit_drops_top_power, _budget_checks),
+    ("budget_estimates", budget_estimates_never_read_table, _budget_checks),
+    ("budget_estimates", budget_estimates_scaled_by_shortest, _budget_checks),
+    ("budget_choose", budget_choose_strict, _budget_checks),
+    ("budget_choose", budget_choose_smallest, _budget_checks),
 ]
 
 
@@ -217,4 +268,5 @@ def test_pins_catch_planted_mistake(monkeypatch, target, mutant, checks):
 
 
 def test_unmutated_oracle_passes_the_same_checks():
-    assert not _fails(*_attention_checks(), *_select_checks(), *_ema_checks(), *_mean_checks(), *_fp8_checks())
+    assert not _fails(*_attention_checks(), *_select_checks(), *_ema_checks(), *_mean_checks(), *_fp8_checks(),
+                      *_budget_checks())
