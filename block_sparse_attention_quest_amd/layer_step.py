@@ -77,8 +77,11 @@ class PRRLayer:
     name for selection).  The metadata kept in ``meta`` is the one the mode reads."""
 
     def __init__(self, kv: bd.KVCache, num_q_heads: int, block: int, topk: int, budget: int,
-                 ema=(0.6, 0.3, 0.5), scale: Optional[float] = None, score_mode: str = "quest"):
+                 ema=(0.6, 0.3, 0.5), scale: Optional[float] = None, score_mode: str = "quest",
+                 max_budget: Optional[int] = None):
         dev = kv.k.device
+        # |P| may later change (set_budget) up to max_budget: sets and workspaces are sized for it
+        self.max_budget = max(1, budget, max_budget or 0)
         self.kv = kv
         self.hq = num_q_heads
         self.block = block
@@ -96,17 +99,24 @@ class PRRLayer:
         self.level = torch.zeros_like(self.scores)
         self.trend = torch.zeros_like(self.scores)
         self.live = torch.zeros((B, H), dtype=torch.int32, device=dev)
-        self.P = [bd.BlockSet.empty(B, H, max(1, budget), dev), bd.BlockSet.empty(B, H, max(1, budget), dev)]
+        self.P = [bd.BlockSet.empty(B, H, self.max_budget, dev), bd.BlockSet.empty(B, H, self.max_budget, dev)]
         self.cur = 0
         self.A = bd.BlockSet.empty(B, H, max(1, topk), dev)
         self.M = bd.BlockSet.empty(B, H, max(1, topk), dev)
         self.state = bd.AttnState.empty(B, num_q_heads, d, dev)
         self.out = torch.zeros((B, num_q_heads, d), dtype=torch.float32, device=dev)
-        self.ws_spec = bd.select_spec_workspace_for(kv, num_q_heads, block, topk, max(1, budget))
+        self.ws_spec = bd.select_spec_workspace_for(kv, num_q_heads, block, topk, self.max_budget)
         self.ws_repair = bd.workspace_for(kv, num_q_heads, block, max(1, topk))
-        self.ws_predict = bd.predict_workspace_for(B, H, self.nmax, budget, dev)
+        self.ws_predict = bd.predict_workspace_for(B, H, self.nmax, self.max_budget, dev)
         self._streams = None
         self.pending_predict: Optional[bd.PredictArgs] = None
+
+    def set_budget(self, budget: int):
+        """|P| of the predictions made from the next step on (e.g. from speculation_budget() as the context
+        grows); 1 <= budget <= max_budget.  The set already predicted for the next step keeps its size."""
+        if not 1 <= int(budget) <= self.max_budget:
+            raise ValueError(f"budget {budget} outside [1, {self.max_budget}] (raise max_budget at construction)")
+        self.budget = int(budget)
 
     @property
     def P_cur(self) -> bd.BlockSet:

@@ -114,15 +114,18 @@ def test_llama3_8b_layer_32k():
 def _trajectory(w, steps, units, ema, budget=None):
     """Run `steps` layer steps through PRRLayer (the single-stream step bench.py times) and check sampled
     units against the oracle's select / spec / repair / predict, step by step.  budget: |P| in blocks
-    (default K)."""
+    (default K), or a list: the budget of the prediction made at each step (PRRLayer.set_budget)."""
     budget = w.topk if budget is None else budget
+    budgets = list(budget) if isinstance(budget, (list, tuple)) else [budget] * steps
     inp = wl.make_inputs(w, "cuda")
     kv = device_kv(inp)
-    layer = PRRLayer(kv, w.num_q_heads, w.block, w.topk, budget, ema=ema, scale=w.scale)
+    layer = PRRLayer(kv, w.num_q_heads, w.block, w.topk, budgets[0], ema=ema, scale=w.scale,
+                     max_budget=max(budgets))
     alpha, beta, gamma = ema
     metas = {u: unit_meta(_kv_view(inp, *u), w.block) for u in units}
     ost = {u: (np.zeros(0), np.zeros(0), 0, np.zeros(0, dtype=np.int64)) for u in units}
     for t in range(steps):
+        layer.set_budget(budgets[t])
         P_before = layer.P_cur.lists()
         out = layer.step(inp.q[t])
         torch.cuda.synchronize()
@@ -135,7 +138,7 @@ def _trajectory(w, steps, units, ema, budget=None):
                                             P_before, layer.M, metas[(b, h)])
             m_h = orc.set_minus(a, P)
             _check_unit_attention(layer.state, out, inp, b, h, t, set(P.tolist()) | set(m_h.tolist()), f"step {t}")
-            lv, tr, live, P = orc.predict_step(lv, tr, live, s, alpha, beta, gamma, budget)
+            lv, tr, live, P = orc.predict_step(lv, tr, live, s, alpha, beta, gamma, budgets[t])
             nb = w.blocks_of(b)
             assert np.array_equal(lv_dev[b, h, :nb], lv) and np.array_equal(tr_dev[b, h, :nb], tr), (t, b, h)
             assert P_after[b][h] == list(P), (t, b, h)
@@ -159,6 +162,12 @@ def test_ctx128k_batch8_trajectory_with_planned_budget(select_us, want_delta):
     budget = speculation_budget(tab, wl.C3.context, wl.C3.topk)
     assert budget == int(round(want_delta * wl.C3.topk))
     _trajectory(wl.C3, 3, [(2, 3), (6, 0)], wl.C3.ema, budget)
+
+
+def test_ctx128k_batch8_trajectory_with_budget_changes():
+    """|P| changed between steps (as a planner would when the context grows): 64, then 128, then 32
+    blocks, with sets and workspaces sized once for the largest."""
+    _trajectory(wl.C3, 4, [(1, 6), (4, 2)], wl.C3.ema, [64, 128, 32, 64])
 
 
 def test_ctx128k_batch8_fp8_trajectory():
