@@ -86,16 +86,21 @@ def test_degenerate_cases():
     assert np.all(H == 0.0) and best == 0
 
 
-def test_full_size_prefill_matrix_sampled():
-    """8192 x 512 lognormal prefill matrix, K = 128, all 80 candidates on the GPU; the oracle evaluates a
-    sample of candidates (it takes about a second each) and the GPU's argmax is checked for consistency."""
+def test_full_size_prefill_matrix_against_golden():
+    """8192 x 512 lognormal prefill matrix, K = 128, all 80 candidates on the GPU against the oracle's
+    stored result (tests/golden/calibration_c5_8192x512.json, written by a script that calls only the
+    oracle; its tie to the generator and the oracle is checked on the CPU): every H within 1e-9 relative
+    and the same theta*."""
+    g = json.load(open(os.path.join(GOLDEN, "calibration_c5_8192x512.json")))
     w = wl.C5
     IS = wl.make_calibration_scores(w)
     grid = orc.calibration_grid()
     H, best = _run(IS, w.topk, grid)
-    assert best == int(np.argmax(H))
-    assert np.all((H >= 0.0) & (H <= 1.0))
-    IS64 = IS.astype(np.float64)
-    for j in (0, 47, int(best)):
-        oH, _ = orc.calibrate(IS64, w.topk, grid[j:j + 1])
-        assert abs(H[j] - oH[0]) <= H_TOL * oH[0], (j, H[j], oH[0])
+    oH = np.array([float.fromhex(x) for x in g["H_hex"]])
+    err = np.abs(H - oH) / oH
+    assert np.all(err <= H_TOL), (int(np.argmax(err)), float(err.max()))
+    order = np.argsort(-oH, kind="stable")
+    if abs(oH[order[0]] - oH[order[1]]) <= 1e-12 * oH[order[0]]:
+        assert best in (order[0], order[1])
+    else:
+        assert best == g["best"], (best, g["best"])
