@@ -12,15 +12,16 @@ each timed step t >= 1 does, on synthetic inputs already resident in HBM:
   2. flush, an empty event pair (the cost of the two event records themselves);
      flush, spec_attn(P^t) alone;  flush, repair(M^t) alone;  flush, select alone;  flush, predict alone
      (on copies of the predictor state);  flush, select_spec alone.
-The trajectory is then replayed twice with only a start and an end event per step: the single-stream
-step (the reported us per layer step: start to the end of repair) and, for comparison, the pages'
+The trajectory is then replayed twice: the single-stream step (the reported us per layer step: the start
+of the selection + speculative kernel to the end of the repair kernel) and, for comparison, the pages'
 three-stream schedule (select on the critical stream, spec_attn on a side stream, predict on a third).
 
-Kernel time = isolated event time minus the median empty-pair time of the same run (the two event
-records cost ~4 us on this platform whatever runs between them; a kernel launch still carries its own
-dispatch and completion latency).  value = effective KV GB/s of spec-attn + repair = algorithmic KV
-bytes ((|P| + |M|) * block * head_dim * 2 tensors * 2 B, summed over (sequence, kv head) units) /
-(spec kernel time + repair kernel time).  The raw event-bracketed figures are reported beside it.
+Kernel time = the GPU time of a call's kernels, read from HIP events bound to the launches themselves
+(prr_time_next_kernel: hipExtLaunchKernel with start/stop events; the start of the call's first kernel
+to the end of its last), so no event-record cost is in it; the same figures rocprofv3's kernel trace
+reports.  Event pairs recorded around each call are reported beside them (*_raw).  value = effective KV
+GB/s of spec-attn + repair = algorithmic KV bytes ((|P| + |M|) * block * head_dim * 2 tensors * 2 B,
+summed over (sequence, kv head) units) / (spec kernel time + repair kernel time).
 
 Also reported: us per layer step, per-kernel us, |M|, overlap and hit rate, the roofline
 of the dominant kernel (spec-attn), and the CPU oracle timed on a bounded sample of the same workload.
@@ -40,7 +41,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E peak
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "spec_attn_ctx128k_b8_hbm_counters.md")
-PROFILE_WORKLOAD = "ctx128k_b8_64steps"   # the workload (fixed context) those counters were taken on
+PROFILE_KERNEL_STATS = os.path.join(ROOT, "profiles", "attn_ctx128k_b8_kernel_stats.md")
+PROFILE_WORKLOAD = "ctx128k_b8_64steps"   # the workload (fixed context) those profiles were taken on
 
 
 def log(*a):
@@ -94,22 +96,28 @@ def kv_bytes_per_block(w) -> int:
     return w.block * w.kv_bytes_per_token()
 
 
-def load_traffic(kernel_hash: str):
-    """HBM bytes per spec-attn launch from the committed counter summary, or None when absent or
-    taken on a different kernel source."""
-    if not os.path.exists(PROFILE_COUNTERS):
+def load_profile_value(path: str, kernel_hash: str, key: str):
+    """A "- key: value" line of a committed profile summary, or None when the file is absent, lacks the
+    key or was taken on a different attention kernel source."""
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(PROFILE_COUNTERS):
+    for line in open(path):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
     if vals.get("kernel_source_sha256") != kernel_hash:
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
+
+
+def load_traffic(kernel_hash: str):
+    """HBM bytes per spec-attn launch from the committed counter summary, or None when absent or
+    taken on a different kernel source."""
+    return load_profile_value(PROFILE_COUNTERS, kernel_hash, "hbm_bytes_per_launch")
 
 
 def _cpu_unit_view(inp, w, b, h):
@@ -347,10 +355,10 @@ def delta_sweep(args, w, inp, kv, meta, flush, ev):
         for i in range(n):
             P = L.P_cur
             flush()
-            tm = StepTimers(ev(), None, ev(), None)
+            tm = StepTimers(None, None, None, None, ev(), ev())
             L.step(inp.q[1 + i], tm)
             torch.cuda.synchronize()
-            times.append(tm.start.elapsed_time(tm.repair_end) * 1e3)
+            times.append(tm.kernel_start.elapsed_time(tm.kernel_end) * 1e3)
             a = L.A.idx.cpu().numpy()
             p_idx, p_cnt = P.idx.cpu().numpy(), P.count.cpu().numpy()
             mc = L.M.count.cpu().numpy()
@@ -367,9 +375,9 @@ def delta_sweep(args, w, inp, kv, meta, flush, ev):
     return out
 
 
-def _budget_point(w, T, deltas, reps, flush, ev, base_us, seed):
+def _budget_point(w, T, deltas, reps, flush, ev, seed):
     """Median selection latency and speculative-attention latency at each delta for the workload's shape
-    at T tokens (each run after the cache flush, event time minus the empty pair).  P at delta is a
+    at T tokens (each run after the cache flush; the GPU time of the call's kernels, prr_time_next_kernel).  P at delta is a
     seeded random set of round(delta K) distinct blocks per (sequence, kv head)."""
     import numpy as np
     import torch
@@ -404,13 +412,12 @@ def _budget_point(w, T, deltas, reps, flush, ev, base_us, seed):
         pairs = []
         for _ in range(reps):
             flush()
-            e0, e1 = ev(), ev()
-            e0.record(crit)
+            k0, k1 = ev(), ev()
+            bd.time_next_kernel(k0, k1)
             fn()
-            e1.record(crit)
-            pairs.append((e0, e1))
+            pairs.append((k0, k1))
         torch.cuda.synchronize()
-        return float(np.median([a.elapsed_time(b) * 1e3 - base_us for a, b in pairs]))
+        return float(np.median([a.elapsed_time(b) * 1e3 for a, b in pairs]))
 
     for P in sets:   # warm every shape once
         bd.spec_attn(q, kv, wt.block, P, wt.scale, out=state, ws=ws)
@@ -423,7 +430,7 @@ def _budget_point(w, T, deltas, reps, flush, ev, base_us, seed):
     return t_sel, t_spec, budgets
 
 
-def budget_profile(args, w, flush, ev, base_us):
+def budget_profile(args, w, flush, ev):
     """The pages' critical-path-aware budget (§4.4, A.6): profile selection and speculative-attention
     latency over context lengths and budget ratios, fit the library's budget table, and report the
     largest delta whose speculative pass ends no later than selection at each profiled length and at
@@ -440,7 +447,7 @@ def budget_profile(args, w, flush, ev, base_us):
                          f"{int(round(max(deltas) * w.topk))} blocks of {w.block} tokens")
     sel, spec = [], [[] for _ in deltas]
     for i, T in enumerate(ctx):
-        t_sel, t_spec, budgets = _budget_point(w, T, deltas, args.budget_reps, flush, ev, base_us, seed=100 + i)
+        t_sel, t_spec, budgets = _budget_point(w, T, deltas, args.budget_reps, flush, ev, seed=100 + i)
         sel.append(t_sel)
         for j, t in enumerate(t_spec):
             spec[j].append(t)
@@ -457,7 +464,7 @@ def budget_profile(args, w, flush, ev, base_us):
     checks = []
     for i, T in enumerate(check):
         c = pick(T)
-        t_sel, t_spec, _ = _budget_point(w, T, deltas, args.budget_reps, flush, ev, base_us, seed=200 + i)
+        t_sel, t_spec, _ = _budget_point(w, T, deltas, args.budget_reps, flush, ev, seed=200 + i)
         c["measured_us_select"] = round(t_sel, 2)
         c["measured_us_spec"] = [round(t, 2) for t in t_spec]
         fits = [j for j, t in enumerate(t_spec) if t <= t_sel]
@@ -467,7 +474,7 @@ def budget_profile(args, w, flush, ev, base_us):
     return {"ctx": ctx, "deltas": deltas, "budget_blocks_at_K": [max(1, int(round(d * w.topk))) for d in deltas],
             "us_select": [round(t, 2) for t in sel], "us_spec": [[round(t, 2) for t in r] for r in spec],
             "degree": args.budget_degree, "coef": tab.coef.tolist(), "choices": choices, "checks": checks,
-            "note": "kernels timed alone, after the cache flush, minus the empty event pair; selection = "
+            "note": "kernels timed alone, after the cache flush (first kernel start to last kernel end); selection = "
                     "prr_select (scores, top-K, M), speculation = prr_spec_attn over round(delta K) blocks"}
 
 
@@ -625,13 +632,13 @@ def main():
 
     crit = torch.cuda.current_stream()
     ev = EventPool()
-    ev.reserve(K * (2 + 4 + 2 * 6))
+    iso_names = ("empty", "spec", "repair", "select", "predict", "select_spec")
+    ev.reserve(K * (6 + 4 * len(iso_names)))
     rec = []
     p_counts = torch.zeros((K, B, H), dtype=torch.int32, device=dev)
     m_counts = torch.zeros_like(p_counts)
     a_sets = torch.zeros((K, B, H, w.topk), dtype=torch.int32, device=dev)
     p_sets = torch.zeros_like(a_sets)
-    iso_names = ("empty", "spec", "repair", "select", "predict", "select_spec")
     append_pairs = []
 
     torch.cuda.synchronize()
@@ -643,28 +650,33 @@ def main():
         P = layer.P_cur
         if args.append:
             flush()
-            e0, e1 = ev(), ev()
+            e0, e1, k0, k1 = ev(), ev(), ev(), ev()
             e0.record(crit)
+            bd.time_next_kernel(k0, k1)
             layer.append(k_app[i], v_app[i], stream=crit)
             e1.record(crit)
-            append_pairs.append((e0, e1))
-        # 1. layer step with a breakdown
+            append_pairs.append((e0, e1, k0, k1))
+        # 1. layer step with a breakdown (events after each call) and its kernel span
         flush()
-        tm = StepTimers(ev(), ev(), ev(), ev())
+        tm = StepTimers(ev(), ev(), ev(), ev(), ev(), ev())
         layer.step(q, tm)
         p_counts[i].copy_(P.count)
         m_counts[i].copy_(layer.M.count)
         a_sets[i].copy_(layer.A.idx)
         p_sets[i].copy_(P.idx)
-        # 2. isolated: empty event pair, then each kernel on the same sets
+        # 2. isolated, each after a flush, on the same sets: an empty event pair, then each call with an
+        #    event pair around it (dispatch and completion included) and events bound to its kernels
+        #    (prr_time_next_kernel: the start of its first kernel, the end of its last)
         pairs = []
         iso_level.copy_(layer.level)
         iso_trend.copy_(layer.trend)
         iso_live.copy_(layer.live)
         for what in iso_names:
             flush()
-            e0, e1 = ev(), ev()
+            e0, e1, k0, k1 = ev(), ev(), ev(), ev()
             e0.record(crit)
+            if what != "empty":
+                bd.time_next_kernel(k0, k1)
             if what == "spec":
                 bd.spec_attn(q, kv, w.block, P, w.scale, out=iso_state, ws=ws_iso_spec, stream=crit)
             elif what == "repair":
@@ -679,7 +691,7 @@ def main():
                 bd.select_spec(q, kv, layer.meta, w.block, w.topk, P, w.scale, scores=iso_scores, A=iso_A,
                                M=iso_M, out=iso_state, ws=ws_iso_spec, mode=args.score_mode, stream=crit)
             e1.record(crit)
-            pairs.append((e0, e1))
+            pairs.append((e0, e1, k0, k1))
         rec.append((tm, *pairs))
         if (i + 1) % 16 == 0:
             log(f"[bench] {i + 1}/{K} steps enqueued")
@@ -687,13 +699,14 @@ def main():
     wall = time.perf_counter() - wall0
 
     def replay(two_streams: bool):
-        """Replay the trajectory with a start and an end event per step only."""
+        """Replay the trajectory with a start and an end event per step only (and, on one stream, the
+        kernel span: the start of the selection + speculative kernel to the end of repair)."""
         layer.reset()
         if args.append:   # back to the initial context: lengths, then the metadata of every block
             inp.seq_len.copy_(len0)
             (bd.build_meta if args.score_mode == "quest" else bd.build_mean_meta)(kv, w.block, layer.meta)
         layer.step(inp.q[0])
-        ev.reserve(2 * K)
+        ev.reserve(4 * K)
         out = []
         for i in range(K):
             if args.append:
@@ -702,10 +715,11 @@ def main():
             if two_streams:
                 tm = TwoStreamTimers(ev(), None, None, None, None, ev())
                 layer.step_two_streams(inp.q[1 + i], tm)
+                out.append((tm.start, tm.repair_end, None, None))
             else:
-                tm = StepTimers(ev(), None, ev(), None)
+                tm = StepTimers(ev(), None, ev(), None, ev(), ev())
                 layer.step(inp.q[1 + i], tm)
-            out.append((tm.start, tm.repair_end))
+                out.append((tm.start, tm.repair_end, tm.kernel_start, tm.kernel_end))
         torch.cuda.synchronize()
         return out
 
@@ -715,13 +729,15 @@ def main():
     def el(a, b):
         return a.elapsed_time(b) * 1e3   # microseconds
 
-    iso_raw = {nm: [el(*r[1 + j]) for r in rec] for j, nm in enumerate(iso_names)}
+    # per call: raw = the event pair around it; kernel = the span of its kernels (prr_time_next_kernel)
+    iso_raw = {nm: [el(r[1 + j][0], r[1 + j][1]) for r in rec] for j, nm in enumerate(iso_names)}
+    iso_us = {nm: [el(r[1 + j][2], r[1 + j][3]) for r in rec] for j, nm in enumerate(iso_names) if nm != "empty"}
     base_us = float(statistics.median(iso_raw["empty"]))
-    iso_us = {nm: [x - base_us for x in xs] for nm, xs in iso_raw.items()}
     spec_raw, rep_raw = iso_raw["spec"], iso_raw["repair"]
     spec_us, rep_us = iso_us["spec"], iso_us["repair"]
-    step_lean_us = [el(a, b) for a, b in lean_one]
-    step_two_us = [el(a, b) for a, b in lean_two]
+    step_lean_us = [el(a, b) for a, b, _, _ in lean_one]
+    step_kernel_us = [el(c, d) for _, _, c, d in lean_one]
+    step_two_us = [el(a, b) for a, b, _, _ in lean_two]
     step_tm_us = [el(r[0].start, r[0].repair_end) for r in rec]
     ss_ov_us = [el(r[0].start, r[0].select_spec_end) for r in rec]
     rep_ov_us = [el(r[0].select_spec_end, r[0].repair_end) for r in rec]
@@ -759,6 +775,12 @@ def main():
                if (w.name == PROFILE_WORKLOAD and not args.append and args.score_mode == "quest"
                    and w.dtype == "bf16") else None)
 
+    rocprof_ref = {"rocprof_avg_launch_us": None, "rocprof_frac": None}
+    if w.name == PROFILE_WORKLOAD and not args.append and args.score_mode == "quest" and w.dtype == "bf16":
+        avg = load_profile_value(PROFILE_KERNEL_STATS, kernel_hash, "attn_spec_avg_us")
+        if avg:
+            rocprof_ref = {"rocprof_avg_launch_us": avg,
+                           "rocprof_frac": round(spec_launch_bytes / (avg * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
     med = lambda xs: round(float(statistics.median(xs)), 2)
     result = {
         "metric": "effective KV GB/s (frac of HBM peak) + us/layer-step, spec-attn+repair",
@@ -782,15 +804,19 @@ def main():
         "value_median_step_gbps": round(float(statistics.median(step_gbps)), 1),
         "value_note": "value = all timed steps' KV bytes / their summed spec + repair kernel time (one slow step "
                       "counts in full); value_median_step_gbps = the median step's own figure",
-        "timing_note": "kernel us = event-bracketed us minus the median empty event pair (each after the same "
-                       "flush); *_raw figures are the event-bracketed ones",
+        "timing_note": "kernel us = the GPU time of a call's kernels, from HIP events bound to them "
+                       "(prr_time_next_kernel: hipExtLaunchKernel with start/stop events, the start of the first "
+                       "kernel to the end of the last), each call alone after the same flush; *_raw figures are "
+                       "event pairs recorded around the call (they add the event records' own cost)",
         "us_empty_event_pair_median": round(base_us, 2),
         "value_raw_events_gbps": round(value_raw, 1),
-        "us_per_layer_step_median": med(step_lean_us),
-        "us_per_layer_step_p10_p90": [round(float(np.percentile(step_lean_us, 10)), 2),
-                                      round(float(np.percentile(step_lean_us, 90)), 2)],
-        "layer_step_note": "event-bracketed, start of select_spec to the end of repair, one stream; the "
-                           "predictor follows repair on the same stream (off this path)",
+        "us_per_layer_step_median": med(step_kernel_us),
+        "us_per_layer_step_p10_p90": [round(float(np.percentile(step_kernel_us, 10)), 2),
+                                      round(float(np.percentile(step_kernel_us, 90)), 2)],
+        "layer_step_note": "one stream: the start of the selection + speculative kernel to the end of the repair "
+                           "kernel (events bound to the kernels); the predictor follows repair on the same stream "
+                           "(off this path)",
+        "us_per_layer_step_events_median": med(step_lean_us),
         "us_per_layer_step_two_streams_median": med(step_two_us),
         "us_spec_attn_median": med(spec_us),
         "us_spec_attn_p10_p90": [round(float(np.percentile(spec_us, 10)), 2),
@@ -819,21 +845,24 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": spec_launch_bytes,
-                     "avg_launch_us": round(spec_launch_us, 2), "kernel_source_sha256": kernel_hash},
+                     "avg_launch_us": round(spec_launch_us, 2), "kernel_source_sha256": kernel_hash,
+                     "avg_launch_note": "mean over the timed steps of the kernel's own duration (HIP events bound "
+                                        "to the launch); rocprof_* = the committed rocprofv3 kernel trace of the "
+                                        "same kernel source (null when the source differs)",
+                     **rocprof_ref},
     }
     if args.append:
         result["decode_append"] = {
-            "us_append_median": round(float(statistics.median(
-                [el(a, b) - base_us for a, b in append_pairs])), 2),
+            "us_append_median": round(float(statistics.median([el(k0, k1) for _, _, k0, k1 in append_pairs])), 2),
             "note": "each timed step appends one token per sequence before its layer step (context grows "
-                    "by one token per step); append time = event time minus the empty pair"}
+                    "by one token per step); append time = the append kernel's own duration"}
         if args.delta_sweep:
             log("[bench] --delta-sweep is skipped in --append mode")
             args.delta_sweep = ""
     if args.delta_sweep:
         result["delta_sweep"] = delta_sweep(args, w, inp, kv, layer.meta, flush, ev)
     if args.budget_profile:
-        result["budget"] = budget_profile(args, w, flush, ev, base_us)
+        result["budget"] = budget_profile(args, w, flush, ev)
     if args.stack > 1 and not args.append:
         result["stack"] = measure_stack(args, w, layer, inp, flush, ev)
     if not args.no_cpu_baseline:

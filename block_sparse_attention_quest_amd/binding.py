@@ -27,7 +27,7 @@ EXPORTS = (
     "prr_predict",
     "prr_spec_attn",
     "prr_repair", "prr_calibrate_workspace_bytes", "prr_calibrate", "prr_budget_fit", "prr_budget_choose",
-    "prr_strerror",
+    "prr_time_next_kernel", "prr_strerror",
 )
 
 
@@ -94,6 +94,7 @@ _SIGS = {
     "prr_calibrate": (ctypes.c_int, [_VP, _I32, _I32, _I32, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]),
     "prr_budget_fit": (ctypes.c_int, [_VP, _I32, _VP, _VP, _I32, _VP, _I32, _VP]),
     "prr_budget_choose": (ctypes.c_int, [_VP, _I32, _VP, _VP, _I32, _VP, _I32, _VP, _D, _VP, _VP]),
+    "prr_time_next_kernel": (ctypes.c_int, [_VP, _VP]),
     "prr_strerror": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -248,6 +249,21 @@ class Workspace:
 # --------------------------------------------------------------------------------------------------
 # Entry points
 # --------------------------------------------------------------------------------------------------
+
+
+def _event_handle(ev) -> Optional[ctypes.c_void_p]:
+    if ev is None:
+        return None
+    if not ev.cuda_event:   # torch creates the HIP event at its first record
+        ev.record()
+    return ctypes.c_void_p(ev.cuda_event)
+
+
+def time_next_kernel(start, stop):
+    """Arm two torch.cuda.Event(enable_timing=True) events (either may be None) for the next library call
+    on this thread that enqueues GPU work: start takes the start of its first kernel and stop the end of
+    its last, so start.elapsed_time(stop) is the GPU time of the call's kernels (prr_time_next_kernel)."""
+    _check(load_library().prr_time_next_kernel(_event_handle(start), _event_handle(stop)), "prr_time_next_kernel")
 
 
 def max_blocks(kv: KVCache, block: int) -> int:

@@ -156,7 +156,7 @@ hipError_t launch_append(const KvDesc &kv, void *k, void *v, int32_t *seq_len, c
     p.stride = stride;
     const int kt = kv.fp8 ? kKtFp8 : kv.bf16 ? kKtBf16 : kKtF32;
 #define PRR_AP(KT, DD, MN) \
-    if (kt == KT && kv.d == DD && mean == MN) append_kernel<KT, DD, MN><<<kv.batch, 256, 0, stream>>>(p); else
+    if (kt == KT && kv.d == DD && mean == MN) PRR_LAUNCH(append_kernel<KT, DD, MN>, dim3(kv.batch), dim3(256), stream, p); else
 #define PRR_AP_T(KT) PRR_AP(KT, 128, false) PRR_AP(KT, 64, false) PRR_AP(KT, 128, true) PRR_AP(KT, 64, true)
     PRR_AP_T(kKtF32) PRR_AP_T(kKtBf16) PRR_AP_T(kKtFp8)
     { return hipErrorInvalidValue; }

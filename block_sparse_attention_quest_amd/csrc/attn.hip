@@ -59,41 +59,26 @@ hipError_t launch_attn(const KvDesc &kv, const void *q, int hq, int block, const
                        float *out, bool repair, void *ws, hipStream_t stream) {
     AttnParams p;
     const int grid = attn_setup(p, kv, q, hq, block, idx, count, cap, scale, acc, l, m, out, repair, ws);
-    const dim3 blk(kThreads);
+    void (*k)(AttnParams);
+    const bool d128 = kv.d == 128;
     if (kv.fp8) {
-        if (repair) {
-            if (kv.d == 128) attn_repair_fp8<128><<<grid, blk, 0, stream>>>(p);
-            else attn_repair_fp8<64><<<grid, blk, 0, stream>>>(p);
-        } else {
-            if (kv.d == 128) attn_spec_fp8<128><<<grid, blk, 0, stream>>>(p);
-            else attn_spec_fp8<64><<<grid, blk, 0, stream>>>(p);
-        }
+        if (repair) k = d128 ? attn_repair_fp8<128> : attn_repair_fp8<64>;
+        else k = d128 ? attn_spec_fp8<128> : attn_spec_fp8<64>;
     } else if (kv.bf16) {
-        if (repair) {
-            if (kv.d == 128) attn_repair_bf16<128><<<grid, blk, 0, stream>>>(p);
-            else attn_repair_bf16<64><<<grid, blk, 0, stream>>>(p);
-        } else {
-            if (kv.d == 128) attn_spec_bf16<128><<<grid, blk, 0, stream>>>(p);
-            else attn_spec_bf16<64><<<grid, blk, 0, stream>>>(p);
-        }
+        if (repair) k = d128 ? attn_repair_bf16<128> : attn_repair_bf16<64>;
+        else k = d128 ? attn_spec_bf16<128> : attn_spec_bf16<64>;
     } else {
-        if (repair) {
-            if (kv.d == 128) attn_repair_f32<128><<<grid, blk, 0, stream>>>(p);
-            else attn_repair_f32<64><<<grid, blk, 0, stream>>>(p);
-        } else {
-            if (kv.d == 128) attn_spec_f32<128><<<grid, blk, 0, stream>>>(p);
-            else attn_spec_f32<64><<<grid, blk, 0, stream>>>(p);
-        }
+        if (repair) k = d128 ? attn_repair_f32<128> : attn_repair_f32<64>;
+        else k = d128 ? attn_spec_f32<128> : attn_spec_f32<64>;
     }
-    return hipGetLastError();
+    return launch(k, dim3(grid), dim3(kThreads), stream, p);
 }
 
 hipError_t launch_clear(void *ws, size_t bytes, hipStream_t stream) {
     const size_t n = bytes / 4;
     if (n == 0) return hipSuccess;
     const int blocks = (int)std::min<size_t>(1024, (n + 255) / 256);
-    clear_kernel<<<blocks, 256, 0, stream>>>((uint32_t *)ws, n);
-    return hipGetLastError();
+    return launch(clear_kernel, dim3(blocks), dim3(256), stream, (uint32_t *)ws, n);
 }
 
 }  // namespace prr

@@ -329,11 +329,11 @@ int calib_chunks(int rows) { return rows > 1 ? (rows - 1 + kCalibChunk - 1) / kC
 template <int KPL>
 hipError_t launch_kpl(const CalibParams &p, hipStream_t stream) {
     if (p.rows > 1) {
-        rows_topk_kernel<KPL><<<(p.rows - 1 + 3) / 4, 256, 0, stream>>>(p);
-        ema_chain_kernel<<<(p.n * p.blocks + 255) / 256, 256, 0, stream>>>(p);
-        replay_kernel<KPL><<<(p.n * p.nchunks + 3) / 4, 256, 0, stream>>>(p);
+        PRR_LAUNCH(rows_topk_kernel<KPL>, dim3((p.rows - 1 + 3) / 4), dim3(256), stream, p);
+        PRR_LAUNCH(ema_chain_kernel, dim3((p.n * p.blocks + 255) / 256), dim3(256), stream, p);
+        PRR_LAUNCH(replay_kernel<KPL>, dim3((p.n * p.nchunks + 3) / 4), dim3(256), stream, p);
     }
-    finish_kernel<<<1, 256, 0, stream>>>(p);
+    PRR_LAUNCH(finish_kernel, dim3(1), dim3(256), stream, p);
     return hipGetLastError();
 }
 

@@ -12,6 +12,30 @@
 
 namespace {
 
+// Kernel timing (prr_time_next_kernel).  The armed events move to the next entry-point call of the thread
+// (the outermost one, when an entry point calls another): its first launch takes the start event and
+// every launch the stop event; the call consumes them whether or not it launches.
+struct TimingEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+thread_local TimingEvents t_armed;
+thread_local TimingEvents t_call;
+thread_local int t_depth = 0;
+
+struct CallTiming {
+    CallTiming() {
+        if (t_depth++ == 0) {
+            t_call = t_armed;
+            t_armed = TimingEvents{};
+        }
+    }
+    ~CallTiming() {
+        if (--t_depth == 0) t_call = TimingEvents{};
+    }
+    CallTiming(const CallTiming &) = delete;
+    CallTiming &operator=(const CallTiming &) = delete;
+};
+
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 prr_status check_kv(const prr_kv_cache *kv) {
@@ -90,7 +114,23 @@ prr_status attn_common(const void *q, int32_t hq, const prr_kv_cache *kv, int32_
 
 }  // namespace
 
+namespace prr {
+bool take_kernel_timing(hipEvent_t *start, hipEvent_t *stop) {
+    if (!t_call.start && !t_call.stop) return false;
+    *start = t_call.start;   // the call's first kernel only
+    *stop = t_call.stop;     // every kernel of the call, so the last one's end remains
+    t_call.start = nullptr;
+    return true;
+}
+}  // namespace prr
+
 extern "C" {
+
+prr_status prr_time_next_kernel(hipEvent_t start, hipEvent_t stop) {
+    t_armed.start = start;
+    t_armed.stop = stop;
+    return PRR_OK;
+}
 
 int32_t prr_max_blocks(const prr_kv_cache *kv, int32_t block) {
     if (!kv || block <= 0) return 0;
@@ -117,11 +157,13 @@ size_t prr_attn_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_
 }
 
 prr_status prr_workspace_clear(void *ws, size_t ws_bytes, hipStream_t stream) {
+    CallTiming timing_;
     if (!ws && ws_bytes) return PRR_EINVAL;
     return hip_status(prr::launch_clear(ws, ws_bytes, stream));
 }
 
 prr_status prr_build_meta(const prr_kv_cache *kv, int32_t block, void *meta, hipStream_t stream) {
+    CallTiming timing_;
     PRR_TRY(check_kv(kv));
     PRR_TRY(check_block(kv, block));
     if (!meta) return PRR_EINVAL;
@@ -134,6 +176,7 @@ size_t prr_mean_meta_bytes(const prr_kv_cache *kv, int32_t block) {
 }
 
 prr_status prr_build_mean_meta(const prr_kv_cache *kv, int32_t block, float *meta, hipStream_t stream) {
+    CallTiming timing_;
     PRR_TRY(check_kv(kv));
     PRR_TRY(check_block(kv, block));
     if (!meta) return PRR_EINVAL;
@@ -142,6 +185,7 @@ prr_status prr_build_mean_meta(const prr_kv_cache *kv, int32_t block, float *met
 
 prr_status prr_append(const prr_kv_cache *kv, int32_t block, const void *k_new, const void *v_new, void *meta,
                       prr_score_mode mode, int32_t *seq_len, hipStream_t stream) {
+    CallTiming timing_;
     PRR_TRY(check_kv(kv));
     PRR_TRY(check_block(kv, block));
     if (!k_new || !v_new || !meta || !seq_len) return PRR_EINVAL;
@@ -155,6 +199,7 @@ prr_status prr_append(const prr_kv_cache *kv, int32_t block, const void *k_new, 
 prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
                       prr_score_mode mode, int32_t block, int32_t topk, const prr_block_set *P, double *scores,
                       prr_block_set *A, prr_block_set *M, hipStream_t stream) {
+    CallTiming timing_;
     if (!q || !meta || !scores) return PRR_EINVAL;
     if (mode != PRR_SCORE_QUEST && mode != PRR_SCORE_MEAN) return PRR_EINVAL;
     PRR_TRY(check_kv(kv));
@@ -205,6 +250,7 @@ prr_status prr_select_spec_predict(const void *q, int32_t num_q_heads, const prr
                                    double *scores, prr_block_set *A, prr_block_set *M, float scale,
                                    prr_attn_state *out, void *ws, size_t ws_bytes, const prr_predict_args *pred,
                                    hipStream_t stream) {
+    CallTiming timing_;
     if (!q || !meta || !scores || !P || !M) return PRR_EINVAL;
     if (mode != PRR_SCORE_QUEST && mode != PRR_SCORE_MEAN) return PRR_EINVAL;
     PRR_TRY(check_kv(kv));
@@ -263,6 +309,7 @@ prr_status prr_select_spec(const void *q, int32_t num_q_heads, const prr_kv_cach
                            prr_score_mode mode, int32_t block, int32_t topk, const prr_block_set *P,
                            double *scores, prr_block_set *A, prr_block_set *M, float scale, prr_attn_state *out,
                            void *ws, size_t ws_bytes, hipStream_t stream) {
+    CallTiming timing_;
     return prr_select_spec_predict(q, num_q_heads, kv, meta, mode, block, topk, P, scores, A, M, scale, out, ws,
                                    ws_bytes, nullptr, stream);
 }
@@ -276,6 +323,7 @@ prr_status prr_predict(const double *scores, const int32_t *seq_len, int32_t bat
                        int32_t num_kv_heads, int32_t block, int32_t max_blocks, double alpha,
                        double beta, double gamma, int32_t budget, double *level, double *trend,
                        int32_t *live, prr_block_set *P_next, void *ws, size_t ws_bytes, hipStream_t stream) {
+    CallTiming timing_;
     PRR_TRY(check_predict(scores, seq_len, batch, num_kv_heads, block, max_blocks, budget, level, trend, live,
                           P_next));
     const size_t need = prr::predict_workspace_bytes(batch, num_kv_heads, max_blocks, budget);
@@ -288,6 +336,7 @@ prr_status prr_predict(const double *scores, const int32_t *seq_len, int32_t bat
 prr_status prr_spec_attn(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, int32_t block,
                          const prr_block_set *P, float scale, prr_attn_state *out, void *ws,
                          size_t ws_bytes, hipStream_t stream) {
+    CallTiming timing_;
     PRR_TRY(attn_common(q, num_q_heads, kv, block, P, ws, ws_bytes));
     if (!out || !out->acc || !out->l || !out->m) return PRR_EINVAL;
     PRR_TRY(check_input_set(kv, block, P, stream));
@@ -298,6 +347,7 @@ prr_status prr_spec_attn(const void *q, int32_t num_q_heads, const prr_kv_cache 
 prr_status prr_repair(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, int32_t block,
                       const prr_block_set *M, float scale, prr_attn_state *state, float *out,
                       void *ws, size_t ws_bytes, hipStream_t stream) {
+    CallTiming timing_;
     PRR_TRY(attn_common(q, num_q_heads, kv, block, M, ws, ws_bytes));
     if (!state || !state->acc || !state->l || !state->m) return PRR_EINVAL;
     PRR_TRY(check_input_set(kv, block, M, stream));
@@ -313,6 +363,7 @@ size_t prr_calibrate_workspace_bytes(int32_t rows, int32_t blocks, int32_t n_can
 prr_status prr_calibrate(const float *scores, int32_t rows, int32_t blocks, int32_t topk, const double *grid,
                          int32_t n_candidates, double *H, int32_t *best, void *ws, size_t ws_bytes,
                          hipStream_t stream) {
+    CallTiming timing_;
     if (!scores || !grid || !H || !best) return PRR_EINVAL;
     if (rows <= 0 || blocks <= 0 || topk < 0 || n_candidates <= 0) return PRR_EINVAL;
     if (blocks > prr::kMaxCalibBlocks || n_candidates > prr::kMaxCalibGrid) return PRR_EUNSUPPORTED;

@@ -1,11 +1,46 @@
 // Internal launch interface between the C ABI (prr_api.cpp) and the kernels.  Host-side only types.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace prr {
+
+// Kernel timing (prr_time_next_kernel): the start event goes to the first kernel an entry-point call
+// launches, the stop event to every kernel it launches (the last one's end remains).  false when none
+// are armed for the calling thread's current call.
+bool take_kernel_timing(hipEvent_t *start, hipEvent_t *stop);
+
+template <typename T>
+struct same_type {
+    typedef T type;
+};
+
+// Launches `kernel` on `stream`; when timing events are armed for the current entry-point call, through
+// hipExtLaunchKernel with them, so that they hold kernel start and end times.  The arguments
+// are converted to the kernel's parameter types at the call.
+template <typename... Params>
+hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t stream,
+                  typename same_type<Params>::type... args) {
+    hipEvent_t start = nullptr, stop = nullptr;
+    if (take_kernel_timing(&start, &stop)) {
+        void *argv[] = {(void *)&args..., nullptr};
+        hipError_t e = hipExtLaunchKernel((const void *)kernel, grid, block, argv, 0, stream, start, stop, 0);
+        if (e != hipSuccess) return e;
+    } else {
+        kernel<<<grid, block, 0, stream>>>(args...);
+    }
+    return hipGetLastError();
+}
+
+// launch(...) inside a function returning hipError_t: returns the launch's error, if any.
+#define PRR_LAUNCH(...)                                     \
+    do {                                                    \
+        const hipError_t prr_e_ = ::prr::launch(__VA_ARGS__); \
+        if (prr_e_ != hipSuccess) return prr_e_;           \
+    } while (0)
 
 constexpr int kPage = 16;          // tokens per page (the only supported page size)
 constexpr int kMaxSelectN = 32768; // blocks per (sequence, kv head) the top-K kernels hold on chip

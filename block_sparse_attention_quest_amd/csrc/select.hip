@@ -249,7 +249,7 @@ hipError_t dispatch_topk(int nmax, int units, const P &p, hipStream_t stream) {
 template <int KPT, int TPB>
 struct TopkLaunch {
     static hipError_t run(int units, const TopkParams &p, hipStream_t stream) {
-        topk_kernel<KPT, TPB><<<units, TPB, 0, stream>>>(p);
+        PRR_LAUNCH(topk_kernel<KPT, TPB>, dim3(units), dim3(TPB), stream, p);
         return hipGetLastError();
     }
 };
@@ -257,7 +257,7 @@ struct TopkLaunch {
 template <int KPT, int TPB>
 struct PredictLaunch {
     static hipError_t run(int units, const PredictParams &p, hipStream_t stream) {
-        predict_kernel<KPT, TPB><<<units, TPB, 0, stream>>>(p);
+        PRR_LAUNCH(predict_kernel<KPT, TPB>, dim3(units), dim3(TPB), stream, p);
         return hipGetLastError();
     }
 };
@@ -280,8 +280,8 @@ hipError_t launch_meta(const KvDesc &kv, int block, int stride, void *meta, bool
     const int kt = kv.fp8 ? kKtFp8 : kv.bf16 ? kKtBf16 : kKtF32;
 #define PRR_META(KT, DD)                                                                             \
     if (kt == KT && kv.d == DD) {                                                                    \
-        if (mean) mean_meta_kernel<KT, DD><<<grid, 256, 0, stream>>>(p);                             \
-        else meta_kernel<KT, DD><<<grid, 256, 0, stream>>>(p);                                       \
+        if (mean) PRR_LAUNCH(mean_meta_kernel<KT, DD>, dim3(grid), dim3(256), stream, p);                             \
+        else PRR_LAUNCH(meta_kernel<KT, DD>, dim3(grid), dim3(256), stream, p);                                       \
     } else
     PRR_META(kKtF32, 128) PRR_META(kKtF32, 64) PRR_META(kKtBf16, 128) PRR_META(kKtBf16, 64)
     PRR_META(kKtFp8, 128) PRR_META(kKtFp8, 64)
@@ -312,18 +312,18 @@ hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *me
     if (mean) {
         // the fp32 block means do not depend on the cache dtype beyond q's
         if (bq) {
-            if (kv.d == 128) score_kernel<true, 128, true><<<sgrid, 256, 0, stream>>>(sp);
-            else score_kernel<true, 64, true><<<sgrid, 256, 0, stream>>>(sp);
+            if (kv.d == 128) PRR_LAUNCH(score_kernel<true, 128, true>, dim3(sgrid), dim3(256), stream, sp);
+            else PRR_LAUNCH(score_kernel<true, 64, true>, dim3(sgrid), dim3(256), stream, sp);
         } else {
-            if (kv.d == 128) score_kernel<false, 128, true><<<sgrid, 256, 0, stream>>>(sp);
-            else score_kernel<false, 64, true><<<sgrid, 256, 0, stream>>>(sp);
+            if (kv.d == 128) PRR_LAUNCH(score_kernel<false, 128, true>, dim3(sgrid), dim3(256), stream, sp);
+            else PRR_LAUNCH(score_kernel<false, 64, true>, dim3(sgrid), dim3(256), stream, sp);
         }
     } else if (bq) {
-        if (kv.d == 128) score_kernel<true, 128, false><<<sgrid, 256, 0, stream>>>(sp);
-        else score_kernel<true, 64, false><<<sgrid, 256, 0, stream>>>(sp);
+        if (kv.d == 128) PRR_LAUNCH(score_kernel<true, 128, false>, dim3(sgrid), dim3(256), stream, sp);
+        else PRR_LAUNCH(score_kernel<true, 64, false>, dim3(sgrid), dim3(256), stream, sp);
     } else {
-        if (kv.d == 128) score_kernel<false, 128, false><<<sgrid, 256, 0, stream>>>(sp);
-        else score_kernel<false, 64, false><<<sgrid, 256, 0, stream>>>(sp);
+        if (kv.d == 128) PRR_LAUNCH(score_kernel<false, 128, false>, dim3(sgrid), dim3(256), stream, sp);
+        else PRR_LAUNCH(score_kernel<false, 64, false>, dim3(sgrid), dim3(256), stream, sp);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -386,7 +386,7 @@ hipError_t launch_topk_groups(const KvDesc &kv, int block, int nmax, int topk, c
     const dim3 grid(plan.ng, units);
 #define PRR_TG(K2, K3)                                                                                      \
     if (plan.kpt2 == K2 && plan.kpt3 == K3) {                                                               \
-        topk_groups_kernel<K2, K3><<<grid, 256, 0, stream>>>(tp, c1, c2, arrivals, nparts, plan.gp, plan.ng, live); \
+        PRR_LAUNCH(topk_groups_kernel<K2, K3>, dim3(grid), dim3(256), stream, tp, c1, c2, arrivals, nparts, plan.gp, plan.ng, live); \
         return hipGetLastError();                                                                           \
     }
     PRR_TG(8, 1) PRR_TG(8, 2) PRR_TG(8, 4) PRR_TG(8, 8) PRR_TG(8, 16)
@@ -483,7 +483,7 @@ hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batc
     cp.kl = pl.kl;
     const dim3 grid(pl.nparts, units);
     if (pl.groups.three) {
-        predict_parts_only_kernel<<<grid, 256, 0, stream>>>(p, cp, pl.nparts);
+        PRR_LAUNCH(predict_parts_only_kernel, dim3(grid), dim3(256), stream, p, cp, pl.nparts);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const size_t s1bytes = slots * 12 + (size_t)units * pl.nparts * 4;
@@ -495,9 +495,9 @@ hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batc
         return launch_topk_groups(kv, block, nmax, budget, nullptr, nullptr, 0, p_idx, p_cnt, p_cap, nullptr, nullptr,
                                   0, pl.groups, pl.nparts, cbase, cand2, arrivals, stream, live);
     }
-    if (pl.kpt == 4) predict_parts_kernel<4><<<grid, 256, 0, stream>>>(p, tp, cp, arrivals, pl.nparts);
-    else if (pl.kpt == 8) predict_parts_kernel<8><<<grid, 256, 0, stream>>>(p, tp, cp, arrivals, pl.nparts);
-    else predict_parts_kernel<16><<<grid, 256, 0, stream>>>(p, tp, cp, arrivals, pl.nparts);
+    if (pl.kpt == 4) PRR_LAUNCH(predict_parts_kernel<4>, dim3(grid), dim3(256), stream, p, tp, cp, arrivals, pl.nparts);
+    else if (pl.kpt == 8) PRR_LAUNCH(predict_parts_kernel<8>, dim3(grid), dim3(256), stream, p, tp, cp, arrivals, pl.nparts);
+    else PRR_LAUNCH(predict_parts_kernel<16>, dim3(grid), dim3(256), stream, p, tp, cp, arrivals, pl.nparts);
     return hipGetLastError();
 }
 

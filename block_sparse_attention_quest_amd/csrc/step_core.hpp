@@ -225,7 +225,7 @@ hipError_t launch_select_spec_t(const KvDesc &kv, const void *q, int hq, const v
     const bool two = plan.two;
 #define PRR_SS(DD, K, T, MN, PR)                                                                           \
     if (kv.d == DD && kpt == K && two == T && mean == MN && fuse_pred == PR) {                              \
-        select_spec_kernel<KT, DD, K, T, MN, PR><<<(int)grid, 256, 0, stream>>>(ap, sp, tp, cp, pp, arrivals,      \
+        PRR_LAUNCH(select_spec_kernel<KT, DD, K, T, MN, PR>, dim3((int)grid), dim3(256), stream, ap, sp, tp, cp, pp, arrivals,      \
                                                                             pred_ctr, nsx * units, nsx, n_spec, \
                                                                             n_pred);                        \
     } else

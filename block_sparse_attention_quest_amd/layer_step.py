@@ -34,16 +34,21 @@ from . import binding as bd
 
 @dataclass
 class StepTimers:
-    """Optional timing events of ``step`` (all on the one stream); a field left None is not recorded."""
+    """Optional timing events of ``step`` (all on the one stream); a field left None is not recorded.
+    kernel_start / kernel_end are bound to kernels (prr_time_next_kernel): the start of the selection +
+    speculative kernel and the end of the repair kernel, so their span is the step's GPU time without the
+    cost of event records."""
 
     start: Optional[torch.cuda.Event]
     select_spec_end: Optional[torch.cuda.Event]
     repair_end: Optional[torch.cuda.Event]
     predict_end: Optional[torch.cuda.Event]
+    kernel_start: Optional[torch.cuda.Event] = None
+    kernel_end: Optional[torch.cuda.Event] = None
 
     @staticmethod
     def make() -> "StepTimers":
-        return StepTimers(*[torch.cuda.Event(enable_timing=True) for _ in range(4)])
+        return StepTimers(*[torch.cuda.Event(enable_timing=True) for _ in range(6)])
 
     @staticmethod
     def lean() -> "StepTimers":
@@ -154,10 +159,14 @@ class PRRLayer:
         P, Pn = self.P[self.cur], self.P[1 - self.cur]
         if timers and timers.start:
             timers.start.record(s)
+        if timers and timers.kernel_start:
+            bd.time_next_kernel(timers.kernel_start, None)
         bd.select_spec(q, self.kv, self.meta, self.block, self.topk, P, self.scale, scores=self.scores, A=self.A,
                        M=self.M, out=self.state, ws=self.ws_spec, mode=self.score_mode, pred=carry, stream=s)
         if timers and timers.select_spec_end:
             timers.select_spec_end.record(s)
+        if timers and timers.kernel_end:
+            bd.time_next_kernel(None, timers.kernel_end)
         bd.repair(q, self.kv, self.block, self.M, self.scale, self.state, out=self.out, ws=self.ws_repair,
                   stream=s)
         if timers and timers.repair_end:

@@ -6,7 +6,9 @@ Usage:
   python -m block_sparse_attention_quest_amd.profiling hbm <fetch counter_collection.csv>
         <write counter_collection.csv> <out.md> --copy-mib N "<fetch command>" "<write command>"
 
-`stats` turns rocprofv3 --kernel-trace --stats output into a short table.  `hbm` takes FETCH_SIZE and
+`stats` turns rocprofv3 --kernel-trace --stats output into a short table; with the kernel trace and the
+bench.py output of the same run it also records the mean duration of the speculative-attention launches
+bench.py timed alone (keyed by the attention source hash, for bench.py to report beside its own figure).  `hbm` takes FETCH_SIZE and
 WRITE_SIZE (KiB per dispatch) of every speculative-attention launch, scales each counter by what it reads
 for a plain device copy of known size (the copy probe bench.py runs with --copy-probe-mib: the copy
 kernel with the largest WRITE_SIZE, matched by dispatch id in the FETCH_SIZE run), and
@@ -85,20 +87,41 @@ def trace_averages(path: str, names=("attn_spec_bf16", "attn_repair_bf16", "sele
     return "\n".join(out)
 
 
-def bench_in_run(log_path: str) -> str:
-    """bench.py's own kernel times (HIP events) from the JSON line of the profiled run, for the
-    cross-check of the two clocks on the same launches."""
+def spec_timed_launches(path: str, skip: int, kernel: str = SPEC_KERNEL) -> list:
+    """Durations (us) of the speculative-attention launches bench.py times alone: the launches on the
+    stream that also runs the cache-flush reductions (the side stream carries the three-stream
+    schedule's launches), after the first `skip` (the warm-up steps')."""
+    rows = list(csv.DictReader(open(path)))
+    flush_streams = {r["Stream_Id"] for r in rows if "reduce_kernel" in r["Kernel_Name"]}
+    sel = [r for r in rows if kernel in r["Kernel_Name"] and r["Stream_Id"] in flush_streams]
+    sel.sort(key=lambda r: int(r["Start_Timestamp"]))
+    return [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in sel[skip:]]
+
+
+def bench_line(log_path: str) -> dict:
     import json
 
     line = [ln for ln in open(log_path) if ln.startswith('{"metric"')][-1]
-    d = json.loads(line)
-    rows = ["bench.py's own figures in the same (profiled) run, event time minus the empty event pair, median "
-            "over the timed steps:", "", "| kernel | us |", "|---|---|"]
+    return json.loads(line)
+
+
+def bench_in_run(d: dict, spec_rocprof: list) -> list:
+    """bench.py's own figures from the JSON line of the profiled run beside rocprofv3's, for the
+    cross-check of the two clocks on the same launches."""
+    rows = ["bench.py's own figures in the same (profiled) run: the GPU time of each call's kernels from HIP "
+            "events bound to the launches (prr_time_next_kernel), over the timed steps:", "",
+            "| kernel | bench.py us (median) |", "|---|---|"]
     for key, name in (("us_spec_attn_median", "attn_spec_bf16"), ("us_repair_median", "attn_repair_bf16"),
                       ("us_select_spec_median", "select_spec_kernel")):
         if d.get(key) is not None:
             rows.append(f"| `{name}` | {d[key]:.2f} |")
-    return "\n".join(rows)
+    rf = d.get("roofline", {})
+    if rf.get("avg_launch_us") is not None and spec_rocprof:
+        r = statistics.mean(spec_rocprof)
+        rows += ["", f"Speculative pass, mean over the {len(spec_rocprof)} timed launches: bench.py "
+                 f"{rf['avg_launch_us']:.2f} us, rocprofv3 {r:.2f} us "
+                 f"({100.0 * (rf['avg_launch_us'] - r) / r:+.2f}%)."]
+    return rows
 
 
 def _per_dispatch(path: str, counter: str) -> dict:
@@ -154,12 +177,25 @@ def main(argv):
         _, src, out, cmd = argv[:4]
         text = ["# Kernel statistics (rocprofv3 --kernel-trace --stats)", "", "Command:", "", "```", cmd, "```",
                 "", stats_table(src), ""]
+        d = bench_line(argv[argv.index("--bench-log") + 1]) if "--bench-log" in argv else None
+        spec = []
         if "--trace" in argv:
+            trace = argv[argv.index("--trace") + 1]
             text += ["Attention launches over non-empty sets (from the kernel trace of the same run):", "",
-                     trace_averages(argv[argv.index("--trace") + 1]), ""]
-        if "--bench-log" in argv:
-            text += [bench_in_run(argv[argv.index("--bench-log") + 1]), ""]
+                     trace_averages(trace), ""]
+            if d is not None:
+                spec = spec_timed_launches(trace, int(d.get("warmup", 0)))
+                spec = spec[-int(d["steps"]):]
+        if spec:
+            text += [f"- kernel: `{SPEC_KERNEL}<128>`",
+                     f"- kernel_source_sha256: `{kernel_source_hash()}`",
+                     f"- attn_spec_timed_launches: {len(spec)}",
+                     f"- attn_spec_avg_us: {statistics.mean(spec):.3f}",
+                     f"- attn_spec_median_us: {statistics.median(spec):.3f}", ""]
+        if d is not None:
+            text += bench_in_run(d, spec) + [""]
         open(out, "w").write("\n".join(text))
+        print("\n".join(text))
     elif argv and argv[0] == "hbm":
         fetch_csv, write_csv, out = argv[1:4]
         i = argv.index("--copy-mib")

@@ -10,7 +10,8 @@
  *
  * Conventions shared by every entry point
  *   - Every pointer named "device" is GPU memory owned by the caller; the library allocates nothing and
- *     keeps no mutable global state.  Host structs are read only during the call.
+ *     keeps no mutable global state (apart from the per-thread arming of prr_time_next_kernel and the
+ *     checking mode's result word).  Host structs are read only during the call.
  *   - Work is enqueued on `stream` and runs asynchronously in stream order.  Nothing is copied to the
  *     host: set sizes stay on the device.
  *   - Problems the host can see (null pointers, sizes, unsupported shapes, a short workspace) return a
@@ -311,6 +312,18 @@ prr_status prr_budget_fit(const double *ctx, int32_t n_ctx, const double *t_sele
 prr_status prr_budget_choose(const double *ctx, int32_t n_ctx, const double *t_select, const double *deltas,
                              int32_t n_delta, const double *t_spec, int32_t degree, const double *coef,
                              double context, int32_t *choice, double *est);
+
+/* ---- kernel timing (measurement) ------------------------------------------------------------ */
+
+/* Arms two HIP events (created by the caller with timing enabled, e.g. hipEventCreate; either may be
+ * NULL) for the next prr_* call on the calling thread that enqueues GPU work.  That call launches its
+ * kernels through hipExtLaunchKernel with these events: `start` takes the start time of its first
+ * kernel and `stop` the end time of its last, so hipEventElapsedTime(start, stop) is the GPU time of the
+ * call's kernels (for a one-kernel call, that kernel's duration), without the cost of separate event
+ * records around them.  The next such call consumes the arming whether or not it launches (a call that
+ * fails its argument checks records nothing); the checking mode's set checks are never timed.  Results
+ * do not depend on it.  Per thread; always PRR_OK. */
+prr_status prr_time_next_kernel(hipEvent_t start, hipEvent_t stop);
 
 /* Human-readable name of a status code (static string). */
 const char *prr_strerror(prr_status status);

@@ -53,7 +53,7 @@ def test_budget_profile_rejects_lengths_that_clip_the_largest_budget():
     args = argparse.Namespace(budget_profile="8192,65536", budget_deltas="0.5,1,4", budget_check="",
                               budget_degree=1, budget_reps=1)
     with pytest.raises(ValueError, match=r"\[8192\]"):   # 128 blocks < 4 x 64
-        bench.budget_profile(args, w, None, None, 0.0)
+        bench.budget_profile(args, w, None, None)
     args.budget_profile, args.budget_check = "16384,65536", "12288"
     with pytest.raises(ValueError, match=r"\[12288\]"):
-        bench.budget_profile(args, w, None, None, 0.0)
+        bench.budget_profile(args, w, None, None)
