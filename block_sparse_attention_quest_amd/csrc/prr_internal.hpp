@@ -44,7 +44,7 @@ hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t 
 
 constexpr int kPage = 16;          // tokens per page (the only supported page size)
 constexpr int kMaxSelectN = 32768; // blocks per (sequence, kv head) the top-K kernels hold on chip
-constexpr int kMaxCalibBlocks = 1024; // calibration: blocks per prefill row (16 per lane of a wave)
+constexpr int kMaxCalibBlocks = 4096; // calibration: blocks per prefill row (16 per thread of four waves)
 constexpr int kMaxCalibGrid = 4096;   // calibration: candidates (alpha, beta, gamma)
 
 struct KvDesc {
@@ -66,6 +66,7 @@ hipError_t launch_attn(const KvDesc &kv, const void *q, int hq, int block, const
                        float *out, bool repair, void *ws, hipStream_t stream);
 
 hipError_t launch_clear(void *ws, size_t bytes, hipStream_t stream);
+
 
 // Checking mode (PRR_CHECK=1 in the environment): validates a block set on the stream and waits for the
 // result; *violation gets a bit mask (1 count outside [0, cap], 2 entry out of range, 4 repeated entry).

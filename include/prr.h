@@ -279,7 +279,7 @@ size_t prr_calibrate_workspace_bytes(int32_t rows, int32_t blocks, int32_t n_can
  * multiply-add).  H[c] = mean of h_phi over phi = 1 .. rows-1 (0 when rows = 1), written to H
  * [n_candidates] (fp64, device); *best (int32, device) = the first candidate with the largest H.
  * Predicted and true sets are exact; H follows float64 rounding of a fixed reduction order.
- * blocks <= 1024, n_candidates <= 4096.  ws: prr_calibrate_workspace_bytes (no initialisation needed). */
+ * blocks <= 4096, n_candidates <= 4096.  ws: prr_calibrate_workspace_bytes (no initialisation needed). */
 prr_status prr_calibrate(const float *scores, int32_t rows, int32_t blocks, int32_t topk, const double *grid,
                          int32_t n_candidates, double *H, int32_t *best, void *ws, size_t ws_bytes,
                          hipStream_t stream);

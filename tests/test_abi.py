@@ -146,7 +146,9 @@ def test_calibrate_argument_errors(lib):
     assert call(rows=0) == 1
     assert call(k=-1) == 1
     assert call(n=0) == 1
-    assert call(blocks=1025) == 2
+    assert call(blocks=4097) == 2
+    # rows of 4096 blocks take four waves: the A-set masks grow with them
+    assert lib.prr_calibrate_workspace_bytes(100, 4096, 80) >= 100 * 256 * 4 + 80 * 2 * 2 * 4096 * 8
     assert call(n=5000) == 2
     assert call(ws=None) == 3
     assert call(wsb=need - 1) == 3

@@ -58,17 +58,27 @@ def test_hand_worked_fixture():
 
 
 @pytest.mark.parametrize("rows,blocks,k,seed", [(300, 100, 17, 1), (129, 64, 8, 2), (200, 512, 128, 3),
-                                                (70, 1000, 300, 4), (66, 33, 5, 5)])
+                                                (70, 1000, 300, 4), (66, 33, 5, 5), (100, 2000, 100, 6),
+                                                (130, 4096, 256, 7), (67, 1025, 1024, 8)])
 def test_random_lognormal_full_grid(rows, blocks, k, seed):
     w = wl.scaled(wl.C5, seed=seed)
     IS = wl.make_calibration_scores(w, rows=rows, blocks=blocks)
     _check(IS, k, orc.calibration_grid(), f"{rows}x{blocks} k={k}")
 
 
-def test_integer_ties():
+@pytest.mark.parametrize("rows,blocks,k", [(90, 70, 20), (60, 3000, 500)])
+def test_integer_ties(rows, blocks, k):
     rng = np.random.default_rng(11)
-    IS = rng.integers(1, 4, size=(90, 70)).astype(np.float32)
-    _check(IS, 20, orc.calibration_grid(), "ties")
+    IS = rng.integers(1, 4, size=(rows, blocks)).astype(np.float32)
+    _check(IS, k, orc.calibration_grid(), f"ties {rows}x{blocks}")
+
+
+def test_prefill_rows_of_4096_blocks():
+    """The pages' 64K-token prefill at 16-token blocks: rows of 4096 blocks (the widest supported), a
+    full grid against the oracle ([paper] A.5)."""
+    w = wl.scaled(wl.C5, seed=9)
+    IS = wl.make_calibration_scores(w, rows=160, blocks=4096)
+    _check(IS, 256, orc.calibration_grid(), "160x4096 k=256")
 
 
 def test_degenerate_cases():
