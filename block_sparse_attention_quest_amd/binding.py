@@ -25,7 +25,7 @@ EXPORTS = (
     "prr_workspace_clear", "prr_build_meta", "prr_mean_meta_bytes", "prr_build_mean_meta", "prr_append",
     "prr_select", "prr_select_spec_workspace_bytes", "prr_select_spec", "prr_select_spec_predict", "prr_predict_workspace_bytes",
     "prr_predict",
-    "prr_spec_attn",
+    "prr_spec_attn", "prr_spec_attn_noalloc",
     "prr_repair", "prr_calibrate_workspace_bytes", "prr_calibrate", "prr_budget_fit", "prr_budget_choose",
     "prr_time_next_kernel", "prr_strerror",
 )
@@ -88,6 +88,8 @@ _SIGS = {
                                    _P(BlockSetStruct), _VP, _SZ, _VP]),
     "prr_spec_attn": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _I32, _P(BlockSetStruct), _F,
                                      _P(AttnStateStruct), _VP, _SZ, _VP]),
+    "prr_spec_attn_noalloc": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _I32, _P(BlockSetStruct), _F,
+                                             _P(AttnStateStruct), _VP]),
     "prr_repair": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _I32, _P(BlockSetStruct), _F,
                                   _P(AttnStateStruct), _VP, _VP, _SZ, _VP]),
     "prr_calibrate_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
@@ -459,6 +461,21 @@ def spec_attn(q: torch.Tensor, kv: KVCache, block: int, P: BlockSet, scale: floa
     st = lib.prr_spec_attn(_ptr(q), Hq, ctypes.byref(s), block, ctypes.byref(ps), float(scale),
                            ctypes.byref(os_), ws.ptr(), ws.nbytes, _stream(stream))
     _check(st, "prr_spec_attn")
+    return out
+
+
+def spec_attn_noalloc(q: torch.Tensor, kv: KVCache, block: int, P: BlockSet, scale: float,
+                      out: Optional[AttnState] = None, stream=None) -> AttnState:
+    """spec_attn with the library's own per-GPU buffer as workspace (prr_spec_attn_noalloc): no
+    workspace argument, nothing allocated by the call; calls that overlap on one GPU race."""
+    lib = load_library()
+    B, Hq, d = q.shape
+    if out is None:
+        out = AttnState.empty(B, Hq, d, q.device)
+    s, ps, os_ = kv.struct(), P.struct(), out.struct()
+    st = lib.prr_spec_attn_noalloc(_ptr(q), Hq, ctypes.byref(s), block, ctypes.byref(ps), float(scale),
+                                   ctypes.byref(os_), _stream(stream))
+    _check(st, "prr_spec_attn_noalloc")
     return out
 
 

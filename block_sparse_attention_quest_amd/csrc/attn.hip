@@ -3,6 +3,8 @@
 
 #include "attn_core.hpp"
 
+#include <mutex>
+
 namespace prr {
 namespace {
 
@@ -46,6 +48,45 @@ __global__ void clear_kernel(uint32_t *w, size_t n) {
         w[i] = 0u;
 }
 
+// The buffer of prr_spec_attn_noalloc: the speculative pass's workspace (arrival counters, partial
+// states) for callers that cannot allocate.  Each GPU the library runs on holds its own copy until the
+// process ends; host code reaches it only through the per-device address below, never by this name.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device of `stream` (the current device for the null stream),
+// looked up once per device with that device current.
+hipError_t scratch_address(hipStream_t stream, void **out) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    int dev = cur;
+    if (stream) {
+        hipDevice_t d = 0;
+        e = hipStreamGetDevice(stream, &d);
+        if (e != hipSuccess) return e;
+        dev = d;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress((void **)&ptr, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 size_t attn_workspace_bytes(int batch, int hq, int hkv, int d, int block, int cap) {
@@ -72,6 +113,19 @@ hipError_t launch_attn(const KvDesc &kv, const void *q, int hq, int block, const
         else k = d128 ? attn_spec_f32<128> : attn_spec_f32<64>;
     }
     return launch(k, dim3(grid), dim3(kThreads), stream, p);
+}
+
+hipError_t launch_spec_noalloc(const KvDesc &kv, const void *q, int hq, int block, const int32_t *idx,
+                               const int32_t *count, int cap, float scale, float *acc, float *l, float *m,
+                               hipStream_t stream) {
+    void *ws = nullptr;
+    hipError_t e = scratch_address(stream, &ws);
+    if (e != hipSuccess) return e;
+    // the arrival counters must start at zero (a fill kernel: no memset node); the partial states are
+    // written before they are read
+    e = launch_clear(ws, counters_bytes(kv.batch * kv.hkv), stream);
+    if (e != hipSuccess) return e;
+    return launch_attn(kv, q, hq, block, idx, count, cap, scale, acc, l, m, nullptr, false, ws, stream);
 }
 
 hipError_t launch_clear(void *ws, size_t bytes, hipStream_t stream) {

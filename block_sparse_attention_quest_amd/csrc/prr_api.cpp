@@ -344,6 +344,24 @@ prr_status prr_spec_attn(const void *q, int32_t num_q_heads, const prr_kv_cache 
                                        out->acc, out->l, out->m, nullptr, false, ws, stream));
 }
 
+prr_status prr_spec_attn_noalloc(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, int32_t block,
+                                 const prr_block_set *P, float scale, prr_attn_state *out, hipStream_t stream) {
+    CallTiming timing_;
+    static_assert(PRR_NOALLOC_SCRATCH_BYTES == prr::kNoAllocScratchBytes, "scratch size");
+    if (!q) return PRR_EINVAL;
+    PRR_TRY(check_kv(kv));
+    PRR_TRY(check_block(kv, block));
+    PRR_TRY(check_heads(kv, num_q_heads));
+    PRR_TRY(check_set(P));
+    if (!out || !out->acc || !out->l || !out->m) return PRR_EINVAL;
+    if (prr::attn_workspace_bytes(kv->batch, num_q_heads, kv->num_kv_heads, kv->head_dim, block, P->cap) >
+        prr::kNoAllocScratchBytes)
+        return PRR_EWORKSPACE;
+    PRR_TRY(check_input_set(kv, block, P, stream));
+    return hip_status(prr::launch_spec_noalloc(desc(kv), q, num_q_heads, block, P->idx, P->count, P->cap, scale,
+                                               out->acc, out->l, out->m, stream));
+}
+
 prr_status prr_repair(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, int32_t block,
                       const prr_block_set *M, float scale, prr_attn_state *state, float *out,
                       void *ws, size_t ws_bytes, hipStream_t stream) {

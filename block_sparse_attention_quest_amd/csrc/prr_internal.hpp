@@ -67,6 +67,12 @@ hipError_t launch_attn(const KvDesc &kv, const void *q, int hq, int block, const
 
 hipError_t launch_clear(void *ws, size_t bytes, hipStream_t stream);
 
+// The speculative pass with the library's own per-device buffer of kNoAllocScratchBytes as its workspace
+// (prr_spec_attn_noalloc); the caller has checked that attn_workspace_bytes fits.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+hipError_t launch_spec_noalloc(const KvDesc &kv, const void *q, int hq, int block, const int32_t *idx,
+                               const int32_t *count, int cap, float scale, float *acc, float *l, float *m,
+                               hipStream_t stream);
 
 // Checking mode (PRR_CHECK=1 in the environment): validates a block set on the stream and waits for the
 // result; *violation gets a bit mask (1 count outside [0, cap], 2 entry out of range, 4 repeated entry).

@@ -254,6 +254,18 @@ prr_status prr_spec_attn(const void *q, int32_t num_q_heads, const prr_kv_cache 
                          const prr_block_set *P, float scale, prr_attn_state *out, void *ws,
                          size_t ws_bytes, hipStream_t stream);
 
+/* prr_spec_attn without a workspace argument, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the arrival counters and
+ * partial states live in a buffer of PRR_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on until the process ends (the GPU of `stream`, the current one for the null stream).  The call
+ * allocates nothing; it clears the counters with a fill kernel, then runs prr_spec_attn's kernel, with the
+ * same results.  Sets whose prr_attn_workspace_bytes(..., P->cap) exceeds the buffer give PRR_EWORKSPACE
+ * (nothing enqueued).  Every call on one GPU shares that GPU's buffer: calls that overlap on one GPU (on
+ * different streams, or from different threads without ordering) race and give wrong results. */
+#define PRR_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+prr_status prr_spec_attn_noalloc(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, int32_t block,
+                                 const prr_block_set *P, float scale, prr_attn_state *out, hipStream_t stream);
+
 /* Incremental repair ([paper] §4.3, repair via online softmax; [blog] Eq. (6)): folds the tokens of the
  * missed blocks M into `state` in place with the online-softmax recurrence
  *     m' = max(m, m~),  l' = e^{m - m'} l + e^{m~ - m'} l~,  acc' = e^{m - m'} acc + e^{m~ - m'} acc~
