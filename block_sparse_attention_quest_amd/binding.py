@@ -95,7 +95,7 @@ _SIGS = {
     "prr_calibrate_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "prr_calibrate": (ctypes.c_int, [_VP, _I32, _I32, _I32, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]),
     "prr_budget_fit": (ctypes.c_int, [_VP, _I32, _VP, _VP, _I32, _VP, _I32, _VP]),
-    "prr_budget_choose": (ctypes.c_int, [_VP, _I32, _VP, _VP, _I32, _VP, _I32, _VP, _D, _VP, _VP]),
+    "prr_budget_choose": (ctypes.c_int, [_VP, _I32, _VP, _VP, _I32, _VP, _I32, _VP, _D, _VP, _VP, _I32, _VP]),
     "prr_time_next_kernel": (ctypes.c_int, [_VP, _VP]),
     "prr_strerror": (ctypes.c_char_p, [ctypes.c_int]),
 }
@@ -294,9 +294,12 @@ def select_spec_workspace_for(kv: KVCache, hq: int, block: int, topk: int, cap: 
                      kv.k.device)
 
 
-def predict_workspace_for(batch: int, num_kv_heads: int, max_blocks: int, budget: int, device="cuda"):
-    """Workspace for predict() (None where the rows are short enough not to need one)."""
-    n = load_library().prr_predict_workspace_bytes(batch, num_kv_heads, max_blocks, budget)
+def predict_workspace_for(batch: int, num_kv_heads: int, max_blocks: int, budget, device="cuda"):
+    """Workspace for predict() at |P| = budget, or at every budget of an iterable of them (the largest
+    size any of them needs); None where none needs one (short rows)."""
+    lib = load_library()
+    budgets = [budget] if isinstance(budget, int) else list(budget)
+    n = max((lib.prr_predict_workspace_bytes(batch, num_kv_heads, max_blocks, b) for b in budgets), default=0)
     return Workspace(n, device) if n else None
 
 
@@ -553,5 +556,16 @@ class BudgetTable:
         est = np.zeros(1 + len(self.deltas), dtype=np.float64)
         choice = ctypes.c_int32(0)
         _check(load_library().prr_budget_choose(*self._table(), self.coef.ctypes.data, float(context),
-                                                ctypes.addressof(choice), est.ctypes.data), "prr_budget_choose")
+                                                ctypes.addressof(choice), est.ctypes.data, 0, None),
+               "prr_budget_choose")
         return int(choice.value), est
+
+    def budget_blocks(self, context: float, topk: int) -> int:
+        """|P| in blocks at `context` tokens for a top-K of `topk` blocks (prr_budget_choose): floor(delta K)
+        at the chosen delta, or at the smallest profiled delta when none fits."""
+        choice = ctypes.c_int32(0)
+        blocks = ctypes.c_int32(0)
+        _check(load_library().prr_budget_choose(*self._table(), self.coef.ctypes.data, float(context),
+                                                ctypes.addressof(choice), None, int(topk), ctypes.addressof(blocks)),
+               "prr_budget_choose")
+        return int(blocks.value)

@@ -792,11 +792,7 @@ int attn_setup(AttnParams &p, const KvDesc &kv, const void *q, int hq, int block
     // missed part of a selection), so repair uses half that chunk size to keep the chip busy, and up
     // to two workgroups per CU (it runs alone, two waves per SIMD), so that every chunk of a set at full
     // capacity has a workgroup of its own instead of waiting for another chunk of the same workgroup.
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) cus = n;
-    }
+    const int cus = device_cu_count();
     const long target = target_wgs > 0 ? target_wgs : cus;
     const long cap_pages = (long)cap * p.ppb;
     const long full = (long)units * cap_pages;

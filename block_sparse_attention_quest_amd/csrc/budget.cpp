@@ -24,6 +24,7 @@
 // The fit solves the least-squares problem by Householder QR of the Vandermonde matrix (no normal
 // equations), in float64.
 
+#include <algorithm>
 #include <cmath>
 
 #include "prr.h"
@@ -121,10 +122,11 @@ prr_status prr_budget_fit(const double *ctx, int32_t n_ctx, const double *t_sele
 
 prr_status prr_budget_choose(const double *ctx, int32_t n_ctx, const double *t_select, const double *deltas,
                              int32_t n_delta, const double *t_spec, int32_t degree, const double *coef,
-                             double context, int32_t *choice, double *est) {
+                             double context, int32_t *choice, double *est, int32_t topk, int32_t *budget_blocks) {
     const prr_status st = check_table(ctx, n_ctx, t_select, deltas, n_delta, t_spec, degree);
     if (st != PRR_OK) return st;
     if (!coef || !choice || !is_fin(context) || context <= 0.0) return PRR_EINVAL;
+    if (budget_blocks && topk < 0) return PRR_EINVAL;
     const int nc = degree + 1;
     int row = -1;
     for (int i = 0; i < n_ctx; ++i)
@@ -137,6 +139,14 @@ prr_status prr_budget_choose(const double *ctx, int32_t n_ctx, const double *t_s
         const double sp = row >= 0 ? t_spec[(size_t)j * n_ctx + row] : horner(coef + (size_t)(1 + j) * nc, nc, x);
         if (est) est[1 + j] = sp;
         if (sp <= sel) best = j;
+    }
+    // |P| <= delta |A| (Eq. 1): the largest admissible set, floor(delta K), with a relative slack of 1e-9 for
+    // products that round just below an integer; no fitting delta: the smallest profiled one
+    if (budget_blocks) {
+        const double x = deltas[best >= 0 ? best : 0] * (double)topk;
+        const double n = std::floor(x + 1e-9 * std::max(1.0, x));
+        if (!(n <= (double)INT32_MAX)) return PRR_EINVAL;
+        *budget_blocks = (int32_t)n;
     }
     *choice = best;
     return PRR_OK;

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 
 #include "prr_internal.hpp"
@@ -115,6 +116,17 @@ prr_status attn_common(const void *q, int32_t hq, const prr_kv_cache *kv, int32_
 }  // namespace
 
 namespace prr {
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 bool take_kernel_timing(hipEvent_t *start, hipEvent_t *stop) {
     if (!t_call.start && !t_call.stop) return false;
     *start = t_call.start;   // the call's first kernel only

@@ -42,6 +42,10 @@ hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t 
         if (prr_e_ != hipSuccess) return prr_e_;           \
     } while (0)
 
+// Compute units of the current device (the launch shapes spread work over them), queried once per
+// device and kept: a device property, not state that calls change.
+int device_cu_count();
+
 constexpr int kPage = 16;          // tokens per page (the only supported page size)
 constexpr int kMaxSelectN = 32768; // blocks per (sequence, kv head) the top-K kernels hold on chip
 constexpr int kMaxCalibBlocks = 4096; // calibration: blocks per prefill row (16 per thread of four waves)

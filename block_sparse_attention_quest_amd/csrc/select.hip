@@ -416,6 +416,8 @@ static PredictPlan predict_plan(int nmax, int budget) {
         SelectSpecPlan &g = pl.groups;
         g.kl = pl.kl;
         g.gp = std::max(1, 2048 / pl.kl);
+        if ((long)((pl.nparts + g.gp - 1) / g.gp) * std::min(budget, g.gp * pl.kl) > 4096)
+            g.gp = std::max(1, 4096 / pl.kl);   // groups of up to 4096 slots leave fewer candidates to rank
         g.ng = (pl.nparts + g.gp - 1) / g.gp;
         g.kl2 = std::min(budget, g.gp * pl.kl);
         const long s2 = (long)std::min(g.gp, pl.nparts) * pl.kl, s3 = (long)g.ng * g.kl2;

@@ -31,8 +31,11 @@ SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean) {
             // three stages: groups of parts with up to 2048 candidate slots keep their top-K each, and
             // one ranking of the groups' candidates (up to 4096 slots) follows.  At 32768 blocks and
             // K = 256 (8 groups of 8 parts) this took the 512K layer step from 96.9 to 73.6 us; groups of
-            // 4096 slots (4 per unit, fewer workgroups) took 76.7 us.
-            const int gp = std::max(1, 2048 / kl);
+            // 4096 slots (4 per unit, fewer workgroups) took 76.7 us, so they are used only where groups
+            // of 2048 slots would leave more than one ranking holds (K above 341 at 32768 blocks).
+            int gp = std::max(1, 2048 / kl);
+            if ((long)((nsx + gp - 1) / gp) * std::min(topk, gp * kl) > 4096)
+                gp = std::max(1, 4096 / kl);   // groups of up to 4096 slots, so that fewer candidates remain
             const int ng = (nsx + gp - 1) / gp;
             const int kl2 = std::min(topk, gp * kl);
             const long slots2 = (long)std::min(gp, nsx) * kl, slots3 = (long)ng * kl2;

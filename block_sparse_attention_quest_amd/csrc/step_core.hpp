@@ -147,11 +147,7 @@ hipError_t launch_select_spec_t(const KvDesc &kv, const void *q, int hq, const v
     // those slots (rows longer than 512 blocks per CU's share, e.g. a cache with room for appended
     // tokens), the speculative pass is spread over the slots that are left, so that the whole grid is
     // resident from the start instead of speculative workgroups waiting for scoring ones to finish.
-    int cus = 256, dev = 0;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) cus = n;
-    }
+    const int cus = device_cu_count();
     const int n_score_wgs = (nmax + select_spec_score_bpw(mean) - 1) / select_spec_score_bpw(mean) *
                             kv.batch * kv.hkv;
     const int spec_target = n_score_wgs > cus ? std::max(cus / 2, 2 * cus - n_score_wgs) : cus;

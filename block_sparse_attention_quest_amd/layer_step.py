@@ -112,15 +112,18 @@ class PRRLayer:
         self.out = torch.zeros((B, num_q_heads, d), dtype=torch.float32, device=dev)
         self.ws_spec = bd.select_spec_workspace_for(kv, num_q_heads, block, topk, self.max_budget)
         self.ws_repair = bd.workspace_for(kv, num_q_heads, block, max(1, topk))
-        self.ws_predict = bd.predict_workspace_for(B, H, self.nmax, self.max_budget, dev)
+        # the predictor's workspace depends on |P| and is not monotone in it (a budget with no part-parallel
+        # plan needs none): sized for every budget set_budget may choose
+        self.ws_predict = bd.predict_workspace_for(B, H, self.nmax, range(1, self.max_budget + 1), dev)
         self._streams = None
         self.pending_predict: Optional[bd.PredictArgs] = None
 
     def set_budget(self, budget: int):
         """|P| of the predictions made from the next step on (e.g. from speculation_budget() as the context
-        grows); 1 <= budget <= max_budget.  The set already predicted for the next step keeps its size."""
-        if not 1 <= int(budget) <= self.max_budget:
-            raise ValueError(f"budget {budget} outside [1, {self.max_budget}] (raise max_budget at construction)")
+        grows); 0 <= budget <= max_budget (0: no speculation, repair covers all of A).  The set already
+        predicted for the next step keeps its size."""
+        if not 0 <= int(budget) <= self.max_budget:
+            raise ValueError(f"budget {budget} outside [0, {self.max_budget}] (raise max_budget at construction)")
         self.budget = int(budget)
 
     @property
@@ -286,10 +289,7 @@ class PRRStack:
 
 
 def speculation_budget(table: bd.BudgetTable, context: int, topk: int) -> int:
-    """|P| in blocks for a layer at `context` tokens ([paper] §4.4; Eq. 1, |P| <= delta |A|): round(delta K)
-    for the table's largest delta whose speculative pass ends no later than selection.  When no profiled
-    delta fits, the smallest one is taken (speculation over fewer blocks leaves more to repair, which is
-    on the critical path as well), and never fewer than one block."""
-    j, _ = table.choose(float(context))
-    delta = float(table.deltas[j if j >= 0 else 0])
-    return max(1, int(round(delta * topk)))
+    """|P| in blocks for a layer at `context` tokens ([paper] §4.4; Eq. 1, |P| <= delta |A|): the library's
+    choice (prr_budget_choose), floor(delta K) for the table's largest delta whose speculative pass ends no
+    later than selection, or for its smallest delta when none fits."""
+    return table.budget_blocks(float(context), int(topk))

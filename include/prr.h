@@ -205,7 +205,9 @@ prr_status prr_select_spec(const void *q, int32_t num_q_heads, const prr_kv_cach
  * 512-block parts in parallel and P_next is ranked from the parts' local top-|P| candidates (exact, as
  * in the two-stage top-K; with more than 4096 candidate slots, groups of parts keep their top-|P| in
  * between); without it one workgroup per (b, kvh) does the whole row.  Same results either way.  A
- * non-NULL ws smaller than the query gives PRR_EWORKSPACE. */
+ * non-NULL ws smaller than the query gives PRR_EWORKSPACE.  The query is 0 where no workspace is used:
+ * rows of up to 2048 blocks, and budgets with no part-parallel plan (above 512 at 32768 blocks); it is not
+ * monotone in the budget, so a workspace for several budgets takes the largest of their queries. */
 size_t prr_predict_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t max_blocks, int32_t budget);
 
 prr_status prr_predict(const double *scores, const int32_t *seq_len, int32_t batch,
@@ -316,14 +318,18 @@ prr_status prr_calibrate(const float *scores, int32_t rows, int32_t blocks, int3
  * a profiled length, else the polynomials of prr_budget_fit (coef from the same table and degree).
  * *choice = the largest j with est_spec[j] <= est_select (the largest delta whose speculative pass ends
  * no later than selection), or -1 when there is none.  est [1 + n_delta] (nullable) receives est_select then
- * est_spec[0 .. n_delta). */
+ * est_spec[0 .. n_delta).  *budget_blocks (nullable; then topk is not read) = |P| in blocks for a top-K of
+ * `topk` (>= 0) blocks: the largest set Eq. (1), |P| <= delta |A|, admits, floor(delta topk) (float64, with a
+ * relative slack of 1e-9 for products that round just below an integer), at the chosen delta, or at the
+ * smallest profiled delta when none fits (speculating over fewer blocks leaves more to repair, which is on
+ * the critical path too). */
 #define PRR_BUDGET_MAX_POINTS 64
 #define PRR_BUDGET_MAX_DEGREE 4
 prr_status prr_budget_fit(const double *ctx, int32_t n_ctx, const double *t_select, const double *deltas,
                           int32_t n_delta, const double *t_spec, int32_t degree, double *coef);
 prr_status prr_budget_choose(const double *ctx, int32_t n_ctx, const double *t_select, const double *deltas,
                              int32_t n_delta, const double *t_spec, int32_t degree, const double *coef,
-                             double context, int32_t *choice, double *est);
+                             double context, int32_t *choice, double *est, int32_t topk, int32_t *budget_blocks);
 
 /* ---- kernel timing (measurement) ------------------------------------------------------------ */
 

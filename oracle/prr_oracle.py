@@ -458,6 +458,17 @@ def budget_estimates(ctx, t_select, t_spec, coef: np.ndarray, context: float) ->
     return np.array([sum(c * x ** k for k, c in enumerate(row)) for row in coef])
 
 
+def budget_blocks(deltas, choice: int, topk: int) -> int:
+    """|P| in blocks for the chosen ratio ([blog] Eq. (1): |P| <= delta |A|, with |A| = topk).  Reading: the
+    largest set the constraint admits, floor(delta topk) (the product in float64 with a relative slack of
+    1e-9, so that a product that rounds just below an integer still reaches it); when no ratio fits
+    (choice -1), the smallest profiled ratio (speculating over fewer blocks leaves more to repair, which
+    is on the critical path too)."""
+    d = float(deltas[choice if choice >= 0 else 0])
+    x = d * float(topk)
+    return int(np.floor(x + 1e-9 * max(1.0, x)))
+
+
 def budget_choose(ctx, t_select, deltas, t_spec, coef: np.ndarray, context: float):
     """The largest profiled budget ratio whose speculative latency is at most the selection latency at
     `context` tokens ([paper] §4.4: speculation must not outlast selection, else it extends the critical

@@ -122,6 +122,12 @@ def test_select_and_predict_argument_errors(lib):
     stage1 = 256 + units * 64 * 256 * 12 + units * 64 * 4
     assert lib.prr_predict_workspace_bytes(1, 8, 32768, 256) == \
         (stage1 + 255) // 256 * 256 + units * 8 * 256 * 12 + units * 8 * 4
+    # above 341 candidates per part, groups of 4096 slots keep the ranking in range up to a budget of 512
+    # (400: 10 parts per group, 7 groups); beyond it, one workgroup per unit and no workspace
+    stage1 = 256 + units * 64 * 400 * 12 + units * 64 * 4
+    assert lib.prr_predict_workspace_bytes(1, 8, 32768, 400) == \
+        (stage1 + 255) // 256 * 256 + units * 7 * 400 * 12 + units * 7 * 4
+    assert lib.prr_predict_workspace_bytes(1, 8, 32768, 513) == 0
     assert pred(nmax=8192, ws=1, wsb=need - 1) == 3
     assert pred(nmax=40000) == 2
     assert lib.prr_build_meta(ctypes.byref(kv), 64, None, None) == 1

@@ -57,3 +57,22 @@ def test_budget_profile_rejects_lengths_that_clip_the_largest_budget():
     args.budget_profile, args.budget_check = "16384,65536", "12288"
     with pytest.raises(ValueError, match=r"\[12288\]"):
         bench.budget_profile(args, w, None, None)
+
+
+def test_oracle_pool_calibration_deals_the_grid_and_matches_the_oracle():
+    """The calibration leg's all-core oracle run: candidates dealt round-robin to the workers come back in
+    grid order and equal the oracle's own grid search."""
+    import numpy as np
+
+    from oracle import prr_oracle as orc
+
+    bench = _bench()
+    IS = wl.make_calibration_scores(wl.C5, rows=40, blocks=48).astype(np.float64)
+    grid = orc.calibration_grid()
+    pool = bench.OraclePool(3)
+    try:
+        wall, H = pool.calibrate(IS, 8, grid)
+    finally:
+        pool.close()
+    ref, _ = orc.calibrate(IS, 8, grid)
+    assert wall > 0 and np.array_equal(H, ref)

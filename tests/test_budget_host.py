@@ -102,11 +102,16 @@ def test_degree_above_the_points_is_rejected_and_choose_checks_context():
     tab = bd.BudgetTable([1.0, 2.0], [1.0, 2.0], [1.0], [[1.0, 1.0]], 1)
     choice = ctypes.c_int32(5)
     for bad in (0.0, -3.0, float("nan"), float("inf")):
-        st = lib.prr_budget_choose(*tab._table(), tab.coef.ctypes.data, bad, ctypes.addressof(choice), None)
+        st = lib.prr_budget_choose(*tab._table(), tab.coef.ctypes.data, bad, ctypes.addressof(choice), None, 0, None)
         assert st == 1 and choice.value == 5
     # est is optional
-    assert lib.prr_budget_choose(*tab._table(), tab.coef.ctypes.data, 1.5, ctypes.addressof(choice), None) == 0
+    assert lib.prr_budget_choose(*tab._table(), tab.coef.ctypes.data, 1.5, ctypes.addressof(choice), None, 0,
+                                 None) == 0
     assert choice.value == 0
+    # a negative top-K is refused when |P| is asked for
+    blocks = ctypes.c_int32(7)
+    assert lib.prr_budget_choose(*tab._table(), tab.coef.ctypes.data, 1.5, ctypes.addressof(choice), None, -1,
+                                 ctypes.addressof(blocks)) == 1 and blocks.value == 7
 
 
 def test_speculation_budget_blocks():
@@ -119,4 +124,21 @@ def test_speculation_budget_blocks():
     assert speculation_budget(tab, 16384, 64) == 128    # delta 2
     slow = bd.BudgetTable(ctx, [1.0, 1.0, 1.0], deltas, spec, 1)
     assert speculation_budget(slow, 8192, 64) == 32     # nothing fits: the smallest delta
-    assert speculation_budget(slow, 8192, 1) == 1
+    assert speculation_budget(slow, 8192, 1) == 0       # |P| <= 0.5 |A| = 0.5 admits no block
+
+
+def test_budget_blocks_match_the_oracle():
+    """|P| in blocks from the C ABI against the oracle's budget_blocks over random tables, lengths (on and
+    off the grid) and top-K sizes, with ratios whose products land near integers."""
+    rng = np.random.default_rng(17)
+    ctx = [4096.0, 8192.0, 16384.0, 32768.0]
+    deltas = [0.0, 0.29, 0.7, 1.0, 1.25, 2.5]
+    for _ in range(40):
+        sel = np.sort(rng.uniform(5, 60, size=4))
+        spec = np.sort(rng.uniform(2, 80, size=(len(deltas), 1)), axis=0) + rng.uniform(0, 5, size=(len(deltas), 4))
+        tab = bd.BudgetTable(ctx, sel, deltas, spec, 1)
+        coef = O.budget_fit(ctx, sel, deltas, spec, 1)
+        for T in (4096.0, 12000.0, 32768.0, 50000.0):
+            for k in (0, 1, 3, 64, 100, 257):
+                j, _ = O.budget_choose(ctx, sel, deltas, spec, coef, T)
+                assert tab.budget_blocks(T, k) == O.budget_blocks(deltas, j, k), (T, k, j)

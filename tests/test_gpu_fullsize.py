@@ -176,6 +176,14 @@ def test_ctx128k_batch8_trajectory_with_budget_changes():
     _trajectory(wl.C3, 4, [(1, 6), (4, 2)], wl.C3.ema, [64, 128, 32, 64])
 
 
+def test_ctx512k_trajectory_with_budgets_above_341():
+    """32768 blocks per row (512K at 16-token blocks) with |P| above 341, where the predictor's ranking
+    takes groups of 4096 candidate slots, and its workspace is sized over every budget the layer may use:
+    |P| = 400, 342, then 256, against the oracle step by step."""
+    w = wl.scaled(wl.C4, name="ctx512k_traj", steps=3, drift_rho=0.9, query_mean_gain=0.64)
+    _trajectory(w, 3, [(0, 1), (0, 6)], wl.C3.ema, [400, 342, 256])
+
+
 def test_ctx128k_batch8_fp8_trajectory():
     """The same workload with an fp8 (E4M3) cache, as `bench.py --kv-dtype fp8` runs it."""
     _trajectory(wl.scaled(wl.C3, dtype="fp8"), 3, [(1, 1), (6, 4)], wl.C3.ema)

@@ -85,6 +85,9 @@ CASES = [
     ("bf16_d128_g16_s32", 1, 16, 1, 128, 32, [900], "bf16"),
     ("bf16_d128_g1_s16", 1, 4, 4, 128, 16, [333], "bf16"),
     ("bf16_d128_g2_s48", 2, 4, 2, 128, 48, [960, 97], "bf16"),
+    ("bf16_d128_g4_s128", 2, 8, 2, 128, 128, [6144, 4999], "bf16"),
+    ("bf16_d128_g4_s256", 1, 8, 2, 128, 256, [8192 - 77], "bf16"),
+    ("fp8_d128_g4_s256", 2, 8, 2, 128, 256, [7000, 8192], "fp8"),
     ("fp8_d128_g4_s16", 2, 8, 2, 128, 16, [1000, 611], "fp8"),
     ("fp8_d64_g8_s32", 1, 16, 2, 64, 32, [1777], "fp8"),
     ("fp8_d128_g2_s64", 2, 4, 2, 128, 64, [2048, 97], "fp8"),
@@ -305,15 +308,17 @@ def test_predictor_trajectory_bit_exact():
 
 
 @pytest.mark.parametrize("nblocks,topk", [(300, 40), (900, 40), (2048, 40), (2049, 40), (4097, 40),
-                                         (8192, 128), (4096, 600), (8192, 600), (16384, 300)])
+                                         (8192, 128), (4096, 600), (8192, 600), (16384, 300), (32768, 400),
+                                         (32768, 512)])
 def test_select_spec_fused_topk_shapes(nblocks, topk):
     """The fused launch's top-K runs in the last scoring workgroup: over all scores with 1, 2 or 4 keys
     per thread (units of up to 1024 blocks), and beyond that in two stages (local top-min(K, 512)
     candidates of every scoring workgroup, then the top-K of the candidates, up to 16 per thread; K = 600
     caps the local candidates at 512).  With more than 4096 candidate slots (8192 blocks at K = 600,
     16384 at K = 300) a third stage follows the launch: groups of parts (up to 2048 candidate slots) keep
-    their top-K, and the unit's last group ranks the groups' candidates.  Every shape against the separate calls (bit for bit) and the
-    oracle's scores and sets."""
+    their top-K, and the unit's last group ranks the groups' candidates; at 32768 blocks with K above 341,
+    groups of up to 4096 slots keep the last ranking within 4096 slots.  Every shape against the separate
+    calls (bit for bit) and the oracle's scores and sets."""
     lens = [nblocks * 16, nblocks * 16 - 37]
     w = wl.Workload(f"fused_{nblocks}", 2, 8, 2, 64, max(lens), 16, topk, "bf16", seed=900 + nblocks,
                     seq_lens=lens)

@@ -106,3 +106,19 @@ def test_longer_selection_never_lowers_the_choice():
             j, _ = O.budget_choose([4096.0], [s], list(range(6)), spec, np.zeros((7, 1)), 4096.0)
             assert j >= last
             last = j
+
+
+@pytest.mark.parametrize("deltas,choice,topk,want", [
+    ([0.5, 1.0, 2.0], 1, 64, 64),        # delta 1: |P| = K
+    ([0.5, 1.0, 2.0], 2, 64, 128),       # delta 2
+    ([0.75], 0, 2, 1),                   # 1.5 blocks allowed: |P| <= delta |A| admits 1, not 2
+    ([0.25, 1.5], 1, 3, 4),              # 4.5 -> 4
+    ([0.5, 1.0], -1, 64, 32),            # nothing fits: the smallest profiled ratio
+    ([0.0, 1.0], 0, 64, 0),              # delta 0: no speculation
+    ([0.29], 0, 100, 29),                # 0.29 * 100 rounds to 28.999999999999996 in float64
+    ([0.7], 0, 10, 7),                   # 7.000000000000001
+    ([1.0], 0, 0, 0),                    # K = 0: |A| = 0
+])
+def test_budget_blocks_is_the_largest_set_the_constraint_admits(deltas, choice, topk, want):
+    """[blog] Eq. (1): |P| <= delta |A|; the largest admissible |P| is floor(delta K)."""
+    assert O.budget_blocks(deltas, choice, topk) == want

@@ -193,13 +193,29 @@ def budget_choose_smallest(ctx, t_select, deltas, t_spec, coef, context):
     return (min(fits) if fits else -1), est
 
 
+def budget_blocks_rounded(deltas, choice, topk):
+    return int(round(float(deltas[choice if choice >= 0 else 0]) * topk))
+
+
+def budget_blocks_no_slack(deltas, choice, topk):
+    return int(np.floor(float(deltas[choice if choice >= 0 else 0]) * topk))
+
+
+def budget_blocks_largest_fallback(deltas, choice, topk):
+    d = float(deltas[choice if choice >= 0 else -1])
+    x = d * topk
+    return int(np.floor(x + 1e-9 * max(1.0, x)))
+
+
 def _budget_checks():
     hand = [(tb.test_choice_on_the_hand_table, (c, w)) for c, w in [(4096.0, 1), (8192.0, 2), (16384.0, 2)]]
     return [(tb.test_fit_recovers_an_exact_polynomial, (2,)), (tb.test_degree_zero_is_the_mean_and_degree_one_the_textbook_line, ()),
             (tb.test_residual_is_orthogonal_to_every_column, (2,)), (tb.test_as_many_points_as_coefficients_interpolates, ()),
             *hand, (tb.test_off_grid_length_reads_the_line, ()),
             (tb.test_no_fitting_ratio_gives_minus_one_and_delta_zero_always_fits, ()),
-            (tb.test_longer_selection_never_lowers_the_choice, ())]
+            (tb.test_longer_selection_never_lowers_the_choice, ()),
+            *[(tb.test_budget_blocks_is_the_largest_set_the_constraint_admits, c) for c in (
+                ([0.75], 0, 2, 1), ([0.25, 1.5], 1, 3, 4), ([0.5, 1.0], -1, 64, 32), ([0.29], 0, 100, 29))]]
 
 
 def _fp8_checks():
@@ -258,6 +274,9 @@ MUTATIONS = [
     ("budget_estimates", budget_estimates_scaled_by_shortest, _budget_checks),
     ("budget_choose", budget_choose_strict, _budget_checks),
     ("budget_choose", budget_choose_smallest, _budget_checks),
+    ("budget_blocks", budget_blocks_rounded, _budget_checks),
+    ("budget_blocks", budget_blocks_no_slack, _budget_checks),
+    ("budget_blocks", budget_blocks_largest_fallback, _budget_checks),
 ]
 
 
