@@ -68,6 +68,8 @@ def parse_args():
                          "with the predictor on its own")
     ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default=None,
                     help="cache element type (default: the workload's, bf16); fp8 = E4M3 K/V with bf16 queries")
+    ap.add_argument("--layer-step", choices=("one", "two"), default="one",
+                    help="the layer step as one launch (prr_layer_step) or as prr_select_spec + prr_repair")
     ap.add_argument("--score-mode", choices=("quest", "mean"), default="quest",
                     help="block summary selection scores: Quest's min/max bound or the block's mean key")
     ap.add_argument("--append", action="store_true",
@@ -438,7 +440,8 @@ def delta_sweep(args, w, inp, kv, meta, flush, ev):
     n = min(args.delta_steps, w.steps - 1)
     for d in [float(x) for x in args.delta_sweep.split(",") if x.strip()]:
         budget = max(1, int(round(d * w.topk)))
-        L = PRRLayer(kv, w.num_q_heads, w.block, w.topk, budget, ema=w.ema, scale=w.scale)
+        L = PRRLayer(kv, w.num_q_heads, w.block, w.topk, budget, ema=w.ema, scale=w.scale,
+                     fused=args.layer_step == "one")
         for t in range(3):
             L.step(inp.q[t])
         torch.cuda.synchronize()
@@ -590,7 +593,7 @@ def measure_stack(args, w, layer0, inp0, flush, ev):
         inp = wl.make_inputs(wi, layer0.kv.k.device)
         kv = bd.KVCache(inp.k_cache, inp.v_cache, inp.page_table, inp.seq_len)
         layers.append(PRRLayer(kv, w.num_q_heads, w.block, w.topk, w.topk, ema=w.ema, scale=w.scale,
-                               score_mode=args.score_mode))
+                               score_mode=args.score_mode, fused=args.layer_step == "one"))
         qs.append(inp.q)
         del inp
     torch.cuda.synchronize()
@@ -667,7 +670,7 @@ def main():
     inp = wl.make_inputs(w, dev)
     kv = bd.KVCache(inp.k_cache, inp.v_cache, inp.page_table, inp.seq_len)
     layer = PRRLayer(kv, w.num_q_heads, w.block, w.topk, w.topk, ema=w.ema, scale=w.scale,
-                     score_mode=args.score_mode)
+                     score_mode=args.score_mode, fused=args.layer_step == "one")
     if args.append:
         k_app, v_app = wl.make_append_tokens(w, dev)
         len0 = inp.seq_len.clone()
@@ -902,6 +905,7 @@ def main():
                    "head_dim": w.head_dim, "context": w.context, "block": w.block, "topk_blocks": w.topk,
                    "spec_budget_blocks": w.topk, "ema": list(w.ema), "decode_steps_timed": K,
                    "score_mode": args.score_mode, "kv_dtype": w.dtype,
+                   "layer_step": "one launch" if args.layer_step == "one" else "select_spec + repair",
                    "parallelism": "none (1 GPU)", "flush_mib_read_between_kernels": args.flush_mib},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "value_median_step_gbps": round(float(statistics.median(step_gbps)), 1),

@@ -23,7 +23,8 @@ PAGE_SIZE = 16
 EXPORTS = (
     "prr_max_blocks", "prr_meta_stride", "prr_meta_bytes", "prr_attn_workspace_bytes",
     "prr_workspace_clear", "prr_build_meta", "prr_mean_meta_bytes", "prr_build_mean_meta", "prr_append",
-    "prr_select", "prr_select_spec_workspace_bytes", "prr_select_spec", "prr_select_spec_predict", "prr_predict_workspace_bytes",
+    "prr_select", "prr_select_spec_workspace_bytes", "prr_select_spec", "prr_select_spec_predict",
+    "prr_layer_step_workspace_bytes", "prr_layer_step", "prr_predict_workspace_bytes",
     "prr_predict",
     "prr_spec_attn", "prr_spec_attn_noalloc",
     "prr_repair", "prr_calibrate_workspace_bytes", "prr_calibrate", "prr_budget_fit", "prr_budget_choose",
@@ -83,6 +84,10 @@ _SIGS = {
     "prr_select_spec_predict": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _VP, ctypes.c_int, _I32, _I32,
                                                _P(BlockSetStruct), _VP, _P(BlockSetStruct), _P(BlockSetStruct),
                                                _F, _P(AttnStateStruct), _VP, _SZ, _P(PredictArgsStruct), _VP]),
+    "prr_layer_step_workspace_bytes": (_SZ, [_P(KvCacheStruct), _I32, _I32, _I32, _I32, _I32]),
+    "prr_layer_step": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _VP, ctypes.c_int, _I32, _I32, _P(BlockSetStruct),
+                                      _VP, _P(BlockSetStruct), _P(BlockSetStruct), _F, _P(AttnStateStruct), _VP, _VP,
+                                      _SZ, _P(PredictArgsStruct), _VP]),
     "prr_predict_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "prr_predict": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _D, _D, _D, _I32, _VP, _VP, _VP,
                                    _P(BlockSetStruct), _VP, _SZ, _VP]),
@@ -405,6 +410,37 @@ def select_spec(q: torch.Tensor, kv: KVCache, meta: torch.Tensor, block: int, to
                                          _stream(stream))
         _check(st, "prr_select_spec_predict")
     return scores, A, M, out
+
+
+def layer_step_workspace_for(kv: KVCache, hq: int, block: int, topk: int, p_cap: int, m_cap: int) -> Workspace:
+    """Workspace for layer_step() (prr_layer_step_workspace_bytes)."""
+    s = kv.struct()
+    return Workspace(load_library().prr_layer_step_workspace_bytes(ctypes.byref(s), hq, block, topk, p_cap, m_cap),
+                     kv.k.device)
+
+
+def layer_step(q: torch.Tensor, kv: KVCache, meta: torch.Tensor, block: int, topk: int, P: BlockSet, scale: float,
+               scores: torch.Tensor, A: BlockSet, M: BlockSet, state: AttnState, out: Optional[torch.Tensor] = None,
+               ws: Optional[Workspace] = None, mode: str = "quest", pred: Optional["PredictArgs"] = None, stream=None):
+    """The layer step (prr_layer_step): selection (scores, A, M = A \\ P), the speculative pass over P and
+    repair over M, the final state over P u M in `state` and acc / l in `out` (optional); one launch where
+    the top-K finishes inside it.  pred: another layer's predictor step carried by the launch."""
+    lib = load_library()
+    Hq = q.shape[1]
+    if ws is None:
+        ws = layer_step_workspace_for(kv, Hq, block, topk, P.cap, M.cap)
+    s = kv.struct()
+    a_s, p_s, m_s, o_s = A.struct(), P.struct(), M.struct(), state.struct()
+    pa = None
+    if pred is not None:
+        pn = pred.P_next.struct()
+        pa = pred.struct(pn)
+    st = lib.prr_layer_step(_ptr(q), Hq, ctypes.byref(s), _ptr(meta), _mode(mode), block, topk, ctypes.byref(p_s),
+                            _ptr(scores), ctypes.byref(a_s), ctypes.byref(m_s), float(scale), ctypes.byref(o_s),
+                            _ptr(out), ws.ptr(), ws.nbytes, ctypes.byref(pa) if pa is not None else None,
+                            _stream(stream))
+    _check(st, "prr_layer_step")
+    return state
 
 
 @dataclass

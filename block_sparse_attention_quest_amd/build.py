@@ -28,6 +28,8 @@ SOURCES = {
     "calib.hip": ["-ffp-contract=off"],
     "step.hip": [],
     "step_fp8.hip": [],
+    "step_layer.hip": [],
+    "step_layer_fp8.hip": [],
     "append.hip": [],
     "check.hip": [],
     "budget.cpp": ["-ffp-contract=off"],

@@ -128,8 +128,17 @@ __device__ __forceinline__ float rescale(float mpart, float mtot) {
     return mpart == -INFINITY ? 0.0f : fexp2(mpart - mtot);
 }
 
+// Set entries and sizes written earlier in the same launch by a workgroup of another XCD are read with
+// device-scope loads (COHERENT); a set from an earlier launch with plain ones.
+template <bool COHERENT = false>
+__device__ __forceinline__ int ld_set(const int32_t *ptr) {
+    if constexpr (COHERENT) return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return *ptr;
+}
+
+template <bool COHERENT = false>
 __device__ __forceinline__ int unit_pages(const AttnParams &p, int u) {
-    return min(max(p.count[u], 0), p.cap) * p.ppb;
+    return min(max(ld_set<COHERENT>(&p.count[u]), 0), p.cap) * p.ppb;
 }
 
 // Page lookups of the wave's pages wbeg .. wbeg + N - 1 of the unit's expanded page list.  Lane
@@ -144,6 +153,7 @@ struct PageLookup {
     bool lp_ok; // set entry in range
 };
 
+template <bool COHERENT = false>
 __device__ __forceinline__ PageLookup page_lookup(const AttnParams &p, int b, int u, int wbeg, int pw) {
     const int i = threadIdx.x & 63;
     PageLookup r;
@@ -154,7 +164,7 @@ __device__ __forceinline__ PageLookup page_lookup(const AttnParams &p, int b, in
         const int gpc = min(wbeg + i, p.cap * p.ppb - 1);
         const int li = gpc / p.ppb;
         const int sub = gpc - li * p.ppb;
-        const int blk = p.idx[(size_t)u * p.cap + li];
+        const int blk = ld_set<COHERENT>(&p.idx[(size_t)u * p.cap + li]);
         const long lp = (long)blk * p.ppb + sub;
         r.lp_ok = blk >= 0 && lp < p.max_pages;
         r.lp = r.lp_ok ? (int)lp : 0;
@@ -534,7 +544,8 @@ __device__ __forceinline__ void write_item(const AttnParams &p, size_t head, int
 // independent of arrival order.
 template <int VW, int D, bool REPAIR>
 __device__ __forceinline__ void merge_partials(const AttnParams &p, const float *base, int nch, size_t head0,
-                                               const float *s_mo, const float *s_lo, int tid) {
+                                               const float *s_mo, const float *s_lo, int tid,
+                                               const float *base2 = nullptr, int n2 = 0) {
     constexpr int MB = 8;
     constexpr int CPH = D / VW;   // channel groups per head
     const int G = p.G;
@@ -553,15 +564,19 @@ __device__ __forceinline__ void merge_partials(const AttnParams &p, const float 
 #pragma unroll
             for (int v = 0; v < VW; ++v) a[v] = p.acc[head * D + c0 + v];
         }
-        for (int w0 = 0; w0 < nch; w0 += MB) {
+        // slots [0, nch) at base, then [nch, nch + n2) at base2
+        const int ntot = nch + n2;
+        for (int w0 = 0; w0 < ntot; w0 += MB) {
             uint64_t lm[MB], pa[MB][VW / 2];
 #pragma unroll
             for (int i = 0; i < MB; ++i) {
                 lm[i] = (uint64_t)__float_as_uint(-INFINITY) << 32;
 #pragma unroll
                 for (int v = 0; v < VW / 2; ++v) pa[i][v] = 0;
-                if (w0 + i < nch) {
-                    const float *pw = base + ((size_t)(w0 + i) * G + jj) * (D + 2);
+                if (w0 + i < ntot) {
+                    const int w = w0 + i;
+                    const float *pw = (w < nch ? base + (size_t)w * G * (D + 2) : base2 + (size_t)(w - nch) * G * (D + 2)) +
+                                      (size_t)jj * (D + 2);
                     lm[i] = ld_dev2(&pw[D]);
 #pragma unroll
                     for (int v = 0; v < VW / 2; ++v) pa[i][v] = ld_dev2(&pw[c0 + 2 * v]);
@@ -591,14 +606,68 @@ __device__ __forceinline__ void merge_partials(const AttnParams &p, const float 
     }
 }
 
+// LDS of the attention chunk walk: the waves' partial states, the incoming state's m and l (repair),
+// the last-arriver flag.  A kernel with several roles declares it once and hands it to each.
+template <int D>
+struct AttnSmem {
+    float acc[kWaves][16 * (D + 4)];   // padded rows
+    float m[kWaves][16];
+    float l[kWaves][16];
+    float mo[16], lo[16];
+    int last;
+};
+
+// The layer step as one launch (selection, the speculative pass and repair in one grid): the speculative
+// chunks of a unit and its repair slots (the missed set M cut into chunks of cp_rep pages, kmax_rep slots
+// per unit at full capacity) all write partial states; every speculative chunk and every repair slot
+// arrives on the unit's counter, nch_spec + kmax_rep in all, and the last one merges the speculative
+// partials and then the repair partials (slot order: deterministic) into the final state over P u M.  A
+// repair slot first waits for the unit's M (the flag its top-K sets after storing M with device-scope
+// stores); slots past M's chunks arrive without a partial.  The merge resets the counter and the flag for
+// the next launch.
+struct FusedParams {
+    AttnParams pm;          // M's set: chunks of cp_rep pages, kmax_rep slots per unit, partials [units][kmax_rep][G][D + 2]
+    uint32_t *ready;        // [units] M of the unit stored (set by its top-K, reset by its merge)
+    uint32_t *status;       // set when a repair slot gave up waiting for M (see wait_ready)
+};
+
+template <int KT, int D, bool REPAIR, int NBUF, bool FUSED>
+__device__ __forceinline__ void attn_chunks(const AttnParams &p, const FusedParams &fp, int wg, int nwg,
+                                            AttnSmem<D> &sm);
+
 template <int KT, int D, bool REPAIR, int NBUF = 2>
 __device__ __forceinline__ void attn_body(const AttnParams &p, int wg, int nwg) {
+    __shared__ AttnSmem<D> sm;
+    attn_chunks<KT, D, REPAIR, NBUF, false>(p, FusedParams{}, wg, nwg, sm);
+}
+
+// The final merge of a unit of the fused launch: its speculative partials (P's chunks), then the partials
+// of M's chunks; resets the unit's counter and M flag.  pm: M's set (for its chunk count).
+template <int D>
+__device__ __forceinline__ void fused_merge(const AttnParams &p, const AttnParams &pm, const FusedParams &fp, int u,
+                                            size_t head0, int nch_spec, int tid) {
+    const int nrep = (unit_pages<true>(pm, u) + pm.cp - 1) / pm.cp;
+    const int G = p.G;
+    const float *base = p.partials + (size_t)u * p.kmax * G * (D + 2);
+    const float *base2 = pm.partials + (size_t)u * pm.kmax * G * (D + 2);
+    if (G * D <= 2 * kThreads) merge_partials<2, D, false>(p, base, nch_spec, head0, nullptr, nullptr, tid, base2, nrep);
+    else merge_partials<4, D, false>(p, base, nch_spec, head0, nullptr, nullptr, tid, base2, nrep);
+    if (tid == 0) {
+        __hip_atomic_store(&p.counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&fp.ready[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+template <int KT, int D, bool REPAIR, int NBUF, bool FUSED>
+__device__ __forceinline__ void attn_chunks(const AttnParams &p, const FusedParams &fp, int wg, int nwg,
+                                            AttnSmem<D> &sm) {
     constexpr int DP = D + 4;  // padded LDS row
-    __shared__ float sm_acc[kWaves][16 * DP];
-    __shared__ float sm_m[kWaves][16];
-    __shared__ float sm_l[kWaves][16];
-    __shared__ float s_mo[16], s_lo[16];   // repair: the incoming state's m and l per query head
-    __shared__ int s_last;
+    auto &sm_acc = sm.acc;
+    auto &sm_m = sm.m;
+    auto &sm_l = sm.l;
+    float *s_mo = sm.mo;   // repair: the incoming state's m and l per query head
+    float *s_lo = sm.lo;
+    int &s_last = sm.last;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -678,7 +747,7 @@ __device__ __forceinline__ void attn_body(const AttnParams &p, int wg, int nwg) 
         }
         __syncthreads();
 
-        const bool single = (nch == 1);
+        const bool single = !FUSED && nch == 1;   // the fused launch merges every unit with its repair
         float *part = p.partials + ((size_t)u * p.kmax + k) * G * (D + 2);
         // The thread index as an opaque value: the per-thread offsets below are then computed here,
         // after the tile walk, instead of being hoisted to the kernel start and kept live through it.
@@ -732,20 +801,132 @@ __device__ __forceinline__ void attn_body(const AttnParams &p, int wg, int nwg) 
         if (threadIdx.x == 0) {
             const uint32_t prev = __hip_atomic_fetch_add(&p.counters[u], 1u, __ATOMIC_RELAXED,
                                                          __HIP_MEMORY_SCOPE_AGENT);
-            s_last = (prev == (uint32_t)(nch - 1));
+            s_last = FUSED ? prev == (uint32_t)(nch + fp.pm.kmax - 1) : prev == (uint32_t)(nch - 1);
         }
         __syncthreads();
         if (s_last) {
-            const float *base = p.partials + (size_t)u * p.kmax * G * (D + 2);
-            if (G * D <= 2 * kThreads) merge_partials<2, D, REPAIR>(p, base, nch, head0, s_mo, s_lo, tid);
-            else merge_partials<4, D, REPAIR>(p, base, nch, head0, s_mo, s_lo, tid);
-            if (threadIdx.x == 0)
-                __hip_atomic_store(&p.counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if constexpr (FUSED) {
+                fused_merge<D>(p, fp.pm, fp, u, head0, nch, tid);
+            } else {
+                const float *base = p.partials + (size_t)u * p.kmax * G * (D + 2);
+                if (G * D <= 2 * kThreads) merge_partials<2, D, REPAIR>(p, base, nch, head0, s_mo, s_lo, tid);
+                else merge_partials<4, D, REPAIR>(p, base, nch, head0, s_mo, s_lo, tid);
+                if (threadIdx.x == 0)
+                    __hip_atomic_store(&p.counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
         __syncthreads();
     }
 }
 
+// Thread 0 of a repair slot waits for the unit's M (set by the unit's top-K in the same launch).  The
+// top-K runs in a scoring workgroup, and workgroups are dispatched in index order, scoring first, so the
+// workgroup a slot waits for is running or done by the time the slot runs.  The wait is bounded all the
+// same, so that no wave can spin forever: after about a second the slot sets *status and goes on (the
+// state then lacks the unit's M).
+__device__ __forceinline__ void wait_ready(const FusedParams &fp, int u) {
+    uint32_t n = 0;
+    while (__hip_atomic_load(&fp.ready[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+        __builtin_amdgcn_s_sleep(8);
+        if (++n >= (1u << 22)) {
+            __hip_atomic_store(fp.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+    }
+}
+
+// The repair slots of the fused launch: slot c covers pages [k cp_rep, (k + 1) cp_rep) of unit u's M
+// (u = c mod units, k = c / units, so the first chunks of every unit come first).  After M is stored, the
+// slot walks its pages like a chunk of prr_repair without an incoming state, stores its partial and
+// arrives; slots past M's pages arrive without one.  ps: P's set (the unit's speculative chunk count and
+// the final outputs).
+template <int KT, int D, int NBUF>
+__device__ __forceinline__ void fused_repair_slots(const AttnParams &ps, const FusedParams &fp, int wg, int nwg,
+                                                   AttnSmem<D> &sm) {
+    constexpr int DP = D + 4;
+    const AttnParams &pm = fp.pm;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = lane & 15;
+    const int g = lane >> 4;
+    const int G = pm.G;
+    const int cp = pm.cp;
+    const int pw = cp / kWaves;
+    const int total = pm.units * pm.kmax;
+    for (int c = wg; c < total; c += nwg) {
+        const int u = c % pm.units, k = c / pm.units;
+        const int b = u / pm.hkv, kvh = u - b * pm.hkv;
+        const int nsp = unit_pages(ps, u);   // P is an input of the launch: plain loads
+        const int slen = pm.seq_len[b];
+        if (threadIdx.x == 0) wait_ready(fp, u);
+        __syncthreads();
+        const int wbeg = k * cp + wave * pw;
+        const PageLookup look = page_lookup<true>(pm, b, u, wbeg, pw);
+        const int npages = unit_pages<true>(pm, u);
+        const int nch_spec = max(1, (nsp + ps.cp - 1) / ps.cp);
+        const size_t head0 = (size_t)b * pm.hq + (size_t)kvh * G;
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        if (k * cp < npages) {
+            const int cend = min(npages, k * cp + cp);
+            const int wend = min(cend, wbeg + pw);
+            WaveState<D> st;
+#pragma unroll
+            for (int cb = 0; cb < D / 16; ++cb) st.o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            st.m = -INFINITY;
+            st.l = 0.0f;
+            if (wbeg < wend) {
+                const LanePage pg = page_finish(pm, look, wbeg, wend, slen);
+                const int nw = wend - wbeg;
+                if constexpr (KT == kKtBf16)
+                    wave_pass_bf16<D, NBUF, false>(pm, head0, kvh, j, g, pg, (nw + 1) / 2, st);
+                else if constexpr (KT == kKtFp8)
+                    wave_pass_fp8<D, NBUF, false>(pm, head0, kvh, j, g, pg, (nw + 1) / 2, st);
+                else wave_pass_f32<D>(pm, head0, kvh, j, g, pg, nw, st);
+            }
+            float lsum = st.l;
+            lsum += __shfl_xor(lsum, 16);
+            lsum += __shfl_xor(lsum, 32);
+            if (j < G) {
+#pragma unroll
+                for (int cb = 0; cb < D / 16; ++cb) *(f32x4 *)&sm.acc[wave][j * DP + 16 * cb + 4 * g] = st.o[cb];
+                if (g == 0) {
+                    sm.m[wave][j] = st.m;
+                    sm.l[wave][j] = lsum;
+                }
+            }
+            __syncthreads();
+            float *part = pm.partials + ((size_t)u * pm.kmax + k) * G * (D + 2);
+            for (int it = tid; it < G * D / 2; it += kThreads) {
+                const int jj = it / (D / 2), cc = (it - jj * (D / 2)) * 2;
+                float mx = -INFINITY;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sm.m[w][jj]);
+                float a0 = 0.0f, a1 = 0.0f, ls = 0.0f;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) {
+                    const float f = rescale(sm.m[w][jj], mx);
+                    const float2 x = *(const float2 *)&sm.acc[w][jj * DP + cc];
+                    a0 += f * x.x;
+                    a1 += f * x.y;
+                    ls += f * sm.l[w][jj];
+                }
+                st_dev2(&part[jj * (D + 2) + cc], a0, a1);
+                if (cc == 0) st_dev2(&part[jj * (D + 2) + D], ls, mx);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t prev = __hip_atomic_fetch_add(&ps.counters[u], 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            sm.last = prev == (uint32_t)(nch_spec + pm.kmax - 1);
+        }
+        __syncthreads();
+        if (sm.last) { fused_merge<D>(ps, pm, fp, u, head0, nch_spec, tid); }
+        __syncthreads();
+    }
+}
 
 // Workspace counters: one chunk-arrival counter per unit (attention), then one scoring-arrival counter
 // per unit (the fused selection + speculation launch), padded to 256 bytes.

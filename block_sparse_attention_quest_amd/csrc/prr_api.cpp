@@ -257,27 +257,11 @@ static prr_status check_predict(const double *scores, const int32_t *seq_len, in
     return PRR_OK;
 }
 
-prr_status prr_select_spec_predict(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
-                                   prr_score_mode mode, int32_t block, int32_t topk, const prr_block_set *P,
-                                   double *scores, prr_block_set *A, prr_block_set *M, float scale,
-                                   prr_attn_state *out, void *ws, size_t ws_bytes, const prr_predict_args *pred,
-                                   hipStream_t stream) {
-    CallTiming timing_;
-    if (!q || !meta || !scores || !P || !M) return PRR_EINVAL;
-    if (mode != PRR_SCORE_QUEST && mode != PRR_SCORE_MEAN) return PRR_EINVAL;
-    PRR_TRY(check_kv(kv));
-    PRR_TRY(check_block(kv, block));
-    PRR_TRY(check_heads(kv, num_q_heads));
-    PRR_TRY(check_set(P));
-    PRR_TRY(check_set(A));
-    PRR_TRY(check_set(M));
-    if (topk < 0 || A->cap < topk || M->cap < topk) return PRR_EINVAL;
-    if (!out || !out->acc || !out->l || !out->m) return PRR_EINVAL;
-    const int nmax = prr_max_blocks(kv, block);
-    if (nmax > prr::kMaxSelectN) return PRR_EUNSUPPORTED;
-    if (!ws || ws_bytes < prr_select_spec_workspace_bytes(kv, num_q_heads, block, topk, P->cap))
-        return PRR_EWORKSPACE;
-    prr::PredictArgs pa;
+// The carried predictor step's arguments (prr_select_spec_predict, prr_layer_step): checked, and with no
+// buffer shared with the selection's outputs or P.
+static prr_status predict_args(const prr_predict_args *pred, const double *scores, const prr_block_set *P,
+                               const prr_block_set *A, const prr_block_set *M, prr::PredictArgs &pa) {
+    pa = prr::PredictArgs{};
     if (pred) {
         PRR_TRY(check_predict(pred->scores, pred->seq_len, pred->batch, pred->num_kv_heads, pred->block,
                               pred->max_blocks, pred->budget, pred->level, pred->trend, pred->live, pred->P_next));
@@ -310,11 +294,73 @@ prr_status prr_select_spec_predict(const void *q, int32_t num_q_heads, const prr
         if (pred->ws && pred->ws_bytes < need) return PRR_EWORKSPACE;
         pa.ws = need ? pred->ws : nullptr;
     }
+    return PRR_OK;
+}
+
+prr_status prr_select_spec_predict(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
+                                   prr_score_mode mode, int32_t block, int32_t topk, const prr_block_set *P,
+                                   double *scores, prr_block_set *A, prr_block_set *M, float scale,
+                                   prr_attn_state *out, void *ws, size_t ws_bytes, const prr_predict_args *pred,
+                                   hipStream_t stream) {
+    CallTiming timing_;
+    if (!q || !meta || !scores || !P || !M) return PRR_EINVAL;
+    if (mode != PRR_SCORE_QUEST && mode != PRR_SCORE_MEAN) return PRR_EINVAL;
+    PRR_TRY(check_kv(kv));
+    PRR_TRY(check_block(kv, block));
+    PRR_TRY(check_heads(kv, num_q_heads));
+    PRR_TRY(check_set(P));
+    PRR_TRY(check_set(A));
+    PRR_TRY(check_set(M));
+    if (topk < 0 || A->cap < topk || M->cap < topk) return PRR_EINVAL;
+    if (!out || !out->acc || !out->l || !out->m) return PRR_EINVAL;
+    const int nmax = prr_max_blocks(kv, block);
+    if (nmax > prr::kMaxSelectN) return PRR_EUNSUPPORTED;
+    if (!ws || ws_bytes < prr_select_spec_workspace_bytes(kv, num_q_heads, block, topk, P->cap))
+        return PRR_EWORKSPACE;
+    prr::PredictArgs pa;
+    PRR_TRY(predict_args(pred, scores, P, A, M, pa));
     PRR_TRY(check_input_set(kv, block, P, stream));
     return hip_status(prr::launch_select_spec(desc(kv), q, num_q_heads, meta, block, prr_meta_stride(kv, block),
                                               nmax, topk, P->idx, P->count, P->cap, scores, A->idx, A->count,
                                               A->cap, M->idx, M->count, M->cap, scale, out->acc, out->l, out->m,
                                               ws, mode == PRR_SCORE_MEAN, pred ? &pa : nullptr, stream));
+}
+
+size_t prr_layer_step_workspace_bytes(const prr_kv_cache *kv, int32_t num_q_heads, int32_t block, int32_t topk,
+                                      int32_t p_cap, int32_t m_cap) {
+    if (!kv || kv->batch <= 0 || kv->num_kv_heads <= 0 || num_q_heads <= 0 || kv->head_dim <= 0 ||
+        block < prr::kPage || p_cap <= 0 || m_cap <= 0 || topk < 0)
+        return 0;
+    return prr::layer_step_workspace_bytes(kv->batch, num_q_heads, kv->num_kv_heads, kv->head_dim, block, p_cap, m_cap,
+                                           prr_max_blocks(kv, block), topk);
+}
+
+prr_status prr_layer_step(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
+                          prr_score_mode mode, int32_t block, int32_t topk, const prr_block_set *P, double *scores,
+                          prr_block_set *A, prr_block_set *M, float scale, prr_attn_state *state, float *out,
+                          void *ws, size_t ws_bytes, const prr_predict_args *pred, hipStream_t stream) {
+    CallTiming timing_;
+    if (!q || !meta || !scores || !P || !M) return PRR_EINVAL;
+    if (mode != PRR_SCORE_QUEST && mode != PRR_SCORE_MEAN) return PRR_EINVAL;
+    PRR_TRY(check_kv(kv));
+    PRR_TRY(check_block(kv, block));
+    PRR_TRY(check_heads(kv, num_q_heads));
+    PRR_TRY(check_set(P));
+    PRR_TRY(check_set(A));
+    PRR_TRY(check_set(M));
+    if (topk < 0 || A->cap < topk || M->cap < topk) return PRR_EINVAL;
+    if (!state || !state->acc || !state->l || !state->m) return PRR_EINVAL;
+    const int nmax = prr_max_blocks(kv, block);
+    if (nmax > prr::kMaxSelectN) return PRR_EUNSUPPORTED;
+    if (!ws || ws_bytes < prr_layer_step_workspace_bytes(kv, num_q_heads, block, topk, P->cap, M->cap))
+        return PRR_EWORKSPACE;
+    prr::PredictArgs pa;
+    PRR_TRY(predict_args(pred, scores, P, A, M, pa));
+    PRR_TRY(check_input_set(kv, block, P, stream));
+    return hip_status(prr::launch_layer_step(desc(kv), q, num_q_heads, meta, block, prr_meta_stride(kv, block), nmax,
+                                             topk, P->idx, P->count, P->cap, scores, A->idx, A->count, A->cap, M->idx,
+                                             M->count, M->cap, scale, state->acc, state->l, state->m, out, ws,
+                                             mode == PRR_SCORE_MEAN, pred ? &pa : nullptr, stream));
 }
 
 prr_status prr_select_spec(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,

@@ -165,6 +165,25 @@ hipError_t launch_select_spec_fp8(const KvDesc &kv, const void *q, int hq, const
                                   int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m, void *ws,
                                   bool mean, const PredictArgs *pred, hipStream_t stream);
 
+// The layer step (selection, the speculative pass over P, repair over M) in one launch where the top-K
+// finishes inside it (bf16 and fp8 caches), else as the select_spec launches followed by repair's.  The
+// final state over P u M goes to acc, l, m, the normalised output to out (may be null).  ws:
+// layer_step_workspace_bytes: the select_spec workspace, then M's attention workspace, the per-unit M flags
+// and a status word (zeroed once; every call leaves it ready for the next).
+size_t layer_step_workspace_bytes(int batch, int hq, int hkv, int d, int block, int p_cap, int m_cap, int nmax,
+                                  int topk);
+hipError_t launch_layer_step(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride, int nmax,
+                             int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap, double *scores,
+                             int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx, int32_t *m_cnt, int m_cap,
+                             float scale, float *acc, float *l, float *m, float *out, void *ws, bool mean,
+                             const PredictArgs *pred, hipStream_t stream);
+// fp8 caches (compiled in its own file); mws: the M part of the workspace
+hipError_t launch_layer_step_fp8(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,
+                                 int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
+                                 double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
+                                 int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m, float *out,
+                                 void *ws, void *mws, bool mean, const PredictArgs *pred, hipStream_t stream);
+
 // ws (may be null): rows longer than 2048 blocks are then updated by 512-block parts in parallel and
 // ranked in two stages (predict_workspace_bytes; 0 where one workgroup per unit is used regardless).
 size_t predict_workspace_bytes(int batch, int hkv, int nmax, int budget);

@@ -418,6 +418,13 @@ __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u) 
 // Top-K + set difference
 // ------------------------------------------------------------------------------------------------
 
+__device__ __forceinline__ void st_dev_u64(uint64_t *ptr, uint64_t v) {
+    __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_i32(int32_t *ptr, int32_t v) {
+    __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 struct TopkParams {
     const double *scores;
     const int32_t *seq_len;
@@ -430,9 +437,17 @@ struct TopkParams {
     int hkv, block, nmax, topk, p_cap, a_cap, m_cap;
 };
 
+// M's entries and count: device-scope stores when a workgroup of the same launch reads them (COH_M).
+template <bool COH_M>
+__device__ __forceinline__ void st_m(int32_t *ptr, int32_t v) {
+    if constexpr (COH_M) st_dev_i32(ptr, v);
+    else *ptr = v;
+}
+
 // Top-K of unit u's scores and M = A \ P, by a workgroup of TPB threads holding KPT keys each.
 // COHERENT: the scores are read with device-scope loads (written by other workgroups of the same launch).
-template <int KPT, int TPB, bool COHERENT = false>
+// COH_M: M is stored with device-scope stores (read by other workgroups of the same launch).
+template <int KPT, int TPB, bool COHERENT = false, bool COH_M = false>
 __device__ __forceinline__ void topk_body(const TopkParams &p, int u) {
     constexpr int W = TPB / 64;
     __shared__ TopkSmem<W> sm;
@@ -484,11 +499,11 @@ __device__ __forceinline__ void topk_body(const TopkParams &p, int u) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         if (sel >> j & 1u) p.a_idx[(size_t)u * p.a_cap + oa++] = base + j;
-        if (inm >> j & 1u) p.m_idx[(size_t)u * p.m_cap + om++] = base + j;
+        if (inm >> j & 1u) st_m<COH_M>(&p.m_idx[(size_t)u * p.m_cap + om++], base + j);
     }
     if (threadIdx.x == 0) {
         p.a_cnt[u] = (int32_t)(total & 0xffffu);
-        if (want_m) p.m_cnt[u] = (int32_t)(total >> 16);
+        if (want_m) st_m<COH_M>(&p.m_cnt[u], (int32_t)(total >> 16));
     }
 }
 
@@ -511,13 +526,6 @@ struct CandParams {
     int32_t *cnt;
     int kl;
 };
-
-__device__ __forceinline__ void st_dev_u64(uint64_t *ptr, uint64_t v) {
-    __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev_i32(int32_t *ptr, int32_t v) {
-    __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Stage 1: the local top-kl of the workgroup's blocks [first_block, first_block + 256 BPL) (lane t holds
 // blocks first_block + BPL t + e with scores kept[e]); n_local of them exist.  Writes the candidates and
@@ -602,7 +610,7 @@ __device__ __forceinline__ void group_candidates(const uint64_t *ckey, const int
 
 // Stage 2: the top-K of unit u over its nparts x kl candidate slots (part c holds ccnt[c] candidates)
 // and M = A \ P, written like topk_body.  256 threads with KPT slots each (256 KPT >= nparts kl).
-template <int KPT>
+template <int KPT, bool COH_M = false>
 __device__ __forceinline__ void topk_candidates_body(const TopkParams &p, int u, const uint64_t *ckey,
                                                      const int32_t *cidx, const int32_t *ccnt, int nparts,
                                                      int kl) {
@@ -672,11 +680,11 @@ __device__ __forceinline__ void topk_candidates_body(const TopkParams &p, int u,
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         if (sel >> j & 1u) p.a_idx[(size_t)u * p.a_cap + oa++] = idx[j];
-        if (inm >> j & 1u) p.m_idx[(size_t)u * p.m_cap + om++] = idx[j];
+        if (inm >> j & 1u) st_m<COH_M>(&p.m_idx[(size_t)u * p.m_cap + om++], idx[j]);
     }
     if (threadIdx.x == 0) {
         p.a_cnt[u] = (int32_t)(total & 0xffffu);
-        if (want_m) p.m_cnt[u] = (int32_t)(total >> 16);
+        if (want_m) st_m<COH_M>(&p.m_cnt[u], (int32_t)(total >> 16));
     }
 }
 

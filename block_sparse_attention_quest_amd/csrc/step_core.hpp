@@ -51,12 +51,23 @@ namespace {
 // workgroup draws until it gets an index >= n_pred, so the launch makes exactly n_pred + n_score draws
 // and the one that draws the last index resets the counter for the next launch.  Register use is the
 // attention part's (two waves per SIMD).
-template <int KT, int D, int KPT, bool TWO, bool MEAN, bool PRED>
+//
+// REP (the layer step as one launch): n_rep repair slots follow the speculative workgroups, every unit's
+// speculative chunks and repair slots end in one merge over P u M (attn_core.hpp: FusedParams), and the
+// top-K stores M with device-scope stores and then raises the unit's flag the repair slots wait for.
+template <int KT, int D, int KPT, bool TWO, bool MEAN, bool PRED, bool REP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void select_spec_kernel(
     AttnParams ap, ScoreParams sp, TopkParams tp, CandParams cp, PredictParams pp, uint32_t *arrivals,
-    uint32_t *pred_ctr, int n_score, int nsx, int n_spec, int n_pred) {
+    uint32_t *pred_ctr, int n_score, int nsx, int n_spec, int n_pred, FusedParams fp, int n_rep) {
     if ((int)blockIdx.x >= n_score) {
-        attn_body<KT, D, false>(ap, (int)blockIdx.x - n_score, n_spec);
+        if constexpr (REP) {
+            __shared__ AttnSmem<D> asm_;
+            const int w = (int)blockIdx.x - n_score;
+            if (w < n_spec) attn_chunks<KT, D, false, 1, true>(ap, fp, w, n_spec, asm_);
+            else fused_repair_slots<KT, D, 2>(ap, fp, w - n_spec, n_rep, asm_);
+        } else {
+            attn_body<KT, D, false, 1>(ap, (int)blockIdx.x - n_score, n_spec);
+        }
         return;
     }
     const int s = (int)blockIdx.x;
@@ -89,10 +100,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
         __syncthreads();
         if (s_last) {
             if constexpr (TWO)
-                topk_candidates_body<KPT>(tp, u, cp.key + (size_t)u * nsx * cp.kl, cp.idx + (size_t)u * nsx * cp.kl,
-                                          cp.cnt + (size_t)u * nsx, nsx, cp.kl);
+                topk_candidates_body<KPT, REP>(tp, u, cp.key + (size_t)u * nsx * cp.kl,
+                                               cp.idx + (size_t)u * nsx * cp.kl, cp.cnt + (size_t)u * nsx, nsx, cp.kl);
             else
-                topk_body<KPT, 256, true>(tp, u);
+                topk_body<KPT, 256, true, REP>(tp, u);
+            if constexpr (REP) {
+                // M's device-scope stores are complete before the unit's repair slots may read it
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                if (threadIdx.x == 0) __hip_atomic_store(&fp.ready[u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
     if constexpr (PRED) {
@@ -113,7 +130,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     }
 }
 
-}  // namespace
 
 // Blocks per scoring workgroup of the fused launch (bf16 queries): 512 for min/max metadata, 512 for
 // block means (two per lane either way).
@@ -121,40 +137,40 @@ inline int select_spec_score_bpw(bool mean) {
     return 256 * (mean ? kScoreBPL<true, true> : kScoreBPL<true, false>);
 }
 
-// The fused launch for caches of element type KT (bf16 or fp8; an f32 cache runs the passes in turn).
-template <int KT>
-hipError_t launch_select_spec_t(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,
-                              int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
-                              double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
-                              int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m,
-                              void *ws, bool mean, const PredictArgs *pred, hipStream_t stream) {
-    auto predict_alone = [&]() -> hipError_t {
-        if (!pred) return hipSuccess;
-        return launch_predict(pred->scores, pred->seq_len, pred->batch, pred->hkv, pred->block, pred->nmax,
-                              pred->alpha, pred->beta, pred->gamma, pred->budget, pred->level, pred->trend,
-                              pred->live, pred->p_idx, pred->p_cnt, pred->p_cap, pred->ws, stream);
-    };
-    if constexpr (KT == kKtF32) {
-        // fp32 caches (exact-input checks): the passes one after the other
-        hipError_t e = launch_select(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_cap, scores,
-                                     a_idx, a_cnt, a_cap, m_idx, m_cnt, m_cap, mean, stream);
-        if (e != hipSuccess) return e;
-        e = launch_attn(kv, q, hq, block, p_idx, p_cnt, p_cap, scale, acc, l, m, nullptr, false, ws, stream);
-        if (e != hipSuccess) return e;
-        return predict_alone();
-    } else {
+// Everything a fused launch needs besides its kernel: the parameters of its roles, its grid, and where the
+// top-K stages after it (if any) keep their candidates.  Shared by the selection + speculation launch and
+// the layer-step launch (which adds the repair slots).
+struct FusedSetup {
+    AttnParams ap;
+    ScoreParams sp;
+    TopkParams tp;
+    CandParams cp;
+    PredictParams pp;
+    SelectSpecPlan plan;
+    uint32_t *arrivals;
+    uint32_t *pred_ctr;
+    char *cbase;
+    int units, nsx, n_spec, n_pred;
+    bool fuse_pred;
+    long grid;   // scoring + speculative workgroups
+};
+
+inline FusedSetup fused_setup(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride, int nmax,
+                              int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap, double *scores,
+                              int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx, int32_t *m_cnt, int m_cap,
+                              float scale, float *acc, float *l, float *m, float *out, void *ws, bool mean,
+                              const PredictArgs *pred) {
+    FusedSetup f;
     // Two workgroups of this kernel fit on a CU.  When the scoring workgroups take more than half of
     // those slots (rows longer than 512 blocks per CU's share, e.g. a cache with room for appended
     // tokens), the speculative pass is spread over the slots that are left, so that the whole grid is
     // resident from the start instead of speculative workgroups waiting for scoring ones to finish.
     const int cus = device_cu_count();
-    const int n_score_wgs = (nmax + select_spec_score_bpw(mean) - 1) / select_spec_score_bpw(mean) *
-                            kv.batch * kv.hkv;
+    const int bpw = select_spec_score_bpw(mean);
+    const int n_score_wgs = (nmax + bpw - 1) / bpw * kv.batch * kv.hkv;
     const int spec_target = n_score_wgs > cus ? std::max(cus / 2, 2 * cus - n_score_wgs) : cus;
-    AttnParams ap;
-    const int n_spec = attn_setup(ap, kv, q, hq, block, p_idx, p_cnt, p_cap, scale, acc, l, m, nullptr, false, ws,
-                                  spec_target);
-    ScoreParams sp;
+    f.n_spec = attn_setup(f.ap, kv, q, hq, block, p_idx, p_cnt, p_cap, scale, acc, l, m, out, false, ws, spec_target);
+    ScoreParams &sp = f.sp;
     sp.q = q;
     sp.meta = meta;
     sp.seq_len = kv.seq_len;
@@ -165,7 +181,7 @@ hipError_t launch_select_spec_t(const KvDesc &kv, const void *q, int hq, const v
     sp.block = block;
     sp.stride = stride;
     sp.nmax = nmax;
-    TopkParams tp;
+    TopkParams &tp = f.tp;
     tp.scores = scores;
     tp.seq_len = kv.seq_len;
     tp.p_idx = p_idx;
@@ -181,14 +197,14 @@ hipError_t launch_select_spec_t(const KvDesc &kv, const void *q, int hq, const v
     tp.p_cap = p_cap;
     tp.a_cap = a_cap;
     tp.m_cap = m_cap;
-    const int units = kv.batch * kv.hkv;
-    uint32_t *arrivals = (uint32_t *)ws + units;   // the scoring-arrival counters of the workspace
-    const int bpw = select_spec_score_bpw(mean);
-    const int nsx = (nmax + bpw - 1) / bpw;
-    const bool fuse_pred = pred && pred->nmax <= kMaxFusedPredictN;
-    PredictParams pp = {};
-    int n_pred = 0;
-    if (fuse_pred) {
+    f.units = kv.batch * kv.hkv;
+    f.arrivals = (uint32_t *)ws + f.units;   // the scoring-arrival counters of the workspace
+    f.nsx = (nmax + bpw - 1) / bpw;
+    f.fuse_pred = pred && pred->nmax <= kMaxFusedPredictN;
+    f.pp = PredictParams{};
+    f.n_pred = 0;
+    if (f.fuse_pred) {
+        PredictParams &pp = f.pp;
         pp.scores = pred->scores;
         pp.seq_len = pred->seq_len;
         pp.level = pred->level;
@@ -204,26 +220,71 @@ hipError_t launch_select_spec_t(const KvDesc &kv, const void *q, int hq, const v
         pp.alpha = pred->alpha;
         pp.beta = pred->beta;
         pp.gamma = pred->gamma;
-        n_pred = pred->batch * pred->hkv;
+        f.n_pred = pred->batch * pred->hkv;
     }
-    const long grid = (long)n_spec + (long)nsx * units;
-    uint32_t *pred_ctr =
-        (uint32_t *)((char *)ws + pred_counter_offset(kv.batch, hq, kv.hkv, kv.d, block, p_cap, nmax, topk));
-    if (grid > 0x7fffffffL) return hipErrorInvalidValue;
-    const SelectSpecPlan plan = select_spec_plan(nmax, topk, mean);
-    CandParams cp;
-    cp.kl = plan.kl;
-    char *cbase = (char *)ws + attn_workspace_bytes(kv.batch, hq, kv.hkv, kv.d, block, p_cap);
-    cp.key = (uint64_t *)cbase;
-    cp.idx = (int32_t *)(cbase + (size_t)units * nsx * plan.kl * 8);
-    cp.cnt = (int32_t *)(cbase + (size_t)units * nsx * plan.kl * 12);
-    const int kpt = plan.kpt;
-    const bool two = plan.two;
+    f.grid = (long)f.n_spec + (long)f.nsx * f.units;
+    f.pred_ctr = (uint32_t *)((char *)ws + pred_counter_offset(kv.batch, hq, kv.hkv, kv.d, block, p_cap, nmax, topk));
+    f.plan = select_spec_plan(nmax, topk, mean);
+    f.cp.kl = f.plan.kl;
+    f.cbase = (char *)ws + attn_workspace_bytes(kv.batch, hq, kv.hkv, kv.d, block, p_cap);
+    f.cp.key = (uint64_t *)f.cbase;
+    f.cp.idx = (int32_t *)(f.cbase + (size_t)f.units * f.nsx * f.plan.kl * 8);
+    f.cp.cnt = (int32_t *)(f.cbase + (size_t)f.units * f.nsx * f.plan.kl * 12);
+    return f;
+}
+
+// The top-K stages that follow a fused launch whose ranking does not finish inside it.
+inline hipError_t fused_after(const FusedSetup &f, const KvDesc &kv, int block, int nmax, int topk, const double *scores,
+                              const int32_t *p_idx, const int32_t *p_cnt, int p_cap, int32_t *a_idx, int32_t *a_cnt,
+                              int a_cap, int32_t *m_idx, int32_t *m_cnt, int m_cap, hipStream_t stream) {
+    if (f.plan.three) {
+        // the parts' candidates are in place; groups of them, then the unit's ranking
+        const size_t s1 = (size_t)f.units * f.nsx * f.plan.kl;
+        char *cand2 = f.cbase + (s1 * 12 + (size_t)f.units * f.nsx * 4 + 255) / 256 * 256;
+        const size_t s2 = (size_t)f.units * f.plan.ng * f.plan.kl2;
+        uint32_t *garr = (uint32_t *)(cand2 + (s2 * 12 + (size_t)f.units * f.plan.ng * 4 + 255) / 256 * 256);
+        return launch_topk_groups(kv, block, nmax, topk, p_idx, p_cnt, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt, m_cap,
+                                  f.plan, f.nsx, f.cbase, cand2, garr, stream);
+    }
+    if (f.plan.kpt == 0)
+        return launch_topk(kv, block, nmax, topk, scores, p_idx, p_cnt, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt, m_cap,
+                           stream);
+    return hipSuccess;
+}
+
+inline hipError_t predict_alone(const PredictArgs *pred, hipStream_t stream) {
+    if (!pred) return hipSuccess;
+    return launch_predict(pred->scores, pred->seq_len, pred->batch, pred->hkv, pred->block, pred->nmax, pred->alpha,
+                          pred->beta, pred->gamma, pred->budget, pred->level, pred->trend, pred->live, pred->p_idx,
+                          pred->p_cnt, pred->p_cap, pred->ws, stream);
+}
+
+// The fused launch for caches of element type KT (bf16 or fp8; an f32 cache runs the passes in turn).
+template <int KT>
+hipError_t launch_select_spec_t(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,
+                              int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
+                              double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
+                              int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m,
+                              void *ws, bool mean, const PredictArgs *pred, hipStream_t stream) {
+    if constexpr (KT == kKtF32) {
+        // fp32 caches (exact-input checks): the passes one after the other
+        hipError_t e = launch_select(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_cap, scores,
+                                     a_idx, a_cnt, a_cap, m_idx, m_cnt, m_cap, mean, stream);
+        if (e != hipSuccess) return e;
+        e = launch_attn(kv, q, hq, block, p_idx, p_cnt, p_cap, scale, acc, l, m, nullptr, false, ws, stream);
+        if (e != hipSuccess) return e;
+        return predict_alone(pred, stream);
+    } else {
+    const FusedSetup f = fused_setup(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_cap, scores, a_idx,
+                                     a_cnt, a_cap, m_idx, m_cnt, m_cap, scale, acc, l, m, nullptr, ws, mean, pred);
+    if (f.grid > 0x7fffffffL) return hipErrorInvalidValue;
+    const int kpt = f.plan.kpt;
+    const bool two = f.plan.two;
+    const FusedParams none{};
 #define PRR_SS(DD, K, T, MN, PR)                                                                           \
-    if (kv.d == DD && kpt == K && two == T && mean == MN && fuse_pred == PR) {                              \
-        PRR_LAUNCH(select_spec_kernel<KT, DD, K, T, MN, PR>, dim3((int)grid), dim3(256), stream, ap, sp, tp, cp, pp, arrivals,      \
-                                                                            pred_ctr, nsx * units, nsx, n_spec, \
-                                                                            n_pred);                        \
+    if (kv.d == DD && kpt == K && two == T && mean == MN && f.fuse_pred == PR) {                            \
+        PRR_LAUNCH(select_spec_kernel<KT, DD, K, T, MN, PR>, dim3((int)f.grid), dim3(256), stream, f.ap, f.sp, f.tp, \
+                   f.cp, f.pp, f.arrivals, f.pred_ctr, f.nsx * f.units, f.nsx, f.n_spec, f.n_pred, none, 0);      \
     } else
 #define PRR_SS_K(DD, MN, PR)                                                                                \
     PRR_SS(DD, 0, false, MN, PR) PRR_SS(DD, 0, true, MN, PR) PRR_SS(DD, 1, false, MN, PR)                     \
@@ -237,25 +298,77 @@ hipError_t launch_select_spec_t(const KvDesc &kv, const void *q, int hq, const v
 #undef PRR_SS_ALL
 #undef PRR_SS_K
 #undef PRR_SS
-    hipError_t e = hipGetLastError();
+    hipError_t e = fused_after(f, kv, block, nmax, topk, scores, p_idx, p_cnt, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt,
+                               m_cap, stream);
     if (e != hipSuccess) return e;
-    if (plan.three) {
-        // the parts' candidates are in place; groups of them, then the unit's ranking
-        const size_t s1 = (size_t)units * nsx * plan.kl;
-        char *cand2 = cbase + (s1 * 12 + (size_t)units * nsx * 4 + 255) / 256 * 256;
-        const size_t s2 = (size_t)units * plan.ng * plan.kl2;
-        uint32_t *garr = (uint32_t *)(cand2 + (s2 * 12 + (size_t)units * plan.ng * 4 + 255) / 256 * 256);
-        e = launch_topk_groups(kv, block, nmax, topk, p_idx, p_cnt, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt, m_cap,
-                               plan, nsx, cbase, cand2, garr, stream);
-        if (e != hipSuccess) return e;
-    } else if (kpt == 0) {
-        e = launch_topk(kv, block, nmax, topk, scores, p_idx, p_cnt, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt,
-                        m_cap, stream);
-        if (e != hipSuccess) return e;
-    }
-    return fuse_pred ? hipSuccess : predict_alone();
+    return f.fuse_pred ? hipSuccess : predict_alone(pred, stream);
     }
 }
 
+// Where the layer-step workspace keeps what prr_select_spec's does not have: M's attention workspace (for
+// the repair chunks' partial states, or for prr_repair's own launch), then the per-unit M flags and the
+// status word, each 256-byte aligned.
+inline size_t layer_extra_m_ws(int batch, int hq, int hkv, int d, int block, int m_cap) {
+    return attn_workspace_bytes(batch, hq, hkv, d, block, m_cap);
+}
 
+// The layer step (selection, the speculative pass over P, repair over M = A \ P) for caches of element
+// type KT: one launch when the cache is bf16 or fp8 and the top-K finishes inside the launch (rows of up
+// to 4096 candidate slots); otherwise prr_select_spec's launches followed by prr_repair's.  mws: the M
+// part of the workspace (layer_extra_m_ws bytes, then the flags).
+template <int KT>
+hipError_t launch_layer_step_t(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,
+                               int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
+                               double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
+                               int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m, float *out,
+                               void *ws, void *mws, bool mean, const PredictArgs *pred, hipStream_t stream) {
+    const int units = kv.batch * kv.hkv;
+    const size_t mbytes = layer_extra_m_ws(kv.batch, hq, kv.hkv, kv.d, block, m_cap);
+    uint32_t *ready = (uint32_t *)((char *)mws + mbytes);
+    uint32_t *status = (uint32_t *)((char *)mws + mbytes + ((size_t)units * 4 + 255) / 256 * 256);
+    const SelectSpecPlan plan = select_spec_plan(nmax, topk, mean);
+    if (KT == kKtF32 || plan.three || plan.kpt == 0) {
+        hipError_t e = launch_select_spec(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_cap, scores,
+                                          a_idx, a_cnt, a_cap, m_idx, m_cnt, m_cap, scale, acc, l, m, ws, mean, pred,
+                                          stream);
+        if (e != hipSuccess) return e;
+        return launch_attn(kv, q, hq, block, m_idx, m_cnt, m_cap, scale, acc, l, m, out, true, mws, stream);
+    } else {
+    const FusedSetup f = fused_setup(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_cap, scores, a_idx,
+                                     a_cnt, a_cap, m_idx, m_cnt, m_cap, scale, acc, l, m, out, ws, mean, pred);
+    FusedParams fp{};
+    attn_setup(fp.pm, kv, q, hq, block, m_idx, m_cnt, m_cap, scale, acc, l, m, out, true, mws);
+    // M's chunks at half prr_repair's size (at least kChunkMin pages, the size the workspace's partial
+    // slots are counted at): the repair slots start only once their unit's top-K is done, late in the
+    // launch, so more and shorter chunks finish sooner
+    fp.pm.cp = std::max(kChunkMin, (fp.pm.cp / 2 + kChunkMin - 1) / kChunkMin * kChunkMin);
+    fp.pm.kmax = std::max(1, (m_cap * (block / kPage) + fp.pm.cp - 1) / fp.pm.cp);
+    fp.ready = ready;
+    fp.status = status;
+    const long n_rep = (long)units * fp.pm.kmax;
+    const long grid = f.grid + n_rep;
+    if (grid > 0x7fffffffL) return hipErrorInvalidValue;
+    const int kpt = plan.kpt;
+    const bool two = plan.two;
+#define PRR_LS(DD, K, T, MN, PR)                                                                           \
+    if (kv.d == DD && kpt == K && two == T && mean == MN && f.fuse_pred == PR) {                            \
+        PRR_LAUNCH(select_spec_kernel<KT, DD, K, T, MN, PR, true>, dim3((int)grid), dim3(256), stream, f.ap, f.sp,   \
+                   f.tp, f.cp, f.pp, f.arrivals, f.pred_ctr, f.nsx * f.units, f.nsx, f.n_spec, f.n_pred, fp,       \
+                   (int)n_rep);                                                                            \
+    } else
+#define PRR_LS_K(DD, MN, PR)                                                                                \
+    PRR_LS(DD, 1, false, MN, PR) PRR_LS(DD, 2, false, MN, PR) PRR_LS(DD, 4, false, MN, PR)                    \
+    PRR_LS(DD, 1, true, MN, PR) PRR_LS(DD, 2, true, MN, PR) PRR_LS(DD, 4, true, MN, PR)                       \
+    PRR_LS(DD, 8, true, MN, PR) PRR_LS(DD, 16, true, MN, PR)
+#define PRR_LS_ALL(MN, PR) PRR_LS_K(128, MN, PR) PRR_LS_K(64, MN, PR)
+    PRR_LS_ALL(false, false) PRR_LS_ALL(true, false) PRR_LS_ALL(false, true) PRR_LS_ALL(true, true)
+    { return hipErrorInvalidValue; }
+#undef PRR_LS_ALL
+#undef PRR_LS_K
+#undef PRR_LS
+    return f.fuse_pred ? hipSuccess : predict_alone(pred, stream);
+    }
+}
+
+}  // namespace
 }  // namespace prr

@@ -9,12 +9,14 @@ LLM Decoding" (full paper text).
 
 Two schedules of the same work, with identical results:
 
-* ``step`` (the default): one stream.  ``prr_select_spec`` runs scoring and the speculative pass in one
-  grid (their workgroups share the GPU, so the overlap happens inside the launch), the top-K follows,
-  then repair, then the predictor:
-      select_spec(q^t, P^t) -> A^t, M^t, IS^t, state  ->  repair(M^t) -> O^t  ->  predict(IS^t) -> P^{t+1}
-  On this GPU a dependency between two streams costs about 10 us from the producer's end to the
-  consumer's start, against about 1 us between kernels of one stream, so this is the fast schedule.
+* ``step`` (the default): one stream.  ``prr_layer_step`` runs scoring, the speculative pass and repair in
+  one grid (their workgroups share the GPU, so the overlap happens inside the launch, and the repair of a
+  (sequence, kv head) starts as soon as its top-K is known), then the predictor:
+      layer_step(q^t, P^t) -> A^t, M^t, IS^t, O^t  ->  predict(IS^t) -> P^{t+1}
+  With fused=False at construction: ``prr_select_spec`` (scoring and the speculative pass in one grid, the
+  top-K), then ``prr_repair``, then the predictor.  On this GPU a dependency between two streams costs
+  about 10 us from the producer's end to the consumer's start, against about 1 us between kernels of one
+  stream, so the one-stream schedules are the fast ones.
 * ``step_two_streams``: the pages' schedule on three streams (selection on the critical stream, the
   speculative pass on a side stream, the predictor on a third), joined by events.  Kept to measure the
   difference.
@@ -83,7 +85,7 @@ class PRRLayer:
 
     def __init__(self, kv: bd.KVCache, num_q_heads: int, block: int, topk: int, budget: int,
                  ema=(0.6, 0.3, 0.5), scale: Optional[float] = None, score_mode: str = "quest",
-                 max_budget: Optional[int] = None):
+                 max_budget: Optional[int] = None, fused: bool = True):
         dev = kv.k.device
         # |P| may later change (set_budget) up to max_budget: sets and workspaces are sized for it
         self.max_budget = max(1, budget, max_budget or 0)
@@ -112,6 +114,10 @@ class PRRLayer:
         self.out = torch.zeros((B, num_q_heads, d), dtype=torch.float32, device=dev)
         self.ws_spec = bd.select_spec_workspace_for(kv, num_q_heads, block, topk, self.max_budget)
         self.ws_repair = bd.workspace_for(kv, num_q_heads, block, max(1, topk))
+        # the layer step in one launch (prr_layer_step), or select_spec then repair
+        self.fused = bool(fused)
+        self.ws_layer = (bd.layer_step_workspace_for(kv, num_q_heads, block, topk, self.max_budget, max(1, topk))
+                         if self.fused else None)
         # the predictor's workspace depends on |P| and is not monotone in it (a budget with no part-parallel
         # plan needs none): sized for every budget set_budget may choose
         self.ws_predict = bd.predict_workspace_for(B, H, self.nmax, range(1, self.max_budget + 1), dev)
@@ -162,16 +168,24 @@ class PRRLayer:
         P, Pn = self.P[self.cur], self.P[1 - self.cur]
         if timers and timers.start:
             timers.start.record(s)
-        if timers and timers.kernel_start:
-            bd.time_next_kernel(timers.kernel_start, None)
-        bd.select_spec(q, self.kv, self.meta, self.block, self.topk, P, self.scale, scores=self.scores, A=self.A,
-                       M=self.M, out=self.state, ws=self.ws_spec, mode=self.score_mode, pred=carry, stream=s)
-        if timers and timers.select_spec_end:
-            timers.select_spec_end.record(s)
-        if timers and timers.kernel_end:
-            bd.time_next_kernel(None, timers.kernel_end)
-        bd.repair(q, self.kv, self.block, self.M, self.scale, self.state, out=self.out, ws=self.ws_repair,
-                  stream=s)
+        if self.fused:
+            if timers and (timers.kernel_start or timers.kernel_end):
+                bd.time_next_kernel(timers.kernel_start, timers.kernel_end)
+            bd.layer_step(q, self.kv, self.meta, self.block, self.topk, P, self.scale, self.scores, self.A, self.M,
+                          self.state, out=self.out, ws=self.ws_layer, mode=self.score_mode, pred=carry, stream=s)
+            if timers and timers.select_spec_end:
+                timers.select_spec_end.record(s)
+        else:
+            if timers and timers.kernel_start:
+                bd.time_next_kernel(timers.kernel_start, None)
+            bd.select_spec(q, self.kv, self.meta, self.block, self.topk, P, self.scale, scores=self.scores, A=self.A,
+                           M=self.M, out=self.state, ws=self.ws_spec, mode=self.score_mode, pred=carry, stream=s)
+            if timers and timers.select_spec_end:
+                timers.select_spec_end.record(s)
+            if timers and timers.kernel_end:
+                bd.time_next_kernel(None, timers.kernel_end)
+            bd.repair(q, self.kv, self.block, self.M, self.scale, self.state, out=self.out, ws=self.ws_repair,
+                      stream=s)
         if timers and timers.repair_end:
             timers.repair_end.record(s)
         args = bd.PredictArgs(self.scores, self.kv.seq_len, self.block, self.alpha, self.beta, self.gamma,

@@ -247,6 +247,31 @@ prr_status prr_select_spec_predict(const void *q, int32_t num_q_heads, const prr
                                    prr_attn_state *out, void *ws, size_t ws_bytes, const prr_predict_args *pred,
                                    hipStream_t stream);
 
+/* The whole layer step of the method ([paper] §1 and the Figure 1 flow, §3, §4.3; [blog] Eq. (6)): selection of
+ * A (with M = A \ P), the speculative pass over P and the repair of its state with M, with the results of
+ *     prr_select_spec_predict(q, ..., P, scores, A, M, scale, state, ws, pred)
+ *     prr_repair(q, ..., M, scale, state, out)
+ * scores, A and M bit for bit; state (fp32, written, not read) = the attention state over P u M, and out
+ * (nullable, [batch][num_q_heads][head_dim] fp32) = acc / l, within float32 rounding of those two calls
+ * (the partial states merge in another grouping).  With a bf16 or fp8 cache and a top-K that finishes inside
+ * the launch (up to 4096 candidate slots per row: every workload here except rows of 32768 blocks at
+ * K = 256), it is one launch: the repair of a (sequence, kv head) starts as soon as its M is known, while
+ * other units still stream their speculative tiles, and the speculative and repair partial states merge
+ * once.  Otherwise it runs the two calls' launches.  Arguments as for prr_select_spec_predict (pred may be
+ * NULL).  ws: prr_layer_step_workspace_bytes(kv, num_q_heads, block, topk, P->cap, M->cap), zeroed once
+ * like an attention workspace; every call leaves it ready for the next.  In the one-launch form a repair
+ * workgroup waits for its unit's M with a bounded wait; the 32-bit word at the start of the workspace's
+ * final 256 bytes is a status word that such a workgroup sets to non-zero if it ever gives up (after about
+ * a second: that state then lacks the unit's repair).  Workgroups are dispatched in index order, selection
+ * first, so it stays zero; the library never clears it. */
+size_t prr_layer_step_workspace_bytes(const prr_kv_cache *kv, int32_t num_q_heads, int32_t block, int32_t topk,
+                                      int32_t p_cap, int32_t m_cap);
+
+prr_status prr_layer_step(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
+                          prr_score_mode mode, int32_t block, int32_t topk, const prr_block_set *P, double *scores,
+                          prr_block_set *A, prr_block_set *M, float scale, prr_attn_state *state, float *out,
+                          void *ws, size_t ws_bytes, const prr_predict_args *pred, hipStream_t stream);
+
 /* Speculative block-sparse decode attention over P ([paper] §3 and §4.3, the instrumented speculative
  * kernel that also stores the softmax denominator and running maximum; [paper] §1).  Writes the
  * unnormalised state of every query head over the tokens of its kv head's blocks in P (tokens at or
