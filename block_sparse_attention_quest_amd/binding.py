@@ -46,7 +46,8 @@ class KvCacheStruct(ctypes.Structure):
 
 
 class BlockSetStruct(ctypes.Structure):
-    _fields_ = [("idx", ctypes.c_void_p), ("count", ctypes.c_void_p), ("cap", ctypes.c_int32)]
+    _fields_ = [("idx", ctypes.c_void_p), ("count", ctypes.c_void_p), ("cap", ctypes.c_int32),
+                ("pages", ctypes.c_void_p)]
 
 
 class AttnStateStruct(ctypes.Structure):
@@ -59,7 +60,7 @@ class PredictArgsStruct(ctypes.Structure):
                 ("alpha", ctypes.c_double), ("beta", ctypes.c_double), ("gamma", ctypes.c_double),
                 ("budget", ctypes.c_int32), ("level", ctypes.c_void_p), ("trend", ctypes.c_void_p),
                 ("live", ctypes.c_void_p), ("P_next", ctypes.POINTER(BlockSetStruct)), ("ws", ctypes.c_void_p),
-                ("ws_bytes", ctypes.c_size_t)]
+                ("ws_bytes", ctypes.c_size_t), ("kv", ctypes.POINTER(KvCacheStruct))]
 
 
 _P = ctypes.POINTER
@@ -90,7 +91,7 @@ _SIGS = {
                                       _SZ, _P(PredictArgsStruct), _VP]),
     "prr_predict_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "prr_predict": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _D, _D, _D, _I32, _VP, _VP, _VP,
-                                   _P(BlockSetStruct), _VP, _SZ, _VP]),
+                                   _P(BlockSetStruct), _P(KvCacheStruct), _VP, _SZ, _VP]),
     "prr_spec_attn": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _I32, _P(BlockSetStruct), _F,
                                      _P(AttnStateStruct), _VP, _SZ, _VP]),
     "prr_spec_attn_noalloc": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _I32, _P(BlockSetStruct), _F,
@@ -194,22 +195,29 @@ class KVCache:
 
 @dataclass
 class BlockSet:
-    """idx [B][Hkv][cap] int32, count [B][Hkv] int32 (device)."""
+    """idx [B][Hkv][cap] int32, count [B][Hkv] int32 (device); pages (optional) [B][Hkv][cap * block / 16]
+    int32: the set's page work list (physical page of every page of the set's blocks, -1 for a page with no
+    token yet), written by the call that produces the set and read by the attention passes over it."""
 
     idx: torch.Tensor
     count: torch.Tensor
+    pages: Optional[torch.Tensor] = None
 
     @property
     def cap(self) -> int:
         return self.idx.shape[-1]
 
     @staticmethod
-    def empty(batch: int, hkv: int, cap: int, device="cuda") -> "BlockSet":
+    def empty(batch: int, hkv: int, cap: int, device="cuda", block: int = 0) -> "BlockSet":
+        """block > 0: with a page work list for that block size."""
+        pages = (torch.full((batch, hkv, cap * (block // PAGE_SIZE)), -1, dtype=torch.int32, device=device)
+                 if block > 0 else None)
         return BlockSet(torch.zeros((batch, hkv, cap), dtype=torch.int32, device=device),
-                        torch.zeros((batch, hkv), dtype=torch.int32, device=device))
+                        torch.zeros((batch, hkv), dtype=torch.int32, device=device), pages)
 
     def struct(self) -> BlockSetStruct:
-        return BlockSetStruct(self.idx.data_ptr(), self.count.data_ptr(), self.cap)
+        return BlockSetStruct(self.idx.data_ptr(), self.count.data_ptr(), self.cap,
+                              self.pages.data_ptr() if self.pages is not None else None)
 
     def lists(self):
         """Host copy as nested python lists [b][kvh] -> list of block ids."""
@@ -402,8 +410,7 @@ def select_spec(q: torch.Tensor, kv: KVCache, meta: torch.Tensor, block: int, to
                                  ctypes.byref(o_s), ws.ptr(), ws.nbytes, _stream(stream))
         _check(st, "prr_select_spec")
     else:
-        pn = pred.P_next.struct()
-        pa = pred.struct(pn)
+        pa, keep = pred.structs()
         st = lib.prr_select_spec_predict(_ptr(q), Hq, ctypes.byref(s), _ptr(meta), _mode(mode), block, topk,
                                          ctypes.byref(p_s), _ptr(scores), ctypes.byref(a_s), ctypes.byref(m_s),
                                          float(scale), ctypes.byref(o_s), ws.ptr(), ws.nbytes, ctypes.byref(pa),
@@ -433,8 +440,7 @@ def layer_step(q: torch.Tensor, kv: KVCache, meta: torch.Tensor, block: int, top
     a_s, p_s, m_s, o_s = A.struct(), P.struct(), M.struct(), state.struct()
     pa = None
     if pred is not None:
-        pn = pred.P_next.struct()
-        pa = pred.struct(pn)
+        pa, keep = pred.structs()
     st = lib.prr_layer_step(_ptr(q), Hq, ctypes.byref(s), _ptr(meta), _mode(mode), block, topk, ctypes.byref(p_s),
                             _ptr(scores), ctypes.byref(a_s), ctypes.byref(m_s), float(scale), ctypes.byref(o_s),
                             _ptr(out), ws.ptr(), ws.nbytes, ctypes.byref(pa) if pa is not None else None,
@@ -459,28 +465,41 @@ class PredictArgs:
     live: torch.Tensor
     P_next: "BlockSet"
     ws: Optional["Workspace"] = None
+    kv: Optional["KVCache"] = None   # needed when P_next has a page list (its page table)
 
-    def struct(self, p_next_struct) -> PredictArgsStruct:
+    def struct(self, p_next_struct, kv_struct=None) -> PredictArgsStruct:
+        """p_next_struct / kv_struct: the caller keeps them alive for the call."""
         B, H, nmax = self.scores.shape
         return PredictArgsStruct(_ptr(self.scores), _ptr(self.seq_len), B, H, self.block, nmax, float(self.alpha),
                                  float(self.beta), float(self.gamma), self.budget, _ptr(self.level),
                                  _ptr(self.trend), _ptr(self.live), ctypes.pointer(p_next_struct),
                                  self.ws.ptr() if self.ws is not None else None,
-                                 self.ws.nbytes if self.ws is not None else 0)
+                                 self.ws.nbytes if self.ws is not None else 0,
+                                 ctypes.pointer(kv_struct) if kv_struct is not None else None)
+
+    def structs(self):
+        """(args, keep-alive) for a call that carries this step."""
+        pn = self.P_next.struct()
+        ks = self.kv.struct() if self.kv is not None else None
+        return self.struct(pn, ks), (pn, ks)
 
 
 def predict(scores: torch.Tensor, seq_len: torch.Tensor, block: int, alpha: float, beta: float,
             gamma: float, budget: int, level: torch.Tensor, trend: torch.Tensor, live: torch.Tensor,
-            P_next: Optional[BlockSet] = None, ws: Optional[Workspace] = None, stream=None) -> BlockSet:
+            P_next: Optional[BlockSet] = None, ws: Optional[Workspace] = None, stream=None,
+            kv: Optional["KVCache"] = None) -> BlockSet:
     """One EMA step over scores [B][Hkv][Nmax]; updates level/trend/live in place; returns P_next.  ws
-    (predict_workspace_for): long rows are then updated in parallel parts."""
+    (predict_workspace_for): long rows are then updated in parallel parts.  kv: the cache whose page table
+    P_next's page list (if it has one) maps through."""
     lib = load_library()
     B, H, nmax = scores.shape
     if P_next is None:
         P_next = BlockSet.empty(B, H, max(1, budget), scores.device)
     ps = P_next.struct()
+    ks = kv.struct() if kv is not None else None
     st = lib.prr_predict(_ptr(scores), _ptr(seq_len), B, H, block, nmax, float(alpha), float(beta),
                          float(gamma), budget, _ptr(level), _ptr(trend), _ptr(live), ctypes.byref(ps),
+                         ctypes.byref(ks) if ks is not None else None,
                          ws.ptr() if ws is not None else None, ws.nbytes if ws is not None else 0,
                          _stream(stream))
     _check(st, "prr_predict")

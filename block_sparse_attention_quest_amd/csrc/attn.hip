@@ -96,10 +96,10 @@ size_t attn_workspace_bytes(int batch, int hq, int hkv, int d, int block, int ca
 }
 
 hipError_t launch_attn(const KvDesc &kv, const void *q, int hq, int block, const int32_t *idx,
-                       const int32_t *count, int cap, float scale, float *acc, float *l, float *m,
-                       float *out, bool repair, void *ws, hipStream_t stream) {
-    AttnParams p;
-    const int grid = attn_setup(p, kv, q, hq, block, idx, count, cap, scale, acc, l, m, out, repair, ws);
+                       const int32_t *count, const int32_t *pages, int cap, float scale, float *acc, float *l,
+                       float *m, float *out, bool repair, void *ws, hipStream_t stream) {
+    AttnParams p{};
+    const int grid = attn_setup(p, kv, q, hq, block, idx, count, pages, cap, scale, acc, l, m, out, repair, ws);
     void (*k)(AttnParams);
     const bool d128 = kv.d == 128;
     if (kv.fp8) {
@@ -116,8 +116,8 @@ hipError_t launch_attn(const KvDesc &kv, const void *q, int hq, int block, const
 }
 
 hipError_t launch_spec_noalloc(const KvDesc &kv, const void *q, int hq, int block, const int32_t *idx,
-                               const int32_t *count, int cap, float scale, float *acc, float *l, float *m,
-                               hipStream_t stream) {
+                               const int32_t *count, const int32_t *pages, int cap, float scale, float *acc,
+                               float *l, float *m, hipStream_t stream) {
     void *ws = nullptr;
     hipError_t e = scratch_address(stream, &ws);
     if (e != hipSuccess) return e;
@@ -125,7 +125,7 @@ hipError_t launch_spec_noalloc(const KvDesc &kv, const void *q, int hq, int bloc
     // written before they are read
     e = launch_clear(ws, counters_bytes(kv.batch * kv.hkv), stream);
     if (e != hipSuccess) return e;
-    return launch_attn(kv, q, hq, block, idx, count, cap, scale, acc, l, m, nullptr, false, ws, stream);
+    return launch_attn(kv, q, hq, block, idx, count, pages, cap, scale, acc, l, m, nullptr, false, ws, stream);
 }
 
 hipError_t launch_clear(void *ws, size_t bytes, hipStream_t stream) {

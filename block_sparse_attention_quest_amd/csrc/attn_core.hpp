@@ -81,6 +81,7 @@ struct AttnParams {
     const int32_t *seq_len;
     const int32_t *idx;
     const int32_t *count;
+    const int32_t *pages;   // the set's page work list (may be null): [units][cap ppb] physical pages or -1
     float *acc;
     float *l;
     float *m;
@@ -144,9 +145,12 @@ __device__ __forceinline__ int unit_pages(const AttnParams &p, int u) {
 // Page lookups of the wave's pages wbeg .. wbeg + N - 1 of the unit's expanded page list.  Lane
 // i < N looks up page wbeg + i with vector loads: the set entry, then the page-table entry (two
 // dependent memory rounds, through the vector memory path, which keeps many more requests in flight
-// than the scalar cache).  The addresses do not depend on the set size, so these loads are issued
-// together with the load of the set size; finish() masks entries at or past wend and broadcasts
-// physical page and valid-token count to scalar registers.
+// than the scalar cache).  With a page work list (p.pages) the physical page comes with the set entry,
+// in the same round: only a list slot of -1 whose page holds tokens by now (slen: the sequence length)
+// is looked up in the page table; a -1 page without tokens is masked whatever its address.  The addresses
+// do not depend on the set size, so these loads are issued together with the load of the set size;
+// finish() masks entries at or past wend and broadcasts physical page and valid-token count to scalar
+// registers.
 struct PageLookup {
     int ph;     // physical page (raw)
     int lp;     // logical page (0 when the set entry is out of range)
@@ -154,7 +158,7 @@ struct PageLookup {
 };
 
 template <bool COHERENT = false>
-__device__ __forceinline__ PageLookup page_lookup(const AttnParams &p, int b, int u, int wbeg, int pw) {
+__device__ __forceinline__ PageLookup page_lookup(const AttnParams &p, int b, int u, int wbeg, int pw, int slen) {
     const int i = threadIdx.x & 63;
     PageLookup r;
     r.ph = 0;
@@ -165,10 +169,14 @@ __device__ __forceinline__ PageLookup page_lookup(const AttnParams &p, int b, in
         const int li = gpc / p.ppb;
         const int sub = gpc - li * p.ppb;
         const int blk = ld_set<COHERENT>(&p.idx[(size_t)u * p.cap + li]);
+        const int listed = p.pages ? ld_set<COHERENT>(&p.pages[((size_t)u * p.cap) * p.ppb + gpc]) : -1;
         const long lp = (long)blk * p.ppb + sub;
         r.lp_ok = blk >= 0 && lp < p.max_pages;
         r.lp = r.lp_ok ? (int)lp : 0;
-        r.ph = p.page_table[(size_t)b * p.max_pages + r.lp];
+        if (!p.pages || (listed < 0 && r.lp_ok && (long)r.lp * kPage < slen))
+            r.ph = p.page_table[(size_t)b * p.max_pages + r.lp];
+        else
+            r.ph = listed;
     }
     return r;
 }
@@ -684,7 +692,8 @@ __device__ __forceinline__ void attn_chunks(const AttnParams &p, const FusedPara
         const int u = c % p.units, k = c / p.units;
         const int b = u / p.hkv, kvh = u - b * p.hkv;
         const int wbeg = k * cp + wave * pw;
-        const PageLookup look = page_lookup(p, b, u, wbeg, pw);
+        const int slen = p.seq_len[b];
+        const PageLookup look = page_lookup(p, b, u, wbeg, pw, slen);
         // In repair mode the incoming m and l go out with the set lookups and reach LDS only after the
         // tile walk, so no tile load waits for them.
         float mo_in = 0.0f, lo_in = 0.0f;
@@ -696,7 +705,6 @@ __device__ __forceinline__ void attn_chunks(const AttnParams &p, const FusedPara
         const int npages = unit_pages(p, u);
         const int nch = max(1, (npages + cp - 1) / cp);
         if (k >= nch) continue;
-        const int slen = p.seq_len[b];
         const size_t head0 = (size_t)b * p.hq + (size_t)kvh * G;
         if (REPAIR && npages == 0) {
             // nothing missed: the state stays bit-for-bit as it is; only the normalised output
@@ -861,7 +869,7 @@ __device__ __forceinline__ void fused_repair_slots(const AttnParams &ps, const F
         if (threadIdx.x == 0) wait_ready(fp, u);
         __syncthreads();
         const int wbeg = k * cp + wave * pw;
-        const PageLookup look = page_lookup<true>(pm, b, u, wbeg, pw);
+        const PageLookup look = page_lookup<true>(pm, b, u, wbeg, pw, slen);
         const int npages = unit_pages<true>(pm, u);
         const int nch_spec = max(1, (nsp + ps.cp - 1) / ps.cp);
         const size_t head0 = (size_t)b * pm.hq + (size_t)kvh * G;
@@ -941,8 +949,8 @@ size_t max_chunks(int units, int block, int cap) {
 // Fills the kernel parameters of one speculative (repair = false) or repair launch and returns its
 // grid size (workgroups).  target_wgs: workgroups to spread a full set over (default: one per CU).
 int attn_setup(AttnParams &p, const KvDesc &kv, const void *q, int hq, int block, const int32_t *idx,
-               const int32_t *count, int cap, float scale, float *acc, float *l, float *m, float *out,
-               bool repair, void *ws, int target_wgs = 0) {
+               const int32_t *count, const int32_t *pages, int cap, float scale, float *acc, float *l, float *m,
+               float *out, bool repair, void *ws, int target_wgs = 0) {
     p.q = q;
     p.k = kv.k;
     p.v = kv.v;
@@ -950,6 +958,7 @@ int attn_setup(AttnParams &p, const KvDesc &kv, const void *q, int hq, int block
     p.seq_len = kv.seq_len;
     p.idx = idx;
     p.count = count;
+    p.pages = pages;
     p.acc = acc;
     p.l = l;
     p.m = m;

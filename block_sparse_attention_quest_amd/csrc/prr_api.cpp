@@ -232,8 +232,8 @@ prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv
     return hip_status(prr::launch_select(desc(kv), q, num_q_heads, meta, block, prr_meta_stride(kv, block),
                                          nmax, topk, P ? P->idx : nullptr, P ? P->count : nullptr,
                                          P ? P->cap : 0, scores, A->idx, A->count, A->cap,
-                                         M ? M->idx : nullptr, M ? M->count : nullptr, M ? M->cap : 0,
-                                         mode == PRR_SCORE_MEAN, stream));
+                                         M ? M->idx : nullptr, M ? M->count : nullptr, M ? M->pages : nullptr,
+                                         M ? M->cap : 0, mode == PRR_SCORE_MEAN, stream));
 }
 
 size_t prr_select_spec_workspace_bytes(const prr_kv_cache *kv, int32_t num_q_heads, int32_t block, int32_t topk,
@@ -248,12 +248,18 @@ size_t prr_select_spec_workspace_bytes(const prr_kv_cache *kv, int32_t num_q_hea
 static prr_status check_predict(const double *scores, const int32_t *seq_len, int32_t batch,
                                 int32_t num_kv_heads, int32_t block, int32_t max_blocks, int32_t budget,
                                 const double *level, const double *trend, const int32_t *live,
-                                const prr_block_set *P_next) {
+                                const prr_block_set *P_next, const prr_kv_cache *kv) {
     if (!scores || !seq_len || !level || !trend || !live) return PRR_EINVAL;
     if (batch <= 0 || num_kv_heads <= 0 || block <= 0 || max_blocks <= 0 || budget < 0) return PRR_EINVAL;
     PRR_TRY(check_set(P_next));
     if (P_next->cap < budget) return PRR_EINVAL;
     if (max_blocks > prr::kMaxSelectN) return PRR_EUNSUPPORTED;
+    if (P_next->pages) {
+        // the page list maps through this cache's page table, for the same sequences and block size
+        PRR_TRY(check_kv(kv));
+        PRR_TRY(check_block(kv, block));
+        if (kv->batch != batch || kv->num_kv_heads != num_kv_heads) return PRR_EINVAL;
+    }
     return PRR_OK;
 }
 
@@ -264,14 +270,16 @@ static prr_status predict_args(const prr_predict_args *pred, const double *score
     pa = prr::PredictArgs{};
     if (pred) {
         PRR_TRY(check_predict(pred->scores, pred->seq_len, pred->batch, pred->num_kv_heads, pred->block,
-                              pred->max_blocks, pred->budget, pred->level, pred->trend, pred->live, pred->P_next));
+                              pred->max_blocks, pred->budget, pred->level, pred->trend, pred->live, pred->P_next,
+                              pred->kv));
         // the predictor writes level, trend, live and P_next while the selection writes scores, A and M
         // and reads P: none of them may be shared
-        const void *sel_bufs[] = {scores, P->idx, P->count, A->idx, A->count, M->idx, M->count};
-        const void *pred_out[] = {pred->level, pred->trend, pred->live, pred->P_next->idx, pred->P_next->count};
+        const void *sel_bufs[] = {scores, P->idx, P->count, P->pages, A->idx, A->count, M->idx, M->count, M->pages};
+        const void *pred_out[] = {pred->level, pred->trend, pred->live, pred->P_next->idx, pred->P_next->count,
+                                  pred->P_next->pages};
         for (const void *x : pred_out)
             for (const void *y : sel_bufs)
-                if (x == y) return PRR_EINVAL;
+                if (x && x == y) return PRR_EINVAL;
         if ((const void *)pred->scores == (const void *)scores) return PRR_EINVAL;
         pa.scores = pred->scores;
         pa.seq_len = pred->seq_len;
@@ -289,6 +297,11 @@ static prr_status predict_args(const prr_predict_args *pred, const double *score
         pa.p_idx = pred->P_next->idx;
         pa.p_cnt = pred->P_next->count;
         pa.p_cap = pred->P_next->cap;
+        if (pred->P_next->pages) {
+            pa.p_pages = pred->P_next->pages;
+            pa.page_table = pred->kv->page_table;
+            pa.max_pages = pred->kv->max_pages;
+        }
         const size_t need = prr::predict_workspace_bytes(pred->batch, pred->num_kv_heads, pred->max_blocks,
                                                          pred->budget);
         if (pred->ws && pred->ws_bytes < need) return PRR_EWORKSPACE;
@@ -321,9 +334,10 @@ prr_status prr_select_spec_predict(const void *q, int32_t num_q_heads, const prr
     PRR_TRY(predict_args(pred, scores, P, A, M, pa));
     PRR_TRY(check_input_set(kv, block, P, stream));
     return hip_status(prr::launch_select_spec(desc(kv), q, num_q_heads, meta, block, prr_meta_stride(kv, block),
-                                              nmax, topk, P->idx, P->count, P->cap, scores, A->idx, A->count,
-                                              A->cap, M->idx, M->count, M->cap, scale, out->acc, out->l, out->m,
-                                              ws, mode == PRR_SCORE_MEAN, pred ? &pa : nullptr, stream));
+                                              nmax, topk, P->idx, P->count, P->pages, P->cap, scores, A->idx,
+                                              A->count, A->cap, M->idx, M->count, M->pages, M->cap, scale, out->acc,
+                                              out->l, out->m, ws, mode == PRR_SCORE_MEAN, pred ? &pa : nullptr,
+                                              stream));
 }
 
 size_t prr_layer_step_workspace_bytes(const prr_kv_cache *kv, int32_t num_q_heads, int32_t block, int32_t topk,
@@ -358,9 +372,10 @@ prr_status prr_layer_step(const void *q, int32_t num_q_heads, const prr_kv_cache
     PRR_TRY(predict_args(pred, scores, P, A, M, pa));
     PRR_TRY(check_input_set(kv, block, P, stream));
     return hip_status(prr::launch_layer_step(desc(kv), q, num_q_heads, meta, block, prr_meta_stride(kv, block), nmax,
-                                             topk, P->idx, P->count, P->cap, scores, A->idx, A->count, A->cap, M->idx,
-                                             M->count, M->cap, scale, state->acc, state->l, state->m, out, ws,
-                                             mode == PRR_SCORE_MEAN, pred ? &pa : nullptr, stream));
+                                             topk, P->idx, P->count, P->pages, P->cap, scores, A->idx, A->count, A->cap,
+                                             M->idx, M->count, M->pages, M->cap, scale, state->acc, state->l,
+                                             state->m, out, ws, mode == PRR_SCORE_MEAN, pred ? &pa : nullptr,
+                                             stream));
 }
 
 prr_status prr_select_spec(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
@@ -380,15 +395,19 @@ size_t prr_predict_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t 
 prr_status prr_predict(const double *scores, const int32_t *seq_len, int32_t batch,
                        int32_t num_kv_heads, int32_t block, int32_t max_blocks, double alpha,
                        double beta, double gamma, int32_t budget, double *level, double *trend,
-                       int32_t *live, prr_block_set *P_next, void *ws, size_t ws_bytes, hipStream_t stream) {
+                       int32_t *live, prr_block_set *P_next, const prr_kv_cache *kv, void *ws, size_t ws_bytes,
+                       hipStream_t stream) {
     CallTiming timing_;
     PRR_TRY(check_predict(scores, seq_len, batch, num_kv_heads, block, max_blocks, budget, level, trend, live,
-                          P_next));
+                          P_next, kv));
     const size_t need = prr::predict_workspace_bytes(batch, num_kv_heads, max_blocks, budget);
     if (ws && ws_bytes < need) return PRR_EWORKSPACE;
+    const bool listed = P_next->pages != nullptr;
     return hip_status(prr::launch_predict(scores, seq_len, batch, num_kv_heads, block, max_blocks, alpha,
                                           beta, gamma, budget, level, trend, live, P_next->idx,
-                                          P_next->count, P_next->cap, need ? ws : nullptr, stream));
+                                          P_next->count, P_next->pages, P_next->cap,
+                                          listed ? kv->page_table : nullptr, listed ? kv->max_pages : 0,
+                                          need ? ws : nullptr, stream));
 }
 
 prr_status prr_spec_attn(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, int32_t block,
@@ -398,7 +417,7 @@ prr_status prr_spec_attn(const void *q, int32_t num_q_heads, const prr_kv_cache 
     PRR_TRY(attn_common(q, num_q_heads, kv, block, P, ws, ws_bytes));
     if (!out || !out->acc || !out->l || !out->m) return PRR_EINVAL;
     PRR_TRY(check_input_set(kv, block, P, stream));
-    return hip_status(prr::launch_attn(desc(kv), q, num_q_heads, block, P->idx, P->count, P->cap, scale,
+    return hip_status(prr::launch_attn(desc(kv), q, num_q_heads, block, P->idx, P->count, P->pages, P->cap, scale,
                                        out->acc, out->l, out->m, nullptr, false, ws, stream));
 }
 
@@ -416,8 +435,8 @@ prr_status prr_spec_attn_noalloc(const void *q, int32_t num_q_heads, const prr_k
         prr::kNoAllocScratchBytes)
         return PRR_EWORKSPACE;
     PRR_TRY(check_input_set(kv, block, P, stream));
-    return hip_status(prr::launch_spec_noalloc(desc(kv), q, num_q_heads, block, P->idx, P->count, P->cap, scale,
-                                               out->acc, out->l, out->m, stream));
+    return hip_status(prr::launch_spec_noalloc(desc(kv), q, num_q_heads, block, P->idx, P->count, P->pages, P->cap,
+                                               scale, out->acc, out->l, out->m, stream));
 }
 
 prr_status prr_repair(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, int32_t block,
@@ -427,7 +446,7 @@ prr_status prr_repair(const void *q, int32_t num_q_heads, const prr_kv_cache *kv
     PRR_TRY(attn_common(q, num_q_heads, kv, block, M, ws, ws_bytes));
     if (!state || !state->acc || !state->l || !state->m) return PRR_EINVAL;
     PRR_TRY(check_input_set(kv, block, M, stream));
-    return hip_status(prr::launch_attn(desc(kv), q, num_q_heads, block, M->idx, M->count, M->cap, scale,
+    return hip_status(prr::launch_attn(desc(kv), q, num_q_heads, block, M->idx, M->count, M->pages, M->cap, scale,
                                        state->acc, state->l, state->m, out, true, ws, stream));
 }
 

@@ -65,9 +65,10 @@ struct KvDesc {
 // then one partial state per chunk.
 size_t attn_workspace_bytes(int batch, int hq, int hkv, int d, int block, int cap);
 
+// pages (may be null): the set's page work list.
 hipError_t launch_attn(const KvDesc &kv, const void *q, int hq, int block, const int32_t *idx,
-                       const int32_t *count, int cap, float scale, float *acc, float *l, float *m,
-                       float *out, bool repair, void *ws, hipStream_t stream);
+                       const int32_t *count, const int32_t *pages, int cap, float scale, float *acc, float *l,
+                       float *m, float *out, bool repair, void *ws, hipStream_t stream);
 
 hipError_t launch_clear(void *ws, size_t bytes, hipStream_t stream);
 
@@ -75,8 +76,8 @@ hipError_t launch_clear(void *ws, size_t bytes, hipStream_t stream);
 // (prr_spec_attn_noalloc); the caller has checked that attn_workspace_bytes fits.
 constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
 hipError_t launch_spec_noalloc(const KvDesc &kv, const void *q, int hq, int block, const int32_t *idx,
-                               const int32_t *count, int cap, float scale, float *acc, float *l, float *m,
-                               hipStream_t stream);
+                               const int32_t *count, const int32_t *pages, int cap, float scale, float *acc,
+                               float *l, float *m, hipStream_t stream);
 
 // Checking mode (PRR_CHECK=1 in the environment): validates a block set on the stream and waits for the
 // result; *violation gets a bit mask (1 count outside [0, cap], 2 entry out of range, 4 repeated entry).
@@ -91,12 +92,13 @@ hipError_t launch_meta(const KvDesc &kv, int block, int stride, void *meta, bool
 hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *meta, int block,
                          int stride, int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt,
                          int p_cap, double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap,
-                         int32_t *m_idx, int32_t *m_cnt, int m_cap, bool mean, hipStream_t stream);
+                         int32_t *m_idx, int32_t *m_cnt, int32_t *m_pages, int m_cap, bool mean, hipStream_t stream);
 
-// Top-K + M = A \ P from scores already in place (the second half of launch_select).
+// Top-K + M = A \ P from scores already in place (the second half of launch_select).  m_pages (may be
+// null): M's page work list, written with M.
 hipError_t launch_topk(const KvDesc &kv, int block, int nmax, int topk, const double *scores,
                        const int32_t *p_idx, const int32_t *p_cnt, int p_cap, int32_t *a_idx, int32_t *a_cnt,
-                       int a_cap, int32_t *m_idx, int32_t *m_cnt, int m_cap, hipStream_t stream);
+                       int a_cap, int32_t *m_idx, int32_t *m_cnt, int32_t *m_pages, int m_cap, hipStream_t stream);
 
 // How prr_select_spec ranks a unit's blocks: kpt keys per thread inside the launch (two: over candidates
 // of a two-stage top-K with kl candidates per scoring workgroup), or kpt = 0: the separate top-K kernel.
@@ -118,8 +120,9 @@ SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean);
 // (zero at rest; the last group of a unit resets its counter).  live (a predictor step's, may be null):
 // set to the unit's block count by its last group.
 hipError_t launch_topk_groups(const KvDesc &kv, int block, int nmax, int topk, const int32_t *p_idx,
-                              const int32_t *p_cnt, int p_cap, int32_t *a_idx, int32_t *a_cnt, int a_cap,
-                              int32_t *m_idx, int32_t *m_cnt, int m_cap, const SelectSpecPlan &plan, int nparts,
+                              const int32_t *p_cnt, int p_cap, int32_t *a_idx, int32_t *a_cnt, int32_t *a_pages,
+                              int a_cap, int32_t *m_idx, int32_t *m_cnt, int32_t *m_pages, int m_cap,
+                              const SelectSpecPlan &plan, int nparts,
                               void *cand1, void *cand2, uint32_t *arrivals, hipStream_t stream,
                               int32_t *live = nullptr);
 
@@ -145,6 +148,9 @@ struct PredictArgs {
     int32_t *p_cnt;
     int p_cap;
     void *ws;   // predictor workspace for long rows (may be null)
+    int32_t *p_pages;             // P's page work list (may be null), through page_table [batch][max_pages]
+    const int32_t *page_table;
+    int max_pages;
 };
 
 // Rows of at most this many blocks let the predictor step run inside the selection + speculative launch.
@@ -153,16 +159,16 @@ constexpr int kMaxFusedPredictN = 2048;
 // pred (may be null): a predictor step over other buffers, run by extra workgroups of the same launch
 // when its rows fit (kMaxFusedPredictN), else as its own launch after it on the stream.
 hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,
-                              int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
+                              int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, const int32_t *p_pages, int p_cap,
                               double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
-                              int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m,
+                              int32_t *m_cnt, int32_t *m_pages, int m_cap, float scale, float *acc, float *l, float *m,
                               void *ws, bool mean, const PredictArgs *pred, hipStream_t stream);
 
 // The fused launch for fp8 caches (compiled in its own file; arguments as launch_select_spec).
 hipError_t launch_select_spec_fp8(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,
-                                  int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
+                                  int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, const int32_t *p_pages, int p_cap,
                                   double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
-                                  int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m, void *ws,
+                                  int32_t *m_cnt, int32_t *m_pages, int m_cap, float scale, float *acc, float *l, float *m, void *ws,
                                   bool mean, const PredictArgs *pred, hipStream_t stream);
 
 // The layer step (selection, the speculative pass over P, repair over M) in one launch where the top-K
@@ -173,24 +179,26 @@ hipError_t launch_select_spec_fp8(const KvDesc &kv, const void *q, int hq, const
 size_t layer_step_workspace_bytes(int batch, int hq, int hkv, int d, int block, int p_cap, int m_cap, int nmax,
                                   int topk);
 hipError_t launch_layer_step(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride, int nmax,
-                             int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap, double *scores,
-                             int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx, int32_t *m_cnt, int m_cap,
+                             int topk, const int32_t *p_idx, const int32_t *p_cnt, const int32_t *p_pages, int p_cap, double *scores,
+                             int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx, int32_t *m_cnt, int32_t *m_pages, int m_cap,
                              float scale, float *acc, float *l, float *m, float *out, void *ws, bool mean,
                              const PredictArgs *pred, hipStream_t stream);
 // fp8 caches (compiled in its own file); mws: the M part of the workspace
 hipError_t launch_layer_step_fp8(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,
-                                 int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
+                                 int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, const int32_t *p_pages, int p_cap,
                                  double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
-                                 int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m, float *out,
+                                 int32_t *m_cnt, int32_t *m_pages, int m_cap, float scale, float *acc, float *l, float *m, float *out,
                                  void *ws, void *mws, bool mean, const PredictArgs *pred, hipStream_t stream);
 
 // ws (may be null): rows longer than 2048 blocks are then updated by 512-block parts in parallel and
 // ranked in two stages (predict_workspace_bytes; 0 where one workgroup per unit is used regardless).
 size_t predict_workspace_bytes(int batch, int hkv, int nmax, int budget);
+// p_pages (may be null): P's page work list, written with P through page_table ([batch][max_pages]).
 hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batch, int hkv,
                           int block, int nmax, double alpha, double beta, double gamma, int budget,
                           double *level, double *trend, int32_t *live, int32_t *p_idx,
-                          int32_t *p_cnt, int p_cap, void *ws, hipStream_t stream);
+                          int32_t *p_cnt, int32_t *p_pages, int p_cap, const int32_t *page_table, int max_pages,
+                          void *ws, hipStream_t stream);
 
 // Decode append: token seq_len[b] of every sequence into the cache and its block's metadata, then
 // seq_len[b] += 1.

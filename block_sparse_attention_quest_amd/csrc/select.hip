@@ -293,7 +293,7 @@ hipError_t launch_meta(const KvDesc &kv, int block, int stride, void *meta, bool
 hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *meta, int block,
                          int stride, int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt,
                          int p_cap, double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap,
-                         int32_t *m_idx, int32_t *m_cnt, int m_cap, bool mean, hipStream_t stream) {
+                         int32_t *m_idx, int32_t *m_cnt, int32_t *m_pages, int m_cap, bool mean, hipStream_t stream) {
     const int units = kv.batch * kv.hkv;
     ScoreParams sp;
     sp.q = q;
@@ -328,13 +328,16 @@ hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *me
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_topk(kv, block, nmax, topk, scores, p_idx, p_cnt, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt,
-                       m_cap, stream);
+                       m_pages, m_cap, stream);
 }
 
 hipError_t launch_topk(const KvDesc &kv, int block, int nmax, int topk, const double *scores,
                        const int32_t *p_idx, const int32_t *p_cnt, int p_cap, int32_t *a_idx, int32_t *a_cnt,
-                       int a_cap, int32_t *m_idx, int32_t *m_cnt, int m_cap, hipStream_t stream) {
-    TopkParams tp;
+                       int a_cap, int32_t *m_idx, int32_t *m_cnt, int32_t *m_pages, int m_cap, hipStream_t stream) {
+    TopkParams tp = {};
+    tp.m_pages = m_pages;
+    tp.page_table = kv.page_table;
+    tp.max_pages = kv.max_pages;
     tp.scores = scores;
     tp.seq_len = kv.seq_len;
     tp.p_idx = p_idx;
@@ -354,10 +357,15 @@ hipError_t launch_topk(const KvDesc &kv, int block, int nmax, int topk, const do
 }
 
 hipError_t launch_topk_groups(const KvDesc &kv, int block, int nmax, int topk, const int32_t *p_idx,
-                              const int32_t *p_cnt, int p_cap, int32_t *a_idx, int32_t *a_cnt, int a_cap,
-                              int32_t *m_idx, int32_t *m_cnt, int m_cap, const SelectSpecPlan &plan, int nparts,
-                              void *cand1, void *cand2, uint32_t *arrivals, hipStream_t stream, int32_t *live) {
+                              const int32_t *p_cnt, int p_cap, int32_t *a_idx, int32_t *a_cnt, int32_t *a_pages,
+                              int a_cap, int32_t *m_idx, int32_t *m_cnt, int32_t *m_pages, int m_cap,
+                              const SelectSpecPlan &plan, int nparts, void *cand1, void *cand2, uint32_t *arrivals,
+                              hipStream_t stream, int32_t *live) {
     TopkParams tp = {};
+    tp.a_pages = a_pages;
+    tp.m_pages = m_pages;
+    tp.page_table = kv.page_table;
+    tp.max_pages = kv.max_pages;
     tp.seq_len = kv.seq_len;
     tp.p_idx = p_idx;
     tp.p_cnt = p_cnt;
@@ -445,8 +453,12 @@ size_t predict_workspace_bytes(int batch, int hkv, int nmax, int budget) {
 hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batch, int hkv,
                           int block, int nmax, double alpha, double beta, double gamma, int budget,
                           double *level, double *trend, int32_t *live, int32_t *p_idx,
-                          int32_t *p_cnt, int p_cap, void *ws, hipStream_t stream) {
-    PredictParams p;
+                          int32_t *p_cnt, int32_t *p_pages, int p_cap, const int32_t *page_table, int max_pages,
+                          void *ws, hipStream_t stream) {
+    PredictParams p = {};
+    p.p_pages = p_pages;
+    p.page_table = page_table;
+    p.max_pages = max_pages;
     p.scores = scores;
     p.seq_len = seq_len;
     p.level = level;
@@ -469,6 +481,9 @@ hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batc
     tp.seq_len = seq_len;
     tp.a_idx = p_idx;
     tp.a_cnt = p_cnt;
+    tp.a_pages = p_pages;
+    tp.page_table = page_table;
+    tp.max_pages = max_pages;
     tp.m_idx = nullptr;   // no set difference
     tp.hkv = hkv;
     tp.block = block;
@@ -492,10 +507,12 @@ hipError_t launch_predict(const double *scores, const int32_t *seq_len, int batc
         char *cand2 = cbase + (s1bytes + 255) / 256 * 256;
         KvDesc kv = {};
         kv.seq_len = seq_len;
+        kv.page_table = page_table;
+        kv.max_pages = max_pages;
         kv.batch = batch;
         kv.hkv = hkv;
-        return launch_topk_groups(kv, block, nmax, budget, nullptr, nullptr, 0, p_idx, p_cnt, p_cap, nullptr, nullptr,
-                                  0, pl.groups, pl.nparts, cbase, cand2, arrivals, stream, live);
+        return launch_topk_groups(kv, block, nmax, budget, nullptr, nullptr, 0, p_idx, p_cnt, p_pages, p_cap, nullptr,
+                                  nullptr, nullptr, 0, pl.groups, pl.nparts, cbase, cand2, arrivals, stream, live);
     }
     if (pl.kpt == 4) PRR_LAUNCH(predict_parts_kernel<4>, dim3(grid), dim3(256), stream, p, tp, cp, arrivals, pl.nparts);
     else if (pl.kpt == 8) PRR_LAUNCH(predict_parts_kernel<8>, dim3(grid), dim3(256), stream, p, tp, cp, arrivals, pl.nparts);

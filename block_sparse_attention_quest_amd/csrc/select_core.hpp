@@ -435,6 +435,11 @@ struct TopkParams {
     int32_t *m_idx;
     int32_t *m_cnt;
     int hkv, block, nmax, topk, p_cap, a_cap, m_cap;
+    // page work lists of A and M (each may be null): [units][cap ppb] physical page ids (set_pages)
+    int32_t *a_pages;
+    int32_t *m_pages;
+    const int32_t *page_table;   // [batch][max_pages]
+    int max_pages;
 };
 
 // M's entries and count: device-scope stores when a workgroup of the same launch reads them (COH_M).
@@ -442,6 +447,55 @@ template <bool COH_M>
 __device__ __forceinline__ void st_m(int32_t *ptr, int32_t v) {
     if constexpr (COH_M) st_dev_i32(ptr, v);
     else *ptr = v;
+}
+
+// Page work lists (the physical pages of a set, for the attention passes that read the set): slot
+// e ppb + s of unit u's list holds the physical page of page s of the set's entry e (logical page
+// idx[e] ppb + s), or -1 where that page holds no token yet.  A page is mapped once a token is written to
+// it and keeps its mapping, so a list written for a sequence stays valid while the sequence grows; the
+// readers look up -1 slots whose page has tokens by then.  The entries go through LDS in stages of
+// kPageStage, and the workgroup's threads then fill the slots together, four page-table loads per thread
+// in flight: one memory round trip per 4 TPB slots.
+constexpr int kPageStage = 1024;
+
+// Written by the workgroup that ranked the set: thread t's selected candidates (bits over its KPT
+// candidates, block ids blk) take output positions pos0, pos0 + 1, ... in candidate order; count = the
+// set size (workgroup-uniform).  COH: device-scope stores (a reader in the same launch).
+template <int KPT, int TPB, bool COH>
+__device__ __forceinline__ void write_set_pages(int32_t *list, const int32_t *page_table, int max_pages, int ppb,
+                                                int b, int slen, uint32_t bits, uint32_t pos0,
+                                                const int (&blk)[KPT], int count, int32_t *s_ent) {
+    for (int c0 = 0; c0 < count; c0 += kPageStage) {
+        __syncthreads();   // the stage is free
+        uint32_t pos = pos0;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            if (bits >> j & 1u) {
+                const int r = (int)pos - c0;
+                if (r >= 0 && r < kPageStage) s_ent[r] = blk[j];
+                ++pos;
+            }
+        __syncthreads();
+        const int n = min(count - c0, kPageStage) * ppb;
+        for (int i0 = threadIdx.x; i0 < n; i0 += 4 * TPB) {
+            int32_t ph[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = i0 + r * TPB;
+                ph[r] = -1;
+                if (i < n) {
+                    const int e = i / ppb;
+                    const long lp = (long)s_ent[e] * ppb + (i - e * ppb);
+                    if (lp < max_pages && lp * kPage < slen) ph[r] = page_table[(size_t)b * max_pages + lp];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = i0 + r * TPB;
+                if (i < n) st_m<COH>(&list[(size_t)c0 * ppb + i], ph[r]);
+            }
+        }
+    }
 }
 
 // Top-K of unit u's scores and M = A \ P, by a workgroup of TPB threads holding KPT keys each.
@@ -504,6 +558,19 @@ __device__ __forceinline__ void topk_body(const TopkParams &p, int u) {
     if (threadIdx.x == 0) {
         p.a_cnt[u] = (int32_t)(total & 0xffffu);
         if (want_m) st_m<COH_M>(&p.m_cnt[u], (int32_t)(total >> 16));
+    }
+    if (p.a_pages || (want_m && p.m_pages)) {
+        __shared__ int32_t s_ent[kPageStage];
+        int blk[KPT];
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) blk[j] = base + j;
+        const int ppb = p.block / kPage;
+        if (p.a_pages)
+            write_set_pages<KPT, TPB, false>(p.a_pages + (size_t)u * p.a_cap * ppb, p.page_table, p.max_pages, ppb, b,
+                                             slen, sel, off & 0xffffu, blk, (int)(total & 0xffffu), s_ent);
+        if (want_m && p.m_pages)
+            write_set_pages<KPT, TPB, COH_M>(p.m_pages + (size_t)u * p.m_cap * ppb, p.page_table, p.max_pages, ppb,
+                                             b, slen, inm, off >> 16, blk, (int)(total >> 16), s_ent);
     }
 }
 
@@ -686,6 +753,16 @@ __device__ __forceinline__ void topk_candidates_body(const TopkParams &p, int u,
         p.a_cnt[u] = (int32_t)(total & 0xffffu);
         if (want_m) st_m<COH_M>(&p.m_cnt[u], (int32_t)(total >> 16));
     }
+    if (p.a_pages || (want_m && p.m_pages)) {
+        __shared__ int32_t s_ent[kPageStage];
+        const int ppb = p.block / kPage;
+        if (p.a_pages)
+            write_set_pages<KPT, TPB, false>(p.a_pages + (size_t)u * p.a_cap * ppb, p.page_table, p.max_pages, ppb, b,
+                                             slen, sel, off & 0xffffu, idx, (int)(total & 0xffffu), s_ent);
+        if (want_m && p.m_pages)
+            write_set_pages<KPT, TPB, COH_M>(p.m_pages + (size_t)u * p.m_cap * ppb, p.page_table, p.max_pages, ppb,
+                                             b, slen, inm, off >> 16, idx, (int)(total >> 16), s_ent);
+    }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -702,6 +779,9 @@ struct PredictParams {
     int32_t *p_cnt;
     int hkv, block, nmax, budget, p_cap;
     double alpha, beta, gamma;
+    int32_t *p_pages;            // P's page work list (may be null), as TopkParams' lists
+    const int32_t *page_table;
+    int max_pages;
 };
 
 // EMA update, prediction and top-|P| of unit u, by a workgroup of TPB threads holding KPT keys each.
@@ -767,6 +847,15 @@ __device__ __forceinline__ void predict_body(const PredictParams &p, int u) {
     if (threadIdx.x == 0) {
         p.p_cnt[u] = (int32_t)total;
         p.live[u] = nb;
+    }
+    if (p.p_pages) {
+        __shared__ int32_t s_ent[kPageStage];
+        int blk[KPT];
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) blk[j] = base + j;
+        const int ppb = p.block / kPage;
+        write_set_pages<KPT, TPB, false>(p.p_pages + (size_t)u * p.p_cap * ppb, p.page_table, p.max_pages, ppb, b,
+                                         slen, sel, off, blk, (int)total, s_ent);
     }
 }
 

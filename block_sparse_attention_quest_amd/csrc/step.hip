@@ -88,20 +88,20 @@ size_t select_spec_workspace_bytes(int batch, int hq, int hkv, int d, int block,
 }
 
 hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,
-                              int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
+                              int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, const int32_t *p_pages, int p_cap,
                               double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
-                              int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m,
+                              int32_t *m_cnt, int32_t *m_pages, int m_cap, float scale, float *acc, float *l, float *m,
                               void *ws, bool mean, const PredictArgs *pred, hipStream_t stream) {
     if (kv.fp8)
-        return launch_select_spec_fp8(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_cap, scores,
-                                      a_idx, a_cnt, a_cap, m_idx, m_cnt, m_cap, scale, acc, l, m, ws, mean, pred,
+        return launch_select_spec_fp8(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_pages, p_cap, scores,
+                                      a_idx, a_cnt, a_cap, m_idx, m_cnt, m_pages, m_cap, scale, acc, l, m, ws, mean, pred,
                                       stream);
     if (kv.bf16)
-        return launch_select_spec_t<kKtBf16>(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_cap,
-                                             scores, a_idx, a_cnt, a_cap, m_idx, m_cnt, m_cap, scale, acc, l, m,
+        return launch_select_spec_t<kKtBf16>(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_pages, p_cap,
+                                             scores, a_idx, a_cnt, a_cap, m_idx, m_cnt, m_pages, m_cap, scale, acc, l, m,
                                              ws, mean, pred, stream);
-    return launch_select_spec_t<kKtF32>(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_cap, scores,
-                                        a_idx, a_cnt, a_cap, m_idx, m_cnt, m_cap, scale, acc, l, m, ws, mean,
+    return launch_select_spec_t<kKtF32>(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_pages, p_cap, scores,
+                                        a_idx, a_cnt, a_cap, m_idx, m_cnt, m_pages, m_cap, scale, acc, l, m, ws, mean,
                                         pred, stream);
 }
 

@@ -156,11 +156,11 @@ struct FusedSetup {
 };
 
 inline FusedSetup fused_setup(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride, int nmax,
-                              int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap, double *scores,
-                              int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx, int32_t *m_cnt, int m_cap,
+                              int topk, const int32_t *p_idx, const int32_t *p_cnt, const int32_t *p_pages, int p_cap, double *scores,
+                              int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx, int32_t *m_cnt, int32_t *m_pages, int m_cap,
                               float scale, float *acc, float *l, float *m, float *out, void *ws, bool mean,
                               const PredictArgs *pred) {
-    FusedSetup f;
+    FusedSetup f{};
     // Two workgroups of this kernel fit on a CU.  When the scoring workgroups take more than half of
     // those slots (rows longer than 512 blocks per CU's share, e.g. a cache with room for appended
     // tokens), the speculative pass is spread over the slots that are left, so that the whole grid is
@@ -169,7 +169,7 @@ inline FusedSetup fused_setup(const KvDesc &kv, const void *q, int hq, const voi
     const int bpw = select_spec_score_bpw(mean);
     const int n_score_wgs = (nmax + bpw - 1) / bpw * kv.batch * kv.hkv;
     const int spec_target = n_score_wgs > cus ? std::max(cus / 2, 2 * cus - n_score_wgs) : cus;
-    f.n_spec = attn_setup(f.ap, kv, q, hq, block, p_idx, p_cnt, p_cap, scale, acc, l, m, out, false, ws, spec_target);
+    f.n_spec = attn_setup(f.ap, kv, q, hq, block, p_idx, p_cnt, p_pages, p_cap, scale, acc, l, m, out, false, ws, spec_target);
     ScoreParams &sp = f.sp;
     sp.q = q;
     sp.meta = meta;
@@ -182,6 +182,10 @@ inline FusedSetup fused_setup(const KvDesc &kv, const void *q, int hq, const voi
     sp.stride = stride;
     sp.nmax = nmax;
     TopkParams &tp = f.tp;
+    tp = TopkParams{};
+    tp.m_pages = m_pages;
+    tp.page_table = kv.page_table;
+    tp.max_pages = kv.max_pages;
     tp.scores = scores;
     tp.seq_len = kv.seq_len;
     tp.p_idx = p_idx;
@@ -220,6 +224,9 @@ inline FusedSetup fused_setup(const KvDesc &kv, const void *q, int hq, const voi
         pp.alpha = pred->alpha;
         pp.beta = pred->beta;
         pp.gamma = pred->gamma;
+        pp.p_pages = pred->p_pages;
+        pp.page_table = pred->page_table;
+        pp.max_pages = pred->max_pages;
         f.n_pred = pred->batch * pred->hkv;
     }
     f.grid = (long)f.n_spec + (long)f.nsx * f.units;
@@ -235,19 +242,19 @@ inline FusedSetup fused_setup(const KvDesc &kv, const void *q, int hq, const voi
 
 // The top-K stages that follow a fused launch whose ranking does not finish inside it.
 inline hipError_t fused_after(const FusedSetup &f, const KvDesc &kv, int block, int nmax, int topk, const double *scores,
-                              const int32_t *p_idx, const int32_t *p_cnt, int p_cap, int32_t *a_idx, int32_t *a_cnt,
-                              int a_cap, int32_t *m_idx, int32_t *m_cnt, int m_cap, hipStream_t stream) {
+                              const int32_t *p_idx, const int32_t *p_cnt, const int32_t *p_pages, int p_cap, int32_t *a_idx, int32_t *a_cnt,
+                              int a_cap, int32_t *m_idx, int32_t *m_cnt, int32_t *m_pages, int m_cap, hipStream_t stream) {
     if (f.plan.three) {
         // the parts' candidates are in place; groups of them, then the unit's ranking
         const size_t s1 = (size_t)f.units * f.nsx * f.plan.kl;
         char *cand2 = f.cbase + (s1 * 12 + (size_t)f.units * f.nsx * 4 + 255) / 256 * 256;
         const size_t s2 = (size_t)f.units * f.plan.ng * f.plan.kl2;
         uint32_t *garr = (uint32_t *)(cand2 + (s2 * 12 + (size_t)f.units * f.plan.ng * 4 + 255) / 256 * 256);
-        return launch_topk_groups(kv, block, nmax, topk, p_idx, p_cnt, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt, m_cap,
+        return launch_topk_groups(kv, block, nmax, topk, p_idx, p_cnt, p_cap, a_idx, a_cnt, nullptr, a_cap, m_idx, m_cnt, m_pages, m_cap,
                                   f.plan, f.nsx, f.cbase, cand2, garr, stream);
     }
     if (f.plan.kpt == 0)
-        return launch_topk(kv, block, nmax, topk, scores, p_idx, p_cnt, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt, m_cap,
+        return launch_topk(kv, block, nmax, topk, scores, p_idx, p_cnt, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt, m_pages, m_cap,
                            stream);
     return hipSuccess;
 }
@@ -256,27 +263,27 @@ inline hipError_t predict_alone(const PredictArgs *pred, hipStream_t stream) {
     if (!pred) return hipSuccess;
     return launch_predict(pred->scores, pred->seq_len, pred->batch, pred->hkv, pred->block, pred->nmax, pred->alpha,
                           pred->beta, pred->gamma, pred->budget, pred->level, pred->trend, pred->live, pred->p_idx,
-                          pred->p_cnt, pred->p_cap, pred->ws, stream);
+                          pred->p_cnt, pred->p_pages, pred->p_cap, pred->page_table, pred->max_pages, pred->ws, stream);
 }
 
 // The fused launch for caches of element type KT (bf16 or fp8; an f32 cache runs the passes in turn).
 template <int KT>
 hipError_t launch_select_spec_t(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,
-                              int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
+                              int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, const int32_t *p_pages, int p_cap,
                               double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
-                              int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m,
+                              int32_t *m_cnt, int32_t *m_pages, int m_cap, float scale, float *acc, float *l, float *m,
                               void *ws, bool mean, const PredictArgs *pred, hipStream_t stream) {
     if constexpr (KT == kKtF32) {
         // fp32 caches (exact-input checks): the passes one after the other
         hipError_t e = launch_select(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_cap, scores,
-                                     a_idx, a_cnt, a_cap, m_idx, m_cnt, m_cap, mean, stream);
+                                     a_idx, a_cnt, a_cap, m_idx, m_cnt, m_pages, m_cap, mean, stream);
         if (e != hipSuccess) return e;
-        e = launch_attn(kv, q, hq, block, p_idx, p_cnt, p_cap, scale, acc, l, m, nullptr, false, ws, stream);
+        e = launch_attn(kv, q, hq, block, p_idx, p_cnt, p_pages, p_cap, scale, acc, l, m, nullptr, false, ws, stream);
         if (e != hipSuccess) return e;
         return predict_alone(pred, stream);
     } else {
-    const FusedSetup f = fused_setup(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_cap, scores, a_idx,
-                                     a_cnt, a_cap, m_idx, m_cnt, m_cap, scale, acc, l, m, nullptr, ws, mean, pred);
+    const FusedSetup f = fused_setup(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_pages, p_cap, scores, a_idx,
+                                     a_cnt, a_cap, m_idx, m_cnt, m_pages, m_cap, scale, acc, l, m, nullptr, ws, mean, pred);
     if (f.grid > 0x7fffffffL) return hipErrorInvalidValue;
     const int kpt = f.plan.kpt;
     const bool two = f.plan.two;
@@ -298,8 +305,8 @@ hipError_t launch_select_spec_t(const KvDesc &kv, const void *q, int hq, const v
 #undef PRR_SS_ALL
 #undef PRR_SS_K
 #undef PRR_SS
-    hipError_t e = fused_after(f, kv, block, nmax, topk, scores, p_idx, p_cnt, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt,
-                               m_cap, stream);
+    hipError_t e = fused_after(f, kv, block, nmax, topk, scores, p_idx, p_cnt, p_pages, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt,
+                               m_pages, m_cap, stream);
     if (e != hipSuccess) return e;
     return f.fuse_pred ? hipSuccess : predict_alone(pred, stream);
     }
@@ -318,9 +325,9 @@ inline size_t layer_extra_m_ws(int batch, int hq, int hkv, int d, int block, int
 // part of the workspace (layer_extra_m_ws bytes, then the flags).
 template <int KT>
 hipError_t launch_layer_step_t(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,
-                               int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
+                               int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, const int32_t *p_pages, int p_cap,
                                double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
-                               int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m, float *out,
+                               int32_t *m_cnt, int32_t *m_pages, int m_cap, float scale, float *acc, float *l, float *m, float *out,
                                void *ws, void *mws, bool mean, const PredictArgs *pred, hipStream_t stream) {
     const int units = kv.batch * kv.hkv;
     const size_t mbytes = layer_extra_m_ws(kv.batch, hq, kv.hkv, kv.d, block, m_cap);
@@ -328,16 +335,16 @@ hipError_t launch_layer_step_t(const KvDesc &kv, const void *q, int hq, const vo
     uint32_t *status = (uint32_t *)((char *)mws + mbytes + ((size_t)units * 4 + 255) / 256 * 256);
     const SelectSpecPlan plan = select_spec_plan(nmax, topk, mean);
     if (KT == kKtF32 || plan.three || plan.kpt == 0) {
-        hipError_t e = launch_select_spec(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_cap, scores,
-                                          a_idx, a_cnt, a_cap, m_idx, m_cnt, m_cap, scale, acc, l, m, ws, mean, pred,
+        hipError_t e = launch_select_spec(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_pages, p_cap, scores,
+                                          a_idx, a_cnt, a_cap, m_idx, m_cnt, m_pages, m_cap, scale, acc, l, m, ws, mean, pred,
                                           stream);
         if (e != hipSuccess) return e;
-        return launch_attn(kv, q, hq, block, m_idx, m_cnt, m_cap, scale, acc, l, m, out, true, mws, stream);
+        return launch_attn(kv, q, hq, block, m_idx, m_cnt, m_pages, m_cap, scale, acc, l, m, out, true, mws, stream);
     } else {
-    const FusedSetup f = fused_setup(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_cap, scores, a_idx,
-                                     a_cnt, a_cap, m_idx, m_cnt, m_cap, scale, acc, l, m, out, ws, mean, pred);
+    const FusedSetup f = fused_setup(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_pages, p_cap, scores, a_idx,
+                                     a_cnt, a_cap, m_idx, m_cnt, m_pages, m_cap, scale, acc, l, m, out, ws, mean, pred);
     FusedParams fp{};
-    attn_setup(fp.pm, kv, q, hq, block, m_idx, m_cnt, m_cap, scale, acc, l, m, out, true, mws);
+    attn_setup(fp.pm, kv, q, hq, block, m_idx, m_cnt, m_pages, m_cap, scale, acc, l, m, out, true, mws);
     // M's chunks at half prr_repair's size (at least kChunkMin pages, the size the workspace's partial
     // slots are counted at): the repair slots start only once their unit's top-K is done, late in the
     // launch, so more and shorter chunks finish sooner

@@ -6,12 +6,12 @@
 namespace prr {
 
 hipError_t launch_layer_step_fp8(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,
-                                 int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, int p_cap,
+                                 int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt, const int32_t *p_pages, int p_cap,
                                  double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx,
-                                 int32_t *m_cnt, int m_cap, float scale, float *acc, float *l, float *m, float *out,
+                                 int32_t *m_cnt, int32_t *m_pages, int m_cap, float scale, float *acc, float *l, float *m, float *out,
                                  void *ws, void *mws, bool mean, const PredictArgs *pred, hipStream_t stream) {
-    return launch_layer_step_t<kKtFp8>(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_cap, scores, a_idx,
-                                       a_cnt, a_cap, m_idx, m_cnt, m_cap, scale, acc, l, m, out, ws, mws, mean, pred,
+    return launch_layer_step_t<kKtFp8>(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_pages, p_cap, scores, a_idx,
+                                       a_cnt, a_cap, m_idx, m_cnt, m_pages, m_cap, scale, acc, l, m, out, ws, mws, mean, pred,
                                        stream);
 }
 

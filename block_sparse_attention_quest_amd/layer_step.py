@@ -85,7 +85,7 @@ class PRRLayer:
 
     def __init__(self, kv: bd.KVCache, num_q_heads: int, block: int, topk: int, budget: int,
                  ema=(0.6, 0.3, 0.5), scale: Optional[float] = None, score_mode: str = "quest",
-                 max_budget: Optional[int] = None, fused: bool = True):
+                 max_budget: Optional[int] = None, fused: bool = True, page_lists: bool = True):
         dev = kv.k.device
         # |P| may later change (set_budget) up to max_budget: sets and workspaces are sized for it
         self.max_budget = max(1, budget, max_budget or 0)
@@ -106,10 +106,13 @@ class PRRLayer:
         self.level = torch.zeros_like(self.scores)
         self.trend = torch.zeros_like(self.scores)
         self.live = torch.zeros((B, H), dtype=torch.int32, device=dev)
-        self.P = [bd.BlockSet.empty(B, H, self.max_budget, dev), bd.BlockSet.empty(B, H, self.max_budget, dev)]
+        # P (double-buffered) and M carry page work lists: the predictor writes P's physical pages a step
+        # ahead and the top-K writes M's, so the speculative pass and repair start on K/V loads
+        lb = block if page_lists else 0
+        self.P = [bd.BlockSet.empty(B, H, self.max_budget, dev, lb), bd.BlockSet.empty(B, H, self.max_budget, dev, lb)]
         self.cur = 0
         self.A = bd.BlockSet.empty(B, H, max(1, topk), dev)
-        self.M = bd.BlockSet.empty(B, H, max(1, topk), dev)
+        self.M = bd.BlockSet.empty(B, H, max(1, topk), dev, lb)
         self.state = bd.AttnState.empty(B, num_q_heads, d, dev)
         self.out = torch.zeros((B, num_q_heads, d), dtype=torch.float32, device=dev)
         self.ws_spec = bd.select_spec_workspace_for(kv, num_q_heads, block, topk, self.max_budget)
@@ -189,7 +192,7 @@ class PRRLayer:
         if timers and timers.repair_end:
             timers.repair_end.record(s)
         args = bd.PredictArgs(self.scores, self.kv.seq_len, self.block, self.alpha, self.beta, self.gamma,
-                              self.budget, self.level, self.trend, self.live, Pn, self.ws_predict)
+                              self.budget, self.level, self.trend, self.live, Pn, self.ws_predict, self.kv)
         if defer_predict:
             self.pending_predict = args
         else:
@@ -238,7 +241,7 @@ class PRRLayer:
         e_spec.record(side)
         aux.wait_event(e_sel)
         bd.predict(self.scores, self.kv.seq_len, self.block, self.alpha, self.beta, self.gamma, self.budget,
-                   self.level, self.trend, self.live, P_next=Pn, ws=self.ws_predict, stream=aux)
+                   self.level, self.trend, self.live, P_next=Pn, ws=self.ws_predict, stream=aux, kv=self.kv)
         e_pred.record(aux)
         crit.wait_event(e_spec)
         if timers and timers.repair_start:
@@ -254,7 +257,7 @@ class PRRLayer:
 def run_predict(args: bd.PredictArgs, stream=None):
     """Enqueue a predictor step on its own."""
     bd.predict(args.scores, args.seq_len, args.block, args.alpha, args.beta, args.gamma, args.budget, args.level,
-               args.trend, args.live, P_next=args.P_next, ws=args.ws, stream=stream)
+               args.trend, args.live, P_next=args.P_next, ws=args.ws, stream=stream, kv=args.kv)
 
 
 class PRRStack:

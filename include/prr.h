@@ -84,11 +84,27 @@ typedef struct prr_kv_cache {
     prr_dtype dtype;
 } prr_kv_cache;
 
-/* A block set per (sequence, kv head): idx [batch][num_kv_heads][cap], count [batch][num_kv_heads]. */
+/* A block set per (sequence, kv head): idx [batch][num_kv_heads][cap], count [batch][num_kv_heads].
+ *
+ * pages (device, may be NULL): the set's page work list, the flat (unit, page) items the attention
+ * passes walk ([paper] §4.3: the repair kernel reads the missed tiles; the survey's M work list), laid out
+ * [batch][num_kv_heads][cap * (block / page_size)] for the block size of the calls that write and read it.
+ * Slot e * (block / page_size) + s of a unit holds the physical page (through the cache's page table) of
+ * page s of block idx[e], for e < count, or -1 where that page held no token when the list was written.
+ * Writers: prr_select, prr_select_spec(_predict) and prr_layer_step write M's list with M; prr_predict and a
+ * carried predictor write P_next's with P_next; A's list is not written.  Readers: the speculative pass
+ * (prr_spec_attn(_noalloc), prr_select_spec(_predict), prr_layer_step) reads P's list, repair (prr_repair,
+ * prr_layer_step) reads M's: the K/V tile loads then start in the round trip that reads the set, instead
+ * of waiting for a page-table lookup.  A -1 slot whose page holds tokens by the time of the read is looked
+ * up in the page table then.  A list stays valid while every page that held a token when it was written
+ * keeps its physical page (an append-only paged cache: a page is mapped when its first token is written
+ * and keeps its mapping); results are the same with and without a list.  A NULL list: the readers look
+ * every page up. */
 typedef struct prr_block_set {
     int32_t *idx;    /* device */
     int32_t *count;  /* device */
     int32_t cap;
+    int32_t *pages;  /* device, may be NULL: the page work list above */
 } prr_block_set;
 
 /* Partial attention state per query head ([paper] §4.3, the speculative kernel's extra outputs):
@@ -210,10 +226,13 @@ prr_status prr_select_spec(const void *q, int32_t num_q_heads, const prr_kv_cach
  * monotone in the budget, so a workspace for several budgets takes the largest of their queries. */
 size_t prr_predict_workspace_bytes(int32_t batch, int32_t num_kv_heads, int32_t max_blocks, int32_t budget);
 
+/* kv (may be NULL unless P_next->pages is set): the cache whose page table P_next's page list maps
+ * through (same batch, num_kv_heads and block; its seq_len should be `seq_len`). */
 prr_status prr_predict(const double *scores, const int32_t *seq_len, int32_t batch,
                        int32_t num_kv_heads, int32_t block, int32_t max_blocks, double alpha,
                        double beta, double gamma, int32_t budget, double *level, double *trend,
-                       int32_t *live, prr_block_set *P_next, void *ws, size_t ws_bytes, hipStream_t stream);
+                       int32_t *live, prr_block_set *P_next, const prr_kv_cache *kv, void *ws, size_t ws_bytes,
+                       hipStream_t stream);
 
 /* The arguments of prr_predict, for prr_select_spec_predict. */
 typedef struct prr_predict_args {
@@ -231,6 +250,7 @@ typedef struct prr_predict_args {
     prr_block_set *P_next;
     void *ws;          /* as prr_predict's (may be NULL) */
     size_t ws_bytes;
+    const prr_kv_cache *kv;   /* as prr_predict's (may be NULL unless P_next->pages is set) */
 } prr_predict_args;
 
 /* prr_select_spec, plus (pred non-NULL) the predictor step prr_predict would run on *pred, typically

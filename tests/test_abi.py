@@ -109,10 +109,19 @@ def test_select_and_predict_argument_errors(lib):
     assert sel(M=None) == 1                       # P without M
     assert sel(M=_set(10)) == 1
     assert sel(kv=_kv(max_pages=65536), block=16) == 2   # more than 32768 blocks per sequence
-    pred = lambda budget=64, nmax=2048, P=P, ws=None, wsb=0: lib.prr_predict(
-        1, 1, 2, 8, 64, nmax, 0.6, 0.3, 0.5, budget, 1, 1, 1, ctypes.byref(P) if P else None, ws, wsb, None)
+    pred = lambda budget=64, nmax=2048, P=P, ws=None, wsb=0, kv=None: lib.prr_predict(
+        1, 1, 2, 8, 64, nmax, 0.6, 0.3, 0.5, budget, 1, 1, 1, ctypes.byref(P) if P else None,
+        ctypes.byref(kv) if kv else None, ws, wsb, None)
     assert pred(budget=65) == 1
     assert pred(P=None) == 1
+    # a page work list for P_next needs the cache it maps through, with the predictor's sequences and a
+    # block size that divides into pages
+    Pl = bd.BlockSetStruct(1, 1, 64, 1)
+    assert pred(P=Pl) == 1                                    # no cache
+    assert pred(P=Pl, kv=_kv(batch=3)) == 1                   # other sequences
+    assert pred(P=Pl, kv=_kv(num_kv_heads=4)) == 1
+    assert pred(P=Pl, kv=_kv(page_size=32)) == 2              # unsupported page size
+    assert pred(P=Pl, kv=_kv(k=None)) == 1
     # long rows: parts of 512 blocks, min(budget, 512) candidates each, plus counters
     need = lib.prr_predict_workspace_bytes(2, 8, 8192, 64)
     assert need == 256 + 16 * 16 * 64 * 12 + 16 * 16 * 4
