@@ -101,6 +101,26 @@ def kv_bytes_per_block(w) -> int:
     return w.block * w.kv_bytes_per_token()
 
 
+def algorithmic_bytes(w, score_mode: str, spec_bytes, rep_bytes) -> dict:
+    """Algorithmic HBM bytes per launch of each kernel of the path (medians over the timed steps where
+    they depend on the sets), for the HBM-counter summaries' traffic ratios:
+      spec / repair: the K/V of the set's blocks (block x 2 x d x element bytes per block);
+      score: the metadata scoring reads, d elements per block (the one row, min or max, that the sign of
+             qbar_i picks per channel; the fp32 mean for mean-pooled scoring), plus the 8-byte score written;
+      topk: the 8-byte scores read; predict: scores, level and trend read and level and trend written
+             (8 bytes each);
+      select_spec = score + spec; layer_step = score + spec + repair.
+    Sets, lengths and queries (a few KiB) are left out."""
+    import numpy as np
+
+    blocks = sum(w.blocks_of(b) for b in range(w.batch)) * w.num_kv_heads
+    elem = 4 if (score_mode == "mean" or w.dtype == "f32") else 2
+    score = blocks * (w.head_dim * elem + 8)
+    spec, rep = float(np.median(spec_bytes)), float(np.median(rep_bytes))
+    return {"spec": spec, "repair": rep, "score": float(score), "topk": float(blocks * 8),
+            "predict": float(blocks * 40), "select_spec": score + spec, "layer_step": score + spec + rep}
+
+
 def load_profile_value(path: str, kernel_hash: str, key: str):
     """A "- key: value" line of a committed profile summary, or None when the file is absent, lacks the
     key or was taken on a different attention kernel source."""
@@ -860,6 +880,7 @@ def main():
     spec_gbps = float(spec_bytes.sum() / (sum(spec_us) * 1e-6) / 1e9)
     rep_gbps = float(rep_bytes.sum() / (sum(rep_us) * 1e-6) / 1e9)
     step_gbps = [(sb + rb) / ((a + b) * 1e-6) / 1e9 for sb, rb, a, b in zip(spec_bytes, rep_bytes, spec_us, rep_us)]
+    algo_bytes = algorithmic_bytes(w, args.score_mode, spec_bytes, rep_bytes)
 
     A_all = a_sets.cpu().numpy()
     P_all = p_sets.cpu().numpy()
@@ -941,6 +962,7 @@ def main():
         "in_layer_step": {"us_select_spec_median": med(ss_ov_us), "us_repair_median": med(rep_ov_us),
                           "us_predict_median": med(pred_ov_us), "us_to_repair_end_median": med(step_tm_us),
                           "note": "one stream with an event after each call (the events add their own cost)"},
+        "algorithmic_bytes_per_launch": {k: round(v) for k, v in algo_bytes.items()},
         "spec_attn_gbps": round(spec_gbps, 1),
         "repair_gbps": round(rep_gbps, 1),
         "mean_missed_blocks_per_unit": round(float(mc.mean()), 2),

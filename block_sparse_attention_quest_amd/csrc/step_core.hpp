@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
                 // M's device-scope stores are complete before the unit's repair slots may read it
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
-                if (threadIdx.x == 0) __hip_atomic_store(&fp.ready[u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (threadIdx.x == 0) __hip_atomic_store(&fp.ready[u * kReadyStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
@@ -332,7 +332,7 @@ hipError_t launch_layer_step_t(const KvDesc &kv, const void *q, int hq, const vo
     const int units = kv.batch * kv.hkv;
     const size_t mbytes = layer_extra_m_ws(kv.batch, hq, kv.hkv, kv.d, block, m_cap);
     uint32_t *ready = (uint32_t *)((char *)mws + mbytes);
-    uint32_t *status = (uint32_t *)((char *)mws + mbytes + ((size_t)units * 4 + 255) / 256 * 256);
+    uint32_t *status = (uint32_t *)((char *)mws + mbytes + (size_t)units * 4 * kReadyStride);
     const SelectSpecPlan plan = select_spec_plan(nmax, topk, mean);
     if (KT == kKtF32 || plan.three || plan.kpt == 0) {
         hipError_t e = launch_select_spec(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_pages, p_cap, scores,

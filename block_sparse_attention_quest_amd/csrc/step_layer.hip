@@ -10,7 +10,7 @@ size_t layer_step_workspace_bytes(int batch, int hq, int hkv, int d, int block, 
                                   int topk) {
     const size_t units = (size_t)batch * hkv;
     return select_spec_workspace_bytes(batch, hq, hkv, d, block, p_cap, nmax, topk) +
-           layer_extra_m_ws(batch, hq, hkv, d, block, m_cap) + (units * 4 + 255) / 256 * 256 + 256;
+           layer_extra_m_ws(batch, hq, hkv, d, block, m_cap) + units * 4 * kReadyStride + 256;
 }
 
 hipError_t launch_layer_step(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride, int nmax,

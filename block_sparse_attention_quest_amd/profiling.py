@@ -36,10 +36,10 @@ def kernel_source_hash() -> str:
 
 
 def _short(name: str) -> str:
-    n = name.split("(")[0]
+    n = name
     for pre in ("void ", "prr::(anonymous namespace)::"):
         n = n.replace(pre, "")
-    return n[:70]
+    return n.split("(")[0][:70]
 
 
 def _get(row: dict, *keys, default=""):
@@ -60,7 +60,7 @@ def stats_table(path: str, top: int = 16) -> str:
     return "\n".join(out)
 
 
-def trace_averages(path: str, names=("attn_spec_bf16", "attn_repair_bf16", "select_spec_kernel")) -> str:
+def trace_averages(path: str, names=("spec", "repair", "select_spec", "layer_step")) -> str:
     """Average and median duration of each named kernel per stream over its launches that did work:
     launches shorter than a fifth of the kernel's longest (calls over empty sets) are left out; the
     warm-up steps' launches, which run slower, stay in (the median is the figure to compare with a
@@ -69,10 +69,10 @@ def trace_averages(path: str, names=("attn_spec_bf16", "attn_repair_bf16", "sele
     other carries the overlapped layer step's speculative pass."""
     rows = list(csv.DictReader(open(path)))
     flush_streams = {r["Stream_Id"] for r in rows if "reduce_kernel" in r["Kernel_Name"]}
-    out = ["| kernel | stream | launches with work | avg us | median us | min us | max us |",
+    out = ["| kernel (role) | stream | launches with work | avg us | median us | min us | max us |",
            "|---|---|---|---|---|---|---|"]
     for nm in names:
-        sel = [r for r in rows if nm in r["Kernel_Name"]]
+        sel = [r for r in rows if kernel_role(r["Kernel_Name"]) == nm]
         if not sel:
             continue
         dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
@@ -82,7 +82,7 @@ def trace_averages(path: str, names=("attn_spec_bf16", "attn_repair_bf16", "sele
             if not ds:
                 continue
             kind = "flush stream (isolated launches + critical path)" if sid in flush_streams else "side stream"
-            out.append(f"| `{nm}` | {sid}: {kind} | {len(ds)} | {statistics.mean(ds):.2f} | "
+            out.append(f"| {nm} | {sid}: {kind} | {len(ds)} | {statistics.mean(ds):.2f} | "
                        f"{statistics.median(ds):.2f} | {min(ds):.2f} | {max(ds):.2f} |")
     return "\n".join(out)
 
@@ -167,9 +167,58 @@ def hbm_summary(fetch_csv: str, write_csv: str, copy_mib: int, kernel: str = Non
             "hbm_bytes_per_launch": statistics.median(per_launch)}
 
 
-# Other kernels reported beside the speculative pass: name, algorithmic bytes per launch at the
-# 128K batch-8 workload (None where it depends on the step's sets).
-OTHER_KERNELS = (("attn_repair_bf16", None), ("select_spec_kernel", None), ("score_kernel", None))
+def kernel_role(name: str):
+    """The role of a kernel of the path, by its (demangled) name: the keys of bench.py's
+    algorithmic_bytes_per_launch, plus the calibration, metadata and top-K stage kernels."""
+    if "attn_spec_" in name:
+        return "spec"
+    if "attn_repair_" in name:
+        return "repair"
+    if "select_spec_kernel" in name:
+        # template arguments <cache type, d, keys per thread, two-stage, mean, carried predictor, repair>
+        targs = name[name.index("<") + 1:].split(">")[0].split(",") if "<" in name else []
+        return "layer_step" if len(targs) >= 7 and targs[6].strip() == "true" else "select_spec"
+    # calibration first: its per-row ranking kernel is also a top-K kernel
+    for key, role in (("rows_topk_kernel", "calibration: rows' true top-K"), ("ema_chain_kernel", "calibration: EMA chain"),
+                      ("replay_kernel", "calibration: replay"), ("score_kernel", "score"),
+                      ("topk_groups_kernel", "topk_groups"), ("topk_kernel", "topk"), ("predict", "predict"),
+                      ("meta_kernel", "meta"), ("append", "append")):
+        if key in name:
+            return role
+    return None
+
+
+def roles_table(fetch_csv: str, write_csv: str, copy_mib: int, algo: dict = None) -> list:
+    """Per role: dispatches that did work, median HBM bytes per launch (FETCH_SIZE and WRITE_SIZE scaled
+    by the copy probe), and with bench.py's algorithmic bytes per launch the ratio of the two."""
+    fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _per_dispatch(write_csv, "WRITE_SIZE")
+    copies = [(v, d) for d, (n, v) in write.items() if "copyBuffer" in n]
+    if not copies:
+        raise SystemExit("no copy dispatch found in the WRITE_SIZE run")
+    copy_write, copy_id = max(copies)
+    f_scale = copy_mib * 1024.0 / fetch[copy_id][1]
+    w_scale = copy_mib * 1024.0 / copy_write
+    by_role = {}
+    for d, (n, f) in fetch.items():
+        role = kernel_role(n)
+        if role and d in write:
+            by_role.setdefault(role, []).append((f * f_scale + write[d][1] * w_scale) * 1024.0)
+    out = ["| kernel (role) | dispatches | HBM bytes per launch, median | algorithmic bytes per launch | "
+           "HBM / algorithmic |", "|---|---|---|---|---|"]
+    for role in ("spec", "repair", "select_spec", "layer_step", "score", "topk", "topk_groups", "predict",
+                 "calibration: rows' true top-K", "calibration: EMA chain", "calibration: replay", "meta", "append"):
+        xs = by_role.get(role)
+        if not xs:
+            continue
+        top = max(xs)
+        xs = [x for x in xs if x >= 0.1 * top]   # launches over empty sets (warm-up, first step) left out
+        med = statistics.median(xs)
+        a = (algo or {}).get(role)
+        ratio = f"{med / a:.3f}" if a else "-"
+        out.append(f"| {role} | {len(xs)} | {med:.0f} | {a:.0f} | {ratio} |" if a else
+                   f"| {role} | {len(xs)} | {med:.0f} | - | - |")
+    return out
 
 
 def main(argv):
@@ -201,27 +250,32 @@ def main(argv):
         i = argv.index("--copy-mib")
         copy_mib = int(argv[i + 1])
         cmds = [a for k, a in enumerate(argv[4:], start=4) if k not in (i, i + 1)]
+        d = None
+        if "--bench-log" in argv:
+            j = argv.index("--bench-log")
+            d = bench_line(argv[j + 1])
+            cmds = [a for a in cmds if a not in (argv[j], argv[j + 1])]
         s = hbm_summary(fetch_csv, write_csv, copy_mib)
-        lines = ["# HBM traffic of the speculative-attention kernel (rocprofv3 --pmc)", "",
+        title = "the path's kernels" if s is None else "the speculative-attention kernel and the path's kernels"
+        workload = f" ({d['config']['workload']})" if d else ""
+        lines = [f"# HBM traffic of {title}{workload} (rocprofv3 --pmc)", "",
                  "FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by what it reads for a "
                  f"{copy_mib} MiB device copy (known bytes read and written) in the same run.", "",
-                 "Commands:", "", "```", *cmds, "```", "",
-                 f"- kernel: `{SPEC_KERNEL}<128>`",
-                 f"- kernel_source_sha256: `{kernel_source_hash()}`",
-                 f"- spec_dispatches: {s['spec_dispatches']}",
-                 f"- fetch_kib_per_dispatch_median: {s['fetch_kib_mean']:.1f}",
-                 f"- write_kib_per_dispatch_median: {s['write_kib_mean']:.1f}",
-                 f"- copy_fetch_kib: {s['copy_fetch_kib']:.1f}",
-                 f"- copy_write_kib: {s['copy_write_kib']:.1f}",
-                 f"- fetch_scale: {s['fetch_scale']:.4f}",
-                 f"- write_scale: {s['write_scale']:.4f}",
-                 f"- hbm_bytes_per_launch: {s['hbm_bytes_per_launch']:.0f}", "",
-                 "Other kernels of the same runs (same scaling; launches that did work):", "",
-                 "| kernel | dispatches | HBM bytes per launch, median (read + write) |", "|---|---|---|"]
-        for name, _ in OTHER_KERNELS:
-            o = hbm_summary(fetch_csv, write_csv, copy_mib, name)
-            if o:
-                lines.append(f"| `{name}` | {o['spec_dispatches']} | {o['hbm_bytes_per_launch']:.0f} |")
+                 "Commands:", "", "```", *cmds, "```", ""]
+        if s is not None:
+            lines += [f"- kernel: `{SPEC_KERNEL}<128>`",
+                      f"- kernel_source_sha256: `{kernel_source_hash()}`",
+                      f"- spec_dispatches: {s['spec_dispatches']}",
+                      f"- fetch_kib_per_dispatch_median: {s['fetch_kib_mean']:.1f}",
+                      f"- write_kib_per_dispatch_median: {s['write_kib_mean']:.1f}",
+                      f"- copy_fetch_kib: {s['copy_fetch_kib']:.1f}",
+                      f"- copy_write_kib: {s['copy_write_kib']:.1f}",
+                      f"- fetch_scale: {s['fetch_scale']:.4f}",
+                      f"- write_scale: {s['write_scale']:.4f}",
+                      f"- hbm_bytes_per_launch: {s['hbm_bytes_per_launch']:.0f}", ""]
+        lines += ["Every kernel of the path in the same runs (same scaling; launches that did work; algorithmic "
+                  "bytes from bench.py's algorithmic_bytes_per_launch of the run):", ""]
+        lines += roles_table(fetch_csv, write_csv, copy_mib, d.get("algorithmic_bytes_per_launch") if d else None)
         lines.append("")
         open(out, "w").write("\n".join(lines))
         print("\n".join(lines))

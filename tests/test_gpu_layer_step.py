@@ -39,13 +39,13 @@ def oracle_view(inp):
 
 def status_word(kv, hq, block, topk, p_cap, m_cap, ws):
     """The layer-step workspace's status word (after the select_spec workspace, M's attention workspace
-    and the per-unit M flags)."""
+    and the per-unit M flags, one per 256 bytes)."""
     lib = bd.load_library()
     s = kv.struct()
     import ctypes
     off = lib.prr_select_spec_workspace_bytes(ctypes.byref(s), hq, block, topk, p_cap)
     off += lib.prr_attn_workspace_bytes(kv.batch, hq, kv.num_kv_heads, kv.head_dim, block, m_cap)
-    off += (kv.batch * kv.num_kv_heads * 4 + 255) // 256 * 256
+    off += kv.batch * kv.num_kv_heads * 256   # one M flag per 256 bytes
     return int(ws.buf[off:off + 4].view(torch.int32).item())
 
 
