@@ -117,27 +117,40 @@ __device__ __forceinline__ uint32_t dpp_or63(uint32_t x) {
     return x;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: row shifts by 1, 2, 4 and 8 scan each
+// 16-lane row, then the row-15 broadcast adds row 0's total to row 1 and row 2's to row 3, and the row-31
+// broadcast adds the total of rows 0 and 1 to rows 2 and 3.
+__device__ __forceinline__ uint32_t dpp_incl_scan(uint32_t x) {
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);  // row_bcast15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);  // row_bcast31 into rows 2, 3
+    return x;
+}
+
 // Exclusive prefix sum over the workgroup (W waves) in thread order; `total` gets the sum.  `buf` selects
 // one of two LDS slots so back-to-back scans need a single barrier each.  A one-wave workgroup scans in
 // registers only.
 template <int W>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, TopkSmem<W> &sm, int buf, uint32_t &total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t v = x;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(v, o);
-        if (lane >= o) v += y;
-    }
+    const uint32_t v = dpp_incl_scan(x);
     if constexpr (W == 1) {
-        total = __shfl(v, 63);
+        total = __builtin_amdgcn_readlane(v, 63);
         return v - x;
     } else {
         if (lane == 63) sm.scan[buf][wave] = v;
         __syncthreads();
-        const uint32_t wt = lane < W ? sm.scan[buf][lane] : 0u;
-        const uint32_t before = wave_sum(lane < wave ? wt : 0u);
-        total = wave_sum(wt);
+        uint32_t before = 0, tot = 0;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const uint32_t sw = sm.scan[buf][w];
+            tot += sw;
+            before += w < wave ? sw : 0u;
+        }
+        total = tot;
         return before + v - x;
     }
 }
