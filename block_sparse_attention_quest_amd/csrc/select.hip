@@ -6,6 +6,8 @@
 //   [paper] "Predict, Reuse, and Repair: Accelerating Dynamic Sparse Attention for Long-Context LLM
 //           Decoding" (full paper text)
 
+#include <type_traits>
+
 #include "select_core.hpp"
 #include "kv_types.hpp"
 
@@ -25,26 +27,26 @@ struct MetaParams {
 };
 
 // 16 bytes of K at element offset off: the channels they hold as floats (4 for f32, 8 for bf16, 16
-// for fp8), exactly.
+// for fp8), exactly.  The load and the widening are separate steps so that a kernel can issue a run of
+// loads before it widens any of them.
 template <int KT>
 constexpr int kElemsPer16B = KT == kKtF32 ? 4 : KT == kKtBf16 ? 8 : 16;
 
 template <int KT>
-__device__ __forceinline__ void load16_as_f32(const void *k, size_t off, float (&x)[kElemsPer16B<KT>]) {
+__device__ __forceinline__ uint4 load16_raw(const void *k, size_t off) {
+    return *(const uint4 *)((const uint8_t *)k + off * (16 / kElemsPer16B<KT>));
+}
+
+template <int KT>
+__device__ __forceinline__ void widen16(const uint4 raw, float (&x)[kElemsPer16B<KT>]) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
     if constexpr (KT == kKtF32) {
-        const float4 raw = *(const float4 *)((const float *)k + off);
-        x[0] = raw.x;
-        x[1] = raw.y;
-        x[2] = raw.z;
-        x[3] = raw.w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(w[e]);
     } else if constexpr (KT == kKtBf16) {
-        const uint4 raw = *(const uint4 *)((const uint16_t *)k + off);
-        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = bf16_to_f32((uint16_t)(w[e >> 1] >> (16 * (e & 1))));
     } else {
-        const uint4 raw = *(const uint4 *)((const uint8_t *)k + off);
-        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             float f[4];
@@ -55,91 +57,112 @@ __device__ __forceinline__ void load16_as_f32(const void *k, size_t off, float (
     }
 }
 
-// Quest min/max metadata, [B][Hkv][d][2][stride]: fp32 for an f32 cache, bf16 otherwise (an fp8 key is a
-// bf16 value, so its min and max are too).  Lane = block (64 per workgroup), waves take channel groups.
-template <int KT, int D>
-__global__ __launch_bounds__(256) void meta_kernel(MetaParams p) {
+// Block summaries of the K cache, written once at prefill.
+//  - Quest min/max metadata (MEAN = false): [B][Hkv][d][2][stride], the channel-wise minimum and maximum
+//    key of every block; fp32 for an f32 cache, bf16 otherwise (an fp8 key is a bf16 value, so its min
+//    and max are too).
+//  - Mean-pooled summary (MEAN = true): [B][Hkv][d][stride] fp32, the channel-wise mean key of every
+//    block over its valid tokens, summed in float64 in token order, divided by the token count and
+//    rounded once to float32.
+// A workgroup covers 64 consecutive blocks of one (sequence, kv head).  A group of G = d / EPL lanes reads
+// one token row of one block per 16-byte-per-lane load (each lane holds EPL channels), so a wave walks
+// 64 / G blocks at once, each lane through its block's tokens in order, with a whole page's loads in
+// flight and the next page's id fetched ahead of them.  The summaries go to LDS and the workgroup writes
+// each output row of its 64 blocks as one contiguous run.
+template <int KT>
+using MetaElem = typename std::conditional<KT == kKtF32, float, uint16_t>::type;
+
+template <int KT>
+__device__ __forceinline__ MetaElem<KT> meta_value(float x) {
+    if constexpr (KT == kKtF32) return x;
+    else return (uint16_t)(__float_as_uint(x) >> 16);   // a bf16 value: its top 16 bits, exactly
+}
+
+template <int KT, int D, bool MEAN>
+__global__ __launch_bounds__(256) void summary_kernel(MetaParams p) {
     constexpr int EPL = kElemsPer16B<KT>;   // channels per 16-byte load
+    constexpr int G = D / EPL;              // lanes per token row
+    constexpr int BPW = 64 / G;             // blocks a wave walks at once
+    static_assert(64 % (4 * BPW) == 0, "the waves' block rounds tile the workgroup's 64 blocks");
+    using OT = typename std::conditional<MEAN, float, MetaElem<KT>>::type;
+    constexpr int ROWS = MEAN ? 1 : 2;      // output rows per channel
+    // [row][block][channel], padded to an odd number of 32-bit words per block so that an output row's
+    // reads by consecutive blocks fall on distinct LDS banks
+    constexpr int PAD = sizeof(OT) == 4 ? 1 : 2;
+    __shared__ OT s_out[ROWS][64][D + PAD];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int u = blockIdx.y;
     const int b = u / p.hkv, kvh = u - b * p.hkv;
-    const int blk = blockIdx.x * 64 + lane;
     const int slen = min(max(p.seq_len[b], 0), p.max_pages * kPage);
     const int nb = min((slen + p.block - 1) / p.block, p.nmax);
-    if (blk >= nb) return;
-    const int t0 = blk * p.block;
-    const int t1 = min(t0 + p.block, slen);
-    for (int cg = wave; cg < D / EPL; cg += 4) {
+    const int blk0 = blockIdx.x * 64;
+    if (blk0 >= nb) return;                 // the whole workgroup
+    const int *prow = p.page_table + (size_t)b * p.max_pages;
+    const int g = lane % G, sub = lane / G;
+    // the id of the page the lane's group reads next, fetched a page ahead (also across rounds)
+    int ph_next = prow[min((blk0 + wave * BPW + sub) * p.block, slen - 1) / kPage];
+    for (int r = wave * BPW; r < 64; r += 4 * BPW) {
+        const int bi = r + sub;
+        if (blk0 + bi >= nb) continue;
+        const int t0 = (blk0 + bi) * p.block;
+        const int t1 = min(t0 + p.block, slen);
         float mn[EPL], mx[EPL];
+        double acc[EPL];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
             mn[e] = INFINITY;
             mx[e] = -INFINITY;
+            acc[e] = 0.0;
         }
-        for (int t = t0; t < t1; ++t) {
-            int ph = p.page_table[(size_t)b * p.max_pages + t / kPage];
-            ph = min(max(ph, 0), p.num_pages - 1);
-            const size_t off = (((size_t)ph * p.hkv + kvh) * kPage + (t % kPage)) * D + cg * EPL;
-            float x[EPL];
-            load16_as_f32<KT>(p.k, off, x);
+        for (int tp = t0; tp < t1; tp += kPage) {   // a block starts on a page boundary
+            const int ph = min(max(ph_next, 0), p.num_pages - 1);
+            // next: this block's next page, else the first page of the group's block in the next round
+            const int tn = tp + kPage < t1 ? tp + kPage : t0 + 4 * BPW * p.block;
+            ph_next = prow[min(tn, slen - 1) / kPage];
+            const size_t pbase = ((size_t)ph * p.hkv + kvh) * kPage * D + (size_t)g * EPL;
+            const int n = min(kPage, t1 - tp);
+            uint4 raw[kPage];
+            // all of the page's loads first; a ragged page repeats its last row, which a minimum or
+            // maximum absorbs and the sum skips
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                mn[e] = fminf(mn[e], x[e]);
-                mx[e] = fmaxf(mx[e], x[e]);
+            for (int i = 0; i < kPage; ++i) raw[i] = load16_raw<KT>(p.k, pbase + (size_t)min(i, n - 1) * D);
+#pragma unroll
+            for (int i = 0; i < kPage; ++i) {
+                float x[EPL];
+                widen16<KT>(raw[i], x);
+                if constexpr (MEAN) {
+                    if (i < n) {
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e) acc[e] = dadd(acc[e], (double)x[e]);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) {
+                        mn[e] = fminf(mn[e], x[e]);
+                        mx[e] = fmaxf(mx[e], x[e]);
+                    }
+                }
             }
         }
+        if constexpr (MEAN) {
+            const double cnt = (double)(t1 - t0);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const int ch = cg * EPL + e;
-            const size_t row = (((size_t)u * D + ch) * 2) * p.stride;
-            if constexpr (KT != kKtF32) {
-                uint16_t *m16 = (uint16_t *)p.meta;
-                m16[row + blk] = (uint16_t)(__float_as_uint(mn[e]) >> 16);
-                m16[row + p.stride + blk] = (uint16_t)(__float_as_uint(mx[e]) >> 16);
-            } else {
-                float *m32 = (float *)p.meta;
-                m32[row + blk] = mn[e];
-                m32[row + p.stride + blk] = mx[e];
+            for (int e = 0; e < EPL; ++e) s_out[0][bi][g * EPL + e] = (float)(acc[e] / cnt);
+        } else {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                s_out[0][bi][g * EPL + e] = meta_value<KT>(mn[e]);
+                s_out[ROWS - 1][bi][g * EPL + e] = meta_value<KT>(mx[e]);
             }
         }
     }
-}
-
-// Mean-pooled block summary: the channel-wise mean key of every block over its valid tokens, summed in
-// float64 in token order, divided by the token count and rounded once to float32.  Layout [B][Hkv][d]
-// [stride] fp32.  Lane = block (64 per workgroup), waves take channel groups.
-template <int KT, int D>
-__global__ __launch_bounds__(256) void mean_meta_kernel(MetaParams p) {
-    constexpr int EPL = kElemsPer16B<KT>;   // channels per 16-byte load
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int u = blockIdx.y;
-    const int b = u / p.hkv, kvh = u - b * p.hkv;
-    const int blk = blockIdx.x * 64 + lane;
-    const int slen = max(p.seq_len[b], 0);
-    const int nb = min((slen + p.block - 1) / p.block, p.nmax);
-    if (blk >= nb) return;
-    const int t0 = blk * p.block;
-    const int t1 = min(t0 + p.block, slen);
-    for (int cg = wave; cg < D / EPL; cg += 4) {
-        double acc[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = 0.0;
-        for (int t = t0; t < t1; ++t) {
-            int ph = p.page_table[(size_t)b * p.max_pages + t / kPage];
-            ph = min(max(ph, 0), p.num_pages - 1);
-            const size_t off = (((size_t)ph * p.hkv + kvh) * kPage + (t % kPage)) * D + cg * EPL;
-            float x[EPL];
-            load16_as_f32<KT>(p.k, off, x);
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[e] = dadd(acc[e], (double)x[e]);
-        }
-        const double n = (double)(t1 - t0);
-        float *m32 = (float *)p.meta;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const int ch = cg * EPL + e;
-            m32[((size_t)u * D + ch) * p.stride + blk] = (float)(acc[e] / n);
-        }
+    __syncthreads();
+    // output row q = channel * ROWS + (0: min or mean, 1: max), 64 consecutive blocks per row
+    const int nblk = min(64, nb - blk0);
+    OT *out = (OT *)p.meta;
+    for (int it = threadIdx.x; it < ROWS * D * 64; it += 256) {
+        const int q = it / 64, bi = it % 64;
+        if (bi < nblk) out[((size_t)u * D * ROWS + q) * p.stride + blk0 + bi] = s_out[q % ROWS][bi][q / ROWS];
     }
 }
 
@@ -265,7 +288,7 @@ struct PredictLaunch {
 }  // namespace
 
 hipError_t launch_meta(const KvDesc &kv, int block, int stride, void *meta, bool mean, hipStream_t stream) {
-    MetaParams p;
+    MetaParams p{};
     p.k = kv.k;
     p.page_table = kv.page_table;
     p.seq_len = kv.seq_len;
@@ -280,8 +303,8 @@ hipError_t launch_meta(const KvDesc &kv, int block, int stride, void *meta, bool
     const int kt = kv.fp8 ? kKtFp8 : kv.bf16 ? kKtBf16 : kKtF32;
 #define PRR_META(KT, DD)                                                                             \
     if (kt == KT && kv.d == DD) {                                                                    \
-        if (mean) PRR_LAUNCH(mean_meta_kernel<KT, DD>, dim3(grid), dim3(256), stream, p);                             \
-        else PRR_LAUNCH(meta_kernel<KT, DD>, dim3(grid), dim3(256), stream, p);                                       \
+        if (mean) PRR_LAUNCH((summary_kernel<KT, DD, true>), dim3(grid), dim3(256), stream, p);     \
+        else PRR_LAUNCH((summary_kernel<KT, DD, false>), dim3(grid), dim3(256), stream, p);         \
     } else
     PRR_META(kKtF32, 128) PRR_META(kKtF32, 64) PRR_META(kKtBf16, 128) PRR_META(kKtBf16, 64)
     PRR_META(kKtFp8, 128) PRR_META(kKtFp8, 64)

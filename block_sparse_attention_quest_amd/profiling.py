@@ -182,7 +182,7 @@ def kernel_role(name: str):
     for key, role in (("rows_topk_kernel", "calibration: rows' true top-K"), ("ema_chain_kernel", "calibration: EMA chain"),
                       ("replay_kernel", "calibration: replay"), ("score_kernel", "score"),
                       ("topk_groups_kernel", "topk_groups"), ("topk_kernel", "topk"), ("predict", "predict"),
-                      ("meta_kernel", "meta"), ("append", "append")):
+                      ("summary_kernel", "meta"), ("meta_kernel", "meta"), ("append", "append")):
         if key in name:
             return role
     return None
