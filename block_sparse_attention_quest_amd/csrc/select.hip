@@ -32,9 +32,13 @@ struct MetaParams {
 template <int KT>
 constexpr int kElemsPer16B = KT == kKtF32 ? 4 : KT == kKtBf16 ? 8 : 16;
 
+// The loads are non-temporal: the summary kernels read every K row once.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 template <int KT>
 __device__ __forceinline__ uint4 load16_raw(const void *k, size_t off) {
-    return *(const uint4 *)((const uint8_t *)k + off * (16 / kElemsPer16B<KT>));
+    const u32x4_t v = __builtin_nontemporal_load((const u32x4_t *)((const uint8_t *)k + off * (16 / kElemsPer16B<KT>)));
+    return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 template <int KT>
