@@ -538,8 +538,10 @@ def _budget_point(w, T, deltas, reps, flush, ev, seed):
 
     for P in sets:   # warm every shape once
         bd.spec_attn(q, kv, wt.block, P, wt.scale, out=state, ws=ws)
-    bd.select(q, kv, meta, wt.block, wt.topk, P=P1, scores=scores, A=A, M=M)
-    t_sel = timed(lambda: bd.select(q, kv, meta, wt.block, wt.topk, P=P1, scores=scores, A=A, M=M, stream=crit))
+    ws_sel = bd.select_workspace_for(kv, wt.block, wt.topk)
+    bd.select(q, kv, meta, wt.block, wt.topk, P=P1, scores=scores, A=A, M=M, ws=ws_sel)
+    t_sel = timed(lambda: bd.select(q, kv, meta, wt.block, wt.topk, P=P1, scores=scores, A=A, M=M, stream=crit,
+                                    ws=ws_sel))
     t_spec = [timed(lambda P=P: bd.spec_attn(q, kv, wt.block, P, wt.scale, out=state, ws=ws, stream=crit))
               for P in sets]
     del inp, kv, meta, order, sets, ws, state, scores
@@ -737,7 +739,7 @@ def main():
         bd.spec_attn(q, kv, w.block, P, w.scale, out=iso_state, ws=ws_iso_spec)
         bd.repair(q, kv, w.block, layer.M, w.scale, iso_state, ws=ws_iso_rep)
         bd.select(q, kv, layer.meta, w.block, w.topk, P=P, scores=iso_scores, A=iso_A, M=iso_M,
-                  mode=args.score_mode)
+                  mode=args.score_mode, ws=layer.ws_select)
         bd.select_spec(q, kv, layer.meta, w.block, w.topk, P, w.scale, scores=iso_scores, A=iso_A, M=iso_M,
                        out=iso_state, ws=ws_iso_spec, mode=args.score_mode)
         iso_level.copy_(layer.level)
@@ -809,7 +811,7 @@ def main():
                 bd.repair(q, kv, w.block, layer.M, w.scale, iso_state, ws=ws_iso_rep, stream=crit)
             elif what == "select":
                 bd.select(q, kv, layer.meta, w.block, w.topk, P=P, scores=iso_scores, A=iso_A, M=iso_M,
-                          mode=args.score_mode, stream=crit)
+                          mode=args.score_mode, stream=crit, ws=layer.ws_select)
             elif what == "predict":
                 bd.predict(layer.scores, kv.seq_len, w.block, *w.ema, w.topk, iso_level, iso_trend, iso_live,
                            P_next=iso_P, ws=ws_iso_pred, stream=crit)

@@ -23,7 +23,7 @@ PAGE_SIZE = 16
 EXPORTS = (
     "prr_max_blocks", "prr_meta_stride", "prr_meta_bytes", "prr_attn_workspace_bytes",
     "prr_workspace_clear", "prr_build_meta", "prr_mean_meta_bytes", "prr_build_mean_meta", "prr_append",
-    "prr_select", "prr_select_spec_workspace_bytes", "prr_select_spec", "prr_select_spec_predict",
+    "prr_select_workspace_bytes", "prr_select", "prr_select_spec_workspace_bytes", "prr_select_spec", "prr_select_spec_predict",
     "prr_layer_step_workspace_bytes", "prr_layer_step", "prr_predict_workspace_bytes",
     "prr_predict",
     "prr_spec_attn", "prr_spec_attn_noalloc",
@@ -76,8 +76,10 @@ _SIGS = {
     "prr_mean_meta_bytes": (_SZ, [_P(KvCacheStruct), _I32]),
     "prr_build_mean_meta": (ctypes.c_int, [_P(KvCacheStruct), _I32, _VP, _VP]),
     "prr_append": (ctypes.c_int, [_P(KvCacheStruct), _I32, _VP, _VP, _VP, ctypes.c_int, _VP, _VP]),
+    "prr_select_workspace_bytes": (_SZ, [_P(KvCacheStruct), ctypes.c_int, _I32, _I32]),
     "prr_select": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _VP, ctypes.c_int, _I32, _I32,
-                                  _P(BlockSetStruct), _VP, _P(BlockSetStruct), _P(BlockSetStruct), _VP]),
+                                  _P(BlockSetStruct), _VP, _P(BlockSetStruct), _P(BlockSetStruct), _VP, _SZ,
+                                  _VP]),
     "prr_select_spec_workspace_bytes": (_SZ, [_P(KvCacheStruct), _I32, _I32, _I32, _I32]),
     "prr_select_spec": (ctypes.c_int, [_VP, _I32, _P(KvCacheStruct), _VP, ctypes.c_int, _I32, _I32,
                                        _P(BlockSetStruct), _VP, _P(BlockSetStruct), _P(BlockSetStruct), _F,
@@ -355,12 +357,25 @@ def append(kv: KVCache, block: int, k_new: torch.Tensor, v_new: torch.Tensor, me
                           _ptr(kv.seq_len), _stream(stream)), "prr_append")
 
 
+def select_workspace_for(kv: KVCache, block: int, topk: int, mode: str = "quest") -> Optional[Workspace]:
+    """Workspace of prr_select (zeroed), or None where it would not be used (rows of up to 8192 blocks).
+    With it, longer rows are ranked in part-parallel stages; rows above 32768 blocks need it."""
+    s = kv.struct()
+    n = load_library().prr_select_workspace_bytes(ctypes.byref(s), _mode(mode), block, topk)
+    return Workspace(n, kv.k.device) if n else None
+
+
 def select(q: torch.Tensor, kv: KVCache, meta: torch.Tensor, block: int, topk: int,
            P: Optional[BlockSet] = None, scores: Optional[torch.Tensor] = None,
-           A: Optional[BlockSet] = None, M: Optional[BlockSet] = None, mode: str = "quest", stream=None):
+           A: Optional[BlockSet] = None, M: Optional[BlockSet] = None, mode: str = "quest", stream=None,
+           ws: Optional[Workspace] = None, staged: bool = True):
     """Block scores [B][Hkv][Nmax] fp64 (Quest's bound, or the mean key's product for mode "mean"),
-    A (top-k, ascending) and M = A \\ P when P is given."""
+    A (top-k, ascending) and M = A \\ P when P is given.  ws: select_workspace_for (allocated here when
+    none is given and staged is true: rows above 8192 blocks are then ranked in part-parallel stages;
+    staged false and no ws: one top-K workgroup per row, up to 32768 blocks)."""
     lib = load_library()
+    if ws is None and staged:
+        ws = select_workspace_for(kv, block, topk, mode)
     s = kv.struct()
     nmax = lib.prr_max_blocks(ctypes.byref(s), block)
     B, H = kv.batch, kv.num_kv_heads
@@ -376,7 +391,8 @@ def select(q: torch.Tensor, kv: KVCache, meta: torch.Tensor, block: int, topk: i
     m_s = M.struct() if M is not None else None
     st = lib.prr_select(_ptr(q), q.shape[1], ctypes.byref(s), _ptr(meta), _mode(mode), block, topk,
                         ctypes.byref(p_s) if p_s is not None else None, _ptr(scores), ctypes.byref(a_s),
-                        ctypes.byref(m_s) if m_s is not None else None, _stream(stream))
+                        ctypes.byref(m_s) if m_s is not None else None, ws.ptr() if ws is not None else None,
+                        ws.nbytes if ws is not None else 0, _stream(stream))
     _check(st, "prr_select")
     return scores, A, M
 

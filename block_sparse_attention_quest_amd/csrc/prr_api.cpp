@@ -208,9 +208,26 @@ prr_status prr_append(const prr_kv_cache *kv, int32_t block, const void *k_new, 
                                          mode == PRR_SCORE_MEAN, stream));
 }
 
+// Whether selection (of any entry point) has a top-K plan for rows of nmax blocks: one top-K workgroup
+// per unit up to prr::kMaxRowTopK blocks, the three part-parallel stages beyond.
+static bool selection_plan_exists(const prr_kv_cache *kv, int nmax, int topk, bool mean, bool fused) {
+    if (nmax > prr::kMaxSelectN) return false;
+    if (nmax <= prr::kMaxRowTopK) return true;
+    const bool bq = kv->dtype != PRR_F32;
+    if (fused && bq) return prr::select_spec_plan(nmax, topk, mean).three;
+    return prr::select_supported(nmax, topk, bq, mean);
+}
+
+size_t prr_select_workspace_bytes(const prr_kv_cache *kv, prr_score_mode mode, int32_t block, int32_t topk) {
+    if (!kv || kv->batch <= 0 || kv->num_kv_heads <= 0 || block < prr::kPage || topk < 0) return 0;
+    if (mode != PRR_SCORE_QUEST && mode != PRR_SCORE_MEAN) return 0;
+    return prr::select_workspace_bytes(kv->batch * kv->num_kv_heads, prr_max_blocks(kv, block), topk,
+                                       kv->dtype != PRR_F32, mode == PRR_SCORE_MEAN);
+}
+
 prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
                       prr_score_mode mode, int32_t block, int32_t topk, const prr_block_set *P, double *scores,
-                      prr_block_set *A, prr_block_set *M, hipStream_t stream) {
+                      prr_block_set *A, prr_block_set *M, void *ws, size_t ws_bytes, hipStream_t stream) {
     CallTiming timing_;
     if (!q || !meta || !scores) return PRR_EINVAL;
     if (mode != PRR_SCORE_QUEST && mode != PRR_SCORE_MEAN) return PRR_EINVAL;
@@ -227,13 +244,17 @@ prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv
         if (M->cap < topk) return PRR_EINVAL;
     }
     const int nmax = prr_max_blocks(kv, block);
-    if (nmax > prr::kMaxSelectN) return PRR_EUNSUPPORTED;
+    if (!selection_plan_exists(kv, nmax, topk, mode == PRR_SCORE_MEAN, false)) return PRR_EUNSUPPORTED;
+    // the stages' workspace: required above one top-K workgroup's rows, optional (faster) below
+    const size_t need = prr_select_workspace_bytes(kv, mode, block, topk);
+    if (nmax > prr::kMaxRowTopK && !ws) return PRR_EWORKSPACE;
+    if (ws && ws_bytes < need) return PRR_EWORKSPACE;
     PRR_TRY(check_input_set(kv, block, P, stream));
     return hip_status(prr::launch_select(desc(kv), q, num_q_heads, meta, block, prr_meta_stride(kv, block),
                                          nmax, topk, P ? P->idx : nullptr, P ? P->count : nullptr,
                                          P ? P->cap : 0, scores, A->idx, A->count, A->cap,
                                          M ? M->idx : nullptr, M ? M->count : nullptr, M ? M->pages : nullptr,
-                                         M ? M->cap : 0, mode == PRR_SCORE_MEAN, stream));
+                                         M ? M->cap : 0, mode == PRR_SCORE_MEAN, need ? ws : nullptr, stream));
 }
 
 size_t prr_select_spec_workspace_bytes(const prr_kv_cache *kv, int32_t num_q_heads, int32_t block, int32_t topk,
@@ -242,7 +263,7 @@ size_t prr_select_spec_workspace_bytes(const prr_kv_cache *kv, int32_t num_q_hea
         block < prr::kPage || cap <= 0 || topk < 0)
         return 0;
     return prr::select_spec_workspace_bytes(kv->batch, num_q_heads, kv->num_kv_heads, kv->head_dim, block, cap,
-                                            prr_max_blocks(kv, block), topk);
+                                            prr_max_blocks(kv, block), topk, kv->dtype == PRR_F32);
 }
 
 static prr_status check_predict(const double *scores, const int32_t *seq_len, int32_t batch,
@@ -253,7 +274,10 @@ static prr_status check_predict(const double *scores, const int32_t *seq_len, in
     if (batch <= 0 || num_kv_heads <= 0 || block <= 0 || max_blocks <= 0 || budget < 0) return PRR_EINVAL;
     PRR_TRY(check_set(P_next));
     if (P_next->cap < budget) return PRR_EINVAL;
-    if (max_blocks > prr::kMaxSelectN) return PRR_EUNSUPPORTED;
+    // rows longer than one workgroup's top-K need the part-parallel plan (and its workspace)
+    if (max_blocks > prr::kMaxSelectN ||
+        (max_blocks > prr::kMaxRowTopK && prr::predict_workspace_bytes(batch, num_kv_heads, max_blocks, budget) == 0))
+        return PRR_EUNSUPPORTED;
     if (P_next->pages) {
         // the page list maps through this cache's page table, for the same sequences and block size
         PRR_TRY(check_kv(kv));
@@ -305,6 +329,7 @@ static prr_status predict_args(const prr_predict_args *pred, const double *score
         const size_t need = prr::predict_workspace_bytes(pred->batch, pred->num_kv_heads, pred->max_blocks,
                                                          pred->budget);
         if (pred->ws && pred->ws_bytes < need) return PRR_EWORKSPACE;
+        if (pred->max_blocks > prr::kMaxRowTopK && !pred->ws) return PRR_EWORKSPACE;
         pa.ws = need ? pred->ws : nullptr;
     }
     return PRR_OK;
@@ -327,7 +352,7 @@ prr_status prr_select_spec_predict(const void *q, int32_t num_q_heads, const prr
     if (topk < 0 || A->cap < topk || M->cap < topk) return PRR_EINVAL;
     if (!out || !out->acc || !out->l || !out->m) return PRR_EINVAL;
     const int nmax = prr_max_blocks(kv, block);
-    if (nmax > prr::kMaxSelectN) return PRR_EUNSUPPORTED;
+    if (!selection_plan_exists(kv, nmax, topk, mode == PRR_SCORE_MEAN, true)) return PRR_EUNSUPPORTED;
     if (!ws || ws_bytes < prr_select_spec_workspace_bytes(kv, num_q_heads, block, topk, P->cap))
         return PRR_EWORKSPACE;
     prr::PredictArgs pa;
@@ -346,7 +371,7 @@ size_t prr_layer_step_workspace_bytes(const prr_kv_cache *kv, int32_t num_q_head
         block < prr::kPage || p_cap <= 0 || m_cap <= 0 || topk < 0)
         return 0;
     return prr::layer_step_workspace_bytes(kv->batch, num_q_heads, kv->num_kv_heads, kv->head_dim, block, p_cap, m_cap,
-                                           prr_max_blocks(kv, block), topk);
+                                           prr_max_blocks(kv, block), topk, kv->dtype == PRR_F32);
 }
 
 prr_status prr_layer_step(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
@@ -365,7 +390,7 @@ prr_status prr_layer_step(const void *q, int32_t num_q_heads, const prr_kv_cache
     if (topk < 0 || A->cap < topk || M->cap < topk) return PRR_EINVAL;
     if (!state || !state->acc || !state->l || !state->m) return PRR_EINVAL;
     const int nmax = prr_max_blocks(kv, block);
-    if (nmax > prr::kMaxSelectN) return PRR_EUNSUPPORTED;
+    if (!selection_plan_exists(kv, nmax, topk, mode == PRR_SCORE_MEAN, true)) return PRR_EUNSUPPORTED;
     if (!ws || ws_bytes < prr_layer_step_workspace_bytes(kv, num_q_heads, block, topk, P->cap, M->cap))
         return PRR_EWORKSPACE;
     prr::PredictArgs pa;
@@ -402,6 +427,7 @@ prr_status prr_predict(const double *scores, const int32_t *seq_len, int32_t bat
                           P_next, kv));
     const size_t need = prr::predict_workspace_bytes(batch, num_kv_heads, max_blocks, budget);
     if (ws && ws_bytes < need) return PRR_EWORKSPACE;
+    if (max_blocks > prr::kMaxRowTopK && !ws) return PRR_EWORKSPACE;
     const bool listed = P_next->pages != nullptr;
     return hip_status(prr::launch_predict(scores, seq_len, batch, num_kv_heads, block, max_blocks, alpha,
                                           beta, gamma, budget, level, trend, live, P_next->idx,

@@ -47,7 +47,11 @@ hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t 
 int device_cu_count();
 
 constexpr int kPage = 16;          // tokens per page (the only supported page size)
-constexpr int kMaxSelectN = 32768; // blocks per (sequence, kv head) the top-K kernels hold on chip
+constexpr int kMaxRowTopK = 32768; // blocks per (sequence, kv head) one top-K workgroup holds on chip
+constexpr int kMaxSelectN = 131072; // blocks per (sequence, kv head) selection and the predictor take;
+                                    // rows longer than kMaxRowTopK are ranked in part-parallel stages
+constexpr int kStagedSelectMin = 8192; // prr_select ranks rows longer than this in stages when given a
+                                       // workspace (one top-K workgroup per unit leaves most CUs idle)
 constexpr int kMaxCalibBlocks = 4096; // calibration: blocks per prefill row (16 per thread of four waves)
 constexpr int kMaxCalibGrid = 4096;   // calibration: candidates (alpha, beta, gamma)
 
@@ -89,10 +93,15 @@ hipError_t check_sets(const KvDesc &kv, int block, const int32_t *idx, const int
 // means ([d][stride] per unit).
 hipError_t launch_meta(const KvDesc &kv, int block, int stride, void *meta, bool mean, hipStream_t stream);
 
+// Scoring and top-K (prr_select).  Without ws (rows of up to kMaxRowTopK blocks): the score kernel, then
+// one top-K workgroup per unit.  With ws (select_workspace_bytes of caller memory, zeroed once; every call
+// leaves it so), rows longer than kStagedSelectMin: every scoring workgroup keeps its part's local top-K
+// candidates, then groups of parts and the unit's final ranking (three stages, as a fused launch's).
 hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *meta, int block,
                          int stride, int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt,
                          int p_cap, double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap,
-                         int32_t *m_idx, int32_t *m_cnt, int32_t *m_pages, int m_cap, bool mean, hipStream_t stream);
+                         int32_t *m_idx, int32_t *m_cnt, int32_t *m_pages, int m_cap, bool mean, void *ws,
+                         hipStream_t stream);
 
 // Top-K + M = A \ P from scores already in place (the second half of launch_select).  m_pages (may be
 // null): M's page work list, written with M.
@@ -114,6 +123,38 @@ struct SelectSpecPlan {
 };
 SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean);
 
+// The plan for parts of bpw blocks.  force_three: the three stages even where two would do, for a top-K
+// that ranks in launches of its own (rows longer than kMaxTwoStageBlocks, whose P bitmap only those
+// launches hold).  No plan (two false): more candidates than the stages rank.
+SelectSpecPlan stage_plan(int nmax, int topk, int bpw, bool force_three);
+
+// Where a three-stage top-K keeps its data, from base: the parts' candidates (nparts per unit; keys,
+// then indices, then counts), the groups' (same layout), then one group arrival counter per unit, each
+// 256-byte aligned.  bytes: the whole.
+struct StageLayout {
+    char *cand1, *cand2;
+    uint32_t *garr;
+    size_t bytes;
+};
+inline StageLayout stage_layout(char *base, int units, int nparts, const SelectSpecPlan &pl) {
+    const auto align = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t parts = (size_t)units * nparts, groups = (size_t)units * pl.ng;
+    const size_t b1 = align(parts * pl.kl * 12 + parts * 4);
+    const size_t b2 = align(groups * pl.kl2 * 12 + groups * 4);
+    StageLayout l;
+    l.cand1 = base;
+    l.cand2 = base + b1;
+    l.garr = (uint32_t *)(base + b1 + b2);
+    l.bytes = b1 + b2 + align((size_t)units * 4);
+    return l;
+}
+
+// launch_select's workspace: 0 for rows of up to kStagedSelectMin blocks and where the stages have no
+// plan, else the three stages' (stage_layout over parts of the score kernel's size).  bq: bf16 queries
+// and metadata.  select_supported: whether launch_select has a plan for the shape.
+size_t select_workspace_bytes(int units, int nmax, int topk, bool bq, bool mean);
+bool select_supported(int nmax, int topk, bool bq, bool mean);
+
 // The second and third stages of a three-stage top-K (plan.three): nparts parts of kl candidates per
 // unit at cand1 (keys, then indices, then counts, as the fused launch writes them); the group candidates
 // go to cand2 (same layout, ng x kl2 slots per unit), the per-unit group arrival counters to arrivals
@@ -127,11 +168,12 @@ hipError_t launch_topk_groups(const KvDesc &kv, int block, int nmax, int topk, c
                               int32_t *live = nullptr);
 
 // Offset of the carried predictor's work counter in the prr_select_spec workspace.
-size_t pred_counter_offset(int batch, int hq, int hkv, int d, int block, int cap, int nmax, int topk);
+size_t pred_counter_offset(int batch, int hq, int hkv, int d, int block, int cap, int nmax, int topk, bool f32);
 
 // Workspace of prr_select_spec: the speculative pass's attention workspace, then (two-stage top-K) the
-// candidates of every scoring workgroup.
-size_t select_spec_workspace_bytes(int batch, int hq, int hkv, int d, int block, int cap, int nmax, int topk);
+// candidates of every scoring workgroup, or for an fp32 cache (f32) launch_select's workspace.
+size_t select_spec_workspace_bytes(int batch, int hq, int hkv, int d, int block, int cap, int nmax, int topk,
+                                   bool f32);
 
 // Selection and the speculative pass over P in one grid (bf16 caches; fp32 caches run the two in turn),
 // then the top-K.  ws: select_spec_workspace_bytes.
@@ -177,7 +219,7 @@ hipError_t launch_select_spec_fp8(const KvDesc &kv, const void *q, int hq, const
 // layer_step_workspace_bytes: the select_spec workspace, then M's attention workspace, the per-unit M flags
 // and a status word (zeroed once; every call leaves it ready for the next).
 size_t layer_step_workspace_bytes(int batch, int hq, int hkv, int d, int block, int p_cap, int m_cap, int nmax,
-                                  int topk);
+                                  int topk, bool f32);
 hipError_t launch_layer_step(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride, int nmax,
                              int topk, const int32_t *p_idx, const int32_t *p_cnt, const int32_t *p_pages, int p_cap, double *scores,
                              int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx, int32_t *m_cnt, int32_t *m_pages, int m_cap,

@@ -179,6 +179,25 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
     score_body<BF16, D, false, MEAN>(p, blockIdx.x, blockIdx.y);
 }
 
+// First stage of a three-stage top-K over rows longer than one top-K workgroup holds: workgroup bx of
+// unit u scores its 256 BPL blocks and keeps their local top-kl as candidates (stages two and three in
+// topk_groups_kernel).
+template <bool BF16, int D, bool MEAN>
+__global__ __launch_bounds__(256) void score_parts_kernel(ScoreParams p, CandParams cp, int nsx) {
+    __shared__ TopkSmem<4> sm;
+    constexpr int BPL = kScoreBPL<BF16, MEAN>;
+    constexpr int BPW = 256 * BPL;
+    const int bx = blockIdx.x, u = blockIdx.y;
+    double kept[BPL] = {};
+    score_body<BF16, D, false, MEAN>(p, bx, u, kept);
+    const int b = u / p.hkv;
+    const int nb = min((max(p.seq_len[b], 0) + p.block - 1) / p.block, p.nmax);
+    const int n_local = min(max(nb - bx * BPW, 0), BPW);
+    const size_t part = (size_t)u * nsx + bx;
+    local_candidates<BPL>(kept, n_local, cp.kl, bx * BPW, cp.key + part * cp.kl, cp.idx + part * cp.kl,
+                          cp.cnt + part, sm);
+}
+
 template <int KPT, int TPB>
 __global__ __launch_bounds__(TPB) void topk_kernel(TopkParams p) {
     topk_body<KPT, TPB>(p, blockIdx.x);
@@ -243,7 +262,7 @@ __global__ __launch_bounds__(256) void topk_groups_kernel(TopkParams tp, CandPar
     }
     __syncthreads();
     if (s_last) {
-        topk_candidates_body<KPT3>(tp, u, c2.key + (size_t)u * ng * c2.kl, c2.idx + (size_t)u * ng * c2.kl,
+        topk_candidates_body<KPT3, false, kMaxSelectN>(tp, u, c2.key + (size_t)u * ng * c2.kl, c2.idx + (size_t)u * ng * c2.kl,
                                    c2.cnt + (size_t)u * ng, ng, c2.kl);
         if (live && threadIdx.x == 0) {   // a predictor step: its blocks are all live from now on
             const int b = u / tp.hkv;
@@ -320,7 +339,8 @@ hipError_t launch_meta(const KvDesc &kv, int block, int stride, void *meta, bool
 hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *meta, int block,
                          int stride, int nmax, int topk, const int32_t *p_idx, const int32_t *p_cnt,
                          int p_cap, double *scores, int32_t *a_idx, int32_t *a_cnt, int a_cap,
-                         int32_t *m_idx, int32_t *m_cnt, int32_t *m_pages, int m_cap, bool mean, hipStream_t stream) {
+                         int32_t *m_idx, int32_t *m_cnt, int32_t *m_pages, int m_cap, bool mean, void *ws,
+                         hipStream_t stream) {
     const int units = kv.batch * kv.hkv;
     ScoreParams sp;
     sp.q = q;
@@ -334,8 +354,31 @@ hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *me
     sp.stride = stride;
     sp.nmax = nmax;
     const bool bq = kv.bf16 || kv.fp8;   // bf16 queries (and bf16 min/max metadata)
-    const int bpw = 256 * (mean ? kScoreBPL<true, true> : bq ? kScoreBPL<true> : kScoreBPL<false>);
+    const int bpw = score_bpw(bq, mean);
     const dim3 sgrid((nmax + bpw - 1) / bpw, units);
+    const SelectSpecPlan plan = ws && nmax > kStagedSelectMin ? stage_plan(nmax, topk, bpw, true) : SelectSpecPlan{};
+    if (nmax > kMaxRowTopK && !plan.three) return hipErrorInvalidValue;
+    if (plan.three) {
+        // three stages: the scoring workgroups keep their parts' candidates, then groups and the ranking
+        const int nsx = (int)sgrid.x;
+        const StageLayout sl = stage_layout((char *)ws, units, nsx, plan);
+        CandParams cp;
+        cp.key = (uint64_t *)sl.cand1;
+        cp.idx = (int32_t *)(sl.cand1 + (size_t)units * nsx * plan.kl * 8);
+        cp.cnt = (int32_t *)(sl.cand1 + (size_t)units * nsx * plan.kl * 12);
+        cp.kl = plan.kl;
+#define PRR_SP(BQ, DD, MN)                                                                                   \
+        if (bq == BQ && kv.d == DD && mean == MN) PRR_LAUNCH((score_parts_kernel<BQ, DD, MN>), dim3(sgrid), dim3(256), stream, sp, cp, nsx); \
+        else
+        PRR_SP(true, 128, false) PRR_SP(true, 64, false) PRR_SP(false, 128, false) PRR_SP(false, 64, false)
+        PRR_SP(true, 128, true) PRR_SP(true, 64, true) PRR_SP(false, 128, true) PRR_SP(false, 64, true)
+        { return hipErrorInvalidValue; }
+#undef PRR_SP
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_topk_groups(kv, block, nmax, topk, p_idx, p_cnt, p_cap, a_idx, a_cnt, nullptr, a_cap, m_idx, m_cnt,
+                                  m_pages, m_cap, plan, nsx, sl.cand1, sl.cand2, sl.garr, stream);
+    }
     if (mean) {
         // the fp32 block means do not depend on the cache dtype beyond q's
         if (bq) {

@@ -316,6 +316,9 @@ struct ScoreParams {
 template <bool BF16, bool MEAN = false>
 constexpr int kScoreBPL = (BF16 || MEAN) ? 2 : 1;
 
+// Blocks per scoring workgroup (256 lanes of kScoreBPL blocks), on the host.
+constexpr int score_bpw(bool bq, bool mean) { return 256 * ((bq || mean) ? 2 : 1); }
+
 // Scores blocks [256 BPL bx, 256 BPL (bx + 1)) of unit u (BPL consecutive blocks per lane).  COHERENT:
 // the scores are stored with device-scope stores, for a reader on another XCD within the same launch.
 template <bool BF16, int D, bool COHERENT = false, bool MEAN = false>
@@ -690,13 +693,14 @@ __device__ __forceinline__ void group_candidates(const uint64_t *ckey, const int
 
 // Stage 2: the top-K of unit u over its nparts x kl candidate slots (part c holds ccnt[c] candidates)
 // and M = A \ P, written like topk_body.  256 threads with KPT slots each (256 KPT >= nparts kl).
-template <int KPT, bool COH_M = false>
+// NBITS: the longest row (in blocks) whose P bitmap the workgroup holds in LDS.
+template <int KPT, bool COH_M = false, int NBITS = kMaxTwoStageBlocks>
 __device__ __forceinline__ void topk_candidates_body(const TopkParams &p, int u, const uint64_t *ckey,
                                                      const int32_t *cidx, const int32_t *ccnt, int nparts,
                                                      int kl) {
     constexpr int TPB = 256, W = 4;
     __shared__ TopkSmem<W> sm;
-    __shared__ uint32_t s_pbits[kMaxTwoStageBlocks / 32];
+    __shared__ uint32_t s_pbits[NBITS / 32];
     __shared__ int s_cnt[TPB];
     __shared__ int s_total;
     const int b = u / p.hkv;

@@ -11,19 +11,18 @@ namespace prr {
 // candidates of all parts).  At 2048 blocks (128K context, block 64, batch 8) two stages took the fused
 // launch from 37.2 to 35.4 us: the candidate selection runs in every scoring workgroup in parallel, and
 // the unit's last workgroup ranks 256 candidates instead of 2048 scores.
-SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean) {
+SelectSpecPlan stage_plan(int nmax, int topk, int bpw, bool force_three) {
     SelectSpecPlan pl = {};
     pl.two = false;
     pl.kl = 0;
-    pl.kpt = nmax <= 256 ? 1 : nmax <= 512 ? 2 : nmax <= 1024 ? 4 : 0;
-    if (pl.kpt == 0 && nmax <= kMaxTwoStageBlocks) {
-        const int bpw = select_spec_score_bpw(mean);
+    pl.kpt = force_three ? 0 : nmax <= 256 ? 1 : nmax <= 512 ? 2 : nmax <= 1024 ? 4 : 0;
+    if (pl.kpt == 0 && nmax <= kMaxSelectN) {
         const int nsx = (nmax + bpw - 1) / bpw;
         const int kl = std::max(1, std::min(topk, bpw));
         const long slots = (long)nsx * kl;
         const int kpt = slots <= 256 ? 1 : slots <= 512 ? 2 : slots <= 1024 ? 4 : slots <= 2048 ? 8
                       : slots <= 4096 ? 16 : 0;
-        if (kpt) {
+        if (kpt && !force_three) {
             pl.two = true;
             pl.kl = kl;
             pl.kpt = kpt;
@@ -32,17 +31,18 @@ SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean) {
             // one ranking of the groups' candidates (up to 4096 slots) follows.  At 32768 blocks and
             // K = 256 (8 groups of 8 parts) this took the 512K layer step from 96.9 to 73.6 us; groups of
             // 4096 slots (4 per unit, fewer workgroups) took 76.7 us, so they are used only where groups
-            // of 2048 slots would leave more than one ranking holds (K above 341 at 32768 blocks).
-            int gp = std::max(1, 2048 / kl);
+            // of 2048 slots would leave more than one ranking holds (K above 341 at 32768 blocks).  A
+            // group is one workgroup of 256 threads, one part's count each: at most 256 parts.
+            int gp = std::min(256, std::max(1, 2048 / kl));
             if ((long)((nsx + gp - 1) / gp) * std::min(topk, gp * kl) > 4096)
-                gp = std::max(1, 4096 / kl);   // groups of up to 4096 slots, so that fewer candidates remain
+                gp = std::min(256, std::max(1, 4096 / kl));   // groups of up to 4096 slots: fewer candidates remain
             const int ng = (nsx + gp - 1) / gp;
             const int kl2 = std::min(topk, gp * kl);
             const long slots2 = (long)std::min(gp, nsx) * kl, slots3 = (long)ng * kl2;
             const int kpt2 = slots2 <= 2048 ? 8 : 16;
             const int kpt3 = slots3 <= 256 ? 1 : slots3 <= 512 ? 2 : slots3 <= 1024 ? 4 : slots3 <= 2048 ? 8
                            : slots3 <= 4096 ? 16 : 0;
-            if (kpt3) {
+            if (kpt3 && ng <= 256) {
                 pl.two = true;
                 pl.kl = kl;
                 pl.kpt = 0;
@@ -58,33 +58,48 @@ SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean) {
     return pl;
 }
 
+// The fused launch ranks a unit inside the launch only for rows whose P bitmap it holds
+// (kMaxTwoStageBlocks); longer rows take the three stages, the last two in launches of their own.
+SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean) {
+    return stage_plan(nmax, topk, select_spec_score_bpw(mean), nmax > kMaxTwoStageBlocks);
+}
+
 // Candidate slots of the two-stage top-K: [units][nsx][kl] keys (8 bytes) and indices (4), [units][nsx]
 // counts.  The workspace covers both block summaries.  A three-stage top-K appends the group candidates
 // ([units][ng][kl2] keys and indices, [units][ng] counts) and one group arrival counter per unit.
-static size_t three_stage_bytes(int units, const SelectSpecPlan &pl) {
-    const size_t groups = (size_t)units * pl.ng;
-    return (groups * pl.kl2 * 12 + groups * 4 + 255) / 256 * 256 + ((size_t)units * 4 + 255) / 256 * 256;
-}
-
 static size_t candidate_bytes(int units, int nmax, int topk, bool mean) {
     const SelectSpecPlan pl = select_spec_plan(nmax, topk, mean);
     if (!pl.two) return 0;
     const int bpw = select_spec_score_bpw(mean);
-    const size_t parts = (size_t)units * ((nmax + bpw - 1) / bpw);
-    size_t bytes = parts * pl.kl * 12 + parts * 4;
-    if (pl.three) bytes = (bytes + 255) / 256 * 256 + three_stage_bytes(units, pl);   // group slots 256-aligned
-    return bytes;
+    const int nparts = (nmax + bpw - 1) / bpw;
+    if (pl.three) return stage_layout(nullptr, units, nparts, pl).bytes;
+    const size_t parts = (size_t)units * nparts;
+    return parts * pl.kl * 12 + parts * 4;
 }
 
-// The carried predictor's work counter sits after the candidates, in a 256-byte slot of its own.
-size_t pred_counter_offset(int batch, int hq, int hkv, int d, int block, int cap, int nmax, int topk) {
-    const size_t cand = std::max(candidate_bytes(batch * hkv, nmax, topk, false),
-                                 candidate_bytes(batch * hkv, nmax, topk, true));
+size_t select_workspace_bytes(int units, int nmax, int topk, bool bq, bool mean) {
+    if (nmax <= kStagedSelectMin) return 0;
+    const int bpw = score_bpw(bq, mean);
+    const SelectSpecPlan pl = stage_plan(nmax, topk, bpw, true);
+    return pl.three ? stage_layout(nullptr, units, (nmax + bpw - 1) / bpw, pl).bytes : 0;
+}
+
+bool select_supported(int nmax, int topk, bool bq, bool mean) {
+    return nmax <= kMaxRowTopK || (nmax <= kMaxSelectN && stage_plan(nmax, topk, score_bpw(bq, mean), true).three);
+}
+
+// The carried predictor's work counter sits after the candidates, in a 256-byte slot of its own.  For an
+// fp32 cache, whose passes run in turn, the candidate room is launch_select's workspace instead.
+size_t pred_counter_offset(int batch, int hq, int hkv, int d, int block, int cap, int nmax, int topk, bool f32) {
+    const int units = batch * hkv;
+    const size_t cand = f32 ? std::max(select_workspace_bytes(units, nmax, topk, false, false),
+                                       select_workspace_bytes(units, nmax, topk, false, true))
+                            : std::max(candidate_bytes(units, nmax, topk, false), candidate_bytes(units, nmax, topk, true));
     return attn_workspace_bytes(batch, hq, hkv, d, block, cap) + (cand + 255) / 256 * 256;
 }
 
-size_t select_spec_workspace_bytes(int batch, int hq, int hkv, int d, int block, int cap, int nmax, int topk) {
-    return pred_counter_offset(batch, hq, hkv, d, block, cap, nmax, topk) + 256;
+size_t select_spec_workspace_bytes(int batch, int hq, int hkv, int d, int block, int cap, int nmax, int topk, bool f32) {
+    return pred_counter_offset(batch, hq, hkv, d, block, cap, nmax, topk, f32) + 256;
 }
 
 hipError_t launch_select_spec(const KvDesc &kv, const void *q, int hq, const void *meta, int block, int stride,

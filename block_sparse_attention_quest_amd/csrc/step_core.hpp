@@ -133,9 +133,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 
 // Blocks per scoring workgroup of the fused launch (bf16 queries): 512 for min/max metadata, 512 for
 // block means (two per lane either way).
-inline int select_spec_score_bpw(bool mean) {
-    return 256 * (mean ? kScoreBPL<true, true> : kScoreBPL<true, false>);
-}
+inline int select_spec_score_bpw(bool mean) { return score_bpw(true, mean); }
 
 // Everything a fused launch needs besides its kernel: the parameters of its roles, its grid, and where the
 // top-K stages after it (if any) keep their candidates.  Shared by the selection + speculation launch and
@@ -230,7 +228,7 @@ inline FusedSetup fused_setup(const KvDesc &kv, const void *q, int hq, const voi
         f.n_pred = pred->batch * pred->hkv;
     }
     f.grid = (long)f.n_spec + (long)f.nsx * f.units;
-    f.pred_ctr = (uint32_t *)((char *)ws + pred_counter_offset(kv.batch, hq, kv.hkv, kv.d, block, p_cap, nmax, topk));
+    f.pred_ctr = (uint32_t *)((char *)ws + pred_counter_offset(kv.batch, hq, kv.hkv, kv.d, block, p_cap, nmax, topk, false));
     f.plan = select_spec_plan(nmax, topk, mean);
     f.cp.kl = f.plan.kl;
     f.cbase = (char *)ws + attn_workspace_bytes(kv.batch, hq, kv.hkv, kv.d, block, p_cap);
@@ -246,12 +244,9 @@ inline hipError_t fused_after(const FusedSetup &f, const KvDesc &kv, int block, 
                               int a_cap, int32_t *m_idx, int32_t *m_cnt, int32_t *m_pages, int m_cap, hipStream_t stream) {
     if (f.plan.three) {
         // the parts' candidates are in place; groups of them, then the unit's ranking
-        const size_t s1 = (size_t)f.units * f.nsx * f.plan.kl;
-        char *cand2 = f.cbase + (s1 * 12 + (size_t)f.units * f.nsx * 4 + 255) / 256 * 256;
-        const size_t s2 = (size_t)f.units * f.plan.ng * f.plan.kl2;
-        uint32_t *garr = (uint32_t *)(cand2 + (s2 * 12 + (size_t)f.units * f.plan.ng * 4 + 255) / 256 * 256);
+        const StageLayout sl = stage_layout(f.cbase, f.units, f.nsx, f.plan);
         return launch_topk_groups(kv, block, nmax, topk, p_idx, p_cnt, p_cap, a_idx, a_cnt, nullptr, a_cap, m_idx, m_cnt, m_pages, m_cap,
-                                  f.plan, f.nsx, f.cbase, cand2, garr, stream);
+                                  f.plan, f.nsx, sl.cand1, sl.cand2, sl.garr, stream);
     }
     if (f.plan.kpt == 0)
         return launch_topk(kv, block, nmax, topk, scores, p_idx, p_cnt, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt, m_pages, m_cap,
@@ -276,7 +271,8 @@ hipError_t launch_select_spec_t(const KvDesc &kv, const void *q, int hq, const v
     if constexpr (KT == kKtF32) {
         // fp32 caches (exact-input checks): the passes one after the other
         hipError_t e = launch_select(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_cap, scores,
-                                     a_idx, a_cnt, a_cap, m_idx, m_cnt, m_pages, m_cap, mean, stream);
+                                     a_idx, a_cnt, a_cap, m_idx, m_cnt, m_pages, m_cap, mean,
+                                     (char *)ws + attn_workspace_bytes(kv.batch, hq, kv.hkv, kv.d, block, p_cap), stream);
         if (e != hipSuccess) return e;
         e = launch_attn(kv, q, hq, block, p_idx, p_cnt, p_pages, p_cap, scale, acc, l, m, nullptr, false, ws, stream);
         if (e != hipSuccess) return e;

@@ -7,9 +7,9 @@
 namespace prr {
 
 size_t layer_step_workspace_bytes(int batch, int hq, int hkv, int d, int block, int p_cap, int m_cap, int nmax,
-                                  int topk) {
+                                  int topk, bool f32) {
     const size_t units = (size_t)batch * hkv;
-    return select_spec_workspace_bytes(batch, hq, hkv, d, block, p_cap, nmax, topk) +
+    return select_spec_workspace_bytes(batch, hq, hkv, d, block, p_cap, nmax, topk, f32) +
            layer_extra_m_ws(batch, hq, hkv, d, block, m_cap) + units * 4 * kReadyStride + 256;
 }
 
@@ -18,7 +18,8 @@ hipError_t launch_layer_step(const KvDesc &kv, const void *q, int hq, const void
                              int32_t *a_idx, int32_t *a_cnt, int a_cap, int32_t *m_idx, int32_t *m_cnt, int32_t *m_pages, int m_cap,
                              float scale, float *acc, float *l, float *m, float *out, void *ws, bool mean,
                              const PredictArgs *pred, hipStream_t stream) {
-    void *mws = (char *)ws + select_spec_workspace_bytes(kv.batch, hq, kv.hkv, kv.d, block, p_cap, nmax, topk);
+    void *mws = (char *)ws + select_spec_workspace_bytes(kv.batch, hq, kv.hkv, kv.d, block, p_cap, nmax, topk,
+                                                         !kv.bf16 && !kv.fp8);
     if (kv.fp8)
         return launch_layer_step_fp8(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_pages, p_cap, scores, a_idx,
                                      a_cnt, a_cap, m_idx, m_cnt, m_pages, m_cap, scale, acc, l, m, out, ws, mws, mean, pred,

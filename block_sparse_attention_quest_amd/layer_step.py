@@ -116,6 +116,7 @@ class PRRLayer:
         self.state = bd.AttnState.empty(B, num_q_heads, d, dev)
         self.out = torch.zeros((B, num_q_heads, d), dtype=torch.float32, device=dev)
         self.ws_spec = bd.select_spec_workspace_for(kv, num_q_heads, block, topk, self.max_budget)
+        self.ws_select = bd.select_workspace_for(kv, block, topk, score_mode)   # separate selection (long rows)
         self.ws_repair = bd.workspace_for(kv, num_q_heads, block, max(1, topk))
         # the layer step in one launch (prr_layer_step), or select_spec then repair
         self.fused = bool(fused)
@@ -229,7 +230,7 @@ class PRRLayer:
         e_ready.record(crit)
         side.wait_event(e_ready)
         bd.select(q, self.kv, self.meta, self.block, self.topk, P=P, scores=self.scores, A=self.A, M=self.M,
-                  mode=self.score_mode, stream=crit)
+                  mode=self.score_mode, stream=crit, ws=self.ws_select)
         e_sel.record(crit)
         if timers and timers.select_end:
             timers.select_end.record(crit)

@@ -180,23 +180,35 @@ prr_status prr_append(const prr_kv_cache *kv, int32_t block, const void *k_new, 
  *   M = A \ P (ascending) when P is given.
  * With mode PRR_SCORE_MEAN, meta holds block means (prr_build_mean_meta) and scores[b][kvh][p] =
  * sum_i qbar_i mean_{p,i}, with the same qbar, order and precision.
- * P may be NULL (then M must be NULL).  A->cap and M->cap must be >= topk.  N_b must not exceed
- * 32768.  q: [batch][num_q_heads][head_dim], device, dtype of the cache (bf16 for fp8). */
+ * P may be NULL (then M must be NULL).  A->cap and M->cap must be >= topk.  q: [batch][num_q_heads]
+ * [head_dim], device, dtype of the cache (bf16 for fp8).
+ * Row length: prr_max_blocks(kv, block) up to 131072 blocks (2M tokens at block 16).  Without a
+ * workspace (ws NULL) one workgroup per (b, kvh) ranks the row, up to 32768 blocks.  With ws
+ * (prr_select_workspace_bytes(kv, mode, block, topk) of caller memory, zeroed once like an attention
+ * workspace; every call leaves it ready for the next), rows of more than 8192 blocks are ranked in three
+ * part-parallel stages: each scoring workgroup keeps its blocks' local top-K, groups of parts keep theirs,
+ * then one ranking per (b, kvh).  The result is the same exact top-K either way.  Rows above 32768 blocks
+ * need ws (PRR_EWORKSPACE without it); a non-NULL ws smaller than the query gives PRR_EWORKSPACE.  The
+ * query is 0 for rows of up to 8192 blocks and for shapes with more candidates than the stages rank
+ * (large topk at long rows; those give PRR_EUNSUPPORTED above 32768 blocks). */
+size_t prr_select_workspace_bytes(const prr_kv_cache *kv, prr_score_mode mode, int32_t block, int32_t topk);
+
 prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv, const void *meta,
                       prr_score_mode mode, int32_t block, int32_t topk, const prr_block_set *P, double *scores,
-                      prr_block_set *A, prr_block_set *M, hipStream_t stream);
+                      prr_block_set *A, prr_block_set *M, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Selection and the speculative pass over P together (the overlap of [paper] §1, Figure 1 flow, and §3:
  * speculation over P runs concurrently with selection; the two only read P).  Computes what
- *     prr_select(q, num_q_heads, kv, meta, block, topk, P, scores, A, M) and
+ *     prr_select(q, num_q_heads, kv, meta, block, topk, P, scores, A, M, ...) and
  *     prr_spec_attn(q, num_q_heads, kv, block, P, scale, out, ws, ws_bytes)
  * compute, as one grid whose workgroups do either part (bf16 caches; fp32 caches run the two calls in
  * turn), followed by the top-K on the same stream.  scores, A and M are the same bit for bit.  The state
  * is too while the scoring workgroups (ceil(N_max / 512) per (sequence, kv head)) number at most the
  * GPU's compute units; with more of them the speculative pass is cut into fewer, longer chunks so that the
  * whole grid is resident at once, and the state then differs from prr_spec_attn's by rounding only (the
- * order of the sums changes).  P and M must be non-NULL; A->cap and M->cap >= topk;
- * N_b <= 32768.  ws: prr_select_spec_workspace_bytes(kv, num_q_heads, block, topk, P->cap): the attention
+ * order of the sums changes).  P and M must be non-NULL; A->cap and M->cap >= topk; rows as for
+ * prr_select (up to 131072 blocks; rows above 32768 blocks, and any row whose candidate slots exceed
+ * what one ranking holds, finish the top-K in launches after the grid).  ws: prr_select_spec_workspace_bytes(kv, num_q_heads, block, topk, P->cap): the attention
  * workspace of prr_spec_attn plus room for top-K candidates and a work counter (zeroed once like an
  * attention workspace; every call leaves it ready for the next). */
 size_t prr_select_spec_workspace_bytes(const prr_kv_cache *kv, int32_t num_q_heads, int32_t block, int32_t topk,
@@ -215,7 +227,8 @@ prr_status prr_select_spec(const void *q, int32_t num_q_heads, const prr_kv_cach
  * live = N_b and P_next = the `budget` blocks with the largest level + gamma trend (ties to the smaller
  * index), ascending.  All arithmetic fp64 in the order written, no fused multiply-add.
  * scores, level, trend: [batch][num_kv_heads][max_blocks] fp64, device; live [batch][num_kv_heads]
- * int32 (zero for a fresh sequence).  P_next->cap >= budget.  max_blocks <= 32768.
+ * int32 (zero for a fresh sequence).  P_next->cap >= budget.  max_blocks <= 131072; rows above 32768
+ * blocks need ws (PRR_EWORKSPACE without it; PRR_EUNSUPPORTED for budgets with no part-parallel plan).
  * ws (may be NULL): prr_predict_workspace_bytes of caller memory, zeroed once like an attention workspace
  * (every call leaves it ready for the next).  With it, rows of more than 2048 blocks are updated by
  * 512-block parts in parallel and P_next is ranked from the parts' local top-|P| candidates (exact, as
@@ -274,8 +287,8 @@ prr_status prr_select_spec_predict(const void *q, int32_t num_q_heads, const prr
  * scores, A and M bit for bit; state (fp32, written, not read) = the attention state over P u M, and out
  * (nullable, [batch][num_q_heads][head_dim] fp32) = acc / l, within float32 rounding of those two calls
  * (the partial states merge in another grouping).  With a bf16 or fp8 cache and a top-K that finishes inside
- * the launch (up to 4096 candidate slots per row: every workload here except rows of 32768 blocks at
- * K = 256), it is one launch: the repair of a (sequence, kv head) starts as soon as its M is known, while
+ * the launch (rows of up to 32768 blocks with up to 4096 candidate slots: 512-block parts times
+ * min(K, 512); e.g. not 32768 blocks at K = 256), it is one launch: the repair of a (sequence, kv head) starts as soon as its M is known, while
  * other units still stream their speculative tiles, and the speculative and repair partial states merge
  * once.  Otherwise it runs the two calls' launches.  Arguments as for prr_select_spec_predict (pred may be
  * NULL).  ws: prr_layer_step_workspace_bytes(kv, num_q_heads, block, topk, P->cap, M->cap), zeroed once

@@ -98,9 +98,9 @@ def test_select_and_predict_argument_errors(lib):
     A = _set(64)
     P = _set(64)
     M = _set(64)
-    sel = lambda topk=64, A=A, P=P, M=M, meta=1, kv=kv, block=64, mode=0: lib.prr_select(
+    sel = lambda topk=64, A=A, P=P, M=M, meta=1, kv=kv, block=64, mode=0, ws=None, wsb=0: lib.prr_select(
         1, 32, ctypes.byref(kv), meta, mode, block, topk, ctypes.byref(P) if P else None, 1, ctypes.byref(A),
-        ctypes.byref(M) if M else None, None)
+        ctypes.byref(M) if M else None, ws, wsb, None)
     assert sel(meta=None) == 1
     assert sel(mode=2) == 1                       # unknown score mode
     assert sel(mode=-1) == 1
@@ -108,7 +108,13 @@ def test_select_and_predict_argument_errors(lib):
     assert sel(topk=-1) == 1
     assert sel(M=None) == 1                       # P without M
     assert sel(M=_set(10)) == 1
-    assert sel(kv=_kv(max_pages=65536), block=16) == 2   # more than 32768 blocks per sequence
+    # rows above 32768 blocks are ranked in part-parallel stages that need the workspace
+    long_kv = _kv(max_pages=65536)
+    need_sel = lib.prr_select_workspace_bytes(ctypes.byref(long_kv), 0, 16, 64)
+    assert need_sel > 0
+    assert sel(kv=long_kv, block=16) == 3
+    assert sel(kv=long_kv, block=16, ws=1, wsb=need_sel - 1) == 3
+    assert sel(kv=_kv(max_pages=131073), block=16) == 2   # more than 131072 blocks per sequence
     pred = lambda budget=64, nmax=2048, P=P, ws=None, wsb=0, kv=None: lib.prr_predict(
         1, 1, 2, 8, 64, nmax, 0.6, 0.3, 0.5, budget, 1, 1, 1, ctypes.byref(P) if P else None,
         ctypes.byref(kv) if kv else None, ws, wsb, None)
@@ -138,7 +144,9 @@ def test_select_and_predict_argument_errors(lib):
         (stage1 + 255) // 256 * 256 + units * 7 * 400 * 12 + units * 7 * 4
     assert lib.prr_predict_workspace_bytes(1, 8, 32768, 513) == 0
     assert pred(nmax=8192, ws=1, wsb=need - 1) == 3
-    assert pred(nmax=40000) == 2
+    assert pred(nmax=40000) == 3                  # a row above 32768 blocks needs the workspace
+    assert pred(nmax=140000) == 2                 # above 131072 blocks
+    assert pred(nmax=65536, budget=513, P=_set(600)) == 2   # 128 parts of 512 candidates: no plan
     assert lib.prr_build_meta(ctypes.byref(kv), 64, None, None) == 1
     assert lib.prr_build_meta(ctypes.byref(_kv(max_pages=10)), 64, 1, None) == 1   # 160 tokens % 64
     assert lib.prr_build_mean_meta(ctypes.byref(kv), 64, None, None) == 1
@@ -191,7 +199,8 @@ def test_select_spec_argument_errors(lib):
     assert call(ws=None) == 3
     assert call(wsb=need - 1) == 3
     assert call(block=24) == 1
-    assert call(kv=_kv(max_pages=65536), block=16, wsb=lib.prr_attn_workspace_bytes(2, 32, 8, 128, 16, 64)) == 2
+    assert call(kv=_kv(max_pages=65536), block=16, wsb=lib.prr_attn_workspace_bytes(2, 32, 8, 128, 16, 64)) == 3
+    assert call(kv=_kv(max_pages=131073), block=16) == 2
 
 
 def test_append_argument_errors(lib):
@@ -240,7 +249,8 @@ def test_select_spec_predict_argument_errors(lib):
     assert call(pred(budget=65)) == 1                 # P_next cap too small
     assert call(pred(budget=-1)) == 1
     assert call(pred(batch=0)) == 1
-    assert call(pred(max_blocks=40000)) == 2
+    assert call(pred(max_blocks=40000)) == 3          # a long row's predictor needs its workspace
+    assert call(pred(max_blocks=140000)) == 2
     # shared buffers
     assert call(pred(scores=scores)) == 1
     assert call(pred(level=scores)) == 1
@@ -272,3 +282,40 @@ def test_select_spec_workspace_for_three_stage_rows(lib):
     two = parts2 * 256 * 12 + parts2 * 4
     need_short = lib.prr_select_spec_workspace_bytes(ctypes.byref(short_kv), 32, 16, 256, 256)
     assert need_short == attn(short_kv) + (two + 255) // 256 * 256 + 256
+
+
+def _stage_bytes(units, nparts, kl, ng, kl2):
+    """The three-stage top-K's memory: part candidates (12 bytes a slot, 4 a count), group candidates,
+    one group arrival counter per unit, each rounded up to 256 bytes."""
+    up = lambda x: (x + 255) // 256 * 256
+    return up(units * nparts * (kl * 12 + 4)) + up(units * ng * (kl2 * 12 + 4)) + up(units * 4)
+
+
+def test_select_workspace_for_long_rows(lib):
+    """prr_select uses a workspace for rows above 8192 blocks (and needs one above 32768).  Each scoring
+    workgroup's part
+    (512 blocks with bf16 queries or block means, 256 with fp32 min/max) keeps min(K, part) candidates;
+    groups of up to 2048 candidate slots (at most 256 parts) keep K each; then one ranking of the groups'
+    candidates, which must fit 4096 slots."""
+    assert lib.prr_select_workspace_bytes(ctypes.byref(_kv(max_pages=8192)), 0, 16, 64) == 0
+    # 16384 blocks: optional (the stages are faster with few units); 32 parts, one group of 2048 slots
+    assert lib.prr_select_workspace_bytes(ctypes.byref(_kv(max_pages=16384)), 0, 16, 64) == _stage_bytes(16, 32, 64, 1, 64)
+    kv = _kv(max_pages=65536)              # 65536 blocks of 16 tokens, 2 x 8 units
+    # bf16: 128 parts of 64 candidates, groups of 32 parts -> 4 groups of 64
+    assert lib.prr_select_workspace_bytes(ctypes.byref(kv), 0, 16, 64) == _stage_bytes(16, 128, 64, 4, 64)
+    # fp32 min/max: 256 parts of 256 blocks
+    kv32 = _kv(max_pages=65536, dtype=bd.PRR_F32)
+    assert lib.prr_select_workspace_bytes(ctypes.byref(kv32), 0, 16, 64) == _stage_bytes(16, 256, 64, 8, 64)
+    # fp32 block means: parts of 512 again
+    assert lib.prr_select_workspace_bytes(ctypes.byref(kv32), 1, 16, 64) == _stage_bytes(16, 128, 64, 4, 64)
+    # K = 256: groups of 8 parts (2048 slots), 16 groups of 256 -> 4096 slots in the ranking
+    assert lib.prr_select_workspace_bytes(ctypes.byref(kv), 0, 16, 256) == _stage_bytes(16, 128, 256, 16, 256)
+    # 131072 blocks at K = 256: groups of 2048 slots would leave 32 x 256 to rank, so groups of 16 parts
+    kv2m = _kv(max_pages=131072, batch=1, num_kv_heads=2)
+    assert lib.prr_select_workspace_bytes(ctypes.byref(kv2m), 0, 16, 256) == _stage_bytes(2, 256, 256, 16, 256)
+    # K = 512 at 65536 blocks: 16 groups of 512 is more than one ranking holds: no plan, no workspace
+    assert lib.prr_select_workspace_bytes(ctypes.byref(kv), 0, 16, 512) == 0
+    A = _set(512)
+    assert lib.prr_select(1, 32, ctypes.byref(kv), 1, 0, 16, 512, None, 1, ctypes.byref(A), None, 1, 1 << 30,
+                          None) == 2
+
