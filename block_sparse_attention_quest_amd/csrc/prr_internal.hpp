@@ -129,11 +129,12 @@ SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean);
 SelectSpecPlan stage_plan(int nmax, int topk, int bpw, bool force_three);
 
 // Where a three-stage top-K keeps its data, from base: the parts' candidates (nparts per unit; keys,
-// then indices, then counts), the groups' (same layout), then one group arrival counter per unit, each
-// 256-byte aligned.  bytes: the whole.
+// then indices, then counts), the groups' (same layout), one group arrival counter per unit, then (for a
+// fused launch that runs the stages itself) one part arrival counter per group, each 256-byte aligned.
+// bytes: the whole.
 struct StageLayout {
     char *cand1, *cand2;
-    uint32_t *garr;
+    uint32_t *garr, *parr;
     size_t bytes;
 };
 inline StageLayout stage_layout(char *base, int units, int nparts, const SelectSpecPlan &pl) {
@@ -141,11 +142,13 @@ inline StageLayout stage_layout(char *base, int units, int nparts, const SelectS
     const size_t parts = (size_t)units * nparts, groups = (size_t)units * pl.ng;
     const size_t b1 = align(parts * pl.kl * 12 + parts * 4);
     const size_t b2 = align(groups * pl.kl2 * 12 + groups * 4);
+    const size_t b3 = align((size_t)units * 4);
     StageLayout l;
     l.cand1 = base;
     l.cand2 = base + b1;
     l.garr = (uint32_t *)(base + b1 + b2);
-    l.bytes = b1 + b2 + align((size_t)units * 4);
+    l.parr = (uint32_t *)(base + b1 + b2 + b3);
+    l.bytes = b1 + b2 + b3 + align(groups * 4);
     return l;
 }
 

@@ -610,6 +610,16 @@ struct CandParams {
     int kl;
 };
 
+// The middle and final stages of a three-stage top-K inside a fused launch: the group candidates (c2:
+// [units][ng][kl2]), one part-arrival counter per (unit, group) and one group-arrival counter per unit
+// (zero at rest; the last arriver resets its counter), groups of gp parts.
+struct GroupParams {
+    CandParams c2;
+    uint32_t *part_arr;    // [units][ng]
+    uint32_t *group_arr;   // [units]
+    int gp, ng;
+};
+
 // Stage 1: the local top-kl of the workgroup's blocks [first_block, first_block + 256 BPL) (lane t holds
 // blocks first_block + BPL t + e with scores kept[e]); n_local of them exist.  Writes the candidates and
 // their count with device-scope stores.

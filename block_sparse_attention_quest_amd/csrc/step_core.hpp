@@ -55,10 +55,13 @@ namespace {
 // REP (the layer step as one launch): n_rep repair slots follow the speculative workgroups, every unit's
 // speculative chunks and repair slots end in one merge over P u M (attn_core.hpp: FusedParams), and the
 // top-K stores M with device-scope stores and then raises the unit's flag the repair slots wait for.
-template <int KT, int D, int KPT, bool TWO, bool MEAN, bool PRED, bool REP = false>
+// K2, K3 (non-zero with TWO and KPT = 0): the three-stage top-K runs inside the launch too.  The last part
+// of a group to arrive keeps the group's top-K (K2 candidate slots per thread), and the last group of a
+// unit ranks the groups' candidates (K3 slots per thread) into A and M.
+template <int KT, int D, int KPT, bool TWO, bool MEAN, bool PRED, bool REP = false, int K2 = 0, int K3 = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void select_spec_kernel(
-    AttnParams ap, ScoreParams sp, TopkParams tp, CandParams cp, PredictParams pp, uint32_t *arrivals,
-    uint32_t *pred_ctr, int n_score, int nsx, int n_spec, int n_pred, FusedParams fp, int n_rep) {
+    AttnParams ap, ScoreParams sp, TopkParams tp, CandParams cp, GroupParams gq, PredictParams pp,
+    uint32_t *arrivals, uint32_t *pred_ctr, int n_score, int nsx, int n_spec, int n_pred, FusedParams fp, int n_rep) {
     if ((int)blockIdx.x >= n_score) {
         if constexpr (REP) {
             __shared__ AttnSmem<D> asm_;
@@ -85,6 +88,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
         const size_t part = (size_t)u * nsx + bx;
         local_candidates<BPL>(kept, n_local, cp.kl, bx * BPW, cp.key + part * cp.kl, cp.idx + part * cp.kl,
                               cp.cnt + part, sm);
+    }
+    if constexpr (K2 != 0) {
+        static_assert(TWO && KPT == 0, "the in-launch groups follow part-local candidates");
+        __shared__ int s_last_part, s_last_group;
+        const int g = bx / gq.gp, p0 = g * gq.gp;
+        const int gparts = min(gq.gp, nsx - p0);
+        // this part's candidate stores are complete before its arrival is counted
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        uint32_t *pa = &gq.part_arr[(size_t)u * gq.ng + g];
+        if (threadIdx.x == 0) {
+            const uint32_t prev = __hip_atomic_fetch_add(pa, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last_part = prev == (uint32_t)(gparts - 1);
+            if (s_last_part) __hip_atomic_store(pa, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (s_last_part) {
+            const size_t in = (size_t)u * nsx + p0, out = (size_t)u * gq.ng + g;
+            group_candidates<K2>(cp.key + in * cp.kl, cp.idx + in * cp.kl, cp.cnt + in, gparts, cp.kl, gq.c2.kl,
+                                 gq.c2.key + out * gq.c2.kl, gq.c2.idx + out * gq.c2.kl, gq.c2.cnt + out);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                const uint32_t prev = __hip_atomic_fetch_add(&gq.group_arr[u], 1u, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT);
+                s_last_group = prev == (uint32_t)(gq.ng - 1);
+                if (s_last_group) __hip_atomic_store(&gq.group_arr[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+            if (s_last_group) {
+                const size_t g0 = (size_t)u * gq.ng;
+                topk_candidates_body<K3, REP, kMaxSelectN>(tp, u, gq.c2.key + g0 * gq.c2.kl, gq.c2.idx + g0 * gq.c2.kl,
+                                                           gq.c2.cnt + g0, gq.ng, gq.c2.kl);
+                if constexpr (REP) {
+                    // M's device-scope stores are complete before the unit's repair slots may read it
+                    __builtin_amdgcn_s_waitcnt(0);
+                    __syncthreads();
+                    if (threadIdx.x == 0) __hip_atomic_store(&fp.ready[u * kReadyStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
     }
     if constexpr (KPT != 0) {
         __shared__ int s_last;
@@ -135,6 +179,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 // block means (two per lane either way).
 inline int select_spec_score_bpw(bool mean) { return score_bpw(true, mean); }
 
+// Candidate slots per thread of a fused launch's in-launch groups (K2) and final ranking (K3), encoded
+// as K2 * 100 + K3: the instantiated pairs (8, 4), (8, 8), (8, 16) and (16, 16) cover every plan, a
+// ranking of fewer slots taking the next width up.  0: the stages do not run inside the launch (no three
+// stages, or more scoring workgroups than are resident at once: a part that ran a group's stage would
+// hold its slot while other parts wait for one).
+inline int three_stage_kpt(const SelectSpecPlan &pl, long n_score_wgs) {
+    if (!pl.three || n_score_wgs > 2L * device_cu_count()) return 0;
+    const int k3 = pl.kpt3 <= 4 ? 4 : pl.kpt3;
+    return pl.kpt2 <= 8 ? 800 + k3 : 1616;
+}
+
 // Everything a fused launch needs besides its kernel: the parameters of its roles, its grid, and where the
 // top-K stages after it (if any) keep their candidates.  Shared by the selection + speculation launch and
 // the layer-step launch (which adds the repair slots).
@@ -143,6 +198,8 @@ struct FusedSetup {
     ScoreParams sp;
     TopkParams tp;
     CandParams cp;
+    GroupParams gq;   // the in-launch groups of a three-stage top-K (plan.three)
+    int k23;          // three_stage_kpt: the in-launch stages' widths, 0 if they run after the launch
     PredictParams pp;
     SelectSpecPlan plan;
     uint32_t *arrivals;
@@ -235,6 +292,20 @@ inline FusedSetup fused_setup(const KvDesc &kv, const void *q, int hq, const voi
     f.cp.key = (uint64_t *)f.cbase;
     f.cp.idx = (int32_t *)(f.cbase + (size_t)f.units * f.nsx * f.plan.kl * 8);
     f.cp.cnt = (int32_t *)(f.cbase + (size_t)f.units * f.nsx * f.plan.kl * 12);
+    f.gq = GroupParams{};
+    f.k23 = three_stage_kpt(f.plan, (long)f.nsx * f.units);
+    if (f.plan.three) {
+        const StageLayout sl = stage_layout(f.cbase, f.units, f.nsx, f.plan);
+        const size_t s2 = (size_t)f.units * f.plan.ng * f.plan.kl2;
+        f.gq.c2.key = (uint64_t *)sl.cand2;
+        f.gq.c2.idx = (int32_t *)(sl.cand2 + s2 * 8);
+        f.gq.c2.cnt = (int32_t *)(sl.cand2 + s2 * 12);
+        f.gq.c2.kl = f.plan.kl2;
+        f.gq.part_arr = sl.parr;
+        f.gq.group_arr = sl.garr;
+        f.gq.gp = f.plan.gp;
+        f.gq.ng = f.plan.ng;
+    }
     return f;
 }
 
@@ -243,10 +314,11 @@ inline hipError_t fused_after(const FusedSetup &f, const KvDesc &kv, int block, 
                               const int32_t *p_idx, const int32_t *p_cnt, const int32_t *p_pages, int p_cap, int32_t *a_idx, int32_t *a_cnt,
                               int a_cap, int32_t *m_idx, int32_t *m_cnt, int32_t *m_pages, int m_cap, hipStream_t stream) {
     if (f.plan.three) {
+        if (f.k23) return hipSuccess;   // the groups and the ranking ran inside the launch
         // the parts' candidates are in place; groups of them, then the unit's ranking
         const StageLayout sl = stage_layout(f.cbase, f.units, f.nsx, f.plan);
-        return launch_topk_groups(kv, block, nmax, topk, p_idx, p_cnt, p_cap, a_idx, a_cnt, nullptr, a_cap, m_idx, m_cnt, m_pages, m_cap,
-                                  f.plan, f.nsx, sl.cand1, sl.cand2, sl.garr, stream);
+        return launch_topk_groups(kv, block, nmax, topk, p_idx, p_cnt, p_cap, a_idx, a_cnt, nullptr, a_cap, m_idx, m_cnt,
+                                  m_pages, m_cap, f.plan, f.nsx, sl.cand1, sl.cand2, sl.garr, stream);
     }
     if (f.plan.kpt == 0)
         return launch_topk(kv, block, nmax, topk, scores, p_idx, p_cnt, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt, m_pages, m_cap,
@@ -283,18 +355,22 @@ hipError_t launch_select_spec_t(const KvDesc &kv, const void *q, int hq, const v
     if (f.grid > 0x7fffffffL) return hipErrorInvalidValue;
     const int kpt = f.plan.kpt;
     const bool two = f.plan.two;
+    const int k23 = f.k23;
     const FusedParams none{};
-#define PRR_SS(DD, K, T, MN, PR)                                                                           \
-    if (kv.d == DD && kpt == K && two == T && mean == MN && f.fuse_pred == PR) {                            \
-        PRR_LAUNCH(select_spec_kernel<KT, DD, K, T, MN, PR>, dim3((int)f.grid), dim3(256), stream, f.ap, f.sp, f.tp, \
-                   f.cp, f.pp, f.arrivals, f.pred_ctr, f.nsx * f.units, f.nsx, f.n_spec, f.n_pred, none, 0);      \
+#define PRR_SS(DD, K, T, MN, PR, K2, K3)                                                                   \
+    if (kv.d == DD && kpt == K && two == T && mean == MN && f.fuse_pred == PR && k23 == K2 * 100 + K3) {    \
+        PRR_LAUNCH((select_spec_kernel<KT, DD, K, T, MN, PR, false, K2, K3>), dim3((int)f.grid), dim3(256), stream, \
+                   f.ap, f.sp, f.tp, f.cp, f.gq, f.pp, f.arrivals, f.pred_ctr, f.nsx * f.units, f.nsx, f.n_spec,  \
+                   f.n_pred, none, 0);                                                                      \
     } else
 #define PRR_SS_K(DD, MN, PR)                                                                                \
-    PRR_SS(DD, 0, false, MN, PR) PRR_SS(DD, 0, true, MN, PR) PRR_SS(DD, 1, false, MN, PR)                     \
-    PRR_SS(DD, 2, false, MN, PR)                                                                            \
-    PRR_SS(DD, 4, false, MN, PR) PRR_SS(DD, 8, false, MN, PR) PRR_SS(DD, 1, true, MN, PR)                     \
-    PRR_SS(DD, 2, true, MN, PR) PRR_SS(DD, 4, true, MN, PR) PRR_SS(DD, 8, true, MN, PR)                       \
-    PRR_SS(DD, 16, true, MN, PR)
+    PRR_SS(DD, 0, false, MN, PR, 0, 0) PRR_SS(DD, 0, true, MN, PR, 0, 0)                                     \
+    PRR_SS(DD, 0, true, MN, PR, 8, 4) PRR_SS(DD, 0, true, MN, PR, 8, 8) PRR_SS(DD, 0, true, MN, PR, 8, 16)    \
+    PRR_SS(DD, 0, true, MN, PR, 16, 16)                                                                     \
+    PRR_SS(DD, 1, false, MN, PR, 0, 0) PRR_SS(DD, 2, false, MN, PR, 0, 0)                                          \
+    PRR_SS(DD, 4, false, MN, PR, 0, 0) PRR_SS(DD, 8, false, MN, PR, 0, 0) PRR_SS(DD, 1, true, MN, PR, 0, 0)           \
+    PRR_SS(DD, 2, true, MN, PR, 0, 0) PRR_SS(DD, 4, true, MN, PR, 0, 0) PRR_SS(DD, 8, true, MN, PR, 0, 0)             \
+    PRR_SS(DD, 16, true, MN, PR, 0, 0)
 #define PRR_SS_ALL(MN, PR) PRR_SS_K(128, MN, PR) PRR_SS_K(64, MN, PR)
     PRR_SS_ALL(false, false) PRR_SS_ALL(true, false) PRR_SS_ALL(false, true) PRR_SS_ALL(true, true)
     { return hipErrorInvalidValue; }
@@ -330,7 +406,9 @@ hipError_t launch_layer_step_t(const KvDesc &kv, const void *q, int hq, const vo
     uint32_t *ready = (uint32_t *)((char *)mws + mbytes);
     uint32_t *status = (uint32_t *)((char *)mws + mbytes + (size_t)units * 4 * kReadyStride);
     const SelectSpecPlan plan = select_spec_plan(nmax, topk, mean);
-    if (KT == kKtF32 || plan.three || plan.kpt == 0) {
+    const int bpw = select_spec_score_bpw(mean);
+    const long n_score_wgs = (long)((nmax + bpw - 1) / bpw) * units;
+    if (KT == kKtF32 || (plan.kpt == 0 && !plan.three) || (plan.three && three_stage_kpt(plan, n_score_wgs) == 0)) {
         hipError_t e = launch_select_spec(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_pages, p_cap, scores,
                                           a_idx, a_cnt, a_cap, m_idx, m_cnt, m_pages, m_cap, scale, acc, l, m, ws, mean, pred,
                                           stream);
@@ -353,16 +431,19 @@ hipError_t launch_layer_step_t(const KvDesc &kv, const void *q, int hq, const vo
     if (grid > 0x7fffffffL) return hipErrorInvalidValue;
     const int kpt = plan.kpt;
     const bool two = plan.two;
-#define PRR_LS(DD, K, T, MN, PR)                                                                           \
-    if (kv.d == DD && kpt == K && two == T && mean == MN && f.fuse_pred == PR) {                            \
-        PRR_LAUNCH(select_spec_kernel<KT, DD, K, T, MN, PR, true>, dim3((int)grid), dim3(256), stream, f.ap, f.sp,   \
-                   f.tp, f.cp, f.pp, f.arrivals, f.pred_ctr, f.nsx * f.units, f.nsx, f.n_spec, f.n_pred, fp,       \
-                   (int)n_rep);                                                                            \
+    const int k23 = f.k23;
+#define PRR_LS(DD, K, T, MN, PR, K2, K3)                                                                   \
+    if (kv.d == DD && kpt == K && two == T && mean == MN && f.fuse_pred == PR && k23 == K2 * 100 + K3) {    \
+        PRR_LAUNCH((select_spec_kernel<KT, DD, K, T, MN, PR, true, K2, K3>), dim3((int)grid), dim3(256), stream, \
+                   f.ap, f.sp, f.tp, f.cp, f.gq, f.pp, f.arrivals, f.pred_ctr, f.nsx * f.units, f.nsx, f.n_spec,  \
+                   f.n_pred, fp, (int)n_rep);                                                               \
     } else
 #define PRR_LS_K(DD, MN, PR)                                                                                \
-    PRR_LS(DD, 1, false, MN, PR) PRR_LS(DD, 2, false, MN, PR) PRR_LS(DD, 4, false, MN, PR)                    \
-    PRR_LS(DD, 1, true, MN, PR) PRR_LS(DD, 2, true, MN, PR) PRR_LS(DD, 4, true, MN, PR)                       \
-    PRR_LS(DD, 8, true, MN, PR) PRR_LS(DD, 16, true, MN, PR)
+    PRR_LS(DD, 1, false, MN, PR, 0, 0) PRR_LS(DD, 2, false, MN, PR, 0, 0) PRR_LS(DD, 4, false, MN, PR, 0, 0)  \
+    PRR_LS(DD, 1, true, MN, PR, 0, 0) PRR_LS(DD, 2, true, MN, PR, 0, 0) PRR_LS(DD, 4, true, MN, PR, 0, 0)     \
+    PRR_LS(DD, 8, true, MN, PR, 0, 0) PRR_LS(DD, 16, true, MN, PR, 0, 0)                                    \
+    PRR_LS(DD, 0, true, MN, PR, 8, 4) PRR_LS(DD, 0, true, MN, PR, 8, 8) PRR_LS(DD, 0, true, MN, PR, 8, 16)    \
+    PRR_LS(DD, 0, true, MN, PR, 16, 16)
 #define PRR_LS_ALL(MN, PR) PRR_LS_K(128, MN, PR) PRR_LS_K(64, MN, PR)
     PRR_LS_ALL(false, false) PRR_LS_ALL(true, false) PRR_LS_ALL(false, true) PRR_LS_ALL(true, true)
     { return hipErrorInvalidValue; }

@@ -287,10 +287,11 @@ prr_status prr_select_spec_predict(const void *q, int32_t num_q_heads, const prr
  * scores, A and M bit for bit; state (fp32, written, not read) = the attention state over P u M, and out
  * (nullable, [batch][num_q_heads][head_dim] fp32) = acc / l, within float32 rounding of those two calls
  * (the partial states merge in another grouping).  With a bf16 or fp8 cache and a top-K that finishes inside
- * the launch (rows of up to 32768 blocks with up to 4096 candidate slots: 512-block parts times
- * min(K, 512); e.g. not 32768 blocks at K = 256), it is one launch: the repair of a (sequence, kv head) starts as soon as its M is known, while
- * other units still stream their speculative tiles, and the speculative and repair partial states merge
- * once.  Otherwise it runs the two calls' launches.  Arguments as for prr_select_spec_predict (pred may be
+ * the launch (rows of up to 4096 candidate slots, 512-block parts times min(K, 512); longer ones when the
+ * launch's scoring workgroups, ceil(N_max / 512) per (sequence, kv head), number at most twice the
+ * GPU's compute units), it is one launch: the repair of a (sequence, kv head) starts as soon as its M is
+ * known, while other units still stream their speculative tiles, and the speculative and repair partial
+ * states merge once.  Otherwise it runs the two calls' launches.  Arguments as for prr_select_spec_predict (pred may be
  * NULL).  ws: prr_layer_step_workspace_bytes(kv, num_q_heads, block, topk, P->cap, M->cap), zeroed once
  * like an attention workspace; every call leaves it ready for the next.  In the one-launch form a repair
  * workgroup waits for its unit's M with a bounded wait; the 32-bit word at the start of the workspace's

@@ -275,7 +275,7 @@ def test_select_spec_workspace_for_three_stage_rows(lib):
     stage1 = parts1 * 256 * 12 + parts1 * 4
     groups = units * 8
     three = (stage1 + 255) // 256 * 256 + (groups * 256 * 12 + groups * 4 + 255) // 256 * 256 \
-        + (units * 4 + 255) // 256 * 256
+        + (units * 4 + 255) // 256 * 256 + (groups * 4 + 255) // 256 * 256
     need_long = lib.prr_select_spec_workspace_bytes(ctypes.byref(long_kv), 32, 16, 256, 256)
     assert need_long == attn(long_kv) + (three + 255) // 256 * 256 + 256
     parts2 = units * 16
@@ -286,9 +286,10 @@ def test_select_spec_workspace_for_three_stage_rows(lib):
 
 def _stage_bytes(units, nparts, kl, ng, kl2):
     """The three-stage top-K's memory: part candidates (12 bytes a slot, 4 a count), group candidates,
-    one group arrival counter per unit, each rounded up to 256 bytes."""
+    one group arrival counter per unit, one part arrival counter per group, each rounded up to 256
+    bytes."""
     up = lambda x: (x + 255) // 256 * 256
-    return up(units * nparts * (kl * 12 + 4)) + up(units * ng * (kl2 * 12 + 4)) + up(units * 4)
+    return up(units * nparts * (kl * 12 + 4)) + up(units * ng * (kl2 * 12 + 4)) + up(units * 4) + up(units * ng * 4)
 
 
 def test_select_workspace_for_long_rows(lib):

@@ -173,17 +173,20 @@ def test_layer_step_with_many_units():
                 assert abs(float(got.l[b, hq]) - st.l) <= 1e-4 * st.l
 
 
-def test_layer_step_three_stage_rows_fall_back_to_the_calls():
-    """Rows of 32768 blocks at K = 256 are ranked in three stages, the last after the launch: the layer
-    step then runs the calls' launches, bit for bit."""
-    lens = [32768 * 16]
-    w = wl.Workload("three_ls", 1, 8, 2, 64, lens[0], 16, 256, "bf16", seed=91, seq_lens=lens)
+@pytest.mark.parametrize("blocks,topk,dt", [(32768, 256, "bf16"), (32768, 400, "fp8"), (20000, 300, "bf16")],
+                         ids=["32768_k256", "32768_k400_fp8", "20000_k300"])
+def test_layer_step_three_stage_rows_in_one_launch(blocks, topk, dt):
+    """Rows with more candidate slots than one ranking holds (512-block parts of min(K, 512) candidates
+    each, more than 4096 in all) are ranked in three stages, all inside the launch: the last part of each
+    group keeps the group's top-K and the last group ranks the unit.  Scores, A and M equal the separate
+    calls' bit for bit, and the state is the oracle's over P u M."""
+    lens = [blocks * 16, blocks * 16 - 1000]
+    w = wl.Workload("three_ls", 2, 8, 2, 64, lens[0], 16, topk, dt, seed=91 + topk, seq_lens=lens)
     inp = wl.make_inputs(w, "cuda")
     rng = np.random.default_rng(6)
-    P = _random_p(w, rng, [200, 256])
-    (_, A, M, ref, ref_out), (got, got_out) = _run_both(w, inp, P, w.topk, 256)
-    for x, y in ((ref.acc, got.acc), (ref.l, got.l), (ref.m, got.m), (ref_out, got_out)):
-        assert torch.equal(x, y)
+    P = _random_p(w, rng, [200, topk, 0, 37])
+    (_, A, M, ref, ref_out), (got, got_out) = _run_both(w, inp, P, w.topk, topk)
+    _check_against_oracle(w, inp, P, A.lists(), M.lists(), got, got_out, ref)
 
 
 def test_layer_step_carrying_a_predictor_step():
