@@ -180,7 +180,7 @@ def kernel_role(name: str):
         return "layer_step" if len(targs) >= 7 and targs[6].strip() == "true" else "select_spec"
     # calibration first: its per-row ranking kernel is also a top-K kernel
     for key, role in (("rows_topk_kernel", "calibration: rows' true top-K"), ("ema_chain_kernel", "calibration: EMA chain"),
-                      ("replay_kernel", "calibration: replay"), ("score_kernel", "score"),
+                      ("replay_kernel", "calibration: replay"), ("score_kernel", "score"), ("score_parts_kernel", "score"),
                       ("topk_groups_kernel", "topk_groups"), ("topk_kernel", "topk"), ("predict", "predict"),
                       ("summary_kernel", "meta"), ("meta_kernel", "meta"), ("append", "append")):
         if key in name:
