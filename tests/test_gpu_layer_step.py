@@ -224,3 +224,49 @@ def test_layer_step_carrying_a_predictor_step():
     for x, y in ((a[0], b[0]), (a[3].acc, b[3].acc), (a[3].l, b[3].l), (a[3].m, b[3].m), (a[4], b[4]), (a[5], b[5]),
                  (a[6], b[6]), (a[7], b[7])):
         assert torch.equal(x, y)
+
+
+def test_layer_step_three_stage_mean_scoring_carrying_a_predictor():
+    """The three in-launch ranking stages with block-mean scoring and another layer's predictor step in
+    the same launch (32768 blocks, K = 256): scores, A, M, the predictor's state and P_next equal the
+    separate calls' bit for bit, and the state theirs within the float32 tolerance (it merges the
+    partial states in another grouping)."""
+    w = wl.Workload("three_mean_pred", 1, 8, 2, 128, 32768 * 16, 16, 256, "bf16", seed=77)
+    inp = wl.make_inputs(w, "cuda")
+    dkv = device_kv(inp)
+    means = bd.build_mean_meta(dkv, w.block)
+    rng = np.random.default_rng(12)
+    Pd = sets_to_device(_random_p(w, rng, [256, 100]), 256)
+    B, H, N = w.batch, w.num_kv_heads, bd.max_blocks(dkv, w.block)
+    other = torch.from_numpy(rng.standard_normal((B, H, N))).cuda()
+    lv0 = torch.from_numpy(rng.standard_normal((B, H, N))).cuda()
+    tr0 = torch.from_numpy(rng.standard_normal((B, H, N))).cuda()
+    live0 = torch.full((B, H), N - 300, dtype=torch.int32, device="cuda")
+    q = inp.q[0]
+
+    lv, tr, live = lv0.clone(), tr0.clone(), live0.clone()
+    Pn = bd.BlockSet.empty(B, H, 64)
+    args = bd.PredictArgs(other, dkv.seq_len, w.block, 0.6, 0.3, 0.5, 64, lv, tr, live, Pn,
+                          ws=bd.predict_workspace_for(B, H, N, 64))
+    st = bd.AttnState.empty(B, w.num_q_heads, w.head_dim)
+    out = torch.empty_like(st.acc)
+    sc = torch.zeros((B, H, N), dtype=torch.float64, device="cuda")
+    A, M = bd.BlockSet.empty(B, H, w.topk), bd.BlockSet.empty(B, H, w.topk)
+    bd.layer_step(q, dkv, means, w.block, w.topk, Pd, w.scale, sc, A, M, st, out=out, mode="mean", pred=args)
+
+    lv2, tr2, live2 = lv0.clone(), tr0.clone(), live0.clone()
+    scores, A2, M2 = bd.select(q, dkv, means, w.block, w.topk, P=Pd, mode="mean")
+    ref = bd.spec_attn(q, dkv, w.block, Pd, w.scale)
+    bd.repair(q, dkv, w.block, M2, w.scale, ref)
+    Pn2 = bd.predict(other, dkv.seq_len, w.block, 0.6, 0.3, 0.5, 64, lv2, tr2, live2,
+                     ws=bd.predict_workspace_for(B, H, N, 64))
+    torch.cuda.synchronize()
+    assert torch.equal(sc, scores) and A.lists() == A2.lists() and M.lists() == M2.lists()
+    assert Pn.lists() == Pn2.lists()
+    assert torch.equal(lv, lv2) and torch.equal(tr, tr2) and torch.equal(live, live2)
+    acc, l, m = (t.double().cpu().numpy() for t in (st.acc, st.l, st.m))
+    racc, rl, rm = (t.double().cpu().numpy() for t in (ref.acc, ref.l, ref.m))
+    assert np.all(rl > 0)
+    assert np.all(np.abs(l - rl) <= 1e-4 * rl)
+    assert np.all(np.abs(m - rm) <= 1e-4 * np.maximum(1.0, np.abs(rm)))
+    assert np.max(np.abs(acc / l[..., None] - racc / rl[..., None])) <= 5e-3

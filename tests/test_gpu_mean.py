@@ -32,8 +32,11 @@ CASES = [
     ("bf16_d128_s16_two_stage", 1, 8, 2, 128, 16, [40000], "bf16", 300, None),
     ("fp8_d128_s32", 2, 8, 2, 128, 32, [9000, 4100], "fp8", 32, None),
     # 8192 blocks at K = 600: more candidate slots than one ranking holds, so groups of parts rank
-    # their candidates after the fused launch (three-stage top-K)
+    # their candidates, inside the fused launch (three-stage top-K)
     ("bf16_d64_s16_three_stage", 1, 4, 1, 64, 16, [131072], "bf16", 600, None),
+    # 32768 blocks at K = 400: groups of 10 parts (4000 slots) and a ranking of 7 x 400, both at 16
+    # candidate slots per thread, inside the launch
+    ("bf16_d128_s16_three_stage_k400", 1, 4, 1, 128, 16, [1 << 19], "bf16", 400, None),
 ]
 
 
