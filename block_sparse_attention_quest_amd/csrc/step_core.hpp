@@ -26,7 +26,10 @@
 //     candidates of all workgroups of the unit (up to 16 per thread; the selection is exact, see
 //     select_core.hpp).  At 2048 blocks and K = 64 the last workgroup ranks 256 candidates instead of
 //     2048 scores;
-// otherwise (more candidates than that) the separate top-K kernel follows the launch.
+//   * with more candidates than one ranking holds, in three stages: the last part of each group of parts
+//     keeps the group's top-K and the unit's last group ranks the groups' candidates (K2, K3 below), as
+//     long as all scoring workgroups are resident at once; otherwise the launch keeps the parts'
+//     candidates and the groups kernel follows it.
 //
 // Predictor step of another layer.  In a stack of layers the predictor of layer l needs only layer l's
 // scores and is off the critical path ([paper] §1, §4.1), so layer l + 1's launch can carry it.  The
