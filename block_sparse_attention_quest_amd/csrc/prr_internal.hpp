@@ -120,8 +120,13 @@ struct SelectSpecPlan {
     // thread) and the unit's last group ranks the ng kl2 group candidates (kpt3 slots per thread).
     bool three;
     int gp, ng, kl2, kpt2, kpt3;
+    int bpw;   // blocks per scoring workgroup (score_bpw: 1024 for wide bf16 min/max scoring)
 };
 SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean);
+
+// The staged plan of launch_select for rows of more than kStagedSelectMin blocks (three stages; wide
+// scoring parts for bf16 min/max rows of kWideScoreBlocks and more where they have a plan).
+SelectSpecPlan select_stage_plan(int nmax, int topk, bool bq, bool mean);
 
 // The plan for parts of bpw blocks.  force_three: the three stages even where two would do, for a top-K
 // that ranks in launches of its own (rows longer than kMaxTwoStageBlocks, whose P bitmap only those

@@ -181,15 +181,14 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
 
 // First stage of a three-stage top-K over rows longer than one top-K workgroup holds: workgroup bx of
 // unit u scores its 256 BPL blocks and keeps their local top-kl as candidates (stages two and three in
-// topk_groups_kernel).
-template <bool BF16, int D, bool MEAN>
+// topk_groups_kernel).  BPL: kScoreBPL, or kWideScoreBPL for the bf16 min/max parts of long rows.
+template <bool BF16, int D, bool MEAN, int BPL = kScoreBPL<BF16, MEAN>>
 __global__ __launch_bounds__(256) void score_parts_kernel(ScoreParams p, CandParams cp, int nsx) {
     __shared__ TopkSmem<4> sm;
-    constexpr int BPL = kScoreBPL<BF16, MEAN>;
     constexpr int BPW = 256 * BPL;
     const int bx = blockIdx.x, u = blockIdx.y;
     double kept[BPL] = {};
-    score_body<BF16, D, false, MEAN>(p, bx, u, kept);
+    score_body<BF16, D, false, MEAN, BPL>(p, bx, u, kept);
     const int b = u / p.hkv;
     const int nb = min((max(p.seq_len[b], 0) + p.block - 1) / p.block, p.nmax);
     const int n_local = min(max(nb - bx * BPW, 0), BPW);
@@ -354,10 +353,10 @@ hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *me
     sp.stride = stride;
     sp.nmax = nmax;
     const bool bq = kv.bf16 || kv.fp8;   // bf16 queries (and bf16 min/max metadata)
-    const int bpw = score_bpw(bq, mean);
-    const dim3 sgrid((nmax + bpw - 1) / bpw, units);
-    const SelectSpecPlan plan = ws && nmax > kStagedSelectMin ? stage_plan(nmax, topk, bpw, true) : SelectSpecPlan{};
+    const SelectSpecPlan plan = ws && nmax > kStagedSelectMin ? select_stage_plan(nmax, topk, bq, mean) : SelectSpecPlan{};
     if (nmax > kMaxRowTopK && !plan.three) return hipErrorInvalidValue;
+    const int bpw = plan.three ? plan.bpw : score_bpw(bq, mean);
+    const dim3 sgrid((nmax + bpw - 1) / bpw, units);
     if (plan.three) {
         // three stages: the scoring workgroups keep their parts' candidates, then groups and the ranking
         const int nsx = (int)sgrid.x;
@@ -367,6 +366,10 @@ hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *me
         cp.idx = (int32_t *)(sl.cand1 + (size_t)units * nsx * plan.kl * 8);
         cp.cnt = (int32_t *)(sl.cand1 + (size_t)units * nsx * plan.kl * 12);
         cp.kl = plan.kl;
+        const bool wide = plan.bpw == score_bpw(true, false, true);
+        if (wide && kv.d == 128) PRR_LAUNCH((score_parts_kernel<true, 128, false, kWideScoreBPL>), dim3(sgrid), dim3(256), stream, sp, cp, nsx);
+        else if (wide && kv.d == 64) PRR_LAUNCH((score_parts_kernel<true, 64, false, kWideScoreBPL>), dim3(sgrid), dim3(256), stream, sp, cp, nsx);
+        else
 #define PRR_SP(BQ, DD, MN)                                                                                   \
         if (bq == BQ && kv.d == DD && mean == MN) PRR_LAUNCH((score_parts_kernel<BQ, DD, MN>), dim3(sgrid), dim3(256), stream, sp, cp, nsx); \
         else

@@ -316,15 +316,26 @@ struct ScoreParams {
 template <bool BF16, bool MEAN = false>
 constexpr int kScoreBPL = (BF16 || MEAN) ? 2 : 1;
 
-// Blocks per scoring workgroup (256 lanes of kScoreBPL blocks), on the host.
-constexpr int score_bpw(bool bq, bool mean) { return 256 * ((bq || mean) ? 2 : 1); }
+// Rows of at least this many blocks (512K tokens at block 16) score bf16 min/max metadata four blocks per
+// lane (one 8-byte load per channel) when their top-K takes three stages either way: half as many
+// scoring workgroups, so that the scoring grid of a long row leaves room for the rest of a fused launch
+// (or is resident at all).  Rows that fill the chip at two blocks per lane lose by it (fewer workgroups
+// for the same bytes), so shorter rows keep two.
+constexpr int kWideScoreBlocks = 32768;
+constexpr int kWideScoreBPL = 4;
+
+// Blocks per scoring workgroup (256 lanes of kScoreBPL blocks, or kWideScoreBPL), on the host.
+constexpr int score_bpw(bool bq, bool mean, bool wide = false) {
+    return 256 * (wide ? kWideScoreBPL : (bq || mean) ? 2 : 1);
+}
 
 // Scores blocks [256 BPL bx, 256 BPL (bx + 1)) of unit u (BPL consecutive blocks per lane).  COHERENT:
 // the scores are stored with device-scope stores, for a reader on another XCD within the same launch.
-template <bool BF16, int D, bool COHERENT = false, bool MEAN = false>
-__device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u,
-                                           double (&kept)[kScoreBPL<BF16, MEAN>]) {
-    constexpr int BPL = kScoreBPL<BF16, MEAN>;
+// BPL: kScoreBPL, or kWideScoreBPL for bf16 min/max metadata.
+template <bool BF16, int D, bool COHERENT = false, bool MEAN = false, int BPL = kScoreBPL<BF16, MEAN>>
+__device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u, double (&kept)[BPL]) {
+    static_assert(BPL == kScoreBPL<BF16, MEAN> || (BF16 && !MEAN && BPL == kWideScoreBPL),
+                  "four blocks per lane: bf16 min/max metadata only");
     __shared__ double s_qbar[D];
     __shared__ int s_row[D];             // metadata row of channel i: 1 (max) when qbar_i >= 0, else 0 (min)
     const int b = u / p.hkv, kvh = u - b * p.hkv;
@@ -381,6 +392,33 @@ __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u,
                 acc[0] = dadd(acc[0], dmul(qb, (double)__uint_as_float(lo[j])));
                 acc[1] = dadd(acc[1], dmul(qb, (double)__uint_as_float(hi[j])));
                 asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));
+                if (j % 16 == 15) __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    } else if constexpr (BPL == kWideScoreBPL) {
+        // bf16 min/max, four blocks per lane: blocks p0 .. p0 + 3 of one row are 8 adjacent bytes (8-byte
+        // aligned: p0 is a multiple of 4 and the row stride of 8).  Channels in two halves, each loaded
+        // before it is used, so that the loaded words take D registers as in the other layouts.
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            uint32_t lo[D / 2], hi[D / 2];
+#pragma unroll
+            for (int j = 0; j < D / 2; ++j) {
+                const int i = half * D / 2 + j;
+                const int sgn = __builtin_amdgcn_readfirstlane(s_row[i]);
+                const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, (2 * i + sgn) * p.stride * ES, 0);
+                lo[j] = v[0];
+                hi[j] = v[1];
+            }
+#pragma unroll
+            for (int j = 0; j < D / 2; ++j) {
+                const double qb = s_qbar[half * D / 2 + j];
+#pragma unroll
+                for (int e = 0; e < BPL; ++e) {
+                    const uint32_t w = e < 2 ? lo[j] : hi[j];
+                    acc[e] = dadd(acc[e], dmul(qb, (double)bf16_to_f32((uint16_t)(w >> (16 * (e & 1))))));
+                }
+                asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
                 if (j % 16 == 15) __builtin_amdgcn_sched_barrier(0);
             }
         }

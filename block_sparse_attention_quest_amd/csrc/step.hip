@@ -13,6 +13,7 @@ namespace prr {
 // the unit's last workgroup ranks 256 candidates instead of 2048 scores.
 SelectSpecPlan stage_plan(int nmax, int topk, int bpw, bool force_three) {
     SelectSpecPlan pl = {};
+    pl.bpw = bpw;
     pl.two = false;
     pl.kl = 0;
     pl.kpt = force_three ? 0 : nmax <= 256 ? 1 : nmax <= 512 ? 2 : nmax <= 1024 ? 4 : 0;
@@ -58,10 +59,25 @@ SelectSpecPlan stage_plan(int nmax, int topk, int bpw, bool force_three) {
     return pl;
 }
 
-// The fused launch ranks a unit inside the launch only for rows whose P bitmap it holds
-// (kMaxTwoStageBlocks); longer rows take the three stages, the last two in launches of their own.
+// The fused launch ranks a unit in two stages only for rows whose P bitmap one ranking holds
+// (kMaxTwoStageBlocks); longer rows take the three stages (inside the launch when its scoring workgroups
+// are resident, else the last two in launches of their own).  Rows of kWideScoreBlocks and more score
+// four blocks per lane where that plan takes three stages too.
 SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean) {
-    return stage_plan(nmax, topk, select_spec_score_bpw(mean), nmax > kMaxTwoStageBlocks);
+    const bool force = nmax > kMaxTwoStageBlocks;
+    if (!mean && nmax >= kWideScoreBlocks) {
+        const SelectSpecPlan wide = stage_plan(nmax, topk, score_bpw(true, false, true), force);
+        if (wide.three) return wide;
+    }
+    return stage_plan(nmax, topk, score_bpw(true, mean), force);
+}
+
+SelectSpecPlan select_stage_plan(int nmax, int topk, bool bq, bool mean) {
+    if (bq && !mean && nmax >= kWideScoreBlocks) {
+        const SelectSpecPlan wide = stage_plan(nmax, topk, score_bpw(true, false, true), true);
+        if (wide.three) return wide;
+    }
+    return stage_plan(nmax, topk, score_bpw(bq, mean), true);
 }
 
 // Candidate slots of the two-stage top-K: [units][nsx][kl] keys (8 bytes) and indices (4), [units][nsx]
@@ -70,8 +86,7 @@ SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean) {
 static size_t candidate_bytes(int units, int nmax, int topk, bool mean) {
     const SelectSpecPlan pl = select_spec_plan(nmax, topk, mean);
     if (!pl.two) return 0;
-    const int bpw = select_spec_score_bpw(mean);
-    const int nparts = (nmax + bpw - 1) / bpw;
+    const int nparts = (nmax + pl.bpw - 1) / pl.bpw;
     if (pl.three) return stage_layout(nullptr, units, nparts, pl).bytes;
     const size_t parts = (size_t)units * nparts;
     return parts * pl.kl * 12 + parts * 4;
@@ -79,13 +94,12 @@ static size_t candidate_bytes(int units, int nmax, int topk, bool mean) {
 
 size_t select_workspace_bytes(int units, int nmax, int topk, bool bq, bool mean) {
     if (nmax <= kStagedSelectMin) return 0;
-    const int bpw = score_bpw(bq, mean);
-    const SelectSpecPlan pl = stage_plan(nmax, topk, bpw, true);
-    return pl.three ? stage_layout(nullptr, units, (nmax + bpw - 1) / bpw, pl).bytes : 0;
+    const SelectSpecPlan pl = select_stage_plan(nmax, topk, bq, mean);
+    return pl.three ? stage_layout(nullptr, units, (nmax + pl.bpw - 1) / pl.bpw, pl).bytes : 0;
 }
 
 bool select_supported(int nmax, int topk, bool bq, bool mean) {
-    return nmax <= kMaxRowTopK || (nmax <= kMaxSelectN && stage_plan(nmax, topk, score_bpw(bq, mean), true).three);
+    return nmax <= kMaxRowTopK || (nmax <= kMaxSelectN && select_stage_plan(nmax, topk, bq, mean).three);
 }
 
 // The carried predictor's work counter sits after the candidates, in a 256-byte slot of its own.  For an

@@ -47,7 +47,8 @@ namespace prr {
 namespace {
 
 // Workgroup s < nsx * units scores blocks [BPW (s mod nsx), +BPW) of unit s / nsx (BPW = 512 blocks, two
-// per lane, for bf16 min/max metadata and for fp32 block means: MEAN) and, if it is the unit's last to finish and
+// per lane, for bf16 min/max metadata and for fp32 block means: MEAN; 1024, four per lane, for the bf16
+// min/max parts of long rows: WIDE) and, if it is the unit's last to finish and
 // KPT > 0, runs the unit's top-K (KPT keys per thread, 256 KPT >= the unit's block count); the remaining
 // n_spec workgroups run the speculative pass.  PRED: the scoring workgroups then draw the n_pred units
 // of another layer's predictor step from *pred_ctr (8 keys per thread: rows of up to 2048 blocks); every
@@ -61,7 +62,8 @@ namespace {
 // K2, K3 (non-zero with TWO and KPT = 0): the three-stage top-K runs inside the launch too.  The last part
 // of a group to arrive keeps the group's top-K (K2 candidate slots per thread), and the last group of a
 // unit ranks the groups' candidates (K3 slots per thread) into A and M.
-template <int KT, int D, int KPT, bool TWO, bool MEAN, bool PRED, bool REP = false, int K2 = 0, int K3 = 0>
+template <int KT, int D, int KPT, bool TWO, bool MEAN, bool PRED, bool REP = false, int K2 = 0, int K3 = 0,
+          bool WIDE = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void select_spec_kernel(
     AttnParams ap, ScoreParams sp, TopkParams tp, CandParams cp, GroupParams gq, PredictParams pp,
     uint32_t *arrivals, uint32_t *pred_ctr, int n_score, int nsx, int n_spec, int n_pred, FusedParams fp, int n_rep) {
@@ -79,9 +81,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     const int s = (int)blockIdx.x;
     const int u = s / nsx;
     const int bx = s - u * nsx;
-    constexpr int BPL = kScoreBPL<true, MEAN>;
+    static_assert(!WIDE || (TWO && !MEAN), "wide scoring parts: bf16 min/max rows of a staged top-K");
+    constexpr int BPL = WIDE ? kWideScoreBPL : kScoreBPL<true, MEAN>;
     double kept[BPL] = {};
-    score_body<true, D, KPT != 0 && !TWO, MEAN>(sp, bx, u, kept);
+    score_body<true, D, KPT != 0 && !TWO, MEAN, BPL>(sp, bx, u, kept);
     if constexpr (TWO) {
         __shared__ TopkSmem<4> sm;
         constexpr int BPW = 256 * BPL;   // blocks per scoring workgroup
@@ -178,10 +181,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 }
 
 
-// Blocks per scoring workgroup of the fused launch (bf16 queries): 512 for min/max metadata, 512 for
-// block means (two per lane either way).
-inline int select_spec_score_bpw(bool mean) { return score_bpw(true, mean); }
-
 // Candidate slots per thread of a fused launch's in-launch groups (K2) and final ranking (K3), encoded
 // as K2 * 100 + K3: the instantiated pairs (8, 4), (8, 8), (8, 16) and (16, 16) cover every plan, a
 // ranking of fewer slots taking the next width up.  0: the stages do not run inside the launch (no three
@@ -224,7 +223,8 @@ inline FusedSetup fused_setup(const KvDesc &kv, const void *q, int hq, const voi
     // tokens), the speculative pass is spread over the slots that are left, so that the whole grid is
     // resident from the start instead of speculative workgroups waiting for scoring ones to finish.
     const int cus = device_cu_count();
-    const int bpw = select_spec_score_bpw(mean);
+    f.plan = select_spec_plan(nmax, topk, mean);
+    const int bpw = f.plan.bpw;
     const int n_score_wgs = (nmax + bpw - 1) / bpw * kv.batch * kv.hkv;
     const int spec_target = n_score_wgs > cus ? std::max(cus / 2, 2 * cus - n_score_wgs) : cus;
     f.n_spec = attn_setup(f.ap, kv, q, hq, block, p_idx, p_cnt, p_pages, p_cap, scale, acc, l, m, out, false, ws, spec_target);
@@ -262,7 +262,8 @@ inline FusedSetup fused_setup(const KvDesc &kv, const void *q, int hq, const voi
     f.units = kv.batch * kv.hkv;
     f.arrivals = (uint32_t *)ws + f.units;   // the scoring-arrival counters of the workspace
     f.nsx = (nmax + bpw - 1) / bpw;
-    f.fuse_pred = pred && pred->nmax <= kMaxFusedPredictN;
+    // (a launch with wide scoring parts leaves a carried predictor to its own launch: no instantiation)
+    f.fuse_pred = pred && pred->nmax <= kMaxFusedPredictN && f.plan.bpw != score_bpw(true, false, true);
     f.pp = PredictParams{};
     f.n_pred = 0;
     if (f.fuse_pred) {
@@ -289,7 +290,6 @@ inline FusedSetup fused_setup(const KvDesc &kv, const void *q, int hq, const voi
     }
     f.grid = (long)f.n_spec + (long)f.nsx * f.units;
     f.pred_ctr = (uint32_t *)((char *)ws + pred_counter_offset(kv.batch, hq, kv.hkv, kv.d, block, p_cap, nmax, topk, false));
-    f.plan = select_spec_plan(nmax, topk, mean);
     f.cp.kl = f.plan.kl;
     f.cbase = (char *)ws + attn_workspace_bytes(kv.batch, hq, kv.hkv, kv.d, block, p_cap);
     f.cp.key = (uint64_t *)f.cbase;
@@ -359,13 +359,21 @@ hipError_t launch_select_spec_t(const KvDesc &kv, const void *q, int hq, const v
     const int kpt = f.plan.kpt;
     const bool two = f.plan.two;
     const int k23 = f.k23;
+    const bool wide = f.plan.bpw == score_bpw(true, false, true);
     const FusedParams none{};
-#define PRR_SS(DD, K, T, MN, PR, K2, K3)                                                                   \
-    if (kv.d == DD && kpt == K && two == T && mean == MN && f.fuse_pred == PR && k23 == K2 * 100 + K3) {    \
-        PRR_LAUNCH((select_spec_kernel<KT, DD, K, T, MN, PR, false, K2, K3>), dim3((int)f.grid), dim3(256), stream, \
+#define PRR_SSW(DD, K, T, MN, PR, K2, K3, W)                                                               \
+    if (kv.d == DD && kpt == K && two == T && mean == MN && f.fuse_pred == PR && k23 == K2 * 100 + K3 &&   \
+        wide == W) {                                                                                        \
+        PRR_LAUNCH((select_spec_kernel<KT, DD, K, T, MN, PR, false, K2, K3, W>), dim3((int)f.grid), dim3(256), stream, \
                    f.ap, f.sp, f.tp, f.cp, f.gq, f.pp, f.arrivals, f.pred_ctr, f.nsx * f.units, f.nsx, f.n_spec,  \
                    f.n_pred, none, 0);                                                                      \
     } else
+#define PRR_SS(DD, K, T, MN, PR, K2, K3) PRR_SSW(DD, K, T, MN, PR, K2, K3, false)
+// wide scoring parts: bf16 min/max rows of three stages; a carried predictor runs as its own launch
+#define PRR_SS_WIDE(DD)                                                                                     \
+    PRR_SSW(DD, 0, true, false, false, 0, 0, true) PRR_SSW(DD, 0, true, false, false, 8, 4, true)            \
+    PRR_SSW(DD, 0, true, false, false, 8, 8, true) PRR_SSW(DD, 0, true, false, false, 8, 16, true)           \
+    PRR_SSW(DD, 0, true, false, false, 16, 16, true)
 #define PRR_SS_K(DD, MN, PR)                                                                                \
     PRR_SS(DD, 0, false, MN, PR, 0, 0) PRR_SS(DD, 0, true, MN, PR, 0, 0)                                     \
     PRR_SS(DD, 0, true, MN, PR, 8, 4) PRR_SS(DD, 0, true, MN, PR, 8, 8) PRR_SS(DD, 0, true, MN, PR, 8, 16)    \
@@ -375,11 +383,14 @@ hipError_t launch_select_spec_t(const KvDesc &kv, const void *q, int hq, const v
     PRR_SS(DD, 2, true, MN, PR, 0, 0) PRR_SS(DD, 4, true, MN, PR, 0, 0) PRR_SS(DD, 8, true, MN, PR, 0, 0)             \
     PRR_SS(DD, 16, true, MN, PR, 0, 0)
 #define PRR_SS_ALL(MN, PR) PRR_SS_K(128, MN, PR) PRR_SS_K(64, MN, PR)
+    PRR_SS_WIDE(128) PRR_SS_WIDE(64)
     PRR_SS_ALL(false, false) PRR_SS_ALL(true, false) PRR_SS_ALL(false, true) PRR_SS_ALL(true, true)
     { return hipErrorInvalidValue; }
 #undef PRR_SS_ALL
 #undef PRR_SS_K
+#undef PRR_SS_WIDE
 #undef PRR_SS
+#undef PRR_SSW
     hipError_t e = fused_after(f, kv, block, nmax, topk, scores, p_idx, p_cnt, p_pages, p_cap, a_idx, a_cnt, a_cap, m_idx, m_cnt,
                                m_pages, m_cap, stream);
     if (e != hipSuccess) return e;
@@ -409,7 +420,7 @@ hipError_t launch_layer_step_t(const KvDesc &kv, const void *q, int hq, const vo
     uint32_t *ready = (uint32_t *)((char *)mws + mbytes);
     uint32_t *status = (uint32_t *)((char *)mws + mbytes + (size_t)units * 4 * kReadyStride);
     const SelectSpecPlan plan = select_spec_plan(nmax, topk, mean);
-    const int bpw = select_spec_score_bpw(mean);
+    const int bpw = plan.bpw;
     const long n_score_wgs = (long)((nmax + bpw - 1) / bpw) * units;
     if (KT == kKtF32 || (plan.kpt == 0 && !plan.three) || (plan.three && three_stage_kpt(plan, n_score_wgs) == 0)) {
         hipError_t e = launch_select_spec(kv, q, hq, meta, block, stride, nmax, topk, p_idx, p_cnt, p_pages, p_cap, scores,
@@ -435,12 +446,18 @@ hipError_t launch_layer_step_t(const KvDesc &kv, const void *q, int hq, const vo
     const int kpt = plan.kpt;
     const bool two = plan.two;
     const int k23 = f.k23;
-#define PRR_LS(DD, K, T, MN, PR, K2, K3)                                                                   \
-    if (kv.d == DD && kpt == K && two == T && mean == MN && f.fuse_pred == PR && k23 == K2 * 100 + K3) {    \
-        PRR_LAUNCH((select_spec_kernel<KT, DD, K, T, MN, PR, true, K2, K3>), dim3((int)grid), dim3(256), stream, \
+    const bool wide = plan.bpw == score_bpw(true, false, true);
+#define PRR_LSW(DD, K, T, MN, PR, K2, K3, W)                                                               \
+    if (kv.d == DD && kpt == K && two == T && mean == MN && f.fuse_pred == PR && k23 == K2 * 100 + K3 &&   \
+        wide == W) {                                                                                        \
+        PRR_LAUNCH((select_spec_kernel<KT, DD, K, T, MN, PR, true, K2, K3, W>), dim3((int)grid), dim3(256), stream, \
                    f.ap, f.sp, f.tp, f.cp, f.gq, f.pp, f.arrivals, f.pred_ctr, f.nsx * f.units, f.nsx, f.n_spec,  \
                    f.n_pred, fp, (int)n_rep);                                                               \
     } else
+#define PRR_LS(DD, K, T, MN, PR, K2, K3) PRR_LSW(DD, K, T, MN, PR, K2, K3, false)
+#define PRR_LS_WIDE(DD)                                                                                     \
+    PRR_LSW(DD, 0, true, false, false, 8, 4, true) PRR_LSW(DD, 0, true, false, false, 8, 8, true)            \
+    PRR_LSW(DD, 0, true, false, false, 8, 16, true) PRR_LSW(DD, 0, true, false, false, 16, 16, true)
 #define PRR_LS_K(DD, MN, PR)                                                                                \
     PRR_LS(DD, 1, false, MN, PR, 0, 0) PRR_LS(DD, 2, false, MN, PR, 0, 0) PRR_LS(DD, 4, false, MN, PR, 0, 0)  \
     PRR_LS(DD, 1, true, MN, PR, 0, 0) PRR_LS(DD, 2, true, MN, PR, 0, 0) PRR_LS(DD, 4, true, MN, PR, 0, 0)     \
@@ -448,11 +465,14 @@ hipError_t launch_layer_step_t(const KvDesc &kv, const void *q, int hq, const vo
     PRR_LS(DD, 0, true, MN, PR, 8, 4) PRR_LS(DD, 0, true, MN, PR, 8, 8) PRR_LS(DD, 0, true, MN, PR, 8, 16)    \
     PRR_LS(DD, 0, true, MN, PR, 16, 16)
 #define PRR_LS_ALL(MN, PR) PRR_LS_K(128, MN, PR) PRR_LS_K(64, MN, PR)
+    PRR_LS_WIDE(128) PRR_LS_WIDE(64)
     PRR_LS_ALL(false, false) PRR_LS_ALL(true, false) PRR_LS_ALL(false, true) PRR_LS_ALL(true, true)
     { return hipErrorInvalidValue; }
 #undef PRR_LS_ALL
 #undef PRR_LS_K
+#undef PRR_LS_WIDE
 #undef PRR_LS
+#undef PRR_LSW
     return f.fuse_pred ? hipSuccess : predict_alone(pred, stream);
     }
 }

@@ -295,28 +295,36 @@ def _stage_bytes(units, nparts, kl, ng, kl2):
 def test_select_workspace_for_long_rows(lib):
     """prr_select uses a workspace for rows above 8192 blocks (and needs one above 32768).  Each scoring
     workgroup's part
-    (512 blocks with bf16 queries or block means, 256 with fp32 min/max) keeps min(K, part) candidates;
-    groups of up to 2048 candidate slots (at most 256 parts) keep K each; then one ranking of the groups'
-    candidates, which must fit 4096 slots."""
+    (512 blocks with bf16 queries or block means, 256 with fp32 min/max, 1024 for bf16 min/max rows of
+    32768 blocks and more) keeps min(K, part) candidates; groups of up to 2048 candidate slots (at most 256
+    parts) keep K each; then one ranking of the groups' candidates, which must fit 4096 slots."""
     assert lib.prr_select_workspace_bytes(ctypes.byref(_kv(max_pages=8192)), 0, 16, 64) == 0
     # 16384 blocks: optional (the stages are faster with few units); 32 parts, one group of 2048 slots
     assert lib.prr_select_workspace_bytes(ctypes.byref(_kv(max_pages=16384)), 0, 16, 64) == _stage_bytes(16, 32, 64, 1, 64)
     kv = _kv(max_pages=65536)              # 65536 blocks of 16 tokens, 2 x 8 units
-    # bf16: 128 parts of 64 candidates, groups of 32 parts -> 4 groups of 64
-    assert lib.prr_select_workspace_bytes(ctypes.byref(kv), 0, 16, 64) == _stage_bytes(16, 128, 64, 4, 64)
+    # bf16: 64 wide parts of 64 candidates, groups of 32 parts -> 2 groups of 64
+    assert lib.prr_select_workspace_bytes(ctypes.byref(kv), 0, 16, 64) == _stage_bytes(16, 64, 64, 2, 64)
     # fp32 min/max: 256 parts of 256 blocks
     kv32 = _kv(max_pages=65536, dtype=bd.PRR_F32)
     assert lib.prr_select_workspace_bytes(ctypes.byref(kv32), 0, 16, 64) == _stage_bytes(16, 256, 64, 8, 64)
-    # fp32 block means: parts of 512 again
+    # fp32 block means: parts of 512
     assert lib.prr_select_workspace_bytes(ctypes.byref(kv32), 1, 16, 64) == _stage_bytes(16, 128, 64, 4, 64)
-    # K = 256: groups of 8 parts (2048 slots), 16 groups of 256 -> 4096 slots in the ranking
-    assert lib.prr_select_workspace_bytes(ctypes.byref(kv), 0, 16, 256) == _stage_bytes(16, 128, 256, 16, 256)
-    # 131072 blocks at K = 256: groups of 2048 slots would leave 32 x 256 to rank, so groups of 16 parts
+    # bf16 block means: parts of 512 too (wide parts are for min/max metadata only)
+    assert lib.prr_select_workspace_bytes(ctypes.byref(kv), 1, 16, 64) == _stage_bytes(16, 128, 64, 4, 64)
+    # K = 256: groups of 8 parts (2048 slots), 8 groups of 256 -> 2048 slots in the ranking
+    assert lib.prr_select_workspace_bytes(ctypes.byref(kv), 0, 16, 256) == _stage_bytes(16, 64, 256, 8, 256)
+    # 131072 blocks at K = 256: 128 wide parts, 16 groups of 8 parts -> 4096 slots in the ranking
     kv2m = _kv(max_pages=131072, batch=1, num_kv_heads=2)
-    assert lib.prr_select_workspace_bytes(ctypes.byref(kv2m), 0, 16, 256) == _stage_bytes(2, 256, 256, 16, 256)
-    # K = 512 at 65536 blocks: 16 groups of 512 is more than one ranking holds: no plan, no workspace
-    assert lib.prr_select_workspace_bytes(ctypes.byref(kv), 0, 16, 512) == 0
-    A = _set(512)
-    assert lib.prr_select(1, 32, ctypes.byref(kv), 1, 0, 16, 512, None, 1, ctypes.byref(A), None, 1, 1 << 30,
+    assert lib.prr_select_workspace_bytes(ctypes.byref(kv2m), 0, 16, 256) == _stage_bytes(2, 128, 256, 16, 256)
+    # ... with block means (parts of 512): groups of 2048 slots would leave 32 x 256 to rank, so groups
+    # of 16 parts
+    assert lib.prr_select_workspace_bytes(ctypes.byref(kv2m), 1, 16, 256) == _stage_bytes(2, 256, 256, 16, 256)
+    # K = 512 at 65536 blocks: groups of 4 wide parts would leave 16 x 512 to rank, so groups of 8 parts
+    # (4096 slots) leave 8 x 512
+    assert lib.prr_select_workspace_bytes(ctypes.byref(kv), 0, 16, 512) == _stage_bytes(16, 64, 512, 8, 512)
+    # K = 1024 at 65536 blocks: 16 groups of 1024 is more than one ranking holds: no plan, no workspace
+    assert lib.prr_select_workspace_bytes(ctypes.byref(kv), 0, 16, 1024) == 0
+    A = _set(1024)
+    assert lib.prr_select(1, 32, ctypes.byref(kv), 1, 0, 16, 1024, None, 1, ctypes.byref(A), None, 1, 1 << 30,
                           None) == 2
 

@@ -120,6 +120,67 @@ def test_long_row_select_spec_repair_layer_step(w, heads):
         _check_attention(w, u, st3, out3, set(P[0][h]) | set(m_h.tolist()), "layer step")
 
 
+# Ragged rows of 40001 and 33001 blocks at K = 512 (2 sequences, 2 kv heads): neither row is a whole
+# number of scoring parts, and K = 512 takes groups of 8 parts (K = 512 at these lengths has a plan only
+# with 1024-block parts)
+WRAG = wl.scaled(wl.C4, name="ragged_long_k512", batch=2, num_q_heads=8, num_kv_heads=2,
+                 seq_lens=[40001 * 16 - 7, 33001 * 16 - 2], topk=512, spec_hit=348, spec_miss=164, seed=44)
+
+
+def test_ragged_long_rows_k512():
+    """prr_select (staged), prr_select_spec + prr_repair and prr_layer_step on ragged rows of more than
+    32768 blocks at K = 512: scores, A and M bit for bit and the states within tolerance on a unit of each
+    sequence; the three calls agree with each other bit for bit on every unit."""
+    w = WRAG
+    assert [w.blocks_of(b) for b in range(w.batch)] == [40001, 33001]
+    _say(f"{w.name}: inputs ({w.max_blocks} blocks max, K = {w.topk})")
+    inp = wl.make_inputs(w, "cuda")
+    kv = device_kv(inp)
+    meta = bd.build_meta(kv, w.block)
+    ws = bd.select_workspace_for(kv, w.block, w.topk)
+    assert ws is not None
+    _say(f"{w.name}: prr_select")
+    scores, A, _ = bd.select(inp.q[0], kv, meta, w.block, w.topk, ws=ws)
+    torch.cuda.synchronize()
+    units = [_Unit(inp, 0, 1), _Unit(inp, 1, 0)]
+    P = [[None] * w.num_kv_heads for _ in range(w.batch)]
+    al = A.lists()
+    for b in range(w.batch):
+        for h in range(w.num_kv_heads):
+            P[b][h] = list(wl.make_spec_set(w, np.array(al[b][h]), w.blocks_of(b), w.spec_hit, w.spec_miss,
+                                            salt=10 * b + h))
+    for u in units:
+        _check_selection(w, u, scores, A)
+    Pd = sets_to_device(P, w.topk)
+    _say(f"{w.name}: prr_select_spec + prr_repair")
+    scores2, A2, M, state = bd.select_spec(inp.q[0], kv, meta, w.block, w.topk, Pd, w.scale)
+    spec_copy = state.clone()
+    out = torch.empty_like(state.acc)
+    bd.repair(inp.q[0], kv, w.block, M, w.scale, state, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(scores2, scores) and A2.lists() == A.lists()
+    for u in units:
+        p_u = P[u.b][u.h]
+        _check_selection(w, u, scores2, A2, M, p_u)
+        m_u = orc.set_minus(u.A, p_u)
+        assert len(m_u) == w.spec_miss, (u.b, u.h)
+        _check_attention(w, u, spec_copy, None, p_u, "spec")
+        _check_attention(w, u, state, out, set(p_u) | set(m_u.tolist()), "repair")
+    _say(f"{w.name}: prr_layer_step")
+    B, H = w.batch, w.num_kv_heads
+    scores3 = torch.zeros_like(scores)
+    A3, M3 = bd.BlockSet.empty(B, H, w.topk), bd.BlockSet.empty(B, H, w.topk)
+    st3 = bd.AttnState.empty(B, w.num_q_heads, w.head_dim)
+    out3 = torch.empty_like(st3.acc)
+    bd.layer_step(inp.q[0], kv, meta, w.block, w.topk, Pd, w.scale, scores3, A3, M3, st3, out=out3)
+    torch.cuda.synchronize()
+    assert torch.equal(scores3, scores2) and A3.lists() == A2.lists() and M3.lists() == M.lists()
+    for u in units:
+        p_u = P[u.b][u.h]
+        m_u = orc.set_minus(u.A, p_u)
+        _check_attention(w, u, st3, out3, set(p_u) | set(m_u.tolist()), "layer step")
+
+
 def test_long_row_mean_scoring_1m():
     """Mean-pooled scoring (block means) over 65536-block rows: means, scores and A bit for bit."""
     w = wl.scaled(W1M, num_q_heads=8, num_kv_heads=2)
