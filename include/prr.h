@@ -203,12 +203,14 @@ prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv
  *     prr_spec_attn(q, num_q_heads, kv, block, P, scale, out, ws, ws_bytes)
  * compute, as one grid whose workgroups do either part (bf16 caches; fp32 caches run the two calls in
  * turn), followed by the top-K on the same stream.  scores, A and M are the same bit for bit.  The state
- * is too while the scoring workgroups (ceil(N_max / 512) per (sequence, kv head)) number at most the
+ * is too while the scoring workgroups (ceil(N_max / 512) per (sequence, kv head); ceil(N_max / 1024) for
+ * min/max scoring of rows of 32768 blocks and more that rank in three stages) number at most the
  * GPU's compute units; with more of them the speculative pass is cut into fewer, longer chunks so that the
  * whole grid is resident at once, and the state then differs from prr_spec_attn's by rounding only (the
  * order of the sums changes).  P and M must be non-NULL; A->cap and M->cap >= topk; rows as for
  * prr_select (up to 131072 blocks; rows above 32768 blocks, and any row whose candidate slots exceed
- * what one ranking holds, finish the top-K in launches after the grid).  ws: prr_select_spec_workspace_bytes(kv, num_q_heads, block, topk, P->cap): the attention
+ * what one ranking holds, rank in three stages: inside the grid while its scoring workgroups number at
+ * most twice the compute units, else in launches after it).  ws: prr_select_spec_workspace_bytes(kv, num_q_heads, block, topk, P->cap): the attention
  * workspace of prr_spec_attn plus room for top-K candidates and a work counter (zeroed once like an
  * attention workspace; every call leaves it ready for the next). */
 size_t prr_select_spec_workspace_bytes(const prr_kv_cache *kv, int32_t num_q_heads, int32_t block, int32_t topk,
@@ -288,8 +290,8 @@ prr_status prr_select_spec_predict(const void *q, int32_t num_q_heads, const prr
  * (nullable, [batch][num_q_heads][head_dim] fp32) = acc / l, within float32 rounding of those two calls
  * (the partial states merge in another grouping).  With a bf16 or fp8 cache and a top-K that finishes inside
  * the launch (rows of up to 4096 candidate slots, 512-block parts times min(K, 512); longer ones when the
- * launch's scoring workgroups, ceil(N_max / 512) per (sequence, kv head), number at most twice the
- * GPU's compute units), it is one launch: the repair of a (sequence, kv head) starts as soon as its M is
+ * launch's scoring workgroups, ceil(N_max / 512) per (sequence, kv head) or ceil(N_max / 1024) as for
+ * prr_select_spec, number at most twice the GPU's compute units), it is one launch: the repair of a (sequence, kv head) starts as soon as its M is
  * known, while other units still stream their speculative tiles, and the speculative and repair partial
  * states merge once.  Otherwise it runs the two calls' launches.  Arguments as for prr_select_spec_predict (pred may be
  * NULL).  ws: prr_layer_step_workspace_bytes(kv, num_q_heads, block, topk, P->cap, M->cap), zeroed once
