@@ -433,10 +433,10 @@ hipError_t launch_layer_step_t(const KvDesc &kv, const void *q, int hq, const vo
                                      a_cnt, a_cap, m_idx, m_cnt, m_pages, m_cap, scale, acc, l, m, out, ws, mean, pred);
     FusedParams fp{};
     attn_setup(fp.pm, kv, q, hq, block, m_idx, m_cnt, m_pages, m_cap, scale, acc, l, m, out, true, mws);
-    // M's chunks at half prr_repair's size (at least kChunkMin pages, the size the workspace's partial
-    // slots are counted at): the repair slots start only once their unit's top-K is done, late in the
+    // M's chunks at half prr_repair's size (at least kChunkMin pages; the workspace's partial slots are
+    // counted at kChunkStep): the repair slots start only once their unit's top-K is done, late in the
     // launch, so more and shorter chunks finish sooner
-    fp.pm.cp = std::max(kChunkMin, (fp.pm.cp / 2 + kChunkMin - 1) / kChunkMin * kChunkMin);
+    fp.pm.cp = std::max(kChunkMin, (fp.pm.cp / 2 + kChunkStep - 1) / kChunkStep * kChunkStep);
     fp.pm.kmax = std::max(1, (m_cap * (block / kPage) + fp.pm.cp - 1) / fp.pm.cp);
     fp.ready = ready;
     fp.status = status;
