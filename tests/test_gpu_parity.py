@@ -307,18 +307,20 @@ def test_predictor_trajectory_bit_exact():
     assert live.cpu().numpy().tolist() == [[-(-l // w.block)] * H for l in lens]
 
 
-@pytest.mark.parametrize("nblocks,topk", [(300, 40), (900, 40), (2048, 40), (2049, 40), (4097, 40),
-                                         (8192, 128), (4096, 600), (8192, 600), (16384, 300), (32768, 400),
-                                         (32768, 512)])
+@pytest.mark.parametrize("nblocks,topk", [(300, 40), (900, 40), (1024, 40), (1025, 40), (2048, 40), (2049, 40),
+                                         (4097, 40), (8192, 128), (4096, 600), (8192, 600), (16384, 300),
+                                         (32768, 400), (32768, 512), (33000, 256)])
 def test_select_spec_fused_topk_shapes(nblocks, topk):
     """The fused launch's top-K runs in the last scoring workgroup: over all scores with 1, 2 or 4 keys
     per thread (units of up to 1024 blocks), and beyond that in two stages (local top-min(K, 512)
     candidates of every scoring workgroup, then the top-K of the candidates, up to 16 per thread; K = 600
-    caps the local candidates at 512).  With more than 4096 candidate slots (8192 blocks at K = 600,
-    16384 at K = 300) a third stage follows the launch: groups of parts (up to 2048 candidate slots) keep
-    their top-K, and the unit's last group ranks the groups' candidates; at 32768 blocks with K above 341,
-    groups of up to 4096 slots keep the last ranking within 4096 slots.  Every shape against the separate
-    calls (bit for bit) and the oracle's scores and sets."""
+    caps the local candidates at 512; 1025 blocks leave one block in the last part).  With more than 4096
+    candidate slots (8192 blocks at K = 600, 16384 at K = 300) a third stage follows: groups of parts (up
+    to 2048 candidate slots) keep their top-K, and the unit's last group ranks the groups' candidates,
+    inside the launch (its scoring workgroups are resident); rows of 32768 blocks and more score in
+    1024-block parts, and at 32768 blocks with K = 512, groups of up to 4096 slots keep the last ranking
+    within 4096 slots; 33000 blocks (above one ranking's P bitmap) leave 232 blocks in the last part.
+    Every shape against the separate calls (bit for bit) and the oracle's scores and sets."""
     lens = [nblocks * 16, nblocks * 16 - 37]
     w = wl.Workload(f"fused_{nblocks}", 2, 8, 2, 64, max(lens), 16, topk, "bf16", seed=900 + nblocks,
                     seq_lens=lens)
