@@ -9,7 +9,8 @@
 // streams costs about 10 us from the producer's end to the consumer's start, while kernels on one
 // stream follow each other about 1 us apart, so the overlap is made inside one grid instead: the first
 // workgroups score blocks (one workgroup per 512 blocks of a unit, two per lane, for min/max metadata and
-// for block means alike), the rest run the speculative chunks (the attention kernels' chunk walk over
+// for block means alike; 1024 blocks, four per lane, for the min/max metadata of rows of 32768 blocks and
+// more that rank in three stages), the rest run the speculative chunks (the attention kernels' chunk walk over
 // n_spec workgroups, on bf16 or fp8 tiles: KT).  Dispatch follows the workgroup index, so
 // the scoring workgroups issue their loads first: the memory system serves them ahead of the
 // speculative stream, selection finishes early and its top-K runs under the speculative pass, which is
@@ -21,8 +22,8 @@
 // overlaps the speculative pass:
 //   * up to 1024 blocks per unit, over all of the unit's scores (up to 4 per thread), stored and re-read
 //     with device-scope accesses, which are coherent across the XCDs' L2s;
-//   * beyond that, in two stages: every scoring workgroup first keeps the local top-min(K, 512) of its
-//     own 512 blocks as candidates (in parallel, right after scoring), and the last one ranks the
+//   * beyond that, in two stages: every scoring workgroup first keeps the local top-min(K, part) of its
+//     own part's blocks as candidates (in parallel, right after scoring), and the last one ranks the
 //     candidates of all workgroups of the unit (up to 16 per thread; the selection is exact, see
 //     select_core.hpp).  At 2048 blocks and K = 64 the last workgroup ranks 256 candidates instead of
 //     2048 scores;
