@@ -5,6 +5,8 @@ Usage:
         [--trace <kernel_trace.csv>] [--bench-log <bench.py output of the same run>]
   python -m block_sparse_attention_quest_amd.profiling hbm <fetch counter_collection.csv>
         <write counter_collection.csv> <out.md> --copy-mib N "<fetch command>" "<write command>"
+  python -m block_sparse_attention_quest_amd.profiling sq <counter_collection.csv>... <out.md>
+        --bench-log <bench.py output of the first run> "<command>"...
 
 `stats` turns rocprofv3 --kernel-trace --stats output into a short table; with the kernel trace and the
 bench.py output of the same run it also records the mean duration of the speculative-attention launches
@@ -12,7 +14,9 @@ bench.py timed alone (keyed by the attention source hash, for bench.py to report
 WRITE_SIZE (KiB per dispatch) of every speculative-attention launch, scales each counter by what it reads
 for a plain device copy of known size (the copy probe bench.py runs with --copy-probe-mib: the copy
 kernel with the largest WRITE_SIZE, matched by dispatch id in the FETCH_SIZE run), and
-records the attention source hash so that bench.py ignores the numbers once the kernel changes.
+records the attention source hash so that bench.py ignores the numbers once the kernel changes.  `sq`
+summarises SQ counter runs (wave cycles spent waiting and issuing, vector-memory reads and MFMA per wave,
+vector-memory latency) per kernel role.
 """
 from __future__ import annotations
 
@@ -221,6 +225,56 @@ def roles_table(fetch_csv: str, write_csv: str, copy_mib: int, algo: dict = None
     return out
 
 
+def _per_dispatch_all(path: str) -> dict:
+    """{dispatch id: (kernel name, {counter: value summed over instances})} for every counter of a run."""
+    out = {}
+    for r in csv.DictReader(open(path)):
+        did = int(_get(r, "Dispatch_Id", "Dispatch-Id"))
+        name = _get(r, "Kernel_Name", "Kernel-Name")
+        c = _get(r, "Counter_Name", "Counter-Name")
+        val = float(_get(r, "Counter_Value", "Counter-Value", default=0))
+        entry = out.setdefault(did, (name, {}))
+        entry[1][c] = entry[1].get(c, 0.0) + val
+    return out
+
+
+def sq_table(paths: list) -> list:
+    """Per role, medians over the launches that did work (SQ_WAVE_CYCLES at least a tenth of the role's
+    largest) of: the share of the waves' cycles spent waiting (SQ_WAIT_ANY / SQ_WAVE_CYCLES, both in
+    quad-cycles), the share spent issuing (SQ_ACTIVE_INST_ANY / SQ_WAVE_CYCLES), vector-memory reads and
+    MFMA instructions per wave, and the average vector-memory latency in cycles (VmemLatency, from its
+    own run)."""
+    per_role = {}
+    for path in paths:
+        for did, (name, cs) in _per_dispatch_all(path).items():
+            role = kernel_role(name)
+            if role is not None:
+                per_role.setdefault(role, {}).setdefault(path, []).append(cs)
+    rows = ["| kernel (role) | launches | waiting, % of wave cycles | issuing, % of wave cycles | vector-memory reads per wave | MFMA per wave | vector-memory latency, cycles |",
+            "|---|---|---|---|---|---|---|"]
+    order = ["spec", "repair", "select_spec", "layer_step", "score", "topk", "topk_groups", "predict"]
+    for role in [r for r in order if r in per_role] + [r for r in per_role if r not in order]:
+        vals = {}
+        n = 0
+        for path, lst in per_role[role].items():
+            if any("SQ_WAVE_CYCLES" in cs for cs in lst):
+                top = max(cs.get("SQ_WAVE_CYCLES", 0.0) for cs in lst)
+                lst = [cs for cs in lst if cs.get("SQ_WAVE_CYCLES", 0.0) >= 0.1 * top]
+                n = max(n, len(lst))
+            for cs in lst:
+                for k, v in cs.items():
+                    vals.setdefault(k, []).append(v)
+        med = {k: statistics.median(v) for k, v in vals.items()}
+        def share(a, b):
+            return f"{100.0 * med[a] / med[b]:.1f}" if a in med and b in med and med[b] > 0 else "-"
+        def per_wave(a):
+            return f"{med[a] / med['SQ_WAVES']:.1f}" if a in med and med.get("SQ_WAVES", 0) > 0 else "-"
+        lat = f"{med['VmemLatency']:.0f}" if "VmemLatency" in med else "-"
+        rows.append(f"| {role} | {n} | {share('SQ_WAIT_ANY', 'SQ_WAVE_CYCLES')} | {share('SQ_ACTIVE_INST_ANY', 'SQ_WAVE_CYCLES')} "
+                    f"| {per_wave('SQ_INSTS_VMEM_RD')} | {per_wave('SQ_INSTS_MFMA')} | {lat} |")
+    return rows
+
+
 def main(argv):
     if argv and argv[0] == "stats":
         _, src, out, cmd = argv[:4]
@@ -276,6 +330,24 @@ def main(argv):
         lines += ["Every kernel of the path in the same runs (same scaling; launches that did work; algorithmic "
                   "bytes from bench.py's algorithmic_bytes_per_launch of the run):", ""]
         lines += roles_table(fetch_csv, write_csv, copy_mib, d.get("algorithmic_bytes_per_launch") if d else None)
+        lines.append("")
+        open(out, "w").write("\n".join(lines))
+        print("\n".join(lines))
+    elif argv and argv[0] == "sq":
+        # sq <counters.csv>... <out.md> --bench-log <log> <commands>...
+        j = argv.index("--bench-log")
+        d = bench_line(argv[j + 1])
+        head = argv[1:j]
+        csvs, out = head[:-1], head[-1]
+        cmds = argv[j + 2:]
+        lines = [f"# Where the waves' time goes ({d['config']['workload']}; rocprofv3 --pmc, SQ counters)", "",
+                 "Per kernel role, medians over the launches that did work; the counters are summed over the "
+                 "GPU per dispatch. Waiting and issuing are shares of the waves' cycles (SQ_WAIT_ANY and "
+                 "SQ_ACTIVE_INST_ANY over SQ_WAVE_CYCLES); the latency is VmemLatency (in-flight vector-memory "
+                 "instructions accumulated over their count).", "",
+                 f"- attention kernel_source_sha256: `{kernel_source_hash()}`", "",
+                 "Commands:", "", "```", *cmds, "```", ""]
+        lines += sq_table(csvs)
         lines.append("")
         open(out, "w").write("\n".join(lines))
         print("\n".join(lines))
