@@ -22,12 +22,12 @@
 //
 // Top-K ([paper] §1, §2.1; ties to the smaller block index): one workgroup per (sequence, kv head) keeps
 // all N keys in registers (order-preserving 64-bit images of the fp64 scores; 256 threads with up to 8
-// contiguous keys each up to 2048 keys) and runs an MSD radix select with 4-bit digits: per pass each
-// lane counts its candidates' digits in 16-bit fields, waves reduce them with DPP row operations, one
-// barrier combines the waves, and a 16-lane suffix sum with one ballot picks the boundary digit.  Leading
-// bits shared by every key are skipped, and the search stops as soon as the boundary digit's bucket
-// is taken whole.  Ties on the full key go to the smaller index through a prefix sum over the
-// threads' contiguous index ranges, which also yields the ascending output positions directly.
+// contiguous keys each up to 2048 keys) and runs an MSD radix select with 8-bit digits: per pass the
+// candidates' digits are counted in an LDS histogram, one barrier completes it, and every wave finds the
+// boundary digit from the 256 counts with a DPP prefix sum over its lanes and one ballot.  Leading bits
+// shared by every key are skipped, and the search stops as soon as the boundary digit's bucket is taken
+// whole.  Ties on the full key go to the smaller index through a prefix sum over the threads'
+// contiguous index ranges, which also yields the ascending output positions directly.
 
 #pragma once
 
