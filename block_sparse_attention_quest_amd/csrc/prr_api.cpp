@@ -214,7 +214,7 @@ static bool selection_plan_exists(const prr_kv_cache *kv, int nmax, int topk, bo
     if (nmax > prr::kMaxSelectN) return false;
     if (nmax <= prr::kMaxRowTopK) return true;
     const bool bq = kv->dtype != PRR_F32;
-    if (fused && bq) return prr::select_spec_plan(nmax, topk, mean).three;
+    if (fused && bq) return prr::select_spec_plan(nmax, topk, mean, kv->batch * kv->num_kv_heads).three;
     return prr::select_supported(nmax, topk, bq, mean);
 }
 

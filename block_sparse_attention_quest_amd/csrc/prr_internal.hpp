@@ -122,7 +122,7 @@ struct SelectSpecPlan {
     int gp, ng, kl2, kpt2, kpt3;
     int bpw;   // blocks per scoring workgroup (score_bpw: 1024 for wide bf16 min/max scoring)
 };
-SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean);
+SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean, int units);
 
 // The staged plan of launch_select for rows of more than kStagedSelectMin blocks (three stages; wide
 // scoring parts for bf16 min/max rows of kWideScoreBlocks and more where they have a plan).

@@ -314,6 +314,9 @@ constexpr int kScoreBPL = (BF16 || MEAN) ? 2 : 1;
 // for the same bytes), so shorter rows keep two.
 constexpr int kWideScoreBlocks = 32768;
 constexpr int kWideScoreBPL = 4;
+// ... and so do rows whose 512-block parts would number more than this over all units (one per CU of
+// the MI355X) in a fused launch, where the scoring grid would otherwise take the speculative pass's slots.
+constexpr long kWideScoreParts = 256;
 
 // Blocks per scoring workgroup (256 lanes of kScoreBPL blocks, or kWideScoreBPL), on the host.
 constexpr int score_bpw(bool bq, bool mean, bool wide = false) {

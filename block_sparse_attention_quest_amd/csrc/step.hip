@@ -63,11 +63,21 @@ SelectSpecPlan stage_plan(int nmax, int topk, int bpw, bool force_three) {
 // (kMaxTwoStageBlocks); longer rows take the three stages (inside the launch when its scoring workgroups
 // are resident, else the last two in launches of their own).  Rows of kWideScoreBlocks and more score
 // four blocks per lane where that plan takes three stages too.
-SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean) {
+// Wide parts also go to rows of more than kMaxFusedPredictN blocks (a carried predictor is never
+// affected) whose 512-block parts would number more than kWideScoreParts over all units, where the plan
+// at 1024 blocks ranks in two stages with 2 to 16 slots per thread or in three: at 256K, batch 4,
+// G = 8 (8192 blocks, 512 parts) select_spec went from 47.3 to 40.9 us and the layer step from 59.8 to
+// 53.5 us.  With fewer parts than CUs the narrow parts keep the chip busier (128K, batch 8: 256 parts).
+SelectSpecPlan select_spec_plan(int nmax, int topk, bool mean, int units) {
     const bool force = nmax > kMaxTwoStageBlocks;
-    if (!mean && nmax >= kWideScoreBlocks) {
-        const SelectSpecPlan wide = stage_plan(nmax, topk, score_bpw(true, false, true), force);
-        if (wide.three) return wide;
+    if (!mean) {
+        const bool long_row = nmax >= kWideScoreBlocks;
+        const bool many_parts = nmax > kMaxFusedPredictN &&
+                                (long)((nmax + score_bpw(true, false) - 1) / score_bpw(true, false)) * units > kWideScoreParts;
+        if (long_row || many_parts) {
+            const SelectSpecPlan wide = stage_plan(nmax, topk, score_bpw(true, false, true), force);
+            if (wide.three || (many_parts && wide.two && wide.kpt >= 2)) return wide;
+        }
     }
     return stage_plan(nmax, topk, score_bpw(true, mean), force);
 }
@@ -84,7 +94,7 @@ SelectSpecPlan select_stage_plan(int nmax, int topk, bool bq, bool mean) {
 // counts.  The workspace covers both block summaries.  A three-stage top-K appends the group candidates
 // ([units][ng][kl2] keys and indices, [units][ng] counts) and one group arrival counter per unit.
 static size_t candidate_bytes(int units, int nmax, int topk, bool mean) {
-    const SelectSpecPlan pl = select_spec_plan(nmax, topk, mean);
+    const SelectSpecPlan pl = select_spec_plan(nmax, topk, mean, units);
     if (!pl.two) return 0;
     const int nparts = (nmax + pl.bpw - 1) / pl.bpw;
     if (pl.three) return stage_layout(nullptr, units, nparts, pl).bytes;

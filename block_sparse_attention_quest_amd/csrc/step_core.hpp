@@ -10,7 +10,8 @@
 // stream follow each other about 1 us apart, so the overlap is made inside one grid instead: the first
 // workgroups score blocks (one workgroup per 512 blocks of a unit, two per lane, for min/max metadata and
 // for block means alike; 1024 blocks, four per lane, for the min/max metadata of rows of 32768 blocks and
-// more that rank in three stages), the rest run the speculative chunks (the attention kernels' chunk walk over
+// more that rank in three stages and of launches with more than 256 such parts), the rest run the
+// speculative chunks (the attention kernels' chunk walk over
 // n_spec workgroups, on bf16 or fp8 tiles: KT).  Dispatch follows the workgroup index, so
 // the scoring workgroups issue their loads first: the memory system serves them ahead of the
 // speculative stream, selection finishes early and its top-K runs under the speculative pass, which is
@@ -49,7 +50,7 @@ namespace {
 
 // Workgroup s < nsx * units scores blocks [BPW (s mod nsx), +BPW) of unit s / nsx (BPW = 512 blocks, two
 // per lane, for bf16 min/max metadata and for fp32 block means: MEAN; 1024, four per lane, for the bf16
-// min/max parts of long rows: WIDE) and, if it is the unit's last to finish and
+// min/max parts of long rows and of many-part launches: WIDE) and, if it is the unit's last to finish and
 // KPT > 0, runs the unit's top-K (KPT keys per thread, 256 KPT >= the unit's block count); the remaining
 // n_spec workgroups run the speculative pass.  PRED: the scoring workgroups then draw the n_pred units
 // of another layer's predictor step from *pred_ctr (8 keys per thread: rows of up to 2048 blocks); every
@@ -224,7 +225,7 @@ inline FusedSetup fused_setup(const KvDesc &kv, const void *q, int hq, const voi
     // tokens), the speculative pass is spread over the slots that are left, so that the whole grid is
     // resident from the start instead of speculative workgroups waiting for scoring ones to finish.
     const int cus = device_cu_count();
-    f.plan = select_spec_plan(nmax, topk, mean);
+    f.plan = select_spec_plan(nmax, topk, mean, kv.batch * kv.hkv);
     const int bpw = f.plan.bpw;
     const int n_score_wgs = (nmax + bpw - 1) / bpw * kv.batch * kv.hkv;
     const int spec_target = n_score_wgs > cus ? std::max(cus / 2, 2 * cus - n_score_wgs) : cus;
@@ -370,8 +371,11 @@ hipError_t launch_select_spec_t(const KvDesc &kv, const void *q, int hq, const v
                    f.n_pred, none, 0);                                                                      \
     } else
 #define PRR_SS(DD, K, T, MN, PR, K2, K3) PRR_SSW(DD, K, T, MN, PR, K2, K3, false)
-// wide scoring parts: bf16 min/max rows of three stages; a carried predictor runs as its own launch
+// wide scoring parts: bf16 min/max rows of two stages (2 to 16 slots per thread) or three; a carried
+// predictor runs as its own launch
 #define PRR_SS_WIDE(DD)                                                                                     \
+    PRR_SSW(DD, 2, true, false, false, 0, 0, true) PRR_SSW(DD, 4, true, false, false, 0, 0, true)            \
+    PRR_SSW(DD, 8, true, false, false, 0, 0, true) PRR_SSW(DD, 16, true, false, false, 0, 0, true)           \
     PRR_SSW(DD, 0, true, false, false, 0, 0, true) PRR_SSW(DD, 0, true, false, false, 8, 4, true)            \
     PRR_SSW(DD, 0, true, false, false, 8, 8, true) PRR_SSW(DD, 0, true, false, false, 8, 16, true)           \
     PRR_SSW(DD, 0, true, false, false, 16, 16, true)
@@ -420,7 +424,7 @@ hipError_t launch_layer_step_t(const KvDesc &kv, const void *q, int hq, const vo
     const size_t mbytes = layer_extra_m_ws(kv.batch, hq, kv.hkv, kv.d, block, m_cap);
     uint32_t *ready = (uint32_t *)((char *)mws + mbytes);
     uint32_t *status = (uint32_t *)((char *)mws + mbytes + (size_t)units * 4 * kReadyStride);
-    const SelectSpecPlan plan = select_spec_plan(nmax, topk, mean);
+    const SelectSpecPlan plan = select_spec_plan(nmax, topk, mean, units);
     const int bpw = plan.bpw;
     const long n_score_wgs = (long)((nmax + bpw - 1) / bpw) * units;
     if (KT == kKtF32 || (plan.kpt == 0 && !plan.three) || (plan.three && three_stage_kpt(plan, n_score_wgs) == 0)) {
@@ -457,6 +461,8 @@ hipError_t launch_layer_step_t(const KvDesc &kv, const void *q, int hq, const vo
     } else
 #define PRR_LS(DD, K, T, MN, PR, K2, K3) PRR_LSW(DD, K, T, MN, PR, K2, K3, false)
 #define PRR_LS_WIDE(DD)                                                                                     \
+    PRR_LSW(DD, 2, true, false, false, 0, 0, true) PRR_LSW(DD, 4, true, false, false, 0, 0, true)            \
+    PRR_LSW(DD, 8, true, false, false, 0, 0, true) PRR_LSW(DD, 16, true, false, false, 0, 0, true)           \
     PRR_LSW(DD, 0, true, false, false, 8, 4, true) PRR_LSW(DD, 0, true, false, false, 8, 8, true)            \
     PRR_LSW(DD, 0, true, false, false, 8, 16, true) PRR_LSW(DD, 0, true, false, false, 16, 16, true)
 #define PRR_LS_K(DD, MN, PR)                                                                                \

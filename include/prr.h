@@ -204,7 +204,8 @@ prr_status prr_select(const void *q, int32_t num_q_heads, const prr_kv_cache *kv
  * compute, as one grid whose workgroups do either part (bf16 caches; fp32 caches run the two calls in
  * turn), followed by the top-K on the same stream.  scores, A and M are the same bit for bit.  The state
  * is too while the scoring workgroups (ceil(N_max / 512) per (sequence, kv head); ceil(N_max / 1024) for
- * min/max scoring of rows of 32768 blocks and more that rank in three stages) number at most the
+ * min/max scoring of rows of 32768 blocks and more that rank in three stages, and of rows of more than
+ * 2048 blocks whose 512-block parts would number more than 256 in all) number at most the
  * GPU's compute units; with more of them the speculative pass is cut into fewer, longer chunks so that the
  * whole grid is resident at once, and the state then differs from prr_spec_attn's by rounding only (the
  * order of the sums changes).  P and M must be non-NULL; A->cap and M->cap >= topk; rows as for

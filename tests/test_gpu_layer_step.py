@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from _gpu import assert_heads, device_kv, require_gpu, sets_to_device, unit_view
+from _gpu import assert_heads, device_kv, require_gpu, sets_to_device, unit_meta, unit_view
 from block_sparse_attention_quest_amd import binding as bd
 from block_sparse_attention_quest_amd import workloads as wl
 from oracle import prr_oracle as orc
@@ -187,6 +187,42 @@ def test_layer_step_three_stage_rows_in_one_launch(blocks, topk, dt):
     P = _random_p(w, rng, [200, topk, 0, 37])
     (_, A, M, ref, ref_out), (got, got_out) = _run_both(w, inp, P, w.topk, topk)
     _check_against_oracle(w, inp, P, A.lists(), M.lists(), got, got_out, ref)
+
+
+@pytest.mark.parametrize("topk", [40, 64, 128, 300, 512], ids=lambda k: f"k{k}")
+def test_wide_parts_when_parts_outnumber_cus(topk):
+    """16 sequences x 2 kv heads of up to 4608 blocks: 288 scoring parts of 512 blocks, more than the GPU
+    has CUs, so the fused launches score 1024 blocks per workgroup (5 parts per row) and rank them in two
+    stages with 2, 4, 8 or 16 slots per thread (K = 64, 128, 300, 512); at K = 40 (1 slot per thread) they
+    keep the 512-block parts.  Scores, A and M of prr_select_spec and prr_layer_step equal prr_select's bit
+    for bit, A the oracle's on sampled units, and the layer step's state the separate calls' within
+    tolerance."""
+    lens = [4608 * 16 - 16 * 37 * k - (k % 3) for k in range(16)]
+    w = wl.Workload("many_parts", 16, 8, 2, 64, lens[0], 16, topk, "bf16", seed=300 + topk, seq_lens=lens)
+    inp = wl.make_inputs(w, "cuda")
+    rng = np.random.default_rng(topk)
+    P = _random_p(w, rng, [topk // 2, topk, 0, 17])
+    (scores, A, M, ref, ref_out), (got, got_out) = _run_both(w, inp, P, topk, topk)
+    dkv = device_kv(inp)
+    meta = bd.build_meta(dkv, w.block)
+    Pd = sets_to_device(P, topk)
+    s3, A3, M3, _ = bd.select_spec(inp.q[0], dkv, meta, w.block, topk, Pd, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(s3, scores) and A3.lists() == A.lists() and M3.lists() == M.lists()
+    for b, h in ((0, 0), (7, 1), (15, 1)):
+        q, ukv = unit_view(inp, b, h)
+        mn, mx = unit_meta(ukv, w.block)
+        s = orc.quest_scores(orc.representative_query(q, 0, 0, w.group), mn, mx)
+        assert np.array_equal(scores[b, h, :w.blocks_of(b)].cpu().numpy(), s), (b, h)
+        assert A.lists()[b][h] == list(orc.topk_blocks(s, topk)), (b, h)
+    acc, l, m = (t.double().cpu().numpy() for t in (got.acc, got.l, got.m))
+    racc, rl, rm = (t.double().cpu().numpy() for t in (ref.acc, ref.l, ref.m))
+    live = rl > 0
+    assert np.array_equal(l > 0, live)
+    assert np.all(np.abs(l - rl)[live] <= 1e-4 * rl[live])
+    assert np.all(np.abs(m - rm)[live] <= 1e-4 * np.maximum(1.0, np.abs(rm[live])))
+    for b, h in zip(*np.nonzero(live)):
+        assert np.max(np.abs(acc[b, h] / l[b, h] - racc[b, h] / rl[b, h])) <= 5e-3
 
 
 def test_layer_step_carrying_a_predictor_step():
