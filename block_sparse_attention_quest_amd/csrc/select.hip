@@ -174,9 +174,10 @@ __global__ __launch_bounds__(256) void summary_kernel(MetaParams p) {
 // Kernels
 // ------------------------------------------------------------------------------------------------
 
-template <bool BF16, int D, bool MEAN>
+template <bool BF16, int D, bool MEAN, int BPL = kScoreBPL<BF16, MEAN>>
 __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
-    score_body<BF16, D, false, MEAN>(p, blockIdx.x, blockIdx.y);
+    double kept[BPL];
+    score_body<BF16, D, false, MEAN, BPL>(p, blockIdx.x, blockIdx.y, kept);
 }
 
 // First stage of a three-stage top-K over rows longer than one top-K workgroup holds: workgroup bx of
@@ -355,7 +356,11 @@ hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *me
     const bool bq = kv.bf16 || kv.fp8;   // bf16 queries (and bf16 min/max metadata)
     const SelectSpecPlan plan = ws && nmax > kStagedSelectMin ? select_stage_plan(nmax, topk, bq, mean) : SelectSpecPlan{};
     if (nmax > kMaxRowTopK && !plan.three) return hipErrorInvalidValue;
-    const int bpw = plan.three ? plan.bpw : score_bpw(bq, mean);
+    // The score kernel alone scores one bf16 min/max block per lane: twice the workgroups of the fused
+    // launches' two per lane (whose grid shares the chip with the speculative pass), two waves per SIMD
+    // to hide each other's float64 chains.  128K, batch 8: selection 21.7 -> 18.9 us; 32K: 18.7 -> 14.8 us.
+    const bool one_per_lane = bq && !mean;
+    const int bpw = plan.three ? plan.bpw : one_per_lane ? 256 : score_bpw(bq, mean);
     const dim3 sgrid((nmax + bpw - 1) / bpw, units);
     if (plan.three) {
         // three stages: the scoring workgroups keep their parts' candidates, then groups and the ranking
@@ -392,8 +397,8 @@ hipError_t launch_select(const KvDesc &kv, const void *q, int hq, const void *me
             else PRR_LAUNCH(score_kernel<false, 64, true>, dim3(sgrid), dim3(256), stream, sp);
         }
     } else if (bq) {
-        if (kv.d == 128) PRR_LAUNCH(score_kernel<true, 128, false>, dim3(sgrid), dim3(256), stream, sp);
-        else PRR_LAUNCH(score_kernel<true, 64, false>, dim3(sgrid), dim3(256), stream, sp);
+        if (kv.d == 128) PRR_LAUNCH((score_kernel<true, 128, false, 1>), dim3(sgrid), dim3(256), stream, sp);
+        else PRR_LAUNCH((score_kernel<true, 64, false, 1>), dim3(sgrid), dim3(256), stream, sp);
     } else {
         if (kv.d == 128) PRR_LAUNCH(score_kernel<false, 128, false>, dim3(sgrid), dim3(256), stream, sp);
         else PRR_LAUNCH(score_kernel<false, 64, false>, dim3(sgrid), dim3(256), stream, sp);

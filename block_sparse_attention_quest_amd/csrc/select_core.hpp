@@ -303,7 +303,8 @@ struct ScoreParams {
 
 // Blocks per lane of the scoring workgroups: two for bf16 min/max metadata (one 4-byte load per channel
 // covers both) and for the fp32 block means of mean-pooled scoring (one 8-byte load per channel, in two
-// halves of the channels), one for fp32 min/max.
+// halves of the channels), one for fp32 min/max.  prr_select's score kernel, which has the chip to
+// itself, takes one bf16 min/max block per lane (a 2-byte load per channel) for twice the waves.
 template <bool BF16, bool MEAN = false>
 constexpr int kScoreBPL = (BF16 || MEAN) ? 2 : 1;
 
@@ -328,8 +329,8 @@ constexpr int score_bpw(bool bq, bool mean, bool wide = false) {
 // BPL: kScoreBPL, or kWideScoreBPL for bf16 min/max metadata.
 template <bool BF16, int D, bool COHERENT = false, bool MEAN = false, int BPL = kScoreBPL<BF16, MEAN>>
 __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u, double (&kept)[BPL]) {
-    static_assert(BPL == kScoreBPL<BF16, MEAN> || (BF16 && !MEAN && BPL == kWideScoreBPL),
-                  "four blocks per lane: bf16 min/max metadata only");
+    static_assert(BPL == kScoreBPL<BF16, MEAN> || (BF16 && !MEAN && (BPL == kWideScoreBPL || BPL == 1)),
+                  "one or four blocks per lane: bf16 min/max metadata only");
     __shared__ double s_qbar[D];
     __shared__ int s_row[D];             // metadata row of channel i: 1 (max) when qbar_i >= 0, else 0 (min)
     const int b = u / p.hkv, kvh = u - b * p.hkv;
@@ -423,7 +424,10 @@ __device__ __forceinline__ void score_body(const ScoreParams &p, int bx, int u, 
             // qbar >= 0: the max term is qbar * mx (row 1); otherwise qbar * mn (row 0).  bf16: the 4 bytes
             // hold blocks p0 and p0 + 1; fp32: block p0.
             const int sgn = __builtin_amdgcn_readfirstlane(s_row[i]);
-            raw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, (2 * i + sgn) * p.stride * ES, 0);
+            if constexpr (BF16 && BPL == 1)   // one bf16 block per lane: a 2-byte load
+                raw[i] = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rsrc, voff, (2 * i + sgn) * p.stride * ES, 0);
+            else
+                raw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, (2 * i + sgn) * p.stride * ES, 0);
         }
 #pragma unroll
         for (int i = 0; i < D; ++i) {
