@@ -286,8 +286,8 @@ hipError_t dispatch_topk(int nmax, int units, const P &p, hipStream_t stream) {
     topk_shape(nmax, tpb, kpt);
 #define PRR_CASE(T, K) \
     if (tpb == T && kpt == K) return Launch<K, T>::run(units, p, stream);
-    PRR_CASE(64, 1) PRR_CASE(64, 2) PRR_CASE(256, 1) PRR_CASE(256, 2) PRR_CASE(256, 4) PRR_CASE(256, 8)
-    PRR_CASE(1024, 4) PRR_CASE(1024, 8) PRR_CASE(1024, 16) PRR_CASE(1024, 32)
+    PRR_CASE(64, 1) PRR_CASE(64, 2) PRR_CASE(256, 1) PRR_CASE(256, 2) PRR_CASE(256, 4)
+    PRR_CASE(1024, 2) PRR_CASE(1024, 4) PRR_CASE(1024, 8) PRR_CASE(1024, 16) PRR_CASE(1024, 32)
 #undef PRR_CASE
     return hipErrorInvalidValue;
 }

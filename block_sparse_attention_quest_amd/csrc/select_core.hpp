@@ -972,11 +972,11 @@ __device__ __forceinline__ void predict_part_body(const PredictParams &p, int u,
 }
 
 // Workgroup shape of the top-K kernels for rows of up to nmax keys: one wave per SIMD (256 threads) with
-// up to 8 keys each up to 2048 keys (the radix passes' cost is the per-wave work, so four busy SIMDs
-// with a few keys each beat many waves or one wave with many keys); 1024 threads with up to 32 keys
-// beyond that.
+// up to 4 keys each up to 1024 keys; 1024 threads with 2 to 32 keys beyond that. With 8-bit digits a
+// pass costs few barriers, so at 2048 keys spreading the per-key work (the predictor's EMA update and
+// the digit histogram) over 16 waves beats 4 waves with 8 keys each.
 void topk_shape(int nmax, int &tpb, int &kpt) {
-    tpb = nmax <= 128 ? 64 : nmax <= 2048 ? 256 : 1024;
+    tpb = nmax <= 128 ? 64 : nmax <= 1024 ? 256 : 1024;
     kpt = 1;
     while (kpt * tpb < nmax) kpt *= 2;
 }
